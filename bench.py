@@ -1,0 +1,212 @@
+#!/usr/bin/env python3
+"""Benchmark of the STA forward (one GPU).
+
+One step = one sta_forward call (pack q/k/v to tile-major order, schedule,
+fused attention, scatter back) on the workload's synthetic bf16 inputs, which
+are resident in HBM before timing starts. Prints one JSON line with the
+end-to-end effective TFLOP/s, the roofline of the fused attention kernel
+(timed live with HIP events on the launch stream) and the fp64 CPU oracle's
+throughput on a bounded sample of the same workload.
+
+Effective FLOPs count 4*D per allowed (query, key) pair over the valid query
+rows (video rows and the first text_length text rows), i.e. only the tiles
+that are computed.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "STA fwd ms/call + effective TFLOP/s (% bf16 MFMA peak), (30,48,80)+256 text"
+# MI355X dense bf16 MFMA peak: 256 CUs x 4096 flop/clk x 2.4 GHz (published: 2.5 PFLOP/s)
+PEAK_BF16_TFLOPS = 256 * 4096 * 2.4e9 / 1e12
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "attention_headline_pmc.txt")
+ATTN_SOURCE = os.path.join(ROOT, "block_sparse_sliding_amd", "csrc", "sta_attention.hip")
+
+
+def effective_flops(wl, include_pad_rows=False) -> float:
+    T, H, W = wl.video
+    nv = T * H * W
+    ell = wl.text_length if wl.has_text else 0
+    text_rows = (256 if include_pad_rows else ell) if wl.has_text else 0
+    pairs = 0
+    for (wt, wh, ww) in wl.windows:
+        pairs += nv * (wt * wh * ww * 384 + ell) + text_rows * (nv + ell)
+    return 4.0 * wl.head_dim * pairs * wl.batch
+
+
+def source_sha() -> str:
+    with open(ATTN_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per attention launch from the committed rocprofv3 counter summary.
+
+    Returns None when there is no summary or the kernel source changed since
+    the counters were taken.
+    """
+    if not os.path.exists(PMC_SUMMARY):
+        return None
+    vals = {}
+    with open(PMC_SUMMARY) as f:
+        for line in f:
+            if ":" in line:
+                key, _, val = line.partition(":")
+                vals[key.strip()] = val.strip()
+    if vals.get("kernel_source_sha256_16") != source_sha():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(wl, q, k, v, budget_s: float, flops: float):
+    """Time the fp64 oracle on a bounded row sample and scale to one full call."""
+    import numpy as np
+
+    import oracle
+    import sta_inputs
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    rows = sta_inputs.sample_rows(wl, per_head=192).numpy()
+    done_rows, elapsed, heads_done = 0, 0.0, 0
+    for h in range(wl.heads):
+        qh, kh, vh = (x[:, h:h + 1].cpu() for x in (q, k, v))
+        t0 = time.perf_counter()
+        oracle.sta_reference(qh, kh, vh, [wl.windows[h]], wl.text_length, wl.has_text, wl.video,
+                             rows=rows)
+        elapsed += time.perf_counter() - t0
+        done_rows += len(rows) * wl.batch
+        heads_done += 1
+        if elapsed >= budget_s:
+            break
+    per_row = elapsed / done_rows
+    full_call_s = per_row * wl.batch * wl.heads * wl.seq_len
+    return {
+        "value": flops / full_call_s / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"{done_rows} query rows ({len(rows)} stratified rows x {heads_done} heads), "
+                   f"each dense over all {wl.seq_len} keys, {elapsed:.1f} s; extrapolated to "
+                   f"B*heads*S = {wl.batch * wl.heads * wl.seq_len} rows"),
+        "ms_per_call_extrapolated": full_call_s * 1e3,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="headline")
+    ap.add_argument("--cpu-budget", type=float, default=12.0,
+                    help="seconds of oracle work for the CPU baseline (0 to skip)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+
+    import block_sparse_sliding_amd as sta
+    import sta_inputs
+
+    if not torch.cuda.is_available():
+        raise RuntimeError("bench.py needs a GPU")
+    wl = sta_inputs.WORKLOADS[args.workload]
+    windows = list(wl.windows)
+    q, k, v = sta_inputs.make_qkv(wl, "cuda")
+    dims = sta.make_dims(wl.batch, wl.heads, wl.head_dim, wl.video)
+    out = torch.empty_like(q)
+    lse = torch.empty(wl.batch, wl.heads, wl.seq_len, dtype=torch.float32, device="cuda")
+    ws = torch.empty(sta.sta_workspace_bytes(dims, windows, wl.has_text), dtype=torch.uint8,
+                     device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(events=None):
+        if events is None:
+            sta.sta_forward(dims, q, k, v, windows, wl.text_length, wl.has_text, out, lse, ws)
+        else:
+            sta.sta_forward_timed(dims, q, k, v, windows, wl.text_length, wl.has_text, out, lse,
+                                  ws, events)
+
+    for _ in range(args.warmup):
+        step()
+    ev_sets = []
+    for _ in range(args.steps):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(sta.TIMED_EVENTS)]
+        for e in evs:
+            e.record(stream)  # materialise the underlying hipEvent
+        ev_sets.append(evs)
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(args.steps):
+        step(ev_sets[i])
+    stop.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    ms_per_step = total_ms / args.steps
+    stage_ms = {name: 0.0 for name in sta.STAGES}
+    for evs in ev_sets:
+        for j, name in enumerate(sta.STAGES):
+            stage_ms[name] += evs[j].elapsed_time(evs[j + 1]) / args.steps
+
+    flops = effective_flops(wl)
+    tflops = flops / (ms_per_step * 1e-3) / 1e12
+    attn_ms = stage_ms["attention"]
+    attn_tflops = flops / (attn_ms * 1e-3) / 1e12
+    traffic = measured_traffic()
+    result = {
+        "metric": METRIC,
+        "value": tflops,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": wl.describe(),
+        "ms_per_call": ms_per_step,
+        "pct_bf16_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
+        "effective_flop_per_call": flops,
+        "stages_ms": stage_ms,
+        "roofline": {
+            "kernel": "sta_attention_kernel<128>" if wl.head_dim == 128 else "sta_attention_kernel<64>",
+            "bound": "mfma",
+            "achieved": attn_tflops,
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": attn_tflops / PEAK_BF16_TFLOPS,
+            "traffic": traffic,
+            "launch_ms": attn_ms,
+        },
+    }
+    if args.cpu_budget > 0:
+        result["cpu_baseline"] = cpu_baseline(wl, q, k, v, args.cpu_budget, flops)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

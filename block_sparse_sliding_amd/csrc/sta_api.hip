@@ -1,0 +1,293 @@
+// Host side of the STA C ABI (include/sta.h): argument validation, geometry,
+// workspace carving and the launch sequence on the caller's stream.
+//
+// Validation is plain C++ and runs before any HIP call, so argument errors
+// are reported synchronously and can be exercised without a GPU.
+#include <cmath>
+#include <cstring>
+
+#include "../../include/sta.h"
+#include "sta_internal.h"
+
+namespace {
+
+using sta::Geom;
+using sta::Windows;
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+sta_status make_geom(const sta_dims* d, int32_t has_text, int32_t text_length, Geom* g) {
+  if (d == nullptr) return STA_ERR_NULL;
+  if (d->batch <= 0 || d->heads <= 0) return STA_ERR_NULL;
+  if (d->heads > STA_MAX_HEADS) return STA_ERR_SHAPE;
+  if (d->head_dim != 64 && d->head_dim != 128) return STA_ERR_SHAPE;
+  if (d->T <= 0 || d->H <= 0 || d->W <= 0) return STA_ERR_SHAPE;
+  if (d->T % sta::kTileT || d->H % sta::kTileH || d->W % sta::kTileW) return STA_ERR_SHAPE;
+  const int64_t nt = d->T / sta::kTileT, nh = d->H / sta::kTileH, nw = d->W / sta::kTileW;
+  if (nt > 1023 || nh > 1023 || nw > 1023) return STA_ERR_SHAPE;
+  const int64_t n_video = int64_t(d->T) * d->H * d->W;
+  const int64_t S = n_video + (has_text ? STA_TEXT_SLOTS : 0);
+  // per-slab element offsets and row indices are 32-bit inside the kernels
+  if (S * d->head_dim >= (int64_t(1) << 31)) return STA_ERR_SHAPE;
+  const int64_t n_q = nt * nh * nw + (has_text ? 1 : 0);
+  if (int64_t(d->batch) * d->heads * n_q >= (int64_t(1) << 31)) return STA_ERR_SHAPE;
+  if (int64_t(d->batch) * d->heads * (S / sta::kKeyBlock) >= (int64_t(1) << 31)) return STA_ERR_SHAPE;
+  if (has_text) {
+    if (text_length < 0 || text_length > STA_TEXT_SLOTS) return STA_ERR_TEXT;
+  } else if (text_length != 0) {
+    return STA_ERR_TEXT;
+  }
+  g->B = d->batch;
+  g->heads = d->heads;
+  g->D = d->head_dim;
+  g->T = d->T;
+  g->H = d->H;
+  g->W = d->W;
+  g->nt = int32_t(nt);
+  g->nh = int32_t(nh);
+  g->nw = int32_t(nw);
+  g->n_tiles = int32_t(nt * nh * nw);
+  g->n_video = int32_t(n_video);
+  g->S = int32_t(S);
+  g->has_text = has_text ? 1 : 0;
+  g->text_length = text_length;
+  g->n_q = int32_t(n_q);
+  return STA_OK;
+}
+
+sta_status make_windows(const Geom& g, const int32_t* ws, Windows* win, int64_t* n_ids) {
+  if (ws == nullptr) return STA_ERR_NULL;
+  int64_t total = 0;
+  std::memset(win, 0, sizeof(*win));
+  for (int h = 0; h < g.heads; ++h) {
+    const int32_t wt = ws[3 * h], wh = ws[3 * h + 1], ww = ws[3 * h + 2];
+    if (wt < 1 || wt > g.nt || wh < 1 || wh > g.nh || ww < 1 || ww > g.nw) return STA_ERR_WINDOW;
+    win->w[h] = uint32_t(wt) | (uint32_t(wh) << 10) | (uint32_t(ww) << 20);
+    total += int64_t(g.n_tiles) * wt * wh * ww + (g.has_text ? g.n_tiles : 0);
+  }
+  if (total >= (int64_t(1) << 31)) return STA_ERR_SHAPE;
+  *n_ids = total;
+  return STA_OK;
+}
+
+struct Carve {
+  size_t q_tiled, k_packed, v_packed, o_tiled, lse_tiled, offsets, ids, work, total;
+};
+
+Carve carve(const Geom& g, int64_t n_ids) {
+  Carve c{};
+  const size_t tensor = size_t(g.B) * g.heads * g.S * g.D * 2;
+  size_t at = 0;
+  c.q_tiled = at; at = align_up(at + tensor);
+  c.k_packed = at; at = align_up(at + tensor);
+  c.v_packed = at; at = align_up(at + tensor);
+  c.o_tiled = at; at = align_up(at + tensor);
+  c.lse_tiled = at; at = align_up(at + size_t(g.B) * g.heads * g.S * 4);
+  c.offsets = at; at = align_up(at + (size_t(g.heads) * g.n_q + 1) * 4);
+  c.ids = at; at = align_up(at + size_t(n_ids) * 4);
+  c.work = at; at = align_up(at + size_t(g.B) * g.heads * g.n_q * 4);
+  c.total = at;
+  return c;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+sta_status hip_status(hipError_t e) { return e == hipSuccess ? STA_OK : STA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* sta_status_str(sta_status s) {
+  switch (s) {
+    case STA_OK: return "STA_OK";
+    case STA_ERR_NULL: return "STA_ERR_NULL: NULL pointer or non-positive batch/heads";
+    case STA_ERR_SHAPE: return "STA_ERR_SHAPE: unsupported video size, head_dim, head count or size";
+    case STA_ERR_WINDOW: return "STA_ERR_WINDOW: window component outside [1, tiles on that axis]";
+    case STA_ERR_TEXT: return "STA_ERR_TEXT: text_length outside [0, 256] or non-zero without text";
+    case STA_ERR_ALIGN: return "STA_ERR_ALIGN: device pointer not 16-byte aligned";
+    case STA_ERR_WORKSPACE: return "STA_ERR_WORKSPACE: workspace missing or too small";
+    case STA_ERR_HIP: return "STA_ERR_HIP: HIP runtime error at launch";
+    case STA_ERR_ALIAS: return "STA_ERR_ALIAS: output overlaps an input";
+  }
+  return "STA_ERR_UNKNOWN";
+}
+
+int64_t sta_seq_len(const sta_dims* dims, int32_t has_text) {
+  Geom g;
+  if (make_geom(dims, has_text, 0, &g) != STA_OK) return 0;
+  return g.S;
+}
+
+size_t sta_workspace_bytes(const sta_dims* dims, const int32_t* window_sizes, int32_t has_text) {
+  Geom g;
+  if (make_geom(dims, has_text, 0, &g) != STA_OK) return 0;
+  Windows win;
+  int64_t n_ids = 0;
+  if (make_windows(g, window_sizes, &win, &n_ids) != STA_OK) return 0;
+  return carve(g, n_ids).total;
+}
+
+sta_status sta_schedule_sizes(const sta_dims* dims, const int32_t* window_sizes, int32_t has_text,
+                              int64_t* n_offsets, int64_t* n_ids, int64_t* n_work) {
+  Geom g;
+  sta_status st = make_geom(dims, has_text, 0, &g);
+  if (st != STA_OK) return st;
+  if (n_offsets == nullptr || n_ids == nullptr || n_work == nullptr) return STA_ERR_NULL;
+  Windows win;
+  int64_t ids = 0;
+  st = make_windows(g, window_sizes, &win, &ids);
+  if (st != STA_OK) return st;
+  *n_offsets = int64_t(g.heads) * g.n_q + 1;
+  *n_ids = ids;
+  *n_work = int64_t(g.B) * g.heads * g.n_q;
+  return STA_OK;
+}
+
+sta_status sta_build_schedule(const sta_dims* dims, const int32_t* window_sizes, int32_t text_length,
+                              int32_t has_text, int32_t* offsets, int32_t* ids, int32_t* work,
+                              void* stream) {
+  Geom g;
+  sta_status st = make_geom(dims, has_text, text_length, &g);
+  if (st != STA_OK) return st;
+  Windows win;
+  int64_t n_ids = 0;
+  st = make_windows(g, window_sizes, &win, &n_ids);
+  if (st != STA_OK) return st;
+  if (offsets == nullptr || ids == nullptr || work == nullptr) return STA_ERR_NULL;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  st = hip_status(sta::launch_schedule_lists(g, win, offsets, ids, s));
+  if (st != STA_OK) return st;
+  return hip_status(sta::launch_schedule_work(g, win, work, s));
+}
+
+sta_status sta_tile_gather(const sta_dims* dims, int32_t has_text, const void* x_raster,
+                           void* x_tiled, void* stream) {
+  Geom g;
+  sta_status st = make_geom(dims, has_text, 0, &g);
+  if (st != STA_OK) return st;
+  if (x_raster == nullptr || x_tiled == nullptr) return STA_ERR_NULL;
+  if (!aligned16(x_raster) || !aligned16(x_tiled)) return STA_ERR_ALIGN;
+  const size_t bytes = size_t(g.B) * g.heads * g.S * g.D * 2;
+  if (overlaps(x_raster, bytes, x_tiled, bytes)) return STA_ERR_ALIAS;
+  return hip_status(sta::launch_rows_permute(g, x_raster, x_tiled, true,
+                                             reinterpret_cast<hipStream_t>(stream)));
+}
+
+sta_status sta_tile_scatter(const sta_dims* dims, int32_t has_text, const void* x_tiled,
+                            void* x_raster, void* stream) {
+  Geom g;
+  sta_status st = make_geom(dims, has_text, 0, &g);
+  if (st != STA_OK) return st;
+  if (x_raster == nullptr || x_tiled == nullptr) return STA_ERR_NULL;
+  if (!aligned16(x_raster) || !aligned16(x_tiled)) return STA_ERR_ALIGN;
+  const size_t bytes = size_t(g.B) * g.heads * g.S * g.D * 2;
+  if (overlaps(x_raster, bytes, x_tiled, bytes)) return STA_ERR_ALIAS;
+  return hip_status(sta::launch_rows_permute(g, x_tiled, x_raster, false,
+                                             reinterpret_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"
+
+namespace {
+
+sta_status forward_impl(const sta_dims* dims, const void* q, const void* k, const void* v,
+                        const int32_t* window_sizes, int32_t text_length, int32_t has_text,
+                        void* out, float* lse, void* workspace, size_t workspace_bytes,
+                        void* stream, void* const* events) {
+  Geom g;
+  sta_status st = make_geom(dims, has_text, text_length, &g);
+  if (st != STA_OK) return st;
+  Windows win;
+  int64_t n_ids = 0;
+  st = make_windows(g, window_sizes, &win, &n_ids);
+  if (st != STA_OK) return st;
+  if (q == nullptr || k == nullptr || v == nullptr || out == nullptr) return STA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
+      (lse != nullptr && !aligned16(lse)))
+    return STA_ERR_ALIGN;
+  const Carve c = carve(g, n_ids);
+  if (workspace == nullptr || workspace_bytes < c.total) return STA_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return STA_ERR_ALIGN;
+  const size_t tbytes = size_t(g.B) * g.heads * g.S * g.D * 2;
+  const size_t lbytes = size_t(g.B) * g.heads * g.S * 4;
+  for (const void* in : {q, k, v, static_cast<const void*>(workspace)}) {
+    const size_t n = in == workspace ? c.total : tbytes;
+    if (overlaps(out, tbytes, in, n)) return STA_ERR_ALIAS;
+    if (lse != nullptr && overlaps(lse, lbytes, in, n)) return STA_ERR_ALIAS;
+  }
+  if (lse != nullptr && overlaps(lse, lbytes, out, tbytes)) return STA_ERR_ALIAS;
+
+  char* ws = static_cast<char*>(workspace);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  // optional timing events: recorded before the first launch and after each one
+  auto mark = [&](int i) -> sta_status {
+    if (events == nullptr) return STA_OK;
+    return hip_status(hipEventRecord(reinterpret_cast<hipEvent_t>(events[i]), s));
+  };
+  st = mark(0);
+  if (st != STA_OK) return st;
+  int32_t* offsets = reinterpret_cast<int32_t*>(ws + c.offsets);
+  int32_t* ids = reinterpret_cast<int32_t*>(ws + c.ids);
+  int32_t* work = reinterpret_cast<int32_t*>(ws + c.work);
+  float* lse_tiled = reinterpret_cast<float*>(ws + c.lse_tiled);
+
+  st = hip_status(sta::launch_pack_qkv(g, q, k, v, ws + c.q_tiled, ws + c.k_packed,
+                                       ws + c.v_packed, s));
+  if (st == STA_OK) st = mark(1);
+  if (st != STA_OK) return st;
+  st = hip_status(sta::launch_schedule_lists(g, win, offsets, ids, s));
+  if (st == STA_OK) st = mark(2);
+  if (st != STA_OK) return st;
+  st = hip_status(sta::launch_schedule_work(g, win, work, s));
+  if (st == STA_OK) st = mark(3);
+  if (st != STA_OK) return st;
+  sta::FwdArgs a;
+  a.q_tiled = ws + c.q_tiled;
+  a.k_packed = ws + c.k_packed;
+  a.v_packed = ws + c.v_packed;
+  a.o_tiled = ws + c.o_tiled;
+  a.lse_tiled = lse_tiled;
+  a.offsets = offsets;
+  a.ids = ids;
+  a.work = work;
+  a.scale_log2 = float(1.4426950408889634 / std::sqrt(double(g.D)));
+  st = hip_status(sta::launch_attention(g, a, s));
+  if (st == STA_OK) st = mark(4);
+  if (st != STA_OK) return st;
+  st = hip_status(sta::launch_unpack_out(g, ws + c.o_tiled, lse_tiled, out, lse, s));
+  if (st == STA_OK) st = mark(5);
+  return st;
+}
+
+}  // namespace
+
+extern "C" {
+
+sta_status sta_forward(const sta_dims* dims, const void* q, const void* k, const void* v,
+                       const int32_t* window_sizes, int32_t text_length, int32_t has_text,
+                       void* out, float* lse, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  return forward_impl(dims, q, k, v, window_sizes, text_length, has_text, out, lse, workspace,
+                      workspace_bytes, stream, nullptr);
+}
+
+sta_status sta_forward_timed(const sta_dims* dims, const void* q, const void* k, const void* v,
+                             const int32_t* window_sizes, int32_t text_length, int32_t has_text,
+                             void* out, float* lse, void* workspace, size_t workspace_bytes,
+                             void* stream, void* const* events) {
+  if (events == nullptr) return STA_ERR_NULL;
+  for (int i = 0; i < STA_TIMED_EVENTS; ++i)
+    if (events[i] == nullptr) return STA_ERR_NULL;
+  return forward_impl(dims, q, k, v, window_sizes, text_length, has_text, out, lse, workspace,
+                      workspace_bytes, stream, events);
+}
+
+}  // extern "C"

@@ -1,0 +1,270 @@
+// Fused STA attention kernel for gfx950 (CDNA4): bf16 MFMA, fp32 online softmax.
+//
+// What it computes (STA README, "Usage" and "Why is STA Fast?"): for every
+// query row, softmax(q k^T / sqrt(D)) v over the keys of whole key tiles in the
+// query tile's window, followed by the valid text keys. Because every
+// (query tile, key tile) block is fully on or fully off, video blocks need no
+// per-element mask; only the last text block is masked, and only when the text
+// length is not a multiple of 64.
+//
+// Work decomposition. One workgroup = one query unit: a 384-row query tile
+// (or the 256 text query slots of one head), 8 waves of 48 rows each (three
+// 16-row column groups), two waves per SIMD. Keys stream in 64-key blocks
+// (K and V, 16 KB each at D=128) straight from global memory into LDS with
+// LDS-DMA loads, double buffered, one barrier per block.
+//
+// Per block and wave, with v_mfma_f32_16x16x32_bf16:
+//   S^T = K Q^T   A = K fragment (LDS), B = Q^T fragment (registers, loaded
+//                 once per unit). Lane l then holds scores of query l%16 for
+//                 keys 4*(l/16) + r of each 16-key group.
+//   softmax       row max over the lane's 16 scores, then across the 4 lanes
+//                 that share the query (permlane16/32 swaps, no LDS). Scores
+//                 are scaled into the log2 domain with one FMA and raised with
+//                 v_exp_f32. The running max is only moved when a block's
+//                 max exceeds it by more than kRescaleSlack (log2 units); the
+//                 accumulator is rescaled only then. Any reference value
+//                 gives the same softmax; the slack bounds p by 2^slack.
+//   O^T += V^T P^T  A = V^T fragment (LDS, packed so its key order matches the
+//                 accumulator layout of S^T), B = P^T straight from the
+//                 lane's own registers after bf16 rounding.
+// Epilogue: O = O^T / l rounded to bf16, lse = (m + log2 l) * ln 2.
+#include "sta_internal.h"
+
+namespace sta {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * 64;
+constexpr int kRowsPerWave = kUnitRows / kWaves;  // 48
+constexpr int kQT = kRowsPerWave / 16;            // 3 query column groups per wave
+constexpr float kRescaleSlack = 8.0f;             // log2 units
+constexpr float kLn2 = 0.69314718055994530942f;
+
+__device__ inline float swap16_max(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float swap32_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float swap16_sum(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ inline float swap32_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(Geom g, FwdArgs a) {
+  constexpr int KS = D / 32;             // k-steps of S^T
+  constexpr int DT = D / 16;             // d groups of O^T
+  constexpr int BLK = kKeyBlock * D * 2; // bytes of one packed K (or V) block
+  constexpr int PER_WAVE = BLK / kWaves; // bytes each wave moves per tensor
+  static_assert(PER_WAVE % 1024 == 0, "LDS-DMA moves 1 KB per wave instruction");
+  __shared__ __attribute__((aligned(1024))) char lds[2][2][BLK];  // [stage][K|V]
+
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int unit = a.work[blockIdx.x];
+  const int u = unit % g.n_q;
+  const int bh = unit / g.n_q;
+  const int hd = bh % g.heads;
+  const bool text_unit = g.has_text && u == g.n_tiles;
+  const int q_row0 = text_unit ? g.n_video : u * kTileRows;
+  const int q_rows = text_unit ? kTextSlots : kTileRows;
+  const size_t slab = size_t(bh) * g.S * D;  // element offset of this (b, head)
+
+  const __bf16* __restrict__ qt = reinterpret_cast<const __bf16*>(a.q_tiled) + slab;
+  const char* __restrict__ kp = reinterpret_cast<const char*>(a.k_packed) + slab * 2;
+  const char* __restrict__ vp = reinterpret_cast<const char*>(a.v_packed) + slab * 2;
+
+  // Q^T fragments for this wave's 48 rows (rows past the unit are clamped to
+  // a valid row; their results are discarded).
+  bf16x8 qf[kQT][KS];
+#pragma unroll
+  for (int c = 0; c < kQT; ++c) {
+    int row = wave * kRowsPerWave + c * 16 + (lane & 15);
+    row = row < q_rows ? row : q_rows - 1;
+    const bf16x8* src = reinterpret_cast<const bf16x8*>(qt + size_t(q_row0 + row) * D + (lane >> 4) * 8);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qf[c][ks] = src[ks * 4];
+  }
+
+  const int l0 = a.offsets[hd * g.n_q + u];
+  const int l1 = a.offsets[hd * g.n_q + u + 1];
+  const int n_vid = (l1 - l0) * (kTileRows / kKeyBlock);
+  const int text_len = g.has_text ? g.text_length : 0;
+  const int n_blk = n_vid + (text_len + kKeyBlock - 1) / kKeyBlock;
+  const bool ragged_text = (text_len % kKeyBlock) != 0;
+
+  auto block_row = [&](int j) -> int {
+    if (j < n_vid) {
+      const int tile = a.ids[l0 + j / (kTileRows / kKeyBlock)];
+      return tile * kTileRows + (j % (kTileRows / kKeyBlock)) * kKeyBlock;
+    }
+    return g.n_video + (j - n_vid) * kKeyBlock;
+  };
+  auto issue = [&](int j, int stage) {
+    const size_t off = size_t(block_row(j)) * D * 2;
+    const char* ks = kp + off;
+    const char* vs = vp + off;
+#pragma unroll
+    for (int c = 0; c < PER_WAVE / 1024; ++c) {
+      const int o = wave * PER_WAVE + c * 1024;
+      __builtin_amdgcn_global_load_lds(ks + o + lane * 16, (lds_void*)&lds[stage][0][o], 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vs + o + lane * 16, (lds_void*)&lds[stage][1][o], 16, 0, 0);
+    }
+  };
+
+  f32x4 acc[kQT][DT];
+#pragma unroll
+  for (int c = 0; c < kQT; ++c)
+#pragma unroll
+    for (int d = 0; d < DT; ++d) acc[c][d] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run[kQT], l_part[kQT];
+#pragma unroll
+  for (int c = 0; c < kQT; ++c) {
+    m_run[c] = -INFINITY;
+    l_part[c] = 0.f;
+  }
+  const float sc = a.scale_log2;
+
+  issue(0, 0);
+  for (int j = 0; j < n_blk; ++j) {
+    const int stage = j & 1;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (j + 1 < n_blk) issue(j + 1, stage ^ 1);
+
+    // ---- S^T = K Q^T
+    const bf16x8* kl = reinterpret_cast<const bf16x8*>(lds[stage][0]);
+    f32x4 s[kQT][4];
+#pragma unroll
+    for (int c = 0; c < kQT; ++c)
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) s[c][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        const bf16x8 kf = kl[(kt * KS + ks) * 64 + lane];
+#pragma unroll
+        for (int c = 0; c < kQT; ++c)
+          s[c][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[c][ks], s[c][kt], 0, 0, 0);
+      }
+    }
+
+    // ---- mask the padded keys of the last, ragged text block
+    if (ragged_text && j == n_blk - 1) {
+      const int key0 = (j - n_vid) * kKeyBlock + 4 * (lane >> 4);
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (key0 + 16 * kt + r >= text_len)
+#pragma unroll
+            for (int c = 0; c < kQT; ++c) s[c][kt][r] = -INFINITY;
+    }
+
+    // ---- online softmax (log2 domain, lazy rescale)
+    float mb[kQT];
+    bool need = false;
+#pragma unroll
+    for (int c = 0; c < kQT; ++c) {
+      float x = fmaxf(fmaxf(s[c][0][0], s[c][0][1]), fmaxf(s[c][0][2], s[c][0][3]));
+#pragma unroll
+      for (int kt = 1; kt < 4; ++kt)
+        x = fmaxf(x, fmaxf(fmaxf(s[c][kt][0], s[c][kt][1]), fmaxf(s[c][kt][2], s[c][kt][3])));
+      x = swap16_max(x);
+      x = swap32_max(x);
+      mb[c] = x * sc;
+      need |= mb[c] > m_run[c] + kRescaleSlack;
+    }
+    if (__builtin_amdgcn_ballot_w64(need) != 0) {
+#pragma unroll
+      for (int c = 0; c < kQT; ++c) {
+        const float m_new = mb[c] > m_run[c] + kRescaleSlack ? mb[c] : m_run[c];
+        const float alpha = __builtin_amdgcn_exp2f(m_run[c] - m_new);
+        m_run[c] = m_new;
+        l_part[c] *= alpha;
+#pragma unroll
+        for (int d = 0; d < DT; ++d) acc[c][d] *= alpha;
+      }
+    }
+    bf16x8 pb[kQT][2];
+#pragma unroll
+    for (int c = 0; c < kQT; ++c) {
+      const float nm = -m_run[c];
+      float rs = 0.f;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        f32x8 p;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[c][2 * h][r], sc, nm));
+          p[4 + r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[c][2 * h + 1][r], sc, nm));
+        }
+#pragma unroll
+        for (int r = 0; r < 8; ++r) rs += p[r];
+        pb[c][h] = __builtin_convertvector(p, bf16x8);
+      }
+      l_part[c] += rs;
+    }
+
+    // ---- O^T += V^T P^T
+    const bf16x8* vl = reinterpret_cast<const bf16x8*>(lds[stage][1]);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int d = 0; d < DT; ++d) {
+        const bf16x8 vf = vl[(h * DT + d) * 64 + lane];
+#pragma unroll
+        for (int c = 0; c < kQT; ++c)
+          acc[c][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[c][h], acc[c][d], 0, 0, 0);
+      }
+    }
+  }
+
+  // ---- epilogue
+  __bf16* __restrict__ ot = reinterpret_cast<__bf16*>(a.o_tiled) + slab;
+  float* __restrict__ lt = a.lse_tiled + size_t(bh) * g.S;
+#pragma unroll
+  for (int c = 0; c < kQT; ++c) {
+    float l = swap16_sum(l_part[c]);
+    l = swap32_sum(l);
+    const float inv = __builtin_amdgcn_rcpf(l);
+    const int row = wave * kRowsPerWave + c * 16 + (lane & 15);
+    if (row < q_rows) {
+      __bf16* dst = ot + size_t(q_row0 + row) * D + (lane >> 4) * 4;
+#pragma unroll
+      for (int d = 0; d < DT; ++d) {
+        const f32x4 o = acc[c][d] * inv;
+        *reinterpret_cast<bf16x4*>(dst + d * 16) = __builtin_convertvector(o, bf16x4);
+      }
+      if (lane < 16) lt[q_row0 + row] = (m_run[c] + __builtin_amdgcn_logf(l)) * kLn2;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_attention(const Geom& g, const FwdArgs& a, hipStream_t stream) {
+  const int units = g.B * g.heads * g.n_q;
+  if (g.D == 128)
+    sta_attention_kernel<128><<<units, kThreads, 0, stream>>>(g, a);
+  else
+    sta_attention_kernel<64><<<units, kThreads, 0, stream>>>(g, a);
+  return hipGetLastError();
+}
+
+}  // namespace sta

@@ -1,0 +1,84 @@
+// Internal declarations shared by the STA host library and its HIP kernels.
+// Not part of the public ABI (include/sta.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sta {
+
+// Tile cube (6, 8, 8) tokens = 384 rows, from the STA README "Usage" section.
+constexpr int kTileT = 6;
+constexpr int kTileH = 8;
+constexpr int kTileW = 8;
+constexpr int kTileRows = kTileT * kTileH * kTileW;  // 384
+constexpr int kTextSlots = 256;
+// Key rows per packed block / per LDS stage of the attention kernel.
+constexpr int kKeyBlock = 64;
+// Query rows per attention workgroup: one whole tile.
+constexpr int kUnitRows = kTileRows;
+constexpr int kMaxHeads = 256;
+constexpr int kWinBits = 10;  // each packed window component uses 10 bits
+
+// Derived geometry, computed on the host and passed by value to kernels.
+struct Geom {
+  int32_t B, heads, D;
+  int32_t T, H, W;
+  int32_t nt, nh, nw;  // tile-grid size
+  int32_t n_tiles;     // nt * nh * nw
+  int32_t n_video;     // T * H * W
+  int32_t S;           // n_video + (has_text ? 256 : 0)
+  int32_t has_text;
+  int32_t text_length;
+  int32_t n_q;         // query units per head: n_tiles (+1 text unit)
+};
+
+// Per-head windows, packed as wt | wh << 10 | ww << 20 (kernel-argument copy).
+struct Windows {
+  uint32_t w[kMaxHeads];
+};
+
+__host__ __device__ inline int win_t(uint32_t p) { return int(p & 1023u); }
+__host__ __device__ inline int win_h(uint32_t p) { return int((p >> 10) & 1023u); }
+__host__ __device__ inline int win_w(uint32_t p) { return int((p >> 20) & 1023u); }
+
+// Tile-major row r (within one [S] slab) -> raster row. Text rows map to themselves.
+__host__ __device__ inline int tiled_to_raster(int r, const Geom& g) {
+  if (r >= g.n_video) return r;
+  const int tile = r / kTileRows;
+  const int j = r - tile * kTileRows;
+  const int dt = j >> 6, dh = (j >> 3) & 7, dw = j & 7;
+  const int tw = tile % g.nw;
+  const int rest = tile / g.nw;
+  const int th = rest % g.nh;
+  const int tt = rest / g.nh;
+  const int t = tt * kTileT + dt, h = th * kTileH + dh, w = tw * kTileW + dw;
+  return (t * g.H + h) * g.W + w;
+}
+
+// Launchers (each enqueues one kernel on `stream` and returns hipGetLastError()).
+hipError_t launch_rows_permute(const Geom& g, const void* src, void* dst, bool to_tiled,
+                               hipStream_t stream);
+hipError_t launch_pack_qkv(const Geom& g, const void* q, const void* k, const void* v,
+                           void* q_tiled, void* k_packed, void* v_packed, hipStream_t stream);
+hipError_t launch_unpack_out(const Geom& g, const void* o_tiled, const float* lse_tiled,
+                             void* out, float* lse, hipStream_t stream);
+hipError_t launch_schedule_lists(const Geom& g, const Windows& win, int32_t* offsets,
+                                 int32_t* ids, hipStream_t stream);
+hipError_t launch_schedule_work(const Geom& g, const Windows& win, int32_t* work,
+                                hipStream_t stream);
+
+struct FwdArgs {
+  const void* q_tiled;   // bf16 tile-major rows
+  const void* k_packed;  // bf16, 64-key blocks in MFMA A-operand fragment order
+  const void* v_packed;  // bf16, 64-key blocks, transposed fragment order
+  void* o_tiled;         // bf16 tile-major rows
+  float* lse_tiled;      // fp32 tile-major
+  const int32_t* offsets;
+  const int32_t* ids;
+  const int32_t* work;
+  float scale_log2;      // log2(e) / sqrt(D)
+};
+hipError_t launch_attention(const Geom& g, const FwdArgs& a, hipStream_t stream);
+
+}  // namespace sta

@@ -1,0 +1,172 @@
+/*
+ * sta.h - C ABI of the Sliding Tile Attention (STA) forward library (gfx950).
+ *
+ * The operation is the one described by the "Sliding Tile Atteniton Kernel"
+ * README (FastVideo, sta_kernel/thunderkitten), sections "Usage" and "Why is
+ * STA Fast?": softmax attention over a T x H x W video latent cut into tiles
+ * of (6, 8, 8) tokens, where each query tile attends to a per-head window of
+ * whole key tiles (given in tiles), plus an optional segment of 256 padded
+ * text slots of which the first `text_length` are valid. The attention map
+ * holds only fully-dense or fully-empty tile blocks.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Sequence order ("raster"): video token (t, h, w) is row (t*H + h)*W + w;
+ *   when has_text != 0 the 256 text slots follow as rows [T*H*W, T*H*W+256).
+ *   S = T*H*W + (has_text ? 256 : 0).
+ * - Tensors q, k, v, out are bf16, row-major [batch][heads][S][head_dim].
+ *   lse is fp32 [batch][heads][S].
+ * - Device pointers are HIP device (or managed) memory, 16-byte aligned.
+ *   The caller owns every buffer; the library allocates nothing, keeps no
+ *   state between calls and is safe to call concurrently on different
+ *   buffers.
+ * - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *   Work is enqueued asynchronously; the return value reports argument
+ *   errors (found on the host before anything is enqueued) and launch
+ *   errors. Faults inside kernels surface at the caller's next stream sync.
+ * - window_sizes is a HOST array of heads*3 int32: (w_t, w_h, w_w) in tiles
+ *   for head 0, then head 1, ... Each component must lie in [1, n_axis]
+ *   where (n_t, n_h, n_w) = (T/6, H/8, W/8). At the grid border the window
+ *   is shifted inward (start = clamp(c - w/2, 0, n - w) per axis) so every
+ *   video query sees exactly w_t*w_h*w_w tiles.
+ */
+#ifndef STA_H
+#define STA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  STA_OK = 0,
+  STA_ERR_NULL = 1,      /* a required pointer is NULL, or batch/heads <= 0      */
+  STA_ERR_SHAPE = 2,     /* T,H,W not positive multiples of (6,8,8); head_dim
+                            not 64 or 128; heads > STA_MAX_HEADS; a tile-grid
+                            axis > 1023 tiles; or sizes too large to index     */
+  STA_ERR_WINDOW = 3,    /* a window component outside [1, n_axis]              */
+  STA_ERR_TEXT = 4,      /* text_length outside [0, 256], or != 0 without text  */
+  STA_ERR_ALIGN = 5,     /* a device pointer is not 16-byte aligned             */
+  STA_ERR_WORKSPACE = 6, /* workspace NULL or smaller than sta_workspace_bytes  */
+  STA_ERR_HIP = 7,       /* the HIP runtime reported an error at launch         */
+  STA_ERR_ALIAS = 8      /* out (or lse) overlaps an input                      */
+} sta_status;
+
+#define STA_MAX_HEADS 256
+#define STA_TEXT_SLOTS 256
+
+typedef struct {
+  int32_t batch;    /* B >= 1                                  */
+  int32_t heads;    /* 1 .. STA_MAX_HEADS                      */
+  int32_t head_dim; /* D: 64 or 128                            */
+  int32_t T, H, W;  /* video size in tokens: multiples of 6, 8, 8 */
+} sta_dims;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* sta_status_str(sta_status s);
+
+/* Sequence length S for these dims (0 if dims are invalid). */
+int64_t sta_seq_len(const sta_dims* dims, int32_t has_text);
+
+/*
+ * Bytes of device workspace sta_forward needs for these arguments, or 0 if
+ * the arguments are invalid. Depends on the windows (the key-tile lists of
+ * the schedule are sized by them). Pure host arithmetic: no HIP call.
+ */
+size_t sta_workspace_bytes(const sta_dims* dims, const int32_t* window_sizes,
+                           int32_t has_text);
+
+/*
+ * STA forward: out = softmax(q k^T / sqrt(D), masked to the sliding tile
+ * window and the valid text keys) v, and lse = natural log of the softmax
+ * denominator, per query row.
+ *
+ * Which keys a query row sees (README "Usage": window in tiles, text length,
+ * Hunyuan-style text mode or StepVideo-style has_text = 0):
+ *   video query -> video keys of the w_t x w_h x w_w key tiles of its
+ *                  clamped window, and text keys [0, text_length);
+ *   text query (every one of the 256 slots, padded slots included)
+ *                -> all video keys and text keys [0, text_length).
+ * Text K/V rows at or after text_length never influence any result (their
+ * contents, even non-finite values, are ignored).
+ *
+ * q, k, v   : device, bf16 [B][heads][S][D], raster order, read only.
+ * out       : device, bf16 [B][heads][S][D], written; must not overlap inputs.
+ * lse       : device, fp32 [B][heads][S], written; may be NULL to skip it.
+ * workspace : device, >= sta_workspace_bytes(dims, window_sizes, has_text)
+ *             bytes, 256-byte aligned; contents on entry are ignored and on
+ *             return are unspecified. Calls that share a workspace must be
+ *             ordered on one stream.
+ * Returns STA_OK once the five launches (pack, schedule lists, work order,
+ * fused attention, scatter) are enqueued on `stream`.
+ */
+sta_status sta_forward(const sta_dims* dims, const void* q, const void* k,
+                       const void* v, const int32_t* window_sizes,
+                       int32_t text_length, int32_t has_text, void* out,
+                       float* lse, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
+/*
+ * sta_forward with stage timing, for measurement. `events` holds
+ * STA_TIMED_EVENTS hipEvent_t handles (as void*, created by the caller);
+ * events[0] is recorded on `stream` before the first launch and events[i]
+ * after launch i of: 1 pack q/k/v, 2 schedule lists, 3 work order,
+ * 4 fused attention, 5 scatter of out/lse. hipEventElapsedTime between
+ * consecutive events then gives each kernel's duration. Nothing else
+ * differs from sta_forward; STA_ERR_NULL if events or an entry is NULL.
+ */
+#define STA_TIMED_EVENTS 6
+sta_status sta_forward_timed(const sta_dims* dims, const void* q, const void* k,
+                             const void* v, const int32_t* window_sizes,
+                             int32_t text_length, int32_t has_text, void* out,
+                             float* lse, void* workspace, size_t workspace_bytes,
+                             void* stream, void* const* events);
+
+/*
+ * Tile-major gather of one bf16 tensor [B][heads][S][D]: every video row
+ * (t, h, w) moves to row  tile*384 + ((t%6)*8 + h%8)*8 + w%8  with
+ * tile = ((t/6)*n_h + h/8)*n_w + w/8, so each tile is 384 contiguous rows;
+ * text rows keep their positions. x_raster and x_tiled are device buffers
+ * of the same size and must not overlap.
+ */
+sta_status sta_tile_gather(const sta_dims* dims, int32_t has_text,
+                           const void* x_raster, void* x_tiled, void* stream);
+
+/* Inverse of sta_tile_gather. */
+sta_status sta_tile_scatter(const sta_dims* dims, int32_t has_text,
+                            const void* x_tiled, void* x_raster, void* stream);
+
+/*
+ * Sizes (in int32 elements) of the three schedule arrays for these
+ * arguments: offsets (heads*n_q + 1), key-tile ids and the work order
+ * (B*heads*n_q), where n_q = n_t*n_h*n_w query tiles plus one text query
+ * unit when has_text. Returns STA_OK or an argument error. Host only.
+ */
+sta_status sta_schedule_sizes(const sta_dims* dims, const int32_t* window_sizes,
+                              int32_t has_text, int64_t* n_offsets,
+                              int64_t* n_ids, int64_t* n_work);
+
+/*
+ * Build the tile-window schedule on the device.
+ *   offsets[hd*n_q + u] .. offsets[hd*n_q + u + 1] delimit, in ids, the key
+ *   tiles that query unit u of head hd sees: for a video query tile, the
+ *   tiles of its clamped window in t-h-w nested order (w fastest); for the
+ *   text unit (u = n_tiles), every tile 0 .. n_tiles-1.
+ *   work[i] is the query unit ((b*heads + hd)*n_q + u) that workgroup i of
+ *   the attention launch processes: heaviest units first, and within each
+ *   run of 256 workgroups, the ones that land on one XCD get consecutive
+ *   units.
+ * All three arrays are device int32 of the sizes sta_schedule_sizes gives.
+ */
+sta_status sta_build_schedule(const sta_dims* dims, const int32_t* window_sizes,
+                              int32_t text_length, int32_t has_text,
+                              int32_t* offsets, int32_t* ids, int32_t* work,
+                              void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* STA_H */

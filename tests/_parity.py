@@ -1,0 +1,74 @@
+"""Shared helpers for the GPU tests: run the HIP path, run the oracle on the
+same inputs, and compare at the stated tolerances.
+
+Tolerances (bf16 inputs, fp32 accumulation, bf16 output):
+  out: max |gpu - oracle| <= 2e-2 and mean |gpu - oracle| <= 2e-3
+  lse: max |gpu - oracle| / |oracle| <= 1e-3
+"""
+
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import block_sparse_sliding_amd as sta
+import oracle
+
+OUT_MAX_ABS = 2e-2
+OUT_MEAN_ABS = 2e-3
+LSE_REL = 1e-3
+
+
+def note(msg: str) -> None:
+    """Name the case on stdout before a GPU step (survives a lost box)."""
+    print(f"[gpu-case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def run_sta(q, k, v, windows, text_length, has_text, video, workspace=None):
+    out, lse = sta.sliding_tile_attention(q, k, v, windows, text_length, has_text, video,
+                                          return_lse=True, workspace=workspace)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def oracle_rows(q, k, v, windows, text_length, has_text, video, rows=None):
+    """Oracle output for all (b, head) slabs, optionally on a subset of rows.
+
+    Runs head by head on host copies so the float64 working set stays small.
+    """
+    B, heads, S, D = q.shape
+    R = S if rows is None else len(rows)
+    out = np.empty((B, heads, R, D))
+    lse = np.empty((B, heads, R))
+    for h in range(heads):
+        qh = q[:, h:h + 1].cpu()
+        kh = k[:, h:h + 1].cpu()
+        vh = v[:, h:h + 1].cpu()
+        o, l = oracle.sta_reference(qh, kh, vh, [windows[h]], text_length, has_text, video,
+                                    rows=rows)
+        out[:, h] = o[:, 0]
+        lse[:, h] = l[:, 0]
+    return out, lse
+
+
+def compare(out_gpu, lse_gpu, out_ref, lse_ref, rows=None, label=""):
+    """Assert parity; returns the error summary."""
+    o = out_gpu if rows is None else out_gpu[:, :, rows]
+    l = lse_gpu if rows is None else lse_gpu[:, :, rows]
+    o = o.float().cpu().numpy().astype(np.float64)
+    l = l.float().cpu().numpy().astype(np.float64)
+    assert np.isfinite(o).all(), f"{label}: non-finite output"
+    assert np.isfinite(l).all(), f"{label}: non-finite lse"
+    err = np.abs(o - out_ref)
+    lrel = np.abs(l - lse_ref) / np.abs(lse_ref)
+    summary = dict(max_abs=float(err.max()), mean_abs=float(err.mean()),
+                   lse_rel=float(lrel.max()),
+                   rel_rms=float(np.sqrt((err ** 2).mean() / (out_ref ** 2).mean())))
+    print(f"[parity] {label} {summary}", flush=True)
+    assert summary["max_abs"] <= OUT_MAX_ABS, (label, summary)
+    assert summary["mean_abs"] <= OUT_MEAN_ABS, (label, summary)
+    assert summary["lse_rel"] <= LSE_REL, (label, summary)
+    return summary

@@ -1,0 +1,151 @@
+"""GPU checks of properties that hold at any size (through the C ABI).
+
+* q = 0 closed form: every allowed score is 0, so lse = ln(count) and the
+  output is the mean of the allowed v rows; with v carrying each key's tile
+  coordinates this pins the window placement on every row, at full size.
+* padded text K/V rows never reach the result (bitwise).
+* repeated calls are bitwise identical; batch entries are independent.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import sta_inputs
+from _parity import note, run_sta
+
+pytestmark = pytest.mark.gpu
+
+TILE = (6, 8, 8)
+
+
+def nearest_box_start(c, w, n):
+    """Placement of w tiles inside [0, n) whose centre is nearest to c (ties: lower)."""
+    c = np.asarray(c)
+    best_d = np.full(c.shape, np.inf)
+    best_s = np.zeros(c.shape, dtype=np.int64)
+    for s in range(0, n - w + 1):
+        d = np.abs(s + (w - 1) / 2.0 - c)
+        better = d < best_d
+        best_d = np.where(better, d, best_d)
+        best_s = np.where(better, s, best_s)
+    return best_s
+
+
+def coord_inputs(B, heads, D, video, has_text, seed=0):
+    T, H, W = video
+    nv = T * H * W
+    S = nv + (256 if has_text else 0)
+    q = torch.zeros(B, heads, S, D, dtype=torch.bfloat16, device="cuda")
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    k = torch.randn(B, heads, S, D, generator=g, device="cuda").to(torch.bfloat16)
+    v = torch.zeros(B, heads, S, D, dtype=torch.bfloat16, device="cuda")
+    t = torch.arange(T, device="cuda").repeat_interleave(H * W)
+    h = torch.arange(H, device="cuda").repeat_interleave(W).repeat(T)
+    w = torch.arange(W, device="cuda").repeat(T * H)
+    v[:, :, :nv, 0] = (t // 6).to(torch.bfloat16)
+    v[:, :, :nv, 1] = (h // 8).to(torch.bfloat16)
+    v[:, :, :nv, 2] = (w // 8).to(torch.bfloat16)
+    if has_text:
+        v[:, :, nv:, 3] = 1
+    return q, k, v
+
+
+def expected_uniform(video, window, ell, has_text):
+    """Closed-form output columns 0..3 and lse for q = 0, every row."""
+    T, H, W = video
+    nv = T * H * W
+    n = [video[a] // TILE[a] for a in range(3)]
+    t = np.arange(T).repeat(H * W)
+    h = np.tile(np.arange(H).repeat(W), T)
+    w = np.tile(np.arange(W), T * H)
+    nwin = window[0] * window[1] * window[2] * 384
+    cnt = nwin + ell
+    cols = []
+    for a, x in enumerate((t, h, w)):
+        tiles = x // TILE[a]
+        lo = {c: int(nearest_box_start(c, window[a], n[a])) for c in range(n[a])}
+        start = np.vectorize(lo.get)(tiles)
+        cols.append((start + (window[a] - 1) / 2.0) * nwin / cnt)
+    vid = np.stack(cols + [np.full(nv, ell / cnt)], axis=1)
+    lse = np.full(nv, math.log(cnt))
+    if has_text:
+        ctext = nv + ell
+        txt = np.array([(n[a] - 1) / 2.0 * nv / ctext for a in range(3)] + [ell / ctext])
+        vid = np.concatenate([vid, np.tile(txt, (256, 1))])
+        lse = np.concatenate([lse, np.full(256, math.log(ctext))])
+    return vid, lse
+
+
+@pytest.mark.parametrize("video,windows,ell,has_text,D", [
+    ((18, 24, 32), [(3, 3, 3), (1, 2, 3), (2, 1, 4)], 77, True, 128),
+    ((30, 48, 80), [(3, 3, 3), (3, 3, 5)], 226, True, 128),
+    ((30, 48, 80), [(5, 6, 10), (3, 3, 3), (1, 6, 10), (5, 1, 1)], 256, True, 128),
+    ((30, 48, 80), [(3, 3, 3)], 0, False, 128),
+    ((48, 72, 128), [(3, 3, 3)], 128, True, 128),
+    ((18, 24, 24), [(1, 3, 3)], 0, False, 64),
+])
+def test_uniform_attention_closed_form(video, windows, ell, has_text, D):
+    heads = len(windows)
+    note(f"q=0 closed form {video} {windows} ell={ell} text={has_text} D={D}")
+    q, k, v = coord_inputs(1, heads, D, video, has_text)
+    out, lse = run_sta(q, k, v, windows, ell, has_text, video)
+    for hd, win in enumerate(windows):
+        exp_out, exp_lse = expected_uniform(video, win, ell, has_text)
+        got = out[0, hd, :, :4].float().cpu().numpy()
+        gl = lse[0, hd].cpu().numpy().astype(np.float64)
+        # bf16 rounding of the output: half an ulp, 2^-9 relative
+        assert np.all(np.abs(got - exp_out) <= np.abs(exp_out) * 2.0 ** -8 + 1e-6), (hd, win)
+        assert np.all(out[0, hd, :, 4:].float().cpu().numpy() == 0.0)
+        np.testing.assert_allclose(gl, exp_lse, rtol=2e-6)
+    del q, k, v, out, lse
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("ell", [0, 1, 100, 226, 255])
+def test_text_padding_never_reaches_output(ell):
+    video = (18, 24, 32)
+    windows = [(3, 3, 3), (1, 2, 3)]
+    nv = video[0] * video[1] * video[2]
+    S = nv + 256
+    note(f"text padding isolation ell={ell}")
+    g = torch.Generator(device="cuda").manual_seed(ell)
+    q, k, v = [torch.randn(1, 2, S, 128, generator=g, device="cuda").to(torch.bfloat16)
+               for _ in range(3)]
+    out1, lse1 = run_sta(q, k, v, windows, ell, True, video)
+    k2, v2 = k.clone(), v.clone()
+    k2[:, :, nv + ell:] = 100.0
+    v2[:, :, nv + ell:] = float("nan")
+    v2[:, :, nv + ell::2] = float("inf")
+    out2, lse2 = run_sta(q, k2, v2, windows, ell, True, video)
+    assert torch.equal(out1.view(torch.int16), out2.view(torch.int16))
+    assert torch.equal(lse1.view(torch.int32), lse2.view(torch.int32))
+
+
+def test_deterministic_and_batch_independent():
+    wl = sta_inputs.WORKLOADS["headline"]
+    video = wl.video
+    heads = 4
+    nv = video[0] * video[1] * video[2]
+    S = nv + 256
+    note("determinism / batch independence at (30,48,80)+256, 4 heads")
+    g = torch.Generator(device="cuda").manual_seed(9)
+    q, k, v = [torch.randn(1, heads, S, 128, generator=g, device="cuda").to(torch.bfloat16)
+               for _ in range(3)]
+    windows = [(3, 3, 3), (5, 6, 10), (1, 6, 10), (5, 1, 1)]
+    out1, lse1 = run_sta(q, k, v, windows, 226, True, video)
+    out2, lse2 = run_sta(q, k, v, windows, 226, True, video)
+    assert torch.equal(out1.view(torch.int16), out2.view(torch.int16))
+    assert torch.equal(lse1.view(torch.int32), lse2.view(torch.int32))
+    g2 = torch.Generator(device="cuda").manual_seed(10)
+    y = [torch.randn(1, heads, S, 128, generator=g2, device="cuda").to(torch.bfloat16)
+         for _ in range(3)]
+    outy, lsey = run_sta(*y, windows, 226, True, video)
+    qb, kb, vb = (torch.cat([a, b], 0).contiguous() for a, b in zip((q, k, v), y))
+    outb, lseb = run_sta(qb, kb, vb, windows, 226, True, video)
+    assert torch.equal(outb[0].view(torch.int16), out1[0].view(torch.int16))
+    assert torch.equal(lseb[0].view(torch.int32), lse1[0].view(torch.int32))
+    assert torch.equal(outb[1].view(torch.int16), outy[0].view(torch.int16))
+    assert torch.equal(lseb[1].view(torch.int32), lsey[0].view(torch.int32))
