@@ -117,6 +117,9 @@ def main():
     ap.add_argument("--workload", default="headline")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for the CPU baseline (0 to skip)")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="after timing, run a plain device copy of this many MiB (3 times) so "
+                         "that hardware byte counters can be scaled against known traffic")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
@@ -203,6 +206,15 @@ def main():
             "launch_ms": attn_ms,
         },
     }
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        result["copy_calibration_bytes"] = n
+        del src, dst
     if args.cpu_budget > 0:
         result["cpu_baseline"] = cpu_baseline(wl, q, k, v, args.cpu_budget, flops)
     print(json.dumps(result), flush=True)
