@@ -14,19 +14,24 @@
 // LDS-DMA loads, double buffered, one barrier per block.
 //
 // Per block and wave, with v_mfma_f32_16x16x32_bf16:
-//   S^T = K Q^T   A = K fragment (LDS), B = Q^T fragment (registers, loaded
-//                 once per unit). Lane l then holds scores of query l%16 for
-//                 keys 4*(l/16) + r of each 16-key group.
-//   softmax       row max over the lane's 16 scores, then across the 4 lanes
-//                 that share the query (permlane16/32 swaps, no LDS). Scores
-//                 are scaled into the log2 domain with one FMA and raised with
-//                 v_exp_f32. The running max is only moved when a block's
-//                 max exceeds it by more than kRescaleSlack (log2 units); the
-//                 accumulator is rescaled only then. Any reference value
-//                 gives the same softmax; the slack bounds p by 2^slack.
+//   S^T - m = K (Q c)^T - m
+//                 A = K fragment (LDS), B = Q^T fragment (registers, loaded
+//                 once per unit and pre-scaled by c = log2(e)/sqrt(D)), and
+//                 the accumulator seeded with -m, the running reference max.
+//                 Lane l then holds s - m of query l%16 for keys 4*(l/16) + r
+//                 of each 16-key group, already in the log2 domain.
+//   softmax       p = 2^(s - m) straight from the MFMA output (one v_exp_f32
+//                 per score). The reference only moves when some score
+//                 exceeds it by more than kRescaleSlack (a per-lane v_max3
+//                 check and a ballot); then the accumulator is rescaled and
+//                 the block's scores are recomputed from the new seed. The
+//                 first block always sets the reference from its exact row
+//                 max. Any reference gives the same softmax; the slack
+//                 bounds p by 2^slack.
 //   O^T += V^T P^T  A = V^T fragment (LDS, packed so its key order matches the
-//                 accumulator layout of S^T), B = P^T straight from the
-//                 lane's own registers after bf16 rounding.
+//                 accumulator layout of S^T), B = P^T from the lane's own
+//                 registers after bf16 rounding. The row sums accumulate the
+//                 same rounded p with v_dot2_f32_bf16.
 // Epilogue: O = O^T / l rounded to bf16, lse = (m + log2 l) * ln 2.
 #include "sta_internal.h"
 
@@ -37,6 +42,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -64,16 +70,22 @@ __device__ inline float swap32_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// LDS-DMA: each lane moves 16 bytes from its own global address into
+// `lds + lane * 16` (the LDS base is wave-uniform).
+__device__ inline void dma16(const char* gsrc, char* lds_dst) {
+  __builtin_amdgcn_global_load_lds(gsrc, (lds_void*)lds_dst, 16, 0, 0);
+}
+
 template <int D>
 __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(Geom g, FwdArgs a) {
-  constexpr int KS = D / 32;             // k-steps of S^T
-  constexpr int DT = D / 16;             // d groups of O^T
-  constexpr int BLK = kKeyBlock * D * 2; // bytes of one packed K (or V) block
-  constexpr int PER_WAVE = BLK / kWaves; // bytes each wave moves per tensor
+  constexpr int KS = D / 32;              // k-steps of S^T
+  constexpr int DT = D / 16;              // d groups of O^T
+  constexpr int BLK = kKeyBlock * D * 2;  // bytes of one packed K (or V) block
+  constexpr int PER_WAVE = BLK / kWaves;  // bytes each wave moves per tensor
   static_assert(PER_WAVE % 1024 == 0, "LDS-DMA moves 1 KB per wave instruction");
   __shared__ __attribute__((aligned(1024))) char lds[2][2][BLK];  // [stage][K|V]
 
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int unit = a.work[blockIdx.x];
   const int u = unit % g.n_q;
@@ -88,18 +100,6 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(Geom g, FwdA
   const char* __restrict__ kp = reinterpret_cast<const char*>(a.k_packed) + slab * 2;
   const char* __restrict__ vp = reinterpret_cast<const char*>(a.v_packed) + slab * 2;
 
-  // Q^T fragments for this wave's 48 rows (rows past the unit are clamped to
-  // a valid row; their results are discarded).
-  bf16x8 qf[kQT][KS];
-#pragma unroll
-  for (int c = 0; c < kQT; ++c) {
-    int row = wave * kRowsPerWave + c * 16 + (lane & 15);
-    row = row < q_rows ? row : q_rows - 1;
-    const bf16x8* src = reinterpret_cast<const bf16x8*>(qt + size_t(q_row0 + row) * D + (lane >> 4) * 8);
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qf[c][ks] = src[ks * 4];
-  }
-
   const int l0 = a.offsets[hd * g.n_q + u];
   const int l1 = a.offsets[hd * g.n_q + u + 1];
   const int n_vid = (l1 - l0) * (kTileRows / kKeyBlock);
@@ -107,37 +107,53 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(Geom g, FwdA
   const int n_blk = n_vid + (text_len + kKeyBlock - 1) / kKeyBlock;
   const bool ragged_text = (text_len % kKeyBlock) != 0;
 
-  auto block_row = [&](int j) -> int {
+  auto issue = [&](int j, int stage) {
+    int row;
     if (j < n_vid) {
       const int tile = a.ids[l0 + j / (kTileRows / kKeyBlock)];
-      return tile * kTileRows + (j % (kTileRows / kKeyBlock)) * kKeyBlock;
+      row = tile * kTileRows + (j % (kTileRows / kKeyBlock)) * kKeyBlock;
+    } else {
+      row = g.n_video + (j - n_vid) * kKeyBlock;
     }
-    return g.n_video + (j - n_vid) * kKeyBlock;
-  };
-  auto issue = [&](int j, int stage) {
-    const size_t off = size_t(block_row(j)) * D * 2;
-    const char* ks = kp + off;
-    const char* vs = vp + off;
+    const size_t off = size_t(row) * D * 2;
 #pragma unroll
     for (int c = 0; c < PER_WAVE / 1024; ++c) {
       const int o = wave * PER_WAVE + c * 1024;
-      __builtin_amdgcn_global_load_lds(ks + o + lane * 16, (lds_void*)&lds[stage][0][o], 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(vs + o + lane * 16, (lds_void*)&lds[stage][1][o], 16, 0, 0);
+      dma16(kp + off + o + lane * 16, &lds[stage][0][o]);
+      dma16(vp + off + o + lane * 16, &lds[stage][1][o]);
     }
   };
 
-  f32x4 acc[kQT][DT];
-#pragma unroll
-  for (int c = 0; c < kQT; ++c)
-#pragma unroll
-    for (int d = 0; d < DT; ++d) acc[c][d] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run[kQT], l_part[kQT];
+  // Q^T fragments for this wave's 48 rows, pre-scaled by log2(e)/sqrt(D) so
+  // the MFMA yields scores in the log2 domain (rows past the unit are clamped
+  // to a valid row; their results are discarded).
+  const float sc = a.scale_log2;
+  bf16x8 qf[kQT][KS];
 #pragma unroll
   for (int c = 0; c < kQT; ++c) {
-    m_run[c] = -INFINITY;
-    l_part[c] = 0.f;
+    int row = wave * kRowsPerWave + c * 16 + (lane & 15);
+    row = row < q_rows ? row : q_rows - 1;
+    const bf16x8* src = reinterpret_cast<const bf16x8*>(qt + size_t(q_row0 + row) * D + (lane >> 4) * 8);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      f32x8 x = __builtin_convertvector(src[ks * 4], f32x8);
+      qf[c][ks] = __builtin_convertvector(x * sc, bf16x8);
+    }
   }
-  const float sc = a.scale_log2;
+
+  f32x4 acc[kQT][DT];
+  float l_part[kQT];  // this lane's share of the row sum of p
+  float m_run[kQT];   // reference max (log2 units); -m seeds the S^T accumulator
+#pragma unroll
+  for (int c = 0; c < kQT; ++c) {
+#pragma unroll
+    for (int d = 0; d < DT; ++d) acc[c][d] = f32x4{0.f, 0.f, 0.f, 0.f};
+    l_part[c] = 0.f;
+    m_run[c] = 0.f;
+  }
+  bf16x2 ones2;
+  ones2[0] = (__bf16)1.0f;
+  ones2[1] = (__bf16)1.0f;
 
   issue(0, 0);
   for (int j = 0; j < n_blk; ++j) {
@@ -146,91 +162,102 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(Geom g, FwdA
     __syncthreads();
     if (j + 1 < n_blk) issue(j + 1, stage ^ 1);
 
-    // ---- S^T = K Q^T
+    // ---- S^T - m = K (Q*scale)^T - m: the running max enters as the accumulator
+    // seed. When the reference must move (always on the first block, rarely
+    // later: some score exceeds it by more than the slack), the reference is
+    // updated and the block's scores are recomputed from the new seed, so the
+    // score registers are only ever written by the MFMAs.
     const bf16x8* kl = reinterpret_cast<const bf16x8*>(lds[stage][0]);
     f32x4 s[kQT][4];
+    for (int pass = 0;; ++pass) {
+      f32x4 seed[kQT];
 #pragma unroll
-    for (int c = 0; c < kQT; ++c)
+      for (int c = 0; c < kQT; ++c) seed[c] = f32x4{-m_run[c], -m_run[c], -m_run[c], -m_run[c]};
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) s[c][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
+        for (int kt = 0; kt < 4; ++kt) {
+          const bf16x8 kf = kl[(kt * KS + ks) * 64 + lane];
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        const bf16x8 kf = kl[(kt * KS + ks) * 64 + lane];
-#pragma unroll
-        for (int c = 0; c < kQT; ++c)
-          s[c][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[c][ks], s[c][kt], 0, 0, 0);
+          for (int c = 0; c < kQT; ++c)
+            s[c][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[c][ks],
+                                                                ks == 0 ? seed[c] : s[c][kt], 0, 0, 0);
+        }
       }
-    }
-
-    // ---- mask the padded keys of the last, ragged text block
-    if (ragged_text && j == n_blk - 1) {
-      const int key0 = (j - n_vid) * kKeyBlock + 4 * (lane >> 4);
+      // mask the padded keys of the last, ragged text block
+      if (ragged_text && j == n_blk - 1) {
+        const int key0 = (j - n_vid) * kKeyBlock + 4 * (lane >> 4);
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
+        for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (key0 + 16 * kt + r >= text_len)
+          for (int r = 0; r < 4; ++r)
+            if (key0 + 16 * kt + r >= text_len)
 #pragma unroll
-            for (int c = 0; c < kQT; ++c) s[c][kt][r] = -INFINITY;
-    }
-
-    // ---- online softmax (log2 domain, lazy rescale)
-    float mb[kQT];
-    bool need = false;
-#pragma unroll
-    for (int c = 0; c < kQT; ++c) {
-      float x = fmaxf(fmaxf(s[c][0][0], s[c][0][1]), fmaxf(s[c][0][2], s[c][0][3]));
-#pragma unroll
-      for (int kt = 1; kt < 4; ++kt)
-        x = fmaxf(x, fmaxf(fmaxf(s[c][kt][0], s[c][kt][1]), fmaxf(s[c][kt][2], s[c][kt][3])));
-      x = swap16_max(x);
-      x = swap32_max(x);
-      mb[c] = x * sc;
-      need |= mb[c] > m_run[c] + kRescaleSlack;
-    }
-    if (__builtin_amdgcn_ballot_w64(need) != 0) {
+              for (int c = 0; c < kQT; ++c) s[c][kt][r] = -INFINITY;
+      }
+      if (pass == 1) break;  // a recomputed block never moves the reference again
+      // per-lane max of s - m; the reference moves only past the slack
+      float lm[kQT];
+      bool need = false;
 #pragma unroll
       for (int c = 0; c < kQT; ++c) {
-        const float m_new = mb[c] > m_run[c] + kRescaleSlack ? mb[c] : m_run[c];
-        const float alpha = __builtin_amdgcn_exp2f(m_run[c] - m_new);
-        m_run[c] = m_new;
-        l_part[c] *= alpha;
-#pragma unroll
-        for (int d = 0; d < DT; ++d) acc[c][d] *= alpha;
+        float x = fmaxf(fmaxf(s[c][0][0], s[c][0][1]), s[c][0][2]);
+        x = fmaxf(fmaxf(x, s[c][0][3]), s[c][1][0]);
+        x = fmaxf(fmaxf(x, s[c][1][1]), s[c][1][2]);
+        x = fmaxf(fmaxf(x, s[c][1][3]), s[c][2][0]);
+        x = fmaxf(fmaxf(x, s[c][2][1]), s[c][2][2]);
+        x = fmaxf(fmaxf(x, s[c][2][3]), s[c][3][0]);
+        x = fmaxf(fmaxf(x, s[c][3][1]), s[c][3][2]);
+        x = fmaxf(x, s[c][3][3]);
+        lm[c] = x;
+        need |= x > kRescaleSlack;
       }
-    }
-    bf16x8 pb[kQT][2];
+      const bool first = j == 0;
+      if (!first && __builtin_amdgcn_ballot_w64(need) == 0) break;
 #pragma unroll
-    for (int c = 0; c < kQT; ++c) {
-      const float nm = -m_run[c];
-      float rs = 0.f;
+      for (int c = 0; c < kQT; ++c) {
+        // exact row max across the 4 lanes holding this query
+        const float mx = swap32_max(swap16_max(lm[c]));
+        if (first) {
+          m_run[c] = mx;  // nothing accumulated yet
+        } else {
+          const float delta = mx > 0.f ? mx : 0.f;
+          const float alpha = __builtin_amdgcn_exp2f(-delta);
+          m_run[c] += delta;
+          l_part[c] *= alpha;
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        f32x8 p;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[c][2 * h][r], sc, nm));
-          p[4 + r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[c][2 * h + 1][r], sc, nm));
+          for (int d = 0; d < DT; ++d) acc[c][d] *= alpha;
         }
-#pragma unroll
-        for (int r = 0; r < 8; ++r) rs += p[r];
-        pb[c][h] = __builtin_convertvector(p, bf16x8);
       }
-      l_part[c] += rs;
     }
 
-    // ---- O^T += V^T P^T
+    // ---- p = 2^(s - m) rounded to bf16; O^T += V^T P^T; row sums += 1^T P^T
     const bf16x8* vl = reinterpret_cast<const bf16x8*>(lds[stage][1]);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
+      bf16x8 pb[kQT];
+#pragma unroll
+      for (int c = 0; c < kQT; ++c) {
+        f32x8 p;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          p[r] = __builtin_amdgcn_exp2f(s[c][2 * h][r]);
+          p[4 + r] = __builtin_amdgcn_exp2f(s[c][2 * h + 1][r]);
+        }
+        pb[c] = __builtin_convertvector(p, bf16x8);
+        // row sum of the rounded p, two at a time
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const bf16x2 pair = {pb[c][2 * i], pb[c][2 * i + 1]};
+          l_part[c] = __builtin_amdgcn_fdot2_f32_bf16(pair, ones2, l_part[c], false);
+        }
+      }
 #pragma unroll
       for (int d = 0; d < DT; ++d) {
         const bf16x8 vf = vl[(h * DT + d) * 64 + lane];
 #pragma unroll
         for (int c = 0; c < kQT; ++c)
-          acc[c][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[c][h], acc[c][d], 0, 0, 0);
+          acc[c][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[c], acc[c][d], 0, 0, 0);
       }
     }
   }
@@ -240,8 +267,7 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(Geom g, FwdA
   float* __restrict__ lt = a.lse_tiled + size_t(bh) * g.S;
 #pragma unroll
   for (int c = 0; c < kQT; ++c) {
-    float l = swap16_sum(l_part[c]);
-    l = swap32_sum(l);
+    const float l = swap32_sum(swap16_sum(l_part[c]));
     const float inv = __builtin_amdgcn_rcpf(l);
     const int row = wave * kRowsPerWave + c * 16 + (lane & 15);
     if (row < q_rows) {
