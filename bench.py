@@ -1,9 +1,10 @@
 #!/usr/bin/env python3
 """Benchmark of the STA forward (one GPU).
 
-One step = one sta_forward call (pack q/k/v to tile-major order, schedule,
-fused attention, scatter back) on the workload's synthetic bf16 inputs, which
-are resident in HBM before timing starts. Prints one JSON line with the
+One step = one sta_forward call (pack k/v to tile-major MFMA order, build
+the tile-window schedule and work order, fused attention reading q and
+writing out/lse in raster order) on the workload's synthetic bf16 inputs,
+which are resident in HBM before timing starts. Prints one JSON line with the
 end-to-end effective TFLOP/s, the roofline of the fused attention kernel
 (timed live with HIP events on the launch stream) and the fp64 CPU oracle's
 throughput on a bounded sample of the same workload.

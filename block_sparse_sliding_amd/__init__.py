@@ -143,14 +143,14 @@ def sta_forward(dims: sta_dims, q, k, v, window_sizes, text_length: int, has_tex
     _check(code, "sta_forward")
 
 
-TIMED_EVENTS = 6
-STAGES = ("pack", "schedule_lists", "schedule_work", "attention", "scatter")
+TIMED_EVENTS = 5
+STAGES = ("pack", "schedule_lists", "schedule_work", "attention")
 
 
 def sta_forward_timed(dims: sta_dims, q, k, v, window_sizes, text_length: int, has_text: bool,
                       out, lse, workspace, events, stream=None) -> None:
-    """sta_forward that records ``events`` (6 torch.cuda.Event, timing enabled)
-    before the first launch and after each of the 5 launches on the stream."""
+    """sta_forward that records ``events`` (5 torch.cuda.Event, timing enabled)
+    before the first launch and after each of the 4 launches on the stream."""
     if len(events) != TIMED_EVENTS:
         raise ValueError(f"need {TIMED_EVENTS} events")
     handles = (ctypes.c_void_p * TIMED_EVENTS)(*[e.cuda_event for e in events])

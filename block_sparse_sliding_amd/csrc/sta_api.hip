@@ -73,18 +73,15 @@ sta_status make_windows(const Geom& g, const int32_t* ws, Windows* win, int64_t*
 }
 
 struct Carve {
-  size_t q_tiled, k_packed, v_packed, o_tiled, lse_tiled, offsets, ids, work, total;
+  size_t k_packed, v_packed, offsets, ids, work, total;
 };
 
 Carve carve(const Geom& g, int64_t n_ids) {
   Carve c{};
   const size_t tensor = size_t(g.B) * g.heads * g.S * g.D * 2;
   size_t at = 0;
-  c.q_tiled = at; at = align_up(at + tensor);
   c.k_packed = at; at = align_up(at + tensor);
   c.v_packed = at; at = align_up(at + tensor);
-  c.o_tiled = at; at = align_up(at + tensor);
-  c.lse_tiled = at; at = align_up(at + size_t(g.B) * g.heads * g.S * 4);
   c.offsets = at; at = align_up(at + (size_t(g.heads) * g.n_q + 1) * 4);
   c.ids = at; at = align_up(at + size_t(n_ids) * 4);
   c.work = at; at = align_up(at + size_t(g.B) * g.heads * g.n_q * 4);
@@ -237,10 +234,9 @@ sta_status forward_impl(const sta_dims* dims, const void* q, const void* k, cons
   int32_t* offsets = reinterpret_cast<int32_t*>(ws + c.offsets);
   int32_t* ids = reinterpret_cast<int32_t*>(ws + c.ids);
   int32_t* work = reinterpret_cast<int32_t*>(ws + c.work);
-  float* lse_tiled = reinterpret_cast<float*>(ws + c.lse_tiled);
 
-  st = hip_status(sta::launch_pack_qkv(g, q, k, v, ws + c.q_tiled, ws + c.k_packed,
-                                       ws + c.v_packed, s));
+  const float k_scale = float(1.4426950408889634 / std::sqrt(double(g.D)));  // log2(e)/sqrt(D)
+  st = hip_status(sta::launch_pack_kv(g, k, v, ws + c.k_packed, ws + c.v_packed, k_scale, s));
   if (st == STA_OK) st = mark(1);
   if (st != STA_OK) return st;
   st = hip_status(sta::launch_schedule_lists(g, win, offsets, ids, s));
@@ -250,20 +246,16 @@ sta_status forward_impl(const sta_dims* dims, const void* q, const void* k, cons
   if (st == STA_OK) st = mark(3);
   if (st != STA_OK) return st;
   sta::FwdArgs a;
-  a.q_tiled = ws + c.q_tiled;
+  a.q = q;
   a.k_packed = ws + c.k_packed;
   a.v_packed = ws + c.v_packed;
-  a.o_tiled = ws + c.o_tiled;
-  a.lse_tiled = lse_tiled;
+  a.out = out;
+  a.lse = lse;
   a.offsets = offsets;
   a.ids = ids;
   a.work = work;
-  a.scale_log2 = float(1.4426950408889634 / std::sqrt(double(g.D)));
   st = hip_status(sta::launch_attention(g, a, s));
   if (st == STA_OK) st = mark(4);
-  if (st != STA_OK) return st;
-  st = hip_status(sta::launch_unpack_out(g, ws + c.o_tiled, lse_tiled, out, lse, s));
-  if (st == STA_OK) st = mark(5);
   return st;
 }
 

@@ -9,15 +9,19 @@
 //
 // Work decomposition. One workgroup = one query unit: a 384-row query tile
 // (or the 256 text query slots of one head), 8 waves of 48 rows each (three
-// 16-row column groups), two waves per SIMD. Keys stream in 64-key blocks
-// (K and V, 16 KB each at D=128) straight from global memory into LDS with
-// LDS-DMA loads, double buffered, one barrier per block.
+// 16-row column groups), two waves per SIMD. Q rows are read from the
+// caller's raster q through the tile map, and O / lse are written back to
+// raster positions, so no separate gather or scatter pass is needed for them.
+// Keys stream in 64-key blocks of the packed K and V (16 KB each at D=128)
+// straight from global memory into LDS with LDS-DMA loads, double buffered,
+// one barrier per block.
 //
 // Per block and wave, with v_mfma_f32_16x16x32_bf16:
-//   S^T - m = K (Q c)^T - m
-//                 A = K fragment (LDS), B = Q^T fragment (registers, loaded
-//                 once per unit and pre-scaled by c = log2(e)/sqrt(D)), and
-//                 the accumulator seeded with -m, the running reference max.
+//   S^T - m = (K c) Q^T - m
+//                 A = K fragment (LDS; the keys were scaled by
+//                 c = log2(e)/sqrt(D) when packed), B = Q^T fragment
+//                 (registers, loaded once per unit), and the accumulator
+//                 seeded with -m, the running reference max.
 //                 Lane l then holds s - m of query l%16 for keys 4*(l/16) + r
 //                 of each 16-key group, already in the log2 domain.
 //   softmax       p = 2^(s - m) straight from the MFMA output (one v_exp_f32
@@ -32,7 +36,7 @@
 //                 accumulator layout of S^T), B = P^T from the lane's own
 //                 registers after bf16 rounding. The row sums accumulate the
 //                 same rounded p with v_dot2_f32_bf16.
-// Epilogue: O = O^T / l rounded to bf16, lse = (m + log2 l) * ln 2.
+// Epilogue: O = O^T / l rounded to bf16, lse = (m + log2 l) * ln 2, at raster rows.
 #include "sta_internal.h"
 
 namespace sta {
@@ -96,7 +100,7 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(Geom g, FwdA
   const int q_rows = text_unit ? kTextSlots : kTileRows;
   const size_t slab = size_t(bh) * g.S * D;  // element offset of this (b, head)
 
-  const __bf16* __restrict__ qt = reinterpret_cast<const __bf16*>(a.q_tiled) + slab;
+  const __bf16* __restrict__ qr = reinterpret_cast<const __bf16*>(a.q) + slab;
   const char* __restrict__ kp = reinterpret_cast<const char*>(a.k_packed) + slab * 2;
   const char* __restrict__ vp = reinterpret_cast<const char*>(a.v_packed) + slab * 2;
 
@@ -124,21 +128,20 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(Geom g, FwdA
     }
   };
 
-  // Q^T fragments for this wave's 48 rows, pre-scaled by log2(e)/sqrt(D) so
-  // the MFMA yields scores in the log2 domain (rows past the unit are clamped
-  // to a valid row; their results are discarded).
-  const float sc = a.scale_log2;
+  // Q^T fragments for this wave's 48 rows, read from the caller's raster q
+  // (row r of the unit is tile-major row q_row0 + r; rows past the unit are
+  // clamped to a valid row and their results discarded). K arrives
+  // pre-scaled by log2(e)/sqrt(D), so the MFMA yields scores in the log2
+  // domain.
   bf16x8 qf[kQT][KS];
 #pragma unroll
   for (int c = 0; c < kQT; ++c) {
     int row = wave * kRowsPerWave + c * 16 + (lane & 15);
     row = row < q_rows ? row : q_rows - 1;
-    const bf16x8* src = reinterpret_cast<const bf16x8*>(qt + size_t(q_row0 + row) * D + (lane >> 4) * 8);
+    const int rr = tiled_to_raster(q_row0 + row, g);
+    const bf16x8* src = reinterpret_cast<const bf16x8*>(qr + size_t(rr) * D + (lane >> 4) * 8);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      f32x8 x = __builtin_convertvector(src[ks * 4], f32x8);
-      qf[c][ks] = __builtin_convertvector(x * sc, bf16x8);
-    }
+    for (int ks = 0; ks < KS; ++ks) qf[c][ks] = src[ks * 4];
   }
 
   f32x4 acc[kQT][DT];
@@ -162,7 +165,7 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(Geom g, FwdA
     __syncthreads();
     if (j + 1 < n_blk) issue(j + 1, stage ^ 1);
 
-    // ---- S^T - m = K (Q*scale)^T - m: the running max enters as the accumulator
+    // ---- S^T - m = (K*scale) Q^T - m: the running max enters as the accumulator
     // seed. When the reference must move (always on the first block, rarely
     // later: some score exceeds it by more than the slack), the reference is
     // updated and the block's scores are recomputed from the new seed, so the
@@ -262,22 +265,23 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(Geom g, FwdA
     }
   }
 
-  // ---- epilogue
-  __bf16* __restrict__ ot = reinterpret_cast<__bf16*>(a.o_tiled) + slab;
-  float* __restrict__ lt = a.lse_tiled + size_t(bh) * g.S;
+  // ---- epilogue: O = O^T / l in bf16 and lse, straight to raster positions
+  __bf16* __restrict__ outr = reinterpret_cast<__bf16*>(a.out) + slab;
+  float* __restrict__ lser = a.lse == nullptr ? nullptr : a.lse + size_t(bh) * g.S;
 #pragma unroll
   for (int c = 0; c < kQT; ++c) {
     const float l = swap32_sum(swap16_sum(l_part[c]));
     const float inv = __builtin_amdgcn_rcpf(l);
     const int row = wave * kRowsPerWave + c * 16 + (lane & 15);
     if (row < q_rows) {
-      __bf16* dst = ot + size_t(q_row0 + row) * D + (lane >> 4) * 4;
+      const int rr = tiled_to_raster(q_row0 + row, g);
+      __bf16* dst = outr + size_t(rr) * D + (lane >> 4) * 4;
 #pragma unroll
       for (int d = 0; d < DT; ++d) {
         const f32x4 o = acc[c][d] * inv;
         *reinterpret_cast<bf16x4*>(dst + d * 16) = __builtin_convertvector(o, bf16x4);
       }
-      if (lane < 16) lt[q_row0 + row] = (m_run[c] + __builtin_amdgcn_logf(l)) * kLn2;
+      if (lser != nullptr && lane < 16) lser[rr] = (m_run[c] + __builtin_amdgcn_logf(l)) * kLn2;
     }
   }
 }

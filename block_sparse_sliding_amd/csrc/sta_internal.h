@@ -59,25 +59,22 @@ __host__ __device__ inline int tiled_to_raster(int r, const Geom& g) {
 // Launchers (each enqueues one kernel on `stream` and returns hipGetLastError()).
 hipError_t launch_rows_permute(const Geom& g, const void* src, void* dst, bool to_tiled,
                                hipStream_t stream);
-hipError_t launch_pack_qkv(const Geom& g, const void* q, const void* k, const void* v,
-                           void* q_tiled, void* k_packed, void* v_packed, hipStream_t stream);
-hipError_t launch_unpack_out(const Geom& g, const void* o_tiled, const float* lse_tiled,
-                             void* out, float* lse, hipStream_t stream);
+hipError_t launch_pack_kv(const Geom& g, const void* k, const void* v, void* k_packed,
+                          void* v_packed, float k_scale, hipStream_t stream);
 hipError_t launch_schedule_lists(const Geom& g, const Windows& win, int32_t* offsets,
                                  int32_t* ids, hipStream_t stream);
 hipError_t launch_schedule_work(const Geom& g, const Windows& win, int32_t* work,
                                 hipStream_t stream);
 
 struct FwdArgs {
-  const void* q_tiled;   // bf16 tile-major rows
-  const void* k_packed;  // bf16, 64-key blocks in MFMA A-operand fragment order
+  const void* q;         // bf16 raster rows (the caller's q)
+  const void* k_packed;  // bf16 k*log2(e)/sqrt(D), 64-key blocks in MFMA A-operand order
   const void* v_packed;  // bf16, 64-key blocks, transposed fragment order
-  void* o_tiled;         // bf16 tile-major rows
-  float* lse_tiled;      // fp32 tile-major
+  void* out;             // bf16 raster rows (the caller's out)
+  float* lse;            // fp32 raster (the caller's lse), or nullptr
   const int32_t* offsets;
   const int32_t* ids;
   const int32_t* work;
-  float scale_log2;      // log2(e) / sqrt(D)
 };
 hipError_t launch_attention(const Geom& g, const FwdArgs& a, hipStream_t stream);
 

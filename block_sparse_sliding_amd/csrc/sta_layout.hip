@@ -1,5 +1,6 @@
 // Layout kernels: tile-major gather / scatter of token rows, and the packing of
-// q, k, v into the forms the fused attention kernel streams.
+// k and v into the forms the fused attention kernel streams (the attention
+// kernel reads q and writes out / lse in raster order itself).
 //
 // Tile-major order (each (6,8,8) tile becomes 384 contiguous rows) follows the
 // tile definition of the STA README "Usage" section; it turns every dense
@@ -10,6 +11,9 @@ namespace sta {
 namespace {
 
 constexpr int kThreads = 256;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
 
 // One workgroup per 64-row block of the tile-major sequence, one grid row per
 // (batch, head) slab. Copies whole rows in 16-byte chunks; both sides coalesce
@@ -33,10 +37,12 @@ __global__ __launch_bounds__(kThreads) void rows_permute_kernel(Geom g, const ui
   }
 }
 
-// Pack q, k, v for the attention kernel (grid.z: 0 = q, 1 = k, 2 = v).
+// Pack k and v for the attention kernel (grid.z: 0 = k, 1 = v), tile-major.
 //
-// q: tile-major rows, unchanged.
-// k: each 64-key block is stored as (4 key groups) x (D/32 k-steps) fragments
+// k: scaled by k_scale = log2(e)/sqrt(D) and rounded to bf16 (so the MFMA
+//    yields scores in the log2 domain; rounding the scaled keys rather than
+//    the queries keeps the rounding error independent from key to key), then
+//    each 64-key block is stored as (4 key groups) x (D/32 k-steps) fragments
 //    of 1 KB; in fragment (kt, ks) lane l's 16 bytes are
 //    K[16*kt + l%16][32*ks + 8*(l/16) .. +8], the A operand of a 16x16x32
 //    MFMA that computes S^T = K Q^T.
@@ -48,12 +54,10 @@ __global__ __launch_bounds__(kThreads) void rows_permute_kernel(Geom g, const ui
 // Text rows at or after text_length are written as zeros in k and v, so that
 // nothing stored there (even non-finite values) can reach the output.
 template <int D>
-__global__ __launch_bounds__(kThreads) void pack_qkv_kernel(Geom g, const uint4* __restrict__ q,
-                                                            const uint4* __restrict__ k,
-                                                            const uint4* __restrict__ v,
-                                                            uint4* __restrict__ qt,
-                                                            uint4* __restrict__ kp,
-                                                            uint4* __restrict__ vp) {
+__global__ __launch_bounds__(kThreads) void pack_kv_kernel(Geom g, const uint4* __restrict__ k,
+                                                           const uint4* __restrict__ v,
+                                                           uint4* __restrict__ kp,
+                                                           uint4* __restrict__ vp, float k_scale) {
   constexpr int CPR = D / 8;
   constexpr int ROWH = D + 4;  // padded LDS row (in bf16) for the V transpose
   __shared__ uint16_t tile[kKeyBlock * ROWH];
@@ -63,21 +67,18 @@ __global__ __launch_bounds__(kThreads) void pack_qkv_kernel(Geom g, const uint4*
   const int valid_end = g.n_video + (g.has_text ? g.text_length : 0);
 
   if (which == 0) {
-#pragma unroll
-    for (int c = threadIdx.x; c < kKeyBlock * CPR; c += kThreads) {
-      const int rt = r0 + c / CPR, col = c % CPR;
-      qt[slab + size_t(rt) * CPR + col] = q[slab + size_t(tiled_to_raster(rt, g)) * CPR + col];
-    }
-    return;
-  }
-  if (which == 1) {
     uint4* dst = kp + slab + size_t(r0) * CPR;
 #pragma unroll
     for (int c = threadIdx.x; c < kKeyBlock * CPR; c += kThreads) {
       const int j = c / CPR, col = c % CPR;
       const int rt = r0 + j;
       uint4 x = make_uint4(0, 0, 0, 0);
-      if (rt < valid_end) x = k[slab + size_t(tiled_to_raster(rt, g)) * CPR + col];
+      if (rt < valid_end) {
+        x = k[slab + size_t(tiled_to_raster(rt, g)) * CPR + col];
+        bf16x8 kv = __builtin_bit_cast(bf16x8, x);
+        f32x8 f = __builtin_convertvector(kv, f32x8) * k_scale;
+        x = __builtin_bit_cast(uint4, __builtin_convertvector(f, bf16x8));
+      }
       const int kt = j >> 4, ks = col >> 2, grp = col & 3;
       dst[(kt * (D / 32) + ks) * 64 + (j & 15) + 16 * grp] = x;
     }
@@ -116,27 +117,6 @@ __global__ __launch_bounds__(kThreads) void pack_qkv_kernel(Geom g, const uint4*
   }
 }
 
-// Scatter the tile-major output rows and LSE back to raster order.
-template <int D>
-__global__ __launch_bounds__(kThreads) void unpack_out_kernel(Geom g, const uint4* __restrict__ ot,
-                                                              const float* __restrict__ lset,
-                                                              uint4* __restrict__ out,
-                                                              float* __restrict__ lse) {
-  constexpr int CPR = D / 8;
-  const size_t slab = size_t(blockIdx.y) * g.S * CPR;
-  const int r0 = blockIdx.x * kKeyBlock;
-#pragma unroll
-  for (int c = threadIdx.x; c < kKeyBlock * CPR; c += kThreads) {
-    const int rt = r0 + c / CPR, col = c % CPR;
-    out[slab + size_t(tiled_to_raster(rt, g)) * CPR + col] = ot[slab + size_t(rt) * CPR + col];
-  }
-  if (lse != nullptr && threadIdx.x < kKeyBlock) {
-    const size_t ls = size_t(blockIdx.y) * g.S;
-    const int rt = r0 + threadIdx.x;
-    lse[ls + tiled_to_raster(rt, g)] = lset[ls + rt];
-  }
-}
-
 }  // namespace
 
 hipError_t launch_rows_permute(const Geom& g, const void* src, void* dst, bool to_tiled,
@@ -149,29 +129,15 @@ hipError_t launch_rows_permute(const Geom& g, const void* src, void* dst, bool t
   return hipGetLastError();
 }
 
-hipError_t launch_pack_qkv(const Geom& g, const void* q, const void* k, const void* v,
-                           void* q_tiled, void* k_packed, void* v_packed, hipStream_t stream) {
-  dim3 grid(g.S / kKeyBlock, g.B * g.heads, 3);
+hipError_t launch_pack_kv(const Geom& g, const void* k, const void* v, void* k_packed,
+                          void* v_packed, float k_scale, hipStream_t stream) {
+  dim3 grid(g.S / kKeyBlock, g.B * g.heads, 2);
   if (g.D == 128)
-    pack_qkv_kernel<128><<<grid, kThreads, 0, stream>>>(g, (const uint4*)q, (const uint4*)k,
-                                                        (const uint4*)v, (uint4*)q_tiled,
-                                                        (uint4*)k_packed, (uint4*)v_packed);
+    pack_kv_kernel<128><<<grid, kThreads, 0, stream>>>(g, (const uint4*)k, (const uint4*)v,
+                                                       (uint4*)k_packed, (uint4*)v_packed, k_scale);
   else
-    pack_qkv_kernel<64><<<grid, kThreads, 0, stream>>>(g, (const uint4*)q, (const uint4*)k,
-                                                       (const uint4*)v, (uint4*)q_tiled,
-                                                       (uint4*)k_packed, (uint4*)v_packed);
-  return hipGetLastError();
-}
-
-hipError_t launch_unpack_out(const Geom& g, const void* o_tiled, const float* lse_tiled,
-                             void* out, float* lse, hipStream_t stream) {
-  dim3 grid(g.S / kKeyBlock, g.B * g.heads);
-  if (g.D == 128)
-    unpack_out_kernel<128><<<grid, kThreads, 0, stream>>>(g, (const uint4*)o_tiled, lse_tiled,
-                                                          (uint4*)out, lse);
-  else
-    unpack_out_kernel<64><<<grid, kThreads, 0, stream>>>(g, (const uint4*)o_tiled, lse_tiled,
-                                                         (uint4*)out, lse);
+    pack_kv_kernel<64><<<grid, kThreads, 0, stream>>>(g, (const uint4*)k, (const uint4*)v,
+                                                      (uint4*)k_packed, (uint4*)v_packed, k_scale);
   return hipGetLastError();
 }
 

@@ -99,8 +99,9 @@ size_t sta_workspace_bytes(const sta_dims* dims, const int32_t* window_sizes,
  *             bytes, 256-byte aligned; contents on entry are ignored and on
  *             return are unspecified. Calls that share a workspace must be
  *             ordered on one stream.
- * Returns STA_OK once the five launches (pack, schedule lists, work order,
- * fused attention, scatter) are enqueued on `stream`.
+ * Returns STA_OK once the four launches (K/V pack into tile-major MFMA
+ * fragment order, schedule lists, work order, fused attention reading q and
+ * writing out/lse in raster order) are enqueued on `stream`.
  */
 sta_status sta_forward(const sta_dims* dims, const void* q, const void* k,
                        const void* v, const int32_t* window_sizes,
@@ -112,12 +113,12 @@ sta_status sta_forward(const sta_dims* dims, const void* q, const void* k,
  * sta_forward with stage timing, for measurement. `events` holds
  * STA_TIMED_EVENTS hipEvent_t handles (as void*, created by the caller);
  * events[0] is recorded on `stream` before the first launch and events[i]
- * after launch i of: 1 pack q/k/v, 2 schedule lists, 3 work order,
- * 4 fused attention, 5 scatter of out/lse. hipEventElapsedTime between
- * consecutive events then gives each kernel's duration. Nothing else
- * differs from sta_forward; STA_ERR_NULL if events or an entry is NULL.
+ * after launch i of: 1 pack k/v, 2 schedule lists, 3 work order,
+ * 4 fused attention. hipEventElapsedTime between consecutive events then
+ * gives each kernel's duration. Nothing else differs from sta_forward;
+ * STA_ERR_NULL if events or an entry is NULL.
  */
-#define STA_TIMED_EVENTS 6
+#define STA_TIMED_EVENTS 5
 sta_status sta_forward_timed(const sta_dims* dims, const void* q, const void* k,
                              const void* v, const int32_t* window_sizes,
                              int32_t text_length, int32_t has_text, void* out,
