@@ -1,8 +1,8 @@
 #!/usr/bin/env python3
 """Benchmark of the STA forward (one GPU).
 
-One step = one sta_forward call (pack k/v to tile-major MFMA order, build
-the tile-window schedule and work order, fused attention reading q and
+One step = one sta_forward call (pack v to tile-major V^T fragments, build
+the tile-window schedule and work order, fused attention reading q and k and
 writing out/lse in raster order) on the workload's synthetic bf16 inputs,
 which are resident in HBM before timing starts. Prints one JSON line with the
 end-to-end effective TFLOP/s, the roofline of the fused attention kernel

@@ -144,7 +144,7 @@ def sta_forward(dims: sta_dims, q, k, v, window_sizes, text_length: int, has_tex
 
 
 TIMED_EVENTS = 5
-STAGES = ("pack", "schedule_lists", "schedule_work", "attention")
+STAGES = ("pack_v", "schedule_lists", "schedule_work", "attention")
 
 
 def sta_forward_timed(dims: sta_dims, q, k, v, window_sizes, text_length: int, has_text: bool,

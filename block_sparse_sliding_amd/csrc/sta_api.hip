@@ -27,6 +27,8 @@ sta_status make_geom(const sta_dims* d, int32_t has_text, int32_t text_length, G
   if (d->T % sta::kTileT || d->H % sta::kTileH || d->W % sta::kTileW) return STA_ERR_SHAPE;
   const int64_t nt = d->T / sta::kTileT, nh = d->H / sta::kTileH, nw = d->W / sta::kTileW;
   if (nt > 1023 || nh > 1023 || nw > 1023) return STA_ERR_SHAPE;
+  // tile decoding divides tile indices by nw and nh with 32-bit reciprocals
+  if (nt * nh * nw * (nh > nw ? nh : nw) >= (int64_t(1) << 32)) return STA_ERR_SHAPE;
   const int64_t n_video = int64_t(d->T) * d->H * d->W;
   const int64_t S = n_video + (has_text ? STA_TEXT_SLOTS : 0);
   // per-slab element offsets and row indices are 32-bit inside the kernels
@@ -54,6 +56,9 @@ sta_status make_geom(const sta_dims* d, int32_t has_text, int32_t text_length, G
   g->has_text = has_text ? 1 : 0;
   g->text_length = text_length;
   g->n_q = int32_t(n_q);
+  auto magic = [](int64_t d) { return d == 1 ? 0u : uint32_t(((int64_t(1) << 32) + d - 1) / d); };
+  g->mag_nw = magic(nw);
+  g->mag_nh = magic(nh);
   return STA_OK;
 }
 
@@ -73,15 +78,14 @@ sta_status make_windows(const Geom& g, const int32_t* ws, Windows* win, int64_t*
 }
 
 struct Carve {
-  size_t k_packed, v_packed, offsets, ids, work, total;
+  size_t vt, offsets, ids, work, total;
 };
 
 Carve carve(const Geom& g, int64_t n_ids) {
   Carve c{};
   const size_t tensor = size_t(g.B) * g.heads * g.S * g.D * 2;
   size_t at = 0;
-  c.k_packed = at; at = align_up(at + tensor);
-  c.v_packed = at; at = align_up(at + tensor);
+  c.vt = at; at = align_up(at + tensor);
   c.offsets = at; at = align_up(at + (size_t(g.heads) * g.n_q + 1) * 4);
   c.ids = at; at = align_up(at + size_t(n_ids) * 4);
   c.work = at; at = align_up(at + size_t(g.B) * g.heads * g.n_q * 4);
@@ -235,8 +239,7 @@ sta_status forward_impl(const sta_dims* dims, const void* q, const void* k, cons
   int32_t* ids = reinterpret_cast<int32_t*>(ws + c.ids);
   int32_t* work = reinterpret_cast<int32_t*>(ws + c.work);
 
-  const float k_scale = float(1.4426950408889634 / std::sqrt(double(g.D)));  // log2(e)/sqrt(D)
-  st = hip_status(sta::launch_pack_kv(g, k, v, ws + c.k_packed, ws + c.v_packed, k_scale, s));
+  st = hip_status(sta::launch_pack_v(g, v, ws + c.vt, s));
   if (st == STA_OK) st = mark(1);
   if (st != STA_OK) return st;
   st = hip_status(sta::launch_schedule_lists(g, win, offsets, ids, s));
@@ -247,13 +250,14 @@ sta_status forward_impl(const sta_dims* dims, const void* q, const void* k, cons
   if (st != STA_OK) return st;
   sta::FwdArgs a;
   a.q = q;
-  a.k_packed = ws + c.k_packed;
-  a.v_packed = ws + c.v_packed;
+  a.k = k;
+  a.vt = ws + c.vt;
   a.out = out;
   a.lse = lse;
   a.offsets = offsets;
   a.ids = ids;
   a.work = work;
+  a.q_scale = float(1.4426950408889634 / std::sqrt(double(g.D)));  // log2(e)/sqrt(D)
   st = hip_status(sta::launch_attention(g, a, s));
   if (st == STA_OK) st = mark(4);
   return st;

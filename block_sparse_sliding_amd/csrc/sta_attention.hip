@@ -11,19 +11,29 @@
 // (or the 256 text query slots of one head), 8 waves of 48 rows each (three
 // 16-row column groups), two waves per SIMD. Q rows are read from the
 // caller's raster q through the tile map, and O / lse are written back to
-// raster positions, so no separate gather or scatter pass is needed for them.
-// Keys stream in 64-key blocks of the packed K and V (16 KB each at D=128)
-// straight from global memory into LDS with LDS-DMA loads, double buffered,
-// one barrier per block.
+// raster positions. Keys stream in 64-key blocks into LDS with LDS-DMA loads,
+// double buffered, one barrier per block: K straight from the caller's raster
+// k (each lane supplies its own source address, which applies the tile map),
+// V as packed V^T fragments (one contiguous 16 KB run per block at D = 128,
+// written by the pack kernel). The next block's loads are issued once the
+// current block's score MFMAs are under way.
+//
+// LDS layout of a K block (64 rows of D bf16). Each 1 KB LDS-DMA transfer
+// fills one group of 1024 / (2D) consecutive rows. Inside a group the rows
+// are interleaved at 64-byte granularity: quad k (16-byte chunks 4k..4k+3) of
+// every row of the group, then quad k + 1, and so on; within a quad the chunks
+// of row r sit XOR-permuted by a 2-bit function of (r / 4) mod 4. The K
+// fragment reads (16 rows x one chunk) then hit distinct banks and every read
+// address is one per-lane base plus compile-time offsets.
 //
 // Per block and wave, with v_mfma_f32_16x16x32_bf16:
-//   S^T - m = (K c) Q^T - m
-//                 A = K fragment (LDS; the keys were scaled by
-//                 c = log2(e)/sqrt(D) when packed), B = Q^T fragment
-//                 (registers, loaded once per unit), and the accumulator
-//                 seeded with -m, the running reference max.
-//                 Lane l then holds s - m of query l%16 for keys 4*(l/16) + r
-//                 of each 16-key group, already in the log2 domain.
+//   S^T - m = K (Q c)^T - m
+//                 A = K fragment (lane l holds K[16kt + l%16][32ks + 8(l/16)
+//                 .. +8]), B = Q^T fragment (registers, loaded once per unit
+//                 and pre-scaled by c = log2(e)/sqrt(D)), accumulator seeded
+//                 with -m, the running reference max. Lane l then holds s - m
+//                 of query l%16 for keys 4(l/16) + r of each 16-key group,
+//                 already in the log2 domain.
 //   softmax       p = 2^(s - m) straight from the MFMA output (one v_exp_f32
 //                 per score). The reference only moves when some score
 //                 exceeds it by more than kRescaleSlack (a per-lane v_max3
@@ -32,10 +42,13 @@
 //                 first block always sets the reference from its exact row
 //                 max. Any reference gives the same softmax; the slack
 //                 bounds p by 2^slack.
-//   O^T += V^T P^T  A = V^T fragment (LDS, packed so its key order matches the
-//                 accumulator layout of S^T), B = P^T from the lane's own
-//                 registers after bf16 rounding. The row sums accumulate the
-//                 same rounded p with v_dot2_f32_bf16.
+//   O^T += V^T P^T  A = packed V^T fragment (one ds_read_b128; its key order
+//                 matches the accumulator layout of S^T), B = P^T from the
+//                 lane's own registers after bf16 rounding. The row sums
+//                 accumulate the same rounded p with v_dot2_f32_bf16.
+// Text rows at or after text_length only ever appear in the last text block:
+// their scores are replaced by -inf (a select, so whatever k holds there is
+// ignored) and their packed V rows are zeros.
 // Epilogue: O = O^T / l rounded to bf16, lse = (m + log2 l) * ln 2, at raster rows.
 #include "sta_internal.h"
 
@@ -80,13 +93,21 @@ __device__ inline void dma16(const char* gsrc, char* lds_dst) {
   __builtin_amdgcn_global_load_lds(gsrc, (lds_void*)lds_dst, 16, 0, 0);
 }
 
+// floor(n / d) for n >= 0, d >= 1, n * d < 2^32, with m = ceil(2^32 / d) (see Geom).
+__device__ inline int div_by(int n, int d, uint32_t m) {
+  return d == 1 ? n : int(__umulhi(uint32_t(n), m));
+}
+
 template <int D>
 __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(Geom g, FwdArgs a) {
-  constexpr int KS = D / 32;              // k-steps of S^T
-  constexpr int DT = D / 16;              // d groups of O^T
-  constexpr int BLK = kKeyBlock * D * 2;  // bytes of one packed K (or V) block
-  constexpr int PER_WAVE = BLK / kWaves;  // bytes each wave moves per tensor
-  static_assert(PER_WAVE % 1024 == 0, "LDS-DMA moves 1 KB per wave instruction");
+  constexpr int KS = D / 32;                // k-steps of S^T
+  constexpr int DT = D / 16;                // d groups of O^T
+  constexpr int ROWB = D * 2;               // bytes per K row
+  constexpr int BLK = kKeyBlock * ROWB;     // bytes of one K (or V^T) block
+  constexpr int RPI = 1024 / ROWB;          // K rows per 1 KB LDS-DMA instruction
+  constexpr int IPW = BLK / 1024 / kWaves;  // DMA instructions per wave per tensor
+  constexpr int BPT = kTileRows / kKeyBlock;  // key blocks per tile (6)
+  static_assert(IPW >= 1 && BLK % (1024 * kWaves) == 0, "block must split over the waves");
   __shared__ __attribute__((aligned(1024))) char lds[2][2][BLK];  // [stage][K|V]
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -101,38 +122,83 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(Geom g, FwdA
   const size_t slab = size_t(bh) * g.S * D;  // element offset of this (b, head)
 
   const __bf16* __restrict__ qr = reinterpret_cast<const __bf16*>(a.q) + slab;
-  const char* __restrict__ kp = reinterpret_cast<const char*>(a.k_packed) + slab * 2;
-  const char* __restrict__ vp = reinterpret_cast<const char*>(a.v_packed) + slab * 2;
+  const char* __restrict__ kr = reinterpret_cast<const char*>(a.k) + slab * 2;
+  const char* __restrict__ vtr = reinterpret_cast<const char*>(a.vt) + slab * 2;
 
   const int l0 = a.offsets[hd * g.n_q + u];
   const int l1 = a.offsets[hd * g.n_q + u + 1];
-  const int n_vid = (l1 - l0) * (kTileRows / kKeyBlock);
+  const int n_vid = (l1 - l0) * BPT;
   const int text_len = g.has_text ? g.text_length : 0;
   const int n_blk = n_vid + (text_len + kKeyBlock - 1) / kKeyBlock;
-  const bool ragged_text = (text_len % kKeyBlock) != 0;
+  const bool ragged = (text_len % kKeyBlock) != 0;
 
-  auto issue = [&](int j, int stage) {
-    int row;
+  // 2-bit chunk permutation of K row r inside its 64-byte quad.
+  auto sw = [](int row) { return ((row >> 1) & 2) | ((row >> 3) & 1); };
+
+  // The schedule is read through the scalar cache (it is never written while
+  // this kernel runs). Key blocks of one tile are consecutive.
+  const __attribute__((address_space(4))) int32_t* ids =
+      (const __attribute__((address_space(4))) int32_t*)(a.ids + l0);
+
+  // Source rows of key block j (blocks are fetched in order 0, 1, 2, ...; the
+  // six blocks of a tile are its six frames, so a tile is decoded once, at its
+  // first block): kbase = raster row of the block's 8x8 (h, w) patch origin
+  // (video) or first slot (text), krs = raster stride between its 8-row
+  // runs, vrow = its first tile-major row (the packed V^T block).
+  int tile_kbase = 0, tile_vrow = 0;
+  auto block_rows = [&](int j, int& kbase, int& krs, int& vrow) {
     if (j < n_vid) {
-      const int tile = a.ids[l0 + j / (kTileRows / kKeyBlock)];
-      row = tile * kTileRows + (j % (kTileRows / kKeyBlock)) * kKeyBlock;
+      const int t = j / BPT;
+      const int sub = j - t * BPT;
+      if (sub == 0) {
+        const int tile = ids[t];
+        const int rest = div_by(tile, g.nw, g.mag_nw);
+        const int tw = tile - rest * g.nw;
+        const int tt = div_by(rest, g.nh, g.mag_nh);
+        const int th = rest - tt * g.nh;
+        tile_kbase = (tt * kTileT * g.H + th * kTileH) * g.W + tw * kTileW;
+        tile_vrow = tile * kTileRows;
+      }
+      kbase = tile_kbase + sub * g.H * g.W;
+      krs = g.W;
+      vrow = tile_vrow + sub * kKeyBlock;
     } else {
-      row = g.n_video + (j - n_vid) * kKeyBlock;
+      kbase = vrow = g.n_video + (j - n_vid) * kKeyBlock;
+      krs = kTileW;
     }
-    const size_t off = size_t(row) * D * 2;
+  };
+
+  // Fetch K block j into LDS stage st. Row rr of the block is raster row
+  // kbase + (rr/8)*krs + rr%8. Each DMA instruction covers RPI rows that
+  // share rr/8, so its source is a wave-uniform row pointer plus a per-lane
+  // offset (row within the group, chunk) that is the same for every block.
+  auto issue_k = [&](int st, int kbase, int krs) {
 #pragma unroll
-    for (int c = 0; c < PER_WAVE / 1024; ++c) {
-      const int o = wave * PER_WAVE + c * 1024;
-      dma16(kp + off + o + lane * 16, &lds[stage][0][o]);
-      dma16(vp + off + o + lane * 16, &lds[stage][1][o]);
+    for (int i = 0; i < IPW; ++i) {
+      const int q = wave * IPW + i;
+      const size_t urow = size_t(kbase + ((q * RPI) >> 3) * krs + ((q * RPI) & 7));
+      const int rin = (lane >> 2) % RPI;
+      const int chunk = 4 * (lane / (4 * RPI)) + ((lane & 3) ^ sw(q * RPI + rin));
+      const unsigned o = unsigned(rin * ROWB + chunk * 16);
+      dma16(kr + urow * ROWB + o, &lds[st][0][q * 1024]);
+    }
+  };
+  // Fetch the packed V^T block starting at tile-major row vrow (contiguous).
+  auto issue_v = [&](int st, int vrow) {
+    const char* src = vtr + size_t(vrow) * ROWB;
+    const unsigned o = unsigned(lane) * 16u;
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+      const int q = wave * IPW + i;
+      dma16(src + q * 1024 + o, &lds[st][1][q * 1024]);
     }
   };
 
   // Q^T fragments for this wave's 48 rows, read from the caller's raster q
   // (row r of the unit is tile-major row q_row0 + r; rows past the unit are
-  // clamped to a valid row and their results discarded). K arrives
-  // pre-scaled by log2(e)/sqrt(D), so the MFMA yields scores in the log2
-  // domain.
+  // clamped to a valid row and their results discarded), pre-scaled by
+  // log2(e)/sqrt(D) so the MFMA yields scores in the log2 domain.
+  const float qs = a.q_scale;
   bf16x8 qf[kQT][KS];
 #pragma unroll
   for (int c = 0; c < kQT; ++c) {
@@ -141,7 +207,10 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(Geom g, FwdA
     const int rr = tiled_to_raster(q_row0 + row, g);
     const bf16x8* src = reinterpret_cast<const bf16x8*>(qr + size_t(rr) * D + (lane >> 4) * 8);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qf[c][ks] = src[ks * 4];
+    for (int ks = 0; ks < KS; ++ks) {
+      const f32x8 x = __builtin_convertvector(src[ks * 4], f32x8);
+      qf[c][ks] = __builtin_convertvector(x * qs, bf16x8);
+    }
   }
 
   f32x4 acc[kQT][DT];
@@ -158,21 +227,33 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(Geom g, FwdA
   ones2[0] = (__bf16)1.0f;
   ones2[1] = (__bf16)1.0f;
 
+  // K fragment (row 16kt + lane%16, chunk 4ks + lane/16) of a block sits at
+  // kofs + kt * 16 * ROWB + ks * 64 * RPI; V^T fragment (h, dt) at
+  // (h * DT + dt) * 1024 + lane * 16.
+  const int l15 = lane & 15;
+  const int kofs = (l15 / RPI) * 1024 + (l15 % RPI) * 64 + (((lane >> 4) ^ sw(l15)) << 4);
+
+  auto issue = [&](int j, int st) {
+    int kbase, krs, vrow;
+    block_rows(j, kbase, krs, vrow);
+    issue_k(st, kbase, krs);
+    issue_v(st, vrow);
+  };
+
   issue(0, 0);
   for (int j = 0; j < n_blk; ++j) {
     const int stage = j & 1;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (j + 1 < n_blk) issue(j + 1, stage ^ 1);
 
-    // ---- S^T - m = (K*scale) Q^T - m: the running max enters as the accumulator
+    // ---- S^T - m = K (Q c)^T - m: the running max enters as the accumulator
     // seed. When the reference must move (always on the first block, rarely
     // later: some score exceeds it by more than the slack), the reference is
     // updated and the block's scores are recomputed from the new seed, so the
-    // score registers are only ever written by the MFMAs.
-    const bf16x8* kl = reinterpret_cast<const bf16x8*>(lds[stage][0]);
+    // score registers are only ever written by the MFMAs (and the mask).
+    const char* kb = lds[stage][0];
     f32x4 s[kQT][4];
-    for (int pass = 0;; ++pass) {
+    auto scores = [&]() {
       f32x4 seed[kQT];
 #pragma unroll
       for (int c = 0; c < kQT; ++c) seed[c] = f32x4{-m_run[c], -m_run[c], -m_run[c], -m_run[c]};
@@ -180,7 +261,7 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(Geom g, FwdA
       for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) {
-          const bf16x8 kf = kl[(kt * KS + ks) * 64 + lane];
+          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kb + kofs + kt * 16 * ROWB + ks * 64 * RPI);
 #pragma unroll
           for (int c = 0; c < kQT; ++c)
             s[c][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[c][ks],
@@ -188,7 +269,7 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(Geom g, FwdA
         }
       }
       // mask the padded keys of the last, ragged text block
-      if (ragged_text && j == n_blk - 1) {
+      if (ragged && j == n_blk - 1) {
         const int key0 = (j - n_vid) * kKeyBlock + 4 * (lane >> 4);
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt)
@@ -198,25 +279,28 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(Geom g, FwdA
 #pragma unroll
               for (int c = 0; c < kQT; ++c) s[c][kt][r] = -INFINITY;
       }
-      if (pass == 1) break;  // a recomputed block never moves the reference again
-      // per-lane max of s - m; the reference moves only past the slack
-      float lm[kQT];
-      bool need = false;
+    };
+    scores();
+    // the next block streams in while this one is finished (its stage was
+    // released by every wave at the barrier above)
+    if (j + 1 < n_blk) issue(j + 1, stage ^ 1);
+    // per-lane max of s - m; the reference moves only past the slack
+    float lm[kQT];
+    bool need = false;
 #pragma unroll
-      for (int c = 0; c < kQT; ++c) {
-        float x = fmaxf(fmaxf(s[c][0][0], s[c][0][1]), s[c][0][2]);
-        x = fmaxf(fmaxf(x, s[c][0][3]), s[c][1][0]);
-        x = fmaxf(fmaxf(x, s[c][1][1]), s[c][1][2]);
-        x = fmaxf(fmaxf(x, s[c][1][3]), s[c][2][0]);
-        x = fmaxf(fmaxf(x, s[c][2][1]), s[c][2][2]);
-        x = fmaxf(fmaxf(x, s[c][2][3]), s[c][3][0]);
-        x = fmaxf(fmaxf(x, s[c][3][1]), s[c][3][2]);
-        x = fmaxf(x, s[c][3][3]);
-        lm[c] = x;
-        need |= x > kRescaleSlack;
-      }
-      const bool first = j == 0;
-      if (!first && __builtin_amdgcn_ballot_w64(need) == 0) break;
+    for (int c = 0; c < kQT; ++c) {
+      float x = fmaxf(fmaxf(s[c][0][0], s[c][0][1]), s[c][0][2]);
+      x = fmaxf(fmaxf(x, s[c][0][3]), s[c][1][0]);
+      x = fmaxf(fmaxf(x, s[c][1][1]), s[c][1][2]);
+      x = fmaxf(fmaxf(x, s[c][1][3]), s[c][2][0]);
+      x = fmaxf(fmaxf(x, s[c][2][1]), s[c][2][2]);
+      x = fmaxf(fmaxf(x, s[c][2][3]), s[c][3][0]);
+      x = fmaxf(fmaxf(x, s[c][3][1]), s[c][3][2]);
+      lm[c] = fmaxf(x, s[c][3][3]);
+      need |= lm[c] > kRescaleSlack;
+    }
+    const bool first = j == 0;
+    if (first || __builtin_amdgcn_ballot_w64(need) != 0) {
 #pragma unroll
       for (int c = 0; c < kQT; ++c) {
         // exact row max across the 4 lanes holding this query
@@ -232,6 +316,9 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(Geom g, FwdA
           for (int d = 0; d < DT; ++d) acc[c][d] *= alpha;
         }
       }
+      // re-read the K fragments rather than keep the first reads live
+      asm volatile("" ::: "memory");
+      scores();  // a recomputed block never moves the reference again
     }
 
     // ---- p = 2^(s - m) rounded to bf16; O^T += V^T P^T; row sums += 1^T P^T

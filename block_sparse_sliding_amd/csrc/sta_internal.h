@@ -31,6 +31,10 @@ struct Geom {
   int32_t has_text;
   int32_t text_length;
   int32_t n_q;         // query units per head: n_tiles (+1 text unit)
+  // ceil(2^32 / nw) and ceil(2^32 / nh) (0 when the divisor is 1):
+  // floor(n / d) = umulhi(n, m) exactly whenever n * d < 2^32, which holds for
+  // every tile index (n_tiles * max(nw, nh) < 2^32 is checked on the host).
+  uint32_t mag_nw, mag_nh;
 };
 
 // Per-head windows, packed as wt | wh << 10 | ww << 20 (kernel-argument copy).
@@ -59,8 +63,11 @@ __host__ __device__ inline int tiled_to_raster(int r, const Geom& g) {
 // Launchers (each enqueues one kernel on `stream` and returns hipGetLastError()).
 hipError_t launch_rows_permute(const Geom& g, const void* src, void* dst, bool to_tiled,
                                hipStream_t stream);
-hipError_t launch_pack_kv(const Geom& g, const void* k, const void* v, void* k_packed,
-                          void* v_packed, float k_scale, hipStream_t stream);
+// V^T fragments: every 64-row tile-major block of v (rows at or after the
+// valid text length zeroed) as (2 key halves) x (D/16 column groups) 1 KB
+// fragments, the A operand of O^T += V^T P^T (layout documented at the pack
+// kernel).
+hipError_t launch_pack_v(const Geom& g, const void* v, void* vt, hipStream_t stream);
 hipError_t launch_schedule_lists(const Geom& g, const Windows& win, int32_t* offsets,
                                  int32_t* ids, hipStream_t stream);
 hipError_t launch_schedule_work(const Geom& g, const Windows& win, int32_t* work,
@@ -68,13 +75,14 @@ hipError_t launch_schedule_work(const Geom& g, const Windows& win, int32_t* work
 
 struct FwdArgs {
   const void* q;         // bf16 raster rows (the caller's q)
-  const void* k_packed;  // bf16 k*log2(e)/sqrt(D), 64-key blocks in MFMA A-operand order
-  const void* v_packed;  // bf16, 64-key blocks, transposed fragment order
+  const void* k;         // bf16 raster rows (the caller's k)
+  const void* vt;        // packed V^T fragments (launch_pack_v)
   void* out;             // bf16 raster rows (the caller's out)
   float* lse;            // fp32 raster (the caller's lse), or nullptr
   const int32_t* offsets;
   const int32_t* ids;
   const int32_t* work;
+  float q_scale;         // log2(e) / sqrt(D)
 };
 hipError_t launch_attention(const Geom& g, const FwdArgs& a, hipStream_t stream);
 

@@ -99,9 +99,11 @@ size_t sta_workspace_bytes(const sta_dims* dims, const int32_t* window_sizes,
  *             bytes, 256-byte aligned; contents on entry are ignored and on
  *             return are unspecified. Calls that share a workspace must be
  *             ordered on one stream.
- * Returns STA_OK once the four launches (K/V pack into tile-major MFMA
- * fragment order, schedule lists, work order, fused attention reading q and
- * writing out/lse in raster order) are enqueued on `stream`.
+ * Returns STA_OK once the four launches (V^T pack into tile-major MFMA
+ * fragment order, schedule lists, work order, fused attention reading q and k
+ * and writing out/lse in raster order, all through the tile map) are
+ * enqueued on `stream`. The workspace holds the packed V^T (the size of v)
+ * and the schedule (a few MB at most).
  */
 sta_status sta_forward(const sta_dims* dims, const void* q, const void* k,
                        const void* v, const int32_t* window_sizes,
@@ -113,7 +115,7 @@ sta_status sta_forward(const sta_dims* dims, const void* q, const void* k,
  * sta_forward with stage timing, for measurement. `events` holds
  * STA_TIMED_EVENTS hipEvent_t handles (as void*, created by the caller);
  * events[0] is recorded on `stream` before the first launch and events[i]
- * after launch i of: 1 pack k/v, 2 schedule lists, 3 work order,
+ * after launch i of: 1 pack v, 2 schedule lists, 3 work order,
  * 4 fused attention. hipEventElapsedTime between consecutive events then
  * gives each kernel's duration. Nothing else differs from sta_forward;
  * STA_ERR_NULL if events or an entry is NULL.

@@ -123,7 +123,7 @@ def test_sizes(lib, B, heads, D, video, windows, text):
     def up(x):
         return (x + 255) // 256 * 256
     tensor = B * heads * S * D * 2
-    expect = 2 * up(tensor) + up(n_off * 4) + up(n_ids * 4) + up(n_work * 4)
+    expect = up(tensor) + up(n_off * 4) + up(n_ids * 4) + up(n_work * 4)
     assert sta.sta_workspace_bytes(d, windows, text) == expect
 
 
