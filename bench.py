@@ -49,21 +49,24 @@ def source_sha() -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def measured_traffic():
+def measured_traffic(workload: str):
     """HBM bytes per attention launch from the committed rocprofv3 counter summary.
 
-    Returns None when there is no summary or the kernel source changed since
-    the counters were taken.
+    Returns None when there is no summary, when it was taken on another
+    workload, or when the kernel source changed since the counters were taken.
     """
     if not os.path.exists(PMC_SUMMARY):
         return None
     vals = {}
+    summary_workload = None
     with open(PMC_SUMMARY) as f:
         for line in f:
-            if ":" in line:
+            if line.startswith("#") and "workload " in line and summary_workload is None:
+                summary_workload = line.rsplit("workload ", 1)[1].strip()
+            elif ":" in line:
                 key, _, val = line.partition(":")
                 vals[key.strip()] = val.strip()
-    if vals.get("kernel_source_sha256_16") != source_sha():
+    if summary_workload != workload or vals.get("kernel_source_sha256_16") != source_sha():
         return None
     try:
         return float(vals["hbm_bytes_per_launch"])
@@ -177,7 +180,7 @@ def main():
     tflops = flops / (ms_per_step * 1e-3) / 1e12
     attn_ms = stage_ms["attention"]
     attn_tflops = flops / (attn_ms * 1e-3) / 1e12
-    traffic = measured_traffic()
+    traffic = measured_traffic(args.workload)
     result = {
         "metric": METRIC,
         "value": tflops,
