@@ -68,6 +68,7 @@ constexpr int kThreads = kWaves * 64;
 constexpr int kRowsPerWave = kUnitRows / kWaves;  // 48
 constexpr int kQT = kRowsPerWave / 16;            // 3 query column groups per wave
 constexpr float kRescaleSlack = 8.0f;             // log2 units
+constexpr int kKPrefetch = 4;                     // K fragments in flight in the score loop
 constexpr float kLn2 = 0.69314718055994530942f;
 
 __device__ inline float swap16_max(float x) {
@@ -257,16 +258,25 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(Geom g, FwdA
       f32x4 seed[kQT];
 #pragma unroll
       for (int c = 0; c < kQT; ++c) seed[c] = f32x4{-m_run[c], -m_run[c], -m_run[c], -m_run[c]};
+      // K fragment f = 4 ks + kt feeds kQT MFMAs; kKPrefetch fragments are kept
+      // in flight (the compiler's own choice, about two, leaves the MFMAs
+      // waiting on LDS), and the order is fenced so it stays that way.
+      constexpr int NF = 4 * KS;
+      bf16x8 kf[NF];
+      auto kload = [&](int f) {
+        kf[f] = *reinterpret_cast<const bf16x8*>(kb + kofs + (f & 3) * 16 * ROWB + (f >> 2) * 64 * RPI);
+      };
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
+      for (int f = 0; f < kKPrefetch; ++f) kload(f);
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
-          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kb + kofs + kt * 16 * ROWB + ks * 64 * RPI);
+      for (int f = 0; f < NF; ++f) {
+        const int ks = f >> 2, kt = f & 3;
 #pragma unroll
-          for (int c = 0; c < kQT; ++c)
-            s[c][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[c][ks],
-                                                                ks == 0 ? seed[c] : s[c][kt], 0, 0, 0);
-        }
+        for (int c = 0; c < kQT; ++c)
+          s[c][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[f], qf[c][ks],
+                                                              ks == 0 ? seed[c] : s[c][kt], 0, 0, 0);
+        if (f + kKPrefetch < NF) kload(f + kKPrefetch);
+        __builtin_amdgcn_sched_barrier(0);
       }
       // mask the padded keys of the last, ragged text block
       if (ragged && j == n_blk - 1) {
