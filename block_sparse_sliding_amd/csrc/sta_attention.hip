@@ -27,21 +27,21 @@
 // address is one per-lane base plus compile-time offsets.
 //
 // Per block and wave, with v_mfma_f32_16x16x32_bf16:
-//   S^T - m = K (Q c)^T - m
-//                 A = K fragment (lane l holds K[16kt + l%16][32ks + 8(l/16)
-//                 .. +8]), B = Q^T fragment (registers, loaded once per unit
-//                 and pre-scaled by c = log2(e)/sqrt(D)), accumulator seeded
-//                 with -m, the running reference max. Lane l then holds s - m
-//                 of query l%16 for keys 4(l/16) + r of each 16-key group,
-//                 already in the log2 domain.
-//   softmax       p = 2^(s - m) straight from the MFMA output (one v_exp_f32
-//                 per score). The reference only moves when some score
-//                 exceeds it by more than kRescaleSlack (a per-lane v_max3
-//                 check and a ballot); then the accumulator is rescaled and
-//                 the block's scores are recomputed from the new seed. The
-//                 first block always sets the reference from its exact row
-//                 max. Any reference gives the same softmax; the slack
-//                 bounds p by 2^slack.
+//   S^T = K Q^T   A = K fragment (lane l holds K[16kt + l%16][32ks + 8(l/16)
+//                 .. +8]), B = Q^T fragment (registers, loaded once per unit),
+//                 fp32 accumulation of the exact bf16 products. Lane l then
+//                 holds the scores of query l%16 for keys 4(l/16) + r of each
+//                 16-key group.
+//   softmax       p = 2^(c s - m) with c = log2(e)/sqrt(D) applied in fp32
+//                 (one v_fma_f32 and one v_exp_f32 per score; folding c into
+//                 a bf16 operand instead would round it and cost accuracy at
+//                 large logits), m the running reference in log2 units. The
+//                 reference only moves when some scaled score exceeds it by
+//                 more than kRescaleSlack (a per-lane v_max3 check and a
+//                 ballot); then the accumulator and row sums are rescaled.
+//                 The first block sets the reference from its exact row max.
+//                 Any reference gives the same softmax; the slack bounds p by
+//                 2^slack.
 //   O^T += V^T P^T  A = packed V^T fragment (one ds_read_b128; its key order
 //                 matches the accumulator layout of S^T), B = P^T from the
 //                 lane's own registers after bf16 rounding. The row sums
@@ -197,9 +197,8 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(Geom g, FwdA
 
   // Q^T fragments for this wave's 48 rows, read from the caller's raster q
   // (row r of the unit is tile-major row q_row0 + r; rows past the unit are
-  // clamped to a valid row and their results discarded), pre-scaled by
-  // log2(e)/sqrt(D) so the MFMA yields scores in the log2 domain.
-  const float qs = a.q_scale;
+  // clamped to a valid row and their results discarded).
+  const float qs = a.q_scale;  // log2(e)/sqrt(D), applied to the fp32 scores
   bf16x8 qf[kQT][KS];
 #pragma unroll
   for (int c = 0; c < kQT; ++c) {
@@ -208,15 +207,12 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(Geom g, FwdA
     const int rr = tiled_to_raster(q_row0 + row, g);
     const bf16x8* src = reinterpret_cast<const bf16x8*>(qr + size_t(rr) * D + (lane >> 4) * 8);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const f32x8 x = __builtin_convertvector(src[ks * 4], f32x8);
-      qf[c][ks] = __builtin_convertvector(x * qs, bf16x8);
-    }
+    for (int ks = 0; ks < KS; ++ks) qf[c][ks] = src[ks * 4];
   }
 
   f32x4 acc[kQT][DT];
   float l_part[kQT];  // this lane's share of the row sum of p
-  float m_run[kQT];   // reference max (log2 units); -m seeds the S^T accumulator
+  float m_run[kQT];   // reference max of the scaled scores (log2 units)
 #pragma unroll
   for (int c = 0; c < kQT; ++c) {
 #pragma unroll
@@ -247,20 +243,10 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(Geom g, FwdA
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
 
-    // ---- S^T - m = K (Q c)^T - m: the running max enters as the accumulator
-    // seed. When the reference must move (always on the first block, rarely
-    // later: some score exceeds it by more than the slack), the reference is
-    // updated and the block's scores are recomputed from the new seed, so the
-    // score registers are only ever written by the MFMAs (and the mask).
+    // ---- raw scores S^T = K Q^T (fp32); p = 2^(c s - m) below
     const char* kb = lds[stage][0];
     f32x4 s[kQT][4];
-    auto scores = [&]() {
-      f32x4 seed[kQT];
-#pragma unroll
-      for (int c = 0; c < kQT; ++c) seed[c] = f32x4{-m_run[c], -m_run[c], -m_run[c], -m_run[c]};
-      // K fragment f = 4 ks + kt feeds kQT MFMAs; kKPrefetch fragments are kept
-      // in flight (the compiler's own choice, about two, leaves the MFMAs
-      // waiting on LDS), and the order is fenced so it stays that way.
+    {
       constexpr int NF = 4 * KS;
       bf16x8 kf[NF];
       auto kload = [&](int f) {
@@ -274,11 +260,10 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(Geom g, FwdA
 #pragma unroll
         for (int c = 0; c < kQT; ++c)
           s[c][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[f], qf[c][ks],
-                                                              ks == 0 ? seed[c] : s[c][kt], 0, 0, 0);
+                                                              ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : s[c][kt], 0, 0, 0);
         if (f + kKPrefetch < NF) kload(f + kKPrefetch);
         __builtin_amdgcn_sched_barrier(0);
       }
-      // mask the padded keys of the last, ragged text block
       if (ragged && j == n_blk - 1) {
         const int key0 = (j - n_vid) * kKeyBlock + 4 * (lane >> 4);
 #pragma unroll
@@ -289,12 +274,11 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(Geom g, FwdA
 #pragma unroll
               for (int c = 0; c < kQT; ++c) s[c][kt][r] = -INFINITY;
       }
-    };
-    scores();
-    // the next block streams in while this one is finished (its stage was
-    // released by every wave at the barrier above)
+    }
     if (j + 1 < n_blk) issue(j + 1, stage ^ 1);
-    // per-lane max of s - m; the reference moves only past the slack
+    // per-lane max of the scaled scores; the reference moves only past the
+    // slack, and then only m, l and the accumulator change (the scores are
+    // raw, so nothing is recomputed)
     float lm[kQT];
     bool need = false;
 #pragma unroll
@@ -306,8 +290,8 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(Geom g, FwdA
       x = fmaxf(fmaxf(x, s[c][2][1]), s[c][2][2]);
       x = fmaxf(fmaxf(x, s[c][2][3]), s[c][3][0]);
       x = fmaxf(fmaxf(x, s[c][3][1]), s[c][3][2]);
-      lm[c] = fmaxf(x, s[c][3][3]);
-      need |= lm[c] > kRescaleSlack;
+      lm[c] = fmaxf(x, s[c][3][3]) * qs;
+      need |= lm[c] - m_run[c] > kRescaleSlack;
     }
     const bool first = j == 0;
     if (first || __builtin_amdgcn_ballot_w64(need) != 0) {
@@ -317,21 +301,17 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(Geom g, FwdA
         const float mx = swap32_max(swap16_max(lm[c]));
         if (first) {
           m_run[c] = mx;  // nothing accumulated yet
-        } else {
-          const float delta = mx > 0.f ? mx : 0.f;
-          const float alpha = __builtin_amdgcn_exp2f(-delta);
-          m_run[c] += delta;
+        } else if (mx > m_run[c]) {
+          const float alpha = __builtin_amdgcn_exp2f(m_run[c] - mx);
+          m_run[c] = mx;
           l_part[c] *= alpha;
 #pragma unroll
           for (int d = 0; d < DT; ++d) acc[c][d] *= alpha;
         }
       }
-      // re-read the K fragments rather than keep the first reads live
-      asm volatile("" ::: "memory");
-      scores();  // a recomputed block never moves the reference again
     }
 
-    // ---- p = 2^(s - m) rounded to bf16; O^T += V^T P^T; row sums += 1^T P^T
+    // ---- p = 2^(c s - m) rounded to bf16; O^T += V^T P^T; row sums += 1^T P^T
     const bf16x8* vl = reinterpret_cast<const bf16x8*>(lds[stage][1]);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -341,8 +321,8 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(Geom g, FwdA
         f32x8 p;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          p[r] = __builtin_amdgcn_exp2f(s[c][2 * h][r]);
-          p[4 + r] = __builtin_amdgcn_exp2f(s[c][2 * h + 1][r]);
+          p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[c][2 * h][r], qs, -m_run[c]));
+          p[4 + r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[c][2 * h + 1][r], qs, -m_run[c]));
         }
         pb[c] = __builtin_convertvector(p, bf16x8);
         // row sum of the rounded p, two at a time

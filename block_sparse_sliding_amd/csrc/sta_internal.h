@@ -82,7 +82,7 @@ struct FwdArgs {
   const int32_t* offsets;
   const int32_t* ids;
   const int32_t* work;
-  float q_scale;         // log2(e) / sqrt(D)
+  float q_scale;         // log2(e) / sqrt(D), applied to the fp32 scores
 };
 hipError_t launch_attention(const Geom& g, const FwdArgs& a, hipStream_t stream);
 

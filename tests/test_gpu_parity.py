@@ -49,6 +49,44 @@ SMALL = [
 ]
 
 
+# Large score jumps: keys of some tiles (and the valid text keys) are scaled so
+# that later key blocks hold scores far above the running reference (tens to
+# hundreds of log2 units), which forces the online softmax to move its
+# reference mid-stream, also in the last, ragged text block. Factors < 1
+# give near-zero scores. Random N(0, 1) inputs never exercise this.
+JUMPS = [
+    # (D, video, windows, text_length, {key tile (tt, th, tw): factor}, text factor)
+    (128, (18, 24, 32), [(3, 3, 3), (2, 2, 2)], 100,
+     {(1, 1, 2): 2.5, (2, 2, 3): 4.0, (0, 0, 0): 0.05}, 3.5),
+    (64, (18, 24, 32), [(3, 3, 3)], 37, {(2, 1, 1): 3.0, (0, 2, 3): 4.0}, 3.5),
+]
+
+
+def scale_key_tiles(k, video, factors, text_factor, ell):
+    B, heads, S, D = k.shape
+    T, H, W = video
+    nv = T * H * W
+    kk = k.float().clone()
+    kv = kk[:, :, :nv].view(B, heads, T, H, W, D)
+    for (tt, th, tw), f in factors.items():
+        kv[:, :, 6 * tt:6 * tt + 6, 8 * th:8 * th + 8, 8 * tw:8 * tw + 8] *= f
+    kk[:, :, nv:nv + ell] *= text_factor
+    return kk.to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("case", JUMPS, ids=[f"j{i}" for i in range(len(JUMPS))])
+def test_large_score_jumps(case):
+    D, video, windows, ell, factors, text_factor = case
+    heads = len(windows)
+    S = video[0] * video[1] * video[2] + 256
+    note(f"score jumps {case}")
+    q, k, v = qkv(1, heads, S, D, 900 + D + ell)
+    k = scale_key_tiles(k, video, factors, text_factor, ell)
+    out, lse = run_sta(q, k, v, windows, ell, True, video)
+    ro, rl = oracle_rows(q, k, v, windows, ell, True, video)
+    compare(out, lse, ro, rl, label=f"jumps D={D}")
+
+
 @pytest.mark.parametrize("case", SMALL, ids=[f"s{i}" for i in range(len(SMALL))])
 def test_small_all_rows(case):
     B, heads, D, video, windows, ell, text = case
