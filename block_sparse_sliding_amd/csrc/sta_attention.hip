@@ -7,9 +7,9 @@
 // per-element mask; only the last text block is masked, and only when the text
 // length is not a multiple of 64.
 //
-// Work decomposition. One workgroup = one query unit: a 384-row query tile
-// (or the 256 text query slots of one head), 8 waves of 48 rows each (three
-// 16-row column groups), two waves per SIMD. Q rows are read from the
+// Work decomposition. One workgroup = one query unit: a 384-row query tile, 8
+// waves of 48 rows each (three 16-row column groups), or the 256 text query
+// slots of one head, 8 waves of 32 rows each; two waves per SIMD. Q rows are read from the
 // caller's raster q through the tile map, and O / lse are written back to
 // raster positions. Keys stream in 64-key blocks into LDS with LDS-DMA loads,
 // double buffered, one barrier per block: K straight from the caller's raster
@@ -50,6 +50,8 @@
 // their scores are replaced by -inf (a select, so whatever k holds there is
 // ignored) and their packed V rows are zeros.
 // Epilogue: O = O^T / l rounded to bf16, lse = (m + log2 l) * ln 2, at raster rows.
+#include <type_traits>
+
 #include "sta_internal.h"
 
 namespace sta {
@@ -195,172 +197,183 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(Geom g, FwdA
     }
   };
 
-  // Q^T fragments for this wave's 48 rows, read from the caller's raster q
-  // (row r of the unit is tile-major row q_row0 + r; rows past the unit are
-  // clamped to a valid row and their results discarded).
-  const float qs = a.q_scale;  // log2(e)/sqrt(D), applied to the fp32 scores
-  bf16x8 qf[kQT][KS];
-#pragma unroll
-  for (int c = 0; c < kQT; ++c) {
-    int row = wave * kRowsPerWave + c * 16 + (lane & 15);
-    row = row < q_rows ? row : q_rows - 1;
-    const int rr = tiled_to_raster(q_row0 + row, g);
-    const bf16x8* src = reinterpret_cast<const bf16x8*>(qr + size_t(rr) * D + (lane >> 4) * 8);
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qf[c][ks] = src[ks * 4];
-  }
-
-  f32x4 acc[kQT][DT];
-  float l_part[kQT];  // this lane's share of the row sum of p
-  float m_run[kQT];   // reference max of the scaled scores (log2 units)
-#pragma unroll
-  for (int c = 0; c < kQT; ++c) {
-#pragma unroll
-    for (int d = 0; d < DT; ++d) acc[c][d] = f32x4{0.f, 0.f, 0.f, 0.f};
-    l_part[c] = 0.f;
-    m_run[c] = 0.f;
-  }
-  bf16x2 ones2;
-  ones2[0] = (__bf16)1.0f;
-  ones2[1] = (__bf16)1.0f;
-
-  // K fragment (row 16kt + lane%16, chunk 4ks + lane/16) of a block sits at
-  // kofs + kt * 16 * ROWB + ks * 64 * RPI; V^T fragment (h, dt) at
-  // (h * DT + dt) * 1024 + lane * 16.
-  const int l15 = lane & 15;
-  const int kofs = (l15 / RPI) * 1024 + (l15 % RPI) * 64 + (((lane >> 4) ^ sw(l15)) << 4);
-
-  auto issue = [&](int j, int st) {
-    int kbase, krs, vrow;
-    block_rows(j, kbase, krs, vrow);
-    issue_k(st, kbase, krs);
-    issue_v(st, vrow);
-  };
-
-  issue(0, 0);
-  for (int j = 0; j < n_blk; ++j) {
-    const int stage = j & 1;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-
-    // ---- raw scores S^T = K Q^T (fp32); p = 2^(c s - m) below
-    const char* kb = lds[stage][0];
-    f32x4 s[kQT][4];
-    {
-      constexpr int NF = 4 * KS;
-      bf16x8 kf[NF];
-      auto kload = [&](int f) {
-        kf[f] = *reinterpret_cast<const bf16x8*>(kb + kofs + (f & 3) * 16 * ROWB + (f >> 2) * 64 * RPI);
-      };
-#pragma unroll
-      for (int f = 0; f < kKPrefetch; ++f) kload(f);
-#pragma unroll
-      for (int f = 0; f < NF; ++f) {
-        const int ks = f >> 2, kt = f & 3;
-#pragma unroll
-        for (int c = 0; c < kQT; ++c)
-          s[c][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[f], qf[c][ks],
-                                                              ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : s[c][kt], 0, 0, 0);
-        if (f + kKPrefetch < NF) kload(f + kKPrefetch);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      if (ragged && j == n_blk - 1) {
-        const int key0 = (j - n_vid) * kKeyBlock + 4 * (lane >> 4);
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (key0 + 16 * kt + r >= text_len)
-#pragma unroll
-              for (int c = 0; c < kQT; ++c) s[c][kt][r] = -INFINITY;
-      }
-    }
-    if (j + 1 < n_blk) issue(j + 1, stage ^ 1);
-    // per-lane max of the scaled scores; the reference moves only past the
-    // slack, and then only m, l and the accumulator change (the scores are
-    // raw, so nothing is recomputed)
-    float lm[kQT];
-    bool need = false;
-#pragma unroll
-    for (int c = 0; c < kQT; ++c) {
-      float x = fmaxf(fmaxf(s[c][0][0], s[c][0][1]), s[c][0][2]);
-      x = fmaxf(fmaxf(x, s[c][0][3]), s[c][1][0]);
-      x = fmaxf(fmaxf(x, s[c][1][1]), s[c][1][2]);
-      x = fmaxf(fmaxf(x, s[c][1][3]), s[c][2][0]);
-      x = fmaxf(fmaxf(x, s[c][2][1]), s[c][2][2]);
-      x = fmaxf(fmaxf(x, s[c][2][3]), s[c][3][0]);
-      x = fmaxf(fmaxf(x, s[c][3][1]), s[c][3][2]);
-      lm[c] = fmaxf(x, s[c][3][3]) * qs;
-      need |= lm[c] - m_run[c] > kRescaleSlack;
-    }
-    const bool first = j == 0;
-    if (first || __builtin_amdgcn_ballot_w64(need) != 0) {
-#pragma unroll
-      for (int c = 0; c < kQT; ++c) {
-        // exact row max across the 4 lanes holding this query
-        const float mx = swap32_max(swap16_max(lm[c]));
-        if (first) {
-          m_run[c] = mx;  // nothing accumulated yet
-        } else if (mx > m_run[c]) {
-          const float alpha = __builtin_amdgcn_exp2f(m_run[c] - mx);
-          m_run[c] = mx;
-          l_part[c] *= alpha;
-#pragma unroll
-          for (int d = 0; d < DT; ++d) acc[c][d] *= alpha;
-        }
-      }
-    }
-
-    // ---- p = 2^(c s - m) rounded to bf16; O^T += V^T P^T; row sums += 1^T P^T
-    const bf16x8* vl = reinterpret_cast<const bf16x8*>(lds[stage][1]);
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      bf16x8 pb[kQT];
-#pragma unroll
-      for (int c = 0; c < kQT; ++c) {
-        f32x8 p;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[c][2 * h][r], qs, -m_run[c]));
-          p[4 + r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[c][2 * h + 1][r], qs, -m_run[c]));
-        }
-        pb[c] = __builtin_convertvector(p, bf16x8);
-        // row sum of the rounded p, two at a time
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const bf16x2 pair = {pb[c][2 * i], pb[c][2 * i + 1]};
-          l_part[c] = __builtin_amdgcn_fdot2_f32_bf16(pair, ones2, l_part[c], false);
-        }
-      }
-#pragma unroll
-      for (int d = 0; d < DT; ++d) {
-        const bf16x8 vf = vl[(h * DT + d) * 64 + lane];
-#pragma unroll
-        for (int c = 0; c < kQT; ++c)
-          acc[c][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[c], acc[c][d], 0, 0, 0);
-      }
-    }
-  }
-
-  // ---- epilogue: O = O^T / l in bf16 and lse, straight to raster positions
-  __bf16* __restrict__ outr = reinterpret_cast<__bf16*>(a.out) + slab;
-  float* __restrict__ lser = a.lse == nullptr ? nullptr : a.lse + size_t(bh) * g.S;
-#pragma unroll
-  for (int c = 0; c < kQT; ++c) {
-    const float l = swap32_sum(swap16_sum(l_part[c]));
-    const float inv = __builtin_amdgcn_rcpf(l);
-    const int row = wave * kRowsPerWave + c * 16 + (lane & 15);
-    if (row < q_rows) {
+  // The rest runs with QT query column groups per wave: 3 (8 x 48 = 384 rows)
+  // for a video tile, 2 (8 x 32 = 256 rows) for the text query slots, so no
+  // wave works on rows past the unit.
+  auto run = [&](auto qt_c) {
+    constexpr int QT = decltype(qt_c)::value;
+    constexpr int RPW = QT * 16;  // query rows per wave
+    // Q^T fragments for this wave's RPW rows, read from the caller's raster q
+    // (row r of the unit is tile-major row q_row0 + r; rows past the unit are
+    // clamped to a valid row and their results discarded).
+    const float qs = a.q_scale;  // log2(e)/sqrt(D), applied to the fp32 scores
+    bf16x8 qf[QT][KS];
+  #pragma unroll
+    for (int c = 0; c < QT; ++c) {
+      int row = wave * RPW + c * 16 + (lane & 15);
+      row = row < q_rows ? row : q_rows - 1;
       const int rr = tiled_to_raster(q_row0 + row, g);
-      __bf16* dst = outr + size_t(rr) * D + (lane >> 4) * 4;
-#pragma unroll
-      for (int d = 0; d < DT; ++d) {
-        const f32x4 o = acc[c][d] * inv;
-        *reinterpret_cast<bf16x4*>(dst + d * 16) = __builtin_convertvector(o, bf16x4);
-      }
-      if (lser != nullptr && lane < 16) lser[rr] = (m_run[c] + __builtin_amdgcn_logf(l)) * kLn2;
+      const bf16x8* src = reinterpret_cast<const bf16x8*>(qr + size_t(rr) * D + (lane >> 4) * 8);
+  #pragma unroll
+      for (int ks = 0; ks < KS; ++ks) qf[c][ks] = src[ks * 4];
     }
-  }
+
+    f32x4 acc[QT][DT];
+    float l_part[QT];  // this lane's share of the row sum of p
+    float m_run[QT];   // reference max of the scaled scores (log2 units)
+  #pragma unroll
+    for (int c = 0; c < QT; ++c) {
+  #pragma unroll
+      for (int d = 0; d < DT; ++d) acc[c][d] = f32x4{0.f, 0.f, 0.f, 0.f};
+      l_part[c] = 0.f;
+      m_run[c] = 0.f;
+    }
+    bf16x2 ones2;
+    ones2[0] = (__bf16)1.0f;
+    ones2[1] = (__bf16)1.0f;
+
+    // K fragment (row 16kt + lane%16, chunk 4ks + lane/16) of a block sits at
+    // kofs + kt * 16 * ROWB + ks * 64 * RPI; V^T fragment (h, dt) at
+    // (h * DT + dt) * 1024 + lane * 16.
+    const int l15 = lane & 15;
+    const int kofs = (l15 / RPI) * 1024 + (l15 % RPI) * 64 + (((lane >> 4) ^ sw(l15)) << 4);
+
+    auto issue = [&](int j, int st) {
+      int kbase, krs, vrow;
+      block_rows(j, kbase, krs, vrow);
+      issue_k(st, kbase, krs);
+      issue_v(st, vrow);
+    };
+
+    issue(0, 0);
+    for (int j = 0; j < n_blk; ++j) {
+      const int stage = j & 1;
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+
+      // ---- raw scores S^T = K Q^T (fp32); p = 2^(c s - m) below
+      const char* kb = lds[stage][0];
+      f32x4 s[QT][4];
+      {
+        constexpr int NF = 4 * KS;
+        bf16x8 kf[NF];
+        auto kload = [&](int f) {
+          kf[f] = *reinterpret_cast<const bf16x8*>(kb + kofs + (f & 3) * 16 * ROWB + (f >> 2) * 64 * RPI);
+        };
+  #pragma unroll
+        for (int f = 0; f < kKPrefetch; ++f) kload(f);
+  #pragma unroll
+        for (int f = 0; f < NF; ++f) {
+          const int ks = f >> 2, kt = f & 3;
+  #pragma unroll
+          for (int c = 0; c < QT; ++c)
+            s[c][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[f], qf[c][ks],
+                                                                ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : s[c][kt], 0, 0, 0);
+          if (f + kKPrefetch < NF) kload(f + kKPrefetch);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if (ragged && j == n_blk - 1) {
+          const int key0 = (j - n_vid) * kKeyBlock + 4 * (lane >> 4);
+  #pragma unroll
+          for (int kt = 0; kt < 4; ++kt)
+  #pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (key0 + 16 * kt + r >= text_len)
+  #pragma unroll
+                for (int c = 0; c < QT; ++c) s[c][kt][r] = -INFINITY;
+        }
+      }
+      if (j + 1 < n_blk) issue(j + 1, stage ^ 1);
+      // per-lane max of the scaled scores; the reference moves only past the
+      // slack, and then only m, l and the accumulator change (the scores are
+      // raw, so nothing is recomputed)
+      float lm[QT];
+      bool need = false;
+  #pragma unroll
+      for (int c = 0; c < QT; ++c) {
+        float x = fmaxf(fmaxf(s[c][0][0], s[c][0][1]), s[c][0][2]);
+        x = fmaxf(fmaxf(x, s[c][0][3]), s[c][1][0]);
+        x = fmaxf(fmaxf(x, s[c][1][1]), s[c][1][2]);
+        x = fmaxf(fmaxf(x, s[c][1][3]), s[c][2][0]);
+        x = fmaxf(fmaxf(x, s[c][2][1]), s[c][2][2]);
+        x = fmaxf(fmaxf(x, s[c][2][3]), s[c][3][0]);
+        x = fmaxf(fmaxf(x, s[c][3][1]), s[c][3][2]);
+        lm[c] = fmaxf(x, s[c][3][3]) * qs;
+        need |= lm[c] - m_run[c] > kRescaleSlack;
+      }
+      const bool first = j == 0;
+      if (first || __builtin_amdgcn_ballot_w64(need) != 0) {
+  #pragma unroll
+        for (int c = 0; c < QT; ++c) {
+          // exact row max across the 4 lanes holding this query
+          const float mx = swap32_max(swap16_max(lm[c]));
+          if (first) {
+            m_run[c] = mx;  // nothing accumulated yet
+          } else if (mx > m_run[c]) {
+            const float alpha = __builtin_amdgcn_exp2f(m_run[c] - mx);
+            m_run[c] = mx;
+            l_part[c] *= alpha;
+  #pragma unroll
+            for (int d = 0; d < DT; ++d) acc[c][d] *= alpha;
+          }
+        }
+      }
+
+      // ---- p = 2^(c s - m) rounded to bf16; O^T += V^T P^T; row sums += 1^T P^T
+      const bf16x8* vl = reinterpret_cast<const bf16x8*>(lds[stage][1]);
+  #pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        bf16x8 pb[QT];
+  #pragma unroll
+        for (int c = 0; c < QT; ++c) {
+          f32x8 p;
+  #pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[c][2 * h][r], qs, -m_run[c]));
+            p[4 + r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[c][2 * h + 1][r], qs, -m_run[c]));
+          }
+          pb[c] = __builtin_convertvector(p, bf16x8);
+          // row sum of the rounded p, two at a time
+  #pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const bf16x2 pair = {pb[c][2 * i], pb[c][2 * i + 1]};
+            l_part[c] = __builtin_amdgcn_fdot2_f32_bf16(pair, ones2, l_part[c], false);
+          }
+        }
+  #pragma unroll
+        for (int d = 0; d < DT; ++d) {
+          const bf16x8 vf = vl[(h * DT + d) * 64 + lane];
+  #pragma unroll
+          for (int c = 0; c < QT; ++c)
+            acc[c][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[c], acc[c][d], 0, 0, 0);
+        }
+      }
+    }
+
+    // ---- epilogue: O = O^T / l in bf16 and lse, straight to raster positions
+    __bf16* __restrict__ outr = reinterpret_cast<__bf16*>(a.out) + slab;
+    float* __restrict__ lser = a.lse == nullptr ? nullptr : a.lse + size_t(bh) * g.S;
+  #pragma unroll
+    for (int c = 0; c < QT; ++c) {
+      const float l = swap32_sum(swap16_sum(l_part[c]));
+      const float inv = __builtin_amdgcn_rcpf(l);
+      const int row = wave * RPW + c * 16 + (lane & 15);
+      if (row < q_rows) {
+        const int rr = tiled_to_raster(q_row0 + row, g);
+        __bf16* dst = outr + size_t(rr) * D + (lane >> 4) * 4;
+  #pragma unroll
+        for (int d = 0; d < DT; ++d) {
+          const f32x4 o = acc[c][d] * inv;
+          *reinterpret_cast<bf16x4*>(dst + d * 16) = __builtin_convertvector(o, bf16x4);
+        }
+        if (lser != nullptr && lane < 16) lser[rr] = (m_run[c] + __builtin_amdgcn_logf(l)) * kLn2;
+      }
+    }
+  };
+  if (text_unit)
+    run(std::integral_constant<int, kTextSlots / 16 / kWaves>{});
+  else
+    run(std::integral_constant<int, kQT>{});
 }
 
 }  // namespace
