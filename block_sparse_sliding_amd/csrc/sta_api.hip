@@ -78,7 +78,7 @@ sta_status make_windows(const Geom& g, const int32_t* ws, Windows* win, int64_t*
 }
 
 struct Carve {
-  size_t vt, offsets, ids, work, total;
+  size_t vt, offsets, ids, work, claim, total;
 };
 
 Carve carve(const Geom& g, int64_t n_ids) {
@@ -89,6 +89,7 @@ Carve carve(const Geom& g, int64_t n_ids) {
   c.offsets = at; at = align_up(at + (size_t(g.heads) * g.n_q + 1) * 4);
   c.ids = at; at = align_up(at + size_t(n_ids) * 4);
   c.work = at; at = align_up(at + size_t(g.B) * g.heads * g.n_q * 4);
+  c.claim = at; at = align_up(at + size_t(sta::kClaimInts) * 4);
   c.total = at;
   return c;
 }
@@ -166,7 +167,7 @@ sta_status sta_build_schedule(const sta_dims* dims, const int32_t* window_sizes,
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   st = hip_status(sta::launch_schedule_lists(g, win, offsets, ids, s));
   if (st != STA_OK) return st;
-  return hip_status(sta::launch_schedule_work(g, win, work, s));
+  return hip_status(sta::launch_schedule_work(g, win, work, nullptr, s));
 }
 
 sta_status sta_tile_gather(const sta_dims* dims, int32_t has_text, const void* x_raster,
@@ -238,6 +239,7 @@ sta_status forward_impl(const sta_dims* dims, const void* q, const void* k, cons
   int32_t* offsets = reinterpret_cast<int32_t*>(ws + c.offsets);
   int32_t* ids = reinterpret_cast<int32_t*>(ws + c.ids);
   int32_t* work = reinterpret_cast<int32_t*>(ws + c.work);
+  int32_t* claim = reinterpret_cast<int32_t*>(ws + c.claim);
 
   st = hip_status(sta::launch_pack_v(g, v, ws + c.vt, s));
   if (st == STA_OK) st = mark(1);
@@ -245,7 +247,7 @@ sta_status forward_impl(const sta_dims* dims, const void* q, const void* k, cons
   st = hip_status(sta::launch_schedule_lists(g, win, offsets, ids, s));
   if (st == STA_OK) st = mark(2);
   if (st != STA_OK) return st;
-  st = hip_status(sta::launch_schedule_work(g, win, work, s));
+  st = hip_status(sta::launch_schedule_work(g, win, work, claim, s));
   if (st == STA_OK) st = mark(3);
   if (st != STA_OK) return st;
   sta::FwdArgs a;
@@ -257,6 +259,7 @@ sta_status forward_impl(const sta_dims* dims, const void* q, const void* k, cons
   a.offsets = offsets;
   a.ids = ids;
   a.work = work;
+  a.claim = claim;
   a.q_scale = float(1.4426950408889634 / std::sqrt(double(g.D)));  // log2(e)/sqrt(D)
   st = hip_status(sta::launch_attention(g, a, s));
   if (st == STA_OK) st = mark(4);

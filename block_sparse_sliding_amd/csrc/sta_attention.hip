@@ -7,10 +7,15 @@
 // per-element mask; only the last text block is masked, and only when the text
 // length is not a multiple of 64.
 //
-// Work decomposition. One workgroup = one query unit: a 384-row query tile, 8
-// waves of 48 rows each (three 16-row column groups), or the 256 text query
-// slots of one head, 8 waves of 32 rows each; two waves per SIMD. Q rows are read from the
-// caller's raster q through the tile map, and O / lse are written back to
+// Work decomposition. A workgroup works on one query unit at a time: a
+// 384-row query tile, 8 waves of 48 rows each (three 16-row column groups),
+// or the 256 text query slots of one head, 8 waves of 32 rows each; two waves
+// per SIMD, one workgroup per CU. The grid is persistent (one workgroup per
+// resident slot): each workgroup pops units from the queue of the XCD it runs
+// on and, once that queue is empty, from the other XCDs' queues, so the split
+// of work between XCDs follows their actual clocks (which differ by several
+// percent under load) instead of being fixed at launch. Q rows are read from
+// the caller's raster q through the tile map, and O / lse are written back to
 // raster positions. Keys stream in 64-key blocks into LDS with LDS-DMA loads,
 // double buffered, one barrier per block: K straight from the caller's raster
 // k (each lane supplies its own source address, which applies the tile map),
@@ -96,13 +101,46 @@ __device__ inline void dma16(const char* gsrc, char* lds_dst) {
   __builtin_amdgcn_global_load_lds(gsrc, (lds_void*)lds_dst, 16, 0, 0);
 }
 
+// Next query unit for a workgroup on XCD `xcd`, or -1 once every queue is
+// empty. Queue y holds work[8k + y], k < ceil((total - y) / 8); its head
+// claim[y * kClaimStride] counts the items taken (it may run past the end).
+// Each successful fetch-add hands out a distinct item, and a workgroup only
+// gets -1 after seeing every queue exhausted, so every unit is run exactly
+// once whatever the grid size.
+__device__ inline int claim_unit(const int32_t* work, int32_t* claim, int total, int xcd) {
+  for (int t = 0; t < kQueues; ++t) {
+    const int y = (xcd + t) & (kQueues - 1);
+    const int n_y = (total - y + kQueues - 1) / kQueues;
+    if (n_y <= 0) continue;
+    const int k = __hip_atomic_fetch_add(claim + y * kClaimStride, 1, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+    if (k < n_y) return work[kQueues * k + y];
+  }
+  return -1;
+}
+
 // floor(n / d) for n >= 0, d >= 1, n * d < 2^32, with m = ceil(2^32 / d) (see Geom).
 __device__ inline int div_by(int n, int d, uint32_t m) {
   return d == 1 ? n : int(__umulhi(uint32_t(n), m));
 }
 
+struct KernelArgs {
+  Geom g;
+  FwdArgs a;
+};
+
+// The kernel arguments seen through an opaque copy of the kernarg pointer:
+// loads through it cannot be hoisted out of the unit loop, so the per-unit
+// code reads them again (scalar loads) instead of keeping them all live in
+// SGPRs across the loop.
+__device__ inline const KernelArgs* kernel_args() {
+  auto kp = (const __attribute__((address_space(4))) KernelArgs*)__builtin_amdgcn_kernarg_segment_ptr();
+  asm volatile("" : "+s"(kp));
+  return (const KernelArgs*)kp;
+}
+
 template <int D>
-__global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(Geom g, FwdArgs a) {
+__global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(KernelArgs) {
   constexpr int KS = D / 32;                // k-steps of S^T
   constexpr int DT = D / 16;                // d groups of O^T
   constexpr int ROWB = D * 2;               // bytes per K row
@@ -114,8 +152,25 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(Geom g, FwdA
   __shared__ __attribute__((aligned(1024))) char lds[2][2][BLK];  // [stage][K|V]
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  const int unit = a.work[blockIdx.x];
+  __shared__ int claimed;
+  for (;;) {
+  // The previous unit's last LDS reads are behind the body's barriers; this
+  // barrier orders the claim (and the next unit's first LDS-DMA writes)
+  // after all of them.
+  if (threadIdx.x == 0) {
+    const KernelArgs* ka = kernel_args();
+    unsigned xcc;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+    claimed = claim_unit(ka->a.work, ka->a.claim, ka->g.B * ka->g.heads * ka->g.n_q, int(xcc));
+  }
+  __syncthreads();
+  const int unit = __builtin_amdgcn_readfirstlane(claimed);
+  if (unit < 0) break;
+  int lane = threadIdx.x & 63;
+  asm volatile("" : "+v"(lane));  // lane-derived offsets are rebuilt per unit, not kept live
+  const KernelArgs* ka = kernel_args();
+  const Geom g = ka->g;
+  const FwdArgs a = ka->a;
   const int u = unit % g.n_q;
   const int bh = unit / g.n_q;
   const int hd = bh % g.heads;
@@ -273,7 +328,8 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(Geom g, FwdA
           __builtin_amdgcn_sched_barrier(0);
         }
         if (ragged && j == n_blk - 1) {
-          const int key0 = (j - n_vid) * kKeyBlock + 4 * (lane >> 4);
+          int key0 = (j - n_vid) * kKeyBlock + 4 * (lane >> 4);
+          asm volatile("" : "+v"(key0));  // build the 16 lane masks here, not before the loop
   #pragma unroll
           for (int kt = 0; kt < 4; ++kt)
   #pragma unroll
@@ -374,16 +430,39 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(Geom g, FwdA
     run(std::integral_constant<int, kTextSlots / 16 / kWaves>{});
   else
     run(std::integral_constant<int, kQT>{});
+  }
+}
+
+// Resident workgroups of the kernel on the current device (cached per device).
+template <int D>
+int persistent_grid() {
+  static int cache[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  int* slot = dev < 64 ? &cache[dev] : nullptr;
+  int n = slot != nullptr ? __atomic_load_n(slot, __ATOMIC_RELAXED) : 0;
+  if (n > 0) return n;
+  int n_cu = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, sta_attention_kernel<D>, kThreads, 0) !=
+          hipSuccess)
+    return 0;
+  n = n_cu * (per_cu > 0 ? per_cu : 1);
+  if (slot != nullptr) __atomic_store_n(slot, n, __ATOMIC_RELAXED);
+  return n;
 }
 
 }  // namespace
 
 hipError_t launch_attention(const Geom& g, const FwdArgs& a, hipStream_t stream) {
   const int units = g.B * g.heads * g.n_q;
+  const int resident = g.D == 128 ? persistent_grid<128>() : persistent_grid<64>();
+  if (resident <= 0) return hipErrorInvalidDevice;
+  const int grid = units < resident ? units : resident;
   if (g.D == 128)
-    sta_attention_kernel<128><<<units, kThreads, 0, stream>>>(g, a);
+    sta_attention_kernel<128><<<grid, kThreads, 0, stream>>>(KernelArgs{g, a});
   else
-    sta_attention_kernel<64><<<units, kThreads, 0, stream>>>(g, a);
+    sta_attention_kernel<64><<<grid, kThreads, 0, stream>>>(KernelArgs{g, a});
   return hipGetLastError();
 }
 

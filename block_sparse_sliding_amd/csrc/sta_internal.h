@@ -70,8 +70,14 @@ hipError_t launch_rows_permute(const Geom& g, const void* src, void* dst, bool t
 hipError_t launch_pack_v(const Geom& g, const void* v, void* vt, hipStream_t stream);
 hipError_t launch_schedule_lists(const Geom& g, const Windows& win, int32_t* offsets,
                                  int32_t* ids, hipStream_t stream);
+// Work order (one query unit per entry, grouped into 8 per-XCD queues: queue x
+// holds entries 8k + x). `claim`, when not null, receives kClaimInts zeros:
+// the queue heads the attention kernel advances.
 hipError_t launch_schedule_work(const Geom& g, const Windows& win, int32_t* work,
-                                hipStream_t stream);
+                                int32_t* claim, hipStream_t stream);
+constexpr int kQueues = 8;        // one per XCD
+constexpr int kClaimStride = 64;  // ints between queue heads (own 256-byte line each)
+constexpr int kClaimInts = kQueues * kClaimStride;
 
 struct FwdArgs {
   const void* q;         // bf16 raster rows (the caller's q)
@@ -81,7 +87,8 @@ struct FwdArgs {
   float* lse;            // fp32 raster (the caller's lse), or nullptr
   const int32_t* offsets;
   const int32_t* ids;
-  const int32_t* work;
+  const int32_t* work;   // per-XCD queues of query units (launch_schedule_work)
+  int32_t* claim;        // queue heads, zeroed by launch_schedule_work
   float q_scale;         // log2(e) / sqrt(D), applied to the fp32 scores
 };
 hipError_t launch_attention(const Geom& g, const FwdArgs& a, hipStream_t stream);

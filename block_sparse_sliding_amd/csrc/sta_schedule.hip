@@ -58,19 +58,25 @@ __global__ __launch_bounds__(256) void schedule_lists_kernel(Geom g, Windows win
 
 constexpr int kWorkThreads = 256;
 constexpr int kMaxClasses = 2 * kMaxHeads;
-constexpr int kXcds = 8;  // workgroup i is dispatched to XCD i % 8
+constexpr int kXcds = kQueues;
+static_assert(kXcds == 8, "the queue index is the XCD id mod 8");
 
 // grid ceil(units / 256). Query units fall into classes of equal cost, one
-// per (head, video|text). Each XCD owns the workgroups i = 8k + x; its queue
-// (k = 0, 1, ...) takes, class by class in decreasing cost, an equal share
-// of every class: a contiguous run of that class's units (so the XCD's L2
-// serves neighbouring tiles), with the remainders of uneven classes rotated
-// over the XCDs. Heavy classes therefore spread evenly over the XCDs and run
-// first, and all XCDs work through the same head at about the same time.
+// per (head, video|text). Entry i = 8k + x is item k of XCD x's queue; each
+// queue takes, class by class in decreasing cost, an equal share of every
+// class: a contiguous run of that class's units (so the XCD's L2 serves
+// neighbouring tiles), with the remainders of uneven classes rotated over the
+// XCDs. Heavy classes therefore spread evenly over the XCDs and run first,
+// and all XCDs work through the same head at about the same time. The
+// attention kernel's workgroups pop their own XCD's queue and, once it is
+// empty, the other queues, so XCDs that run at a higher clock take more units.
 // Every workgroup rebuilds the small class table in LDS, then each thread
-// resolves one workgroup index to its query unit.
+// resolves one entry to its query unit; block 0 also zeroes the queue heads.
 __global__ __launch_bounds__(kWorkThreads) void schedule_work_kernel(Geom g, Windows win,
-                                                                     int32_t* __restrict__ work) {
+                                                                     int32_t* __restrict__ work,
+                                                                     int32_t* __restrict__ claim) {
+  if (claim != nullptr && blockIdx.x == 0)
+    for (int i = threadIdx.x; i < kClaimInts; i += kWorkThreads) claim[i] = 0;
   __shared__ long long cost[kMaxClasses];
   __shared__ int count[kMaxClasses];
   __shared__ int order[kMaxClasses];  // order[rank] = class
@@ -142,10 +148,10 @@ hipError_t launch_schedule_lists(const Geom& g, const Windows& win, int32_t* off
 }
 
 hipError_t launch_schedule_work(const Geom& g, const Windows& win, int32_t* work,
-                                hipStream_t stream) {
+                                int32_t* claim, hipStream_t stream) {
   const int total = g.B * g.heads * g.n_q;
   dim3 grid((total + kWorkThreads - 1) / kWorkThreads);
-  schedule_work_kernel<<<grid, kWorkThreads, 0, stream>>>(g, win, work);
+  schedule_work_kernel<<<grid, kWorkThreads, 0, stream>>>(g, win, work, claim);
   return hipGetLastError();
 }
 

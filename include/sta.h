@@ -102,8 +102,12 @@ size_t sta_workspace_bytes(const sta_dims* dims, const int32_t* window_sizes,
  * Returns STA_OK once the four launches (V^T pack into tile-major MFMA
  * fragment order, schedule lists, work order, fused attention reading q and k
  * and writing out/lse in raster order, all through the tile map) are
- * enqueued on `stream`. The workspace holds the packed V^T (the size of v)
- * and the schedule (a few MB at most).
+ * enqueued on `stream`. The workspace holds the packed V^T (the size of v),
+ * the schedule (a few MB at most) and 2 KB of work-queue heads. The attention
+ * launch is a persistent grid (one workgroup per resident slot on the current
+ * device) whose workgroups take query units from per-XCD queues, their own
+ * XCD's first; which workgroup runs which unit varies from call to call, the
+ * results do not.
  */
 sta_status sta_forward(const sta_dims* dims, const void* q, const void* k,
                        const void* v, const int32_t* window_sizes,

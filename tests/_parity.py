@@ -28,8 +28,18 @@ def note(msg: str) -> None:
 
 
 def run_sta(q, k, v, windows, text_length, has_text, video, workspace=None):
-    out, lse = sta.sliding_tile_attention(q, k, v, windows, text_length, has_text, video,
-                                          return_lse=True, workspace=workspace)
+    """One forward through the C ABI. out and lse start as NaN, so a row that no
+    workgroup wrote fails every check made on it."""
+    B, heads, S, D = q.shape
+    dims = sta.make_dims(B, heads, D, video)
+    assert sta.sta_seq_len(dims, has_text) == S
+    out = torch.full_like(q, float("nan"))
+    lse = torch.full((B, heads, S), float("nan"), dtype=torch.float32, device=q.device)
+    need = sta.sta_workspace_bytes(dims, windows, has_text)
+    assert need > 0
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    sta.sta_forward(dims, q, k, v, windows, text_length, has_text, out, lse, workspace)
     torch.cuda.synchronize()
     return out, lse
 

@@ -123,7 +123,8 @@ def test_sizes(lib, B, heads, D, video, windows, text):
     def up(x):
         return (x + 255) // 256 * 256
     tensor = B * heads * S * D * 2
-    expect = up(tensor) + up(n_off * 4) + up(n_ids * 4) + up(n_work * 4)
+    queue_heads = 8 * 64 * 4  # one int per XCD queue, each on its own 256-byte line
+    expect = up(tensor) + up(n_off * 4) + up(n_ids * 4) + up(n_work * 4) + queue_heads
     assert sta.sta_workspace_bytes(d, windows, text) == expect
 
 

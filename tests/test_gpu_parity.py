@@ -112,6 +112,8 @@ def test_full_size_sampled(name):
     note(f"full-size {name}: {wl.describe()}")
     q, k, v = sta_inputs.make_qkv(wl, "cuda")
     out, lse = run_sta(q, k, v, list(wl.windows), wl.text_length, wl.has_text, wl.video)
+    # every row of every (batch, head) was written (the outputs start as NaN)
+    assert bool(torch.isfinite(out).all()) and bool(torch.isfinite(lse).all()), name
     rows = sta_inputs.sample_rows(wl, per_head=24)
     ro, rl = oracle_rows(q, k, v, list(wl.windows), wl.text_length, wl.has_text, wl.video,
                          rows=rows.numpy())
