@@ -7,9 +7,9 @@
 // gives every query the same (18,24,24) token box of the (30,48,80) video.)
 // The text query unit of a head sees every tile.
 //
-// The work order lists query units heaviest first, spreading every class of
-// equal-cost units evenly over the 8 XCDs (workgroup i runs on XCD i % 8)
-// with each XCD taking a contiguous run of each class.
+// The work order holds one queue of query units per XCD, heaviest first,
+// spreading every class of equal-cost units evenly over the 8 queues with
+// each queue taking a contiguous run of each class.
 #include "sta_internal.h"
 
 namespace sta {
@@ -19,6 +19,18 @@ __device__ inline int clamp_start(int c, int w, int n) {
   int s = c - w / 2;
   s = s < 0 ? 0 : s;
   return s > n - w ? n - w : s;
+}
+
+// Offset inside a window [s, s + w) of the coordinate congruent to r mod w
+// (r in [0, w)). Listing a window's tiles by the residues of their absolute
+// coordinates, rather than by their offsets from the window start, makes
+// query tiles whose windows overlap read each shared key tile at the same
+// step of their key loop; workgroups on one XCD run in step, so the shared
+// tile is then fetched into that XCD's L2 once rather than once per query
+// tile.
+__device__ inline int residue_offset(int r, int s, int w) {
+  const int d = (r - s) % w;
+  return d < 0 ? d + w : d;
 }
 
 __device__ inline int64_t head_list_len(const Geom& g, uint32_t p) {
@@ -45,7 +57,9 @@ __global__ __launch_bounds__(256) void schedule_lists_kernel(Geom g, Windows win
               sw = clamp_start(tw, ww, g.nw);
     for (int j = threadIdx.x; j < wv; j += blockDim.x) {
       const int a = j / (wh * ww), b = (j / ww) % wh, c = j % ww;
-      ids[off + j] = ((st + a) * g.nh + (sh + b)) * g.nw + (sw + c);
+      ids[off + j] = ((st + residue_offset(a, st, wt)) * g.nh + (sh + residue_offset(b, sh, wh))) *
+                         g.nw +
+                     (sw + residue_offset(c, sw, ww));
     }
   } else {
     const int64_t off = base + int64_t(g.n_tiles) * wv;

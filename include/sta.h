@@ -159,12 +159,15 @@ sta_status sta_schedule_sizes(const sta_dims* dims, const int32_t* window_sizes,
  * Build the tile-window schedule on the device.
  *   offsets[hd*n_q + u] .. offsets[hd*n_q + u + 1] delimit, in ids, the key
  *   tiles that query unit u of head hd sees: for a video query tile, the
- *   tiles of its clamped window in t-h-w nested order (w fastest); for the
- *   text unit (u = n_tiles), every tile 0 .. n_tiles-1.
- *   work[i] is the query unit ((b*heads + hd)*n_q + u) that workgroup i of
- *   the attention launch processes: heaviest units first, and within each
- *   run of 256 workgroups, the ones that land on one XCD get consecutive
- *   units.
+ *   tiles of its clamped window, ordered by the residues of their tile
+ *   coordinates (t mod w_t, h mod w_h, w mod w_w) in nested order with the
+ *   last fastest, so query tiles with overlapping windows reach each shared
+ *   tile at the same step; for the text unit (u = n_tiles), every tile
+ *   0 .. n_tiles-1.
+ *   work holds 8 queues of query units ((b*heads + hd)*n_q + u), one per
+ *   XCD: queue x is work[x], work[8 + x], work[16 + x], ...; each queue
+ *   runs heaviest units first and takes a contiguous run of every class of
+ *   equal-cost units.
  * All three arrays are device int32 of the sizes sta_schedule_sizes gives.
  */
 sta_status sta_build_schedule(const sta_dims* dims, const int32_t* window_sizes,

@@ -2,8 +2,9 @@
 
 Gather/scatter are compared bit for bit with an index map built here from the
 tile definition; the schedule's key-tile lists with the key tiles the
-oracle's token mask touches (brute force per query tile); the work order is
-checked for being a permutation, heaviest first, XCD-grouped.
+oracle's token mask touches (brute force per query tile), and their order by
+coordinate residues; the work order is checked for being a permutation split
+into 8 per-XCD queues, each heaviest first.
 """
 
 import numpy as np
@@ -98,8 +99,16 @@ def test_schedule_matches_mask(case):
             first_head[windows[hd]] = lists
             tiles = range(n_tiles) if n_tiles <= 40 else sorted(
                 set(rng.integers(0, n_tiles, 6).tolist()) | {0, n_tiles - 1})
+            w = windows[hd]
+            nt, nh, nw = video[0] // 6, video[1] // 8, video[2] // 8
+            digits = [(a, b, c) for a in range(w[0]) for b in range(w[1]) for c in range(w[2])]
             for qt in tiles:
-                assert lists[qt] == oracle.key_tiles_of_query_tile(video, windows[hd], qt), (hd, qt)
+                # the window's tiles, each once ...
+                assert sorted(lists[qt]) == oracle.key_tiles_of_query_tile(video, windows[hd], qt), (hd, qt)
+                # ... listed by the residues of their coordinates mod the window size
+                res = [((x // (nh * nw)) % w[0], ((x // nw) % nh) % w[1], (x % nw) % w[2])
+                       for x in lists[qt]]
+                assert res == digits, (hd, qt)
             # every list has the window's tile count
             w = windows[hd]
             assert all(len(x) == w[0] * w[1] * w[2] for x in lists)
@@ -110,7 +119,7 @@ def test_schedule_matches_mask(case):
     # the work order: a permutation of all query units
     assert sorted(work.tolist()) == list(range(B * heads * n_q))
 
-    # workgroup i runs on XCD i % 8; each XCD's queue must run heaviest first,
+    # queue x is work[x::8]; each queue must run heaviest first,
     # every class of equal-cost units must be split evenly over the XCDs, and
     # the XCD loads may differ by at most one unit's cost
     def cost(unit):
