@@ -26,10 +26,15 @@
 // LDS layout of a K block (64 rows of D bf16). Each 1 KB LDS-DMA transfer
 // fills one group of 1024 / (2D) consecutive rows. Inside a group the rows
 // are interleaved at 64-byte granularity: quad k (16-byte chunks 4k..4k+3) of
-// every row of the group, then quad k + 1, and so on; within a quad the chunks
-// of row r sit XOR-permuted by a 2-bit function of (r / 4) mod 4. The K
-// fragment reads (16 rows x one chunk) then hit distinct banks and every read
-// address is one per-lane base plus compile-time offsets.
+// every row of the group, then quad k + 1, and so on; within a quad, chunk j
+// of row r sits at position j XOR (2 * bit 3 of r). Every read address is one
+// per-lane base plus compile-time offsets. gfx950 serves a ds_read_b128 in
+// four LDS cycles of 16 lanes each, lane l in cycle (bit 5 of l, parity of
+// bits 2..4 of l) (measured with the LDS bank-conflict counter); with this
+// permutation the 16 lanes of every cycle of a K fragment read (16 rows x one
+// chunk) cover all 64 banks, for D = 128 and D = 64 alike. Without it, or
+// with a permutation that ignores that lane grouping, two lanes of each cycle
+// share banks and every K fragment read takes 8 LDS cycles instead of 4.
 //
 // Per block and wave, with v_mfma_f32_16x16x32_bf16:
 //   S^T = K Q^T   A = K fragment (lane l holds K[16kt + l%16][32ks + 8(l/16)
@@ -190,8 +195,8 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(KernelArgs) 
   const int n_blk = n_vid + (text_len + kKeyBlock - 1) / kKeyBlock;
   const bool ragged = (text_len % kKeyBlock) != 0;
 
-  // 2-bit chunk permutation of K row r inside its 64-byte quad.
-  auto sw = [](int row) { return ((row >> 1) & 2) | ((row >> 3) & 1); };
+  // Chunk permutation of K row r inside its 64-byte quad (see the layout above).
+  auto sw = [](int row) { return (row >> 2) & 2; };
 
   // The schedule is read through the scalar cache (it is never written while
   // this kernel runs). Key blocks of one tile are consecutive.
