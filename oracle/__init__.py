@@ -11,5 +11,7 @@ from .sta_oracle import (  # noqa: F401
     window_start,
     allowed_mask,
     key_tiles_of_query_tile,
+    query_rows_seeing,
     sta_reference,
+    sta_reference_backward,
 )

@@ -1,4 +1,4 @@
-"""Plain fp64 CPU oracle for the Sliding Tile Attention (STA) forward pass.
+"""Plain fp64 CPU oracle for Sliding Tile Attention (STA): forward pass and its gradients.
 
 Test infrastructure only: imported by the tests, the smoke check and the
 benchmark's CPU-baseline leg, never by the HIP library, with which it shares
@@ -37,6 +37,11 @@ Precision: inputs are upcast exactly to float64 and everything is computed
 in float64. The computation is the plain definition: an explicit
 token-level boolean mask built from token coordinates (no tile list), a
 dense masked softmax over all keys, and a dense product with V.
+
+The gradients (``sta_reference_backward``) are those of that same function
+with respect to q, k and v for an upstream gradient ``dout`` of the output:
+the chain rule through the masked softmax, written out. The page shows only
+the forward call; the backward is defined by it and by nothing else.
 """
 
 from __future__ import annotations
@@ -205,3 +210,127 @@ def sta_reference(q, k, v, window_sizes, text_length: int, has_text: bool,
                 out[b, h, r0:r0 + len(rr)] = (p @ v64[b, h]) / l
                 lse[b, h, r0:r0 + len(rr)] = (m + np.log(l))[:, 0]
     return out, lse
+
+
+def query_rows_seeing(key_rows: Sequence[int], video: Tuple[int, int, int],
+                      window: Tuple[int, int, int], text_length: int,
+                      has_text: bool) -> np.ndarray:
+    """Every query position whose mask row allows at least one of ``key_rows``.
+
+    Video query tiles are tested one at a time with the same window rule
+    ``allowed_mask`` applies to their tokens (all 384 tokens of a tile share
+    one window); every text query sees every video key and every valid text
+    key. Used to restrict a key-side gradient to the rows that reach it.
+    """
+    n_t, n_h, n_w = _check_video(video)
+    T, H, W = video
+    n_video = T * H * W
+    key_rows = np.asarray(key_rows, dtype=np.int64)
+    vid_keys = key_rows[key_rows < n_video]
+    txt_keys = key_rows[key_rows >= n_video]
+    if np.any(txt_keys >= n_video + (TEXT_SLOTS if has_text else 0)):
+        raise IndexError("key row out of range")
+    # key tiles touched by the requested video keys
+    kt = (vid_keys // (H * W)) // TILE[0]
+    kh = ((vid_keys // W) % H) // TILE[1]
+    kw = (vid_keys % W) // TILE[2]
+    touched = set(zip(kt.tolist(), kh.tolist(), kw.tolist()))
+    sees_text = bool(np.any(txt_keys < n_video + text_length)) if has_text else False
+    rows = []
+    for tt in range(n_t):
+        for th in range(n_h):
+            for tw in range(n_w):
+                s_t = window_start(tt, window[0], n_t)
+                s_h = window_start(th, window[1], n_h)
+                s_w = window_start(tw, window[2], n_w)
+                hit = sees_text or any(s_t <= a < s_t + window[0] and s_h <= b < s_h + window[1]
+                                       and s_w <= c < s_w + window[2] for a, b, c in touched)
+                if not hit:
+                    continue
+                for dt in range(TILE[0]):
+                    for dh in range(TILE[1]):
+                        t = tt * TILE[0] + dt
+                        h = th * TILE[1] + dh
+                        base = (t * H + h) * W + tw * TILE[2]
+                        rows.extend(range(base, base + TILE[2]))
+    if has_text and (len(vid_keys) > 0 or sees_text):
+        rows.extend(range(n_video, n_video + TEXT_SLOTS))
+    return np.unique(np.asarray(rows, dtype=np.int64))
+
+
+def _masked_probabilities(q64, k64, rr, mask, scale):
+    """Softmax probabilities of query rows ``rr`` over all keys (0 where masked), fp64."""
+    scores = (q64[rr] @ k64.T) * scale
+    scores = np.where(mask, scores, -np.inf)
+    m = scores.max(axis=1, keepdims=True)
+    p = np.exp(scores - m)
+    return p / p.sum(axis=1, keepdims=True)
+
+
+def sta_reference_backward(q, k, v, dout, window_sizes, text_length: int, has_text: bool,
+                           video: Tuple[int, int, int],
+                           query_rows: Optional[Iterable[int]] = None,
+                           key_rows: Optional[Iterable[int]] = None, chunk: int = 256):
+    """Gradients of ``sta_reference``'s output, float64.
+
+    For a query row i, allowed keys j and scale c = 1/sqrt(head_dim):
+    ``p_ij = softmax_j(c q_i.k_j)`` (0 for masked j), ``out_i = sum_j p_ij v_j``.
+    With ``dout`` the gradient of a scalar loss with respect to ``out``:
+
+    * ``dv_j = sum_i p_ij dout_i``;
+    * ``dp_ij = dout_i . v_j`` and ``delta_i = sum_j p_ij dp_ij`` (which
+      equals ``dout_i . out_i``);
+    * ``ds_ij = p_ij (dp_ij - delta_i)``, the gradient of the scaled score;
+    * ``dq_i = c sum_j ds_ij k_j`` and ``dk_j = c sum_i ds_ij q_i``.
+
+    ``query_rows`` selects the dq rows returned and ``key_rows`` the dk/dv
+    rows (default: all). A key row's gradient sums over every query row that
+    sees it, so those rows are all evaluated, each densely over all S keys.
+
+    Returns ``(dq, dk, dv)`` as float64 arrays ``[B, heads, Rq, D]``,
+    ``[B, heads, Rk, D]``, ``[B, heads, Rk, D]``.
+    """
+    q64, k64, v64, do64 = _as_np64(q), _as_np64(k), _as_np64(v), _as_np64(dout)
+    B, heads, S, D = q64.shape
+    n_video = video[0] * video[1] * video[2]
+    if S != n_video + (TEXT_SLOTS if has_text else 0):
+        raise ValueError(f"sequence length {S} does not match video {video} / text {has_text}")
+    for x in (k64, v64, do64):
+        if x.shape != q64.shape:
+            raise ValueError("q, k, v, dout must share one shape")
+    if len(window_sizes) == 3 and np.isscalar(window_sizes[0]):
+        window_sizes = [tuple(window_sizes)] * heads
+    if len(window_sizes) != heads:
+        raise ValueError("one window per head is required")
+    qrows = np.arange(S) if query_rows is None else np.asarray(list(query_rows), dtype=np.int64)
+    krows = np.arange(S) if key_rows is None else np.asarray(list(key_rows), dtype=np.int64)
+    scale = softmax_scale(D)
+    dq = np.zeros((B, heads, len(qrows), D))
+    dk = np.zeros((B, heads, len(krows), D))
+    dv = np.zeros((B, heads, len(krows), D))
+    for h in range(heads):
+        win = tuple(int(x) for x in window_sizes[h])
+        need = (np.arange(S) if key_rows is None
+                else query_rows_seeing(krows, video, win, text_length, has_text))
+        for b in range(B):
+            qb, kb, vb, dob = q64[b, h], k64[b, h], v64[b, h], do64[b, h]
+            # query side: dq
+            for r0 in range(0, len(qrows), chunk):
+                rr = qrows[r0:r0 + chunk]
+                p = _masked_probabilities(qb, kb, rr, allowed_mask(rr, video, win, text_length,
+                                                                   has_text), scale)
+                dp = dob[rr] @ vb.T
+                delta = (p * dp).sum(axis=1, keepdims=True)
+                ds = p * (dp - delta)
+                dq[b, h, r0:r0 + len(rr)] = scale * (ds @ kb)
+            # key side: dk, dv, summed over every query row that reaches the keys
+            for r0 in range(0, len(need), chunk):
+                rr = need[r0:r0 + chunk]
+                p = _masked_probabilities(qb, kb, rr, allowed_mask(rr, video, win, text_length,
+                                                                   has_text), scale)
+                dp = dob[rr] @ vb.T
+                delta = (p * dp).sum(axis=1, keepdims=True)
+                ds = p * (dp - delta)
+                dk[b, h] += scale * (ds[:, krows].T @ qb[rr])
+                dv[b, h] += p[:, krows].T @ dob[rr]
+    return dq, dk, dv
