@@ -1,5 +1,5 @@
 #!/usr/bin/env python3
-"""Benchmark of the STA forward (one GPU).
+"""Benchmark of the STA forward (one GPU); ``--pass backward`` times the backward.
 
 One step = one sta_forward call (pack v to tile-major V^T fragments, build
 the tile-window schedule and work order, fused attention reading q and k and
@@ -12,6 +12,12 @@ throughput on a bounded sample of the same workload.
 Effective FLOPs count 4*D per allowed (query, key) pair over the valid query
 rows (video rows and the first text_length text rows), i.e. only the tiles
 that are computed.
+
+With ``--pass backward`` one step is one sta_backward call (row statistics,
+fragment packing of k, q and dout, tile lists, the dq pass, the dk/dv pass)
+for the forward's out/lse and a synthetic dout; its effective FLOPs are
+10*D per allowed pair (five products of 2*D: the recomputed scores, dP, dV,
+dQ and dK), the usual count for an attention backward.
 """
 
 from __future__ import annotations
@@ -119,6 +125,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="headline")
+    ap.add_argument("--pass", dest="which", choices=("forward", "backward"), default="forward")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for the CPU baseline (0 to skip)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -146,6 +153,8 @@ def main():
     ws = torch.empty(sta.sta_workspace_bytes(dims, windows, wl.has_text), dtype=torch.uint8,
                      device="cuda")
     stream = torch.cuda.current_stream()
+    if args.which == "backward":
+        return bench_backward(args, wl, windows, q, k, v, dims, out, lse, ws)
 
     def step(events=None):
         if events is None:
@@ -221,6 +230,83 @@ def main():
         del src, dst
     if args.cpu_budget > 0:
         result["cpu_baseline"] = cpu_baseline(wl, q, k, v, args.cpu_budget, flops)
+    print(json.dumps(result), flush=True)
+
+
+def bench_backward(args, wl, windows, q, k, v, dims, out, lse, fwd_ws):
+    import torch
+
+    import block_sparse_sliding_amd as sta
+
+    sta.sta_forward(dims, q, k, v, windows, wl.text_length, wl.has_text, out, lse, fwd_ws)
+    del fwd_ws
+    g = torch.Generator(device="cuda").manual_seed(10 * wl.seed_base + 3)
+    dout = torch.randn(q.shape, generator=g, device="cuda").to(torch.bfloat16)
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    ws = torch.empty(sta.sta_backward_workspace_bytes(dims, windows, wl.has_text),
+                     dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(events=None):
+        if events is None:
+            sta.sta_backward(dims, q, k, v, out, lse, dout, windows, wl.text_length, wl.has_text,
+                             dq, dk, dv, ws)
+        else:
+            sta.sta_backward_timed(dims, q, k, v, out, lse, dout, windows, wl.text_length,
+                                   wl.has_text, dq, dk, dv, ws, events)
+
+    for _ in range(args.warmup):
+        step()
+    ev_sets = []
+    for _ in range(args.steps):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(sta.BWD_TIMED_EVENTS)]
+        for e in evs:
+            e.record(stream)
+        ev_sets.append(evs)
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(args.steps):
+        step(ev_sets[i])
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = start.elapsed_time(stop) / args.steps
+    stage_ms = {name: 0.0 for name in sta.BWD_STAGES}
+    for evs in ev_sets:
+        for j, name in enumerate(sta.BWD_STAGES):
+            stage_ms[name] += evs[j].elapsed_time(evs[j + 1]) / args.steps
+    flops = 2.5 * effective_flops(wl)
+    tflops = flops / (ms_per_step * 1e-3) / 1e12
+    # the dq pass executes three of the five products (S, dP, dQ), the dk/dv pass four
+    dq_flops, dkv_flops = 0.6 * flops, 0.8 * flops
+    sfx = "<128>" if wl.head_dim == 128 else "<64>"
+    kernels = {}
+    for name, kname, kfl in (("dq", "bwd_dq_kernel" + sfx, dq_flops),
+                             ("dkv", "bwd_dkv_kernel" + sfx, dkv_flops)):
+        t = kfl / (stage_ms[name] * 1e-3) / 1e12
+        kernels[name] = {"kernel": kname, "bound": "mfma", "achieved": t,
+                         "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": t / PEAK_BF16_TFLOPS, "launch_ms": stage_ms[name],
+                         "executed_flop": kfl}
+    result = {
+        "metric": "STA bwd ms/call + effective TFLOP/s (% bf16 MFMA peak)",
+        "value": tflops,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": wl.describe(),
+        "pct_bf16_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
+        "effective_flop_per_call": flops,
+        "stages_ms": stage_ms,
+        "kernels": kernels,
+    }
     print(json.dumps(result), flush=True)
 
 

@@ -1,4 +1,4 @@
-"""Sliding Tile Attention (STA) forward for AMD MI355X (gfx950).
+"""Sliding Tile Attention (STA) forward and backward for AMD MI355X (gfx950).
 
 Thin Python binding over the C ABI of ``libsta.so`` (declared in
 ``include/sta.h``). Every step of the computation runs in the library's HIP
@@ -8,7 +8,7 @@ and the current stream.
 The page's call ``sliding_tile_attention(q, k, v, window_size, text_length)``
 (text mode) and ``sliding_tile_attention(q, k, v, window_size, 0, False)`` (no
 text) is mirrored by :func:`sliding_tile_attention`, with the video size made
-explicit.
+explicit; :func:`sliding_tile_attention_backward` gives its gradients.
 """
 
 from __future__ import annotations
@@ -28,6 +28,7 @@ EXPORTS = (
     "sta_status_str", "sta_seq_len", "sta_workspace_bytes", "sta_forward", "sta_forward_timed",
     "sta_tile_gather",
     "sta_tile_scatter", "sta_schedule_sizes", "sta_build_schedule",
+    "sta_backward_workspace_bytes", "sta_backward", "sta_backward_timed",
 )
 
 
@@ -79,6 +80,13 @@ def load_library() -> ctypes.CDLL:
     lib.sta_schedule_sizes.restype = ctypes.c_int
     lib.sta_build_schedule.argtypes = [PD, PI32, I32, I32, PI32, PI32, PI32, P]
     lib.sta_build_schedule.restype = ctypes.c_int
+    lib.sta_backward_workspace_bytes.argtypes = [PD, PI32, I32]
+    lib.sta_backward_workspace_bytes.restype = ctypes.c_size_t
+    bwd = [PD, P, P, P, P, P, P, PI32, I32, I32, P, P, P, P, ctypes.c_size_t, P]
+    lib.sta_backward.argtypes = bwd
+    lib.sta_backward.restype = ctypes.c_int
+    lib.sta_backward_timed.argtypes = bwd + [ctypes.POINTER(ctypes.c_void_p)]
+    lib.sta_backward_timed.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -221,3 +229,72 @@ def sliding_tile_attention(q, k, v, window_size, text_length: int = 0, has_text:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     sta_forward(dims, q, k, v, window_size, text_length, has_text, out, lse, workspace)
     return (out, lse) if return_lse else out
+
+
+# ----------------------------------------------------------------- backward
+BWD_TIMED_EVENTS = 6
+BWD_STAGES = ("row_stats", "pack_k_q_dout", "schedule_lists", "dq", "dkv")
+
+
+def sta_backward_workspace_bytes(dims: sta_dims, window_sizes, has_text: bool) -> int:
+    wa = window_array(window_sizes, dims.heads)
+    return int(load_library().sta_backward_workspace_bytes(ctypes.byref(dims), wa, int(has_text)))
+
+
+def _backward_args(dims, q, k, v, out, lse, dout, window_sizes, text_length, has_text, dq, dk,
+                   dv, workspace, stream):
+    wa = window_array(window_sizes, dims.heads)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return (ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout), wa,
+            int(text_length), int(has_text), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+            ws_bytes, _stream(stream))
+
+
+def sta_backward(dims: sta_dims, q, k, v, out, lse, dout, window_sizes, text_length: int,
+                 has_text: bool, dq, dk, dv, workspace, stream=None) -> None:
+    """Enqueue the STA backward on the stream; see include/sta.h."""
+    _check(load_library().sta_backward(*_backward_args(
+        dims, q, k, v, out, lse, dout, window_sizes, text_length, has_text, dq, dk, dv, workspace,
+        stream)), "sta_backward")
+
+
+def sta_backward_timed(dims: sta_dims, q, k, v, out, lse, dout, window_sizes, text_length: int,
+                       has_text: bool, dq, dk, dv, workspace, events, stream=None) -> None:
+    """sta_backward recording ``events`` (6 torch.cuda.Event) around its launches."""
+    if len(events) != BWD_TIMED_EVENTS:
+        raise ValueError(f"need {BWD_TIMED_EVENTS} events")
+    handles = (ctypes.c_void_p * BWD_TIMED_EVENTS)(*[e.cuda_event for e in events])
+    _check(load_library().sta_backward_timed(*_backward_args(
+        dims, q, k, v, out, lse, dout, window_sizes, text_length, has_text, dq, dk, dv, workspace,
+        stream), handles), "sta_backward_timed")
+
+
+def sliding_tile_attention_backward(q, k, v, out, lse, dout, window_size, text_length: int = 0,
+                                    has_text: bool = True, video: Sequence[int] = (30, 48, 80),
+                                    workspace=None):
+    """Gradients (dq, dk, dv) of :func:`sliding_tile_attention` for ``dout``.
+
+    ``out`` and ``lse`` are the forward's results for the same q, k, v
+    (``sliding_tile_attention(..., return_lse=True)``).
+    """
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout)):
+        if not (t.is_cuda and t.dtype == torch.bfloat16 and t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous bf16 tensor on the GPU")
+        if t.shape != q.shape or t.dim() != 4:
+            raise ValueError(f"{name} must have q's [B, heads, S, D] shape")
+    B, heads, S, D = q.shape
+    if not (lse.is_cuda and lse.dtype == torch.float32 and lse.is_contiguous()
+            and tuple(lse.shape) == (B, heads, S)):
+        raise ValueError("lse must be a contiguous fp32 [B, heads, S] tensor on the GPU")
+    dims = make_dims(B, heads, D, video)
+    need = sta_backward_workspace_bytes(dims, window_size, has_text)
+    if need == 0:
+        raise ValueError("invalid arguments (window sizes or shapes)")
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    sta_backward(dims, q, k, v, out, lse, dout, window_size, text_length, has_text, dq, dk, dv,
+                 workspace)
+    return dq, dk, dv

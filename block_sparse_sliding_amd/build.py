@@ -18,7 +18,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsta.so")
-SOURCES = ["sta_api.hip", "sta_layout.hip", "sta_schedule.hip", "sta_attention.hip"]
+SOURCES = ["sta_api.hip", "sta_layout.hip", "sta_schedule.hip", "sta_attention.hip",
+           "sta_backward.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

@@ -290,3 +290,150 @@ sta_status sta_forward_timed(const sta_dims* dims, const void* q, const void* k,
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------- backward
+namespace {
+
+struct BwdCarve {
+  size_t kt, qt, dot, lse2, delta, offsets, ids, claim_q, claim_kv, total;
+};
+
+BwdCarve bwd_carve(const Geom& g, int64_t n_ids) {
+  BwdCarve c{};
+  const size_t tensor = size_t(g.B) * g.heads * g.S * g.D * 2;
+  const size_t rows = size_t(g.B) * g.heads * g.S * 4;
+  size_t at = 0;
+  c.kt = at; at = align_up(at + tensor);
+  c.qt = at; at = align_up(at + tensor);
+  c.dot = at; at = align_up(at + tensor);
+  c.lse2 = at; at = align_up(at + rows);
+  c.delta = at; at = align_up(at + rows);
+  c.offsets = at; at = align_up(at + (size_t(g.heads) * g.n_q + 1) * 4);
+  c.ids = at; at = align_up(at + size_t(n_ids) * 4);
+  c.claim_q = at; at = align_up(at + size_t(sta::kClaimInts) * 4);
+  c.claim_kv = at; at = align_up(at + size_t(sta::kClaimInts) * 4);
+  c.total = at;
+  return c;
+}
+
+sta_status backward_impl(const sta_dims* dims, const void* q, const void* k, const void* v,
+                         const void* out, const float* lse, const void* dout,
+                         const int32_t* window_sizes, int32_t text_length, int32_t has_text,
+                         void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                         void* stream, void* const* events) {
+  Geom g;
+  sta_status st = make_geom(dims, has_text, text_length, &g);
+  if (st != STA_OK) return st;
+  // key units (3 per tile, 2 for the text slots) are numbered in 32 bits
+  if (int64_t(g.B) * g.heads * (3 * int64_t(g.n_tiles) + 2) >= (int64_t(1) << 31)) return STA_ERR_SHAPE;
+  Windows win;
+  int64_t n_ids = 0;
+  st = make_windows(g, window_sizes, &win, &n_ids);
+  if (st != STA_OK) return st;
+  for (const void* p : {q, k, v, out, static_cast<const void*>(lse), dout,
+                        static_cast<const void*>(dq), static_cast<const void*>(dk),
+                        static_cast<const void*>(dv)})
+    if (p == nullptr) return STA_ERR_NULL;
+  for (const void* p : {q, k, v, out, static_cast<const void*>(lse), dout,
+                        static_cast<const void*>(dq), static_cast<const void*>(dk),
+                        static_cast<const void*>(dv)})
+    if (!aligned16(p)) return STA_ERR_ALIGN;
+  const BwdCarve c = bwd_carve(g, n_ids);
+  if (workspace == nullptr || workspace_bytes < c.total) return STA_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return STA_ERR_ALIGN;
+  const size_t tbytes = size_t(g.B) * g.heads * g.S * g.D * 2;
+  const size_t lbytes = size_t(g.B) * g.heads * g.S * 4;
+  const void* ins[] = {q, k, v, out, lse, dout, workspace};
+  const size_t in_n[] = {tbytes, tbytes, tbytes, tbytes, lbytes, tbytes, c.total};
+  void* outs[] = {dq, dk, dv};
+  for (int o = 0; o < 3; ++o) {
+    for (int i = 0; i < 7; ++i)
+      if (overlaps(outs[o], tbytes, ins[i], in_n[i])) return STA_ERR_ALIAS;
+    for (int o2 = o + 1; o2 < 3; ++o2)
+      if (overlaps(outs[o], tbytes, outs[o2], tbytes)) return STA_ERR_ALIAS;
+  }
+
+  char* ws = static_cast<char*>(workspace);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  auto mark = [&](int i) -> sta_status {
+    if (events == nullptr) return STA_OK;
+    return hip_status(hipEventRecord(reinterpret_cast<hipEvent_t>(events[i]), s));
+  };
+  sta::BwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.dout = dout;
+  a.kt = ws + c.kt;
+  a.qt = ws + c.qt;
+  a.dot = ws + c.dot;
+  a.lse2 = reinterpret_cast<float*>(ws + c.lse2);
+  a.delta = reinterpret_cast<float*>(ws + c.delta);
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  int32_t* offsets = reinterpret_cast<int32_t*>(ws + c.offsets);
+  int32_t* ids = reinterpret_cast<int32_t*>(ws + c.ids);
+  a.offsets = offsets;
+  a.ids = ids;
+  a.claim_q = reinterpret_cast<int32_t*>(ws + c.claim_q);
+  a.claim_kv = reinterpret_cast<int32_t*>(ws + c.claim_kv);
+  a.q_scale = float(1.4426950408889634 / std::sqrt(double(g.D)));  // log2(e)/sqrt(D)
+  a.scale = float(1.0 / std::sqrt(double(g.D)));
+
+  st = mark(0);
+  if (st == STA_OK)
+    st = hip_status(sta::launch_bwd_prep(g, out, dout, lse, reinterpret_cast<float*>(ws + c.lse2),
+                                         reinterpret_cast<float*>(ws + c.delta), a.claim_q,
+                                         a.claim_kv, s));
+  if (st == STA_OK) st = mark(1);
+  if (st == STA_OK)
+    st = hip_status(sta::launch_pack_rows(g, k, ws + c.kt, g.n_video + (g.has_text ? g.text_length : 0), s));
+  if (st == STA_OK) st = hip_status(sta::launch_pack_rows(g, q, ws + c.qt, g.S, s));
+  if (st == STA_OK) st = hip_status(sta::launch_pack_rows(g, dout, ws + c.dot, g.S, s));
+  if (st == STA_OK) st = mark(2);
+  if (st == STA_OK) st = hip_status(sta::launch_schedule_lists(g, win, offsets, ids, s));
+  if (st == STA_OK) st = mark(3);
+  if (st == STA_OK) st = hip_status(sta::launch_bwd_dq(g, win, a, s));
+  if (st == STA_OK) st = mark(4);
+  if (st == STA_OK) st = hip_status(sta::launch_bwd_dkv(g, win, a, s));
+  if (st == STA_OK) st = mark(5);
+  return st;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t sta_backward_workspace_bytes(const sta_dims* dims, const int32_t* window_sizes,
+                                    int32_t has_text) {
+  Geom g;
+  if (make_geom(dims, has_text, 0, &g) != STA_OK) return 0;
+  Windows win;
+  int64_t n_ids = 0;
+  if (make_windows(g, window_sizes, &win, &n_ids) != STA_OK) return 0;
+  return bwd_carve(g, n_ids).total;
+}
+
+sta_status sta_backward(const sta_dims* dims, const void* q, const void* k, const void* v,
+                        const void* out, const float* lse, const void* dout,
+                        const int32_t* window_sizes, int32_t text_length, int32_t has_text,
+                        void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  return backward_impl(dims, q, k, v, out, lse, dout, window_sizes, text_length, has_text, dq, dk,
+                       dv, workspace, workspace_bytes, stream, nullptr);
+}
+
+sta_status sta_backward_timed(const sta_dims* dims, const void* q, const void* k, const void* v,
+                              const void* out, const float* lse, const void* dout,
+                              const int32_t* window_sizes, int32_t text_length, int32_t has_text,
+                              void* dq, void* dk, void* dv, void* workspace,
+                              size_t workspace_bytes, void* stream, void* const* events) {
+  if (events == nullptr) return STA_ERR_NULL;
+  for (int i = 0; i < STA_BWD_TIMED_EVENTS; ++i)
+    if (events[i] == nullptr) return STA_ERR_NULL;
+  return backward_impl(dims, q, k, v, out, lse, dout, window_sizes, text_length, has_text, dq, dk,
+                       dv, workspace, workspace_bytes, stream, events);
+}
+
+}  // extern "C"

@@ -1,0 +1,680 @@
+// STA backward for gfx950: dq, dk, dv of the fused forward, bf16 MFMA with
+// fp32 accumulation.
+//
+// What it computes: the gradients of softmax(q k^T / sqrt(D)) v under the STA
+// mask (STA README, "Usage" and "Why is STA Fast?": whole key tiles of each
+// query tile's window, then the valid text keys) for an upstream gradient
+// dout. With c = 1/sqrt(D), P the forward's probabilities (recomputed from
+// the saved lse) and delta_i = dout_i . out_i:
+//   dP = dout v^T,   dS = P * (dP - delta),
+//   dq = c dS k,     dk = c dS^T q,     dv = P^T dout.
+// The page shows only the forward call; these follow from its definition.
+//
+// Three passes over the inputs, each a launch on the caller's stream:
+//   prep   lse2 = lse * log2(e) and delta, per row in tile-major order;
+//   pack   K^T, Q^T and dout^T as MFMA A-operand fragments (the forward's V^T
+//          packing, applied to these tensors);
+//   dq     query-stationary: the forward's loop with S^T = K Q^T and
+//          dP^T = V dout^T from LDS (K and V raw, same swizzled layout), then
+//          dq^T += K^T dS^T with K^T fragments from LDS;
+//   dk/dv  key-stationary: 128 keys per unit, 16 per wave (their K and V rows
+//          held as MFMA B operands), streaming every query block that sees the
+//          keys: S = Q K^T and dP = dout V^T with Q and dout raw in LDS, then
+//          dv^T += dout^T P and dk^T += Q^T dS with Q^T / dout^T fragments.
+// The packed fragments present their 64 rows in the order in which a
+// 16x16x32 MFMA accumulator leaves its rows in the lanes, so P and dS go from
+// the accumulator straight into the B operand, as in the forward's PV step.
+//
+// Key-side work: a key tile is seen by the query tiles whose clamped window
+// holds it. Along one axis the window start clamp(c - w/2, 0, n - w) never
+// decreases with c, so those query tiles form a box (an interval per axis),
+// found per unit by a scan over the axis; text query rows see every video key
+// and every valid text key. Text key slots at or after text_length are seen by
+// no query and get zero gradients.
+#include <type_traits>
+
+#include "sta_device.h"
+#include "sta_internal.h"
+
+namespace sta {
+namespace {
+
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * 64;
+constexpr int kKeysPerWave = 16;                    // dk/dv: one 16-key group per wave
+constexpr int kKeyUnit = kWaves * kKeysPerWave;     // 128 keys per dk/dv unit
+constexpr int kQueryBlock = 64;                     // query rows per streamed block (dk/dv)
+constexpr int kKPrefetch = 4;                       // A fragments in flight in a contraction
+constexpr float kLog2e = 1.44269504088896340736f;
+
+static_assert(kKeyBlock == kQueryBlock, "one packed block size for keys and queries");
+static_assert(kTileRows % kKeyUnit == 0 && kTextSlots % kKeyUnit == 0, "key units tile the keys");
+
+struct KernelArgs {
+  Geom g;
+  Windows win;
+  BwdArgs a;
+};
+
+__device__ inline const KernelArgs* kernel_args() {
+  auto kp = (const __attribute__((address_space(4))) KernelArgs*)__builtin_amdgcn_kernarg_segment_ptr();
+  asm volatile("" : "+s"(kp));
+  return (const KernelArgs*)kp;
+}
+
+// Next entry of the unit order for a workgroup on XCD `xcd`, or -1 once every
+// queue is empty. Entry e = 8k + y is item k of queue y; the heads in claim
+// (one per 256-byte line) count the items taken. Same protocol as the
+// forward's queues: each fetch-add hands out a distinct item.
+__device__ inline int claim_entry(int32_t* claim, int total, int xcd) {
+  for (int t = 0; t < kQueues; ++t) {
+    const int y = (xcd + t) & (kQueues - 1);
+    const int n_y = (total - y + kQueues - 1) / kQueues;
+    if (n_y <= 0) continue;
+    const int k = __hip_atomic_fetch_add(claim + y * kClaimStride, 1, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+    if (k < n_y) return kQueues * k + y;
+  }
+  return -1;
+}
+
+__device__ inline int xcd_id() {
+  unsigned xcc;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+  return int(xcc);
+}
+
+// Window start along one axis (as the forward's schedule) and the interval of
+// query coordinates whose window holds key coordinate kc.
+__device__ inline int win_start(int c, int w, int n) {
+  int s = c - w / 2;
+  s = s < 0 ? 0 : s;
+  return s > n - w ? n - w : s;
+}
+__device__ inline void seeing_interval(int kc, int w, int n, int& lo, int& len) {
+  int first = n, last = -1;
+  for (int c = 0; c < n; ++c) {
+    const int s = win_start(c, w, n);
+    if (s <= kc && kc < s + w) {
+      first = c < first ? c : first;
+      last = c;
+    }
+  }
+  lo = first;
+  len = last - first + 1;
+}
+
+// ---------------------------------------------------------------- prep
+// grid (S / 64, B*heads), 256 threads: 4 threads per tile-major row.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(Geom g, const __bf16* __restrict__ out,
+                                                      const __bf16* __restrict__ dout,
+                                                      const float* __restrict__ lse,
+                                                      float* __restrict__ lse2,
+                                                      float* __restrict__ delta) {
+  constexpr int PER = D / 4;  // elements per thread
+  const size_t bh = blockIdx.y;
+  const int r = blockIdx.x * 64 + (threadIdx.x >> 2);
+  const int part = threadIdx.x & 3;
+  const int rr = tiled_to_raster(r, g);
+  const size_t base = (bh * g.S + rr) * D + part * PER;
+  float acc = 0.f;
+#pragma unroll
+  for (int i = 0; i < PER; i += 8) {
+    const bf16x8 a = *reinterpret_cast<const bf16x8*>(out + base + i);
+    const bf16x8 b = *reinterpret_cast<const bf16x8*>(dout + base + i);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = __builtin_fmaf(float(a[e]), float(b[e]), acc);
+  }
+  acc += __shfl_xor(acc, 1);
+  acc += __shfl_xor(acc, 2);
+  if (part == 0) {
+    delta[bh * g.S + r] = acc;
+    lse2[bh * g.S + r] = lse[bh * g.S + rr] * kLog2e;
+  }
+}
+
+// ---------------------------------------------------------------- dq
+// Query units per (b, head): two per video tile (rows 0..255 with 8 waves x
+// 32 rows, rows 256..383 with 8 waves x 16 rows), plus the 256 text query
+// slots (8 waves x 32 rows). Unit order: text units first, then the tiles.
+__device__ inline int dq_units_per_head(const Geom& g) { return 2 * g.n_tiles + (g.has_text ? 1 : 0); }
+
+template <int D>
+__global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(KernelArgs) {
+  constexpr int KS = D / 32;
+  constexpr int DT = D / 16;
+  constexpr int ROWB = D * 2;
+  constexpr int BLK = kKeyBlock * ROWB;
+  constexpr int RPI = 1024 / ROWB;
+  constexpr int IPW = BLK / 1024 / kWaves;
+  constexpr int BPT = kTileRows / kKeyBlock;
+  static_assert(IPW >= 1 && BLK % (1024 * kWaves) == 0, "block must split over the waves");
+  // [stage][K raw | V raw | K^T packed]
+  __shared__ __attribute__((aligned(1024))) char lds[2][3][BLK];
+  __shared__ int claimed;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+
+  for (;;) {
+    // every wave has read the previous claim and finished the previous
+    // unit's LDS reads (a unit may stream no block, so its body need not
+    // contain a barrier)
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const KernelArgs* ka = kernel_args();
+      const int n_qu = dq_units_per_head(ka->g);
+      claimed = claim_entry(ka->a.claim_q, ka->g.B * ka->g.heads * n_qu, xcd_id());
+    }
+    __syncthreads();
+    const int entry = __builtin_amdgcn_readfirstlane(claimed);
+    if (entry < 0) break;
+    int lane = threadIdx.x & 63;
+    asm volatile("" : "+v"(lane));
+    const KernelArgs* ka = kernel_args();
+    const Geom g = ka->g;
+    const BwdArgs a = ka->a;
+
+    // entry -> unit: the B*heads text units first, then (bh, tile, part)
+    const int n_text_units = g.has_text ? g.B * g.heads : 0;
+    int bh, u;  // u: list index into the forward schedule (tile, or n_tiles for text)
+    int q_row0, q_rows;
+    if (entry < n_text_units) {
+      bh = entry;
+      u = g.n_tiles;
+      q_row0 = g.n_video;
+      q_rows = kTextSlots;
+    } else {
+      const int e = entry - n_text_units;
+      bh = e / (2 * g.n_tiles);
+      const int r = e - bh * 2 * g.n_tiles;
+      u = r >> 1;
+      q_row0 = u * kTileRows + (r & 1) * 256;
+      q_rows = (r & 1) ? kTileRows - 256 : 256;
+    }
+    const int hd = bh % g.heads;
+    const size_t slab = size_t(bh) * g.S * D;
+    const __bf16* __restrict__ qr = reinterpret_cast<const __bf16*>(a.q) + slab;
+    const __bf16* __restrict__ dor = reinterpret_cast<const __bf16*>(a.dout) + slab;
+    const char* __restrict__ kr = reinterpret_cast<const char*>(a.k) + slab * 2;
+    const char* __restrict__ vr = reinterpret_cast<const char*>(a.v) + slab * 2;
+    const char* __restrict__ ktr = reinterpret_cast<const char*>(a.kt) + slab * 2;
+    const float* __restrict__ lse2 = a.lse2 + size_t(bh) * g.S;
+    const float* __restrict__ dlt = a.delta + size_t(bh) * g.S;
+
+    const int l0 = a.offsets[hd * g.n_q + u];
+    const int l1 = a.offsets[hd * g.n_q + u + 1];
+    const int n_vid = (l1 - l0) * BPT;
+    const int text_len = g.has_text ? g.text_length : 0;
+    const int n_blk = n_vid + (text_len + kKeyBlock - 1) / kKeyBlock;
+    const bool ragged = (text_len % kKeyBlock) != 0;
+    auto sw = [](int row) { return (row >> 2) & 2; };
+    const __attribute__((address_space(4))) int32_t* ids =
+        (const __attribute__((address_space(4))) int32_t*)(a.ids + l0);
+
+    int tile_kbase = 0, tile_vrow = 0;
+    auto block_rows = [&](int j, int& kbase, int& krs, int& vrow) {
+      if (j < n_vid) {
+        const int t = j / BPT;
+        const int sub = j - t * BPT;
+        if (sub == 0) {
+          const int tile = ids[t];
+          const int rest = div_by(tile, g.nw, g.mag_nw);
+          const int tw = tile - rest * g.nw;
+          const int tt = div_by(rest, g.nh, g.mag_nh);
+          const int th = rest - tt * g.nh;
+          tile_kbase = (tt * kTileT * g.H + th * kTileH) * g.W + tw * kTileW;
+          tile_vrow = tile * kTileRows;
+        }
+        kbase = tile_kbase + sub * g.H * g.W;
+        krs = g.W;
+        vrow = tile_vrow + sub * kKeyBlock;
+      } else {
+        kbase = vrow = g.n_video + (j - n_vid) * kKeyBlock;
+        krs = kTileW;
+      }
+    };
+    // raw rows kbase + (rr/8)*krs + rr%8 of tensor `src` into LDS region `dst`
+    // (the forward's swizzled K layout)
+    auto issue_raw = [&](const char* src, char* dst, int kbase, int krs) {
+#pragma unroll
+      for (int i = 0; i < IPW; ++i) {
+        const int q = wave * IPW + i;
+        const size_t urow = size_t(kbase + ((q * RPI) >> 3) * krs + ((q * RPI) & 7));
+        const int rin = (lane >> 2) % RPI;
+        const int chunk = 4 * (lane / (4 * RPI)) + ((lane & 3) ^ sw(q * RPI + rin));
+        const unsigned o = unsigned(rin * ROWB + chunk * 16);
+        dma16(src + urow * ROWB + o, dst + q * 1024);
+      }
+    };
+    auto issue_packed = [&](const char* src, char* dst, int vrow) {
+      const char* p = src + size_t(vrow) * ROWB;
+      const unsigned o = unsigned(lane) * 16u;
+#pragma unroll
+      for (int i = 0; i < IPW; ++i) {
+        const int q = wave * IPW + i;
+        dma16(p + q * 1024 + o, dst + q * 1024);
+      }
+    };
+
+    auto run = [&](auto qt_c) {
+      constexpr int QT = decltype(qt_c)::value;
+      constexpr int RPW = QT * 16;
+      const float qs = a.q_scale;
+      bf16x8 qf[QT][KS], dof[QT][KS];
+      float l2[QT], dl[QT];
+#pragma unroll
+      for (int c = 0; c < QT; ++c) {
+        const int row = wave * RPW + c * 16 + (lane & 15);  // < q_rows for every unit shape
+        const int rr = tiled_to_raster(q_row0 + row, g);
+        const bf16x8* qs8 = reinterpret_cast<const bf16x8*>(qr + size_t(rr) * D + (lane >> 4) * 8);
+        const bf16x8* ds8 = reinterpret_cast<const bf16x8*>(dor + size_t(rr) * D + (lane >> 4) * 8);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          qf[c][ks] = qs8[ks * 4];
+          dof[c][ks] = ds8[ks * 4];
+        }
+        l2[c] = lse2[q_row0 + row];
+        dl[c] = dlt[q_row0 + row];
+      }
+      f32x4 acc[QT][DT];
+#pragma unroll
+      for (int c = 0; c < QT; ++c)
+#pragma unroll
+        for (int d = 0; d < DT; ++d) acc[c][d] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+      const int l15 = lane & 15;
+      const int kofs = (l15 / RPI) * 1024 + (l15 % RPI) * 64 + (((lane >> 4) ^ sw(l15)) << 4);
+      auto issue = [&](int j, int st) {
+        int kbase, krs, vrow;
+        block_rows(j, kbase, krs, vrow);
+        issue_raw(kr, lds[st][0], kbase, krs);
+        issue_raw(vr, lds[st][1], kbase, krs);
+        issue_packed(ktr, lds[st][2], vrow);
+      };
+
+      // A x B^T-style score product over one raw block in LDS: out[c][kt] =
+      // sum over d of blk[16 kt + l%16][d] * frag[c][d]
+      auto scores = [&](const char* blk, const bf16x8 (&frag)[QT][KS], f32x4 (&out)[QT][4]) {
+        constexpr int NF = 4 * KS;
+        bf16x8 kf[NF];
+        auto kload = [&](int f) {
+          kf[f] = *reinterpret_cast<const bf16x8*>(blk + kofs + (f & 3) * 16 * ROWB + (f >> 2) * 64 * RPI);
+        };
+#pragma unroll
+        for (int f = 0; f < kKPrefetch; ++f) kload(f);
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+          const int ks = f >> 2, kt = f & 3;
+#pragma unroll
+          for (int c = 0; c < QT; ++c)
+            out[c][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[f], frag[c][ks],
+                                                                  ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : out[c][kt], 0, 0, 0);
+          if (f + kKPrefetch < NF) kload(f + kKPrefetch);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      };
+
+      issue(0, 0);
+      for (int j = 0; j < n_blk; ++j) {
+        const int stage = j & 1;
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        f32x4 s[QT][4], dp[QT][4];
+        scores(lds[stage][0], qf, s);
+        scores(lds[stage][1], dof, dp);
+        if (j + 1 < n_blk) issue(j + 1, stage ^ 1);
+        // P = 2^(c' s - lse2), dS = P (dP - delta); keys at or after the text
+        // length (last text block only) give P = dS = 0 by select
+        const bool mask = ragged && j == n_blk - 1;
+        int key0 = (j - n_vid) * kKeyBlock + 4 * (lane >> 4);
+        asm volatile("" : "+v"(key0));
+#pragma unroll
+        for (int c = 0; c < QT; ++c)
+#pragma unroll
+          for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[c][kt][r], qs, -l2[c]));
+              const float d = p * (dp[c][kt][r] - dl[c]);
+              dp[c][kt][r] = (mask && key0 + 16 * kt + r >= text_len) ? 0.f : d;
+            }
+        // dq^T += K^T dS^T
+        const bf16x8* ktl = reinterpret_cast<const bf16x8*>(lds[stage][2]);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          bf16x8 db[QT];
+#pragma unroll
+          for (int c = 0; c < QT; ++c) {
+            f32x8 x;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              x[r] = dp[c][2 * h][r];
+              x[4 + r] = dp[c][2 * h + 1][r];
+            }
+            db[c] = __builtin_convertvector(x, bf16x8);
+          }
+#pragma unroll
+          for (int d = 0; d < DT; ++d) {
+            const bf16x8 kf = ktl[(h * DT + d) * 64 + lane];
+#pragma unroll
+            for (int c = 0; c < QT; ++c)
+              acc[c][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, db[c], acc[c][d], 0, 0, 0);
+          }
+        }
+      }
+      // dq = c * acc, rows to raster positions
+      __bf16* __restrict__ dqr = reinterpret_cast<__bf16*>(a.dq) + slab;
+#pragma unroll
+      for (int c = 0; c < QT; ++c) {
+        const int row = wave * RPW + c * 16 + (lane & 15);
+        const int rr = tiled_to_raster(q_row0 + row, g);
+        __bf16* dst = dqr + size_t(rr) * D + (lane >> 4) * 4;
+#pragma unroll
+        for (int d = 0; d < DT; ++d) {
+          const f32x4 o = acc[c][d] * a.scale;
+          *reinterpret_cast<bf16x4*>(dst + d * 16) = __builtin_convertvector(o, bf16x4);
+        }
+      }
+    };
+    if (q_rows == 256)
+      run(std::integral_constant<int, 2>{});
+    else
+      run(std::integral_constant<int, 1>{});
+  }
+}
+
+// ---------------------------------------------------------------- dk, dv
+// Key units per (b, head): three 128-key parts per video tile, plus two for
+// the text slots. Unit order: the text parts first (each streams every query
+// row), then (bh, tile, part).
+__device__ inline int kv_units_per_head(const Geom& g) { return 3 * g.n_tiles + (g.has_text ? 2 : 0); }
+
+template <int D>
+__global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(KernelArgs) {
+  constexpr int KS = D / 32;
+  constexpr int DT = D / 16;
+  constexpr int ROWB = D * 2;
+  constexpr int BLK = kQueryBlock * ROWB;
+  constexpr int RPI = 1024 / ROWB;
+  constexpr int IPW = BLK / 1024 / kWaves;
+  constexpr int BPT = kTileRows / kQueryBlock;
+  static_assert(IPW >= 1 && BLK % (1024 * kWaves) == 0, "block must split over the waves");
+  // [stage][Q raw | dout raw | Q^T packed | dout^T packed], then lse2 and delta
+  __shared__ __attribute__((aligned(1024))) char lds[2][4][BLK];
+  __shared__ __attribute__((aligned(16))) float rowv[2][2][kQueryBlock];
+  __shared__ int claimed;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+
+  for (;;) {
+    __syncthreads();  // as in the dq kernel
+    if (threadIdx.x == 0) {
+      const KernelArgs* ka = kernel_args();
+      const int n_ku = kv_units_per_head(ka->g);
+      claimed = claim_entry(ka->a.claim_kv, ka->g.B * ka->g.heads * n_ku, xcd_id());
+    }
+    __syncthreads();
+    const int entry = __builtin_amdgcn_readfirstlane(claimed);
+    if (entry < 0) break;
+    int lane = threadIdx.x & 63;
+    asm volatile("" : "+v"(lane));
+    const KernelArgs* ka = kernel_args();
+    const Geom g = ka->g;
+    const BwdArgs a = ka->a;
+
+    const int n_text_units = g.has_text ? 2 * g.B * g.heads : 0;
+    int bh, key_row0;
+    bool text_unit;
+    int box_t = 0, box_h = 0, box_w = 0, lo_t = 0, lo_h = 0, lo_w = 0;
+    if (entry < n_text_units) {
+      bh = entry >> 1;
+      key_row0 = g.n_video + (entry & 1) * kKeyUnit;
+      text_unit = true;
+    } else {
+      const int e = entry - n_text_units;
+      bh = e / (3 * g.n_tiles);
+      const int r = e - bh * 3 * g.n_tiles;
+      const int tile = r / 3;
+      key_row0 = tile * kTileRows + (r - tile * 3) * kKeyUnit;
+      text_unit = false;
+      const uint32_t p = ka->win.w[bh % g.heads];
+      const int rest = div_by(tile, g.nw, g.mag_nw);
+      const int tw = tile - rest * g.nw;
+      const int tt = div_by(rest, g.nh, g.mag_nh);
+      const int th = rest - tt * g.nh;
+      seeing_interval(tt, win_t(p), g.nt, lo_t, box_t);
+      seeing_interval(th, win_h(p), g.nh, lo_h, box_h);
+      seeing_interval(tw, win_w(p), g.nw, lo_w, box_w);
+    }
+    const size_t slab = size_t(bh) * g.S * D;
+    const int text_len = g.has_text ? g.text_length : 0;
+    // text key slots at or after text_len are seen by nobody
+    const int valid_keys = text_unit ? min(max(g.n_video + text_len - key_row0, 0), kKeyUnit) : kKeyUnit;
+    const int n_qtiles = text_unit ? g.n_tiles : box_t * box_h * box_w;
+    const int n_blk = valid_keys == 0 ? 0 : n_qtiles * BPT + (g.has_text ? kTextSlots / kQueryBlock : 0);
+
+    const char* __restrict__ qr = reinterpret_cast<const char*>(a.q) + slab * 2;
+    const char* __restrict__ dor = reinterpret_cast<const char*>(a.dout) + slab * 2;
+    const char* __restrict__ qtr = reinterpret_cast<const char*>(a.qt) + slab * 2;
+    const char* __restrict__ dotr = reinterpret_cast<const char*>(a.dot) + slab * 2;
+    const char* __restrict__ lse2 = reinterpret_cast<const char*>(a.lse2 + size_t(bh) * g.S);
+    const char* __restrict__ dlt = reinterpret_cast<const char*>(a.delta + size_t(bh) * g.S);
+    auto sw = [](int row) { return (row >> 2) & 2; };
+
+    // query block j: raster origin of its rows and its first tile-major row
+    int tile_qbase = 0, tile_vrow = 0;
+    auto block_rows = [&](int j, int& qbase, int& qrs, int& vrow) {
+      if (j < n_qtiles * BPT) {
+        const int t = j / BPT;
+        const int sub = j - t * BPT;
+        if (sub == 0) {
+          int tt, th, tw;
+          if (text_unit) {
+            const int rest = div_by(t, g.nw, g.mag_nw);
+            tw = t - rest * g.nw;
+            tt = div_by(rest, g.nh, g.mag_nh);
+            th = rest - tt * g.nh;
+          } else {
+            const int rest = t / box_w;
+            tw = lo_w + (t - rest * box_w);
+            tt = lo_t + rest / box_h;
+            th = lo_h + (rest - (rest / box_h) * box_h);
+          }
+          tile_qbase = (tt * kTileT * g.H + th * kTileH) * g.W + tw * kTileW;
+          tile_vrow = ((tt * g.nh + th) * g.nw + tw) * kTileRows;
+        }
+        qbase = tile_qbase + sub * g.H * g.W;
+        qrs = g.W;
+        vrow = tile_vrow + sub * kQueryBlock;
+      } else {
+        qbase = vrow = g.n_video + (j - n_qtiles * BPT) * kQueryBlock;
+        qrs = kTileW;
+      }
+    };
+    auto issue_raw = [&](const char* src, char* dst, int qbase, int qrs) {
+#pragma unroll
+      for (int i = 0; i < IPW; ++i) {
+        const int q = wave * IPW + i;
+        const size_t urow = size_t(qbase + ((q * RPI) >> 3) * qrs + ((q * RPI) & 7));
+        const int rin = (lane >> 2) % RPI;
+        const int chunk = 4 * (lane / (4 * RPI)) + ((lane & 3) ^ sw(q * RPI + rin));
+        const unsigned o = unsigned(rin * ROWB + chunk * 16);
+        dma16(src + urow * ROWB + o, dst + q * 1024);
+      }
+    };
+    auto issue_packed = [&](const char* src, char* dst, int vrow) {
+      const char* p = src + size_t(vrow) * ROWB;
+      const unsigned o = unsigned(lane) * 16u;
+#pragma unroll
+      for (int i = 0; i < IPW; ++i) {
+        const int q = wave * IPW + i;
+        dma16(p + q * 1024 + o, dst + q * 1024);
+      }
+    };
+    auto issue = [&](int j, int st) {
+      int qbase, qrs, vrow;
+      block_rows(j, qbase, qrs, vrow);
+      issue_raw(qr, lds[st][0], qbase, qrs);
+      issue_raw(dor, lds[st][1], qbase, qrs);
+      issue_packed(qtr, lds[st][2], vrow);
+      issue_packed(dotr, lds[st][3], vrow);
+      if (wave == 0) dma4(lse2 + size_t(vrow) * 4 + lane * 4, reinterpret_cast<char*>(rowv[st][0]));
+      if (wave == 1) dma4(dlt + size_t(vrow) * 4 + lane * 4, reinterpret_cast<char*>(rowv[st][1]));
+    };
+
+    // this wave's 16 keys: K and V rows as B operands (lane: key l%16, d chunk l/16)
+    const int key = key_row0 + wave * kKeysPerWave + (lane & 15);
+    const bool key_ok = !text_unit || key < g.n_video + text_len;
+    const int kraster = tiled_to_raster(key, g);
+    bf16x8 kf[KS], vf[KS];
+    {
+      const bf16x8* k8 = reinterpret_cast<const bf16x8*>(reinterpret_cast<const __bf16*>(a.k) + slab +
+                                                         size_t(kraster) * D + (lane >> 4) * 8);
+      const bf16x8* v8 = reinterpret_cast<const bf16x8*>(reinterpret_cast<const __bf16*>(a.v) + slab +
+                                                         size_t(kraster) * D + (lane >> 4) * 8);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        kf[ks] = k8[ks * 4];
+        vf[ks] = v8[ks * 4];
+      }
+    }
+    f32x4 dk[DT], dv[DT];
+#pragma unroll
+    for (int d = 0; d < DT; ++d) {
+      dk[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+      dv[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    const float qs = a.q_scale;
+    const int l15 = lane & 15;
+    const int qofs = (l15 / RPI) * 1024 + (l15 % RPI) * 64 + (((lane >> 4) ^ sw(l15)) << 4);
+
+    // out[qt] = sum over d of blk[16 qt + l%16][d] * frag[d] (rows: queries)
+    auto scores = [&](const char* blk, const bf16x8 (&frag)[KS], f32x4 (&out)[4]) {
+      constexpr int NF = 4 * KS;
+      bf16x8 af[NF];
+      auto aload = [&](int f) {
+        af[f] = *reinterpret_cast<const bf16x8*>(blk + qofs + (f & 3) * 16 * ROWB + (f >> 2) * 64 * RPI);
+      };
+#pragma unroll
+      for (int f = 0; f < kKPrefetch; ++f) aload(f);
+#pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        const int ks = f >> 2, qt = f & 3;
+        out[qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[f], frag[ks],
+                                                          ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : out[qt], 0, 0, 0);
+        if (f + kKPrefetch < NF) aload(f + kKPrefetch);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+
+    if (n_blk > 0) issue(0, 0);
+    for (int j = 0; j < n_blk; ++j) {
+      const int stage = j & 1;
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      f32x4 s[4], dp[4];
+      scores(lds[stage][0], kf, s);
+      scores(lds[stage][1], vf, dp);
+      if (j + 1 < n_blk) issue(j + 1, stage ^ 1);
+      // rows of the accumulators: query 16 qt + 4 (l/16) + r
+      const f32x4* l2v = reinterpret_cast<const f32x4*>(rowv[stage][0]);
+      const f32x4* dlv = reinterpret_cast<const f32x4*>(rowv[stage][1]);
+#pragma unroll
+      for (int qt = 0; qt < 4; ++qt) {
+        const f32x4 l2 = l2v[qt * 4 + (lane >> 4)];
+        const f32x4 dl = dlv[qt * 4 + (lane >> 4)];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qt][r], qs, -l2[r]));
+          const float d = p * (dp[qt][r] - dl[r]);
+          s[qt][r] = key_ok ? p : 0.f;
+          dp[qt][r] = key_ok ? d : 0.f;
+        }
+      }
+      // dv^T += dout^T P,  dk^T += Q^T dS
+      const bf16x8* qtl = reinterpret_cast<const bf16x8*>(lds[stage][2]);
+      const bf16x8* dotl = reinterpret_cast<const bf16x8*>(lds[stage][3]);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        f32x8 x, y;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          x[r] = s[2 * h][r];
+          x[4 + r] = s[2 * h + 1][r];
+          y[r] = dp[2 * h][r];
+          y[4 + r] = dp[2 * h + 1][r];
+        }
+        const bf16x8 pb = __builtin_convertvector(x, bf16x8);
+        const bf16x8 db = __builtin_convertvector(y, bf16x8);
+#pragma unroll
+        for (int d = 0; d < DT; ++d) {
+          dv[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dotl[(h * DT + d) * 64 + lane], pb, dv[d], 0, 0, 0);
+          dk[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qtl[(h * DT + d) * 64 + lane], db, dk[d], 0, 0, 0);
+        }
+      }
+    }
+    // dk = c * acc, dv = acc; C row = d (4 (l/16) + r of each 16-group), column = key
+    __bf16* dkr = reinterpret_cast<__bf16*>(a.dk) + slab + size_t(kraster) * D + (lane >> 4) * 4;
+    __bf16* dvr = reinterpret_cast<__bf16*>(a.dv) + slab + size_t(kraster) * D + (lane >> 4) * 4;
+#pragma unroll
+    for (int d = 0; d < DT; ++d) {
+      *reinterpret_cast<bf16x4*>(dkr + d * 16) = __builtin_convertvector(dk[d] * a.scale, bf16x4);
+      *reinterpret_cast<bf16x4*>(dvr + d * 16) = __builtin_convertvector(dv[d], bf16x4);
+    }
+  }
+}
+
+template <int D>
+int dq_grid() {
+  static int cache[kMaxDevices] = {};
+  return resident_workgroups(bwd_dq_kernel<D>, kThreads, cache);
+}
+template <int D>
+int dkv_grid() {
+  static int cache[kMaxDevices] = {};
+  return resident_workgroups(bwd_dkv_kernel<D>, kThreads, cache);
+}
+
+__global__ void zero_claims_kernel(int32_t* a, int32_t* b) {
+  a[threadIdx.x] = 0;
+  b[threadIdx.x] = 0;
+}
+
+}  // namespace
+
+hipError_t launch_bwd_prep(const Geom& g, const void* out, const void* dout, const float* lse,
+                           float* lse2, float* delta, int32_t* claim_q, int32_t* claim_kv,
+                           hipStream_t stream) {
+  dim3 grid(g.S / 64, g.B * g.heads);
+  if (g.D == 128)
+    bwd_prep_kernel<128><<<grid, 256, 0, stream>>>(g, (const __bf16*)out, (const __bf16*)dout, lse, lse2, delta);
+  else
+    bwd_prep_kernel<64><<<grid, 256, 0, stream>>>(g, (const __bf16*)out, (const __bf16*)dout, lse, lse2, delta);
+  zero_claims_kernel<<<1, kClaimInts, 0, stream>>>(claim_q, claim_kv);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dq(const Geom& g, const Windows& win, const BwdArgs& a, hipStream_t stream) {
+  const int units = g.B * g.heads * (2 * g.n_tiles + (g.has_text ? 1 : 0));
+  const int resident = g.D == 128 ? dq_grid<128>() : dq_grid<64>();
+  if (resident <= 0) return hipErrorInvalidDevice;
+  const int grid = units < resident ? units : resident;
+  if (g.D == 128)
+    bwd_dq_kernel<128><<<grid, kThreads, 0, stream>>>(KernelArgs{g, win, a});
+  else
+    bwd_dq_kernel<64><<<grid, kThreads, 0, stream>>>(KernelArgs{g, win, a});
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dkv(const Geom& g, const Windows& win, const BwdArgs& a, hipStream_t stream) {
+  const int units = g.B * g.heads * (3 * g.n_tiles + (g.has_text ? 2 : 0));
+  const int resident = g.D == 128 ? dkv_grid<128>() : dkv_grid<64>();
+  if (resident <= 0) return hipErrorInvalidDevice;
+  const int grid = units < resident ? units : resident;
+  if (g.D == 128)
+    bwd_dkv_kernel<128><<<grid, kThreads, 0, stream>>>(KernelArgs{g, win, a});
+  else
+    bwd_dkv_kernel<64><<<grid, kThreads, 0, stream>>>(KernelArgs{g, win, a});
+  return hipGetLastError();
+}
+
+}  // namespace sta

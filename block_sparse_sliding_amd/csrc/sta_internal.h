@@ -68,6 +68,10 @@ hipError_t launch_rows_permute(const Geom& g, const void* src, void* dst, bool t
 // fragments, the A operand of O^T += V^T P^T (layout documented at the pack
 // kernel).
 hipError_t launch_pack_v(const Geom& g, const void* v, void* vt, hipStream_t stream);
+// The same fragment packing for any [B][heads][S][D] bf16 tensor; tile-major
+// rows at or after valid_end are written as zeros.
+hipError_t launch_pack_rows(const Geom& g, const void* src, void* dst, int valid_end,
+                            hipStream_t stream);
 hipError_t launch_schedule_lists(const Geom& g, const Windows& win, int32_t* offsets,
                                  int32_t* ids, hipStream_t stream);
 // Work order (one query unit per entry, grouped into 8 per-XCD queues: queue x
@@ -92,5 +96,32 @@ struct FwdArgs {
   float q_scale;         // log2(e) / sqrt(D), applied to the fp32 scores
 };
 hipError_t launch_attention(const Geom& g, const FwdArgs& a, hipStream_t stream);
+
+// Backward (gradients of the forward for an upstream gradient dout).
+struct BwdArgs {
+  const void* q;         // bf16 raster rows (the caller's q, k, v, dout)
+  const void* k;
+  const void* v;
+  const void* dout;
+  const void* kt;        // packed K^T fragments, text rows past the valid length zero
+  const void* qt;        // packed Q^T fragments
+  const void* dot;       // packed dout^T fragments
+  const float* lse2;     // tile-major lse * log2(e)
+  const float* delta;    // tile-major rowsum(dout * out)
+  void* dq;              // bf16 raster rows (the caller's dq, dk, dv)
+  void* dk;
+  void* dv;
+  const int32_t* offsets;  // forward schedule lists (launch_schedule_lists)
+  const int32_t* ids;
+  int32_t* claim_q;      // queue heads of the dq and dk/dv launches, zeroed by
+  int32_t* claim_kv;     // launch_bwd_prep
+  float q_scale;         // log2(e) / sqrt(D)
+  float scale;           // 1 / sqrt(D)
+};
+hipError_t launch_bwd_prep(const Geom& g, const void* out, const void* dout, const float* lse,
+                           float* lse2, float* delta, int32_t* claim_q, int32_t* claim_kv,
+                           hipStream_t stream);
+hipError_t launch_bwd_dq(const Geom& g, const Windows& win, const BwdArgs& a, hipStream_t stream);
+hipError_t launch_bwd_dkv(const Geom& g, const Windows& win, const BwdArgs& a, hipStream_t stream);
 
 }  // namespace sta

@@ -42,18 +42,18 @@ __global__ __launch_bounds__(kThreads) void rows_permute_kernel(Geom g, const ui
 // 16x16x32 MFMA computing O^T += V^T P^T, with the keys in the order in which
 // an S^T = K Q^T accumulator leaves them in the lanes (lane l holds keys
 // 4(l/16) .. +3 of each 16-key group), so P^T is used where it is produced.
-// Rows at or after the valid text length are written as zeros, so padded text
-// slots (whatever they hold) contribute exactly nothing.
+// Rows at or after valid_end (for V: the valid text length) are written as
+// zeros, so padded text slots (whatever they hold) contribute exactly nothing.
+// The backward packs K, Q and dout the same way.
 template <int D>
 __global__ __launch_bounds__(kThreads) void pack_v_kernel(Geom g, const uint4* __restrict__ v,
-                                                          uint4* __restrict__ vt) {
+                                                          uint4* __restrict__ vt, int valid_end) {
   constexpr int CPR = D / 8;     // 16-byte chunks per row
   constexpr int DT = D / 16;     // column groups
   constexpr int PITCH = D + 2;   // LDS row pitch in bf16 (odd word count: no bank aliasing)
   __shared__ uint16_t rows[kKeyBlock * PITCH];
   const size_t slab = size_t(blockIdx.y) * g.S * CPR;
   const int r0 = blockIdx.x * kKeyBlock;
-  const int valid_end = g.n_video + (g.has_text ? g.text_length : 0);
 #pragma unroll
   for (int c = threadIdx.x; c < kKeyBlock * CPR; c += kThreads) {
     const int r = c / CPR, col = c % CPR;
@@ -95,13 +95,18 @@ hipError_t launch_rows_permute(const Geom& g, const void* src, void* dst, bool t
   return hipGetLastError();
 }
 
-hipError_t launch_pack_v(const Geom& g, const void* v, void* vt, hipStream_t stream) {
+hipError_t launch_pack_rows(const Geom& g, const void* src, void* dst, int valid_end,
+                            hipStream_t stream) {
   dim3 grid(g.S / kKeyBlock, g.B * g.heads);
   if (g.D == 128)
-    pack_v_kernel<128><<<grid, kThreads, 0, stream>>>(g, (const uint4*)v, (uint4*)vt);
+    pack_v_kernel<128><<<grid, kThreads, 0, stream>>>(g, (const uint4*)src, (uint4*)dst, valid_end);
   else
-    pack_v_kernel<64><<<grid, kThreads, 0, stream>>>(g, (const uint4*)v, (uint4*)vt);
+    pack_v_kernel<64><<<grid, kThreads, 0, stream>>>(g, (const uint4*)src, (uint4*)dst, valid_end);
   return hipGetLastError();
+}
+
+hipError_t launch_pack_v(const Geom& g, const void* v, void* vt, hipStream_t stream) {
+  return launch_pack_rows(g, v, vt, g.n_video + (g.has_text ? g.text_length : 0), stream);
 }
 
 }  // namespace sta

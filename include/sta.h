@@ -175,6 +175,65 @@ sta_status sta_build_schedule(const sta_dims* dims, const int32_t* window_sizes,
                               int32_t* offsets, int32_t* ids, int32_t* work,
                               void* stream);
 
+/*
+ * Bytes of device workspace sta_backward needs for these arguments, or 0 if
+ * they are invalid: three packed copies of a [B][heads][S][D] bf16 tensor,
+ * two fp32 values per row, the forward's tile lists and 4 KB of queue heads.
+ * Pure host arithmetic: no HIP call.
+ */
+size_t sta_backward_workspace_bytes(const sta_dims* dims, const int32_t* window_sizes,
+                                    int32_t has_text);
+
+/*
+ * STA backward: the gradients of sta_forward's out with respect to q, k and
+ * v, for an upstream gradient dout. With c = 1/sqrt(D), P the probabilities
+ * of the forward (softmax over the keys each query row sees, as documented
+ * at sta_forward) and delta_i = sum_d dout[i][d] * out[i][d]:
+ *   dv_j = sum_i P_ij dout_i,   dS_ij = P_ij (dout_i . v_j - delta_i),
+ *   dq_i = c sum_j dS_ij k_j,   dk_j = c sum_i dS_ij q_i.
+ * This is the chain rule through the forward's definition (STA README
+ * "Usage" and "Why is STA Fast?"; the page shows only the forward call).
+ * P is recomputed from q, k and lse; delta from out and dout.
+ *
+ * q, k, v   : device, bf16 [B][heads][S][D], raster order: the forward's inputs.
+ * out, lse  : device, the forward's outputs for these inputs (bf16 rows and
+ *             fp32 natural-log lse, as sta_forward writes them). Read only.
+ * dout      : device, bf16 [B][heads][S][D], read only. Every row, padded
+ *             text query rows included, is a row of the forward's output and
+ *             contributes.
+ * dq, dk, dv: device, bf16 [B][heads][S][D], written. They must not overlap
+ *             each other, an input or the workspace. Text key slots at or
+ *             after text_length are seen by no query: their dk and dv rows
+ *             are written as zeros.
+ * workspace : device, >= sta_backward_workspace_bytes(...) bytes, 256-byte
+ *             aligned; contents on entry ignored, on return unspecified.
+ *             Calls that share a workspace must be ordered on one stream.
+ * Errors as for sta_forward (all found on the host before any launch).
+ * Returns STA_OK once the launches (row statistics, fragment packing of k,
+ * q and dout, the tile lists, the dq pass, the dk/dv pass) are enqueued on
+ * `stream`. The dq and dk/dv launches are persistent grids pulling units
+ * from per-XCD queues, like the forward's attention launch.
+ */
+sta_status sta_backward(const sta_dims* dims, const void* q, const void* k, const void* v,
+                        const void* out, const float* lse, const void* dout,
+                        const int32_t* window_sizes, int32_t text_length, int32_t has_text,
+                        void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                        void* stream);
+
+/*
+ * sta_backward with stage timing. `events` holds STA_BWD_TIMED_EVENTS
+ * hipEvent_t handles (as void*): events[0] before the first launch, then
+ * after 1 row statistics, 2 the three packings, 3 tile lists, 4 the dq pass,
+ * 5 the dk/dv pass. STA_ERR_NULL if events or an entry is NULL.
+ */
+#define STA_BWD_TIMED_EVENTS 6
+sta_status sta_backward_timed(const sta_dims* dims, const void* q, const void* k,
+                              const void* v, const void* out, const float* lse,
+                              const void* dout, const int32_t* window_sizes,
+                              int32_t text_length, int32_t has_text, void* dq, void* dk,
+                              void* dv, void* workspace, size_t workspace_bytes,
+                              void* stream, void* const* events);
+
 #ifdef __cplusplus
 }
 #endif

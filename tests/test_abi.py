@@ -132,3 +132,59 @@ def test_workspace_bytes_invalid_is_zero(lib):
     assert sta.sta_workspace_bytes(sta.make_dims(1, 1, 64, (18, 24, 24)), [(4, 1, 1)], False) == 0
     assert sta.sta_workspace_bytes(sta.make_dims(1, 1, 32, (18, 24, 24)), [(1, 1, 1)], False) == 0
     assert sta.sta_seq_len(sta.make_dims(1, 1, 64, (18, 24, 23)), False) == 0
+
+
+def bwd(lib, dims, q=16, k=1 << 36, v=1 << 37, out=1 << 38, lse=1 << 39, dout=(1 << 39) + (1 << 34),
+        windows=((3, 3, 3), (3, 3, 3)), ell=226, text=1, dq=1 << 40, dk=1 << 41, dv=1 << 42,
+        ws=1 << 44, ws_bytes=1 << 42):
+    """sta_backward with fake, never dereferenced, well-separated device addresses."""
+    wa = sta.window_array(list(windows), len(windows)) if windows is not None else None
+    return lib.sta_backward(ctypes.byref(dims) if dims is not None else None, q, k, v, out, lse,
+                            dout, wa, ell, text, dq, dk, dv, ws, ws_bytes, None)
+
+
+def test_backward_rejects_bad_arguments(lib):
+    d = sta.make_dims(1, 2, 128, (30, 48, 80))
+    need = sta.sta_backward_workspace_bytes(d, [(3, 3, 3)] * 2, True)
+    assert need > 0
+    assert bwd(lib, None) == 1
+    for name in ("q", "k", "v", "out", "lse", "dout", "dq", "dk", "dv"):
+        assert bwd(lib, d, **{name: 0}) == 1, name
+    assert bwd(lib, d, windows=None) == 1
+    assert bwd(lib, sta.make_dims(1, 2, 96, (30, 48, 80))) == 2
+    assert bwd(lib, sta.make_dims(1, 2, 128, (30, 44, 80))) == 2
+    assert bwd(lib, d, windows=((6, 3, 3), (3, 3, 3))) == 3
+    assert bwd(lib, d, ell=257) == 4
+    assert bwd(lib, d, ell=3, text=0) == 4
+    for name in ("q", "out", "lse", "dout", "dq", "dv"):
+        assert bwd(lib, d, **{name: {"q": 16, "out": 1 << 38, "lse": 1 << 39,
+                                     "dout": (1 << 39) + (1 << 34), "dq": 1 << 40,
+                                     "dv": 1 << 42}[name] + 4}) == 5, name
+    assert bwd(lib, d, ws_bytes=need - 1) == 6
+    assert bwd(lib, d, ws=0, ws_bytes=need) == 6
+    assert bwd(lib, d, ws=(1 << 44) + 16, ws_bytes=need) == 5
+    # outputs may overlap nothing: an input, the workspace or each other
+    assert bwd(lib, d, dq=16, ws_bytes=need) == 8
+    assert bwd(lib, d, dk=(1 << 39) + (1 << 34) + 64, ws_bytes=need) == 8
+    assert bwd(lib, d, dv=(1 << 44) + 1024, ws_bytes=need) == 8
+    assert bwd(lib, d, dk=(1 << 40) + 256, ws_bytes=need) == 8
+
+
+@pytest.mark.parametrize("B,heads,D,video,windows,text", [
+    (1, 1, 64, (18, 24, 24), [(1, 3, 3)], False),
+    (1, 24, 128, (30, 48, 80), [(3, 3, 3)] * 24, True),
+    (2, 4, 128, (30, 48, 80), [(5, 6, 10), (3, 3, 3), (1, 6, 10), (5, 1, 1)], True),
+])
+def test_backward_workspace_bytes(lib, B, heads, D, video, windows, text):
+    d = sta.make_dims(B, heads, D, video)
+    S = seq(video, text)
+    n_off, n_ids, _ = sta.sta_schedule_sizes(d, windows, text)
+
+    def up(x):
+        return (x + 255) // 256 * 256
+    tensor = B * heads * S * D * 2
+    rows = B * heads * S * 4
+    queue_heads = 8 * 64 * 4
+    expect = (3 * up(tensor) + 2 * up(rows) + up(n_off * 4) + up(n_ids * 4) + 2 * queue_heads)
+    assert sta.sta_backward_workspace_bytes(d, windows, text) == expect
+    assert sta.sta_backward_workspace_bytes(sta.make_dims(B, heads, 96, video), windows, text) == 0

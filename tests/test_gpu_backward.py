@@ -1,0 +1,205 @@
+"""GPU parity of the STA backward (through the C ABI) with the fp64 oracle.
+
+The forward's out and lse come from the HIP forward on the same inputs; the
+oracle differentiates its own exact forward. Gradients start as NaN, so an
+unwritten row fails every check.
+
+Tolerance, per (batch, head) tensor, from the arithmetic: P and dS enter
+their products rounded to bf16 (relative 2^-9 each), the products accumulate
+in fp32, and the result is rounded to bf16 (2^-9). With independent rounding
+errors the relative RMS error is a few times 2^-9 ~ 2e-3; the test allows
+1e-2, and a largest element error of 2e-2 of the tensor's largest magnitude.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sta_inputs
+import block_sparse_sliding_amd as sta
+from _parity import note, run_sta
+
+pytestmark = pytest.mark.gpu
+
+REL_RMS = 1e-2
+MAX_REL = 2e-2
+
+
+def run_backward(q, k, v, out, lse, dout, windows, ell, has_text, video):
+    B, heads, S, D = q.shape
+    dims = sta.make_dims(B, heads, D, video)
+    need = sta.sta_backward_workspace_bytes(dims, windows, has_text)
+    assert need > 0
+    ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+    dq, dk, dv = (torch.full_like(q, float("nan")) for _ in range(3))
+    sta.sta_backward(dims, q, k, v, out, lse, dout, windows, ell, has_text, dq, dk, dv, ws)
+    torch.cuda.synchronize()
+    return dq, dk, dv
+
+
+def compare_grad(got, ref, label):
+    """got: torch [B, heads, R, D] (any float), ref: numpy float64 of the same shape."""
+    g = got.float().cpu().numpy().astype(np.float64)
+    assert np.isfinite(g).all(), f"{label}: non-finite gradient"
+    worst = {}
+    for b in range(ref.shape[0]):
+        for h in range(ref.shape[1]):
+            r = ref[b, h]
+            e = g[b, h] - r
+            scale = np.abs(r).max()
+            rms = np.sqrt((r ** 2).mean())
+            if scale == 0:
+                assert np.all(e == 0), (label, b, h)
+                continue
+            stats = dict(rel_rms=float(np.sqrt((e ** 2).mean()) / rms),
+                         max_rel=float(np.abs(e).max() / scale))
+            for kk, vv in stats.items():
+                worst[kk] = max(worst.get(kk, 0.0), vv)
+    print(f"[parity] {label} {worst}", flush=True)
+    assert worst.get("rel_rms", 0.0) <= REL_RMS, (label, worst)
+    assert worst.get("max_rel", 0.0) <= MAX_REL, (label, worst)
+    return worst
+
+
+def inputs(B, heads, S, D, seed):
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    return [torch.randn(B, heads, S, D, generator=g, device="cuda").to(torch.bfloat16)
+            for _ in range(4)]
+
+
+SMALL = [
+    # video, windows, ell, has_text, D, B
+    ((12, 16, 16), [(1, 2, 1), (2, 1, 2)], 100, True, 128, 1),
+    ((12, 16, 16), [(2, 2, 2)], 0, False, 128, 2),
+    ((12, 16, 24), [(1, 1, 3), (2, 2, 1)], 37, True, 64, 1),
+    ((18, 16, 16), [(3, 1, 1)], 256, True, 128, 1),
+    ((12, 16, 16), [(1, 1, 1)], 0, True, 128, 1),
+    ((6, 8, 8), [(1, 1, 1)], 64, True, 64, 1),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[f"s{i}" for i in range(len(SMALL))])
+def test_backward_small_all_rows(case):
+    video, windows, ell, has_text, D, B = case
+    heads = len(windows)
+    S = video[0] * video[1] * video[2] + (256 if has_text else 0)
+    note(f"backward small {case}")
+    q, k, v, dout = inputs(B, heads, S, D, 1000 + S + D + ell)
+    out, lse = run_sta(q, k, v, windows, ell, has_text, video)
+    dq, dk, dv = run_backward(q, k, v, out, lse, dout, windows, ell, has_text, video)
+    rq, rk, rv = oracle.sta_reference_backward(q.cpu(), k.cpu(), v.cpu(), dout.cpu(), windows,
+                                               ell, has_text, video)
+    compare_grad(dq, rq, f"dq {case}")
+    compare_grad(dk, rk, f"dk {case}")
+    compare_grad(dv, rv, f"dv {case}")
+    if has_text:
+        nv = S - 256
+        assert bool((dk[:, :, nv + ell:] == 0).all()) and bool((dv[:, :, nv + ell:] == 0).all())
+
+
+def test_backward_padding_never_reaches_gradients():
+    """Padded text K/V (even NaN/inf) change no gradient bit."""
+    video, windows, ell = (12, 16, 16), [(1, 2, 1), (2, 1, 2)], 77
+    nv = video[0] * video[1] * video[2]
+    S = nv + 256
+    note("backward padding isolation")
+    q, k, v, dout = inputs(1, 2, S, 128, 55)
+    out, lse = run_sta(q, k, v, windows, ell, True, video)
+    g1 = run_backward(q, k, v, out, lse, dout, windows, ell, True, video)
+    k2, v2 = k.clone(), v.clone()
+    k2[:, :, nv + ell:] = float("nan")
+    v2[:, :, nv + ell:] = float("inf")
+    g2 = run_backward(q, k2, v2, out, lse, dout, windows, ell, True, video)
+    for a, b in zip(g1, g2):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+MEDIUM = [
+    ((18, 24, 32), [(1, 2, 2), (2, 1, 3)], 226, True, 128),
+    ((18, 24, 32), [(3, 3, 2)], 0, False, 64),
+]
+
+
+@pytest.mark.parametrize("case", MEDIUM, ids=[f"m{i}" for i in range(len(MEDIUM))])
+def test_backward_medium_sampled(case):
+    video, windows, ell, has_text, D = case
+    heads = len(windows)
+    nv = video[0] * video[1] * video[2]
+    S = nv + (256 if has_text else 0)
+    note(f"backward medium {case}")
+    q, k, v, dout = inputs(1, heads, S, D, 2000 + S + D)
+    out, lse = run_sta(q, k, v, windows, ell, has_text, video)
+    dq, dk, dv = run_backward(q, k, v, out, lse, dout, windows, ell, has_text, video)
+    rng = np.random.default_rng(S)
+    qrows = np.unique(np.concatenate([rng.integers(0, S, 200), [0, nv - 1, S - 1]]))
+    # two key tiles (all 384 rows each) and, with text, the first and last valid text keys
+    T, H, W = video
+    keys = []
+    for tile in (0, (video[0] // 6) * (video[1] // 8) * (video[2] // 8) - 1):
+        tt, rest = divmod(tile, (H // 8) * (W // 8))
+        th, tw = divmod(rest, W // 8)
+        for dt in range(6):
+            for dh in range(8):
+                base = ((tt * 6 + dt) * H + th * 8 + dh) * W + tw * 8
+                keys.extend(range(base, base + 8))
+    if has_text and ell > 0:
+        keys += [nv, nv + ell - 1]
+    keys = np.unique(np.asarray(keys))
+    for h in range(heads):
+        sl = slice(h, h + 1)
+        rq, rk, rv = oracle.sta_reference_backward(
+            q[:, sl].cpu(), k[:, sl].cpu(), v[:, sl].cpu(), dout[:, sl].cpu(), [windows[h]], ell,
+            has_text, video, query_rows=qrows, key_rows=keys)
+        compare_grad(dq[:, sl][:, :, torch.from_numpy(qrows)], rq, f"dq {case} head {h}")
+        compare_grad(dk[:, sl][:, :, torch.from_numpy(keys)], rk, f"dk {case} head {h}")
+        compare_grad(dv[:, sl][:, :, torch.from_numpy(keys)], rv, f"dv {case} head {h}")
+    assert bool(torch.isfinite(dq).all() and torch.isfinite(dk).all() and torch.isfinite(dv).all())
+
+
+def test_backward_full_size():
+    """(30,48,80) + 256 text at D = 128: every gradient written, sum rules on every head,
+    sampled dq rows, and the dk/dv rows of one key tile of a (1,1,1)-window head."""
+    wl = sta_inputs.WORKLOADS["headline"]
+    video = wl.video
+    heads = 4
+    windows = [(1, 1, 1), (3, 3, 3), (5, 6, 10), (3, 3, 5)]
+    ell = wl.text_length
+    nv = video[0] * video[1] * video[2]
+    S = nv + 256
+    note(f"backward full size {video}+256, {heads} heads, windows {windows}")
+    q, k, v, dout = inputs(1, heads, S, 128, 77)
+    out, lse = run_sta(q, k, v, windows, ell, True, video)
+    dq, dk, dv = run_backward(q, k, v, out, lse, dout, windows, ell, True, video)
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        assert bool(torch.isfinite(t).all()), name
+    # sum rules: sum_j dv_j = sum_i dout_i, sum_j dk_j = 0 (per head, fp64 sums)
+    sdv = dv.double().sum(dim=2)
+    sdo = dout.double().sum(dim=2)
+    sdk = dk.double().sum(dim=2)
+    dv_scale = dv.double().abs().sum(dim=2)
+    dk_scale = dk.double().abs().sum(dim=2)
+    assert bool(((sdv - sdo).abs() <= 1e-2 * dv_scale + 1e-3).all())
+    assert bool((sdk.abs() <= 1e-2 * dk_scale + 1e-3).all())
+    rng = np.random.default_rng(5)
+    qrows = np.unique(np.concatenate([rng.integers(0, nv, 16), [nv, S - 1]]))
+    for h in range(heads):
+        sl = slice(h, h + 1)
+        kr = None
+        if h == 0:
+            # key tile 137 of the (1,1,1) head: its 384 rows, seen by one query tile and the text
+            tile = 137
+            tt, rest = divmod(tile, 6 * 10)
+            th, tw = divmod(rest, 10)
+            kr = [((tt * 6 + a) * 48 + th * 8 + b) * 80 + tw * 8 + c
+                  for a in range(6) for b in range(8) for c in range(8)]
+        rq, rk, rv = oracle.sta_reference_backward(
+            q[:, sl].cpu(), k[:, sl].cpu(), v[:, sl].cpu(), dout[:, sl].cpu(), [windows[h]], ell,
+            True, video, query_rows=qrows, key_rows=kr if kr is not None else [])
+        compare_grad(dq[:, sl][:, :, torch.from_numpy(qrows)], rq, f"dq full head {h}")
+        if kr is not None:
+            idx = torch.tensor(kr)
+            compare_grad(dk[:, sl][:, :, idx], rk, "dk full head 0")
+            compare_grad(dv[:, sl][:, :, idx], rv, "dv full head 0")
+    del q, k, v, dout, out, lse, dq, dk, dv
+    torch.cuda.empty_cache()
