@@ -220,17 +220,24 @@ def main():
         },
     }
     if args.copy_calibration_mib > 0:
-        n = args.copy_calibration_mib << 20
-        src = torch.ones(n, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        result["copy_calibration_bytes"] = n
-        del src, dst
+        result["copy_calibration_bytes"] = copy_calibration(args.copy_calibration_mib)
     if args.cpu_budget > 0:
         result["cpu_baseline"] = cpu_baseline(wl, q, k, v, args.cpu_budget, flops)
     print(json.dumps(result), flush=True)
+
+
+def copy_calibration(mib: int) -> int:
+    """A plain device copy of known size (3 times), for scaling byte counters."""
+    import torch
+
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    return n
 
 
 def bench_backward(args, wl, windows, q, k, v, dims, out, lse, fwd_ws):
@@ -307,6 +314,8 @@ def bench_backward(args, wl, windows, q, k, v, dims, out, lse, fwd_ws):
         "stages_ms": stage_ms,
         "kernels": kernels,
     }
+    if args.copy_calibration_mib > 0:
+        result["copy_calibration_bytes"] = copy_calibration(args.copy_calibration_mib)
     print(json.dumps(result), flush=True)
 
 

@@ -78,6 +78,21 @@ __device__ inline int claim_entry(int32_t* claim, int total, int xcd) {
   return -1;
 }
 
+// Unit of entry e when the first `heavy` units are dealt round-robin over the
+// 8 queues and every queue then takes one contiguous run of the remaining
+// units (queue y holds ceil((total - y) / 8) entries, as claim_entry
+// assumes). Neighbouring units, which read mostly the same blocks, thus run
+// at about the same time on one XCD and share its L2.
+__device__ inline int entry_unit(int e, int total, int heavy) {
+  if (e < heavy) return e;
+  const int x = e & (kQueues - 1), k = e / kQueues;
+  auto len = [&](int y) { return (total - y + kQueues - 1) / kQueues; };
+  auto n_heavy = [&](int y) { return heavy > y ? (heavy - y + kQueues - 1) / kQueues : 0; };
+  int base = 0;
+  for (int y = 0; y < x; ++y) base += len(y) - n_heavy(y);
+  return heavy + base + (k - n_heavy(x));
+}
+
 __device__ inline int xcd_id() {
   unsigned xcc;
   asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
@@ -176,15 +191,16 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(KernelArgs) {
 
     // entry -> unit: the B*heads text units first, then (bh, tile, part)
     const int n_text_units = g.has_text ? g.B * g.heads : 0;
+    const int unit = entry_unit(entry, g.B * g.heads * dq_units_per_head(g), n_text_units);
     int bh, u;  // u: list index into the forward schedule (tile, or n_tiles for text)
     int q_row0, q_rows;
-    if (entry < n_text_units) {
-      bh = entry;
+    if (unit < n_text_units) {
+      bh = unit;
       u = g.n_tiles;
       q_row0 = g.n_video;
       q_rows = kTextSlots;
     } else {
-      const int e = entry - n_text_units;
+      const int e = unit - n_text_units;
       bh = e / (2 * g.n_tiles);
       const int r = e - bh * 2 * g.n_tiles;
       u = r >> 1;
@@ -422,15 +438,16 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(KernelArgs) {
     const BwdArgs a = ka->a;
 
     const int n_text_units = g.has_text ? 2 * g.B * g.heads : 0;
+    const int unit = entry_unit(entry, g.B * g.heads * kv_units_per_head(g), n_text_units);
     int bh, key_row0;
     bool text_unit;
     int box_t = 0, box_h = 0, box_w = 0, lo_t = 0, lo_h = 0, lo_w = 0;
-    if (entry < n_text_units) {
-      bh = entry >> 1;
-      key_row0 = g.n_video + (entry & 1) * kKeyUnit;
+    if (unit < n_text_units) {
+      bh = unit >> 1;
+      key_row0 = g.n_video + (unit & 1) * kKeyUnit;
       text_unit = true;
     } else {
-      const int e = entry - n_text_units;
+      const int e = unit - n_text_units;
       bh = e / (3 * g.n_tiles);
       const int r = e - bh * 3 * g.n_tiles;
       const int tile = r / 3;
