@@ -339,11 +339,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(KernelArgs) {
         scores(lds[stage][0], qf, s);
         scores(lds[stage][1], dof, dp);
         if (j + 1 < n_blk) issue(j + 1, stage ^ 1);
-        // P = 2^(c' s - lse2), dS = P (dP - delta); keys at or after the text
-        // length (last text block only) give P = dS = 0 by select
-        const bool mask = ragged && j == n_blk - 1;
-        int key0 = (j - n_vid) * kKeyBlock + 4 * (lane >> 4);
-        asm volatile("" : "+v"(key0));
+        // P = 2^(c' s - lse2), dS = P (dP - delta)
 #pragma unroll
         for (int c = 0; c < QT; ++c)
 #pragma unroll
@@ -351,9 +347,21 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(KernelArgs) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
               const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[c][kt][r], qs, -l2[c]));
-              const float d = p * (dp[c][kt][r] - dl[c]);
-              dp[c][kt][r] = (mask && key0 + 16 * kt + r >= text_len) ? 0.f : d;
+              dp[c][kt][r] = p * (dp[c][kt][r] - dl[c]);
             }
+        // keys at or after the text length (last text block only): dS = 0 by
+        // select, so whatever k and v hold there cannot reach dq
+        if (ragged && j == n_blk - 1) {
+          int key0 = (j - n_vid) * kKeyBlock + 4 * (lane >> 4);
+          asm volatile("" : "+v"(key0));
+#pragma unroll
+          for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (key0 + 16 * kt + r >= text_len)
+#pragma unroll
+                for (int c = 0; c < QT; ++c) dp[c][kt][r] = 0.f;
+        }
         // dq^T += K^T dS^T
         const bf16x8* ktl = reinterpret_cast<const bf16x8*>(lds[stage][2]);
 #pragma unroll
@@ -602,10 +610,20 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(KernelArgs) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qt][r], qs, -l2[r]));
-          const float d = p * (dp[qt][r] - dl[r]);
-          s[qt][r] = key_ok ? p : 0.f;
-          dp[qt][r] = key_ok ? d : 0.f;
+          dp[qt][r] = p * (dp[qt][r] - dl[r]);
+          s[qt][r] = p;
         }
+      }
+      // a text key slot at or after the text length: P = dS = 0 by select
+      // (whatever k and v hold there)
+      if (text_unit && !key_ok) {
+#pragma unroll
+        for (int qt = 0; qt < 4; ++qt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            s[qt][r] = 0.f;
+            dp[qt][r] = 0.f;
+          }
       }
       // dv^T += dout^T P,  dk^T += Q^T dS
       const bf16x8* qtl = reinterpret_cast<const bf16x8*>(lds[stage][2]);
