@@ -17,10 +17,13 @@
 //   dq     query-stationary: the forward's loop with S^T = K Q^T and
 //          dP^T = V dout^T from LDS (K and V raw, same swizzled layout), then
 //          dq^T += K^T dS^T with K^T fragments from LDS;
-//   dk/dv  key-stationary: 128 keys per unit, 16 per wave (their K and V rows
-//          held as MFMA B operands), streaming every query block that sees the
-//          keys: S = Q K^T and dP = dout V^T with Q and dout raw in LDS, then
-//          dv^T += dout^T P and dk^T += Q^T dS with Q^T / dout^T fragments.
+//   dk/dv  key-stationary: units of 256 keys (32 per wave) or 128 keys (16
+//          per wave), their K and V rows held as MFMA B operands, streaming
+//          every query block that sees the keys: S = Q K^T and dP = dout V^T
+//          with Q and dout raw in LDS, then dv^T += dout^T P and
+//          dk^T += Q^T dS with Q^T / dout^T fragments, each 64-row block in
+//          two halves of 32 queries (so two key groups fit the registers and
+//          every fragment read from LDS feeds two MFMAs).
 // The packed fragments present their 64 rows in the order in which a
 // 16x16x32 MFMA accumulator leaves its rows in the lanes, so P and dS go from
 // the accumulator straight into the B operand, as in the forward's PV step.
@@ -41,14 +44,13 @@ namespace {
 
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
-constexpr int kKeysPerWave = 16;                    // dk/dv: one 16-key group per wave
-constexpr int kKeyUnit = kWaves * kKeysPerWave;     // 128 keys per dk/dv unit
 constexpr int kQueryBlock = 64;                     // query rows per streamed block (dk/dv)
-constexpr int kKPrefetch = 4;                       // A fragments in flight in a contraction
+constexpr int kKPrefetch = 4;                       // A fragments in flight (dq contractions)
+constexpr int kKvPrefetch = 2;                      // A fragments in flight (dk/dv contractions)
 constexpr float kLog2e = 1.44269504088896340736f;
 
 static_assert(kKeyBlock == kQueryBlock, "one packed block size for keys and queries");
-static_assert(kTileRows % kKeyUnit == 0 && kTextSlots % kKeyUnit == 0, "key units tile the keys");
+static_assert(kTileRows == 256 + 128 && kTextSlots == 256, "dk/dv unit shapes below");
 
 struct KernelArgs {
   Geom g;
@@ -408,10 +410,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(KernelArgs) {
 }
 
 // ---------------------------------------------------------------- dk, dv
-// Key units per (b, head): three 128-key parts per video tile, plus two for
-// the text slots. Unit order: the text parts first (each streams every query
-// row), then (bh, tile, part).
-__device__ inline int kv_units_per_head(const Geom& g) { return 3 * g.n_tiles + (g.has_text ? 2 : 0); }
+// Key units per (b, head): per video tile keys 0..255 (8 waves x 32 keys) and
+// keys 256..383 (8 waves x 16 keys), plus the 256 text slots (8 waves x 32).
+// Unit order: the text units first (each streams every query row), then
+// (bh, tile, part).
+__device__ inline int kv_units_per_head(const Geom& g) { return 2 * g.n_tiles + (g.has_text ? 1 : 0); }
 
 template <int D>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(KernelArgs) {
@@ -445,21 +448,23 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(KernelArgs) {
     const Geom g = ka->g;
     const BwdArgs a = ka->a;
 
-    const int n_text_units = g.has_text ? 2 * g.B * g.heads : 0;
+    const int n_text_units = g.has_text ? g.B * g.heads : 0;
     const int unit = entry_unit(entry, g.B * g.heads * kv_units_per_head(g), n_text_units);
-    int bh, key_row0;
+    int bh, key_row0, unit_keys;
     bool text_unit;
     int box_t = 0, box_h = 0, box_w = 0, lo_t = 0, lo_h = 0, lo_w = 0;
     if (unit < n_text_units) {
-      bh = unit >> 1;
-      key_row0 = g.n_video + (unit & 1) * kKeyUnit;
+      bh = unit;
+      key_row0 = g.n_video;
+      unit_keys = kTextSlots;
       text_unit = true;
     } else {
       const int e = unit - n_text_units;
-      bh = e / (3 * g.n_tiles);
-      const int r = e - bh * 3 * g.n_tiles;
-      const int tile = r / 3;
-      key_row0 = tile * kTileRows + (r - tile * 3) * kKeyUnit;
+      bh = e / (2 * g.n_tiles);
+      const int r = e - bh * 2 * g.n_tiles;
+      const int tile = r >> 1;
+      key_row0 = tile * kTileRows + (r & 1) * 256;
+      unit_keys = (r & 1) ? kTileRows - 256 : 256;
       text_unit = false;
       const uint32_t p = ka->win.w[bh % g.heads];
       const int rest = div_by(tile, g.nw, g.mag_nw);
@@ -473,7 +478,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(KernelArgs) {
     const size_t slab = size_t(bh) * g.S * D;
     const int text_len = g.has_text ? g.text_length : 0;
     // text key slots at or after text_len are seen by nobody
-    const int valid_keys = text_unit ? min(max(g.n_video + text_len - key_row0, 0), kKeyUnit) : kKeyUnit;
+    const int valid_keys = text_unit ? min(max(g.n_video + text_len - key_row0, 0), unit_keys) : unit_keys;
     const int n_qtiles = text_unit ? g.n_tiles : box_t * box_h * box_w;
     const int n_blk = valid_keys == 0 ? 0 : n_qtiles * BPT + (g.has_text ? kTextSlots / kQueryBlock : 0);
 
@@ -522,13 +527,15 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(KernelArgs) {
         const size_t urow = size_t(qbase + ((q * RPI) >> 3) * qrs + ((q * RPI) & 7));
         const int rin = (lane >> 2) % RPI;
         const int chunk = 4 * (lane / (4 * RPI)) + ((lane & 3) ^ sw(q * RPI + rin));
-        const unsigned o = unsigned(rin * ROWB + chunk * 16);
+        unsigned o = unsigned(rin * ROWB + chunk * 16);
+        asm volatile("" : "+v"(o));  // keep base + offset per block (no hoisted 64-bit address)
         dma16(src + urow * ROWB + o, dst + q * 1024);
       }
     };
     auto issue_packed = [&](const char* src, char* dst, int vrow) {
       const char* p = src + size_t(vrow) * ROWB;
-      const unsigned o = unsigned(lane) * 16u;
+      unsigned o = unsigned(lane) * 16u;
+      asm volatile("" : "+v"(o));
 #pragma unroll
       for (int i = 0; i < IPW; ++i) {
         const int q = wave * IPW + i;
@@ -542,119 +549,151 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(KernelArgs) {
       issue_raw(dor, lds[st][1], qbase, qrs);
       issue_packed(qtr, lds[st][2], vrow);
       issue_packed(dotr, lds[st][3], vrow);
-      if (wave == 0) dma4(lse2 + size_t(vrow) * 4 + lane * 4, reinterpret_cast<char*>(rowv[st][0]));
-      if (wave == 1) dma4(dlt + size_t(vrow) * 4 + lane * 4, reinterpret_cast<char*>(rowv[st][1]));
+      unsigned o4 = unsigned(lane) * 4u;
+      asm volatile("" : "+v"(o4));
+      if (wave == 0) dma4(lse2 + size_t(vrow) * 4 + o4, reinterpret_cast<char*>(rowv[st][0]));
+      if (wave == 1) dma4(dlt + size_t(vrow) * 4 + o4, reinterpret_cast<char*>(rowv[st][1]));
     };
 
-    // this wave's 16 keys: K and V rows as B operands (lane: key l%16, d chunk l/16)
-    const int key = key_row0 + wave * kKeysPerWave + (lane & 15);
-    const bool key_ok = !text_unit || key < g.n_video + text_len;
-    const int kraster = tiled_to_raster(key, g);
-    bf16x8 kf[KS], vf[KS];
-    {
-      const bf16x8* k8 = reinterpret_cast<const bf16x8*>(reinterpret_cast<const __bf16*>(a.k) + slab +
-                                                         size_t(kraster) * D + (lane >> 4) * 8);
-      const bf16x8* v8 = reinterpret_cast<const bf16x8*>(reinterpret_cast<const __bf16*>(a.v) + slab +
-                                                         size_t(kraster) * D + (lane >> 4) * 8);
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        kf[ks] = k8[ks * 4];
-        vf[ks] = v8[ks * 4];
-      }
-    }
-    f32x4 dk[DT], dv[DT];
-#pragma unroll
-    for (int d = 0; d < DT; ++d) {
-      dk[d] = f32x4{0.f, 0.f, 0.f, 0.f};
-      dv[d] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
     const float qs = a.q_scale;
     const int l15 = lane & 15;
     const int qofs = (l15 / RPI) * 1024 + (l15 % RPI) * 64 + (((lane >> 4) ^ sw(l15)) << 4);
 
-    // out[qt] = sum over d of blk[16 qt + l%16][d] * frag[d] (rows: queries)
-    auto scores = [&](const char* blk, const bf16x8 (&frag)[KS], f32x4 (&out)[4]) {
-      constexpr int NF = 4 * KS;
-      bf16x8 af[NF];
-      auto aload = [&](int f) {
-        af[f] = *reinterpret_cast<const bf16x8*>(blk + qofs + (f & 3) * 16 * ROWB + (f >> 2) * 64 * RPI);
-      };
+    auto run = [&](auto kt_c) {
+      constexpr int KT = decltype(kt_c)::value;  // 16-key groups per wave
+      // this wave's keys: K and V rows as B operands (lane: key l%16, d chunk l/16)
+      int kras[KT];
+      bool key_ok[KT];
+      bf16x8 kf[KT][KS], vf[KT][KS];
 #pragma unroll
-      for (int f = 0; f < kKPrefetch; ++f) aload(f);
+      for (int kg = 0; kg < KT; ++kg) {
+        const int key = key_row0 + wave * 16 * KT + 16 * kg + (lane & 15);
+        key_ok[kg] = !text_unit || key < g.n_video + text_len;
+        kras[kg] = tiled_to_raster(key, g);
+        const bf16x8* k8 = reinterpret_cast<const bf16x8*>(reinterpret_cast<const __bf16*>(a.k) + slab +
+                                                           size_t(kras[kg]) * D + (lane >> 4) * 8);
+        const bf16x8* v8 = reinterpret_cast<const bf16x8*>(reinterpret_cast<const __bf16*>(a.v) + slab +
+                                                           size_t(kras[kg]) * D + (lane >> 4) * 8);
 #pragma unroll
-      for (int f = 0; f < NF; ++f) {
-        const int ks = f >> 2, qt = f & 3;
-        out[qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[f], frag[ks],
-                                                          ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : out[qt], 0, 0, 0);
-        if (f + kKPrefetch < NF) aload(f + kKPrefetch);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    };
-
-    if (n_blk > 0) issue(0, 0);
-    for (int j = 0; j < n_blk; ++j) {
-      const int stage = j & 1;
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
-      f32x4 s[4], dp[4];
-      scores(lds[stage][0], kf, s);
-      scores(lds[stage][1], vf, dp);
-      if (j + 1 < n_blk) issue(j + 1, stage ^ 1);
-      // rows of the accumulators: query 16 qt + 4 (l/16) + r
-      const f32x4* l2v = reinterpret_cast<const f32x4*>(rowv[stage][0]);
-      const f32x4* dlv = reinterpret_cast<const f32x4*>(rowv[stage][1]);
-#pragma unroll
-      for (int qt = 0; qt < 4; ++qt) {
-        const f32x4 l2 = l2v[qt * 4 + (lane >> 4)];
-        const f32x4 dl = dlv[qt * 4 + (lane >> 4)];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qt][r], qs, -l2[r]));
-          dp[qt][r] = p * (dp[qt][r] - dl[r]);
-          s[qt][r] = p;
+        for (int ks = 0; ks < KS; ++ks) {
+          kf[kg][ks] = k8[ks * 4];
+          vf[kg][ks] = v8[ks * 4];
         }
       }
-      // a text key slot at or after the text length: P = dS = 0 by select
-      // (whatever k and v hold there)
-      if (text_unit && !key_ok) {
+      f32x4 dk[KT][DT], dv[KT][DT];
 #pragma unroll
-        for (int qt = 0; qt < 4; ++qt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            s[qt][r] = 0.f;
-            dp[qt][r] = 0.f;
-          }
-      }
-      // dv^T += dout^T P,  dk^T += Q^T dS
-      const bf16x8* qtl = reinterpret_cast<const bf16x8*>(lds[stage][2]);
-      const bf16x8* dotl = reinterpret_cast<const bf16x8*>(lds[stage][3]);
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        f32x8 x, y;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          x[r] = s[2 * h][r];
-          x[4 + r] = s[2 * h + 1][r];
-          y[r] = dp[2 * h][r];
-          y[4 + r] = dp[2 * h + 1][r];
-        }
-        const bf16x8 pb = __builtin_convertvector(x, bf16x8);
-        const bf16x8 db = __builtin_convertvector(y, bf16x8);
+      for (int kg = 0; kg < KT; ++kg)
 #pragma unroll
         for (int d = 0; d < DT; ++d) {
-          dv[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dotl[(h * DT + d) * 64 + lane], pb, dv[d], 0, 0, 0);
-          dk[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qtl[(h * DT + d) * 64 + lane], db, dk[d], 0, 0, 0);
+          dk[kg][d] = f32x4{0.f, 0.f, 0.f, 0.f};
+          dv[kg][d] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+
+      // out[kg][i] = sum over d of blk[16 (2 hq + i) + l%16][d] * frag[kg][d]
+      auto scores = [&](const char* blk, int hq, const bf16x8 (&frag)[KT][KS], f32x4 (&out)[KT][2]) {
+        constexpr int NF = 2 * KS;
+        bf16x8 af[NF];
+        auto aload = [&](int f) {
+          af[f] = *reinterpret_cast<const bf16x8*>(blk + qofs + (2 * hq + (f & 1)) * 16 * ROWB + (f >> 1) * 64 * RPI);
+        };
+#pragma unroll
+        for (int f = 0; f < kKvPrefetch; ++f) aload(f);
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+          const int ks = f >> 1, i = f & 1;
+#pragma unroll
+          for (int kg = 0; kg < KT; ++kg)
+            out[kg][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[f], frag[kg][ks],
+                                                                 ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : out[kg][i], 0, 0, 0);
+          if (f + kKvPrefetch < NF) aload(f + kKvPrefetch);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      };
+
+      if (n_blk > 0) issue(0, 0);
+      for (int j = 0; j < n_blk; ++j) {
+        const int stage = j & 1;
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        const f32x4* l2v = reinterpret_cast<const f32x4*>(rowv[stage][0]);
+        const f32x4* dlv = reinterpret_cast<const f32x4*>(rowv[stage][1]);
+        const bf16x8* qtl = reinterpret_cast<const bf16x8*>(lds[stage][2]);
+        const bf16x8* dotl = reinterpret_cast<const bf16x8*>(lds[stage][3]);
+#pragma unroll
+        for (int hq = 0; hq < 2; ++hq) {
+          f32x4 s[KT][2], dp[KT][2];
+          scores(lds[stage][0], hq, kf, s);
+          scores(lds[stage][1], hq, vf, dp);
+          if (hq == 0 && j + 1 < n_blk) issue(j + 1, stage ^ 1);
+          // rows of the accumulators: query 16 (2 hq + i) + 4 (l/16) + r
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            const f32x4 l2 = l2v[(2 * hq + i) * 4 + (lane >> 4)];
+            const f32x4 dl = dlv[(2 * hq + i) * 4 + (lane >> 4)];
+#pragma unroll
+            for (int kg = 0; kg < KT; ++kg)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kg][i][r], qs, -l2[r]));
+                dp[kg][i][r] = p * (dp[kg][i][r] - dl[r]);
+                s[kg][i][r] = p;
+              }
+          }
+          if (text_unit) {
+#pragma unroll
+            for (int kg = 0; kg < KT; ++kg)
+              if (!key_ok[kg])
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+#pragma unroll
+                  for (int r = 0; r < 4; ++r) {
+                    s[kg][i][r] = 0.f;
+                    dp[kg][i][r] = 0.f;
+                  }
+          }
+          bf16x8 pb[KT], db[KT];
+#pragma unroll
+          for (int kg = 0; kg < KT; ++kg) {
+            f32x8 x, y;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              x[r] = s[kg][0][r];
+              x[4 + r] = s[kg][1][r];
+              y[r] = dp[kg][0][r];
+              y[4 + r] = dp[kg][1][r];
+            }
+            pb[kg] = __builtin_convertvector(x, bf16x8);
+            db[kg] = __builtin_convertvector(y, bf16x8);
+          }
+          // dv^T += dout^T P, dk^T += Q^T dS over this half's 32 queries
+#pragma unroll
+          for (int d = 0; d < DT; ++d) {
+            const bf16x8 fo = dotl[(hq * DT + d) * 64 + lane];
+            const bf16x8 fq = qtl[(hq * DT + d) * 64 + lane];
+#pragma unroll
+            for (int kg = 0; kg < KT; ++kg) {
+              dv[kg][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fo, pb[kg], dv[kg][d], 0, 0, 0);
+              dk[kg][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fq, db[kg], dk[kg][d], 0, 0, 0);
+            }
+          }
         }
       }
-    }
-    // dk = c * acc, dv = acc; C row = d (4 (l/16) + r of each 16-group), column = key
-    __bf16* dkr = reinterpret_cast<__bf16*>(a.dk) + slab + size_t(kraster) * D + (lane >> 4) * 4;
-    __bf16* dvr = reinterpret_cast<__bf16*>(a.dv) + slab + size_t(kraster) * D + (lane >> 4) * 4;
+      // dk = c * acc, dv = acc; C row = d (4 (l/16) + r of each 16-group), column = key
 #pragma unroll
-    for (int d = 0; d < DT; ++d) {
-      *reinterpret_cast<bf16x4*>(dkr + d * 16) = __builtin_convertvector(dk[d] * a.scale, bf16x4);
-      *reinterpret_cast<bf16x4*>(dvr + d * 16) = __builtin_convertvector(dv[d], bf16x4);
-    }
+      for (int kg = 0; kg < KT; ++kg) {
+        __bf16* dkr = reinterpret_cast<__bf16*>(a.dk) + slab + size_t(kras[kg]) * D + (lane >> 4) * 4;
+        __bf16* dvr = reinterpret_cast<__bf16*>(a.dv) + slab + size_t(kras[kg]) * D + (lane >> 4) * 4;
+#pragma unroll
+        for (int d = 0; d < DT; ++d) {
+          *reinterpret_cast<bf16x4*>(dkr + d * 16) = __builtin_convertvector(dk[kg][d] * a.scale, bf16x4);
+          *reinterpret_cast<bf16x4*>(dvr + d * 16) = __builtin_convertvector(dv[kg][d], bf16x4);
+        }
+      }
+    };
+    if (unit_keys == 256)
+      run(std::integral_constant<int, 2>{});
+    else
+      run(std::integral_constant<int, 1>{});
   }
 }
 
@@ -701,7 +740,7 @@ hipError_t launch_bwd_dq(const Geom& g, const Windows& win, const BwdArgs& a, hi
 }
 
 hipError_t launch_bwd_dkv(const Geom& g, const Windows& win, const BwdArgs& a, hipStream_t stream) {
-  const int units = g.B * g.heads * (3 * g.n_tiles + (g.has_text ? 2 : 0));
+  const int units = g.B * g.heads * (2 * g.n_tiles + (g.has_text ? 1 : 0));
   const int resident = g.D == 128 ? dkv_grid<128>() : dkv_grid<64>();
   if (resident <= 0) return hipErrorInvalidDevice;
   const int grid = units < resident ? units : resident;
