@@ -82,3 +82,17 @@ def compare(out_gpu, lse_gpu, out_ref, lse_ref, rows=None, label=""):
     assert summary["mean_abs"] <= OUT_MEAN_ABS, (label, summary)
     assert summary["lse_rel"] <= LSE_REL, (label, summary)
     return summary
+
+
+def scale_key_tiles(k, video, factors, text_factor, ell):
+    """k with whole key tiles (t, h, w) multiplied by factors[(t, h, w)] and the
+    valid text keys by text_factor: large, uneven score jumps between blocks."""
+    B, heads, S, D = k.shape
+    T, H, W = video
+    nv = T * H * W
+    kk = k.float().clone()
+    kv = kk[:, :, :nv].view(B, heads, T, H, W, D)
+    for (tt, th, tw), f in factors.items():
+        kv[:, :, 6 * tt:6 * tt + 6, 8 * th:8 * th + 8, 8 * tw:8 * tw + 8] *= f
+    kk[:, :, nv:nv + ell] *= text_factor
+    return kk.to(torch.bfloat16)

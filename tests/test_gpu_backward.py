@@ -18,7 +18,7 @@ import torch
 import oracle
 import sta_inputs
 import block_sparse_sliding_amd as sta
-from _parity import note, run_sta
+from _parity import note, run_sta, scale_key_tiles
 
 pytestmark = pytest.mark.gpu
 
@@ -113,6 +113,23 @@ def test_backward_padding_never_reaches_gradients():
     g2 = run_backward(q, k2, v2, out, lse, dout, windows, ell, True, video)
     for a, b in zip(g1, g2):
         assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_backward_large_score_jumps():
+    """Key tiles scaled by 0.05 .. 4 and text keys by 3.5: logits spread over tens of
+    log2 units, so P is recomputed far from the row maximum on many blocks."""
+    video, windows, ell, D = (12, 16, 24), [(1, 2, 2), (2, 1, 3)], 100, 128
+    S = video[0] * video[1] * video[2] + 256
+    note("backward score jumps")
+    q, k, v, dout = inputs(1, 2, S, D, 4242)
+    k = scale_key_tiles(k, video, {(0, 0, 1): 2.5, (1, 1, 2): 4.0, (0, 1, 0): 0.05}, 3.5, ell)
+    out, lse = run_sta(q, k, v, windows, ell, True, video)
+    dq, dk, dv = run_backward(q, k, v, out, lse, dout, windows, ell, True, video)
+    rq, rk, rv = oracle.sta_reference_backward(q.cpu(), k.cpu(), v.cpu(), dout.cpu(), windows,
+                                               ell, True, video)
+    compare_grad(dq, rq, "dq jumps")
+    compare_grad(dk, rk, "dk jumps")
+    compare_grad(dv, rv, "dv jumps")
 
 
 MEDIUM = [

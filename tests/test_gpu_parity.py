@@ -10,7 +10,7 @@ import pytest
 import torch
 
 import sta_inputs
-from _parity import compare, note, oracle_rows, run_sta
+from _parity import compare, note, oracle_rows, run_sta, scale_key_tiles
 
 pytestmark = pytest.mark.gpu
 
@@ -60,18 +60,6 @@ JUMPS = [
      {(1, 1, 2): 2.5, (2, 2, 3): 4.0, (0, 0, 0): 0.05}, 3.5),
     (64, (18, 24, 32), [(3, 3, 3)], 37, {(2, 1, 1): 3.0, (0, 2, 3): 4.0}, 3.5),
 ]
-
-
-def scale_key_tiles(k, video, factors, text_factor, ell):
-    B, heads, S, D = k.shape
-    T, H, W = video
-    nv = T * H * W
-    kk = k.float().clone()
-    kv = kk[:, :, :nv].view(B, heads, T, H, W, D)
-    for (tt, th, tw), f in factors.items():
-        kv[:, :, 6 * tt:6 * tt + 6, 8 * th:8 * th + 8, 8 * tw:8 * tw + 8] *= f
-    kk[:, :, nv:nv + ell] *= text_factor
-    return kk.to(torch.bfloat16)
 
 
 @pytest.mark.parametrize("case", JUMPS, ids=[f"j{i}" for i in range(len(JUMPS))])
