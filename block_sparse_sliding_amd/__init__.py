@@ -298,3 +298,42 @@ def sliding_tile_attention_backward(q, k, v, out, lse, dout, window_size, text_l
     sta_backward(dims, q, k, v, out, lse, dout, window_size, text_length, has_text, dq, dk, dv,
                  workspace)
     return dq, dk, dv
+
+
+# ----------------------------------------------------------------- autograd
+def _autograd_function():
+    import torch
+
+    class _STAFunction(torch.autograd.Function):
+        """Autograd glue: forward = sta_forward, backward = sta_backward (no arithmetic here)."""
+
+        @staticmethod
+        def forward(ctx, q, k, v, window_size, text_length, has_text, video):
+            out, lse = sliding_tile_attention(q, k, v, window_size, text_length, has_text, video,
+                                              return_lse=True)
+            ctx.save_for_backward(q, k, v, out, lse)
+            ctx.args = (window_size, text_length, has_text, video)
+            return out
+
+        @staticmethod
+        def backward(ctx, dout):
+            q, k, v, out, lse = ctx.saved_tensors
+            window_size, text_length, has_text, video = ctx.args
+            dq, dk, dv = sliding_tile_attention_backward(q, k, v, out, lse, dout.contiguous(),
+                                                         window_size, text_length, has_text, video)
+            return dq, dk, dv, None, None, None, None
+
+    return _STAFunction
+
+
+_STA_FUNCTION = None
+
+
+def sliding_tile_attention_autograd(q, k, v, window_size, text_length: int = 0,
+                                    has_text: bool = True, video: Sequence[int] = (30, 48, 80)):
+    """:func:`sliding_tile_attention` as a differentiable op: out.backward(...) runs
+    sta_backward (dq, dk, dv in bf16, like the inputs)."""
+    global _STA_FUNCTION
+    if _STA_FUNCTION is None:
+        _STA_FUNCTION = _autograd_function()
+    return _STA_FUNCTION.apply(q, k, v, window_size, text_length, has_text, tuple(video))

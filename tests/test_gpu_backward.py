@@ -220,3 +220,21 @@ def test_backward_full_size():
             compare_grad(dv[:, sl][:, :, idx], rv, "dv full head 0")
     del q, k, v, dout, out, lse, dq, dk, dv
     torch.cuda.empty_cache()
+
+
+def test_autograd_glue_matches_direct_calls():
+    """loss.backward() through sliding_tile_attention_autograd gives exactly the
+    gradients of a direct sta_backward call (the glue adds no arithmetic)."""
+    video, windows, ell = (12, 16, 16), [(1, 2, 1), (2, 1, 2)], 90
+    S = video[0] * video[1] * video[2] + 256
+    note("autograd glue")
+    q, k, v, dout = inputs(1, 2, S, 128, 31)
+    qq, kk, vv = (x.clone().requires_grad_(True) for x in (q, k, v))
+    out = sta.sliding_tile_attention_autograd(qq, kk, vv, windows, ell, True, video)
+    out.backward(dout)
+    torch.cuda.synchronize()
+    o2, l2 = run_sta(q, k, v, windows, ell, True, video)
+    assert torch.equal(out.detach().view(torch.int16), o2.view(torch.int16))
+    g = run_backward(q, k, v, o2, l2, dout, windows, ell, True, video)
+    for a, b in zip((qq.grad, kk.grad, vv.grad), g):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
