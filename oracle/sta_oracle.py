@@ -11,6 +11,7 @@ What that page fixes, restated:
 * q, k, v are ``[batch, heads, seq, head_dim]`` with ``seq = T*H*W + 256``
   when a text segment is present (Usage).
 * the video is cut into tiles that are cubes of (6, 8, 8) tokens (Usage);
+  the page's sizes are multiples of the tile;
 * each head has a window given in tiles ``(w_t, w_h, w_w)``; a window of
   (3, 3, 3) lets a query see (18, 24, 24) video tokens of the (30, 48, 80)
   video (Usage, the window example);
@@ -31,7 +32,11 @@ the design notes of the repository):
 * video queries also see the valid text keys; text queries (all 256 slots,
   padded ones included) see every video key and the valid text keys;
 * the softmax scale is ``1/sqrt(head_dim)``; ``lse`` is the natural log of
-  the sum of ``exp(q.k * scale)`` over the allowed keys.
+  the sum of ``exp(q.k * scale)`` over the allowed keys;
+* a video size that is not a multiple of the tile is covered by the same
+  grid of tiles, the last tile along that axis holding the remainder:
+  windows are placed on that grid (``n = ceil(size / tile)`` tiles per
+  axis) and a query sees the tokens that exist in its window tiles.
 
 Precision: inputs are upcast exactly to float64 and everything is computed
 in float64. The computation is the plain definition: an explicit
@@ -93,10 +98,12 @@ def _video_tile_coords(video: Tuple[int, int, int]):
 
 
 def _check_video(video):
+    """Tile-grid size: the (6, 8, 8) tiles that cover the video; when a size is not a
+    multiple of the tile, the last tile along that axis holds the remainder (a reading)."""
     T, H, W = video
-    if T % TILE[0] or H % TILE[1] or W % TILE[2] or min(video) <= 0:
-        raise ValueError(f"video {video} is not a positive multiple of the tile {TILE}")
-    return T // TILE[0], H // TILE[1], W // TILE[2]
+    if min(video) <= 0:
+        raise ValueError(f"video {video} must have positive sizes")
+    return -(-T // TILE[0]), -(-H // TILE[1]), -(-W // TILE[2])
 
 
 def allowed_mask(rows: Sequence[int], video: Tuple[int, int, int],
@@ -151,10 +158,9 @@ def key_tiles_of_query_tile(video: Tuple[int, int, int], window: Tuple[int, int,
     tt, rem = divmod(query_tile, n_h * n_w)
     th, tw = divmod(rem, n_w)
     rows = []
-    for dt in range(TILE[0]):
-        for dh in range(TILE[1]):
-            for dw in range(TILE[2]):
-                t, h, w = tt * TILE[0] + dt, th * TILE[1] + dh, tw * TILE[2] + dw
+    for t in range(tt * TILE[0], min(T, tt * TILE[0] + TILE[0])):
+        for h in range(th * TILE[1], min(H, th * TILE[1] + TILE[1])):
+            for w in range(tw * TILE[2], min(W, tw * TILE[2] + TILE[2])):
                 rows.append((t * H + h) * W + w)
     m = allowed_mask(rows, video, window, 0, False)
     kt, kh, kw = _video_tile_coords(video)
@@ -247,12 +253,10 @@ def query_rows_seeing(key_rows: Sequence[int], video: Tuple[int, int, int],
                                        and s_w <= c < s_w + window[2] for a, b, c in touched)
                 if not hit:
                     continue
-                for dt in range(TILE[0]):
-                    for dh in range(TILE[1]):
-                        t = tt * TILE[0] + dt
-                        h = th * TILE[1] + dh
+                for t in range(tt * TILE[0], min(T, tt * TILE[0] + TILE[0])):
+                    for h in range(th * TILE[1], min(H, th * TILE[1] + TILE[1])):
                         base = (t * H + h) * W + tw * TILE[2]
-                        rows.extend(range(base, base + TILE[2]))
+                        rows.extend(range(base, base + min(TILE[2], W - tw * TILE[2])))
     if has_text and (len(vid_keys) > 0 or sees_text):
         rows.extend(range(n_video, n_video + TEXT_SLOTS))
     return np.unique(np.asarray(rows, dtype=np.int64))

@@ -64,7 +64,7 @@ def brute_force(q, k, v, video, window, ell, has_text, rows):
     T, H, W = video
     nv = T * H * W
     S = seq_len(video, has_text)
-    ntiles = [video[a] // TILE[a] for a in range(3)]
+    ntiles = [-(-video[a] // TILE[a]) for a in range(3)]  # partial last tiles included
     D = q.shape[-1]
     qd, kd, vd = q.double().tolist(), k.double().tolist(), v.double().tolist()
 
@@ -142,6 +142,31 @@ def test_attended_key_counts(video, window, ell, has_text):
         assert (counts[nv:] == nv + ell).all()
 
 
+@pytest.mark.parametrize("video,window,ell,has_text", [
+    ((7, 9, 11), (1, 2, 1), 0, False),
+    ((13, 8, 20), (2, 1, 2), 40, True),
+    ((6, 17, 8), (1, 3, 1), 0, True),
+    ((1, 10, 10), (1, 1, 2), 0, False),
+])
+def test_attended_key_counts_partial_tiles(video, window, ell, has_text):
+    """Sizes that are not tile multiples: a video query sees, per axis, the tokens that
+    exist in the span of its window's tiles (placement from the characterisation)."""
+    nv = video[0] * video[1] * video[2]
+    S = seq_len(video, has_text)
+    n = [-(-video[a] // TILE[a]) for a in range(3)]
+    rows = np.arange(S)
+    counts = oracle.allowed_mask(rows, video, window, ell, has_text).sum(axis=1)
+    for i in range(0, nv, 7):
+        c = raster_coords(i, video)
+        span = 1
+        for a in range(3):
+            st = nearest_box_start(c[a] // TILE[a], window[a], n[a])
+            span *= min(video[a], (st + window[a]) * TILE[a]) - st * TILE[a]
+        assert counts[i] == span + ell, (i, counts[i], span + ell)
+    if has_text:
+        assert (counts[nv:] == nv + ell).all()
+
+
 @pytest.mark.parametrize("ell,has_text", [(0, False), (0, True), (100, True), (256, True)])
 def test_full_window_is_sdpa(ell, has_text):
     """A window covering the whole tile grid is plain attention (key padding for text)."""
@@ -167,6 +192,9 @@ def test_full_window_is_sdpa(ell, has_text):
     ((6, 16, 16), (1, 1, 1), 3, True, 4),
     ((18, 16, 32), (3, 1, 3), 0, False, 3),
     ((18, 16, 32), (1, 2, 3), 5, True, 2),
+    ((7, 9, 11), (1, 2, 1), 5, True, 3),
+    ((13, 8, 20), (2, 1, 2), 0, False, 2),
+    ((1, 12, 20), (1, 1, 2), 9, True, 2),
 ])
 def test_brute_force_tiny(video, window, ell, has_text, D):
     S = seq_len(video, has_text)
@@ -327,7 +355,7 @@ def test_key_tiles_from_mask_match_box():
 
 def test_rejects_bad_arguments():
     with pytest.raises(ValueError):
-        oracle.allowed_mask([0], (7, 8, 8), (1, 1, 1), 0, False)
+        oracle.allowed_mask([0], (0, 8, 8), (1, 1, 1), 0, False)
     with pytest.raises(ValueError):
         oracle.allowed_mask([0], (6, 8, 8), (2, 1, 1), 0, False)
     with pytest.raises(ValueError):

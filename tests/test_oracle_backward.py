@@ -39,7 +39,7 @@ def independent_mask(video, window, ell, has_text):
     T, H, W = video
     nv = T * H * W
     S = nv + (256 if has_text else 0)
-    n = [video[a] // TILE[a] for a in range(3)]
+    n = [-(-video[a] // TILE[a]) for a in range(3)]  # partial last tiles included
     idx = np.arange(nv)
     tc = np.stack([(idx // (H * W)) // 6, ((idx // W) % H) // 8, (idx % W) // 8], 1)
     m = np.zeros((S, S), dtype=bool)
@@ -81,6 +81,7 @@ CASES = [
     ((12, 16, 24), [(1, 1, 3), (2, 2, 1)], 100, True, 8, 2),
     ((18, 8, 16), [(3, 1, 1)], 256, True, 8, 1),
     ((6, 16, 24), [(1, 1, 1)], 1, True, 4, 1),
+    ((7, 9, 11), [(1, 2, 1), (2, 1, 2)], 30, True, 4, 1),
 ]
 
 
