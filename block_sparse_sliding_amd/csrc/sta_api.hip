@@ -24,18 +24,23 @@ sta_status make_geom(const sta_dims* d, int32_t has_text, int32_t text_length, G
   if (d->heads > STA_MAX_HEADS) return STA_ERR_SHAPE;
   if (d->head_dim != 64 && d->head_dim != 128) return STA_ERR_SHAPE;
   if (d->T <= 0 || d->H <= 0 || d->W <= 0) return STA_ERR_SHAPE;
-  if (d->T % sta::kTileT || d->H % sta::kTileH || d->W % sta::kTileW) return STA_ERR_SHAPE;
-  const int64_t nt = d->T / sta::kTileT, nh = d->H / sta::kTileH, nw = d->W / sta::kTileW;
+  // sizes that are not tile multiples are covered by the same tile grid, the
+  // last tile along an axis holding the remainder
+  const int64_t nt = (d->T + sta::kTileT - 1) / sta::kTileT;
+  const int64_t nh = (d->H + sta::kTileH - 1) / sta::kTileH;
+  const int64_t nw = (d->W + sta::kTileW - 1) / sta::kTileW;
   if (nt > 1023 || nh > 1023 || nw > 1023) return STA_ERR_SHAPE;
   // tile decoding divides tile indices by nw and nh with 32-bit reciprocals
   if (nt * nh * nw * (nh > nw ? nh : nw) >= (int64_t(1) << 32)) return STA_ERR_SHAPE;
   const int64_t n_video = int64_t(d->T) * d->H * d->W;
   const int64_t S = n_video + (has_text ? STA_TEXT_SLOTS : 0);
+  const int64_t n_vt = nt * nh * nw * sta::kTileRows;
+  const int64_t S_t = n_vt + (has_text ? STA_TEXT_SLOTS : 0);
   // per-slab element offsets and row indices are 32-bit inside the kernels
-  if (S * d->head_dim >= (int64_t(1) << 31)) return STA_ERR_SHAPE;
+  if (S_t * d->head_dim >= (int64_t(1) << 31)) return STA_ERR_SHAPE;
   const int64_t n_q = nt * nh * nw + (has_text ? 1 : 0);
   if (int64_t(d->batch) * d->heads * n_q >= (int64_t(1) << 31)) return STA_ERR_SHAPE;
-  if (int64_t(d->batch) * d->heads * (S / sta::kKeyBlock) >= (int64_t(1) << 31)) return STA_ERR_SHAPE;
+  if (int64_t(d->batch) * d->heads * (S_t / sta::kKeyBlock) >= (int64_t(1) << 31)) return STA_ERR_SHAPE;
   if (has_text) {
     if (text_length < 0 || text_length > STA_TEXT_SLOTS) return STA_ERR_TEXT;
   } else if (text_length != 0) {
@@ -53,6 +58,9 @@ sta_status make_geom(const sta_dims* d, int32_t has_text, int32_t text_length, G
   g->n_tiles = int32_t(nt * nh * nw);
   g->n_video = int32_t(n_video);
   g->S = int32_t(S);
+  g->n_vt = int32_t(n_vt);
+  g->S_t = int32_t(S_t);
+  g->full = (n_vt == n_video) ? 1 : 0;
   g->has_text = has_text ? 1 : 0;
   g->text_length = text_length;
   g->n_q = int32_t(n_q);
@@ -83,7 +91,7 @@ struct Carve {
 
 Carve carve(const Geom& g, int64_t n_ids) {
   Carve c{};
-  const size_t tensor = size_t(g.B) * g.heads * g.S * g.D * 2;
+  const size_t tensor = size_t(g.B) * g.heads * g.S_t * g.D * 2;  // packed, tile-major
   size_t at = 0;
   c.vt = at; at = align_up(at + tensor);
   c.offsets = at; at = align_up(at + (size_t(g.heads) * g.n_q + 1) * 4);
@@ -175,6 +183,7 @@ sta_status sta_tile_gather(const sta_dims* dims, int32_t has_text, const void* x
   Geom g;
   sta_status st = make_geom(dims, has_text, 0, &g);
   if (st != STA_OK) return st;
+  if (!g.full) return STA_ERR_SHAPE;  // both orders have the same rows only for tile multiples
   if (x_raster == nullptr || x_tiled == nullptr) return STA_ERR_NULL;
   if (!aligned16(x_raster) || !aligned16(x_tiled)) return STA_ERR_ALIGN;
   const size_t bytes = size_t(g.B) * g.heads * g.S * g.D * 2;
@@ -188,6 +197,7 @@ sta_status sta_tile_scatter(const sta_dims* dims, int32_t has_text, const void* 
   Geom g;
   sta_status st = make_geom(dims, has_text, 0, &g);
   if (st != STA_OK) return st;
+  if (!g.full) return STA_ERR_SHAPE;
   if (x_raster == nullptr || x_tiled == nullptr) return STA_ERR_NULL;
   if (!aligned16(x_raster) || !aligned16(x_tiled)) return STA_ERR_ALIGN;
   const size_t bytes = size_t(g.B) * g.heads * g.S * g.D * 2;
@@ -300,8 +310,8 @@ struct BwdCarve {
 
 BwdCarve bwd_carve(const Geom& g, int64_t n_ids) {
   BwdCarve c{};
-  const size_t tensor = size_t(g.B) * g.heads * g.S * g.D * 2;
-  const size_t rows = size_t(g.B) * g.heads * g.S * 4;
+  const size_t tensor = size_t(g.B) * g.heads * g.S_t * g.D * 2;  // packed, tile-major
+  const size_t rows = size_t(g.B) * g.heads * g.S_t * 4;          // tile-major rows
   size_t at = 0;
   c.kt = at; at = align_up(at + tensor);
   c.qt = at; at = align_up(at + tensor);
@@ -388,9 +398,9 @@ sta_status backward_impl(const sta_dims* dims, const void* q, const void* k, con
                                          a.claim_kv, s));
   if (st == STA_OK) st = mark(1);
   if (st == STA_OK)
-    st = hip_status(sta::launch_pack_rows(g, k, ws + c.kt, g.n_video + (g.has_text ? g.text_length : 0), s));
-  if (st == STA_OK) st = hip_status(sta::launch_pack_rows(g, q, ws + c.qt, g.S, s));
-  if (st == STA_OK) st = hip_status(sta::launch_pack_rows(g, dout, ws + c.dot, g.S, s));
+    st = hip_status(sta::launch_pack_rows(g, k, ws + c.kt, g.n_vt + (g.has_text ? g.text_length : 0), s));
+  if (st == STA_OK) st = hip_status(sta::launch_pack_rows(g, q, ws + c.qt, g.S_t, s));
+  if (st == STA_OK) st = hip_status(sta::launch_pack_rows(g, dout, ws + c.dot, g.S_t, s));
   if (st == STA_OK) st = mark(2);
   if (st == STA_OK) st = hip_status(sta::launch_schedule_lists(g, win, offsets, ids, s));
   if (st == STA_OK) st = mark(3);

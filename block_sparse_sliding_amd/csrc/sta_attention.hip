@@ -59,6 +59,13 @@
 // Text rows at or after text_length only ever appear in the last text block:
 // their scores are replaced by -inf (a select, so whatever k holds there is
 // ignored) and their packed V rows are zeros.
+// Video sizes that are not tile multiples (the PAD instantiation): the last
+// tile along an axis holds the remainder. Its K rows that do not exist are
+// fetched from a clamped row that does (every source address stays inside
+// the video), their scores are replaced by -inf and their packed V rows are
+// zeros; padding query rows compute on a valid row and are not written. The
+// first block of every window is frame 0 of an existing tile, so the running
+// max is finite from the first block on.
 // Epilogue: O = O^T / l rounded to bf16, lse = (m + log2 l) * ln 2, at raster rows.
 #include <type_traits>
 
@@ -91,7 +98,7 @@ __device__ inline const KernelArgs* kernel_args() {
   return (const KernelArgs*)kp;
 }
 
-template <int D>
+template <int D, bool PAD>
 __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(KernelArgs) {
   constexpr int KS = D / 32;                // k-steps of S^T
   constexpr int DT = D / 16;                // d groups of O^T
@@ -127,13 +134,14 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(KernelArgs) 
   const int bh = unit / g.n_q;
   const int hd = bh % g.heads;
   const bool text_unit = g.has_text && u == g.n_tiles;
-  const int q_row0 = text_unit ? g.n_video : u * kTileRows;
+  const int q_row0 = text_unit ? g.n_vt : u * kTileRows;  // tile-major
   const int q_rows = text_unit ? kTextSlots : kTileRows;
-  const size_t slab = size_t(bh) * g.S * D;  // element offset of this (b, head)
+  const size_t slab = size_t(bh) * g.S * D;      // element offset of this (b, head), raster
+  const size_t slab_t = size_t(bh) * g.S_t * D;  // the same in the packed tile-major V^T
 
   const __bf16* __restrict__ qr = reinterpret_cast<const __bf16*>(a.q) + slab;
   const char* __restrict__ kr = reinterpret_cast<const char*>(a.k) + slab * 2;
-  const char* __restrict__ vtr = reinterpret_cast<const char*>(a.vt) + slab * 2;
+  const char* __restrict__ vtr = reinterpret_cast<const char*>(a.vt) + slab_t * 2;
 
   const int l0 = a.offsets[hd * g.n_q + u];
   const int l1 = a.offsets[hd * g.n_q + u + 1];
@@ -154,8 +162,13 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(KernelArgs) 
   // six blocks of a tile are its six frames, so a tile is decoded once, at its
   // first block): kbase = raster row of the block's 8x8 (h, w) patch origin
   // (video) or first slot (text), krs = raster stride between its 8-row
-  // runs, vrow = its first tile-major row (the packed V^T block).
+  // runs, vrow = its first tile-major row (the packed V^T block). With PAD,
+  // tile_f/h/w are the frames, rows and columns of the current tile that
+  // exist, tile_part says some are missing, and kbase names the last existing
+  // frame in place of one that does not exist.
   int tile_kbase = 0, tile_vrow = 0;
+  int tile_f = kTileT, tile_h = kTileH, tile_w = kTileW;
+  bool tile_part = false;
   auto block_rows = [&](int j, int& kbase, int& krs, int& vrow) {
     if (j < n_vid) {
       const int t = j / BPT;
@@ -168,13 +181,22 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(KernelArgs) 
         const int th = rest - tt * g.nh;
         tile_kbase = (tt * kTileT * g.H + th * kTileH) * g.W + tw * kTileW;
         tile_vrow = tile * kTileRows;
+        if constexpr (PAD) {
+          tile_extent(tt, th, tw, g, tile_f, tile_h, tile_w);
+          tile_part = tile_f < kTileT || tile_h < kTileH || tile_w < kTileW;
+        }
       }
-      kbase = tile_kbase + sub * g.H * g.W;
+      if constexpr (PAD)
+        kbase = tile_kbase + (sub < tile_f ? sub : tile_f - 1) * g.H * g.W;
+      else
+        kbase = tile_kbase + sub * g.H * g.W;
       krs = g.W;
       vrow = tile_vrow + sub * kKeyBlock;
     } else {
-      kbase = vrow = g.n_video + (j - n_vid) * kKeyBlock;
+      kbase = g.n_video + (j - n_vid) * kKeyBlock;
+      vrow = g.n_vt + (j - n_vid) * kKeyBlock;
       krs = kTileW;
+      if constexpr (PAD) tile_part = false;
     }
   };
 
@@ -183,6 +205,21 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(KernelArgs) 
   // share rr/8, so its source is a wave-uniform row pointer plus a per-lane
   // offset (row within the group, chunk) that is the same for every block.
   auto issue_k = [&](int st, int kbase, int krs) {
+    if constexpr (PAD) {
+      if (tile_part) {
+        // per-lane source row, clamped to the rows and columns that exist
+#pragma unroll
+        for (int i = 0; i < IPW; ++i) {
+          const int q = wave * IPW + i;
+          const int rin = (lane >> 2) % RPI;
+          const int h = (q * RPI) >> 3, w = ((q * RPI) & 7) + rin;
+          const int row = kbase + (h < tile_h ? h : tile_h - 1) * krs + (w < tile_w ? w : tile_w - 1);
+          const int chunk = 4 * (lane / (4 * RPI)) + ((lane & 3) ^ sw(q * RPI + rin));
+          dma16(kr + size_t(row) * ROWB + chunk * 16, &lds[st][0][q * 1024]);
+        }
+        return;
+      }
+    }
 #pragma unroll
     for (int i = 0; i < IPW; ++i) {
       const int q = wave * IPW + i;
@@ -219,7 +256,8 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(KernelArgs) 
     for (int c = 0; c < QT; ++c) {
       int row = wave * RPW + c * 16 + (lane & 15);
       row = row < q_rows ? row : q_rows - 1;
-      const int rr = tiled_to_raster(q_row0 + row, g);
+      int rr = tiled_to_raster(q_row0 + row, g);
+      if constexpr (PAD) rr = rr < 0 ? 0 : rr;  // padding row: any valid row, result discarded
       const bf16x8* src = reinterpret_cast<const bf16x8*>(qr + size_t(rr) * D + (lane >> 4) * 8);
   #pragma unroll
       for (int ks = 0; ks < KS; ++ks) qf[c][ks] = src[ks * 4];
@@ -289,6 +327,24 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(KernelArgs) 
               if (key0 + 16 * kt + r >= text_len)
   #pragma unroll
                 for (int c = 0; c < QT; ++c) s[c][kt][r] = -INFINITY;
+        }
+        if constexpr (PAD) {
+          // keys of a partial tile that do not exist (the tile state still
+          // describes block j: block j + 1 is decoded below). Key 16kt + 4(l/16)
+          // + r of the block sits at patch row 2kt + l/32, column 4((l/16)&1) + r.
+          if (j < n_vid && tile_part) {
+            const int sub = j - (j / BPT) * BPT;
+            int hb = lane >> 5;
+            asm volatile("" : "+v"(hb));
+            const int wb = ((lane >> 4) & 1) * 4;
+  #pragma unroll
+            for (int kt = 0; kt < 4; ++kt)
+  #pragma unroll
+              for (int r = 0; r < 4; ++r)
+                if (sub >= tile_f || 2 * kt + hb >= tile_h || wb + r >= tile_w)
+  #pragma unroll
+                  for (int c = 0; c < QT; ++c) s[c][kt][r] = -INFINITY;
+          }
         }
       }
       if (j + 1 < n_blk) issue(j + 1, stage ^ 1);
@@ -366,8 +422,8 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(KernelArgs) 
       const float l = swap32_sum(swap16_sum(l_part[c]));
       const float inv = __builtin_amdgcn_rcpf(l);
       const int row = wave * RPW + c * 16 + (lane & 15);
-      if (row < q_rows) {
-        const int rr = tiled_to_raster(q_row0 + row, g);
+      const int rr = row < q_rows ? tiled_to_raster(q_row0 + row, g) : -1;
+      if (rr >= 0) {
         __bf16* dst = outr + size_t(rr) * D + (lane >> 4) * 4;
   #pragma unroll
         for (int d = 0; d < DT; ++d) {
@@ -386,24 +442,27 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(KernelArgs) 
 }
 
 // Resident workgroups of the kernel on the current device (cached per device).
-template <int D>
+template <int D, bool PAD>
 int persistent_grid() {
   static int cache[kMaxDevices] = {};
-  return resident_workgroups(sta_attention_kernel<D>, kThreads, cache);
+  return resident_workgroups(sta_attention_kernel<D, PAD>, kThreads, cache);
+}
+
+template <int D, bool PAD>
+hipError_t launch(const Geom& g, const FwdArgs& a, hipStream_t stream) {
+  const int units = g.B * g.heads * g.n_q;
+  const int resident = persistent_grid<D, PAD>();
+  if (resident <= 0) return hipErrorInvalidDevice;
+  const int grid = units < resident ? units : resident;
+  sta_attention_kernel<D, PAD><<<grid, kThreads, 0, stream>>>(KernelArgs{g, a});
+  return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_attention(const Geom& g, const FwdArgs& a, hipStream_t stream) {
-  const int units = g.B * g.heads * g.n_q;
-  const int resident = g.D == 128 ? persistent_grid<128>() : persistent_grid<64>();
-  if (resident <= 0) return hipErrorInvalidDevice;
-  const int grid = units < resident ? units : resident;
-  if (g.D == 128)
-    sta_attention_kernel<128><<<grid, kThreads, 0, stream>>>(KernelArgs{g, a});
-  else
-    sta_attention_kernel<64><<<grid, kThreads, 0, stream>>>(KernelArgs{g, a});
-  return hipGetLastError();
+  if (g.full) return g.D == 128 ? launch<128, false>(g, a, stream) : launch<64, false>(g, a, stream);
+  return g.D == 128 ? launch<128, true>(g, a, stream) : launch<64, true>(g, a, stream);
 }
 
 }  // namespace sta

@@ -34,6 +34,15 @@
 // found per unit by a scan over the axis; text query rows see every video key
 // and every valid text key. Text key slots at or after text_length are seen by
 // no query and get zero gradients.
+//
+// Video sizes that are not tile multiples (the PAD instantiations): the last
+// tile along an axis holds the remainder, and its rows that do not exist are
+// padding. Raw rows of a partial tile are fetched from clamped rows that exist
+// (every address stays inside the video); packed rows of padding are zeros.
+// prep gives padding query rows lse2 = +inf and delta = 0, so their P and dS
+// are exactly 0 wherever they are streamed; padding key rows add nothing to dq
+// (their packed K^T rows are zero and their dS finite, the clamped copy of a
+// key of the same tile) and padding rows of dq, dk, dv are not written.
 #include <type_traits>
 
 #include "sta_device.h"
@@ -122,7 +131,7 @@ __device__ inline void seeing_interval(int kc, int w, int n, int& lo, int& len) 
 }
 
 // ---------------------------------------------------------------- prep
-// grid (S / 64, B*heads), 256 threads: 4 threads per tile-major row.
+// grid (S_t / 64, B*heads), 256 threads: 4 threads per tile-major row.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(Geom g, const __bf16* __restrict__ out,
                                                       const __bf16* __restrict__ dout,
@@ -134,6 +143,13 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(Geom g, const __bf16* __r
   const int r = blockIdx.x * 64 + (threadIdx.x >> 2);
   const int part = threadIdx.x & 3;
   const int rr = tiled_to_raster(r, g);
+  if (rr < 0) {  // padding row of a partial tile: P = 2^(s c' - inf) = 0 wherever it is streamed
+    if (part == 0) {
+      delta[bh * g.S_t + r] = 0.f;
+      lse2[bh * g.S_t + r] = INFINITY;
+    }
+    return;
+  }
   const size_t base = (bh * g.S + rr) * D + part * PER;
   float acc = 0.f;
 #pragma unroll
@@ -146,8 +162,8 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(Geom g, const __bf16* __r
   acc += __shfl_xor(acc, 1);
   acc += __shfl_xor(acc, 2);
   if (part == 0) {
-    delta[bh * g.S + r] = acc;
-    lse2[bh * g.S + r] = lse[bh * g.S + rr] * kLog2e;
+    delta[bh * g.S_t + r] = acc;
+    lse2[bh * g.S_t + r] = lse[bh * g.S + rr] * kLog2e;
   }
 }
 
@@ -157,7 +173,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(Geom g, const __bf16* __r
 // slots (8 waves x 32 rows). Unit order: text units first, then the tiles.
 __device__ inline int dq_units_per_head(const Geom& g) { return 2 * g.n_tiles + (g.has_text ? 1 : 0); }
 
-template <int D>
+template <int D, bool PAD>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(KernelArgs) {
   constexpr int KS = D / 32;
   constexpr int DT = D / 16;
@@ -199,7 +215,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(KernelArgs) {
     if (unit < n_text_units) {
       bh = unit;
       u = g.n_tiles;
-      q_row0 = g.n_video;
+      q_row0 = g.n_vt;
       q_rows = kTextSlots;
     } else {
       const int e = unit - n_text_units;
@@ -215,9 +231,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(KernelArgs) {
     const __bf16* __restrict__ dor = reinterpret_cast<const __bf16*>(a.dout) + slab;
     const char* __restrict__ kr = reinterpret_cast<const char*>(a.k) + slab * 2;
     const char* __restrict__ vr = reinterpret_cast<const char*>(a.v) + slab * 2;
-    const char* __restrict__ ktr = reinterpret_cast<const char*>(a.kt) + slab * 2;
-    const float* __restrict__ lse2 = a.lse2 + size_t(bh) * g.S;
-    const float* __restrict__ dlt = a.delta + size_t(bh) * g.S;
+    const size_t slab_t = size_t(bh) * g.S_t * D;  // packed tile-major tensors
+    const char* __restrict__ ktr = reinterpret_cast<const char*>(a.kt) + slab_t * 2;
+    const float* __restrict__ lse2 = a.lse2 + size_t(bh) * g.S_t;
+    const float* __restrict__ dlt = a.delta + size_t(bh) * g.S_t;
 
     const int l0 = a.offsets[hd * g.n_q + u];
     const int l1 = a.offsets[hd * g.n_q + u + 1];
@@ -229,7 +246,12 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(KernelArgs) {
     const __attribute__((address_space(4))) int32_t* ids =
         (const __attribute__((address_space(4))) int32_t*)(a.ids + l0);
 
+    // with PAD, tile_f/h/w: frames, rows and columns of the current key tile
+    // that exist (tile_part: some are missing); kbase then names the last
+    // existing frame in place of one that does not exist
     int tile_kbase = 0, tile_vrow = 0;
+    int tile_f = kTileT, tile_h = kTileH, tile_w = kTileW;
+    bool tile_part = false;
     auto block_rows = [&](int j, int& kbase, int& krs, int& vrow) {
       if (j < n_vid) {
         const int t = j / BPT;
@@ -242,18 +264,41 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(KernelArgs) {
           const int th = rest - tt * g.nh;
           tile_kbase = (tt * kTileT * g.H + th * kTileH) * g.W + tw * kTileW;
           tile_vrow = tile * kTileRows;
+          if constexpr (PAD) {
+            tile_extent(tt, th, tw, g, tile_f, tile_h, tile_w);
+            tile_part = tile_f < kTileT || tile_h < kTileH || tile_w < kTileW;
+          }
         }
-        kbase = tile_kbase + sub * g.H * g.W;
+        if constexpr (PAD)
+          kbase = tile_kbase + (sub < tile_f ? sub : tile_f - 1) * g.H * g.W;
+        else
+          kbase = tile_kbase + sub * g.H * g.W;
         krs = g.W;
         vrow = tile_vrow + sub * kKeyBlock;
       } else {
-        kbase = vrow = g.n_video + (j - n_vid) * kKeyBlock;
+        kbase = g.n_video + (j - n_vid) * kKeyBlock;
+        vrow = g.n_vt + (j - n_vid) * kKeyBlock;
         krs = kTileW;
+        if constexpr (PAD) tile_part = false;
       }
     };
     // raw rows kbase + (rr/8)*krs + rr%8 of tensor `src` into LDS region `dst`
     // (the forward's swizzled K layout)
     auto issue_raw = [&](const char* src, char* dst, int kbase, int krs) {
+      if constexpr (PAD) {
+        if (tile_part) {  // per-lane rows, clamped to the rows and columns that exist
+#pragma unroll
+          for (int i = 0; i < IPW; ++i) {
+            const int q = wave * IPW + i;
+            const int rin = (lane >> 2) % RPI;
+            const int h = (q * RPI) >> 3, w = ((q * RPI) & 7) + rin;
+            const int row = kbase + (h < tile_h ? h : tile_h - 1) * krs + (w < tile_w ? w : tile_w - 1);
+            const int chunk = 4 * (lane / (4 * RPI)) + ((lane & 3) ^ sw(q * RPI + rin));
+            dma16(src + size_t(row) * ROWB + chunk * 16, dst + q * 1024);
+          }
+          return;
+        }
+      }
 #pragma unroll
       for (int i = 0; i < IPW; ++i) {
         const int q = wave * IPW + i;
@@ -283,7 +328,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(KernelArgs) {
 #pragma unroll
       for (int c = 0; c < QT; ++c) {
         const int row = wave * RPW + c * 16 + (lane & 15);  // < q_rows for every unit shape
-        const int rr = tiled_to_raster(q_row0 + row, g);
+        int rr = tiled_to_raster(q_row0 + row, g);
+        if constexpr (PAD) rr = rr < 0 ? 0 : rr;  // padding row: any valid row, result discarded
         const bf16x8* qs8 = reinterpret_cast<const bf16x8*>(qr + size_t(rr) * D + (lane >> 4) * 8);
         const bf16x8* ds8 = reinterpret_cast<const bf16x8*>(dor + size_t(rr) * D + (lane >> 4) * 8);
 #pragma unroll
@@ -394,6 +440,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(KernelArgs) {
       for (int c = 0; c < QT; ++c) {
         const int row = wave * RPW + c * 16 + (lane & 15);
         const int rr = tiled_to_raster(q_row0 + row, g);
+        if (PAD && rr < 0) continue;
         __bf16* dst = dqr + size_t(rr) * D + (lane >> 4) * 4;
 #pragma unroll
         for (int d = 0; d < DT; ++d) {
@@ -416,7 +463,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(KernelArgs) {
 // (bh, tile, part).
 __device__ inline int kv_units_per_head(const Geom& g) { return 2 * g.n_tiles + (g.has_text ? 1 : 0); }
 
-template <int D>
+template <int D, bool PAD>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(KernelArgs) {
   constexpr int KS = D / 32;
   constexpr int DT = D / 16;
@@ -453,9 +500,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(KernelArgs) {
     int bh, key_row0, unit_keys;
     bool text_unit;
     int box_t = 0, box_h = 0, box_w = 0, lo_t = 0, lo_h = 0, lo_w = 0;
+    bool keys_exist = true;  // PAD: false when none of the unit's key frames exist
     if (unit < n_text_units) {
       bh = unit;
-      key_row0 = g.n_video;
+      key_row0 = g.n_vt;
       unit_keys = kTextSlots;
       text_unit = true;
     } else {
@@ -474,24 +522,31 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(KernelArgs) {
       seeing_interval(tt, win_t(p), g.nt, lo_t, box_t);
       seeing_interval(th, win_h(p), g.nh, lo_h, box_h);
       seeing_interval(tw, win_w(p), g.nw, lo_w, box_w);
+      if constexpr (PAD) keys_exist = (r & 1) == 0 || g.T - tt * kTileT > 256 / (kTileH * kTileW);
     }
     const size_t slab = size_t(bh) * g.S * D;
+    const size_t slab_t = size_t(bh) * g.S_t * D;  // packed tile-major tensors
     const int text_len = g.has_text ? g.text_length : 0;
     // text key slots at or after text_len are seen by nobody
-    const int valid_keys = text_unit ? min(max(g.n_video + text_len - key_row0, 0), unit_keys) : unit_keys;
+    const int valid_keys = text_unit ? min(max(g.n_vt + text_len - key_row0, 0), unit_keys)
+                                     : (keys_exist ? unit_keys : 0);
     const int n_qtiles = text_unit ? g.n_tiles : box_t * box_h * box_w;
     const int n_blk = valid_keys == 0 ? 0 : n_qtiles * BPT + (g.has_text ? kTextSlots / kQueryBlock : 0);
 
     const char* __restrict__ qr = reinterpret_cast<const char*>(a.q) + slab * 2;
     const char* __restrict__ dor = reinterpret_cast<const char*>(a.dout) + slab * 2;
-    const char* __restrict__ qtr = reinterpret_cast<const char*>(a.qt) + slab * 2;
-    const char* __restrict__ dotr = reinterpret_cast<const char*>(a.dot) + slab * 2;
-    const char* __restrict__ lse2 = reinterpret_cast<const char*>(a.lse2 + size_t(bh) * g.S);
-    const char* __restrict__ dlt = reinterpret_cast<const char*>(a.delta + size_t(bh) * g.S);
+    const char* __restrict__ qtr = reinterpret_cast<const char*>(a.qt) + slab_t * 2;
+    const char* __restrict__ dotr = reinterpret_cast<const char*>(a.dot) + slab_t * 2;
+    const char* __restrict__ lse2 = reinterpret_cast<const char*>(a.lse2 + size_t(bh) * g.S_t);
+    const char* __restrict__ dlt = reinterpret_cast<const char*>(a.delta + size_t(bh) * g.S_t);
     auto sw = [](int row) { return (row >> 2) & 2; };
 
-    // query block j: raster origin of its rows and its first tile-major row
+    // query block j: raster origin of its rows and its first tile-major row;
+    // with PAD, tile_f/h/w and tile_part describe the current query tile as in
+    // the dq kernel
     int tile_qbase = 0, tile_vrow = 0;
+    int tile_f = kTileT, tile_h = kTileH, tile_w = kTileW;
+    bool tile_part = false;
     auto block_rows = [&](int j, int& qbase, int& qrs, int& vrow) {
       if (j < n_qtiles * BPT) {
         const int t = j / BPT;
@@ -511,16 +566,39 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(KernelArgs) {
           }
           tile_qbase = (tt * kTileT * g.H + th * kTileH) * g.W + tw * kTileW;
           tile_vrow = ((tt * g.nh + th) * g.nw + tw) * kTileRows;
+          if constexpr (PAD) {
+            tile_extent(tt, th, tw, g, tile_f, tile_h, tile_w);
+            tile_part = tile_f < kTileT || tile_h < kTileH || tile_w < kTileW;
+          }
         }
-        qbase = tile_qbase + sub * g.H * g.W;
+        if constexpr (PAD)
+          qbase = tile_qbase + (sub < tile_f ? sub : tile_f - 1) * g.H * g.W;
+        else
+          qbase = tile_qbase + sub * g.H * g.W;
         qrs = g.W;
         vrow = tile_vrow + sub * kQueryBlock;
       } else {
-        qbase = vrow = g.n_video + (j - n_qtiles * BPT) * kQueryBlock;
+        qbase = g.n_video + (j - n_qtiles * BPT) * kQueryBlock;
+        vrow = g.n_vt + (j - n_qtiles * BPT) * kQueryBlock;
         qrs = kTileW;
+        if constexpr (PAD) tile_part = false;
       }
     };
     auto issue_raw = [&](const char* src, char* dst, int qbase, int qrs) {
+      if constexpr (PAD) {
+        if (tile_part) {  // per-lane rows, clamped to the rows and columns that exist
+#pragma unroll
+          for (int i = 0; i < IPW; ++i) {
+            const int q = wave * IPW + i;
+            const int rin = (lane >> 2) % RPI;
+            const int h = (q * RPI) >> 3, w = ((q * RPI) & 7) + rin;
+            const int row = qbase + (h < tile_h ? h : tile_h - 1) * qrs + (w < tile_w ? w : tile_w - 1);
+            const int chunk = 4 * (lane / (4 * RPI)) + ((lane & 3) ^ sw(q * RPI + rin));
+            dma16(src + size_t(row) * ROWB + chunk * 16, dst + q * 1024);
+          }
+          return;
+        }
+      }
 #pragma unroll
       for (int i = 0; i < IPW; ++i) {
         const int q = wave * IPW + i;
@@ -568,12 +646,14 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(KernelArgs) {
 #pragma unroll
       for (int kg = 0; kg < KT; ++kg) {
         const int key = key_row0 + wave * 16 * KT + 16 * kg + (lane & 15);
-        key_ok[kg] = !text_unit || key < g.n_video + text_len;
+        key_ok[kg] = !text_unit || key < g.n_vt + text_len;
         kras[kg] = tiled_to_raster(key, g);
+        // padding key row (PAD): computes on a valid row, never written
+        const int ksrc = PAD && kras[kg] < 0 ? 0 : kras[kg];
         const bf16x8* k8 = reinterpret_cast<const bf16x8*>(reinterpret_cast<const __bf16*>(a.k) + slab +
-                                                           size_t(kras[kg]) * D + (lane >> 4) * 8);
+                                                           size_t(ksrc) * D + (lane >> 4) * 8);
         const bf16x8* v8 = reinterpret_cast<const bf16x8*>(reinterpret_cast<const __bf16*>(a.v) + slab +
-                                                           size_t(kras[kg]) * D + (lane >> 4) * 8);
+                                                           size_t(ksrc) * D + (lane >> 4) * 8);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
           kf[kg][ks] = k8[ks * 4];
@@ -681,6 +761,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(KernelArgs) {
       // dk = c * acc, dv = acc; C row = d (4 (l/16) + r of each 16-group), column = key
 #pragma unroll
       for (int kg = 0; kg < KT; ++kg) {
+        if (PAD && kras[kg] < 0) continue;
         __bf16* dkr = reinterpret_cast<__bf16*>(a.dk) + slab + size_t(kras[kg]) * D + (lane >> 4) * 4;
         __bf16* dvr = reinterpret_cast<__bf16*>(a.dv) + slab + size_t(kras[kg]) * D + (lane >> 4) * 4;
 #pragma unroll
@@ -697,15 +778,25 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(KernelArgs) {
   }
 }
 
-template <int D>
-int dq_grid() {
+template <int D, bool PAD>
+hipError_t launch_dq(const Geom& g, const Windows& win, const BwdArgs& a, hipStream_t stream) {
   static int cache[kMaxDevices] = {};
-  return resident_workgroups(bwd_dq_kernel<D>, kThreads, cache);
+  const int units = g.B * g.heads * (2 * g.n_tiles + (g.has_text ? 1 : 0));
+  const int resident = resident_workgroups(bwd_dq_kernel<D, PAD>, kThreads, cache);
+  if (resident <= 0) return hipErrorInvalidDevice;
+  const int grid = units < resident ? units : resident;
+  bwd_dq_kernel<D, PAD><<<grid, kThreads, 0, stream>>>(KernelArgs{g, win, a});
+  return hipGetLastError();
 }
-template <int D>
-int dkv_grid() {
+template <int D, bool PAD>
+hipError_t launch_dkv(const Geom& g, const Windows& win, const BwdArgs& a, hipStream_t stream) {
   static int cache[kMaxDevices] = {};
-  return resident_workgroups(bwd_dkv_kernel<D>, kThreads, cache);
+  const int units = g.B * g.heads * (2 * g.n_tiles + (g.has_text ? 1 : 0));
+  const int resident = resident_workgroups(bwd_dkv_kernel<D, PAD>, kThreads, cache);
+  if (resident <= 0) return hipErrorInvalidDevice;
+  const int grid = units < resident ? units : resident;
+  bwd_dkv_kernel<D, PAD><<<grid, kThreads, 0, stream>>>(KernelArgs{g, win, a});
+  return hipGetLastError();
 }
 
 __global__ void zero_claims_kernel(int32_t* a, int32_t* b) {
@@ -718,7 +809,7 @@ __global__ void zero_claims_kernel(int32_t* a, int32_t* b) {
 hipError_t launch_bwd_prep(const Geom& g, const void* out, const void* dout, const float* lse,
                            float* lse2, float* delta, int32_t* claim_q, int32_t* claim_kv,
                            hipStream_t stream) {
-  dim3 grid(g.S / 64, g.B * g.heads);
+  dim3 grid(g.S_t / 64, g.B * g.heads);
   if (g.D == 128)
     bwd_prep_kernel<128><<<grid, 256, 0, stream>>>(g, (const __bf16*)out, (const __bf16*)dout, lse, lse2, delta);
   else
@@ -728,27 +819,13 @@ hipError_t launch_bwd_prep(const Geom& g, const void* out, const void* dout, con
 }
 
 hipError_t launch_bwd_dq(const Geom& g, const Windows& win, const BwdArgs& a, hipStream_t stream) {
-  const int units = g.B * g.heads * (2 * g.n_tiles + (g.has_text ? 1 : 0));
-  const int resident = g.D == 128 ? dq_grid<128>() : dq_grid<64>();
-  if (resident <= 0) return hipErrorInvalidDevice;
-  const int grid = units < resident ? units : resident;
-  if (g.D == 128)
-    bwd_dq_kernel<128><<<grid, kThreads, 0, stream>>>(KernelArgs{g, win, a});
-  else
-    bwd_dq_kernel<64><<<grid, kThreads, 0, stream>>>(KernelArgs{g, win, a});
-  return hipGetLastError();
+  if (g.full) return g.D == 128 ? launch_dq<128, false>(g, win, a, stream) : launch_dq<64, false>(g, win, a, stream);
+  return g.D == 128 ? launch_dq<128, true>(g, win, a, stream) : launch_dq<64, true>(g, win, a, stream);
 }
 
 hipError_t launch_bwd_dkv(const Geom& g, const Windows& win, const BwdArgs& a, hipStream_t stream) {
-  const int units = g.B * g.heads * (2 * g.n_tiles + (g.has_text ? 1 : 0));
-  const int resident = g.D == 128 ? dkv_grid<128>() : dkv_grid<64>();
-  if (resident <= 0) return hipErrorInvalidDevice;
-  const int grid = units < resident ? units : resident;
-  if (g.D == 128)
-    bwd_dkv_kernel<128><<<grid, kThreads, 0, stream>>>(KernelArgs{g, win, a});
-  else
-    bwd_dkv_kernel<64><<<grid, kThreads, 0, stream>>>(KernelArgs{g, win, a});
-  return hipGetLastError();
+  if (g.full) return g.D == 128 ? launch_dkv<128, false>(g, win, a, stream) : launch_dkv<64, false>(g, win, a, stream);
+  return g.D == 128 ? launch_dkv<128, true>(g, win, a, stream) : launch_dkv<64, true>(g, win, a, stream);
 }
 
 }  // namespace sta

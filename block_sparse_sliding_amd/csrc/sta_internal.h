@@ -24,10 +24,13 @@ constexpr int kWinBits = 10;  // each packed window component uses 10 bits
 struct Geom {
   int32_t B, heads, D;
   int32_t T, H, W;
-  int32_t nt, nh, nw;  // tile-grid size
+  int32_t nt, nh, nw;  // tile-grid size: ceil(T/6), ceil(H/8), ceil(W/8)
   int32_t n_tiles;     // nt * nh * nw
-  int32_t n_video;     // T * H * W
-  int32_t S;           // n_video + (has_text ? 256 : 0)
+  int32_t n_video;     // T * H * W (raster video rows)
+  int32_t S;           // n_video + (has_text ? 256 : 0): rows of the caller's tensors
+  int32_t n_vt;        // n_tiles * 384: tile-major video rows, padding rows of partial tiles included
+  int32_t S_t;         // n_vt + (has_text ? 256 : 0): rows of the tile-major (packed) tensors
+  int32_t full;        // 1 when T, H, W are multiples of the tile (no padding rows)
   int32_t has_text;
   int32_t text_length;
   int32_t n_q;         // query units per head: n_tiles (+1 text unit)
@@ -46,9 +49,12 @@ __host__ __device__ inline int win_t(uint32_t p) { return int(p & 1023u); }
 __host__ __device__ inline int win_h(uint32_t p) { return int((p >> 10) & 1023u); }
 __host__ __device__ inline int win_w(uint32_t p) { return int((p >> 20) & 1023u); }
 
-// Tile-major row r (within one [S] slab) -> raster row. Text rows map to themselves.
+// Tile-major row r (within one [S_t] slab) -> raster row, or -1 for a padding
+// row of a partial tile (a video size that is not a multiple of the tile is
+// covered by the same tile grid, the last tile along an axis holding the
+// remainder). Text rows follow the video in both orders.
 __host__ __device__ inline int tiled_to_raster(int r, const Geom& g) {
-  if (r >= g.n_video) return r;
+  if (r >= g.n_vt) return r - g.n_vt + g.n_video;
   const int tile = r / kTileRows;
   const int j = r - tile * kTileRows;
   const int dt = j >> 6, dh = (j >> 3) & 7, dw = j & 7;
@@ -57,7 +63,20 @@ __host__ __device__ inline int tiled_to_raster(int r, const Geom& g) {
   const int th = rest % g.nh;
   const int tt = rest / g.nh;
   const int t = tt * kTileT + dt, h = th * kTileH + dh, w = tw * kTileW + dw;
+  if (t >= g.T || h >= g.H || w >= g.W) return -1;
   return (t * g.H + h) * g.W + w;
+}
+
+// Extent of tile (tt, th, tw) inside the video: frames (of 6), rows (of 8)
+// and columns (of 8) that exist.
+__host__ __device__ inline void tile_extent(int tt, int th, int tw, const Geom& g, int& frames,
+                                            int& rows, int& cols) {
+  frames = g.T - tt * kTileT;
+  frames = frames < kTileT ? frames : kTileT;
+  rows = g.H - th * kTileH;
+  rows = rows < kTileH ? rows : kTileH;
+  cols = g.W - tw * kTileW;
+  cols = cols < kTileW ? cols : kTileW;
 }
 
 // Launchers (each enqueues one kernel on `stream` and returns hipGetLastError()).
@@ -68,8 +87,9 @@ hipError_t launch_rows_permute(const Geom& g, const void* src, void* dst, bool t
 // fragments, the A operand of O^T += V^T P^T (layout documented at the pack
 // kernel).
 hipError_t launch_pack_v(const Geom& g, const void* v, void* vt, hipStream_t stream);
-// The same fragment packing for any [B][heads][S][D] bf16 tensor; tile-major
-// rows at or after valid_end are written as zeros.
+// The same fragment packing for any [B][heads][S][D] bf16 raster tensor, into
+// [B][heads][S_t][D] tile-major fragments; tile-major rows at or after
+// valid_end, and padding rows of partial tiles, are written as zeros.
 hipError_t launch_pack_rows(const Geom& g, const void* src, void* dst, int valid_end,
                             hipStream_t stream);
 hipError_t launch_schedule_lists(const Geom& g, const Windows& win, int32_t* offsets,

@@ -52,13 +52,15 @@ __global__ __launch_bounds__(kThreads) void pack_v_kernel(Geom g, const uint4* _
   constexpr int DT = D / 16;     // column groups
   constexpr int PITCH = D + 2;   // LDS row pitch in bf16 (odd word count: no bank aliasing)
   __shared__ uint16_t rows[kKeyBlock * PITCH];
-  const size_t slab = size_t(blockIdx.y) * g.S * CPR;
+  const size_t slab_in = size_t(blockIdx.y) * g.S * CPR;     // raster rows
+  const size_t slab_out = size_t(blockIdx.y) * g.S_t * CPR;  // tile-major rows
   const int r0 = blockIdx.x * kKeyBlock;
 #pragma unroll
   for (int c = threadIdx.x; c < kKeyBlock * CPR; c += kThreads) {
     const int r = c / CPR, col = c % CPR;
     uint4 x = make_uint4(0, 0, 0, 0);
-    if (r0 + r < valid_end) x = v[slab + size_t(tiled_to_raster(r0 + r, g)) * CPR + col];
+    const int rr = r0 + r < valid_end ? tiled_to_raster(r0 + r, g) : -1;
+    if (rr >= 0) x = v[slab_in + size_t(rr) * CPR + col];
     uint32_t* dst = reinterpret_cast<uint32_t*>(&rows[r * PITCH]) + col * 4;
     dst[0] = x.x;
     dst[1] = x.y;
@@ -66,7 +68,7 @@ __global__ __launch_bounds__(kThreads) void pack_v_kernel(Geom g, const uint4* _
     dst[3] = x.w;
   }
   __syncthreads();
-  uint4* out = vt + slab + size_t(r0) * CPR;
+  uint4* out = vt + slab_out + size_t(r0) * CPR;
 #pragma unroll
   for (int o = threadIdx.x; o < kKeyBlock * CPR; o += kThreads) {
     const int frag = o >> 6, l = o & 63;
@@ -97,7 +99,7 @@ hipError_t launch_rows_permute(const Geom& g, const void* src, void* dst, bool t
 
 hipError_t launch_pack_rows(const Geom& g, const void* src, void* dst, int valid_end,
                             hipStream_t stream) {
-  dim3 grid(g.S / kKeyBlock, g.B * g.heads);
+  dim3 grid(g.S_t / kKeyBlock, g.B * g.heads);
   if (g.D == 128)
     pack_v_kernel<128><<<grid, kThreads, 0, stream>>>(g, (const uint4*)src, (uint4*)dst, valid_end);
   else
@@ -106,7 +108,7 @@ hipError_t launch_pack_rows(const Geom& g, const void* src, void* dst, int valid
 }
 
 hipError_t launch_pack_v(const Geom& g, const void* v, void* vt, hipStream_t stream) {
-  return launch_pack_rows(g, v, vt, g.n_video + (g.has_text ? g.text_length : 0), stream);
+  return launch_pack_rows(g, v, vt, g.n_vt + (g.has_text ? g.text_length : 0), stream);
 }
 
 }  // namespace sta

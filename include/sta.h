@@ -9,6 +9,15 @@
  * text slots of which the first `text_length` are valid. The attention map
  * holds only fully-dense or fully-empty tile blocks.
  *
+ * Video sizes need not be tile multiples. The page's kernel takes only
+ * multiples of (6, 8, 8) and leaves other sizes to the caller; this library
+ * reads them as follows: the tile grid is (n_t, n_h, n_w) = (ceil(T/6),
+ * ceil(H/8), ceil(W/8)), the last tile along an axis holds the remainder
+ * (the tokens of tile (i, j, k) are those of its 6x8x8 box that exist),
+ * windows are placed on that grid exactly as for multiples, and a query sees
+ * the tokens that exist in its window's tiles. For multiples this is the
+ * page's operation unchanged.
+ *
  * Conventions shared by every entry point
  * ---------------------------------------
  * - Sequence order ("raster"): video token (t, h, w) is row (t*H + h)*W + w;
@@ -26,9 +35,9 @@
  *   errors. Faults inside kernels surface at the caller's next stream sync.
  * - window_sizes is a HOST array of heads*3 int32: (w_t, w_h, w_w) in tiles
  *   for head 0, then head 1, ... Each component must lie in [1, n_axis]
- *   where (n_t, n_h, n_w) = (T/6, H/8, W/8). At the grid border the window
- *   is shifted inward (start = clamp(c - w/2, 0, n - w) per axis) so every
- *   video query sees exactly w_t*w_h*w_w tiles.
+ *   where (n_t, n_h, n_w) = (ceil(T/6), ceil(H/8), ceil(W/8)). At the grid
+ *   border the window is shifted inward (start = clamp(c - w/2, 0, n - w)
+ *   per axis) so every video query sees exactly w_t*w_h*w_w tiles.
  */
 #ifndef STA_H
 #define STA_H
@@ -43,9 +52,10 @@ extern "C" {
 typedef enum {
   STA_OK = 0,
   STA_ERR_NULL = 1,      /* a required pointer is NULL, or batch/heads <= 0      */
-  STA_ERR_SHAPE = 2,     /* T,H,W not positive multiples of (6,8,8); head_dim
-                            not 64 or 128; heads > STA_MAX_HEADS; a tile-grid
-                            axis > 1023 tiles; or sizes too large to index     */
+  STA_ERR_SHAPE = 2,     /* T,H,W not positive (for sta_tile_gather/scatter:
+                            not multiples of (6,8,8)); head_dim not 64 or 128;
+                            heads > STA_MAX_HEADS; a tile-grid axis > 1023
+                            tiles; or sizes too large to index                 */
   STA_ERR_WINDOW = 3,    /* a window component outside [1, n_axis]              */
   STA_ERR_TEXT = 4,      /* text_length outside [0, 256], or != 0 without text  */
   STA_ERR_ALIGN = 5,     /* a device pointer is not 16-byte aligned             */
@@ -61,7 +71,7 @@ typedef struct {
   int32_t batch;    /* B >= 1                                  */
   int32_t heads;    /* 1 .. STA_MAX_HEADS                      */
   int32_t head_dim; /* D: 64 or 128                            */
-  int32_t T, H, W;  /* video size in tokens: multiples of 6, 8, 8 */
+  int32_t T, H, W;  /* video size in tokens, each >= 1             */
 } sta_dims;
 
 /* Human-readable name of a status code (static string, never NULL). */
@@ -102,7 +112,8 @@ size_t sta_workspace_bytes(const sta_dims* dims, const int32_t* window_sizes,
  * Returns STA_OK once the four launches (V^T pack into tile-major MFMA
  * fragment order, schedule lists, work order, fused attention reading q and k
  * and writing out/lse in raster order, all through the tile map) are
- * enqueued on `stream`. The workspace holds the packed V^T (the size of v),
+ * enqueued on `stream`. The workspace holds the packed V^T (the size of v,
+ * its video rows padded to whole tiles),
  * the schedule (a few MB at most) and 2 KB of work-queue heads. The attention
  * launch is a persistent grid (one workgroup per resident slot on the current
  * device) whose workgroups take query units from per-XCD queues, their own
@@ -136,7 +147,8 @@ sta_status sta_forward_timed(const sta_dims* dims, const void* q, const void* k,
  * (t, h, w) moves to row  tile*384 + ((t%6)*8 + h%8)*8 + w%8  with
  * tile = ((t/6)*n_h + h/8)*n_w + w/8, so each tile is 384 contiguous rows;
  * text rows keep their positions. x_raster and x_tiled are device buffers
- * of the same size and must not overlap.
+ * of the same size and must not overlap. Only for T, H, W multiples of
+ * (6, 8, 8) (otherwise STA_ERR_SHAPE): then both orders hold the same rows.
  */
 sta_status sta_tile_gather(const sta_dims* dims, int32_t has_text,
                            const void* x_raster, void* x_tiled, void* stream);
@@ -177,8 +189,9 @@ sta_status sta_build_schedule(const sta_dims* dims, const int32_t* window_sizes,
 
 /*
  * Bytes of device workspace sta_backward needs for these arguments, or 0 if
- * they are invalid: three packed copies of a [B][heads][S][D] bf16 tensor,
- * two fp32 values per row, the forward's tile lists and 4 KB of queue heads.
+ * they are invalid: three packed copies of a [B][heads][S][D] bf16 tensor
+ * and two fp32 values per row (video rows padded to whole tiles), the
+ * forward's tile lists and 4 KB of queue heads.
  * Pure host arithmetic: no HIP call.
  */
 size_t sta_backward_workspace_bytes(const sta_dims* dims, const int32_t* window_sizes,
@@ -204,7 +217,8 @@ size_t sta_backward_workspace_bytes(const sta_dims* dims, const int32_t* window_
  * dq, dk, dv: device, bf16 [B][heads][S][D], written. They must not overlap
  *             each other, an input or the workspace. Text key slots at or
  *             after text_length are seen by no query: their dk and dv rows
- *             are written as zeros.
+ *             are written as zeros. With video sizes that are not tile
+ *             multiples, every existing row is written.
  * workspace : device, >= sta_backward_workspace_bytes(...) bytes, 256-byte
  *             aligned; contents on entry ignored, on return unspecified.
  *             Calls that share a workspace must be ordered on one stream.

@@ -62,10 +62,15 @@ def test_forward_rejects_bad_arguments(lib):
     assert fwd(lib, d, out=0) == 1
     assert fwd(lib, d, windows=None) == 1
     assert fwd(lib, sta.make_dims(1, 2, 96, (30, 48, 80))) == 2
-    assert fwd(lib, sta.make_dims(1, 2, 128, (31, 48, 80))) == 2
-    assert fwd(lib, sta.make_dims(1, 2, 128, (30, 44, 80))) == 2
-    assert fwd(lib, sta.make_dims(1, 2, 128, (30, 48, 84))) == 2
     assert fwd(lib, sta.make_dims(1, 2, 128, (0, 48, 80))) == 2
+    assert fwd(lib, sta.make_dims(1, 2, 128, (30, -8, 80))) == 2
+    assert fwd(lib, sta.make_dims(1, 2, 128, (30, 48, 0))) == 2
+    # sizes that are not tile multiples are valid (tile grid (6, 6, 11) here):
+    # the shape and windows pass, and the check after them (workspace) fails,
+    # so nothing is launched on the fake pointers
+    assert fwd(lib, sta.make_dims(1, 2, 128, (31, 44, 84)), windows=((3, 3, 11), (6, 6, 3)),
+               ws_bytes=1) == 6
+    assert fwd(lib, sta.make_dims(1, 2, 128, (31, 44, 84)), windows=((3, 7, 3), (3, 3, 3))) == 3
     assert fwd(lib, sta.make_dims(1, 257, 128, (30, 48, 80)), windows=[(1, 1, 1)] * 257) == 2
     # windows: each component in [1, tiles on the axis] = [1, (5, 6, 10)]
     assert fwd(lib, d, windows=((6, 3, 3), (3, 3, 3))) == 3
@@ -95,8 +100,11 @@ def test_layout_calls_reject_bad_arguments(lib):
     assert lib.sta_tile_gather(ctypes.byref(d), 0, None, 16, None) == 1
     assert lib.sta_tile_gather(ctypes.byref(d), 0, 16, 24, None) == 5
     assert lib.sta_tile_gather(ctypes.byref(d), 0, 16, 32, None) == 8
+    # only tile multiples (both orders then hold the same rows)
     assert lib.sta_tile_scatter(ctypes.byref(sta.make_dims(1, 1, 64, (18, 24, 20))), 0, 16,
                                 1 << 30, None) == 2
+    assert lib.sta_tile_gather(ctypes.byref(sta.make_dims(1, 1, 64, (17, 24, 24))), 0, 16,
+                               1 << 30, None) == 2
 
 
 def seq(video, text):
@@ -108,12 +116,14 @@ def seq(video, text):
     (1, 24, 128, (30, 48, 80), [(3, 3, 3)] * 24, True),
     (2, 4, 128, (30, 48, 80), [(5, 6, 10), (3, 3, 3), (1, 6, 10), (5, 1, 1)], True),
     (1, 24, 128, (48, 72, 128), [(3, 3, 3)] * 24, True),
+    (1, 2, 128, (7, 9, 11), [(2, 2, 2), (1, 1, 2)], True),
+    (2, 3, 64, (13, 8, 20), [(3, 1, 3), (1, 1, 1), (2, 1, 2)], False),
 ])
 def test_sizes(lib, B, heads, D, video, windows, text):
     d = sta.make_dims(B, heads, D, video)
     S = seq(video, text)
     assert sta.sta_seq_len(d, text) == S
-    n_tiles = (video[0] // 6) * (video[1] // 8) * (video[2] // 8)
+    n_tiles = -(-video[0] // 6) * -(-video[1] // 8) * -(-video[2] // 8)  # ceil tile grid
     n_q = n_tiles + (1 if text else 0)
     n_off, n_ids, n_work = sta.sta_schedule_sizes(d, windows, text)
     assert n_off == heads * n_q + 1
@@ -122,7 +132,8 @@ def test_sizes(lib, B, heads, D, video, windows, text):
 
     def up(x):
         return (x + 255) // 256 * 256
-    tensor = B * heads * S * D * 2
+    S_t = n_tiles * 384 + (256 if text else 0)  # packed rows: video padded to whole tiles
+    tensor = B * heads * S_t * D * 2
     queue_heads = 8 * 64 * 4  # one int per XCD queue, each on its own 256-byte line
     expect = up(tensor) + up(n_off * 4) + up(n_ids * 4) + up(n_work * 4) + queue_heads
     assert sta.sta_workspace_bytes(d, windows, text) == expect
@@ -131,7 +142,8 @@ def test_sizes(lib, B, heads, D, video, windows, text):
 def test_workspace_bytes_invalid_is_zero(lib):
     assert sta.sta_workspace_bytes(sta.make_dims(1, 1, 64, (18, 24, 24)), [(4, 1, 1)], False) == 0
     assert sta.sta_workspace_bytes(sta.make_dims(1, 1, 32, (18, 24, 24)), [(1, 1, 1)], False) == 0
-    assert sta.sta_seq_len(sta.make_dims(1, 1, 64, (18, 24, 23)), False) == 0
+    assert sta.sta_seq_len(sta.make_dims(1, 1, 64, (18, 24, 23)), False) == 18 * 24 * 23
+    assert sta.sta_seq_len(sta.make_dims(1, 1, 64, (18, 0, 23)), False) == 0
 
 
 def bwd(lib, dims, q=16, k=1 << 36, v=1 << 37, out=1 << 38, lse=1 << 39, dout=(1 << 39) + (1 << 34),
@@ -152,7 +164,9 @@ def test_backward_rejects_bad_arguments(lib):
         assert bwd(lib, d, **{name: 0}) == 1, name
     assert bwd(lib, d, windows=None) == 1
     assert bwd(lib, sta.make_dims(1, 2, 96, (30, 48, 80))) == 2
-    assert bwd(lib, sta.make_dims(1, 2, 128, (30, 44, 80))) == 2
+    assert bwd(lib, sta.make_dims(1, 2, 128, (30, 0, 80))) == 2
+    assert bwd(lib, sta.make_dims(1, 2, 128, (31, 44, 84)), windows=((3, 3, 11), (6, 6, 3)),
+               ws_bytes=1) == 6
     assert bwd(lib, d, windows=((6, 3, 3), (3, 3, 3))) == 3
     assert bwd(lib, d, ell=257) == 4
     assert bwd(lib, d, ell=3, text=0) == 4
@@ -174,16 +188,18 @@ def test_backward_rejects_bad_arguments(lib):
     (1, 1, 64, (18, 24, 24), [(1, 3, 3)], False),
     (1, 24, 128, (30, 48, 80), [(3, 3, 3)] * 24, True),
     (2, 4, 128, (30, 48, 80), [(5, 6, 10), (3, 3, 3), (1, 6, 10), (5, 1, 1)], True),
+    (1, 2, 128, (7, 9, 11), [(2, 2, 2), (1, 1, 2)], True),
 ])
 def test_backward_workspace_bytes(lib, B, heads, D, video, windows, text):
     d = sta.make_dims(B, heads, D, video)
-    S = seq(video, text)
     n_off, n_ids, _ = sta.sta_schedule_sizes(d, windows, text)
+    n_tiles = -(-video[0] // 6) * -(-video[1] // 8) * -(-video[2] // 8)
+    S_t = n_tiles * 384 + (256 if text else 0)
 
     def up(x):
         return (x + 255) // 256 * 256
-    tensor = B * heads * S * D * 2
-    rows = B * heads * S * 4
+    tensor = B * heads * S_t * D * 2
+    rows = B * heads * S_t * 4
     queue_heads = 8 * 64 * 4
     expect = (3 * up(tensor) + 2 * up(rows) + up(n_off * 4) + up(n_ids * 4) + 2 * queue_heads)
     assert sta.sta_backward_workspace_bytes(d, windows, text) == expect
