@@ -35,19 +35,51 @@ sys.path.insert(0, ROOT)
 METRIC = "STA fwd ms/call + effective TFLOP/s (% bf16 MFMA peak), (30,48,80)+256 text"
 # MI355X dense bf16 MFMA peak: 256 CUs x 4096 flop/clk x 2.4 GHz (published: 2.5 PFLOP/s)
 PEAK_BF16_TFLOPS = 256 * 4096 * 2.4e9 / 1e12
-PMC_SUMMARY = os.path.join(ROOT, "profiles", "attention_headline_pmc.txt")
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "attention_{workload}_pmc.txt")
 ATTN_SOURCE = os.path.join(ROOT, "block_sparse_sliding_amd", "csrc", "sta_attention.hip")
 
 
+TILE = (6, 8, 8)
+
+
+def _axis_pairs(size: int, tile: int, w: int) -> int:
+    """Sum over the query tokens of one axis of the key tokens its window holds.
+
+    The tile grid along the axis has ceil(size/tile) tiles, the last holding the
+    remainder; tile c's window starts at clamp(c - w//2, 0, n - w). For sizes
+    that are tile multiples this is size * w * tile.
+    """
+    n = -(-size // tile)
+    sizes = [min(tile, size - i * tile) for i in range(n)]
+    total = 0
+    for c in range(n):
+        start = min(max(c - w // 2, 0), n - w)
+        total += sizes[c] * sum(sizes[start:start + w])
+    return total
+
+
 def effective_flops(wl, include_pad_rows=False) -> float:
+    """4*D per allowed (query, key) pair: video queries see the existing tokens of
+    their window's tiles (the count factors over the three axes) and the valid
+    text keys; valid text queries see every video key and the valid text keys."""
     T, H, W = wl.video
     nv = T * H * W
     ell = wl.text_length if wl.has_text else 0
     text_rows = (256 if include_pad_rows else ell) if wl.has_text else 0
     pairs = 0
     for (wt, wh, ww) in wl.windows:
-        pairs += nv * (wt * wh * ww * 384 + ell) + text_rows * (nv + ell)
+        video_pairs = 1
+        for size, tile, w in zip(wl.video, TILE, (wt, wh, ww)):
+            video_pairs *= _axis_pairs(size, tile, w)
+        pairs += video_pairs + nv * ell + text_rows * (nv + ell)
     return 4.0 * wl.head_dim * pairs * wl.batch
+
+
+def kernel_suffix(wl) -> str:
+    """Template arguments of the kernels a workload runs: <D, PAD>, PAD when a
+    video size is not a tile multiple."""
+    pad = any(size % tile for size, tile in zip(wl.video, TILE))
+    return f"<{wl.head_dim}, {'true' if pad else 'false'}>"
 
 
 def source_sha() -> str:
@@ -61,11 +93,12 @@ def measured_traffic(workload: str):
     Returns None when there is no summary, when it was taken on another
     workload, or when the kernel source changed since the counters were taken.
     """
-    if not os.path.exists(PMC_SUMMARY):
+    path = PMC_SUMMARY.format(workload=workload)
+    if not os.path.exists(path):
         return None
     vals = {}
     summary_workload = None
-    with open(PMC_SUMMARY) as f:
+    with open(path) as f:
         for line in f:
             if line.startswith("#") and "workload " in line and summary_workload is None:
                 summary_workload = line.rsplit("workload ", 1)[1].strip()
@@ -209,7 +242,7 @@ def main():
         "effective_flop_per_call": flops,
         "stages_ms": stage_ms,
         "roofline": {
-            "kernel": "sta_attention_kernel<128>" if wl.head_dim == 128 else "sta_attention_kernel<64>",
+            "kernel": "sta_attention_kernel" + kernel_suffix(wl),
             "bound": "mfma",
             "achieved": attn_tflops,
             "peak": PEAK_BF16_TFLOPS,
@@ -286,7 +319,7 @@ def bench_backward(args, wl, windows, q, k, v, dims, out, lse, fwd_ws):
     tflops = flops / (ms_per_step * 1e-3) / 1e12
     # the dq pass executes three of the five products (S, dP, dQ), the dk/dv pass four
     dq_flops, dkv_flops = 0.6 * flops, 0.8 * flops
-    sfx = "<128>" if wl.head_dim == 128 else "<64>"
+    sfx = kernel_suffix(wl)
     kernels = {}
     for name, kname, kfl in (("dq", "bwd_dq_kernel" + sfx, dq_flops),
                              ("dkv", "bwd_dkv_kernel" + sfx, dkv_flops)):

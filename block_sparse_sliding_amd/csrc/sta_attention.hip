@@ -127,6 +127,7 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(KernelArgs) 
   if (unit < 0) break;
   int lane = threadIdx.x & 63;
   asm volatile("" : "+v"(lane));  // lane-derived offsets are rebuilt per unit, not kept live
+  const int this_lane = lane;
   const KernelArgs* ka = kernel_args();
   const Geom g = ka->g;
   const FwdArgs a = ka->a;
@@ -163,12 +164,11 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(KernelArgs) 
   // first block): kbase = raster row of the block's 8x8 (h, w) patch origin
   // (video) or first slot (text), krs = raster stride between its 8-row
   // runs, vrow = its first tile-major row (the packed V^T block). With PAD,
-  // tile_f/h/w are the frames, rows and columns of the current tile that
-  // exist, tile_part says some are missing, and kbase names the last existing
-  // frame in place of one that does not exist.
+  // tile_ext is the packed extent of the current tile (the frames, rows and
+  // columns that exist) and kbase names the last existing frame in place of
+  // one that does not exist.
   int tile_kbase = 0, tile_vrow = 0;
-  int tile_f = kTileT, tile_h = kTileH, tile_w = kTileW;
-  bool tile_part = false;
+  int tile_ext = kFullExtent;  // PAD: packed extent of the current tile
   auto block_rows = [&](int j, int& kbase, int& krs, int& vrow) {
     if (j < n_vid) {
       const int t = j / BPT;
@@ -181,13 +181,10 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(KernelArgs) 
         const int th = rest - tt * g.nh;
         tile_kbase = (tt * kTileT * g.H + th * kTileH) * g.W + tw * kTileW;
         tile_vrow = tile * kTileRows;
-        if constexpr (PAD) {
-          tile_extent(tt, th, tw, g, tile_f, tile_h, tile_w);
-          tile_part = tile_f < kTileT || tile_h < kTileH || tile_w < kTileW;
-        }
+        if constexpr (PAD) tile_ext = tile_extent(tt, th, tw, g);
       }
       if constexpr (PAD)
-        kbase = tile_kbase + (sub < tile_f ? sub : tile_f - 1) * g.H * g.W;
+        kbase = tile_kbase + min(sub, extent_frames(tile_ext) - 1) * g.H * g.W;
       else
         kbase = tile_kbase + sub * g.H * g.W;
       krs = g.W;
@@ -196,7 +193,7 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(KernelArgs) 
       kbase = g.n_video + (j - n_vid) * kKeyBlock;
       vrow = g.n_vt + (j - n_vid) * kKeyBlock;
       krs = kTileW;
-      if constexpr (PAD) tile_part = false;
+      if constexpr (PAD) tile_ext = kFullExtent;
     }
   };
 
@@ -205,15 +202,19 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(KernelArgs) 
   // share rr/8, so its source is a wave-uniform row pointer plus a per-lane
   // offset (row within the group, chunk) that is the same for every block.
   auto issue_k = [&](int st, int kbase, int krs) {
+    // PAD: per-lane offsets come from a fresh opaque copy of the lane id, so
+    // they are rebuilt per block rather than hoisted (and spilled) as 64-bit
+    // addresses
+    int lane = opaque_lane<PAD>(this_lane);
     if constexpr (PAD) {
-      if (tile_part) {
+      if (tile_ext != kFullExtent) {
         // per-lane source row, clamped to the rows and columns that exist
 #pragma unroll
         for (int i = 0; i < IPW; ++i) {
           const int q = wave * IPW + i;
           const int rin = (lane >> 2) % RPI;
           const int h = (q * RPI) >> 3, w = ((q * RPI) & 7) + rin;
-          const int row = kbase + (h < tile_h ? h : tile_h - 1) * krs + (w < tile_w ? w : tile_w - 1);
+          const int row = kbase + min(h, extent_rows(tile_ext) - 1) * krs + min(w, extent_cols(tile_ext) - 1);
           const int chunk = 4 * (lane / (4 * RPI)) + ((lane & 3) ^ sw(q * RPI + rin));
           dma16(kr + size_t(row) * ROWB + chunk * 16, &lds[st][0][q * 1024]);
         }
@@ -232,6 +233,7 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(KernelArgs) 
   };
   // Fetch the packed V^T block starting at tile-major row vrow (contiguous).
   auto issue_v = [&](int st, int vrow) {
+    int lane = opaque_lane<PAD>(this_lane);
     const char* src = vtr + size_t(vrow) * ROWB;
     const unsigned o = unsigned(lane) * 16u;
 #pragma unroll
@@ -332,8 +334,9 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(KernelArgs) 
           // keys of a partial tile that do not exist (the tile state still
           // describes block j: block j + 1 is decoded below). Key 16kt + 4(l/16)
           // + r of the block sits at patch row 2kt + l/32, column 4((l/16)&1) + r.
-          if (j < n_vid && tile_part) {
+          if (j < n_vid && tile_ext != kFullExtent) {
             const int sub = j - (j / BPT) * BPT;
+            const int nf = extent_frames(tile_ext), nr = extent_rows(tile_ext), nc = extent_cols(tile_ext);
             int hb = lane >> 5;
             asm volatile("" : "+v"(hb));
             const int wb = ((lane >> 4) & 1) * 4;
@@ -341,7 +344,7 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(KernelArgs) 
             for (int kt = 0; kt < 4; ++kt)
   #pragma unroll
               for (int r = 0; r < 4; ++r)
-                if (sub >= tile_f || 2 * kt + hb >= tile_h || wb + r >= tile_w)
+                if (sub >= nf || 2 * kt + hb >= nr || wb + r >= nc)
   #pragma unroll
                   for (int c = 0; c < QT; ++c) s[c][kt][r] = -INFINITY;
           }

@@ -203,6 +203,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(KernelArgs) {
     if (entry < 0) break;
     int lane = threadIdx.x & 63;
     asm volatile("" : "+v"(lane));
+    const int this_lane = lane;
     const KernelArgs* ka = kernel_args();
     const Geom g = ka->g;
     const BwdArgs a = ka->a;
@@ -246,12 +247,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(KernelArgs) {
     const __attribute__((address_space(4))) int32_t* ids =
         (const __attribute__((address_space(4))) int32_t*)(a.ids + l0);
 
-    // with PAD, tile_f/h/w: frames, rows and columns of the current key tile
-    // that exist (tile_part: some are missing); kbase then names the last
-    // existing frame in place of one that does not exist
+    // with PAD, tile_ext: packed extent of the current key tile (the frames,
+    // rows and columns that exist); kbase then names the last existing frame
+    // in place of one that does not exist
     int tile_kbase = 0, tile_vrow = 0;
-    int tile_f = kTileT, tile_h = kTileH, tile_w = kTileW;
-    bool tile_part = false;
+    int tile_ext = kFullExtent;  // PAD: packed extent of the current tile
     auto block_rows = [&](int j, int& kbase, int& krs, int& vrow) {
       if (j < n_vid) {
         const int t = j / BPT;
@@ -264,13 +264,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(KernelArgs) {
           const int th = rest - tt * g.nh;
           tile_kbase = (tt * kTileT * g.H + th * kTileH) * g.W + tw * kTileW;
           tile_vrow = tile * kTileRows;
-          if constexpr (PAD) {
-            tile_extent(tt, th, tw, g, tile_f, tile_h, tile_w);
-            tile_part = tile_f < kTileT || tile_h < kTileH || tile_w < kTileW;
-          }
+          if constexpr (PAD) tile_ext = tile_extent(tt, th, tw, g);
         }
         if constexpr (PAD)
-          kbase = tile_kbase + (sub < tile_f ? sub : tile_f - 1) * g.H * g.W;
+          kbase = tile_kbase + min(sub, extent_frames(tile_ext) - 1) * g.H * g.W;
         else
           kbase = tile_kbase + sub * g.H * g.W;
         krs = g.W;
@@ -279,20 +276,23 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(KernelArgs) {
         kbase = g.n_video + (j - n_vid) * kKeyBlock;
         vrow = g.n_vt + (j - n_vid) * kKeyBlock;
         krs = kTileW;
-        if constexpr (PAD) tile_part = false;
+        if constexpr (PAD) tile_ext = kFullExtent;
       }
     };
     // raw rows kbase + (rr/8)*krs + rr%8 of tensor `src` into LDS region `dst`
     // (the forward's swizzled K layout)
     auto issue_raw = [&](const char* src, char* dst, int kbase, int krs) {
+      // PAD: per-lane offsets from a fresh opaque lane id, rebuilt per block
+      // rather than hoisted (and spilled) as 64-bit addresses
+      int lane = opaque_lane<PAD>(this_lane);
       if constexpr (PAD) {
-        if (tile_part) {  // per-lane rows, clamped to the rows and columns that exist
+        if (tile_ext != kFullExtent) {  // per-lane rows, clamped to the rows and columns that exist
 #pragma unroll
           for (int i = 0; i < IPW; ++i) {
             const int q = wave * IPW + i;
             const int rin = (lane >> 2) % RPI;
             const int h = (q * RPI) >> 3, w = ((q * RPI) & 7) + rin;
-            const int row = kbase + (h < tile_h ? h : tile_h - 1) * krs + (w < tile_w ? w : tile_w - 1);
+            const int row = kbase + min(h, extent_rows(tile_ext) - 1) * krs + min(w, extent_cols(tile_ext) - 1);
             const int chunk = 4 * (lane / (4 * RPI)) + ((lane & 3) ^ sw(q * RPI + rin));
             dma16(src + size_t(row) * ROWB + chunk * 16, dst + q * 1024);
           }
@@ -310,6 +310,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(KernelArgs) {
       }
     };
     auto issue_packed = [&](const char* src, char* dst, int vrow) {
+      int lane = opaque_lane<PAD>(this_lane);
       const char* p = src + size_t(vrow) * ROWB;
       const unsigned o = unsigned(lane) * 16u;
 #pragma unroll
@@ -491,6 +492,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(KernelArgs) {
     if (entry < 0) break;
     int lane = threadIdx.x & 63;
     asm volatile("" : "+v"(lane));
+    const int this_lane = lane;
     const KernelArgs* ka = kernel_args();
     const Geom g = ka->g;
     const BwdArgs a = ka->a;
@@ -542,11 +544,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(KernelArgs) {
     auto sw = [](int row) { return (row >> 2) & 2; };
 
     // query block j: raster origin of its rows and its first tile-major row;
-    // with PAD, tile_f/h/w and tile_part describe the current query tile as in
-    // the dq kernel
+    // with PAD, tile_ext describes the current query tile as in the dq kernel
     int tile_qbase = 0, tile_vrow = 0;
-    int tile_f = kTileT, tile_h = kTileH, tile_w = kTileW;
-    bool tile_part = false;
+    int tile_ext = kFullExtent;  // PAD: packed extent of the current tile
     auto block_rows = [&](int j, int& qbase, int& qrs, int& vrow) {
       if (j < n_qtiles * BPT) {
         const int t = j / BPT;
@@ -566,13 +566,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(KernelArgs) {
           }
           tile_qbase = (tt * kTileT * g.H + th * kTileH) * g.W + tw * kTileW;
           tile_vrow = ((tt * g.nh + th) * g.nw + tw) * kTileRows;
-          if constexpr (PAD) {
-            tile_extent(tt, th, tw, g, tile_f, tile_h, tile_w);
-            tile_part = tile_f < kTileT || tile_h < kTileH || tile_w < kTileW;
-          }
+          if constexpr (PAD) tile_ext = tile_extent(tt, th, tw, g);
         }
         if constexpr (PAD)
-          qbase = tile_qbase + (sub < tile_f ? sub : tile_f - 1) * g.H * g.W;
+          qbase = tile_qbase + min(sub, extent_frames(tile_ext) - 1) * g.H * g.W;
         else
           qbase = tile_qbase + sub * g.H * g.W;
         qrs = g.W;
@@ -581,18 +578,19 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(KernelArgs) {
         qbase = g.n_video + (j - n_qtiles * BPT) * kQueryBlock;
         vrow = g.n_vt + (j - n_qtiles * BPT) * kQueryBlock;
         qrs = kTileW;
-        if constexpr (PAD) tile_part = false;
+        if constexpr (PAD) tile_ext = kFullExtent;
       }
     };
     auto issue_raw = [&](const char* src, char* dst, int qbase, int qrs) {
+      int lane = opaque_lane<PAD>(this_lane);  // as in the dq kernel
       if constexpr (PAD) {
-        if (tile_part) {  // per-lane rows, clamped to the rows and columns that exist
+        if (tile_ext != kFullExtent) {  // per-lane rows, clamped to the rows and columns that exist
 #pragma unroll
           for (int i = 0; i < IPW; ++i) {
             const int q = wave * IPW + i;
             const int rin = (lane >> 2) % RPI;
             const int h = (q * RPI) >> 3, w = ((q * RPI) & 7) + rin;
-            const int row = qbase + (h < tile_h ? h : tile_h - 1) * qrs + (w < tile_w ? w : tile_w - 1);
+            const int row = qbase + min(h, extent_rows(tile_ext) - 1) * qrs + min(w, extent_cols(tile_ext) - 1);
             const int chunk = 4 * (lane / (4 * RPI)) + ((lane & 3) ^ sw(q * RPI + rin));
             dma16(src + size_t(row) * ROWB + chunk * 16, dst + q * 1024);
           }

@@ -71,6 +71,14 @@ __device__ inline void dma4(const char* gsrc, char* lds_dst) {
   __builtin_amdgcn_global_load_lds(gsrc, (lds_void*)lds_dst, 4, 0, 0);
 }
 
+// The lane id through an empty asm when OPAQUE: values derived from it are
+// recomputed where they are used instead of being hoisted out of a loop.
+template <bool OPAQUE>
+__device__ inline int opaque_lane(int lane) {
+  if constexpr (OPAQUE) asm volatile("" : "+v"(lane));
+  return lane;
+}
+
 // Workgroups of `kernel` that fit on the current device at once (CU count
 // times occupancy), cached per device in `cache` (kMaxDevices entries,
 // zero-initialised). 0 on error.

@@ -67,17 +67,19 @@ __host__ __device__ inline int tiled_to_raster(int r, const Geom& g) {
   return (t * g.H + h) * g.W + w;
 }
 
-// Extent of tile (tt, th, tw) inside the video: frames (of 6), rows (of 8)
-// and columns (of 8) that exist.
-__host__ __device__ inline void tile_extent(int tt, int th, int tw, const Geom& g, int& frames,
-                                            int& rows, int& cols) {
-  frames = g.T - tt * kTileT;
+// Extent of tile (tt, th, tw) inside the video, packed in one int: the frames
+// (of 6) | rows (of 8) << 8 | columns (of 8) << 16 of the tile that exist.
+constexpr int kFullExtent = kTileT | (kTileH << 8) | (kTileW << 16);
+__host__ __device__ inline int tile_extent(int tt, int th, int tw, const Geom& g) {
+  int frames = g.T - tt * kTileT, rows = g.H - th * kTileH, cols = g.W - tw * kTileW;
   frames = frames < kTileT ? frames : kTileT;
-  rows = g.H - th * kTileH;
   rows = rows < kTileH ? rows : kTileH;
-  cols = g.W - tw * kTileW;
   cols = cols < kTileW ? cols : kTileW;
+  return frames | (rows << 8) | (cols << 16);
 }
+__host__ __device__ inline int extent_frames(int e) { return e & 255; }
+__host__ __device__ inline int extent_rows(int e) { return (e >> 8) & 255; }
+__host__ __device__ inline int extent_cols(int e) { return e >> 16; }
 
 // Launchers (each enqueues one kernel on `stream` and returns hipGetLastError()).
 hipError_t launch_rows_permute(const Geom& g, const void* src, void* dst, bool to_tiled,

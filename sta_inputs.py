@@ -60,9 +60,10 @@ def _per_head(heads: int, cycle: Sequence[Tuple[int, int, int]]):
     return tuple(tuple(cycle[h % len(cycle)]) for h in range(heads))
 
 
-# Workloads: the tiny CPU-checkable case, the four full-size cases and the
+# Workloads: the tiny CPU-checkable case, the four full-size cases, the
 # headline shape (video (30,48,80) + 256 text slots, 24 heads, D=128,
-# window (3,3,3); its text length 226 is the one the text case uses).
+# window (3,3,3); its text length 226 is the one the text case uses) and the
+# headline at a height that is not a tile multiple.
 WORKLOADS = {
     "tiny": Workload("tiny", 1, 1, 64, (18, 24, 24), _per_head(1, [(1, 3, 3)]),
                      False, 0, 10),
@@ -77,6 +78,11 @@ WORKLOADS = {
                       _per_head(24, [(3, 3, 3)]), True, 128, 50),
     "headline": Workload("headline", 1, 24, 128, (30, 48, 80),
                          _per_head(24, [(3, 3, 3)]), True, 226, 60),
+    # the headline with 45 rows (a 720-pixel frame height at a 16x spatial
+    # reduction): not a multiple of the tile height, so the last tile row
+    # holds 5 of 8 rows; same tile grid (5, 6, 10)
+    "ragged": Workload("ragged", 1, 24, 128, (30, 45, 80),
+                       _per_head(24, [(3, 3, 3)]), True, 226, 70),
 }
 
 

@@ -118,3 +118,44 @@ def test_partial_tiles_medium_sampled():
         compare_grad(dv[:, sl][:, :, torch.from_numpy(keys)], rv, f"dv medium head {h}")
     for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
         assert bool(torch.isfinite(t).all()), name
+
+
+def test_backward_full_size_ragged():
+    """(30, 45, 80) + 256 text, D = 128 (the last tile row holds 5 of 8 rows):
+    every gradient written, sum rules per head, sampled dq rows and every key
+    row of one partial key tile, at the launch shape the benchmark times."""
+    import sta_inputs
+
+    wl = sta_inputs.WORKLOADS["ragged"]
+    T, H, W = wl.video
+    heads = 3
+    windows = [(3, 3, 3), (1, 1, 1), (5, 6, 10)]
+    ell = wl.text_length
+    nv = T * H * W
+    S = nv + 256
+    note(f"backward full size ragged {wl.video}+256, {heads} heads")
+    q, k, v, dout = inputs(1, heads, S, 128, 91)
+    out, lse = run_sta(q, k, v, windows, ell, True, wl.video)
+    assert bool(torch.isfinite(out).all() and torch.isfinite(lse).all())
+    dq, dk, dv = run_backward(q, k, v, out, lse, dout, windows, ell, True, wl.video)
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        assert bool(torch.isfinite(t).all()), name
+    sdv, sdo, sdk = dv.double().sum(dim=2), dout.double().sum(dim=2), dk.double().sum(dim=2)
+    assert bool(((sdv - sdo).abs() <= 1e-2 * dv.double().abs().sum(dim=2) + 1e-3).all())
+    assert bool((sdk.abs() <= 1e-2 * dk.double().abs().sum(dim=2) + 1e-3).all())
+    rng = np.random.default_rng(11)
+    qrows = np.unique(np.concatenate([rng.integers(0, nv, 16), [nv - 1, nv, S - 1]]))
+    # key tile (2, 5, 4): rows 40..44 of the frame exist, 5 of 8
+    keys = np.asarray([((12 + a) * H + 40 + b) * W + 32 + c
+                       for a in range(6) for b in range(5) for c in range(8)])
+    for h in range(heads):
+        sl = slice(h, h + 1)
+        rq, rk, rv = oracle.sta_reference_backward(
+            q[:, sl].cpu(), k[:, sl].cpu(), v[:, sl].cpu(), dout[:, sl].cpu(), [windows[h]], ell,
+            True, wl.video, query_rows=qrows, key_rows=keys if h == 1 else [])
+        compare_grad(dq[:, sl][:, :, torch.from_numpy(qrows)], rq, f"dq ragged head {h}")
+        if h == 1:
+            compare_grad(dk[:, sl][:, :, torch.from_numpy(keys)], rk, "dk ragged head 1")
+            compare_grad(dv[:, sl][:, :, torch.from_numpy(keys)], rv, "dv ragged head 1")
+    del q, k, v, dout, out, lse, dq, dk, dv
+    torch.cuda.empty_cache()
