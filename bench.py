@@ -35,8 +35,6 @@ sys.path.insert(0, ROOT)
 METRIC = "STA fwd ms/call + effective TFLOP/s (% bf16 MFMA peak), (30,48,80)+256 text"
 # MI355X dense bf16 MFMA peak: 256 CUs x 4096 flop/clk x 2.4 GHz (published: 2.5 PFLOP/s)
 PEAK_BF16_TFLOPS = 256 * 4096 * 2.4e9 / 1e12
-PMC_SUMMARY = os.path.join(ROOT, "profiles", "attention_{workload}_pmc.txt")
-ATTN_SOURCE = os.path.join(ROOT, "block_sparse_sliding_amd", "csrc", "sta_attention.hip")
 
 
 TILE = (6, 8, 8)
@@ -82,33 +80,28 @@ def kernel_suffix(wl) -> str:
     return f"<{wl.head_dim}, {'true' if pad else 'false'}>"
 
 
-def source_sha() -> str:
-    with open(ATTN_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def measured_traffic(summary: str, kernel: str, source: str):
+    """HBM bytes per launch of `kernel` from a committed rocprofv3 counter summary.
 
-
-def measured_traffic(workload: str):
-    """HBM bytes per attention launch from the committed rocprofv3 counter summary.
-
-    Returns None when there is no summary, when it was taken on another
-    workload, or when the kernel source changed since the counters were taken.
+    `summary` is a file under profiles/; None when it is missing, holds no figure
+    for the kernel, or when `source` (the kernel's file) changed since the
+    counters were taken.
     """
-    path = PMC_SUMMARY.format(workload=workload)
+    path = os.path.join(ROOT, "profiles", summary)
     if not os.path.exists(path):
         return None
     vals = {}
-    summary_workload = None
     with open(path) as f:
         for line in f:
-            if line.startswith("#") and "workload " in line and summary_workload is None:
-                summary_workload = line.rsplit("workload ", 1)[1].strip()
-            elif ":" in line:
+            if not line.startswith("#") and ":" in line:
                 key, _, val = line.partition(":")
                 vals[key.strip()] = val.strip()
-    if summary_workload != workload or vals.get("kernel_source_sha256_16") != source_sha():
+    with open(os.path.join(ROOT, "block_sparse_sliding_amd", "csrc", source), "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()[:16]
+    if vals.get("kernel_source_sha256_16") != sha:
         return None
     try:
-        return float(vals["hbm_bytes_per_launch"])
+        return float(vals[f"hbm_bytes_per_launch[{kernel}]"])
     except (KeyError, ValueError):
         return None
 
@@ -222,7 +215,8 @@ def main():
     tflops = flops / (ms_per_step * 1e-3) / 1e12
     attn_ms = stage_ms["attention"]
     attn_tflops = flops / (attn_ms * 1e-3) / 1e12
-    traffic = measured_traffic(args.workload)
+    attn_kernel = "sta_attention_kernel" + kernel_suffix(wl)
+    traffic = measured_traffic(f"attention_{args.workload}_pmc.txt", attn_kernel, "sta_attention.hip")
     result = {
         "metric": METRIC,
         "value": tflops,
@@ -242,7 +236,7 @@ def main():
         "effective_flop_per_call": flops,
         "stages_ms": stage_ms,
         "roofline": {
-            "kernel": "sta_attention_kernel" + kernel_suffix(wl),
+            "kernel": attn_kernel,
             "bound": "mfma",
             "achieved": attn_tflops,
             "peak": PEAK_BF16_TFLOPS,
@@ -327,7 +321,9 @@ def bench_backward(args, wl, windows, q, k, v, dims, out, lse, fwd_ws):
         kernels[name] = {"kernel": kname, "bound": "mfma", "achieved": t,
                          "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                          "frac": t / PEAK_BF16_TFLOPS, "launch_ms": stage_ms[name],
-                         "executed_flop": kfl}
+                         "executed_flop": kfl,
+                         "traffic": measured_traffic(f"backward_{args.workload}_pmc.txt", kname,
+                                                     "sta_backward.hip")}
     result = {
         "metric": "STA bwd ms/call + effective TFLOP/s (% bf16 MFMA peak)",
         "value": tflops,

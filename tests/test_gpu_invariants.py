@@ -2,7 +2,8 @@
 
 * q = 0 closed form: every allowed score is 0, so lse = ln(count) and the
   output is the mean of the allowed v rows; with v carrying each key's tile
-  coordinates this pins the window placement on every row, at full size.
+  coordinates this pins the window placement on every row, at full size,
+  also for sizes that are not tile multiples (partial last tiles).
 * padded text K/V rows never reach the result (bitwise).
 * repeated calls are bitwise identical; batch entries are independent.
 """
@@ -54,26 +55,37 @@ def coord_inputs(B, heads, D, video, has_text, seed=0):
 
 
 def expected_uniform(video, window, ell, has_text):
-    """Closed-form output columns 0..3 and lse for q = 0, every row."""
+    """Closed-form output columns 0..3 and lse for q = 0, every row.
+
+    Any video size: the tile grid along an axis has ceil(size/tile) tiles, the
+    last holding the remainder. The allowed video keys of a row form a box, so
+    their count is the product of the per-axis spans and the mean tile
+    coordinate along an axis is that axis' token-weighted mean.
+    """
     T, H, W = video
     nv = T * H * W
-    n = [video[a] // TILE[a] for a in range(3)]
-    t = np.arange(T).repeat(H * W)
-    h = np.tile(np.arange(H).repeat(W), T)
-    w = np.tile(np.arange(W), T * H)
-    nwin = window[0] * window[1] * window[2] * 384
-    cnt = nwin + ell
-    cols = []
-    for a, x in enumerate((t, h, w)):
+    n = [-(-video[a] // TILE[a]) for a in range(3)]
+    sizes = [np.array([min(TILE[a], video[a] - i * TILE[a]) for i in range(n[a])])
+             for a in range(3)]
+    coords = (np.arange(T).repeat(H * W), np.tile(np.arange(H).repeat(W), T),
+              np.tile(np.arange(W), T * H))
+    span = np.ones(nv)
+    mean = []
+    for a, x in enumerate(coords):
         tiles = x // TILE[a]
         lo = {c: int(nearest_box_start(c, window[a], n[a])) for c in range(n[a])}
         start = np.vectorize(lo.get)(tiles)
-        cols.append((start + (window[a] - 1) / 2.0) * nwin / cnt)
-    vid = np.stack(cols + [np.full(nv, ell / cnt)], axis=1)
-    lse = np.full(nv, math.log(cnt))
+        idx = start[:, None] + np.arange(window[a])[None, :]
+        sz = sizes[a][idx]
+        span = span * sz.sum(axis=1)
+        mean.append((idx * sz).sum(axis=1) / sz.sum(axis=1))
+    cnt = span + ell
+    vid = np.stack([m * span / cnt for m in mean] + [ell / cnt], axis=1)
+    lse = np.log(cnt)
     if has_text:
         ctext = nv + ell
-        txt = np.array([(n[a] - 1) / 2.0 * nv / ctext for a in range(3)] + [ell / ctext])
+        txt = np.array([(np.arange(n[a]) * sizes[a]).sum() / video[a] * nv / ctext
+                        for a in range(3)] + [ell / ctext])
         vid = np.concatenate([vid, np.tile(txt, (256, 1))])
         lse = np.concatenate([lse, np.full(256, math.log(ctext))])
     return vid, lse
@@ -86,6 +98,11 @@ def expected_uniform(video, window, ell, has_text):
     ((30, 48, 80), [(3, 3, 3)], 0, False, 128),
     ((48, 72, 128), [(3, 3, 3)], 128, True, 128),
     ((18, 24, 24), [(1, 3, 3)], 0, False, 64),
+    # sizes that are not tile multiples (partial last tiles)
+    ((30, 45, 80), [(3, 3, 3), (1, 2, 4)], 226, True, 128),
+    ((17, 21, 30), [(2, 2, 3), (3, 1, 1)], 100, True, 128),
+    ((1, 12, 20), [(1, 2, 3)], 0, False, 64),
+    ((13, 9, 33), [(3, 2, 5)], 256, True, 64),
 ])
 def test_uniform_attention_closed_form(video, windows, ell, has_text, D):
     heads = len(windows)
@@ -104,9 +121,9 @@ def test_uniform_attention_closed_form(video, windows, ell, has_text, D):
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("ell", [0, 1, 100, 226, 255])
-def test_text_padding_never_reaches_output(ell):
-    video = (18, 24, 32)
+@pytest.mark.parametrize("ell,video", [(0, (18, 24, 32)), (1, (18, 24, 32)), (100, (18, 24, 32)),
+                                       (226, (18, 24, 32)), (255, (18, 24, 32)), (77, (17, 21, 30))])
+def test_text_padding_never_reaches_output(ell, video):
     windows = [(3, 3, 3), (1, 2, 3)]
     nv = video[0] * video[1] * video[2]
     S = nv + 256

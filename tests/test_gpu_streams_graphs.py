@@ -21,12 +21,18 @@ pytestmark = pytest.mark.gpu
 VIDEO = (18, 24, 32)
 WINDOWS = [(3, 3, 3), (1, 2, 3)]
 ELL = 141
-S = VIDEO[0] * VIDEO[1] * VIDEO[2] + 256
 
 
-def tensors(seed, D=128, heads=2):
+def seq(video):
+    return video[0] * video[1] * video[2] + 256
+
+
+S = seq(VIDEO)
+
+
+def tensors(seed, D=128, heads=2, video=VIDEO):
     g = torch.Generator(device="cuda").manual_seed(seed)
-    return [torch.randn(1, heads, S, D, generator=g, device="cuda").to(torch.bfloat16)
+    return [torch.randn(1, heads, seq(video), D, generator=g, device="cuda").to(torch.bfloat16)
             for _ in range(4)]
 
 
@@ -34,15 +40,16 @@ def bits(t):
     return t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
 
 
-def test_graph_replays_match_eager():
-    note("graph capture of forward + backward")
-    q, k, v, dout = tensors(11)
-    dims = sta.make_dims(1, 2, 128, VIDEO)
+@pytest.mark.parametrize("video", [VIDEO, (17, 21, 30)])
+def test_graph_replays_match_eager(video):
+    note(f"graph capture of forward + backward {video}")
+    q, k, v, dout = tensors(11, video=video)
+    dims = sta.make_dims(1, 2, 128, video)
     fws = torch.empty(sta.sta_workspace_bytes(dims, WINDOWS, True), dtype=torch.uint8, device="cuda")
     bws = torch.empty(sta.sta_backward_workspace_bytes(dims, WINDOWS, True), dtype=torch.uint8,
                       device="cuda")
     out, dq, dk, dv = (torch.empty_like(q) for _ in range(4))
-    lse = torch.empty(1, 2, S, dtype=torch.float32, device="cuda")
+    lse = torch.empty(1, 2, seq(video), dtype=torch.float32, device="cuda")
 
     def step():
         sta.sta_forward(dims, q, k, v, WINDOWS, ELL, True, out, lse, fws)
