@@ -63,9 +63,11 @@
 // tile along an axis holds the remainder. Its K rows that do not exist are
 // fetched from a clamped row that does (every source address stays inside
 // the video), their scores are replaced by -inf and their packed V rows are
-// zeros; padding query rows compute on a valid row and are not written. The
-// first block of every window is frame 0 of an existing tile, so the running
-// max is finite from the first block on.
+// zeros. A video unit's rows are its tile's existing tokens in compact order
+// (a partial tile of at most 256 runs with 8 waves x 32 rows); rows past them
+// compute on a valid row and are not written. The first block of every window
+// is frame 0 of an existing tile, so the running max is finite from the first
+// block on.
 // Epilogue: O = O^T / l rounded to bf16, lse = (m + log2 l) * ln 2, at raster rows.
 #include <type_traits>
 
@@ -136,7 +138,33 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(KernelArgs) 
   const int hd = bh % g.heads;
   const bool text_unit = g.has_text && u == g.n_tiles;
   const int q_row0 = text_unit ? g.n_vt : u * kTileRows;  // tile-major
-  const int q_rows = text_unit ? kTextSlots : kTileRows;
+  int q_rows = text_unit ? kTextSlots : kTileRows;
+  // PAD: the rows of a video unit are the existing tokens of its tile in
+  // compact order (frame, row, column), so a partial tile of at most 256
+  // tokens runs as a 256-row unit
+  int q_ext = kFullExtent, q_base = 0;  // extent and raster origin of the query tile
+  if constexpr (PAD) {
+    if (!text_unit) {
+      const int rest = div_by(u, g.nw, g.mag_nw);
+      const int tw = u - rest * g.nw;
+      const int tt = div_by(rest, g.nh, g.mag_nh);
+      const int th = rest - tt * g.nh;
+      q_ext = tile_extent(tt, th, tw, g);
+      q_rows = extent_tokens(q_ext);
+      q_base = (tt * kTileT * g.H + th * kTileH) * g.W + tw * kTileW;
+    }
+  }
+  // raster row of unit row `row` (< q_rows)
+  auto query_raster = [&](int row) {
+    if constexpr (PAD) {
+      if (!text_unit) {
+        int dt, dh, dw;
+        compact_token(row, q_ext, dt, dh, dw);
+        return q_base + (dt * g.H + dh) * g.W + dw;
+      }
+    }
+    return tiled_to_raster(q_row0 + row, g);
+  };
   const size_t slab = size_t(bh) * g.S * D;      // element offset of this (b, head), raster
   const size_t slab_t = size_t(bh) * g.S_t * D;  // the same in the packed tile-major V^T
 
@@ -250,16 +278,15 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(KernelArgs) 
     constexpr int QT = decltype(qt_c)::value;
     constexpr int RPW = QT * 16;  // query rows per wave
     // Q^T fragments for this wave's RPW rows, read from the caller's raster q
-    // (row r of the unit is tile-major row q_row0 + r; rows past the unit are
-    // clamped to a valid row and their results discarded).
+    // (row r of the unit: see query_raster; rows past the unit are clamped to
+    // a valid row and their results discarded).
     const float qs = a.q_scale;  // log2(e)/sqrt(D), applied to the fp32 scores
     bf16x8 qf[QT][KS];
   #pragma unroll
     for (int c = 0; c < QT; ++c) {
       int row = wave * RPW + c * 16 + (lane & 15);
       row = row < q_rows ? row : q_rows - 1;
-      int rr = tiled_to_raster(q_row0 + row, g);
-      if constexpr (PAD) rr = rr < 0 ? 0 : rr;  // padding row: any valid row, result discarded
+      const int rr = query_raster(row);
       const bf16x8* src = reinterpret_cast<const bf16x8*>(qr + size_t(rr) * D + (lane >> 4) * 8);
   #pragma unroll
       for (int ks = 0; ks < KS; ++ks) qf[c][ks] = src[ks * 4];
@@ -425,8 +452,8 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(KernelArgs) 
       const float l = swap32_sum(swap16_sum(l_part[c]));
       const float inv = __builtin_amdgcn_rcpf(l);
       const int row = wave * RPW + c * 16 + (lane & 15);
-      const int rr = row < q_rows ? tiled_to_raster(q_row0 + row, g) : -1;
-      if (rr >= 0) {
+      if (row < q_rows) {
+        const int rr = query_raster(row);
         __bf16* dst = outr + size_t(rr) * D + (lane >> 4) * 4;
   #pragma unroll
         for (int d = 0; d < DT; ++d) {
@@ -437,7 +464,7 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(KernelArgs) 
       }
     }
   };
-  if (text_unit)
+  if (text_unit || (PAD && q_rows <= kTextSlots))
     run(std::integral_constant<int, kTextSlots / 16 / kWaves>{});
   else
     run(std::integral_constant<int, kQT>{});

@@ -226,6 +226,37 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(KernelArgs) {
       q_row0 = u * kTileRows + (r & 1) * 256;
       q_rows = (r & 1) ? kTileRows - 256 : 256;
     }
+    // PAD: the rows of a video unit are its tile's existing tokens in compact
+    // order (frame, row, column), part 1 starting at token 256; n_valid of
+    // them exist (possibly none: the unit then streams nothing)
+    int q_ext = kFullExtent, q_base = 0, n_valid = q_rows;
+    if constexpr (PAD) {
+      if (unit >= n_text_units) {
+        const int rest = div_by(u, g.nw, g.mag_nw);
+        const int tw = u - rest * g.nw;
+        const int tt = div_by(rest, g.nh, g.mag_nh);
+        const int th = rest - tt * g.nh;
+        q_ext = tile_extent(tt, th, tw, g);
+        q_base = (tt * kTileT * g.H + th * kTileH) * g.W + tw * kTileW;
+        n_valid = min(extent_tokens(q_ext) - (q_row0 - u * kTileRows), q_rows);
+      }
+    }
+    // unit row `row` -> raster row and tile-major row (the index of lse2 and
+    // delta); rows at or past n_valid map to the last existing one
+    auto query_rows = [&](int row, int& raster, int& tiled) {
+      if constexpr (PAD) {
+        if (unit >= n_text_units) {
+          const int first = q_row0 - u * kTileRows;  // 0 or 256
+          int dt, dh, dw;
+          compact_token(first + (row < n_valid ? row : n_valid - 1), q_ext, dt, dh, dw);
+          raster = q_base + (dt * g.H + dh) * g.W + dw;
+          tiled = u * kTileRows + (dt * kTileH + dh) * kTileW + dw;
+          return;
+        }
+      }
+      raster = tiled_to_raster(q_row0 + row, g);
+      tiled = q_row0 + row;
+    };
     const int hd = bh % g.heads;
     const size_t slab = size_t(bh) * g.S * D;
     const __bf16* __restrict__ qr = reinterpret_cast<const __bf16*>(a.q) + slab;
@@ -241,7 +272,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(KernelArgs) {
     const int l1 = a.offsets[hd * g.n_q + u + 1];
     const int n_vid = (l1 - l0) * BPT;
     const int text_len = g.has_text ? g.text_length : 0;
-    const int n_blk = n_vid + (text_len + kKeyBlock - 1) / kKeyBlock;
+    const int n_blk = n_valid > 0 ? n_vid + (text_len + kKeyBlock - 1) / kKeyBlock : 0;
     const bool ragged = (text_len % kKeyBlock) != 0;
     auto sw = [](int row) { return (row >> 2) & 2; };
     const __attribute__((address_space(4))) int32_t* ids =
@@ -329,8 +360,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(KernelArgs) {
 #pragma unroll
       for (int c = 0; c < QT; ++c) {
         const int row = wave * RPW + c * 16 + (lane & 15);  // < q_rows for every unit shape
-        int rr = tiled_to_raster(q_row0 + row, g);
-        if constexpr (PAD) rr = rr < 0 ? 0 : rr;  // padding row: any valid row, result discarded
+        int rr, rt;
+        query_rows(row, rr, rt);
         const bf16x8* qs8 = reinterpret_cast<const bf16x8*>(qr + size_t(rr) * D + (lane >> 4) * 8);
         const bf16x8* ds8 = reinterpret_cast<const bf16x8*>(dor + size_t(rr) * D + (lane >> 4) * 8);
 #pragma unroll
@@ -338,8 +369,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(KernelArgs) {
           qf[c][ks] = qs8[ks * 4];
           dof[c][ks] = ds8[ks * 4];
         }
-        l2[c] = lse2[q_row0 + row];
-        dl[c] = dlt[q_row0 + row];
+        l2[c] = lse2[rt];
+        dl[c] = dlt[rt];
       }
       f32x4 acc[QT][DT];
 #pragma unroll
@@ -379,7 +410,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(KernelArgs) {
         }
       };
 
-      issue(0, 0);
+      if (!PAD || n_blk > 0) issue(0, 0);
       for (int j = 0; j < n_blk; ++j) {
         const int stage = j & 1;
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -440,8 +471,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(KernelArgs) {
 #pragma unroll
       for (int c = 0; c < QT; ++c) {
         const int row = wave * RPW + c * 16 + (lane & 15);
-        const int rr = tiled_to_raster(q_row0 + row, g);
-        if (PAD && rr < 0) continue;
+        if (PAD && row >= n_valid) continue;  // no such token
+        int rr, rt;
+        query_rows(row, rr, rt);
         __bf16* dst = dqr + size_t(rr) * D + (lane >> 4) * 4;
 #pragma unroll
         for (int d = 0; d < DT; ++d) {
@@ -502,7 +534,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(KernelArgs) {
     int bh, key_row0, unit_keys;
     bool text_unit;
     int box_t = 0, box_h = 0, box_w = 0, lo_t = 0, lo_h = 0, lo_w = 0;
-    bool keys_exist = true;  // PAD: false when none of the unit's key frames exist
+    // PAD: the keys of a video unit are its tile's existing tokens in compact
+    // order (frame, row, column), part 1 starting at token 256; n_keys of them
+    // exist (none or fewer: the unit then streams nothing or writes fewer rows)
+    int k_ext = kFullExtent, k_base = 0, k_first = 0, n_keys = 0;
     if (unit < n_text_units) {
       bh = unit;
       key_row0 = g.n_vt;
@@ -524,14 +559,19 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(KernelArgs) {
       seeing_interval(tt, win_t(p), g.nt, lo_t, box_t);
       seeing_interval(th, win_h(p), g.nh, lo_h, box_h);
       seeing_interval(tw, win_w(p), g.nw, lo_w, box_w);
-      if constexpr (PAD) keys_exist = (r & 1) == 0 || g.T - tt * kTileT > 256 / (kTileH * kTileW);
+      if constexpr (PAD) {
+        k_ext = tile_extent(tt, th, tw, g);
+        k_base = (tt * kTileT * g.H + th * kTileH) * g.W + tw * kTileW;
+        k_first = (r & 1) * 256;
+        n_keys = min(extent_tokens(k_ext) - k_first, unit_keys);
+      }
     }
     const size_t slab = size_t(bh) * g.S * D;
     const size_t slab_t = size_t(bh) * g.S_t * D;  // packed tile-major tensors
     const int text_len = g.has_text ? g.text_length : 0;
     // text key slots at or after text_len are seen by nobody
     const int valid_keys = text_unit ? min(max(g.n_vt + text_len - key_row0, 0), unit_keys)
-                                     : (keys_exist ? unit_keys : 0);
+                                     : (PAD ? max(n_keys, 0) : unit_keys);
     const int n_qtiles = text_unit ? g.n_tiles : box_t * box_h * box_w;
     const int n_blk = valid_keys == 0 ? 0 : n_qtiles * BPT + (g.has_text ? kTextSlots / kQueryBlock : 0);
 
@@ -643,11 +683,19 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(KernelArgs) {
       bf16x8 kf[KT][KS], vf[KT][KS];
 #pragma unroll
       for (int kg = 0; kg < KT; ++kg) {
-        const int key = key_row0 + wave * 16 * KT + 16 * kg + (lane & 15);
+        const int local = wave * 16 * KT + 16 * kg + (lane & 15);
+        const int key = key_row0 + local;
         key_ok[kg] = !text_unit || key < g.n_vt + text_len;
         kras[kg] = tiled_to_raster(key, g);
-        // padding key row (PAD): computes on a valid row, never written
-        const int ksrc = PAD && kras[kg] < 0 ? 0 : kras[kg];
+        int ksrc = kras[kg];
+        if constexpr (PAD) {
+          if (!text_unit) {  // compact order; a key past n_keys computes on the last one, never written
+            int dt, dh, dw;
+            compact_token(k_first + (local < n_keys ? local : n_keys - 1), k_ext, dt, dh, dw);
+            ksrc = k_base + (dt * g.H + dh) * g.W + dw;
+            kras[kg] = local < n_keys ? ksrc : -1;
+          }
+        }
         const bf16x8* k8 = reinterpret_cast<const bf16x8*>(reinterpret_cast<const __bf16*>(a.k) + slab +
                                                            size_t(ksrc) * D + (lane >> 4) * 8);
         const bf16x8* v8 = reinterpret_cast<const bf16x8*>(reinterpret_cast<const __bf16*>(a.v) + slab +

@@ -80,6 +80,18 @@ __host__ __device__ inline int tile_extent(int tt, int th, int tw, const Geom& g
 __host__ __device__ inline int extent_frames(int e) { return e & 255; }
 __host__ __device__ inline int extent_rows(int e) { return (e >> 8) & 255; }
 __host__ __device__ inline int extent_cols(int e) { return e >> 16; }
+__host__ __device__ inline int extent_tokens(int e) {
+  return extent_frames(e) * extent_rows(e) * extent_cols(e);
+}
+// Compact order of a tile's existing tokens: frame, then row, then column.
+// Token r (< extent_tokens(e)) of tile (tt, th, tw) -> its offsets in the tile.
+__host__ __device__ inline void compact_token(int r, int e, int& dt, int& dh, int& dw) {
+  const int cols = extent_cols(e), plane = extent_rows(e) * cols;
+  dt = r / plane;
+  const int rem = r - dt * plane;
+  dh = rem / cols;
+  dw = rem - dh * cols;
+}
 
 // Launchers (each enqueues one kernel on `stream` and returns hipGetLastError()).
 hipError_t launch_rows_permute(const Geom& g, const void* src, void* dst, bool to_tiled,
