@@ -60,10 +60,10 @@
 // their scores are replaced by -inf (a select, so whatever k holds there is
 // ignored) and their packed V rows are zeros.
 // Video sizes that are not tile multiples (the PAD instantiation): the last
-// tile along an axis holds the remainder. Its K rows that do not exist are
-// fetched from a clamped row that does (every source address stays inside
-// the video), their scores are replaced by -inf and their packed V rows are
-// zeros. A video unit's rows are its tile's existing tokens in compact order
+// tile along an axis holds the remainder. Only the frames of a key tile that
+// exist are streamed; inside them, K rows that do not exist are fetched from
+// a clamped row that does (every source address stays inside the video),
+// their scores are replaced by -inf and their packed V rows are zeros. A video unit's rows are its tile's existing tokens in compact order
 // (a partial tile of at most 256 runs with 8 waves x 32 rows); rows past them
 // compute on a valid row and are not written. The first block of every window
 // is frame 0 of an existing tile, so the running max is finite from the first
@@ -174,7 +174,20 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(KernelArgs) 
 
   const int l0 = a.offsets[hd * g.n_q + u];
   const int l1 = a.offsets[hd * g.n_q + u + 1];
-  const int n_vid = (l1 - l0) * BPT;
+  // video key blocks: six frames per listed tile; with PAD only the frames
+  // that exist (all tiles of one tile row in t have the same count)
+  int n_vid = (l1 - l0) * BPT;
+  if constexpr (PAD) {
+    if (text_unit) {
+      n_vid = g.T * g.nh * g.nw;
+    } else {
+      n_vid = 0;
+      for (int t = l0; t < l1; ++t) {
+        const int tt = div_by(div_by(a.ids[t], g.nw, g.mag_nw), g.nh, g.mag_nh);
+        n_vid += min(g.T - tt * kTileT, kTileT);
+      }
+    }
+  }
   const int text_len = g.has_text ? g.text_length : 0;
   const int n_blk = n_vid + (text_len + kKeyBlock - 1) / kKeyBlock;
   const bool ragged = (text_len % kKeyBlock) != 0;
@@ -197,10 +210,24 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(KernelArgs) 
   // one that does not exist.
   int tile_kbase = 0, tile_vrow = 0;
   int tile_ext = kFullExtent;  // PAD: packed extent of the current tile
+  // PAD: blocks walk the existing frames of each listed tile in turn (block
+  // j + 1 is always decoded right after block j): cur_t is the next list
+  // entry, cur_sub the frame of the last decoded block
+  int cur_t = 0, cur_sub = -1;
   auto block_rows = [&](int j, int& kbase, int& krs, int& vrow) {
     if (j < n_vid) {
-      const int t = j / BPT;
-      const int sub = j - t * BPT;
+      int t, sub;
+      if constexpr (PAD) {
+        sub = cur_sub + 1;
+        if (j == 0 || sub == extent_frames(tile_ext)) {
+          sub = 0;
+          t = cur_t++;
+        }
+        cur_sub = sub;
+      } else {
+        t = j / BPT;
+        sub = j - t * BPT;
+      }
       if (sub == 0) {
         const int tile = ids[t];
         const int rest = div_by(tile, g.nw, g.mag_nw);
@@ -211,10 +238,7 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(KernelArgs) 
         tile_vrow = tile * kTileRows;
         if constexpr (PAD) tile_ext = tile_extent(tt, th, tw, g);
       }
-      if constexpr (PAD)
-        kbase = tile_kbase + min(sub, extent_frames(tile_ext) - 1) * g.H * g.W;
-      else
-        kbase = tile_kbase + sub * g.H * g.W;
+      kbase = tile_kbase + sub * g.H * g.W;
       krs = g.W;
       vrow = tile_vrow + sub * kKeyBlock;
     } else {
@@ -235,7 +259,7 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(KernelArgs) 
     // addresses
     int lane = opaque_lane<PAD>(this_lane);
     if constexpr (PAD) {
-      if (tile_ext != kFullExtent) {
+      if ((tile_ext >> 8) != (kFullExtent >> 8)) {
         // per-lane source row, clamped to the rows and columns that exist
 #pragma unroll
         for (int i = 0; i < IPW; ++i) {
@@ -361,9 +385,8 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(KernelArgs) 
           // keys of a partial tile that do not exist (the tile state still
           // describes block j: block j + 1 is decoded below). Key 16kt + 4(l/16)
           // + r of the block sits at patch row 2kt + l/32, column 4((l/16)&1) + r.
-          if (j < n_vid && tile_ext != kFullExtent) {
-            const int sub = j - (j / BPT) * BPT;
-            const int nf = extent_frames(tile_ext), nr = extent_rows(tile_ext), nc = extent_cols(tile_ext);
+          if (j < n_vid && (tile_ext >> 8) != (kFullExtent >> 8)) {
+            const int nr = extent_rows(tile_ext), nc = extent_cols(tile_ext);
             int hb = lane >> 5;
             asm volatile("" : "+v"(hb));
             const int wb = ((lane >> 4) & 1) * 4;
@@ -371,7 +394,7 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(KernelArgs) 
             for (int kt = 0; kt < 4; ++kt)
   #pragma unroll
               for (int r = 0; r < 4; ++r)
-                if (sub >= nf || 2 * kt + hb >= nr || wb + r >= nc)
+                if (2 * kt + hb >= nr || wb + r >= nc)
   #pragma unroll
                   for (int c = 0; c < QT; ++c) s[c][kt][r] = -INFINITY;
           }

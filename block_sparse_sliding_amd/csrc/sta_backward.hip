@@ -270,7 +270,20 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(KernelArgs) {
 
     const int l0 = a.offsets[hd * g.n_q + u];
     const int l1 = a.offsets[hd * g.n_q + u + 1];
-    const int n_vid = (l1 - l0) * BPT;
+    // video key blocks: six frames per listed tile; with PAD only the frames
+    // that exist (as in the forward)
+    int n_vid = (l1 - l0) * BPT;
+    if constexpr (PAD) {
+      if (unit < n_text_units) {
+        n_vid = g.T * g.nh * g.nw;
+      } else {
+        n_vid = 0;
+        for (int t = l0; t < l1; ++t) {
+          const int tt = div_by(div_by(a.ids[t], g.nw, g.mag_nw), g.nh, g.mag_nh);
+          n_vid += min(g.T - tt * kTileT, kTileT);
+        }
+      }
+    }
     const int text_len = g.has_text ? g.text_length : 0;
     const int n_blk = n_valid > 0 ? n_vid + (text_len + kKeyBlock - 1) / kKeyBlock : 0;
     const bool ragged = (text_len % kKeyBlock) != 0;
@@ -283,10 +296,21 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(KernelArgs) {
     // in place of one that does not exist
     int tile_kbase = 0, tile_vrow = 0;
     int tile_ext = kFullExtent;  // PAD: packed extent of the current tile
+    int cur_t = 0, cur_sub = -1;  // PAD: the forward's walk over existing frames
     auto block_rows = [&](int j, int& kbase, int& krs, int& vrow) {
       if (j < n_vid) {
-        const int t = j / BPT;
-        const int sub = j - t * BPT;
+        int t, sub;
+        if constexpr (PAD) {
+          sub = cur_sub + 1;
+          if (j == 0 || sub == extent_frames(tile_ext)) {
+            sub = 0;
+            t = cur_t++;
+          }
+          cur_sub = sub;
+        } else {
+          t = j / BPT;
+          sub = j - t * BPT;
+        }
         if (sub == 0) {
           const int tile = ids[t];
           const int rest = div_by(tile, g.nw, g.mag_nw);
@@ -297,10 +321,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(KernelArgs) {
           tile_vrow = tile * kTileRows;
           if constexpr (PAD) tile_ext = tile_extent(tt, th, tw, g);
         }
-        if constexpr (PAD)
-          kbase = tile_kbase + min(sub, extent_frames(tile_ext) - 1) * g.H * g.W;
-        else
-          kbase = tile_kbase + sub * g.H * g.W;
+        kbase = tile_kbase + sub * g.H * g.W;
         krs = g.W;
         vrow = tile_vrow + sub * kKeyBlock;
       } else {
@@ -317,7 +338,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(KernelArgs) {
       // rather than hoisted (and spilled) as 64-bit addresses
       int lane = opaque_lane<PAD>(this_lane);
       if constexpr (PAD) {
-        if (tile_ext != kFullExtent) {  // per-lane rows, clamped to the rows and columns that exist
+        if ((tile_ext >> 8) != (kFullExtent >> 8)) {  // per-lane rows, clamped to the rows and columns that exist
 #pragma unroll
           for (int i = 0; i < IPW; ++i) {
             const int q = wave * IPW + i;
@@ -572,8 +593,15 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(KernelArgs) {
     // text key slots at or after text_len are seen by nobody
     const int valid_keys = text_unit ? min(max(g.n_vt + text_len - key_row0, 0), unit_keys)
                                      : (PAD ? max(n_keys, 0) : unit_keys);
-    const int n_qtiles = text_unit ? g.n_tiles : box_t * box_h * box_w;
-    const int n_blk = valid_keys == 0 ? 0 : n_qtiles * BPT + (g.has_text ? kTextSlots / kQueryBlock : 0);
+    // streamed video query blocks: six frames per query tile of the box (or of
+    // the video, for a text unit); with PAD only the frames that exist (the
+    // frame count depends on the tile row in t alone)
+    int n_vblk = text_unit ? g.n_tiles * BPT : box_t * box_h * box_w * BPT;
+    if constexpr (PAD) {
+      n_vblk = text_unit ? g.T * g.nh * g.nw
+                         : (min(g.T, (lo_t + box_t) * kTileT) - lo_t * kTileT) * box_h * box_w;
+    }
+    const int n_blk = valid_keys == 0 ? 0 : n_vblk + (g.has_text ? kTextSlots / kQueryBlock : 0);
 
     const char* __restrict__ qr = reinterpret_cast<const char*>(a.q) + slab * 2;
     const char* __restrict__ dor = reinterpret_cast<const char*>(a.dout) + slab * 2;
@@ -587,10 +615,21 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(KernelArgs) {
     // with PAD, tile_ext describes the current query tile as in the dq kernel
     int tile_qbase = 0, tile_vrow = 0;
     int tile_ext = kFullExtent;  // PAD: packed extent of the current tile
+    int cur_t = 0, cur_sub = -1;  // PAD: the walk over existing frames of the dq kernel
     auto block_rows = [&](int j, int& qbase, int& qrs, int& vrow) {
-      if (j < n_qtiles * BPT) {
-        const int t = j / BPT;
-        const int sub = j - t * BPT;
+      if (j < n_vblk) {
+        int t, sub;
+        if constexpr (PAD) {
+          sub = cur_sub + 1;
+          if (j == 0 || sub == extent_frames(tile_ext)) {
+            sub = 0;
+            t = cur_t++;
+          }
+          cur_sub = sub;
+        } else {
+          t = j / BPT;
+          sub = j - t * BPT;
+        }
         if (sub == 0) {
           int tt, th, tw;
           if (text_unit) {
@@ -608,15 +647,12 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(KernelArgs) {
           tile_vrow = ((tt * g.nh + th) * g.nw + tw) * kTileRows;
           if constexpr (PAD) tile_ext = tile_extent(tt, th, tw, g);
         }
-        if constexpr (PAD)
-          qbase = tile_qbase + min(sub, extent_frames(tile_ext) - 1) * g.H * g.W;
-        else
-          qbase = tile_qbase + sub * g.H * g.W;
+        qbase = tile_qbase + sub * g.H * g.W;
         qrs = g.W;
         vrow = tile_vrow + sub * kQueryBlock;
       } else {
-        qbase = g.n_video + (j - n_qtiles * BPT) * kQueryBlock;
-        vrow = g.n_vt + (j - n_qtiles * BPT) * kQueryBlock;
+        qbase = g.n_video + (j - n_vblk) * kQueryBlock;
+        vrow = g.n_vt + (j - n_vblk) * kQueryBlock;
         qrs = kTileW;
         if constexpr (PAD) tile_ext = kFullExtent;
       }
@@ -624,7 +660,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(KernelArgs) {
     auto issue_raw = [&](const char* src, char* dst, int qbase, int qrs) {
       int lane = opaque_lane<PAD>(this_lane);  // as in the dq kernel
       if constexpr (PAD) {
-        if (tile_ext != kFullExtent) {  // per-lane rows, clamped to the rows and columns that exist
+        if ((tile_ext >> 8) != (kFullExtent >> 8)) {  // per-lane rows, clamped to the rows and columns that exist
 #pragma unroll
           for (int i = 0; i < IPW; ++i) {
             const int q = wave * IPW + i;

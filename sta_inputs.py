@@ -78,10 +78,11 @@ WORKLOADS = {
                       _per_head(24, [(3, 3, 3)]), True, 128, 50),
     "headline": Workload("headline", 1, 24, 128, (30, 48, 80),
                          _per_head(24, [(3, 3, 3)]), True, 226, 60),
-    # the headline with 45 rows (a 720-pixel frame height at a 16x spatial
-    # reduction): not a multiple of the tile height, so the last tile row
-    # holds 5 of 8 rows; same tile grid (5, 6, 10)
-    "ragged": Workload("ragged", 1, 24, 128, (30, 45, 80),
+    # the headline at 33 frames and 45 rows (a 129-frame clip at 4x temporal
+    # and a 720-pixel height at 16x spatial reduction): neither is a tile
+    # multiple, so the last tile row in t holds 3 of 6 frames and the last in
+    # h 5 of 8 rows; tile grid (6, 6, 10)
+    "ragged": Workload("ragged", 1, 24, 128, (33, 45, 80),
                        _per_head(24, [(3, 3, 3)]), True, 226, 70),
 }
 

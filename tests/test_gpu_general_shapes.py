@@ -121,9 +121,10 @@ def test_partial_tiles_medium_sampled():
 
 
 def test_backward_full_size_ragged():
-    """(30, 45, 80) + 256 text, D = 128 (the last tile row holds 5 of 8 rows):
-    every gradient written, sum rules per head, sampled dq rows and every key
-    row of one partial key tile, at the launch shape the benchmark times."""
+    """(33, 45, 80) + 256 text, D = 128 (last tile row in t: 3 of 6 frames; in h:
+    5 of 8 rows): every gradient written, sum rules per head, sampled dq rows
+    and every key row of two partial key tiles, at the launch shape the
+    benchmark times."""
     import sta_inputs
 
     wl = sta_inputs.WORKLOADS["ragged"]
@@ -145,9 +146,12 @@ def test_backward_full_size_ragged():
     assert bool((sdk.abs() <= 1e-2 * dk.double().abs().sum(dim=2) + 1e-3).all())
     rng = np.random.default_rng(11)
     qrows = np.unique(np.concatenate([rng.integers(0, nv, 16), [nv - 1, nv, S - 1]]))
-    # key tile (2, 5, 4): rows 40..44 of the frame exist, 5 of 8
+    # key tile (2, 5, 4): rows 40..44 exist (5 of 8); key tile (5, 2, 3): frames
+    # 30..32 exist (3 of 6)
     keys = np.asarray([((12 + a) * H + 40 + b) * W + 32 + c
-                       for a in range(6) for b in range(5) for c in range(8)])
+                       for a in range(6) for b in range(5) for c in range(8)]
+                      + [((30 + a) * H + 16 + b) * W + 24 + c
+                         for a in range(3) for b in range(8) for c in range(8)])
     for h in range(heads):
         sl = slice(h, h + 1)
         rq, rk, rv = oracle.sta_reference_backward(

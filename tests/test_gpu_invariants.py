@@ -99,7 +99,7 @@ def expected_uniform(video, window, ell, has_text):
     ((48, 72, 128), [(3, 3, 3)], 128, True, 128),
     ((18, 24, 24), [(1, 3, 3)], 0, False, 64),
     # sizes that are not tile multiples (partial last tiles)
-    ((30, 45, 80), [(3, 3, 3), (1, 2, 4)], 226, True, 128),
+    ((33, 45, 80), [(3, 3, 3), (1, 2, 4)], 226, True, 128),
     ((17, 21, 30), [(2, 2, 3), (3, 1, 1)], 100, True, 128),
     ((1, 12, 20), [(1, 2, 3)], 0, False, 64),
     ((13, 9, 33), [(3, 2, 5)], 256, True, 64),
