@@ -11,7 +11,7 @@
 // The page shows only the forward call; these follow from its definition.
 //
 // Three passes over the inputs, each a launch on the caller's stream:
-//   prep   lse2 = lse * log2(e) and delta, per row in tile-major order;
+//   prep   lse2 = lse * log2(e) and -delta, per row in tile-major order;
 //   pack   K^T, Q^T and dout^T as MFMA A-operand fragments (the forward's V^T
 //          packing, applied to these tensors);
 //   dq     query-stationary: the forward's loop with S^T = K Q^T and
@@ -145,7 +145,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(Geom g, const __bf16* __r
   const int rr = tiled_to_raster(r, g);
   if (rr < 0) {  // padding row of a partial tile: P = 2^(s c' - inf) = 0 wherever it is streamed
     if (part == 0) {
-      delta[bh * g.S_t + r] = 0.f;
+      delta[bh * g.S_t + r] = -0.f;
       lse2[bh * g.S_t + r] = INFINITY;
     }
     return;
@@ -162,7 +162,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(Geom g, const __bf16* __r
   acc += __shfl_xor(acc, 1);
   acc += __shfl_xor(acc, 2);
   if (part == 0) {
-    delta[bh * g.S_t + r] = acc;
+    delta[bh * g.S_t + r] = -acc;  // stored negated: it starts the dP accumulators
     lse2[bh * g.S_t + r] = lse[bh * g.S + rr] * kLog2e;
   }
 }
@@ -377,7 +377,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(KernelArgs) {
       constexpr int RPW = QT * 16;
       const float qs = a.q_scale;
       bf16x8 qf[QT][KS], dof[QT][KS];
-      float l2[QT], dl[QT];
+      float l2[QT], dl[QT];  // lse2 and -delta of this lane's query rows
 #pragma unroll
       for (int c = 0; c < QT; ++c) {
         const int row = wave * RPW + c * 16 + (lane & 15);  // < q_rows for every unit shape
@@ -410,8 +410,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(KernelArgs) {
       };
 
       // A x B^T-style score product over one raw block in LDS: out[c][kt] =
-      // sum over d of blk[16 kt + l%16][d] * frag[c][d]
-      auto scores = [&](const char* blk, const bf16x8 (&frag)[QT][KS], f32x4 (&out)[QT][4]) {
+      // init[c] + sum over d of blk[16 kt + l%16][d] * frag[c][d]
+      auto scores = [&](const char* blk, const bf16x8 (&frag)[QT][KS], const f32x4 (&init)[QT],
+                        f32x4 (&out)[QT][4]) {
         constexpr int NF = 4 * KS;
         bf16x8 kf[NF];
         auto kload = [&](int f) {
@@ -425,7 +426,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(KernelArgs) {
 #pragma unroll
           for (int c = 0; c < QT; ++c)
             out[c][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[f], frag[c][ks],
-                                                                  ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : out[c][kt], 0, 0, 0);
+                                                                  ks == 0 ? init[c] : out[c][kt], 0, 0, 0);
           if (f + kKPrefetch < NF) kload(f + kKPrefetch);
           __builtin_amdgcn_sched_barrier(0);
         }
@@ -437,10 +438,18 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(KernelArgs) {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
         f32x4 s[QT][4], dp[QT][4];
-        scores(lds[stage][0], qf, s);
-        scores(lds[stage][1], dof, dp);
+        f32x4 zero[QT], nd[QT];  // dP^T starts at -delta of its query (column)
+#pragma unroll
+        for (int c = 0; c < QT; ++c) {
+          float x = dl[c];
+          asm volatile("" : "+v"(x));  // built here, per block, not kept live across the loop
+          zero[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+          nd[c] = f32x4{x, x, x, x};
+        }
+        scores(lds[stage][0], qf, zero, s);
+        scores(lds[stage][1], dof, nd, dp);
         if (j + 1 < n_blk) issue(j + 1, stage ^ 1);
-        // P = 2^(c' s - lse2), dS = P (dP - delta)
+        // P = 2^(c' s - lse2), dS = P (dP - delta) with dP - delta from the MFMAs
 #pragma unroll
         for (int c = 0; c < QT; ++c)
 #pragma unroll
@@ -448,7 +457,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(KernelArgs) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
               const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[c][kt][r], qs, -l2[c]));
-              dp[c][kt][r] = p * (dp[c][kt][r] - dl[c]);
+              dp[c][kt][r] = p * dp[c][kt][r];
             }
         // keys at or after the text length (last text block only): dS = 0 by
         // select, so whatever k and v hold there cannot reach dq
@@ -751,8 +760,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(KernelArgs) {
           dv[kg][d] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
 
-      // out[kg][i] = sum over d of blk[16 (2 hq + i) + l%16][d] * frag[kg][d]
-      auto scores = [&](const char* blk, int hq, const bf16x8 (&frag)[KT][KS], f32x4 (&out)[KT][2]) {
+      // out[kg][i] = init[i] + sum over d of blk[16 (2 hq + i) + l%16][d] * frag[kg][d]
+      auto scores = [&](const char* blk, int hq, const bf16x8 (&frag)[KT][KS], const f32x4 (&init)[2],
+                        f32x4 (&out)[KT][2]) {
         constexpr int NF = 2 * KS;
         bf16x8 af[NF];
         auto aload = [&](int f) {
@@ -766,7 +776,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(KernelArgs) {
 #pragma unroll
           for (int kg = 0; kg < KT; ++kg)
             out[kg][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[f], frag[kg][ks],
-                                                                 ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : out[kg][i], 0, 0, 0);
+                                                                 ks == 0 ? init[i] : out[kg][i], 0, 0, 0);
           if (f + kKvPrefetch < NF) aload(f + kKvPrefetch);
           __builtin_amdgcn_sched_barrier(0);
         }
@@ -784,20 +794,22 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(KernelArgs) {
 #pragma unroll
         for (int hq = 0; hq < 2; ++hq) {
           f32x4 s[KT][2], dp[KT][2];
-          scores(lds[stage][0], hq, kf, s);
-          scores(lds[stage][1], hq, vf, dp);
+          // rows of the accumulators: query 16 (2 hq + i) + 4 (l/16) + r; dP
+          // starts at -delta of those rows
+          const f32x4 zero[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+          const f32x4 nd[2] = {dlv[(2 * hq) * 4 + (lane >> 4)], dlv[(2 * hq + 1) * 4 + (lane >> 4)]};
+          scores(lds[stage][0], hq, kf, zero, s);
+          scores(lds[stage][1], hq, vf, nd, dp);
           if (hq == 0 && j + 1 < n_blk) issue(j + 1, stage ^ 1);
-          // rows of the accumulators: query 16 (2 hq + i) + 4 (l/16) + r
 #pragma unroll
           for (int i = 0; i < 2; ++i) {
             const f32x4 l2 = l2v[(2 * hq + i) * 4 + (lane >> 4)];
-            const f32x4 dl = dlv[(2 * hq + i) * 4 + (lane >> 4)];
 #pragma unroll
             for (int kg = 0; kg < KT; ++kg)
 #pragma unroll
               for (int r = 0; r < 4; ++r) {
                 const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kg][i][r], qs, -l2[r]));
-                dp[kg][i][r] = p * (dp[kg][i][r] - dl[r]);
+                dp[kg][i][r] = p * dp[kg][i][r];
                 s[kg][i][r] = p;
               }
           }

@@ -141,7 +141,7 @@ struct BwdArgs {
   const void* qt;        // packed Q^T fragments
   const void* dot;       // packed dout^T fragments
   const float* lse2;     // tile-major lse * log2(e)
-  const float* delta;    // tile-major rowsum(dout * out)
+  const float* delta;    // tile-major -rowsum(dout * out), negated: it starts the dP accumulators
   void* dq;              // bf16 raster rows (the caller's dq, dk, dv)
   void* dk;
   void* dv;
