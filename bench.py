@@ -119,7 +119,9 @@ def cpu_baseline(wl, q, k, v, budget_s: float, flops: float):
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         threads = os.cpu_count() or 1
-    rows = sta_inputs.sample_rows(wl, per_head=192).numpy()
+    # about 0.2 ms of oracle work per row at the headline shape on 16 host
+    # threads: 512 rows per head fill a 10-30 s budget before every head is done
+    rows = sta_inputs.sample_rows(wl, per_head=512).numpy()
     done_rows, elapsed, heads_done = 0, 0.0, 0
     for h in range(wl.heads):
         qh, kh, vh = (x[:, h:h + 1].cpu() for x in (q, k, v))
