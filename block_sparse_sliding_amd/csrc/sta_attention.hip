@@ -63,11 +63,12 @@
 // tile along an axis holds the remainder. Only the frames of a key tile that
 // exist are streamed; inside them, K rows that do not exist are fetched from
 // a clamped row that does (every source address stays inside the video),
-// their scores are replaced by -inf and their packed V rows are zeros. A video unit's rows are its tile's existing tokens in compact order
-// (a partial tile of at most 256 runs with 8 waves x 32 rows); rows past them
-// compute on a valid row and are not written. The first block of every window
-// is frame 0 of an existing tile, so the running max is finite from the first
-// block on.
+// their scores are replaced by -inf and their packed V rows are zeros. A
+// video unit's rows are its tile's existing tokens in compact order (frame,
+// row, column; a partial tile of at most 256 runs with 8 waves x 32 rows);
+// rows past them compute on a valid row and are not written. The first block
+// of every window is frame 0 of an existing tile, so the running max is
+// finite from the first block on.
 // Epilogue: O = O^T / l rounded to bf16, lse = (m + log2 l) * ln 2, at raster rows.
 #include <type_traits>
 
