@@ -6,6 +6,7 @@
   also for sizes that are not tile multiples (partial last tiles).
 * padded text K/V rows never reach the result (bitwise).
 * repeated calls are bitwise identical; batch entries are independent.
+* lse is optional: without it, out is the same to the bit.
 """
 
 import math
@@ -14,6 +15,7 @@ import numpy as np
 import pytest
 import torch
 
+import block_sparse_sliding_amd as sta
 import sta_inputs
 from _parity import note, run_sta
 
@@ -166,3 +168,22 @@ def test_deterministic_and_batch_independent():
     assert torch.equal(lseb[0].view(torch.int32), lse1[0].view(torch.int32))
     assert torch.equal(outb[1].view(torch.int16), outy[0].view(torch.int16))
     assert torch.equal(lseb[1].view(torch.int32), lsey[0].view(torch.int32))
+
+
+@pytest.mark.parametrize("video", [(18, 24, 32), (17, 21, 30)])
+def test_lse_is_optional(video):
+    """sta_forward with lse = NULL writes the same out bits as with lse."""
+    nv = video[0] * video[1] * video[2]
+    S = nv + 256
+    windows = [(3, 3, 3), (1, 2, 3)]
+    note(f"lse = NULL {video}")
+    g = torch.Generator(device="cuda").manual_seed(31)
+    q, k, v = [torch.randn(1, 2, S, 128, generator=g, device="cuda").to(torch.bfloat16)
+               for _ in range(3)]
+    out1, _ = run_sta(q, k, v, windows, 99, True, video)
+    dims = sta.make_dims(1, 2, 128, video)
+    ws = torch.empty(sta.sta_workspace_bytes(dims, windows, True), dtype=torch.uint8, device="cuda")
+    out2 = torch.full_like(q, float("nan"))
+    sta.sta_forward(dims, q, k, v, windows, 99, True, out2, None, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out1.view(torch.int16), out2.view(torch.int16))
