@@ -65,7 +65,8 @@
 // a clamped row that does (every source address stays inside the video),
 // their scores are replaced by -inf and their packed V rows are zeros. A
 // video unit's rows are its tile's existing tokens in compact order (frame,
-// row, column; a partial tile of at most 256 runs with 8 waves x 32 rows);
+// row, column; a partial tile of at most 256 or 128 runs with 8 waves x 32 or
+// 16 rows);
 // rows past them compute on a valid row and are not written. The first block
 // of every window is frame 0 of an existing tile, so the running max is
 // finite from the first block on.
@@ -488,6 +489,12 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(KernelArgs) 
       }
     }
   };
+  if constexpr (PAD) {
+    if (q_rows <= 16 * kWaves) {  // a small partial tile: 8 waves x 16 rows
+      run(std::integral_constant<int, 1>{});
+      continue;
+    }
+  }
   if (text_unit || (PAD && q_rows <= kTextSlots))
     run(std::integral_constant<int, kTextSlots / 16 / kWaves>{});
   else

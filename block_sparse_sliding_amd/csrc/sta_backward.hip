@@ -512,7 +512,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(KernelArgs) {
         }
       }
     };
-    if (q_rows == 256)
+    if (q_rows == 256 && !(PAD && n_valid <= 128))  // PAD: a small partial tile runs 8 x 16 rows
       run(std::integral_constant<int, 2>{});
     else
       run(std::integral_constant<int, 1>{});
@@ -865,7 +865,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(KernelArgs) {
         }
       }
     };
-    if (unit_keys == 256)
+    if (unit_keys == 256 && !(PAD && !text_unit && n_keys <= 128))  // PAD: a small partial tile runs 8 x 16 keys
       run(std::integral_constant<int, 2>{});
     else
       run(std::integral_constant<int, 1>{});
