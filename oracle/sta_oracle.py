@@ -21,8 +21,7 @@ What that page fixes, restated:
 * attention is exact softmax attention whose map holds only fully-dense or
   fully-empty tile blocks, with no mixed blocks (Why is STA Fast?).
 
-Readings where the page is silent (each one is listed with its reason in
-the design notes of the repository):
+Readings where the page is silent:
 
 * video tokens come in raster order (t slowest, w fastest), the text slots
   follow the video, and the valid text slots are the first ``text_length``;
