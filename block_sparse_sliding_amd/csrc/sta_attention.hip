@@ -60,10 +60,12 @@
 // their scores are replaced by -inf (a select, so whatever k holds there is
 // ignored) and their packed V rows are zeros.
 // Video sizes that are not tile multiples (the PAD instantiation): the last
-// tile along an axis holds the remainder. Only the frames of a key tile that
-// exist are streamed; inside them, K rows that do not exist are fetched from
-// a clamped row that does (every source address stays inside the video),
-// their scores are replaced by -inf and their packed V rows are zeros. A
+// tile along an axis holds the remainder, and a partial key tile streams
+// ceil(tokens / 64) blocks of its existing tokens in compact order (frame,
+// row, column; the packed V^T uses the same order). In the last block, keys
+// past the tile's tokens are fetched from the last token that exists (every
+// source address stays inside the video), their scores are replaced by -inf
+// and their packed V rows are zeros. A
 // video unit's rows are its tile's existing tokens in compact order (frame,
 // row, column; a partial tile of at most 256 or 128 runs with 8 waves x 32 or
 // 16 rows);
@@ -165,7 +167,7 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(KernelArgs) 
         return q_base + (dt * g.H + dh) * g.W + dw;
       }
     }
-    return tiled_to_raster(q_row0 + row, g);
+    return PAD ? tiled_to_raster(q_row0 + row, g) : tiled_to_raster_full(q_row0 + row, g);
   };
   const size_t slab = size_t(bh) * g.S * D;      // element offset of this (b, head), raster
   const size_t slab_t = size_t(bh) * g.S_t * D;  // the same in the packed tile-major V^T
@@ -176,18 +178,17 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(KernelArgs) 
 
   const int l0 = a.offsets[hd * g.n_q + u];
   const int l1 = a.offsets[hd * g.n_q + u + 1];
-  // video key blocks: six frames per listed tile; with PAD only the frames
-  // that exist (all tiles of one tile row in t have the same count)
+  // video key blocks: six per listed tile; with PAD, ceil(tokens / 64) per
+  // tile, its existing tokens in compact order
   int n_vid = (l1 - l0) * BPT;
   if constexpr (PAD) {
-    if (text_unit) {
-      n_vid = g.T * g.nh * g.nw;
-    } else {
-      n_vid = 0;
-      for (int t = l0; t < l1; ++t) {
-        const int tt = div_by(div_by(a.ids[t], g.nw, g.mag_nw), g.nh, g.mag_nh);
-        n_vid += min(g.T - tt * kTileT, kTileT);
-      }
+    n_vid = 0;
+    for (int t = l0; t < l1; ++t) {
+      const int tile = a.ids[t];
+      const int rest = div_by(tile, g.nw, g.mag_nw);
+      const int tt = div_by(rest, g.nh, g.mag_nh);
+      n_vid += (extent_tokens(tile_extent(tt, rest - tt * g.nh, tile - rest * g.nw, g)) + kKeyBlock - 1) /
+               kKeyBlock;
     }
   }
   const int text_len = g.has_text ? g.text_length : 0;
@@ -212,16 +213,16 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(KernelArgs) 
   // one that does not exist.
   int tile_kbase = 0, tile_vrow = 0;
   int tile_ext = kFullExtent;  // PAD: packed extent of the current tile
-  // PAD: blocks walk the existing frames of each listed tile in turn (block
-  // j + 1 is always decoded right after block j): cur_t is the next list
-  // entry, cur_sub the frame of the last decoded block
+  // PAD: blocks walk the blocks of each listed tile in turn (block j + 1 is
+  // always decoded right after block j): cur_t is the next list entry,
+  // cur_sub the block within its tile of the last decoded block
   int cur_t = 0, cur_sub = -1;
   auto block_rows = [&](int j, int& kbase, int& krs, int& vrow) {
     if (j < n_vid) {
       int t, sub;
       if constexpr (PAD) {
         sub = cur_sub + 1;
-        if (j == 0 || sub == extent_frames(tile_ext)) {
+        if (j == 0 || sub * kKeyBlock >= extent_tokens(tile_ext)) {
           sub = 0;
           t = cur_t++;
         }
@@ -262,13 +263,16 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(KernelArgs) 
     int lane = opaque_lane<PAD>(this_lane);
     if constexpr (PAD) {
       if ((tile_ext >> 8) != (kFullExtent >> 8)) {
-        // per-lane source row, clamped to the rows and columns that exist
+        // a tile with missing rows or columns: block row r is token 64 sub + r
+        // of the tile in compact order, clamped to the last one that exists
+        const int last = extent_tokens(tile_ext) - 1;
 #pragma unroll
         for (int i = 0; i < IPW; ++i) {
           const int q = wave * IPW + i;
           const int rin = (lane >> 2) % RPI;
-          const int h = (q * RPI) >> 3, w = ((q * RPI) & 7) + rin;
-          const int row = kbase + min(h, extent_rows(tile_ext) - 1) * krs + min(w, extent_cols(tile_ext) - 1);
+          int dt, dh, dw;
+          compact_token(min(cur_sub * kKeyBlock + q * RPI + rin, last), tile_ext, dt, dh, dw);
+          const int row = tile_kbase + (dt * g.H + dh) * g.W + dw;
           const int chunk = 4 * (lane / (4 * RPI)) + ((lane & 3) ^ sw(q * RPI + rin));
           dma16(kr + size_t(row) * ROWB + chunk * 16, &lds[st][0][q * 1024]);
         }
@@ -384,19 +388,18 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(KernelArgs) 
                 for (int c = 0; c < QT; ++c) s[c][kt][r] = -INFINITY;
         }
         if constexpr (PAD) {
-          // keys of a partial tile that do not exist (the tile state still
-          // describes block j: block j + 1 is decoded below). Key 16kt + 4(l/16)
-          // + r of the block sits at patch row 2kt + l/32, column 4((l/16)&1) + r.
-          if (j < n_vid && (tile_ext >> 8) != (kFullExtent >> 8)) {
-            const int nr = extent_rows(tile_ext), nc = extent_cols(tile_ext);
-            int hb = lane >> 5;
-            asm volatile("" : "+v"(hb));
-            const int wb = ((lane >> 4) & 1) * 4;
+          // the last block of a tile whose token count is not a multiple of
+          // 64: keys past the tile's tokens (the tile state still describes
+          // block j; block j + 1 is decoded below)
+          const int n_tok = extent_tokens(tile_ext);
+          if (j < n_vid && (cur_sub + 1) * kKeyBlock > n_tok) {
+            int key0 = cur_sub * kKeyBlock + 4 * (lane >> 4);
+            asm volatile("" : "+v"(key0));
   #pragma unroll
             for (int kt = 0; kt < 4; ++kt)
   #pragma unroll
               for (int r = 0; r < 4; ++r)
-                if (2 * kt + hb >= nr || wb + r >= nc)
+                if (key0 + 16 * kt + r >= n_tok)
   #pragma unroll
                   for (int c = 0; c < QT; ++c) s[c][kt][r] = -INFINITY;
           }

@@ -250,11 +250,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(KernelArgs) {
           int dt, dh, dw;
           compact_token(first + (row < n_valid ? row : n_valid - 1), q_ext, dt, dh, dw);
           raster = q_base + (dt * g.H + dh) * g.W + dw;
-          tiled = u * kTileRows + (dt * kTileH + dh) * kTileW + dw;
+          tiled = u * kTileRows + first + (row < n_valid ? row : n_valid - 1);  // compact layout
           return;
         }
       }
-      raster = tiled_to_raster(q_row0 + row, g);
+      raster = PAD ? tiled_to_raster(q_row0 + row, g) : tiled_to_raster_full(q_row0 + row, g);
       tiled = q_row0 + row;
     };
     const int hd = bh % g.heads;
@@ -270,18 +270,17 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(KernelArgs) {
 
     const int l0 = a.offsets[hd * g.n_q + u];
     const int l1 = a.offsets[hd * g.n_q + u + 1];
-    // video key blocks: six frames per listed tile; with PAD only the frames
-    // that exist (as in the forward)
+    // video key blocks: six per listed tile; with PAD, ceil(tokens / 64) per
+    // tile (as in the forward)
     int n_vid = (l1 - l0) * BPT;
     if constexpr (PAD) {
-      if (unit < n_text_units) {
-        n_vid = g.T * g.nh * g.nw;
-      } else {
-        n_vid = 0;
-        for (int t = l0; t < l1; ++t) {
-          const int tt = div_by(div_by(a.ids[t], g.nw, g.mag_nw), g.nh, g.mag_nh);
-          n_vid += min(g.T - tt * kTileT, kTileT);
-        }
+      n_vid = 0;
+      for (int t = l0; t < l1; ++t) {
+        const int tile = a.ids[t];
+        const int rest = div_by(tile, g.nw, g.mag_nw);
+        const int tt = div_by(rest, g.nh, g.mag_nh);
+        n_vid += (extent_tokens(tile_extent(tt, rest - tt * g.nh, tile - rest * g.nw, g)) + kKeyBlock - 1) /
+                 kKeyBlock;
       }
     }
     const int text_len = g.has_text ? g.text_length : 0;
@@ -302,7 +301,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(KernelArgs) {
         int t, sub;
         if constexpr (PAD) {
           sub = cur_sub + 1;
-          if (j == 0 || sub == extent_frames(tile_ext)) {
+          if (j == 0 || sub * kKeyBlock >= extent_tokens(tile_ext)) {
             sub = 0;
             t = cur_t++;
           }
@@ -338,13 +337,17 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(KernelArgs) {
       // rather than hoisted (and spilled) as 64-bit addresses
       int lane = opaque_lane<PAD>(this_lane);
       if constexpr (PAD) {
-        if ((tile_ext >> 8) != (kFullExtent >> 8)) {  // per-lane rows, clamped to the rows and columns that exist
+        if ((tile_ext >> 8) != (kFullExtent >> 8)) {
+          // a tile with missing rows or columns: block row r is token 64 sub + r
+          // of the tile in compact order, clamped to the last one that exists
+          const int last = extent_tokens(tile_ext) - 1;
 #pragma unroll
           for (int i = 0; i < IPW; ++i) {
             const int q = wave * IPW + i;
             const int rin = (lane >> 2) % RPI;
-            const int h = (q * RPI) >> 3, w = ((q * RPI) & 7) + rin;
-            const int row = kbase + min(h, extent_rows(tile_ext) - 1) * krs + min(w, extent_cols(tile_ext) - 1);
+            int dt, dh, dw;
+            compact_token(min(cur_sub * kKeyBlock + q * RPI + rin, last), tile_ext, dt, dh, dw);
+            const int row = tile_kbase + (dt * g.H + dh) * g.W + dw;
             const int chunk = 4 * (lane / (4 * RPI)) + ((lane & 3) ^ sw(q * RPI + rin));
             dma16(src + size_t(row) * ROWB + chunk * 16, dst + q * 1024);
           }
@@ -602,13 +605,18 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(KernelArgs) {
     // text key slots at or after text_len are seen by nobody
     const int valid_keys = text_unit ? min(max(g.n_vt + text_len - key_row0, 0), unit_keys)
                                      : (PAD ? max(n_keys, 0) : unit_keys);
-    // streamed video query blocks: six frames per query tile of the box (or of
-    // the video, for a text unit); with PAD only the frames that exist (the
-    // frame count depends on the tile row in t alone)
+    // streamed video query blocks: six per query tile of the box (or of the
+    // video, for a text unit); with PAD, ceil(tokens / 64) per tile
     int n_vblk = text_unit ? g.n_tiles * BPT : box_t * box_h * box_w * BPT;
     if constexpr (PAD) {
-      n_vblk = text_unit ? g.T * g.nh * g.nw
-                         : (min(g.T, (lo_t + box_t) * kTileT) - lo_t * kTileT) * box_h * box_w;
+      const int t0 = text_unit ? 0 : lo_t, t1 = text_unit ? g.nt : lo_t + box_t;
+      const int h0 = text_unit ? 0 : lo_h, h1 = text_unit ? g.nh : lo_h + box_h;
+      const int w0 = text_unit ? 0 : lo_w, w1 = text_unit ? g.nw : lo_w + box_w;
+      n_vblk = 0;
+      for (int tt = t0; tt < t1; ++tt)
+        for (int th = h0; th < h1; ++th)
+          for (int tw = w0; tw < w1; ++tw)
+            n_vblk += (extent_tokens(tile_extent(tt, th, tw, g)) + kQueryBlock - 1) / kQueryBlock;
     }
     const int n_blk = valid_keys == 0 ? 0 : n_vblk + (g.has_text ? kTextSlots / kQueryBlock : 0);
 
@@ -630,7 +638,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(KernelArgs) {
         int t, sub;
         if constexpr (PAD) {
           sub = cur_sub + 1;
-          if (j == 0 || sub == extent_frames(tile_ext)) {
+          if (j == 0 || sub * kKeyBlock >= extent_tokens(tile_ext)) {
             sub = 0;
             t = cur_t++;
           }
@@ -669,13 +677,15 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(KernelArgs) {
     auto issue_raw = [&](const char* src, char* dst, int qbase, int qrs) {
       int lane = opaque_lane<PAD>(this_lane);  // as in the dq kernel
       if constexpr (PAD) {
-        if ((tile_ext >> 8) != (kFullExtent >> 8)) {  // per-lane rows, clamped to the rows and columns that exist
+        if ((tile_ext >> 8) != (kFullExtent >> 8)) {  // compact order, as in the dq kernel
+          const int last = extent_tokens(tile_ext) - 1;
 #pragma unroll
           for (int i = 0; i < IPW; ++i) {
             const int q = wave * IPW + i;
             const int rin = (lane >> 2) % RPI;
-            const int h = (q * RPI) >> 3, w = ((q * RPI) & 7) + rin;
-            const int row = qbase + min(h, extent_rows(tile_ext) - 1) * qrs + min(w, extent_cols(tile_ext) - 1);
+            int dt, dh, dw;
+            compact_token(min(cur_sub * kQueryBlock + q * RPI + rin, last), tile_ext, dt, dh, dw);
+            const int row = tile_qbase + (dt * g.H + dh) * g.W + dw;
             const int chunk = 4 * (lane / (4 * RPI)) + ((lane & 3) ^ sw(q * RPI + rin));
             dma16(src + size_t(row) * ROWB + chunk * 16, dst + q * 1024);
           }
@@ -731,7 +741,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(KernelArgs) {
         const int local = wave * 16 * KT + 16 * kg + (lane & 15);
         const int key = key_row0 + local;
         key_ok[kg] = !text_unit || key < g.n_vt + text_len;
-        kras[kg] = tiled_to_raster(key, g);
+        kras[kg] = PAD ? tiled_to_raster(key, g) : tiled_to_raster_full(key, g);
         int ksrc = kras[kg];
         if constexpr (PAD) {
           if (!text_unit) {  // compact order; a key past n_keys computes on the last one, never written

@@ -49,24 +49,6 @@ __host__ __device__ inline int win_t(uint32_t p) { return int(p & 1023u); }
 __host__ __device__ inline int win_h(uint32_t p) { return int((p >> 10) & 1023u); }
 __host__ __device__ inline int win_w(uint32_t p) { return int((p >> 20) & 1023u); }
 
-// Tile-major row r (within one [S_t] slab) -> raster row, or -1 for a padding
-// row of a partial tile (a video size that is not a multiple of the tile is
-// covered by the same tile grid, the last tile along an axis holding the
-// remainder). Text rows follow the video in both orders.
-__host__ __device__ inline int tiled_to_raster(int r, const Geom& g) {
-  if (r >= g.n_vt) return r - g.n_vt + g.n_video;
-  const int tile = r / kTileRows;
-  const int j = r - tile * kTileRows;
-  const int dt = j >> 6, dh = (j >> 3) & 7, dw = j & 7;
-  const int tw = tile % g.nw;
-  const int rest = tile / g.nw;
-  const int th = rest % g.nh;
-  const int tt = rest / g.nh;
-  const int t = tt * kTileT + dt, h = th * kTileH + dh, w = tw * kTileW + dw;
-  if (t >= g.T || h >= g.H || w >= g.W) return -1;
-  return (t * g.H + h) * g.W + w;
-}
-
 // Extent of tile (tt, th, tw) inside the video, packed in one int: the frames
 // (of 6) | rows (of 8) << 8 | columns (of 8) << 16 of the tile that exist.
 constexpr int kFullExtent = kTileT | (kTileH << 8) | (kTileW << 16);
@@ -91,6 +73,42 @@ __host__ __device__ inline void compact_token(int r, int e, int& dt, int& dh, in
   const int rem = r - dt * plane;
   dh = rem / cols;
   dw = rem - dh * cols;
+}
+
+// Tile-major row r (within one [S_t] slab) -> raster row, or -1 for a padding
+// row. Tile t owns rows 384t .. 384t + 383; a video size that is not a
+// multiple of the tile is covered by the same tile grid, the last tile along
+// an axis holding the remainder, and a partial tile's slot holds its existing
+// tokens first, in compact order (frame, row, column), then padding rows. For
+// a full tile the compact order is (frame, row, column) of 6 x 8 x 8. Text
+// rows follow the video in both orders.
+// The same for a video size that is a tile multiple (g.full): bit operations
+// only inside the tile.
+__host__ __device__ inline int tiled_to_raster_full(int r, const Geom& g) {
+  if (r >= g.n_vt) return r - g.n_vt + g.n_video;
+  const int tile = r / kTileRows;
+  const int j = r - tile * kTileRows;
+  const int tw = tile % g.nw;
+  const int rest = tile / g.nw;
+  const int th = rest % g.nh;
+  const int tt = rest / g.nh;
+  return ((tt * kTileT + (j >> 6)) * g.H + th * kTileH + ((j >> 3) & 7)) * g.W + tw * kTileW + (j & 7);
+}
+__host__ __device__ inline int tiled_to_raster(int r, const Geom& g) {
+  if (r >= g.n_vt) return r - g.n_vt + g.n_video;
+  const int tile = r / kTileRows;
+  const int j = r - tile * kTileRows;
+  const int tw = tile % g.nw;
+  const int rest = tile / g.nw;
+  const int th = rest % g.nh;
+  const int tt = rest / g.nh;
+  int dt = j >> 6, dh = (j >> 3) & 7, dw = j & 7;
+  if (!g.full) {
+    const int e = tile_extent(tt, th, tw, g);
+    if (j >= extent_tokens(e)) return -1;
+    compact_token(j, e, dt, dh, dw);
+  }
+  return ((tt * kTileT + dt) * g.H + th * kTileH + dh) * g.W + tw * kTileW + dw;
 }
 
 // Launchers (each enqueues one kernel on `stream` and returns hipGetLastError()).

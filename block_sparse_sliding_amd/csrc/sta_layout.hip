@@ -27,7 +27,7 @@ __global__ __launch_bounds__(kThreads) void rows_permute_kernel(Geom g, const ui
   for (int c = threadIdx.x; c < kKeyBlock * CPR; c += kThreads) {
     const int rt = r0 + c / CPR;
     const int col = c % CPR;
-    const int rr = tiled_to_raster(rt, g);
+    const int rr = tiled_to_raster_full(rt, g);  // gather/scatter: tile multiples only
     if (to_tiled)
       dst[slab + size_t(rt) * CPR + col] = src[slab + size_t(rr) * CPR + col];
     else
