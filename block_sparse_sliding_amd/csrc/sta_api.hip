@@ -271,7 +271,7 @@ sta_status forward_impl(const sta_dims* dims, const void* q, const void* k, cons
   a.work = work;
   a.claim = claim;
   a.q_scale = float(1.4426950408889634 / std::sqrt(double(g.D)));  // log2(e)/sqrt(D)
-  st = hip_status(sta::launch_attention(g, a, s));
+  st = hip_status(sta::launch_attention(g, win, a, s));
   if (st == STA_OK) st = mark(4);
   return st;
 }

@@ -92,6 +92,7 @@ constexpr float kLn2 = 0.69314718055994530942f;
 struct KernelArgs {
   Geom g;
   FwdArgs a;
+  Windows win;  // read by the PAD instantiation only
 };
 
 // The kernel arguments seen through an opaque copy of the kernarg pointer:
@@ -179,16 +180,19 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(KernelArgs) 
   const int l0 = a.offsets[hd * g.n_q + u];
   const int l1 = a.offsets[hd * g.n_q + u + 1];
   // video key blocks: six per listed tile; with PAD, ceil(tokens / 64) per
-  // tile, its existing tokens in compact order
+  // tile, its existing tokens in compact order, summed over the unit's list:
+  // the query tile's window (a box of tiles) or, for the text unit, the grid
   int n_vid = (l1 - l0) * BPT;
   if constexpr (PAD) {
-    n_vid = 0;
-    for (int t = l0; t < l1; ++t) {
-      const int tile = a.ids[t];
-      const int rest = div_by(tile, g.nw, g.mag_nw);
+    if (text_unit) {
+      n_vid = box_blocks(0, g.nt, 0, g.nh, 0, g.nw, g);
+    } else {
+      const uint32_t p = ka->win.w[hd];
+      const int rest = div_by(u, g.nw, g.mag_nw);
       const int tt = div_by(rest, g.nh, g.mag_nh);
-      n_vid += (extent_tokens(tile_extent(tt, rest - tt * g.nh, tile - rest * g.nw, g)) + kKeyBlock - 1) /
-               kKeyBlock;
+      const int th = rest - tt * g.nh, tw = u - rest * g.nw;
+      n_vid = box_blocks(window_start(tt, win_t(p), g.nt), win_t(p), window_start(th, win_h(p), g.nh),
+                         win_h(p), window_start(tw, win_w(p), g.nw), win_w(p), g);
     }
   }
   const int text_len = g.has_text ? g.text_length : 0;
@@ -513,20 +517,20 @@ int persistent_grid() {
 }
 
 template <int D, bool PAD>
-hipError_t launch(const Geom& g, const FwdArgs& a, hipStream_t stream) {
+hipError_t launch(const Geom& g, const Windows& win, const FwdArgs& a, hipStream_t stream) {
   const int units = g.B * g.heads * g.n_q;
   const int resident = persistent_grid<D, PAD>();
   if (resident <= 0) return hipErrorInvalidDevice;
   const int grid = units < resident ? units : resident;
-  sta_attention_kernel<D, PAD><<<grid, kThreads, 0, stream>>>(KernelArgs{g, a});
+  sta_attention_kernel<D, PAD><<<grid, kThreads, 0, stream>>>(KernelArgs{g, a, win});
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_attention(const Geom& g, const FwdArgs& a, hipStream_t stream) {
-  if (g.full) return g.D == 128 ? launch<128, false>(g, a, stream) : launch<64, false>(g, a, stream);
-  return g.D == 128 ? launch<128, true>(g, a, stream) : launch<64, true>(g, a, stream);
+hipError_t launch_attention(const Geom& g, const Windows& win, const FwdArgs& a, hipStream_t stream) {
+  if (g.full) return g.D == 128 ? launch<128, false>(g, win, a, stream) : launch<64, false>(g, win, a, stream);
+  return g.D == 128 ? launch<128, true>(g, win, a, stream) : launch<64, true>(g, win, a, stream);
 }
 
 }  // namespace sta

@@ -110,17 +110,12 @@ __device__ inline int xcd_id() {
   return int(xcc);
 }
 
-// Window start along one axis (as the forward's schedule) and the interval of
-// query coordinates whose window holds key coordinate kc.
-__device__ inline int win_start(int c, int w, int n) {
-  int s = c - w / 2;
-  s = s < 0 ? 0 : s;
-  return s > n - w ? n - w : s;
-}
+// The interval of query coordinates whose window (window_start) holds key
+// coordinate kc.
 __device__ inline void seeing_interval(int kc, int w, int n, int& lo, int& len) {
   int first = n, last = -1;
   for (int c = 0; c < n; ++c) {
-    const int s = win_start(c, w, n);
+    const int s = window_start(c, w, n);
     if (s <= kc && kc < s + w) {
       first = c < first ? c : first;
       last = c;
@@ -274,13 +269,15 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(KernelArgs) {
     // tile (as in the forward)
     int n_vid = (l1 - l0) * BPT;
     if constexpr (PAD) {
-      n_vid = 0;
-      for (int t = l0; t < l1; ++t) {
-        const int tile = a.ids[t];
-        const int rest = div_by(tile, g.nw, g.mag_nw);
+      if (unit < n_text_units) {
+        n_vid = box_blocks(0, g.nt, 0, g.nh, 0, g.nw, g);
+      } else {  // the list is the query tile's window, a box
+        const uint32_t p = ka->win.w[hd];
+        const int rest = div_by(u, g.nw, g.mag_nw);
         const int tt = div_by(rest, g.nh, g.mag_nh);
-        n_vid += (extent_tokens(tile_extent(tt, rest - tt * g.nh, tile - rest * g.nw, g)) + kKeyBlock - 1) /
-                 kKeyBlock;
+        const int th = rest - tt * g.nh, tw = u - rest * g.nw;
+        n_vid = box_blocks(window_start(tt, win_t(p), g.nt), win_t(p), window_start(th, win_h(p), g.nh),
+                           win_h(p), window_start(tw, win_w(p), g.nw), win_w(p), g);
       }
     }
     const int text_len = g.has_text ? g.text_length : 0;
@@ -609,14 +606,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(KernelArgs) {
     // video, for a text unit); with PAD, ceil(tokens / 64) per tile
     int n_vblk = text_unit ? g.n_tiles * BPT : box_t * box_h * box_w * BPT;
     if constexpr (PAD) {
-      const int t0 = text_unit ? 0 : lo_t, t1 = text_unit ? g.nt : lo_t + box_t;
-      const int h0 = text_unit ? 0 : lo_h, h1 = text_unit ? g.nh : lo_h + box_h;
-      const int w0 = text_unit ? 0 : lo_w, w1 = text_unit ? g.nw : lo_w + box_w;
-      n_vblk = 0;
-      for (int tt = t0; tt < t1; ++tt)
-        for (int th = h0; th < h1; ++th)
-          for (int tw = w0; tw < w1; ++tw)
-            n_vblk += (extent_tokens(tile_extent(tt, th, tw, g)) + kQueryBlock - 1) / kQueryBlock;
+      n_vblk = text_unit ? box_blocks(0, g.nt, 0, g.nh, 0, g.nw, g)
+                         : box_blocks(lo_t, box_t, lo_h, box_h, lo_w, box_w, g);
     }
     const int n_blk = valid_keys == 0 ? 0 : n_vblk + (g.has_text ? kTextSlots / kQueryBlock : 0);
 

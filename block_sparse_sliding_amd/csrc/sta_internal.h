@@ -45,6 +45,15 @@ struct Windows {
   uint32_t w[kMaxHeads];
 };
 
+// Start of a window of w tiles along an axis of n tiles for query tile c:
+// centred on c and shifted inward at the grid border, so it always holds w
+// tiles (the STA README "Usage" example gives every query of the (30,48,80)
+// video the same (18,24,24) token box).
+__host__ __device__ inline int window_start(int c, int w, int n) {
+  int s = c - w / 2;
+  s = s < 0 ? 0 : s;
+  return s > n - w ? n - w : s;
+}
 __host__ __device__ inline int win_t(uint32_t p) { return int(p & 1023u); }
 __host__ __device__ inline int win_h(uint32_t p) { return int((p >> 10) & 1023u); }
 __host__ __device__ inline int win_w(uint32_t p) { return int((p >> 20) & 1023u); }
@@ -73,6 +82,29 @@ __host__ __device__ inline void compact_token(int r, int e, int& dt, int& dh, in
   const int rem = r - dt * plane;
   dh = rem / cols;
   dw = rem - dh * cols;
+}
+
+// Blocks of 64 tokens over a box of tiles [lo, lo + len) per axis, each tile
+// counting ceil(tokens / 64). Along an axis every tile but the grid's last is
+// full, so the sum has at most eight distinct terms.
+__host__ __device__ inline int box_blocks(int lo_t, int len_t, int lo_h, int len_h, int lo_w, int len_w,
+                                          const Geom& g) {
+  int n_full[3], n_part[3], ext[3];
+  const int lo[3] = {lo_t, lo_h, lo_w}, len[3] = {len_t, len_h, len_w};
+  const int n[3] = {g.nt, g.nh, g.nw}, size[3] = {g.T, g.H, g.W}, tile[3] = {kTileT, kTileH, kTileW};
+  for (int a = 0; a < 3; ++a) {
+    ext[a] = size[a] - (n[a] - 1) * tile[a];  // extent of the grid's last tile
+    n_part[a] = (lo[a] + len[a] == n[a] && ext[a] < tile[a]) ? 1 : 0;
+    n_full[a] = len[a] - n_part[a];
+  }
+  int sum = 0;
+  for (int m = 0; m < 8; ++m) {
+    const int ct = (m & 1) ? n_part[0] : n_full[0], ch = (m & 2) ? n_part[1] : n_full[1];
+    const int cw = (m & 4) ? n_part[2] : n_full[2];
+    const int tok = ((m & 1) ? ext[0] : kTileT) * ((m & 2) ? ext[1] : kTileH) * ((m & 4) ? ext[2] : kTileW);
+    sum += ct * ch * cw * ((tok + kKeyBlock - 1) / kKeyBlock);
+  }
+  return sum;
 }
 
 // Tile-major row r (within one [S_t] slab) -> raster row, or -1 for a padding
@@ -147,7 +179,7 @@ struct FwdArgs {
   int32_t* claim;        // queue heads, zeroed by launch_schedule_work
   float q_scale;         // log2(e) / sqrt(D), applied to the fp32 scores
 };
-hipError_t launch_attention(const Geom& g, const FwdArgs& a, hipStream_t stream);
+hipError_t launch_attention(const Geom& g, const Windows& win, const FwdArgs& a, hipStream_t stream);
 
 // Backward (gradients of the forward for an upstream gradient dout).
 struct BwdArgs {

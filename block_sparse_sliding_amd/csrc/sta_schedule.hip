@@ -15,12 +15,6 @@
 namespace sta {
 namespace {
 
-__device__ inline int clamp_start(int c, int w, int n) {
-  int s = c - w / 2;
-  s = s < 0 ? 0 : s;
-  return s > n - w ? n - w : s;
-}
-
 // Offset inside a window [s, s + w) of the coordinate congruent to r mod w
 // (r in [0, w)). Listing a window's tiles by the residues of their absolute
 // coordinates, rather than by their offsets from the window start, makes
@@ -53,8 +47,8 @@ __global__ __launch_bounds__(256) void schedule_lists_kernel(Geom g, Windows win
     const int64_t off = base + int64_t(u) * wv;
     if (threadIdx.x == 0) offsets[hd * g.n_q + u] = int32_t(off);
     const int tw = u % g.nw, th = (u / g.nw) % g.nh, tt = u / (g.nw * g.nh);
-    const int st = clamp_start(tt, wt, g.nt), sh = clamp_start(th, wh, g.nh),
-              sw = clamp_start(tw, ww, g.nw);
+    const int st = window_start(tt, wt, g.nt), sh = window_start(th, wh, g.nh),
+              sw = window_start(tw, ww, g.nw);
     for (int j = threadIdx.x; j < wv; j += blockDim.x) {
       const int a = j / (wh * ww), b = (j / ww) % wh, c = j % ww;
       ids[off + j] = ((st + residue_offset(a, st, wt)) * g.nh + (sh + residue_offset(b, sh, wh))) *
