@@ -213,8 +213,8 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(KernelArgs) 
   // (video) or first slot (text), krs = raster stride between its 8-row
   // runs, vrow = its first tile-major row (the packed V^T block). With PAD,
   // tile_ext is the packed extent of the current tile (the frames, rows and
-  // columns that exist) and kbase names the last existing frame in place of
-  // one that does not exist.
+  // columns that exist); a tile with only frames missing still has one frame
+  // per block, otherwise a block is 64 tokens in compact order (issue_k).
   int tile_kbase = 0, tile_vrow = 0;
   int tile_ext = kFullExtent;  // PAD: packed extent of the current tile
   // PAD: blocks walk the blocks of each listed tile in turn (block j + 1 is

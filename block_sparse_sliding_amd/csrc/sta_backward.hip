@@ -36,13 +36,16 @@
 // no query and get zero gradients.
 //
 // Video sizes that are not tile multiples (the PAD instantiations): the last
-// tile along an axis holds the remainder, and its rows that do not exist are
-// padding. Raw rows of a partial tile are fetched from clamped rows that exist
-// (every address stays inside the video); packed rows of padding are zeros.
-// prep gives padding query rows lse2 = +inf and delta = 0, so their P and dS
-// are exactly 0 wherever they are streamed; padding key rows add nothing to dq
-// (their packed K^T rows are zero and their dS finite, the clamped copy of a
-// key of the same tile) and padding rows of dq, dk, dv are not written.
+// tile along an axis holds the remainder, and a partial tile's tile-major
+// slot holds its existing tokens first, in compact order (frame, row,
+// column), then padding. Stationary rows and keys are those tokens; streamed
+// tiles contribute ceil(tokens / 64) blocks whose raw rows are fetched per
+// lane through the compact map, clamped to the last token (every address
+// stays inside the video). Packed padding rows are zeros and prep gives
+// padding query rows lse2 = +inf and -delta = 0, so their P and dS are
+// exactly 0 wherever they are streamed; padding key rows add nothing to dq
+// (their packed K^T rows are zero and their dS finite, computed on a copy of
+// a key of the same tile), and padding rows of dq, dk, dv are not written.
 #include <type_traits>
 
 #include "sta_device.h"
@@ -164,8 +167,9 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(Geom g, const __bf16* __r
 
 // ---------------------------------------------------------------- dq
 // Query units per (b, head): two per video tile (rows 0..255 with 8 waves x
-// 32 rows, rows 256..383 with 8 waves x 16 rows), plus the 256 text query
-// slots (8 waves x 32 rows). Unit order: text units first, then the tiles.
+// 32 rows, rows 256..383 with 8 waves x 16 rows; with PAD, a unit of at most
+// 128 existing rows also runs 8 x 16), plus the 256 text query slots (8 waves
+// x 32 rows). Unit order: text units first, then the tiles.
 __device__ inline int dq_units_per_head(const Geom& g) { return 2 * g.n_tiles + (g.has_text ? 1 : 0); }
 
 template <int D, bool PAD>
@@ -288,8 +292,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(KernelArgs) {
         (const __attribute__((address_space(4))) int32_t*)(a.ids + l0);
 
     // with PAD, tile_ext: packed extent of the current key tile (the frames,
-    // rows and columns that exist); kbase then names the last existing frame
-    // in place of one that does not exist
+    // rows and columns that exist); its blocks are 64 compact tokens each
     int tile_kbase = 0, tile_vrow = 0;
     int tile_ext = kFullExtent;  // PAD: packed extent of the current tile
     int cur_t = 0, cur_sub = -1;  // PAD: the forward's walk over existing frames
@@ -521,7 +524,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(KernelArgs) {
 
 // ---------------------------------------------------------------- dk, dv
 // Key units per (b, head): per video tile keys 0..255 (8 waves x 32 keys) and
-// keys 256..383 (8 waves x 16 keys), plus the 256 text slots (8 waves x 32).
+// keys 256..383 (8 waves x 16 keys; with PAD, a unit of at most 128 existing
+// keys also runs 8 x 16), plus the 256 text slots (8 waves x 32).
 // Unit order: the text units first (each streams every query row), then
 // (bh, tile, part).
 __device__ inline int kv_units_per_head(const Geom& g) { return 2 * g.n_tiles + (g.has_text ? 1 : 0); }
