@@ -25,7 +25,8 @@ STATUS = {
     5: "STA_ERR_ALIGN", 6: "STA_ERR_WORKSPACE", 7: "STA_ERR_HIP", 8: "STA_ERR_ALIAS",
 }
 EXPORTS = (
-    "sta_status_str", "sta_seq_len", "sta_workspace_bytes", "sta_forward", "sta_forward_timed",
+    "sta_status_str", "sta_seq_len", "sta_tiled_seq_len", "sta_workspace_bytes", "sta_forward",
+    "sta_forward_timed",
     "sta_tile_gather",
     "sta_tile_scatter", "sta_schedule_sizes", "sta_build_schedule",
     "sta_backward_workspace_bytes", "sta_backward", "sta_backward_timed",
@@ -65,6 +66,8 @@ def load_library() -> ctypes.CDLL:
     lib.sta_status_str.restype = ctypes.c_char_p
     lib.sta_seq_len.argtypes = [PD, I32]
     lib.sta_seq_len.restype = ctypes.c_int64
+    lib.sta_tiled_seq_len.argtypes = [PD, I32]
+    lib.sta_tiled_seq_len.restype = ctypes.c_int64
     lib.sta_workspace_bytes.argtypes = [PD, PI32, I32]
     lib.sta_workspace_bytes.restype = ctypes.c_size_t
     lib.sta_forward.argtypes = [PD, P, P, P, PI32, I32, I32, P, P, P, ctypes.c_size_t, P]
@@ -133,6 +136,10 @@ def _check(code: int, where: str):
 # ----------------------------------------------------------------- C-ABI calls
 def sta_seq_len(dims: sta_dims, has_text: bool) -> int:
     return int(load_library().sta_seq_len(ctypes.byref(dims), int(has_text)))
+
+
+def sta_tiled_seq_len(dims: sta_dims, has_text: bool) -> int:
+    return int(load_library().sta_tiled_seq_len(ctypes.byref(dims), int(has_text)))
 
 
 def sta_workspace_bytes(dims: sta_dims, window_sizes, has_text: bool) -> int:

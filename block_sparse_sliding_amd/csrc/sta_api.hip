@@ -136,6 +136,12 @@ int64_t sta_seq_len(const sta_dims* dims, int32_t has_text) {
   return g.S;
 }
 
+int64_t sta_tiled_seq_len(const sta_dims* dims, int32_t has_text) {
+  Geom g;
+  if (make_geom(dims, has_text, 0, &g) != STA_OK) return 0;
+  return g.S_t;
+}
+
 size_t sta_workspace_bytes(const sta_dims* dims, const int32_t* window_sizes, int32_t has_text) {
   Geom g;
   if (make_geom(dims, has_text, 0, &g) != STA_OK) return 0;
@@ -183,11 +189,11 @@ sta_status sta_tile_gather(const sta_dims* dims, int32_t has_text, const void* x
   Geom g;
   sta_status st = make_geom(dims, has_text, 0, &g);
   if (st != STA_OK) return st;
-  if (!g.full) return STA_ERR_SHAPE;  // both orders have the same rows only for tile multiples
   if (x_raster == nullptr || x_tiled == nullptr) return STA_ERR_NULL;
   if (!aligned16(x_raster) || !aligned16(x_tiled)) return STA_ERR_ALIGN;
-  const size_t bytes = size_t(g.B) * g.heads * g.S * g.D * 2;
-  if (overlaps(x_raster, bytes, x_tiled, bytes)) return STA_ERR_ALIAS;
+  const size_t raster_bytes = size_t(g.B) * g.heads * g.S * g.D * 2;
+  const size_t tiled_bytes = size_t(g.B) * g.heads * g.S_t * g.D * 2;
+  if (overlaps(x_raster, raster_bytes, x_tiled, tiled_bytes)) return STA_ERR_ALIAS;
   return hip_status(sta::launch_rows_permute(g, x_raster, x_tiled, true,
                                              reinterpret_cast<hipStream_t>(stream)));
 }
@@ -197,11 +203,11 @@ sta_status sta_tile_scatter(const sta_dims* dims, int32_t has_text, const void* 
   Geom g;
   sta_status st = make_geom(dims, has_text, 0, &g);
   if (st != STA_OK) return st;
-  if (!g.full) return STA_ERR_SHAPE;
   if (x_raster == nullptr || x_tiled == nullptr) return STA_ERR_NULL;
   if (!aligned16(x_raster) || !aligned16(x_tiled)) return STA_ERR_ALIGN;
-  const size_t bytes = size_t(g.B) * g.heads * g.S * g.D * 2;
-  if (overlaps(x_raster, bytes, x_tiled, bytes)) return STA_ERR_ALIAS;
+  const size_t raster_bytes = size_t(g.B) * g.heads * g.S * g.D * 2;
+  const size_t tiled_bytes = size_t(g.B) * g.heads * g.S_t * g.D * 2;
+  if (overlaps(x_raster, raster_bytes, x_tiled, tiled_bytes)) return STA_ERR_ALIAS;
   return hip_status(sta::launch_rows_permute(g, x_tiled, x_raster, false,
                                              reinterpret_cast<hipStream_t>(stream)));
 }

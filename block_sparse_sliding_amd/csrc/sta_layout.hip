@@ -13,25 +13,27 @@ namespace {
 
 constexpr int kThreads = 256;
 
-// One workgroup per 64-row block of the tile-major sequence, one grid row per
-// (batch, head) slab. Copies whole rows in 16-byte chunks; both sides coalesce
-// (a 64-row tile-major block is the 8x8 (h, w) patch of one frame: 8 raster
-// runs of 8 rows).
+// One workgroup per 64-row block of the tile-major sequence (S_t rows), one
+// grid row per (batch, head) slab. Copies whole rows in 16-byte chunks; both
+// sides coalesce (a 64-row tile-major block of a full tile is the 8x8 (h, w)
+// patch of one frame: 8 raster runs of 8 rows). Padding rows of partial tiles
+// are written as zeros by the gather and not read by the scatter.
 template <int D>
 __global__ __launch_bounds__(kThreads) void rows_permute_kernel(Geom g, const uint4* __restrict__ src,
                                                                 uint4* __restrict__ dst, int to_tiled) {
   constexpr int CPR = D / 8;  // 16-byte chunks per row
-  const size_t slab = size_t(blockIdx.y) * g.S * CPR;
+  const size_t slab_r = size_t(blockIdx.y) * g.S * CPR;    // raster rows
+  const size_t slab_t = size_t(blockIdx.y) * g.S_t * CPR;  // tile-major rows
   const int r0 = blockIdx.x * kKeyBlock;
 #pragma unroll
   for (int c = threadIdx.x; c < kKeyBlock * CPR; c += kThreads) {
     const int rt = r0 + c / CPR;
     const int col = c % CPR;
-    const int rr = tiled_to_raster_full(rt, g);  // gather/scatter: tile multiples only
+    const int rr = tiled_to_raster(rt, g);  // -1: padding
     if (to_tiled)
-      dst[slab + size_t(rt) * CPR + col] = src[slab + size_t(rr) * CPR + col];
-    else
-      dst[slab + size_t(rr) * CPR + col] = src[slab + size_t(rt) * CPR + col];
+      dst[slab_t + size_t(rt) * CPR + col] = rr >= 0 ? src[slab_r + size_t(rr) * CPR + col] : make_uint4(0, 0, 0, 0);
+    else if (rr >= 0)
+      dst[slab_r + size_t(rr) * CPR + col] = src[slab_t + size_t(rt) * CPR + col];
   }
 }
 
@@ -89,7 +91,7 @@ __global__ __launch_bounds__(kThreads) void pack_v_kernel(Geom g, const uint4* _
 
 hipError_t launch_rows_permute(const Geom& g, const void* src, void* dst, bool to_tiled,
                                hipStream_t stream) {
-  dim3 grid(g.S / kKeyBlock, g.B * g.heads);
+  dim3 grid(g.S_t / kKeyBlock, g.B * g.heads);
   if (g.D == 128)
     rows_permute_kernel<128><<<grid, kThreads, 0, stream>>>(g, (const uint4*)src, (uint4*)dst, to_tiled);
   else

@@ -52,8 +52,7 @@ extern "C" {
 typedef enum {
   STA_OK = 0,
   STA_ERR_NULL = 1,      /* a required pointer is NULL, or batch/heads <= 0      */
-  STA_ERR_SHAPE = 2,     /* T,H,W not positive (for sta_tile_gather/scatter:
-                            not multiples of (6,8,8)); head_dim not 64 or 128;
+  STA_ERR_SHAPE = 2,     /* T,H,W not positive; head_dim not 64 or 128;
                             heads > STA_MAX_HEADS; a tile-grid axis > 1023
                             tiles; or sizes too large to index                 */
   STA_ERR_WINDOW = 3,    /* a window component outside [1, n_axis]              */
@@ -79,6 +78,13 @@ const char* sta_status_str(sta_status s);
 
 /* Sequence length S for these dims (0 if dims are invalid). */
 int64_t sta_seq_len(const sta_dims* dims, int32_t has_text);
+
+/*
+ * Rows per (batch, head) of the tile-major order (0 if dims are invalid):
+ * n_t*n_h*n_w*384 (+256 with text). Equal to S for video sizes that are tile
+ * multiples; otherwise it includes the padding rows of partial tiles.
+ */
+int64_t sta_tiled_seq_len(const sta_dims* dims, int32_t has_text);
 
 /*
  * Bytes of device workspace sta_forward needs for these arguments, or 0 if
@@ -143,17 +149,22 @@ sta_status sta_forward_timed(const sta_dims* dims, const void* q, const void* k,
                              void* stream, void* const* events);
 
 /*
- * Tile-major gather of one bf16 tensor [B][heads][S][D]: every video row
- * (t, h, w) moves to row  tile*384 + ((t%6)*8 + h%8)*8 + w%8  with
- * tile = ((t/6)*n_h + h/8)*n_w + w/8, so each tile is 384 contiguous rows;
- * text rows keep their positions. x_raster and x_tiled are device buffers
- * of the same size and must not overlap. Only for T, H, W multiples of
- * (6, 8, 8) (otherwise STA_ERR_SHAPE): then both orders hold the same rows.
+ * Tile-major gather of one bf16 tensor: x_raster [B][heads][S][D] into
+ * x_tiled [B][heads][S_t][D] with S_t = sta_tiled_seq_len(dims, has_text).
+ * Tile tile = ((t/6)*n_h + h/8)*n_w + w/8 owns the 384 contiguous rows
+ * tile*384 ..; its video rows (t, h, w) come first in (frame, row, column)
+ * order, i.e. row tile*384 + ((t%6)*ch + h%8)*cw + w%8 where ch and cw are
+ * the rows and columns of the tile that exist (8 and 8 except in the last
+ * tile along h or w of a size that is not a tile multiple), and the slot's
+ * remaining rows (a partial tile's padding) are written as zeros. The text
+ * rows follow the video (row n_t*n_h*n_w*384 + slot). For tile multiples
+ * S_t = S and this is a plain row permutation. The two buffers must not
+ * overlap.
  */
 sta_status sta_tile_gather(const sta_dims* dims, int32_t has_text,
                            const void* x_raster, void* x_tiled, void* stream);
 
-/* Inverse of sta_tile_gather. */
+/* Inverse of sta_tile_gather (padding rows of x_tiled are not read). */
 sta_status sta_tile_scatter(const sta_dims* dims, int32_t has_text,
                             const void* x_tiled, void* x_raster, void* stream);
 

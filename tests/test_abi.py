@@ -100,11 +100,15 @@ def test_layout_calls_reject_bad_arguments(lib):
     assert lib.sta_tile_gather(ctypes.byref(d), 0, None, 16, None) == 1
     assert lib.sta_tile_gather(ctypes.byref(d), 0, 16, 24, None) == 5
     assert lib.sta_tile_gather(ctypes.byref(d), 0, 16, 32, None) == 8
-    # only tile multiples (both orders then hold the same rows)
-    assert lib.sta_tile_scatter(ctypes.byref(sta.make_dims(1, 1, 64, (18, 24, 20))), 0, 16,
-                                1 << 30, None) == 2
-    assert lib.sta_tile_gather(ctypes.byref(sta.make_dims(1, 1, 64, (17, 24, 24))), 0, 16,
+    assert lib.sta_tile_gather(ctypes.byref(sta.make_dims(1, 1, 64, (0, 24, 24))), 0, 16,
                                1 << 30, None) == 2
+    # sizes that are not tile multiples pass the shape checks: the tiled buffer
+    # has sta_tiled_seq_len rows (S_t = 2*3*4*384 here, > S), so a raster buffer
+    # starting inside it overlaps (the call stops there, before any launch)
+    pd = sta.make_dims(1, 1, 64, (7, 24, 30))
+    assert sta.sta_tiled_seq_len(pd, False) == 2 * 3 * 4 * 384
+    assert lib.sta_tile_scatter(ctypes.byref(pd), 0, 1 << 30, (1 << 30) + 7 * 24 * 30 * 128, None) == 8
+    assert lib.sta_tile_gather(ctypes.byref(pd), 0, (1 << 30) + 9216 * 128 - 16, 1 << 30, None) == 8
 
 
 def seq(video, text):
@@ -124,6 +128,7 @@ def test_sizes(lib, B, heads, D, video, windows, text):
     S = seq(video, text)
     assert sta.sta_seq_len(d, text) == S
     n_tiles = -(-video[0] // 6) * -(-video[1] // 8) * -(-video[2] // 8)  # ceil tile grid
+    assert sta.sta_tiled_seq_len(d, text) == n_tiles * 384 + (256 if text else 0)
     n_q = n_tiles + (1 if text else 0)
     n_off, n_ids, n_work = sta.sta_schedule_sizes(d, windows, text)
     assert n_off == heads * n_q + 1

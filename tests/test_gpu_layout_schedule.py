@@ -19,17 +19,23 @@ pytestmark = pytest.mark.gpu
 
 
 def tile_major_index(video, has_text):
-    """Raster row of every tile-major row (text rows map to themselves)."""
+    """Raster row of every tile-major row, -1 for padding (text rows follow the video).
+
+    Tile (tt, th, tw) owns 384 rows: the tokens of its (6, 8, 8) box that exist,
+    in (frame, row, column) order, then padding (only for sizes that are not
+    tile multiples, where the last tile along an axis holds the remainder).
+    """
     T, H, W = video
-    n = (T // 6, H // 8, W // 8)
+    n = (-(-T // 6), -(-H // 8), -(-W // 8))
     idx = []
     for tt in range(n[0]):
         for th in range(n[1]):
             for tw in range(n[2]):
-                t = tt * 6 + np.arange(6)[:, None, None]
-                h = th * 8 + np.arange(8)[None, :, None]
-                w = tw * 8 + np.arange(8)[None, None, :]
-                idx.append(((t * H + h) * W + w).reshape(-1))
+                t = np.arange(tt * 6, min(T, tt * 6 + 6))[:, None, None]
+                h = np.arange(th * 8, min(H, th * 8 + 8))[None, :, None]
+                w = np.arange(tw * 8, min(W, tw * 8 + 8))[None, None, :]
+                rows = ((t * H + h) * W + w).reshape(-1)
+                idx.append(np.concatenate([rows, -np.ones(384 - rows.size, dtype=rows.dtype)]))
     idx = np.concatenate(idx)
     if has_text:
         idx = np.concatenate([idx, T * H * W + np.arange(256)])
@@ -41,20 +47,27 @@ def tile_major_index(video, has_text):
     (2, 3, 128, (18, 24, 32), True),
     (1, 2, 128, (30, 48, 80), True),
     (1, 1, 64, (6, 8, 8), True),
+    (2, 2, 128, (7, 9, 11), True),
+    (1, 1, 64, (13, 8, 21), False),
+    (1, 2, 128, (33, 45, 80), True),
 ])
 def test_gather_scatter(B, heads, D, video, has_text):
     note(f"gather/scatter {B} {heads} {D} {video} {has_text}")
     dims = sta.make_dims(B, heads, D, video)
     S = sta.sta_seq_len(dims, has_text)
+    S_t = sta.sta_tiled_seq_len(dims, has_text)
     g = torch.Generator(device="cuda").manual_seed(S)
     x = torch.randn(B, heads, S, D, generator=g, device="cuda").to(torch.bfloat16)
-    tiled = torch.empty_like(x)
+    tiled = torch.full((B, heads, S_t, D), float("nan"), dtype=torch.bfloat16, device="cuda")
     back = torch.full_like(x, float("nan"))
     sta.sta_tile_gather(dims, has_text, x, tiled)
     sta.sta_tile_scatter(dims, has_text, tiled, back)
     torch.cuda.synchronize()
     idx = tile_major_index(video, has_text).cuda()
-    assert torch.equal(tiled.view(torch.int16), x[:, :, idx].view(torch.int16))
+    assert idx.numel() == S_t
+    real = idx >= 0
+    assert torch.equal(tiled[:, :, real].view(torch.int16), x[:, :, idx[real]].view(torch.int16))
+    assert bool((tiled[:, :, ~real] == 0).all())
     assert torch.equal(back.view(torch.int16), x.view(torch.int16))
 
 
@@ -76,6 +89,9 @@ SCHED = [
     (1, 24, (30, 48, 80), [(3, 3, 3)] * 24, 226, True),
     (1, 24, (48, 72, 128), [(3, 3, 3)] * 24, 128, True),
     (3, 5, (12, 16, 24), [(1, 1, 1), (2, 2, 3), (2, 1, 2), (1, 2, 1), (2, 2, 1)], 5, True),
+    # sizes that are not tile multiples: the same schedule on the ceil tile grid
+    (1, 2, (7, 9, 11), [(2, 2, 2), (1, 1, 2)], 77, True),
+    (1, 3, (33, 45, 80), [(3, 3, 3), (2, 4, 5), (6, 6, 10)], 226, True),
 ]
 
 
@@ -84,7 +100,8 @@ def test_schedule_matches_mask(case):
     B, heads, video, windows, ell, has_text = case
     note(f"schedule {case[:3]}")
     off, ids, work = build_schedule(B, heads, video, windows, ell, has_text)
-    n_tiles = (video[0] // 6) * (video[1] // 8) * (video[2] // 8)
+    nt, nh, nw = -(-video[0] // 6), -(-video[1] // 8), -(-video[2] // 8)  # ceil tile grid
+    n_tiles = nt * nh * nw
     n_q = n_tiles + (1 if has_text else 0)
     assert off[0] == 0 and off[-1] == len(ids)
     assert (np.diff(off) >= 0).all()
@@ -100,7 +117,6 @@ def test_schedule_matches_mask(case):
             tiles = range(n_tiles) if n_tiles <= 40 else sorted(
                 set(rng.integers(0, n_tiles, 6).tolist()) | {0, n_tiles - 1})
             w = windows[hd]
-            nt, nh, nw = video[0] // 6, video[1] // 8, video[2] // 8
             digits = [(a, b, c) for a in range(w[0]) for b in range(w[1]) for c in range(w[2])]
             for qt in tiles:
                 # the window's tiles, each once ...
