@@ -7,6 +7,7 @@
 * padded text K/V rows never reach the result (bitwise).
 * repeated calls are bitwise identical; batch entries are independent.
 * lse is optional: without it, out is the same to the bit.
+* the maximum head count (256), with per-head windows, forward and backward.
 """
 
 import math
@@ -187,3 +188,36 @@ def test_lse_is_optional(video):
     sta.sta_forward(dims, q, k, v, windows, 99, True, out2, None, ws)
     torch.cuda.synchronize()
     assert torch.equal(out1.view(torch.int16), out2.view(torch.int16))
+
+
+def test_max_heads():
+    """256 heads (the maximum) with per-head windows on a small partial grid:
+    every head's window is read from the kernel arguments; heads are checked
+    against the oracle on a sample, forward and backward."""
+    import oracle
+    from _parity import compare
+    from test_gpu_backward import compare_grad, run_backward
+
+    video, D, ell = (7, 16, 17), 64, 10  # tile grid (2, 2, 3)
+    heads = 256
+    cycle = [(1, 1, 1), (2, 2, 3), (1, 2, 2), (2, 1, 1), (1, 1, 3)]
+    windows = [cycle[h % len(cycle)] for h in range(heads)]
+    S = video[0] * video[1] * video[2] + 256
+    note(f"max heads {heads} {video}")
+    g = torch.Generator(device="cuda").manual_seed(256)
+    q, k, v, dout = [torch.randn(1, heads, S, D, generator=g, device="cuda").to(torch.bfloat16)
+                     for _ in range(4)]
+    out, lse = run_sta(q, k, v, windows, ell, True, video)
+    dq, dk, dv = run_backward(q, k, v, out, lse, dout, windows, ell, True, video)
+    for t in (out, lse, dq, dk, dv):
+        assert bool(torch.isfinite(t).all())
+    for h in (0, 1, 2, 3, 4, 127, 255):
+        sl = slice(h, h + 1)
+        ro, rl = oracle.sta_reference(q[:, sl].cpu(), k[:, sl].cpu(), v[:, sl].cpu(), [windows[h]],
+                                      ell, True, video)
+        compare(out[:, sl], lse[:, sl], ro, rl, label=f"max heads, head {h}")
+        rq, rk, rv = oracle.sta_reference_backward(q[:, sl].cpu(), k[:, sl].cpu(), v[:, sl].cpu(),
+                                                   dout[:, sl].cpu(), [windows[h]], ell, True, video)
+        compare_grad(dq[:, sl], rq, f"dq head {h}")
+        compare_grad(dk[:, sl], rk, f"dk head {h}")
+        compare_grad(dv[:, sl], rv, f"dv head {h}")
