@@ -311,6 +311,9 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(KernelArgs) 
   auto run = [&](auto qt_c) {
     constexpr int QT = decltype(qt_c)::value;
     constexpr int RPW = QT * 16;  // query rows per wave
+    // a wave whose rows all lie past a partial tile's tokens only loads and
+    // synchronises (its SIMD then runs one wave of the unit instead of two)
+    const bool active = !PAD || wave * RPW < q_rows;
     // Q^T fragments for this wave's RPW rows, read from the caller's raster q
     // (row r of the unit: see query_raster; rows past the unit are clamped to
     // a valid row and their results discarded).
@@ -354,6 +357,16 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(KernelArgs) 
     };
 
     issue(0, 0);
+    if (!active) {
+      // the same loads and barriers as the loop below; once every wave has
+      // passed barrier j, no wave reads the other stage any more
+      for (int j = 0; j < n_blk; ++j) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (j + 1 < n_blk) issue(j + 1, (j & 1) ^ 1);
+      }
+      return;
+    }
     for (int j = 0; j < n_blk; ++j) {
       const int stage = j & 1;
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -497,12 +510,14 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(KernelArgs) 
     }
   };
   if constexpr (PAD) {
-    if (q_rows <= 16 * kWaves) {  // a small partial tile: 8 waves x 16 rows
+    if (q_rows <= 16 * kWaves) {  // a small partial tile: 8 (or 4) waves x 16 rows
       run(std::integral_constant<int, 1>{});
       continue;
     }
   }
-  if (text_unit || (PAD && q_rows <= kTextSlots))
+  // 8 waves x 32 rows for the text slots and for partial tiles of 193 to 256
+  // tokens; otherwise 48 rows per wave (4 waves do the work for at most 192)
+  if (text_unit || (PAD && q_rows > 4 * 16 * kQT && q_rows <= kTextSlots))
     run(std::integral_constant<int, kTextSlots / 16 / kWaves>{});
   else
     run(std::integral_constant<int, kQT>{});
