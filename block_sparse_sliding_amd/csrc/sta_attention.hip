@@ -67,8 +67,9 @@
 // source address stays inside the video), their scores are replaced by -inf
 // and their packed V rows are zeros. A
 // video unit's rows are its tile's existing tokens in compact order (frame,
-// row, column; a partial tile of at most 256 or 128 runs with 8 waves x 32 or
-// 16 rows);
+// row, column; a partial tile of at most 128, 192 or 256 tokens runs with
+// 8 waves x 16 rows, 4 waves x 48 or 8 waves x 32; a wave whose rows all lie
+// past the tokens only loads and synchronises);
 // rows past them compute on a valid row and are not written. The first block
 // of every window is frame 0 of an existing tile, so the running max is
 // finite from the first block on.
@@ -145,8 +146,8 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(KernelArgs) 
   const int q_row0 = text_unit ? g.n_vt : u * kTileRows;  // tile-major
   int q_rows = text_unit ? kTextSlots : kTileRows;
   // PAD: the rows of a video unit are the existing tokens of its tile in
-  // compact order (frame, row, column), so a partial tile of at most 256
-  // tokens runs as a 256-row unit
+  // compact order (frame, row, column), so a partial tile runs as a unit of
+  // 128, 192, 256 or 384 rows (the shapes are chosen below)
   int q_ext = kFullExtent, q_base = 0;  // extent and raster origin of the query tile
   if constexpr (PAD) {
     if (!text_unit) {
@@ -306,8 +307,9 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(KernelArgs) 
   };
 
   // The rest runs with QT query column groups per wave: 3 (8 x 48 = 384 rows)
-  // for a video tile, 2 (8 x 32 = 256 rows) for the text query slots, so no
-  // wave works on rows past the unit.
+  // for a video tile, 2 (8 x 32 = 256 rows) for the text query slots; a
+  // partial tile also uses 1 (16 rows per wave) or 3 with only waves 0-3
+  // holding rows.
   auto run = [&](auto qt_c) {
     constexpr int QT = decltype(qt_c)::value;
     constexpr int RPW = QT * 16;  // query rows per wave
