@@ -436,6 +436,17 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(KernelArgs) {
       };
 
       if (!PAD || n_blk > 0) issue(0, 0);
+      // a wave whose rows all lie past a partial tile's tokens only loads
+      if (PAD && wave * RPW >= n_valid) {
+        // the same loads and barriers as the loop below; once every wave has
+        // passed barrier j, no wave reads the other stage any more
+        for (int j = 0; j < n_blk; ++j) {
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+          __syncthreads();
+          if (j + 1 < n_blk) issue(j + 1, (j & 1) ^ 1);
+        }
+        return;
+      }
       for (int j = 0; j < n_blk; ++j) {
         const int stage = j & 1;
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -788,6 +799,17 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(KernelArgs) {
       };
 
       if (n_blk > 0) issue(0, 0);
+      // a wave whose keys all lie past a partial tile's tokens only loads
+      if (PAD && !text_unit && wave * 16 * KT >= n_keys) {
+        // the same loads and barriers as the loop below; once every wave has
+        // passed barrier j, no wave reads the other stage any more
+        for (int j = 0; j < n_blk; ++j) {
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+          __syncthreads();
+          if (j + 1 < n_blk) issue(j + 1, (j & 1) ^ 1);
+        }
+        return;
+      }
       for (int j = 0; j < n_blk; ++j) {
         const int stage = j & 1;
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
