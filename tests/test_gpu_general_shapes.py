@@ -11,8 +11,10 @@ the kernels skip fails the checks.
 
 The shapes cover partial tiles along each axis alone and together, a last
 frame tile holding 1 frame (the second key unit of such a tile has no keys)
-or 5 frames, a video of one frame, a single partial tile, both head sizes,
-with and without text, and large score jumps between key tiles.
+or 5 frames, a video of one frame, a single partial tile, every unit shape
+of the partial-tile kernels (16 rows per wave on 4 or 8 waves, 4 waves x 48
+rows for 129 to 192 tokens, 8 x 32, 8 x 48), both head sizes, with and without
+text, and large score jumps between key tiles.
 """
 
 import numpy as np
@@ -34,6 +36,8 @@ CASES = [
     (1, 128, (11, 17, 9), [(2, 3, 2), (1, 1, 1)], 200, True),
     (1, 128, (12, 15, 16), [(2, 2, 2)], 63, True),
     (1, 64, (18, 24, 21), [(3, 3, 2), (1, 2, 3)], 0, False),
+    # partial tiles of 150 and 180 tokens (4 waves x 48 rows), 240 and 320
+    (1, 128, (17, 21, 30), [(2, 2, 2)], 100, True),
 ]
 IDS = [f"g{i}" for i in range(len(CASES))]
 
