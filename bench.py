@@ -106,6 +106,25 @@ def measured_traffic(summary: str, kernel: str, source: str):
         return None
 
 
+def host_cpu() -> dict:
+    """The host the CPU baseline ran on: CPU model, logical CPUs online and the
+    CPUs this process may run on."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.partition(":")[2].strip()
+                    break
+    except OSError:  # pragma: no cover - /proc is always present on Linux
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        usable = os.cpu_count() or 1
+    return {"cpu_model": model, "nproc": usable, "logical_cpus": os.cpu_count() or 1}
+
+
 def cpu_baseline(wl, q, k, v, budget_s: float, flops: float):
     """Time the fp64 oracle on a bounded row sample and scale to one full call."""
     import numpy as np
@@ -140,6 +159,7 @@ def cpu_baseline(wl, q, k, v, budget_s: float, flops: float):
         "unit": "TFLOP/s",
         "cores": int(threads),
         "kind": "oracle",
+        "host": host_cpu(),
         "sample": (f"{done_rows} query rows ({len(rows)} stratified rows x {heads_done} heads), "
                    f"each dense over all {wl.seq_len} keys, {elapsed:.1f} s; extrapolated to "
                    f"B*heads*S = {wl.batch * wl.heads * wl.seq_len} rows"),

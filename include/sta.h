@@ -26,9 +26,12 @@
  * - Tensors q, k, v, out are bf16, row-major [batch][heads][S][head_dim].
  *   lse is fp32 [batch][heads][S].
  * - Device pointers are HIP device (or managed) memory, 16-byte aligned.
- *   The caller owns every buffer; the library allocates nothing, keeps no
- *   state between calls and is safe to call concurrently on different
- *   buffers.
+ *   The caller owns every buffer and the library allocates no device
+ *   memory. Its only state is a per-device cache, filled on the first call
+ *   on a device, of how many workgroups of each persistent kernel fit on
+ *   that device at once (a value the runtime reports and that never
+ *   changes); it affects no result. Calls on different buffers may run
+ *   concurrently.
  * - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *   Work is enqueued asynchronously; the return value reports argument
  *   errors (found on the host before anything is enqueued) and launch
@@ -149,7 +152,11 @@ sta_status sta_forward_timed(const sta_dims* dims, const void* q, const void* k,
                              void* stream, void* const* events);
 
 /*
- * Tile-major gather of one bf16 tensor: x_raster [B][heads][S][D] into
+ * Tile-major gather of one bf16 tensor. The tile is the one the STA README
+ * ("Usage") fixes: a cube of (6, 8, 8) video tokens; laying each tile's 384
+ * tokens out contiguously turns every dense (query tile, key tile) block of
+ * the attention map into a contiguous slab (README "Why is STA Fast?").
+ * x_raster [B][heads][S][D] into
  * x_tiled [B][heads][S_t][D] with S_t = sta_tiled_seq_len(dims, has_text).
  * Tile tile = ((t/6)*n_h + h/8)*n_w + w/8 owns the 384 contiguous rows
  * tile*384 ..; its video rows (t, h, w) come first in (frame, row, column)
@@ -164,7 +171,8 @@ sta_status sta_forward_timed(const sta_dims* dims, const void* q, const void* k,
 sta_status sta_tile_gather(const sta_dims* dims, int32_t has_text,
                            const void* x_raster, void* x_tiled, void* stream);
 
-/* Inverse of sta_tile_gather (padding rows of x_tiled are not read). */
+/* Inverse of sta_tile_gather (README "Usage": the (6, 8, 8) tile); the padding
+ * rows of x_tiled are not read. Same argument rules as sta_tile_gather. */
 sta_status sta_tile_scatter(const sta_dims* dims, int32_t has_text,
                             const void* x_tiled, void* x_raster, void* stream);
 

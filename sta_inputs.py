@@ -150,3 +150,55 @@ def sample_rows(wl: Workload, per_head: int, seed: int = 7) -> torch.Tensor:
         n_rand = max(per_head - len(picks), 0)
     picks |= {int(x) for x in torch.randint(0, nv, (n_rand,), generator=g)}
     return torch.tensor(sorted(picks), dtype=torch.int64)
+
+
+def sample_rows_stratified(wl: Workload, per_head: int, head: int, seed: int = 11) -> torch.Tensor:
+    """A stratified sample of query rows for head ``head`` (a different draw per head).
+
+    Strata are the video tiles grouped by how many of their axes touch the
+    border of the tile grid (0: interior, 1: face, 2: edge, 3: corner; a
+    one-tile axis counts as border); each present stratum gets an equal share
+    of random (tile, token) picks. Added to them: the rows of
+    ``sample_rows`` (video corners and face centres, first / last-valid /
+    first-padded / last text slots) and, with text, 8 further random text
+    slots. Sorted, unique, int64; at least ``per_head`` rows when the video
+    has that many.
+    """
+    T, H, W = wl.video
+    nv = T * H * W
+    n = tuple(-(-s // t) for s, t in zip(wl.video, TILE))
+    g = torch.Generator().manual_seed(seed + 7919 * head + 104729 * wl.seed_base)
+    picks = {int(x) for x in sample_rows(wl, per_head=0, seed=seed + head)}
+    if wl.has_text:
+        picks |= {nv + int(x) for x in torch.randint(0, TEXT_SLOTS, (8,), generator=g)}
+    strata = {}
+    for tt in range(n[0]):
+        for th in range(n[1]):
+            for tw in range(n[2]):
+                b = sum(int(c == 0 or c == m - 1) for c, m in zip((tt, th, tw), n))
+                strata.setdefault(b, []).append((tt, th, tw))
+    want = max(per_head - len(picks), 0)
+    share = -(-want // len(strata))
+    for b in sorted(strata):
+        tiles = strata[b]
+        for _ in range(share):
+            tt, th, tw = tiles[int(torch.randint(0, len(tiles), (1,), generator=g))]
+            # a token that exists in the tile (the last tile along an axis may be partial)
+            ft, fh, fw = (min(t, s - c * t) for t, s, c in zip(TILE, wl.video, (tt, th, tw)))
+            dt, dh, dw = (int(torch.randint(0, f, (1,), generator=g)) for f in (ft, fh, fw))
+            picks.add(((tt * TILE[0] + dt) * H + th * TILE[1] + dh) * W + tw * TILE[2] + dw)
+    # top up (duplicates) with uniform draws over the video
+    while len(picks) < min(per_head, nv):
+        picks.add(int(torch.randint(0, nv, (1,), generator=g)))
+    return torch.tensor(sorted(picks), dtype=torch.int64)
+
+
+def tile_of_row(wl: Workload, row: int) -> int:
+    """Query unit of a sequence row: its video tile (raster tile index) or, for a
+    text slot, -1 (the text slots of a head form one unit)."""
+    T, H, W = wl.video
+    if row >= T * H * W:
+        return -1
+    n_h, n_w = -(-H // TILE[1]), -(-W // TILE[2])
+    t, h, w = row // (H * W), (row // W) % H, row % W
+    return ((t // TILE[0]) * n_h + h // TILE[1]) * n_w + w // TILE[2]

@@ -8,7 +8,9 @@ Tolerances (bf16 inputs, fp32 accumulation, bf16 output):
 
 from __future__ import annotations
 
+import os
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import torch
@@ -64,12 +66,68 @@ def oracle_rows(q, k, v, windows, text_length, has_text, video, rows=None):
     return out, lse
 
 
+def _oracle_threads(n_tasks: int) -> int:
+    """Worker threads for per-head oracle calls: numpy releases the GIL in its
+    loops and BLAS calls, so heads run in parallel on the host's cores (each
+    thread's BLAS limited to one thread)."""
+    try:
+        cpus = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        cpus = os.cpu_count() or 1
+    return max(1, min(n_tasks, cpus, 16))
+
+
+def map_heads(fn, heads):
+    """[fn(h) for h in heads], evaluated on a thread pool (see _oracle_threads)."""
+    from threadpoolctl import threadpool_limits
+
+    heads = list(heads)
+    with threadpool_limits(limits=1):
+        with ThreadPoolExecutor(max_workers=_oracle_threads(len(heads))) as ex:
+            return list(ex.map(fn, heads))
+
+
+def oracle_rows_per_head(q, k, v, windows, text_length, has_text, video, rows_per_head):
+    """Oracle out / lse of head h on its own query rows ``rows_per_head[h]``.
+
+    Returns a list over heads of (out [B, R_h, D], lse [B, R_h]) float64 arrays.
+    """
+    heads = q.shape[1]
+    host = [x.cpu() for x in (q, k, v)]
+
+    def one(h):
+        o, l = oracle.sta_reference(*(x[:, h:h + 1] for x in host), [windows[h]], text_length,
+                                    has_text, video, rows=np.asarray(rows_per_head[h]))
+        return o[:, 0], l[:, 0]
+
+    return map_heads(one, range(heads))
+
+
+def compare_per_head(out_gpu, lse_gpu, refs, rows_per_head, label=""):
+    """Parity of every head on its own rows (refs from oracle_rows_per_head), at
+    the same tolerances as compare(), pooled over the heads."""
+    outs, lses, ros, rls = [], [], [], []
+    for h, (ro, rl) in enumerate(refs):
+        idx = torch.as_tensor(np.asarray(rows_per_head[h]), dtype=torch.int64)
+        outs.append(out_gpu[:, h, idx.to(out_gpu.device)].float().cpu().numpy())
+        lses.append(lse_gpu[:, h, idx.to(lse_gpu.device)].float().cpu().numpy())
+        ros.append(ro)
+        rls.append(rl)
+    o = np.concatenate(outs, axis=1).astype(np.float64)
+    l = np.concatenate(lses, axis=1).astype(np.float64)
+    return _check(o, l, np.concatenate(ros, axis=1), np.concatenate(rls, axis=1), label)
+
+
 def compare(out_gpu, lse_gpu, out_ref, lse_ref, rows=None, label=""):
     """Assert parity; returns the error summary."""
     o = out_gpu if rows is None else out_gpu[:, :, rows]
     l = lse_gpu if rows is None else lse_gpu[:, :, rows]
     o = o.float().cpu().numpy().astype(np.float64)
     l = l.float().cpu().numpy().astype(np.float64)
+    return _check(o, l, out_ref, lse_ref, label)
+
+
+def _check(o, l, out_ref, lse_ref, label):
     assert np.isfinite(o).all(), f"{label}: non-finite output"
     assert np.isfinite(l).all(), f"{label}: non-finite lse"
     err = np.abs(o - out_ref)

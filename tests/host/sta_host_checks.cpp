@@ -1,0 +1,325 @@
+// Host-only checks of the STA library's host code (argument validation,
+// geometry, workspace carving, the launch sequence) and of the index helpers
+// that its kernels share with the host. tests/test_host_sanitized.py builds
+// this file together with the library's host source under AddressSanitizer
+// and UndefinedBehaviorSanitizer with the host C++ compiler. No GPU and no
+// HIP runtime take part: the kernel launchers and hipEventRecord are replaced
+// by stubs that record their arguments, and no "device" pointer is ever
+// dereferenced (the fake addresses used here are only compared).
+//
+//   sta_host_checks validate
+//       self-checking cases; prints "ok <n>" and exits 0, or names the first
+//       failing case and exits 1
+//   sta_host_checks dump <B> <heads> <D> <T> <H> <W> <has_text> <ell> <wt> <wh> <ww>
+//       prints the helpers' values for one geometry (every head gets the
+//       window (wt, wh, ww)); the Python test compares them with maps built
+//       from the oracle's token coordinates
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/sta.h"
+#include "../../block_sparse_sliding_amd/csrc/sta_internal.h"
+
+namespace {
+
+struct Launch {
+  std::string name;
+  std::vector<uintptr_t> ptrs;  // pointer arguments, in declaration order
+  sta::Geom g;
+};
+std::vector<Launch> g_launches;
+int g_events = 0;
+
+uintptr_t P(const void* p) { return reinterpret_cast<uintptr_t>(p); }
+void record(const char* name, const sta::Geom& g, std::vector<uintptr_t> ptrs) {
+  g_launches.push_back(Launch{name, std::move(ptrs), g});
+}
+
+}  // namespace
+
+// ---- stubs for the device side of the library
+extern "C" hipError_t hipEventRecord(hipEvent_t, hipStream_t) {
+  ++g_events;
+  return hipSuccess;
+}
+
+namespace sta {
+hipError_t launch_rows_permute(const Geom& g, const void* src, void* dst, bool, hipStream_t) {
+  record("rows_permute", g, {P(src), P(dst)});
+  return hipSuccess;
+}
+hipError_t launch_pack_v(const Geom& g, const void* v, void* vt, hipStream_t) {
+  record("pack_v", g, {P(v), P(vt)});
+  return hipSuccess;
+}
+hipError_t launch_pack_rows(const Geom& g, const void* src, void* dst, int, hipStream_t) {
+  record("pack_rows", g, {P(src), P(dst)});
+  return hipSuccess;
+}
+hipError_t launch_schedule_lists(const Geom& g, const Windows&, int32_t* offsets, int32_t* ids,
+                                 hipStream_t) {
+  record("schedule_lists", g, {P(offsets), P(ids)});
+  return hipSuccess;
+}
+hipError_t launch_schedule_work(const Geom& g, const Windows&, int32_t* work, int32_t* claim,
+                                hipStream_t) {
+  record("schedule_work", g, {P(work), P(claim)});
+  return hipSuccess;
+}
+hipError_t launch_attention(const Geom& g, const Windows&, const FwdArgs& a, hipStream_t) {
+  record("attention", g, {P(a.q), P(a.k), P(a.vt), P(a.out), P(a.lse), P(a.offsets), P(a.ids),
+                          P(a.work), P(a.claim)});
+  return hipSuccess;
+}
+hipError_t launch_bwd_prep(const Geom& g, const void* out, const void* dout, const float* lse,
+                           float* lse2, float* delta, int32_t* claim_q, int32_t* claim_kv,
+                           hipStream_t) {
+  record("bwd_prep", g, {P(out), P(dout), P(lse), P(lse2), P(delta), P(claim_q), P(claim_kv)});
+  return hipSuccess;
+}
+hipError_t launch_bwd_dq(const Geom& g, const Windows&, const BwdArgs& a, hipStream_t) {
+  record("bwd_dq", g, {P(a.kt), P(a.qt), P(a.dot), P(a.lse2), P(a.delta), P(a.offsets), P(a.ids),
+                       P(a.claim_q), P(a.claim_kv)});
+  return hipSuccess;
+}
+hipError_t launch_bwd_dkv(const Geom& g, const Windows&, const BwdArgs& a, hipStream_t) {
+  record("bwd_dkv", g, {P(a.kt), P(a.qt), P(a.dot), P(a.lse2), P(a.delta), P(a.offsets),
+                        P(a.ids), P(a.claim_q), P(a.claim_kv)});
+  return hipSuccess;
+}
+}  // namespace sta
+
+namespace {
+
+int g_checks = 0;
+#define CHECK(cond, ...)                                                     \
+  do {                                                                       \
+    ++g_checks;                                                              \
+    if (!(cond)) {                                                           \
+      std::fprintf(stderr, "FAIL %s:%d: %s: ", __FILE__, __LINE__, #cond);   \
+      std::fprintf(stderr, __VA_ARGS__);                                     \
+      std::fprintf(stderr, "\n");                                            \
+      std::exit(1);                                                          \
+    }                                                                        \
+  } while (0)
+
+// Fake, well-separated, 256-byte aligned "device" addresses (never dereferenced).
+constexpr uintptr_t kGiB = uintptr_t(1) << 30;
+void* fake(int slot) { return reinterpret_cast<void*>(uintptr_t(slot + 1) * 64 * kGiB); }
+
+std::vector<int32_t> windows_for(int heads, int wt, int wh, int ww) {
+  std::vector<int32_t> w;
+  for (int h = 0; h < heads; ++h) w.insert(w.end(), {wt, wh, ww});
+  return w;
+}
+
+sta_status fwd(const sta_dims* d, const int32_t* win, int ell, int text, void* q, void* k, void* v,
+               void* out, float* lse, void* ws, size_t ws_bytes, void* const* events = nullptr) {
+  g_launches.clear();
+  if (events != nullptr)
+    return sta_forward_timed(d, q, k, v, win, ell, text, out, lse, ws, ws_bytes, nullptr, events);
+  return sta_forward(d, q, k, v, win, ell, text, out, lse, ws, ws_bytes, nullptr);
+}
+
+// Every pointer that a launch got which is not one of the caller's tensors
+// lies inside the workspace, at a 256-byte aligned offset.
+void check_in_workspace(const Launch& l, const std::vector<uintptr_t>& caller, uintptr_t ws,
+                        size_t bytes) {
+  for (uintptr_t p : l.ptrs) {
+    bool is_caller = p == 0;
+    for (uintptr_t c : caller) is_caller |= p == c;
+    if (is_caller) continue;
+    CHECK(p >= ws && p < ws + bytes, "%s: pointer %#zx outside workspace [%#zx, +%zu)",
+          l.name.c_str(), size_t(p), size_t(ws), bytes);
+    CHECK(((p - ws) & 255) == 0, "%s: workspace offset %zu not 256-aligned", l.name.c_str(),
+          size_t(p - ws));
+  }
+}
+
+void validate() {
+  const sta_dims d{1, 2, 128, 30, 48, 80};
+  std::vector<int32_t> w = windows_for(2, 3, 3, 3);
+  void *q = fake(0), *k = fake(1), *v = fake(2), *out = fake(3), *ws = fake(8);
+  float* lse = static_cast<float*>(fake(4));
+  const size_t need = sta_workspace_bytes(&d, w.data(), 1);
+  CHECK(need > 0, "workspace bytes");
+
+  struct Case {
+    const char* what;
+    sta_status expect;
+    sta_status got;
+  };
+  std::vector<Case> cases;
+  auto add = [&](const char* what, sta_status expect, sta_status got) {
+    cases.push_back({what, expect, got});
+    CHECK(g_launches.empty(), "%s: launched %zu kernels on a rejected call", what,
+          g_launches.size());
+  };
+  const sta_dims d0{0, 2, 128, 30, 48, 80}, dh0{1, 0, 128, 30, 48, 80}, dd{1, 2, 96, 30, 48, 80};
+  const sta_dims dt0{1, 2, 128, 0, 48, 80}, dhn{1, 2, 128, 30, -8, 80};
+  const sta_dims dbig{1, 2, 128, 6 * 1024, 8, 8}, dheads{1, 257, 128, 30, 48, 80};
+  std::vector<int32_t> w257 = windows_for(257, 1, 1, 1);
+  add("null dims", STA_ERR_NULL, fwd(nullptr, w.data(), 226, 1, q, k, v, out, lse, ws, need));
+  add("batch 0", STA_ERR_NULL, fwd(&d0, w.data(), 226, 1, q, k, v, out, lse, ws, need));
+  add("heads 0", STA_ERR_NULL, fwd(&dh0, w.data(), 226, 1, q, k, v, out, lse, ws, need));
+  add("null q", STA_ERR_NULL, fwd(&d, w.data(), 226, 1, nullptr, k, v, out, lse, ws, need));
+  add("null v", STA_ERR_NULL, fwd(&d, w.data(), 226, 1, q, k, nullptr, out, lse, ws, need));
+  add("null out", STA_ERR_NULL, fwd(&d, w.data(), 226, 1, q, k, v, nullptr, lse, ws, need));
+  add("null windows", STA_ERR_NULL, fwd(&d, nullptr, 226, 1, q, k, v, out, lse, ws, need));
+  add("head_dim 96", STA_ERR_SHAPE, fwd(&dd, w.data(), 226, 1, q, k, v, out, lse, ws, need));
+  add("T 0", STA_ERR_SHAPE, fwd(&dt0, w.data(), 226, 1, q, k, v, out, lse, ws, need));
+  add("H -8", STA_ERR_SHAPE, fwd(&dhn, w.data(), 226, 1, q, k, v, out, lse, ws, need));
+  add("1024 tiles on t", STA_ERR_SHAPE, fwd(&dbig, w.data(), 0, 0, q, k, v, out, lse, ws, need));
+  add("257 heads", STA_ERR_SHAPE, fwd(&dheads, w257.data(), 0, 1, q, k, v, out, lse, ws, need));
+  for (int axis = 0; axis < 3; ++axis)
+    for (int bad : {0, -1, 7, 11}) {
+      std::vector<int32_t> wb = w;
+      const int n_axis[3] = {5, 6, 10};
+      if (bad >= 1 && bad <= n_axis[axis]) continue;
+      wb[3 + axis] = bad;
+      add("window out of range", STA_ERR_WINDOW,
+          fwd(&d, wb.data(), 226, 1, q, k, v, out, lse, ws, need));
+    }
+  add("ell 257", STA_ERR_TEXT, fwd(&d, w.data(), 257, 1, q, k, v, out, lse, ws, need));
+  add("ell -1", STA_ERR_TEXT, fwd(&d, w.data(), -1, 1, q, k, v, out, lse, ws, need));
+  add("ell without text", STA_ERR_TEXT, fwd(&d, w.data(), 5, 0, q, k, v, out, lse, ws, need));
+  char* qc = static_cast<char*>(q);
+  add("q misaligned", STA_ERR_ALIGN, fwd(&d, w.data(), 226, 1, qc + 1, k, v, out, lse, ws, need));
+  add("out misaligned", STA_ERR_ALIGN,
+      fwd(&d, w.data(), 226, 1, q, k, v, static_cast<char*>(out) + 8, lse, ws, need));
+  add("lse misaligned", STA_ERR_ALIGN,
+      fwd(&d, w.data(), 226, 1, q, k, v, out, lse + 1, ws, need));
+  add("workspace small", STA_ERR_WORKSPACE,
+      fwd(&d, w.data(), 226, 1, q, k, v, out, lse, ws, need - 1));
+  add("workspace null", STA_ERR_WORKSPACE,
+      fwd(&d, w.data(), 226, 1, q, k, v, out, lse, nullptr, need));
+  add("workspace misaligned", STA_ERR_ALIGN,
+      fwd(&d, w.data(), 226, 1, q, k, v, out, lse, static_cast<char*>(ws) + 16, need));
+  add("out over q", STA_ERR_ALIAS, fwd(&d, w.data(), 226, 1, q, k, v, q, lse, ws, need));
+  add("lse over out", STA_ERR_ALIAS,
+      fwd(&d, w.data(), 226, 1, q, k, v, out, static_cast<float*>(out) + 256, ws, need));
+  add("out over workspace", STA_ERR_ALIAS,
+      fwd(&d, w.data(), 226, 1, q, k, v, static_cast<char*>(ws) + 1024, lse, ws, need));
+  void* null_events[STA_TIMED_EVENTS] = {};
+  add("timed, null event", STA_ERR_NULL,
+      fwd(&d, w.data(), 226, 1, q, k, v, out, lse, ws, need, null_events));
+  for (const Case& c : cases)
+    CHECK(c.got == c.expect, "%s: expected %d (%s), got %d (%s)", c.what, int(c.expect),
+          sta_status_str(c.expect), int(c.got), sta_status_str(c.got));
+
+  // Valid forward calls on every workload shape: the launch sequence runs on
+  // the caller's tensors and workspace regions only; the timed variant records
+  // one event before the first launch and one after each.
+  struct Shape {
+    sta_dims d;
+    int text, ell, wt, wh, ww;
+  };
+  const Shape shapes[] = {
+      {{1, 1, 64, 18, 24, 24}, 0, 0, 1, 3, 3},    {{1, 24, 128, 30, 48, 80}, 1, 226, 3, 3, 3},
+      {{1, 24, 128, 48, 72, 128}, 1, 128, 3, 3, 3}, {{1, 24, 128, 33, 45, 80}, 1, 226, 3, 3, 3},
+      {{2, 3, 64, 7, 9, 11}, 1, 50, 2, 2, 2},     {{1, 2, 128, 1, 128, 128}, 0, 0, 1, 5, 5},
+      {{3, 5, 128, 1, 1, 1}, 1, 256, 1, 1, 1},
+  };
+  for (const Shape& s : shapes) {
+    std::vector<int32_t> ws_win = windows_for(s.d.heads, s.wt, s.wh, s.ww);
+    const size_t n = sta_workspace_bytes(&s.d, ws_win.data(), s.text);
+    CHECK(n > 0, "workspace bytes of a valid shape");
+    void* events[STA_TIMED_EVENTS];
+    for (int i = 0; i < STA_TIMED_EVENTS; ++i) events[i] = fake(20 + i);
+    g_events = 0;
+    sta_status st = fwd(&s.d, ws_win.data(), s.ell, s.text, q, k, v, out, lse, ws, n, events);
+    CHECK(st == STA_OK, "valid forward returned %s", sta_status_str(st));
+    CHECK(g_events == STA_TIMED_EVENTS, "timed forward recorded %d events", g_events);
+    CHECK(!g_launches.empty() && g_launches.back().name == "attention", "attention launched last");
+    for (const Launch& l : g_launches)
+      check_in_workspace(l, {P(q), P(k), P(v), P(out), P(lse)}, P(ws), n);
+    // the backward: same rules, with its own workspace
+    const size_t nb = sta_backward_workspace_bytes(&s.d, ws_win.data(), s.text);
+    CHECK(nb > 0, "backward workspace bytes of a valid shape");
+    g_launches.clear();
+    void *dq = fake(10), *dk = fake(11), *dv = fake(12), *dout = fake(13);
+    st = sta_backward(&s.d, q, k, v, out, lse, dout, ws_win.data(), s.ell, s.text, dq, dk, dv, ws,
+                      nb, nullptr);
+    CHECK(st == STA_OK, "valid backward returned %s", sta_status_str(st));
+    CHECK(g_launches.size() >= 2 && g_launches.back().name == "bwd_dkv", "backward sequence");
+    for (const Launch& l : g_launches)
+      check_in_workspace(l, {P(q), P(k), P(v), P(out), P(lse), P(dout), P(dq), P(dk), P(dv)},
+                         P(ws), nb);
+    g_launches.clear();
+    st = sta_backward(&s.d, q, k, v, out, lse, dout, ws_win.data(), s.ell, s.text, dq, dk, dv, ws,
+                      nb - 1, nullptr);
+    CHECK(st == STA_ERR_WORKSPACE && g_launches.empty(), "backward, workspace short by one byte");
+    st = sta_backward(&s.d, q, k, v, out, lse, dout, ws_win.data(), s.ell, s.text, dq, dq, dv, ws,
+                      nb, nullptr);
+    CHECK(st == STA_ERR_ALIAS && g_launches.empty(), "backward, dk over dq");
+  }
+  std::printf("ok %d\n", g_checks);
+}
+
+void dump(int argc, char** argv) {
+  if (argc != 13) {
+    std::fprintf(stderr, "dump needs 11 integers\n");
+    std::exit(2);
+  }
+  int a[11];
+  for (int i = 0; i < 11; ++i) a[i] = std::atoi(argv[2 + i]);
+  const sta_dims d{a[0], a[1], a[2], a[3], a[4], a[5]};
+  const int text = a[6], ell = a[7];
+  std::vector<int32_t> w = windows_for(d.heads, a[8], a[9], a[10]);
+  // geometry through the public calls, then the Geom the launches received
+  int64_t n_off = 0, n_ids = 0, n_work = 0;
+  CHECK(sta_schedule_sizes(&d, w.data(), text, &n_off, &n_ids, &n_work) == STA_OK, "sizes");
+  std::printf("sizes %lld %lld %lld %lld %lld\n", (long long)sta_seq_len(&d, text),
+              (long long)sta_tiled_seq_len(&d, text), (long long)n_off, (long long)n_ids,
+              (long long)n_work);
+  const size_t n = sta_workspace_bytes(&d, w.data(), text);
+  g_launches.clear();
+  CHECK(fwd(&d, w.data(), ell, text, fake(0), fake(1), fake(2), fake(3),
+            static_cast<float*>(fake(4)), fake(8), n) == STA_OK,
+        "forward on the dumped geometry");
+  const sta::Geom g = g_launches.back().g;
+  std::printf("geom %d %d %d %d %d %d %d %d %d %d %d\n", g.nt, g.nh, g.nw, g.n_tiles, g.n_video,
+              g.S, g.n_vt, g.S_t, g.full, g.n_q, g.text_length);
+  // window placement: every start on each axis, for every window size
+  const int nax[3] = {g.nt, g.nh, g.nw};
+  for (int ax = 0; ax < 3; ++ax)
+    for (int wl = 1; wl <= nax[ax]; ++wl)
+      for (int c = 0; c < nax[ax]; ++c)
+        std::printf("ws %d %d %d %d\n", ax, wl, c, sta::window_start(c, wl, nax[ax]));
+  // tile extents, and the blocks of each query tile's window and of the grid
+  for (int t = 0; t < g.n_tiles; ++t) {
+    const int tw = t % g.nw, th = (t / g.nw) % g.nh, tt = t / (g.nw * g.nh);
+    const int e = sta::tile_extent(tt, th, tw, g);
+    const int st = sta::window_start(tt, a[8], g.nt), sh = sta::window_start(th, a[9], g.nh),
+              sw = sta::window_start(tw, a[10], g.nw);
+    std::printf("tile %d %d %d %d %d %d\n", t, sta::extent_frames(e), sta::extent_rows(e),
+                sta::extent_cols(e), sta::extent_tokens(e),
+                sta::box_blocks(st, a[8], sh, a[9], sw, a[10], g));
+  }
+  std::printf("grid %d\n", sta::box_blocks(0, g.nt, 0, g.nh, 0, g.nw, g));
+  // tile-major row -> raster row (-1 for padding), and the multiples-only form
+  for (int r = 0; r < g.S_t; ++r) {
+    const int x = sta::tiled_to_raster(r, g);
+    if (g.full) CHECK(x == sta::tiled_to_raster_full(r, g), "tiled_to_raster_full row %d", r);
+    std::printf("%d\n", x);
+  }
+}
+
+}  // namespace
+
+int main(int argc, char** argv) {
+  if (argc >= 2 && std::strcmp(argv[1], "validate") == 0) {
+    validate();
+    return 0;
+  }
+  if (argc >= 2 && std::strcmp(argv[1], "dump") == 0) {
+    dump(argc, argv);
+    return 0;
+  }
+  std::fprintf(stderr, "usage: %s validate | dump B heads D T H W has_text ell wt wh ww\n", argv[0]);
+  return 2;
+}

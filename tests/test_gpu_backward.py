@@ -18,12 +18,13 @@ import torch
 import oracle
 import sta_inputs
 import block_sparse_sliding_amd as sta
-from _parity import note, run_sta, scale_key_tiles
+from _parity import map_heads, note, run_sta, scale_key_tiles
 
 pytestmark = pytest.mark.gpu
 
 REL_RMS = 1e-2
 MAX_REL = 2e-2
+BWD_DQ_ROWS = 256  # sampled dq rows per head at full size
 
 
 def run_backward(q, k, v, out, lse, dout, windows, ell, has_text, video):
@@ -174,9 +175,76 @@ def test_backward_medium_sampled(case):
     assert bool(torch.isfinite(dq).all() and torch.isfinite(dk).all() and torch.isfinite(dv).all())
 
 
+def tile_rows(video, tile):
+    """Raster rows of the tokens of video tile (tt, th, tw) that exist."""
+    T, H, W = video
+    tt, th, tw = tile
+    return [(t * H + h) * W + w
+            for t in range(6 * tt, min(T, 6 * tt + 6))
+            for h in range(8 * th, min(H, 8 * th + 8))
+            for w in range(8 * tw, min(W, 8 * tw + 8))]
+
+
+def corner_tiles(video, corner, interior):
+    """Key tiles near one corner of the tile grid: the corner tile, the edge tile
+    next to it along w, and (interior=True) the tile one step in along every axis
+    (not on the border of any axis when the grid has at least 3 tiles per axis).
+    corner: 3 bits, bit a set = the high end of axis a."""
+    n = tuple(-(-s // t) for s, t in zip(video, (6, 8, 8)))
+
+    def at(offsets):
+        return tuple((m - 1 - o) if (corner >> a) & 1 else o for a, (m, o) in
+                     enumerate(zip(n, offsets)))
+
+    tiles = [at((0, 0, 0)), at((0, 0, 1))]
+    if interior:
+        tiles.append(at((1, 1, 1)))
+    return tiles
+
+
+def check_heads(q, k, v, dout, dq, dk, dv, windows, ell, has_text, video, heads, qrows_of,
+                key_tiles_of, label):
+    """Oracle backward of each listed head (on a thread pool): dq on the head's
+    own query rows, dk and dv on every row of the head's key tiles."""
+    host = [x.cpu() for x in (q, k, v, dout)]
+
+    def one(h):
+        keys = sorted({r for t in key_tiles_of(h) for r in tile_rows(video, t)})
+        sl = slice(h, h + 1)
+        ref = oracle.sta_reference_backward(*(x[:, sl] for x in host), [windows[h]], ell, has_text,
+                                            video, query_rows=qrows_of(h), key_rows=keys)
+        return keys, ref
+
+    for h, (keys, (rq, rk, rv)) in zip(heads, map_heads(one, heads)):
+        sl = slice(h, h + 1)
+        qi = torch.as_tensor(np.asarray(qrows_of(h)), dtype=torch.int64)
+        ki = torch.as_tensor(np.asarray(keys), dtype=torch.int64)
+        compare_grad(dq[:, sl][:, :, qi], rq, f"dq {label} head {h}")
+        if len(keys):
+            compare_grad(dk[:, sl][:, :, ki], rk, f"dk {label} head {h} tiles {key_tiles_of(h)}")
+            compare_grad(dv[:, sl][:, :, ki], rv, f"dv {label} head {h} tiles {key_tiles_of(h)}")
+
+
+def sum_rules(dout, dq, dk, dv):
+    """sum_j dv_j = sum_i dout_i and sum_j dk_j = 0, per (batch, head), in fp64."""
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        assert bool(torch.isfinite(t).all()), name
+    sdv = dv.double().sum(dim=2)
+    sdo = dout.double().sum(dim=2)
+    sdk = dk.double().sum(dim=2)
+    dv_scale = dv.double().abs().sum(dim=2)
+    dk_scale = dk.double().abs().sum(dim=2)
+    assert bool(((sdv - sdo).abs() <= 1e-2 * dv_scale + 1e-3).all())
+    assert bool((sdk.abs() <= 1e-2 * dk_scale + 1e-3).all())
+
+
 def test_backward_full_size():
-    """(30,48,80) + 256 text at D = 128: every gradient written, sum rules on every head,
-    sampled dq rows, and the dk/dv rows of one key tile of a (1,1,1)-window head."""
+    """(30,48,80) + 256 text at D = 128 with four different windows: every
+    gradient written, sum rules on every head, 256 dq rows per head (its own
+    stratified draw), and dk/dv on whole key tiles: a corner, an edge and an
+    interior tile of the (1,1,1) head, a corner and an edge tile of the
+    (3,3,3) and (3,3,5) heads (the (5,6,10) head sees every key from every
+    query, so any key tile needs every query row: the sum rules cover it)."""
     wl = sta_inputs.WORKLOADS["headline"]
     video = wl.video
     heads = 4
@@ -188,36 +256,41 @@ def test_backward_full_size():
     q, k, v, dout = inputs(1, heads, S, 128, 77)
     out, lse = run_sta(q, k, v, windows, ell, True, video)
     dq, dk, dv = run_backward(q, k, v, out, lse, dout, windows, ell, True, video)
-    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
-        assert bool(torch.isfinite(t).all()), name
-    # sum rules: sum_j dv_j = sum_i dout_i, sum_j dk_j = 0 (per head, fp64 sums)
-    sdv = dv.double().sum(dim=2)
-    sdo = dout.double().sum(dim=2)
-    sdk = dk.double().sum(dim=2)
-    dv_scale = dv.double().abs().sum(dim=2)
-    dk_scale = dk.double().abs().sum(dim=2)
-    assert bool(((sdv - sdo).abs() <= 1e-2 * dv_scale + 1e-3).all())
-    assert bool((sdk.abs() <= 1e-2 * dk_scale + 1e-3).all())
-    rng = np.random.default_rng(5)
-    qrows = np.unique(np.concatenate([rng.integers(0, nv, 16), [nv, S - 1]]))
-    for h in range(heads):
-        sl = slice(h, h + 1)
-        kr = None
-        if h == 0:
-            # key tile 137 of the (1,1,1) head: its 384 rows, seen by one query tile and the text
-            tile = 137
-            tt, rest = divmod(tile, 6 * 10)
-            th, tw = divmod(rest, 10)
-            kr = [((tt * 6 + a) * 48 + th * 8 + b) * 80 + tw * 8 + c
-                  for a in range(6) for b in range(8) for c in range(8)]
-        rq, rk, rv = oracle.sta_reference_backward(
-            q[:, sl].cpu(), k[:, sl].cpu(), v[:, sl].cpu(), dout[:, sl].cpu(), [windows[h]], ell,
-            True, video, query_rows=qrows, key_rows=kr if kr is not None else [])
-        compare_grad(dq[:, sl][:, :, torch.from_numpy(qrows)], rq, f"dq full head {h}")
-        if kr is not None:
-            idx = torch.tensor(kr)
-            compare_grad(dk[:, sl][:, :, idx], rk, "dk full head 0")
-            compare_grad(dv[:, sl][:, :, idx], rv, "dv full head 0")
+    sum_rules(dout, dq, dk, dv)
+    wl4 = sta_inputs.custom("bwd4", 1, heads, 128, video, windows, True, ell)
+    qrows = {h: sta_inputs.sample_rows_stratified(wl4, BWD_DQ_ROWS, h).numpy() for h in range(heads)}
+    tiles = {0: corner_tiles(video, 5, True), 1: corner_tiles(video, 2, False), 2: [],
+             3: corner_tiles(video, 7, False)}
+    check_heads(q, k, v, dout, dq, dk, dv, windows, ell, True, video, range(heads),
+                qrows.__getitem__, tiles.__getitem__, "full")
+    del q, k, v, dout, out, lse, dq, dk, dv
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("part", [0, 1])
+def test_backward_headline_all_heads(part):
+    """The benchmarked backward configuration ((30,48,80) + 256 text, 24 heads,
+    window (3,3,3), text length 226, its seeded inputs): sum rules on every
+    head; for half of the heads (``part``), 256 dq rows per head (its own
+    stratified draw) and dk/dv on whole key tiles at one corner of the grid,
+    a different corner per head: the corner tile and the edge tile next to it,
+    and on every third head also the interior tile one step in on every axis."""
+    wl = sta_inputs.WORKLOADS["headline"]
+    windows = list(wl.windows)
+    note(f"backward headline, all heads, part {part}")
+    q, k, v = sta_inputs.make_qkv(wl, "cuda")
+    g = torch.Generator(device="cuda").manual_seed(10 * wl.seed_base + 3)
+    dout = torch.randn(q.shape, generator=g, device="cuda").to(torch.bfloat16)
+    out, lse = run_sta(q, k, v, windows, wl.text_length, wl.has_text, wl.video)
+    dq, dk, dv = run_backward(q, k, v, out, lse, dout, windows, wl.text_length, wl.has_text,
+                              wl.video)
+    sum_rules(dout, dq, dk, dv)
+    heads = list(range(part, wl.heads, 2))
+    qrows = {h: sta_inputs.sample_rows_stratified(wl, BWD_DQ_ROWS, h, seed=23).numpy()
+             for h in heads}
+    tiles = {h: corner_tiles(wl.video, h % 8, h % 3 == 0) for h in heads}
+    check_heads(q, k, v, dout, dq, dk, dv, windows, wl.text_length, wl.has_text, wl.video, heads,
+                qrows.__getitem__, tiles.__getitem__, "headline")
     del q, k, v, dout, out, lse, dq, dk, dv
     torch.cuda.empty_cache()
 

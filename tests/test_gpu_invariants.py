@@ -124,19 +124,29 @@ def test_uniform_attention_closed_form(video, windows, ell, has_text, D):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("kfill", ["large", "nonfinite"])
 @pytest.mark.parametrize("ell,video", [(0, (18, 24, 32)), (1, (18, 24, 32)), (100, (18, 24, 32)),
                                        (226, (18, 24, 32)), (255, (18, 24, 32)), (77, (17, 21, 30))])
-def test_text_padding_never_reaches_output(ell, video):
+def test_text_padding_never_reaches_output(ell, video, kfill):
+    """Padded text K/V (slots at or after text_length) change no bit of out or lse:
+    K padded with a large finite value, or with NaN, +inf and -inf (every slot
+    of the last, partly valid text block included); V with NaN and +inf."""
     windows = [(3, 3, 3), (1, 2, 3)]
     nv = video[0] * video[1] * video[2]
     S = nv + 256
-    note(f"text padding isolation ell={ell}")
+    note(f"text padding isolation ell={ell} k={kfill}")
     g = torch.Generator(device="cuda").manual_seed(ell)
     q, k, v = [torch.randn(1, 2, S, 128, generator=g, device="cuda").to(torch.bfloat16)
                for _ in range(3)]
     out1, lse1 = run_sta(q, k, v, windows, ell, True, video)
     k2, v2 = k.clone(), v.clone()
-    k2[:, :, nv + ell:] = 100.0
+    if kfill == "large":
+        k2[:, :, nv + ell:] = 100.0
+    else:
+        k2[:, :, nv + ell:] = float("nan")
+        k2[:, :, nv + ell::3] = float("inf")
+        k2[:, :, nv + ell + 1::3] = float("-inf")
+        k2[:, :, nv + ell:, 5] = float("nan")  # inf - inf inside a dot product as well
     v2[:, :, nv + ell:] = float("nan")
     v2[:, :, nv + ell::2] = float("inf")
     out2, lse2 = run_sta(q, k2, v2, windows, ell, True, video)

@@ -10,9 +10,12 @@ import pytest
 import torch
 
 import sta_inputs
-from _parity import compare, note, oracle_rows, run_sta, scale_key_tiles
+from _parity import (compare, compare_per_head, note, oracle_rows, oracle_rows_per_head, run_sta,
+                     scale_key_tiles)
 
 pytestmark = pytest.mark.gpu
+
+FULL_SIZE_ROWS = 512  # sampled query rows per head at the full-size workloads
 
 
 def rand(shape, seed, device="cuda"):
@@ -102,9 +105,15 @@ def test_full_size_sampled(name):
     out, lse = run_sta(q, k, v, list(wl.windows), wl.text_length, wl.has_text, wl.video)
     # every row of every (batch, head) was written (the outputs start as NaN)
     assert bool(torch.isfinite(out).all()) and bool(torch.isfinite(lse).all()), name
-    rows = sta_inputs.sample_rows(wl, per_head=24)
-    ro, rl = oracle_rows(q, k, v, list(wl.windows), wl.text_length, wl.has_text, wl.video,
-                         rows=rows.numpy())
-    compare(out, lse, ro, rl, rows=rows, label=name)
+    # 512 stratified rows per head, a different draw for every head: at these
+    # shapes each workgroup of the persistent grid runs many query units in
+    # turn, and the draws reach nearly every query tile of every head
+    rows = [sta_inputs.sample_rows_stratified(wl, FULL_SIZE_ROWS, h).numpy()
+            for h in range(wl.heads)]
+    tiles_hit = min(len({sta_inputs.tile_of_row(wl, int(r)) for r in rh}) for rh in rows)
+    note(f"full-size {name}: {FULL_SIZE_ROWS} rows per head, >= {tiles_hit} query units per head")
+    refs = oracle_rows_per_head(q, k, v, list(wl.windows), wl.text_length, wl.has_text, wl.video,
+                                rows)
+    compare_per_head(out, lse, refs, rows, label=name)
     del q, k, v, out, lse
     torch.cuda.empty_cache()

@@ -1,0 +1,159 @@
+"""Host code and index helpers under AddressSanitizer and UndefinedBehaviorSanitizer.
+
+``tests/host/sta_host_checks.cpp`` is compiled here, with the host C++
+compiler, together with the library's host source (argument validation,
+geometry, workspace carving, the launch sequence); the kernel launchers are
+recording stubs, so no GPU and no HIP runtime are involved. Its ``validate``
+mode checks every argument error and that valid calls hand the kernels only
+the caller's tensors and workspace regions. Its ``dump`` mode prints the index
+helpers the kernels share with the host (window placement, tile extents,
+blocks per window box, the tile-major to raster row map) for one geometry;
+the tests below compare them with maps built from the oracle's token
+coordinates (``oracle.window_start``, ``oracle.key_tiles_of_query_tile``,
+token counts per tile from the oracle's coordinate map).
+"""
+
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import sta_oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HOST_SRC = os.path.join(ROOT, "block_sparse_sliding_amd", "csrc", "sta_api" + ".hip")
+CHECKS_SRC = os.path.join(ROOT, "tests", "host", "sta_host_checks.cpp")
+SANITIZERS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer"]
+CXX_FLAGS = ["-std=c++17", "-O1", "-g", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include"]
+TILE = (6, 8, 8)
+
+
+@pytest.fixture(scope="module")
+def checks_bin(tmp_path_factory):
+    cxx = shutil.which("g++")
+    if cxx is None:
+        pytest.skip("no host C++ compiler")
+    exe = tmp_path_factory.mktemp("host_checks") / "sta_host_checks"
+    # the host source is compiled as plain C++ (its HIP calls are stubbed)
+    sources = ["-x", "c++", HOST_SRC, "-x", "none", CHECKS_SRC]
+    cmd = [cxx, *CXX_FLAGS, *SANITIZERS, *sources, "-o", str(exe)]
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    assert r.returncode == 0, r.stdout
+    return str(exe)
+
+
+def run(exe, *args):
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:abort_on_error=0",
+               UBSAN_OPTIONS="print_stacktrace=1:halt_on_error=1")
+    env.pop("LD_PRELOAD", None)
+    r = subprocess.run([exe, *map(str, args)], stdout=subprocess.PIPE, stderr=subprocess.PIPE,
+                       text=True, env=env)
+    assert r.returncode == 0, r.stderr[-4000:]
+    assert "runtime error" not in r.stderr, r.stderr[-4000:]
+    return r.stdout
+
+
+def test_validation_and_launch_sequence(checks_bin):
+    out = run(checks_bin, "validate")
+    assert out.startswith("ok "), out
+    assert int(out.split()[1]) > 500
+
+
+SHAPES = [
+    # B, heads, D, video, has_text, ell, window
+    (1, 1, 64, (18, 24, 24), 0, 0, (1, 3, 3)),
+    (1, 24, 128, (30, 48, 80), 1, 226, (3, 3, 3)),
+    (1, 24, 128, (30, 48, 80), 1, 256, (5, 6, 10)),
+    (1, 24, 128, (33, 45, 80), 1, 226, (3, 3, 3)),
+    (1, 24, 128, (48, 72, 128), 1, 128, (3, 3, 3)),
+    (2, 3, 128, (7, 9, 11), 1, 50, (2, 2, 2)),
+    (1, 2, 128, (17, 21, 30), 1, 77, (2, 3, 2)),
+    (1, 2, 64, (13, 8, 20), 0, 0, (3, 1, 3)),
+    (1, 1, 128, (20, 30, 45), 1, 100, (3, 2, 4)),
+    (1, 2, 128, (1, 128, 128), 0, 0, (1, 5, 5)),
+    (1, 2, 128, (1, 100, 100), 1, 33, (1, 6, 6)),
+    (3, 5, 128, (1, 1, 1), 1, 256, (1, 1, 1)),
+    (1, 1, 128, (6, 8, 8), 1, 17, (1, 1, 1)),
+    (1, 1, 64, (5, 7, 9), 0, 0, (1, 1, 2)),
+]
+
+
+def oracle_maps(video):
+    """Tile id of every raster video row and tokens per tile, from the oracle's
+    token coordinates."""
+    n = sta_oracle._check_video(video)
+    kt, kh, kw = sta_oracle._video_tile_coords(video)
+    tile = (kt * n[1] + kh) * n[2] + kw
+    return n, tile, np.bincount(tile, minlength=n[0] * n[1] * n[2])
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=[f"{s[3]}w{s[6]}t{s[5] if s[4] else '-'}"
+                                               for s in SHAPES])
+def test_helpers_match_oracle_maps(checks_bin, shape):
+    B, heads, D, video, text, ell, win = shape
+    T, H, W = video
+    out = run(checks_bin, "dump", B, heads, D, T, H, W, text, ell, *win).splitlines()
+    n, tile_of_row, tokens = oracle_maps(video)
+    nv = T * H * W
+    n_tiles = int(np.prod(n))
+    S = nv + (256 if text else 0)
+    S_t = n_tiles * 384 + (256 if text else 0)
+
+    sizes = [int(x) for x in out[0].split()[1:]]
+    assert sizes == [S, S_t, heads * (n_tiles + text) + 1,
+                     heads * (n_tiles * win[0] * win[1] * win[2] + (n_tiles if text else 0)),
+                     B * heads * (n_tiles + text)]
+    geom = [int(x) for x in out[1].split()[1:]]
+    assert geom == [*n, n_tiles, nv, S, n_tiles * 384, S_t, int(n_tiles * 384 == nv),
+                    n_tiles + text, ell]
+
+    ws = [ln for ln in out if ln.startswith("ws ")]
+    assert len(ws) == sum(m * m for m in n)
+    for ln in ws:
+        ax, w, c, start = (int(x) for x in ln.split()[1:])
+        assert start == oracle.window_start(c, w, n[ax]), ln
+
+    tiles = [ln for ln in out if ln.startswith("tile ")]
+    assert len(tiles) == n_tiles
+    t_of = np.arange(T) // TILE[0]
+    h_of = np.arange(H) // TILE[1]
+    w_of = np.arange(W) // TILE[2]
+    for ln in tiles:
+        t, frames, rows, cols, tok, blocks = (int(x) for x in ln.split()[1:])
+        tt, rest = divmod(t, n[1] * n[2])
+        th, tw = divmod(rest, n[2])
+        assert (frames, rows, cols) == (int((t_of == tt).sum()), int((h_of == th).sum()),
+                                        int((w_of == tw).sum())), ln
+        assert tok == tokens[t], ln
+        # the window box of this query tile, placed by the oracle, in 64-token blocks
+        box = [(a, b, c) for a in range(oracle.window_start(tt, win[0], n[0]),
+                                         oracle.window_start(tt, win[0], n[0]) + win[0])
+               for b in range(oracle.window_start(th, win[1], n[1]),
+                              oracle.window_start(th, win[1], n[1]) + win[1])
+               for c in range(oracle.window_start(tw, win[2], n[2]),
+                              oracle.window_start(tw, win[2], n[2]) + win[2])]
+        ids = [(a * n[1] + b) * n[2] + c for a, b, c in box]
+        assert blocks == sum(-(-int(tokens[i]) // 64) for i in ids), ln
+        if n_tiles <= 40:
+            # the box is exactly the set of key tiles the oracle's mask reaches
+            assert sorted(ids) == oracle.key_tiles_of_query_tile(video, win, t), ln
+    grid = int(next(ln for ln in out if ln.startswith("grid ")).split()[1])
+    assert grid == sum(-(-int(x) // 64) for x in tokens)
+
+    # tile-major rows: tile t owns rows 384 t ..; its tokens come first, in raster
+    # order (frame, row, column), then padding (-1); text rows follow the video
+    t2r = np.array([int(x) for x in out[out.index(next(ln for ln in out if ln.startswith("grid "))) + 1:]])
+    assert len(t2r) == S_t
+    expect = np.full(S_t, -1, dtype=np.int64)
+    order = np.argsort(tile_of_row, kind="stable")  # raster order inside each tile
+    starts = np.concatenate([[0], np.cumsum(tokens)[:-1]])
+    rank = np.arange(nv) - starts[tile_of_row[order]]
+    expect[384 * tile_of_row[order] + rank] = order
+    if text:
+        expect[n_tiles * 384:] = nv + np.arange(256)
+    assert np.array_equal(t2r, expect)
