@@ -158,8 +158,8 @@ def sta_forward(dims: sta_dims, q, k, v, window_sizes, text_length: int, has_tex
     _check(code, "sta_forward")
 
 
-TIMED_EVENTS = 5
-STAGES = ("pack_v", "schedule_lists", "schedule_work", "attention")
+TIMED_EVENTS = 3
+STAGES = ("schedule_work", "attention")
 
 
 def sta_forward_timed(dims: sta_dims, q, k, v, window_sizes, text_length: int, has_text: bool,

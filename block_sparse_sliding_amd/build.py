@@ -35,9 +35,11 @@ HIPCC_FLAGS = [
 ]
 
 
-# The attention kernel never creates a NaN (padded text keys are masked to
-# -inf and zero-filled), so its max reductions need no NaN quieting.
-EXTRA_FLAGS = {"sta_attention.hip": ["-fno-honor-nans"]}
+# The attention kernel never creates a NaN (keys that must not contribute are
+# masked to -inf and read from a zero row), so its max reductions need no NaN
+# quieting. Its score MFMAs are selected in the VGPR form (the softmax reads
+# the scores from VGPRs); the P V accumulators are AGPRs, named by inline asm.
+EXTRA_FLAGS = {"sta_attention.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def _hipcc() -> str:

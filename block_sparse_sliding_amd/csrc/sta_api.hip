@@ -85,19 +85,18 @@ sta_status make_windows(const Geom& g, const int32_t* ws, Windows* win, int64_t*
   return STA_OK;
 }
 
+// Forward workspace: the work order (one int32 per query unit), the queue
+// heads and a zero row (the source of keys that must not contribute).
 struct Carve {
-  size_t vt, offsets, ids, work, claim, total;
+  size_t work, claim, zero_row, total;
 };
 
-Carve carve(const Geom& g, int64_t n_ids) {
+Carve carve(const Geom& g) {
   Carve c{};
-  const size_t tensor = size_t(g.B) * g.heads * g.S_t * g.D * 2;  // packed, tile-major
   size_t at = 0;
-  c.vt = at; at = align_up(at + tensor);
-  c.offsets = at; at = align_up(at + (size_t(g.heads) * g.n_q + 1) * 4);
-  c.ids = at; at = align_up(at + size_t(n_ids) * 4);
   c.work = at; at = align_up(at + size_t(g.B) * g.heads * g.n_q * 4);
   c.claim = at; at = align_up(at + size_t(sta::kClaimInts) * 4);
+  c.zero_row = at; at = align_up(at + size_t(sta::kZeroRowBytes));
   c.total = at;
   return c;
 }
@@ -148,7 +147,7 @@ size_t sta_workspace_bytes(const sta_dims* dims, const int32_t* window_sizes, in
   Windows win;
   int64_t n_ids = 0;
   if (make_windows(g, window_sizes, &win, &n_ids) != STA_OK) return 0;
-  return carve(g, n_ids).total;
+  return carve(g).total;
 }
 
 sta_status sta_schedule_sizes(const sta_dims* dims, const int32_t* window_sizes, int32_t has_text,
@@ -181,7 +180,7 @@ sta_status sta_build_schedule(const sta_dims* dims, const int32_t* window_sizes,
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   st = hip_status(sta::launch_schedule_lists(g, win, offsets, ids, s));
   if (st != STA_OK) return st;
-  return hip_status(sta::launch_schedule_work(g, win, work, nullptr, s));
+  return hip_status(sta::launch_schedule_work(g, win, work, nullptr, nullptr, s));
 }
 
 sta_status sta_tile_gather(const sta_dims* dims, int32_t has_text, const void* x_raster,
@@ -231,7 +230,7 @@ sta_status forward_impl(const sta_dims* dims, const void* q, const void* k, cons
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
       (lse != nullptr && !aligned16(lse)))
     return STA_ERR_ALIGN;
-  const Carve c = carve(g, n_ids);
+  const Carve c = carve(g);
   if (workspace == nullptr || workspace_bytes < c.total) return STA_ERR_WORKSPACE;
   if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return STA_ERR_ALIGN;
   const size_t tbytes = size_t(g.B) * g.heads * g.S * g.D * 2;
@@ -252,33 +251,23 @@ sta_status forward_impl(const sta_dims* dims, const void* q, const void* k, cons
   };
   st = mark(0);
   if (st != STA_OK) return st;
-  int32_t* offsets = reinterpret_cast<int32_t*>(ws + c.offsets);
-  int32_t* ids = reinterpret_cast<int32_t*>(ws + c.ids);
   int32_t* work = reinterpret_cast<int32_t*>(ws + c.work);
   int32_t* claim = reinterpret_cast<int32_t*>(ws + c.claim);
-
-  st = hip_status(sta::launch_pack_v(g, v, ws + c.vt, s));
+  st = hip_status(sta::launch_schedule_work(g, win, work, claim, ws + c.zero_row, s));
   if (st == STA_OK) st = mark(1);
-  if (st != STA_OK) return st;
-  st = hip_status(sta::launch_schedule_lists(g, win, offsets, ids, s));
-  if (st == STA_OK) st = mark(2);
-  if (st != STA_OK) return st;
-  st = hip_status(sta::launch_schedule_work(g, win, work, claim, s));
-  if (st == STA_OK) st = mark(3);
   if (st != STA_OK) return st;
   sta::FwdArgs a;
   a.q = q;
   a.k = k;
-  a.vt = ws + c.vt;
+  a.v = v;
   a.out = out;
   a.lse = lse;
-  a.offsets = offsets;
-  a.ids = ids;
   a.work = work;
   a.claim = claim;
+  a.zero_row = ws + c.zero_row;
   a.q_scale = float(1.4426950408889634 / std::sqrt(double(g.D)));  // log2(e)/sqrt(D)
   st = hip_status(sta::launch_attention(g, win, a, s));
-  if (st == STA_OK) st = mark(4);
+  if (st == STA_OK) st = mark(2);
   return st;
 }
 

@@ -1,78 +1,85 @@
-// Fused STA attention kernel for gfx950 (CDNA4): bf16 MFMA, fp32 online softmax.
+// Fused STA attention kernel for gfx950 (CDNA4): bf16 MFMA, fp32 softmax.
 //
 // What it computes (STA README, "Usage" and "Why is STA Fast?"): for every
 // query row, softmax(q k^T / sqrt(D)) v over the keys of whole key tiles in the
 // query tile's window, followed by the valid text keys. Because every
 // (query tile, key tile) block is fully on or fully off, video blocks need no
 // per-element mask; only the last text block is masked, and only when the text
-// length is not a multiple of 64.
+// length is not a multiple of 64 (and, for video sizes that are not tile
+// multiples, the last block of a partial key tile).
 //
-// Work decomposition. A workgroup works on one query unit at a time: a
-// 384-row query tile, 8 waves of 48 rows each (three 16-row column groups),
-// or the 256 text query slots of one head, 8 waves of 32 rows each; two waves
-// per SIMD, one workgroup per CU. The grid is persistent (one workgroup per
-// resident slot): each workgroup pops units from the queue of the XCD it runs
-// on and, once that queue is empty, from the other XCDs' queues, so the split
-// of work between XCDs follows their actual clocks (which differ by several
-// percent under load) instead of being fixed at launch. Q rows are read from
-// the caller's raster q through the tile map, and O / lse are written back to
-// raster positions. Keys stream in 64-key blocks into LDS with LDS-DMA loads,
-// double buffered, one barrier per block: K straight from the caller's raster
-// k (each lane supplies its own source address, which applies the tile map),
-// V as packed V^T fragments (one contiguous 16 KB run per block at D = 128,
-// written by the pack kernel). The next block's loads are issued once the
-// current block's score MFMAs are under way.
+// Work decomposition. A workgroup of 4 waves (one per SIMD) works on one query
+// unit at a time: a 384-row query tile (96 rows per wave), or the 256 text
+// query slots of one head (64 rows per wave). The grid is persistent: each
+// workgroup pops units from the queue of the XCD it runs on and, once that
+// queue is empty, from the other XCDs' queues. The key tiles of a unit's
+// window are enumerated in the kernel (residue order, see key_tile), so no
+// schedule list is read. Q rows are read from the caller's raster q through
+// the tile map, K and V rows from the caller's raster k and v (LDS-DMA, one
+// source address per lane, which applies the tile map), and O / lse are
+// written to raster positions.
 //
-// LDS layout of a K block (64 rows of D bf16). Each 1 KB LDS-DMA transfer
-// fills one group of 1024 / (2D) consecutive rows. Inside a group the rows
-// are interleaved at 64-byte granularity: quad k (16-byte chunks 4k..4k+3) of
-// every row of the group, then quad k + 1, and so on; within a quad, chunk j
-// of row r sits at position j XOR (2 * bit 3 of r). Every read address is one
-// per-lane base plus compile-time offsets. gfx950 serves a ds_read_b128 in
-// four LDS cycles of 16 lanes each, lane l in cycle (bit 5 of l, parity of
-// bits 2..4 of l) (measured with the LDS bank-conflict counter); with this
-// permutation the 16 lanes of every cycle of a K fragment read (16 rows x one
-// chunk) cover all 64 banks, for D = 128 and D = 64 alike. Without it, or
-// with a permutation that ignores that lane grouping, two lanes of each cycle
-// share banks and every K fragment read takes 8 LDS cycles instead of 4.
+// Products: v_mfma_f32_32x32x16_bf16 throughout.
+//   S^T = K Q^T    A = K fragment (lane l: key 32h + l%32, d 16ks + 8(l/32)
+//                  .. +8), B = Q^T fragment (registers, loaded once per unit).
+//                  Lane l then holds the scores of query l%32 for keys
+//                  8(i/4) + 4(l/32) + i%4, i = 0..15, of each 32-key half.
+//   O^T += V^T P^T A = V^T fragment read with ds_read_b64_tr_b16 from V rows
+//                  in LDS (the transposing read turns 4 keys x 16 columns of
+//                  row-major V into the k-contiguous operand), B = P^T from
+//                  the lane's own registers: the 16 scores of a half are two
+//                  16-key chunks in exactly the key order the A operand uses.
+//                  The accumulators live in AGPRs (inline-asm MFMAs with "+a"
+//                  operands); the score MFMAs write VGPRs.
 //
-// Per block and wave, with v_mfma_f32_16x16x32_bf16:
-//   S^T = K Q^T   A = K fragment (lane l holds K[16kt + l%16][32ks + 8(l/16)
-//                 .. +8]), B = Q^T fragment (registers, loaded once per unit),
-//                 fp32 accumulation of the exact bf16 products. Lane l then
-//                 holds the scores of query l%16 for keys 4(l/16) + r of each
-//                 16-key group.
-//   softmax       p = 2^(c s - m) with c = log2(e)/sqrt(D) applied in fp32
-//                 (one v_fma_f32 and one v_exp_f32 per score; folding c into
-//                 a bf16 operand instead would round it and cost accuracy at
-//                 large logits), m the running reference in log2 units. The
-//                 reference only moves when some scaled score exceeds it by
-//                 more than kRescaleSlack (a per-lane v_max3 check and a
-//                 ballot); then the accumulator and row sums are rescaled.
-//                 The first block sets the reference from its exact row max.
-//                 Any reference gives the same softmax; the slack bounds p by
-//                 2^slack.
-//   O^T += V^T P^T  A = packed V^T fragment (one ds_read_b128; its key order
-//                 matches the accumulator layout of S^T), B = P^T from the
-//                 lane's own registers after bf16 rounding. The row sums
-//                 accumulate the same rounded p with v_dot2_f32_bf16.
-// Text rows at or after text_length only ever appear in the last text block:
-// their scores are replaced by -inf (a select, so whatever k holds there is
-// ignored) and their packed V rows are zeros.
-// Video sizes that are not tile multiples (the PAD instantiation): the last
-// tile along an axis holds the remainder, and a partial key tile streams
-// ceil(tokens / 64) blocks of its existing tokens in compact order (frame,
-// row, column; the packed V^T uses the same order). In the last block, keys
-// past the tile's tokens are fetched from the last token that exists (every
-// source address stays inside the video), their scores are replaced by -inf
-// and their packed V rows are zeros. A
-// video unit's rows are its tile's existing tokens in compact order (frame,
-// row, column; a partial tile of at most 128, 192 or 256 tokens runs with
-// 8 waves x 16 rows, 4 waves x 48 or 8 waves x 32; a wave whose rows all lie
-// past the tokens only loads and synchronises);
-// rows past them compute on a valid row and are not written. The first block
-// of every window is frame 0 of an existing tile, so the running max is
-// finite from the first block on.
+// Software pipeline. Each 64-key block is two 32-key halves; half-step hh
+// issues, for all 96 rows of the wave, the score MFMAs of half hh + 1 and the
+// P V MFMAs of half hh - 1, and between consecutive MFMAs one slice of the
+// softmax of half hh: p = 2^(c s - m) (one v_fma_f32, one v_exp_f32), pairs
+// rounded to bf16 (v_cvt_pk_bf16_f32, the P operand) and summed into the row
+// sum (v_dot2_f32_bf16 with ones). The fma, exp and pack of one score sit in
+// three consecutive MFMA slots, so no VALU instruction waits on the one
+// before it; one wave per SIMD then keeps the matrix core busy while it
+// issues the softmax. K and V each have two LDS stages; the K stream runs one
+// block ahead of the V stream, and one barrier per block orders the LDS-DMA
+// writes against the reads.
+//
+// Softmax reference. The reference m of a row is the exact maximum of its
+// scaled scores over the first 32 keys of the unit, and it never moves:
+// p = 2^(c s - m) stays within fp32 as long as no later score exceeds m by
+// about 127 (log2 units). At the end of a unit, a row whose sum of p reaches
+// 2^32 (some later key scored at least 32 above the first half's maximum)
+// makes the workgroup redo the unit with m set to the row's maximum over all
+// its keys, found by a pass that computes only the scores. With random data
+// the redo never happens; large score jumps between key tiles trigger it.
+//
+// LDS layouts (row-major rows of D bf16 = 2D bytes, grouped by 1 KB: RPG rows
+// per group, 4 for D = 128 and 8 for D = 64; a group is one LDS-DMA
+// instruction). Inside a group, 16-byte chunk c of group row rr sits at
+// (c / 4) * RPG * 64 + rr * 64 + 16 * (c % 4) for V, and at the same place
+// with c % 4 replaced by (c % 4) XOR ((row / 4) % 4) for K. A score-MFMA K
+// read (16 lanes per LDS cycle, rows {0-3, 12-15, 20-23, 24-27} or the other
+// parity class, one chunk) then covers all 64 banks, and so does a V^T
+// transposing read (4 rows x 64 bytes per 32 lanes); every read address is one
+// of a few per-lane bases plus a compile-time offset.
+//
+// Masking. Keys that must not contribute (text slots at or after text_length;
+// with PAD, keys past a partial tile's tokens) are fetched from a zero row in
+// the workspace, K and V alike, and their scores are replaced by -inf before
+// the exponential; their p is exactly 0 and their V rows are zeros, so the
+// contents of padded text slots never reach a result.
+//
+// Video sizes that are not tile multiples (PAD): the last tile along an axis
+// holds the remainder. A partial key tile streams ceil(tokens / 64) blocks of
+// its existing tokens in compact order (frame, row, column); its full blocks
+// take their place in the walk, and its last, partial block is deferred to a
+// tail of masked blocks after all whole ones (KeyStream), so the main loop
+// runs the unmasked half-steps only and the masked variant appears in the
+// tail alone (one loop holding both would exceed the register file). A video unit's
+// rows are its tile's existing tokens in compact order; a tile of at most 128
+// or 256 tokens runs with 32 or 64 rows per wave, and a wave whose rows all lie
+// past the tokens only loads and synchronises. Rows past the tokens compute on
+// a valid row and are not written.
 // Epilogue: O = O^T / l rounded to bf16, lse = (m + log2 l) * ln 2, at raster rows.
 #include <type_traits>
 
@@ -82,447 +89,616 @@
 namespace sta {
 namespace {
 
-constexpr int kWaves = 8;
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+constexpr int kWaves = 4;  // one wave per SIMD
 constexpr int kThreads = kWaves * 64;
-constexpr int kRowsPerWave = kUnitRows / kWaves;  // 48
-constexpr int kQT = kRowsPerWave / 16;            // 3 query column groups per wave
-constexpr float kRescaleSlack = 8.0f;             // log2 units
-constexpr int kKPrefetch = 4;                     // K fragments in flight in the score loop
 constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kRedoSum = 4294967296.0f;  // 2^32: a row sum this large redoes the unit
 
 struct KernelArgs {
   Geom g;
   FwdArgs a;
-  Windows win;  // read by the PAD instantiation only
+  Windows win;
 };
 
-// The kernel arguments seen through an opaque copy of the kernarg pointer:
-// loads through it cannot be hoisted out of the unit loop, so the per-unit
-// code reads them again (scalar loads) instead of keeping them all live in
-// SGPRs across the loop.
+// The kernel arguments through an opaque copy of the kernarg pointer: loads
+// through it are not hoisted out of the unit loop.
 __device__ inline const KernelArgs* kernel_args() {
   auto kp = (const __attribute__((address_space(4))) KernelArgs*)__builtin_amdgcn_kernarg_segment_ptr();
   asm volatile("" : "+s"(kp));
   return (const KernelArgs*)kp;
 }
 
+// O^T += V^T P^T on AGPR accumulators (the compiler's hazard checks do not see
+// inline asm: every VGPR this reads was written at least two instructions
+// earlier, see the slot order, and the accumulators are read only after an
+// explicit wait).
+// (The host pass of this single-source file checks asm constraints against
+// the host target, where "a" means a general register: the statements exist
+// in the device pass only.)
+#if defined(__HIP_DEVICE_COMPILE__)
+#define STA_PV_MFMA_ASM(NOP, acc, vf, pf) \
+  asm volatile(NOP "v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(vf), "v"(pf))
+#else
+#define STA_PV_MFMA_ASM(NOP, acc, vf, pf) ((void)(acc), (void)(vf), (void)(pf))
+#endif
+#define STA_PV_MFMA(acc, vf, pf) STA_PV_MFMA_ASM("", acc, vf, pf)
+
+// LDS-DMA of 16 bytes per lane from base + soff (wave-uniform) + voff (per
+// lane) into lds_dst + 16 lane, through a buffer resource over base (the
+// uniform part stays in a scalar register). (The buffer-resource type exists
+// in the device pass only.)
+__device__ inline void dma16_buf(const char* base, int voff, int soff, char* lds_dst) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, 0x7fffffff, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_dst, 16, voff, soff, 0, 0);
+#endif
+}
+
+template <int D>
+struct Lay {
+  static constexpr int ROWB = 2 * D;        // bytes per row
+  static constexpr int RPG = 1024 / ROWB;   // rows per 1 KB group
+  static constexpr int KS = D / 16;         // k-steps of the score MFMAs
+  static constexpr int DT = D / 32;         // 32-column tiles of O
+  static constexpr int BLKB = 64 * ROWB;    // bytes of a 64-row K or V block
+  static constexpr int GPB = 64 / RPG;      // 1 KB groups per block
+  static constexpr int GPW = GPB / kWaves;  // groups per wave
+  static constexpr int NVF = 2 * DT;        // V^T fragments per half (2 chunks of 16 keys x DT)
+  static constexpr int NF = NVF + KS;       // fragments per half-step
+  static constexpr int SPS = 16 / NF;       // scores (per lane and query group) per MFMA slot
+  static constexpr int QSEG = RPG * 64;     // bytes between chunk quads inside a group
+  static_assert(GPW >= 1 && GPB % kWaves == 0, "groups split evenly over the waves");
+};
+
 template <int D, bool PAD>
 __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(KernelArgs) {
-  constexpr int KS = D / 32;                // k-steps of S^T
-  constexpr int DT = D / 16;                // d groups of O^T
-  constexpr int ROWB = D * 2;               // bytes per K row
-  constexpr int BLK = kKeyBlock * ROWB;     // bytes of one K (or V^T) block
-  constexpr int RPI = 1024 / ROWB;          // K rows per 1 KB LDS-DMA instruction
-  constexpr int IPW = BLK / 1024 / kWaves;  // DMA instructions per wave per tensor
-  constexpr int BPT = kTileRows / kKeyBlock;  // key blocks per tile (6)
-  static_assert(IPW >= 1 && BLK % (1024 * kWaves) == 0, "block must split over the waves");
-  __shared__ __attribute__((aligned(1024))) char lds[2][2][BLK];  // [stage][K|V]
+  using L = Lay<D>;
+  constexpr int ROWB = L::ROWB, RPG = L::RPG, KS = L::KS, DT = L::DT, BLKB = L::BLKB;
+  // K stages at [0, 2 BLKB), V stages at [2 BLKB, 5 BLKB)
+  __shared__ __attribute__((aligned(1024))) char lds[5 * BLKB];
+  __shared__ int shared_word[2];
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  __shared__ int claimed;
   for (;;) {
-  // The previous unit's last LDS reads are behind the body's barriers; this
-  // barrier orders the claim (and the next unit's first LDS-DMA writes)
-  // after all of them.
-  if (threadIdx.x == 0) {
+    // the previous unit's LDS reads are behind its barriers; this barrier
+    // orders the claim (and the next unit's first LDS-DMA writes) after them
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const KernelArgs* ka = kernel_args();
+      unsigned xcc;
+      asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+      shared_word[0] = claim_unit(ka->a.work, ka->a.claim, ka->g.B * ka->g.heads * ka->g.n_q, int(xcc));
+      shared_word[1] = 0;
+    }
+    __syncthreads();
+    const int unit = __builtin_amdgcn_readfirstlane(shared_word[0]);
+    if (unit < 0) break;
+    int lane = threadIdx.x & 63;
+    asm volatile("" : "+v"(lane));  // lane-derived values are rebuilt per unit
+    const int this_lane = lane;
     const KernelArgs* ka = kernel_args();
-    unsigned xcc;
-    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
-    claimed = claim_unit(ka->a.work, ka->a.claim, ka->g.B * ka->g.heads * ka->g.n_q, int(xcc));
-  }
-  __syncthreads();
-  const int unit = __builtin_amdgcn_readfirstlane(claimed);
-  if (unit < 0) break;
-  int lane = threadIdx.x & 63;
-  asm volatile("" : "+v"(lane));  // lane-derived offsets are rebuilt per unit, not kept live
-  const int this_lane = lane;
-  const KernelArgs* ka = kernel_args();
-  const Geom g = ka->g;
-  const FwdArgs a = ka->a;
-  const int u = unit % g.n_q;
-  const int bh = unit / g.n_q;
-  const int hd = bh % g.heads;
-  const bool text_unit = g.has_text && u == g.n_tiles;
-  const int q_row0 = text_unit ? g.n_vt : u * kTileRows;  // tile-major
-  int q_rows = text_unit ? kTextSlots : kTileRows;
-  // PAD: the rows of a video unit are the existing tokens of its tile in
-  // compact order (frame, row, column), so a partial tile runs as a unit of
-  // 128, 192, 256 or 384 rows (the shapes are chosen below)
-  int q_ext = kFullExtent, q_base = 0;  // extent and raster origin of the query tile
-  if constexpr (PAD) {
+    const Geom g = ka->g;
+    const FwdArgs a = ka->a;
+    const int u = unit % g.n_q;
+    const int bh = unit / g.n_q;
+    const int hd = bh % g.heads;
+    const uint32_t wp = ka->win.w[hd];
+    const bool text_unit = g.has_text && u == g.n_tiles;
+
+    // query tile coordinates and rows (PAD: its existing tokens, compact order)
+    int qtt = 0, qth = 0, qtw = 0;
+    int q_ext = kFullExtent, q_base = 0;
+    int q_rows = text_unit ? kTextSlots : kTileRows;
     if (!text_unit) {
       const int rest = div_by(u, g.nw, g.mag_nw);
-      const int tw = u - rest * g.nw;
-      const int tt = div_by(rest, g.nh, g.mag_nh);
-      const int th = rest - tt * g.nh;
-      q_ext = tile_extent(tt, th, tw, g);
-      q_rows = extent_tokens(q_ext);
-      q_base = (tt * kTileT * g.H + th * kTileH) * g.W + tw * kTileW;
-    }
-  }
-  // raster row of unit row `row` (< q_rows)
-  auto query_raster = [&](int row) {
-    if constexpr (PAD) {
-      if (!text_unit) {
-        int dt, dh, dw;
-        compact_token(row, q_ext, dt, dh, dw);
-        return q_base + (dt * g.H + dh) * g.W + dw;
-      }
-    }
-    return PAD ? tiled_to_raster(q_row0 + row, g) : tiled_to_raster_full(q_row0 + row, g);
-  };
-  const size_t slab = size_t(bh) * g.S * D;      // element offset of this (b, head), raster
-  const size_t slab_t = size_t(bh) * g.S_t * D;  // the same in the packed tile-major V^T
-
-  const __bf16* __restrict__ qr = reinterpret_cast<const __bf16*>(a.q) + slab;
-  const char* __restrict__ kr = reinterpret_cast<const char*>(a.k) + slab * 2;
-  const char* __restrict__ vtr = reinterpret_cast<const char*>(a.vt) + slab_t * 2;
-
-  const int l0 = a.offsets[hd * g.n_q + u];
-  const int l1 = a.offsets[hd * g.n_q + u + 1];
-  // video key blocks: six per listed tile; with PAD, ceil(tokens / 64) per
-  // tile, its existing tokens in compact order, summed over the unit's list:
-  // the query tile's window (a box of tiles) or, for the text unit, the grid
-  int n_vid = (l1 - l0) * BPT;
-  if constexpr (PAD) {
-    if (text_unit) {
-      n_vid = box_blocks(0, g.nt, 0, g.nh, 0, g.nw, g);
-    } else {
-      const uint32_t p = ka->win.w[hd];
-      const int rest = div_by(u, g.nw, g.mag_nw);
-      const int tt = div_by(rest, g.nh, g.mag_nh);
-      const int th = rest - tt * g.nh, tw = u - rest * g.nw;
-      n_vid = box_blocks(window_start(tt, win_t(p), g.nt), win_t(p), window_start(th, win_h(p), g.nh),
-                         win_h(p), window_start(tw, win_w(p), g.nw), win_w(p), g);
-    }
-  }
-  const int text_len = g.has_text ? g.text_length : 0;
-  const int n_blk = n_vid + (text_len + kKeyBlock - 1) / kKeyBlock;
-  const bool ragged = (text_len % kKeyBlock) != 0;
-
-  // Chunk permutation of K row r inside its 64-byte quad (see the layout above).
-  auto sw = [](int row) { return (row >> 2) & 2; };
-
-  // The schedule is read through the scalar cache (it is never written while
-  // this kernel runs). Key blocks of one tile are consecutive.
-  const __attribute__((address_space(4))) int32_t* ids =
-      (const __attribute__((address_space(4))) int32_t*)(a.ids + l0);
-
-  // Source rows of key block j (blocks are fetched in order 0, 1, 2, ...; the
-  // six blocks of a tile are its six frames, so a tile is decoded once, at its
-  // first block): kbase = raster row of the block's 8x8 (h, w) patch origin
-  // (video) or first slot (text), krs = raster stride between its 8-row
-  // runs, vrow = its first tile-major row (the packed V^T block). With PAD,
-  // tile_ext is the packed extent of the current tile (the frames, rows and
-  // columns that exist); a tile with only frames missing still has one frame
-  // per block, otherwise a block is 64 tokens in compact order (issue_k).
-  int tile_kbase = 0, tile_vrow = 0;
-  int tile_ext = kFullExtent;  // PAD: packed extent of the current tile
-  // PAD: blocks walk the blocks of each listed tile in turn (block j + 1 is
-  // always decoded right after block j): cur_t is the next list entry,
-  // cur_sub the block within its tile of the last decoded block
-  int cur_t = 0, cur_sub = -1;
-  auto block_rows = [&](int j, int& kbase, int& krs, int& vrow) {
-    if (j < n_vid) {
-      int t, sub;
+      qtw = u - rest * g.nw;
+      qtt = div_by(rest, g.nh, g.mag_nh);
+      qth = rest - qtt * g.nh;
+      q_base = (qtt * kTileT * g.H + qth * kTileH) * g.W + qtw * kTileW;
       if constexpr (PAD) {
-        sub = cur_sub + 1;
-        if (j == 0 || sub * kKeyBlock >= extent_tokens(tile_ext)) {
-          sub = 0;
-          t = cur_t++;
-        }
-        cur_sub = sub;
-      } else {
-        t = j / BPT;
-        sub = j - t * BPT;
+        q_ext = tile_extent(qtt, qth, qtw, g);
+        q_rows = extent_tokens(q_ext);
       }
-      if (sub == 0) {
-        const int tile = ids[t];
-        const int rest = div_by(tile, g.nw, g.mag_nw);
-        const int tw = tile - rest * g.nw;
-        const int tt = div_by(rest, g.nh, g.mag_nh);
-        const int th = rest - tt * g.nh;
-        tile_kbase = (tt * kTileT * g.H + th * kTileH) * g.W + tw * kTileW;
-        tile_vrow = tile * kTileRows;
-        if constexpr (PAD) tile_ext = tile_extent(tt, th, tw, g);
-      }
-      kbase = tile_kbase + sub * g.H * g.W;
-      krs = g.W;
-      vrow = tile_vrow + sub * kKeyBlock;
-    } else {
-      kbase = g.n_video + (j - n_vid) * kKeyBlock;
-      vrow = g.n_vt + (j - n_vid) * kKeyBlock;
-      krs = kTileW;
-      if constexpr (PAD) tile_ext = kFullExtent;
     }
-  };
+    // raster row of unit row `row` (< q_rows)
+    auto query_raster = [&](int row) {
+      if (text_unit) return g.n_video + row;
+      int dt, dh, dw;
+      if constexpr (PAD) {
+        compact_token(row, q_ext, dt, dh, dw);
+      } else {
+        dt = row >> 6;
+        dh = (row >> 3) & 7;
+        dw = row & 7;
+      }
+      return q_base + (dt * g.H + dh) * g.W + dw;
+    };
 
-  // Fetch K block j into LDS stage st. Row rr of the block is raster row
-  // kbase + (rr/8)*krs + rr%8. Each DMA instruction covers RPI rows that
-  // share rr/8, so its source is a wave-uniform row pointer plus a per-lane
-  // offset (row within the group, chunk) that is the same for every block.
-  auto issue_k = [&](int st, int kbase, int krs) {
-    // PAD: per-lane offsets come from a fresh opaque copy of the lane id, so
-    // they are rebuilt per block rather than hoisted (and spilled) as 64-bit
-    // addresses
-    int lane = opaque_lane<PAD>(this_lane);
-    if constexpr (PAD) {
-      if ((tile_ext >> 8) != (kFullExtent >> 8)) {
-        // a tile with missing rows or columns: block row r is token 64 sub + r
-        // of the tile in compact order, clamped to the last one that exists
-        const int last = extent_tokens(tile_ext) - 1;
+    // key blocks: the window of the query tile, or every tile for the text unit
+    const int wt = win_t(wp), wh = win_h(wp), ww = win_w(wp);
+    KeyStream<PAD> keys;
+    if (text_unit)
+      keys.init(g, 0, g.nt, 0, g.nh, 0, g.nw);
+    else
+      keys.init(g, window_start(qtt, wt, g.nt), wt, window_start(qth, wh, g.nh), wh, window_start(qtw, ww, g.nw), ww);
+    const int n_plain = keys.n_plain, n_blk = keys.n_blk;
+
+    const size_t slab = size_t(bh) * g.S * D;
+    const char* __restrict__ kr = reinterpret_cast<const char*>(a.k) + slab * 2;
+    const char* __restrict__ vr = reinterpret_cast<const char*>(a.v) + slab * 2;
+    const char* __restrict__ zr = reinterpret_cast<const char*>(a.zero_row);
+
+    auto decode = [&](int j) { return keys.block(g, j); };
+    auto reset_walk = [&]() { keys.reset(); };
+
+    // ---- LDS-DMA of one block (this wave's GPW groups). Lane p of a group
+    // covers group row rr = (p / 4) % RPG and chunk 4 (p / (4 RPG)) + p % 4,
+    // XOR-ed with the row's (row / 4) % 4 for K. The source of a full frame's
+    // rows (the common case) is a wave-uniform row pointer plus a per-lane
+    // offset; text rows past the valid length and, with PAD, keys past a
+    // partial tile's tokens come from the zero row.
+    auto issue = [&](const KeyBlock& s, int stage_off, bool is_k) {
+      const int ln = opaque_lane<true>(this_lane);
+      const int rr = (ln >> 2) % RPG, j4 = ln & 3, q4 = 4 * (ln / (4 * RPG));
+      const char* base = is_k ? kr : vr;
+      char* dst = lds + stage_off + wave * L::GPW * 1024;
+      auto chunk = [&](int G) {  // this lane's chunk for group G
+        const int x = ((G * RPG + rr) >> 2) & 3;
+        return q4 + (is_k ? (j4 ^ x) : j4);
+      };
+      if (s.kind == 0) {
 #pragma unroll
-        for (int i = 0; i < IPW; ++i) {
-          const int q = wave * IPW + i;
-          const int rin = (lane >> 2) % RPI;
+        for (int i = 0; i < L::GPW; ++i) {
+          const int G = wave * L::GPW + i, r0 = G * RPG;
+          // rows r0 .. r0 + RPG - 1 lie in one 8-row run of the frame
+          const int row0 = s.base + (r0 >> 3) * g.W + (r0 & 7);
+          dma16_buf(base, rr * ROWB + chunk(G) * 16, row0 * ROWB, dst + i * 1024);
+        }
+      } else if (!PAD || s.kind == 1) {
+#pragma unroll
+        for (int i = 0; i < L::GPW; ++i) {
+          const int G = wave * L::GPW + i, r = G * RPG + rr;
+          const char* src = r < s.lim ? base + size_t(s.base + r) * ROWB : zr;
+          dma16(src + chunk(G) * 16, dst + i * 1024);
+        }
+      } else {
+        const int n_tok = extent_tokens(s.ext);
+#pragma unroll
+        for (int i = 0; i < L::GPW; ++i) {
+          const int G = wave * L::GPW + i, tok = s.sub * kKeyBlock + G * RPG + rr;
           int dt, dh, dw;
-          compact_token(min(cur_sub * kKeyBlock + q * RPI + rin, last), tile_ext, dt, dh, dw);
-          const int row = tile_kbase + (dt * g.H + dh) * g.W + dw;
-          const int chunk = 4 * (lane / (4 * RPI)) + ((lane & 3) ^ sw(q * RPI + rin));
-          dma16(kr + size_t(row) * ROWB + chunk * 16, &lds[st][0][q * 1024]);
+          compact_token(tok < n_tok ? tok : 0, s.ext, dt, dh, dw);
+          const char* src = tok < n_tok ? base + size_t(s.base + (dt * g.H + dh) * g.W + dw) * ROWB : zr;
+          dma16(src + chunk(G) * 16, dst + i * 1024);
+        }
+      }
+    };
+
+    // ---- per-lane LDS read bases
+    const int kl = lane & 31, kx = (kl >> 2) & 3;
+    const int k_lane = (kl / RPG) * 1024 + (kl % RPG) * 64;
+    const int kb_even = k_lane + (((lane >> 5)) ^ kx) * 16;
+    const int kb_odd = k_lane + ((2 | (lane >> 5)) ^ kx) * 16;
+    const int vi = lane & 15;
+    const int vrow = 4 * (lane >> 5) + (vi >> 2);  // row inside a 16-key chunk
+    const int vb = 2 * BLKB + (vrow / RPG) * 1024 + (vrow % RPG) * 64 + 32 * ((lane >> 4) & 1) + 8 * (vi & 1) +
+                   16 * ((vi & 3) >> 1);
+    const char* lds_ke = lds + kb_even;
+    const char* lds_ko = lds + kb_odd;
+    const char* lds_v = lds + vb;
+
+    const float qs = a.q_scale;  // log2(e)/sqrt(D)
+    const bf16x2 ones2 = {(__bf16)1.0f, (__bf16)1.0f};
+
+    // The rest runs with QG query groups of 32 rows per wave: 3 for a video
+    // tile, 2 for the text slots (and partial tiles of 129..256 tokens), 1 for
+    // partial tiles of at most 128 tokens.
+    auto run = [&](auto qg_c) {
+      constexpr int QG = decltype(qg_c)::value;
+      constexpr int RPW = 32 * QG;
+      constexpr int NF = L::NF, NVF = L::NVF, SPS = L::SPS;
+      constexpr int SLOTS = NF * QG;  // MFMAs per half-step
+      constexpr int NSC = 16 * QG;    // scores per lane per half-step
+      const bool active = wave * RPW < q_rows;
+      (void)active;
+
+      // Q^T fragments: lane l, group c, step ks: row 32 c + l % 32 of this wave,
+      // columns 16 ks + 8 (l / 32) .. + 8 (rows past the unit clamp to its last)
+      bf16x8 qf[QG][KS];
+#pragma unroll
+      for (int c = 0; c < QG; ++c) {
+        int row = wave * RPW + 32 * c + (lane & 31);
+        row = row < q_rows ? row : q_rows - 1;
+        const __bf16* src = reinterpret_cast<const __bf16*>(a.q) + slab + size_t(query_raster(row)) * D +
+                            8 * (lane >> 5);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) qf[c][ks] = *reinterpret_cast<const bf16x8*>(src + 16 * ks);
+      }
+
+      f32x16 acc[QG][DT];
+      float lsum[QG], m_run[QG];
+
+      // K fragment ks of K half kh in K stage kst (compile-time offsets when
+      // the stage is)
+      auto kfrag = [&](int kst, int kh, int ks) -> bf16x8 {
+        return *reinterpret_cast<const bf16x8*>(((ks & 1) ? lds_ko : lds_ke) + kst * BLKB + (32 * kh) / RPG * 1024 +
+                                                (ks >> 1) * L::QSEG);
+      };
+      // V^T fragment f (chunk f / DT, tile f % DT) of V half vh at V offset voff
+      auto vfrag_at = [&](int voff, int vh, int f) -> bf16x8 {
+        const int kc = f / DT, dt = f % DT;
+        const char* p = lds_v + voff + (32 * vh + 16 * kc) / RPG * 1024 + dt * L::QSEG;
+        const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+        const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 8 / RPG * 1024));
+        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+      };
+
+      // softmax pipeline state: t = c s - m of the last scores (stage A),
+      // e = exponentials by group and element parity (stage B)
+      float vt[2 * SPS];
+      float ve[QG][2];
+      // slot k, stage A of scores SPS k .. SPS k + SPS - 1, B of the SPS
+      // before, C (pack + row sum) of those before that; score sc is element
+      // i = sc / QG of group c = sc % QG
+      auto vstage = [&](int k, f32x16 (&s)[QG], uint32_t (&pw)[QG][8], bool do_a, bool do_mask, int lim_lane) {
+#pragma unroll
+        for (int x = 0; x < SPS; ++x) {
+          const int c2 = SPS * (k - 2) + x;  // stage C
+          if (c2 >= 0 && c2 < NSC && ((c2 / QG) & 1)) {
+            const int c = c2 % QG, i = c2 / QG;
+            const bf16x2 pr = __builtin_convertvector((f32x2){ve[c][0], ve[c][1]}, bf16x2);
+            lsum[c] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones2, lsum[c], false);
+            pw[c][i >> 1] = __builtin_bit_cast(uint32_t, pr);
+          }
+        }
+#pragma unroll
+        for (int x = 0; x < SPS; ++x) {
+          const int b1 = SPS * (k - 1) + x;  // stage B
+          if (b1 >= 0 && b1 < NSC) ve[b1 % QG][(b1 / QG) & 1] = __builtin_amdgcn_exp2f(vt[b1 % (2 * SPS)]);
+        }
+        if (do_a) {
+#pragma unroll
+          for (int x = 0; x < SPS; ++x) {
+            const int a0 = SPS * k + x;  // stage A
+            const int i = a0 / QG;
+            const float t = __builtin_fmaf(s[a0 % QG][i], qs, -m_run[a0 % QG]);
+            // masked half: key 8 (i / 4) + 4 (l / 32) + i % 4 at or past the limit
+            vt[a0 % (2 * SPS)] = (do_mask && 8 * (i >> 2) + (i & 3) >= lim_lane) ? -INFINITY : t;
+          }
+        }
+      };
+
+      // One half-step: SLOTS MFMA slots over NF fragments x QG groups.
+      // Fragment f + PF is read when fragment f is first used; V^T fragments
+      // of the next half-step are read during the last slots. Scores of
+      // s_cur pass through the softmax stages, one group of SPS per slot; the
+      // last scores' B and C stages run in the first slots of the next
+      // half-step (carried through vt / ve). DO_S, DO_PV, DO_P: whether the
+      // step scores the next half, multiplies the previous half's P by V, and
+      // has scores of its own. voff / nvoff: byte offsets of the V stages of
+      // this step's and the next step's P V; kst: K stage of the next half.
+      constexpr int PF = 3;
+      auto step = [&](auto do_s_c, auto do_pv_c, auto do_p_c, auto do_mask_c, auto kst, int voff, int vh, int kh,
+                      int nvoff, int nvh, int lim, bf16x8 (&fr)[PF], f32x16 (&s_next)[QG], f32x16 (&s_cur)[QG],
+                      uint32_t (&p_prev)[QG][8], uint32_t (&p_cur)[QG][8]) {
+        constexpr bool DO_S = decltype(do_s_c)::value, DO_PV = decltype(do_pv_c)::value;
+        constexpr bool DO_P = decltype(do_p_c)::value, DO_MASK = decltype(do_mask_c)::value;
+        const int KST = kst;
+        // masked half: this lane's keys 8 (i / 4) + 4 (l / 32) + i % 4 at or past lim are dead
+        const int lim_lane = lim - 4 * (lane >> 5);
+        // opaque stage offsets (32-bit LDS byte offsets): every V^T read is
+        // one of them plus an immediate
+        int vcur = vb + voff + (32 * vh) / RPG * 1024;
+        int vnext = vb + nvoff + (32 * nvh) / RPG * 1024;
+        asm volatile("" : "+v"(vcur), "+v"(vnext));
+        auto vfrag = [&](int vb0, int f) -> bf16x8 {
+          const int kc = f / DT, dt = f % DT;
+          const char* p = lds + vb0 + (16 * kc) / RPG * 1024 + dt * L::QSEG;
+          const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+          const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 8 / RPG * 1024));
+          return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+        };
+        bf16x8 ring[NF + PF];
+#pragma unroll
+        for (int i = 0; i < PF; ++i) ring[i] = fr[i];
+#pragma unroll
+        for (int k = 0; k < SLOTS; ++k) {
+          const int f = k / QG, c = k % QG;
+          if (c == 0) {
+            const int nf = f + PF;
+            if (nf < NVF) {
+              if (DO_PV) ring[nf] = vfrag(vcur, nf);
+            } else if (nf < NF) {
+              if (DO_S) ring[nf] = kfrag(KST, kh, nf - NVF);
+            } else {
+              ring[nf] = vfrag(vnext, nf - NF);  // next half-step's V^T
+            }
+          }
+          if (f < NVF) {
+            if constexpr (DO_PV) {
+              const int kc = f / DT, dt = f % DT;
+              const bf16x8 pb = __builtin_bit_cast(
+                  bf16x8, (uint4){p_prev[c][4 * kc], p_prev[c][4 * kc + 1], p_prev[c][4 * kc + 2], p_prev[c][4 * kc + 3]});
+              if (kc == 1 && dt == 0)  // its last dwords may have been packed in slot 0 or 1
+                STA_PV_MFMA_ASM("s_nop 1\n\t", acc[c][dt], ring[f], pb);
+              else
+                STA_PV_MFMA(acc[c][dt], ring[f], pb);
+            }
+          } else if constexpr (DO_S) {
+            const int ks = f - NVF;
+            s_next[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[f], qf[c][ks], ks == 0 ? f32x16{} : s_next[c],
+                                                                0, 0, 0);
+          }
+          if constexpr (DO_PV) {  // a previous half exists: finish its last scores
+            if (k == 0) vstage(SLOTS, s_cur, p_prev, false, false, 0);
+            if (k == 1) vstage(SLOTS + 1, s_cur, p_prev, false, false, 0);
+          }
+          if constexpr (DO_P) vstage(k, s_cur, p_cur, true, DO_MASK, lim_lane);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int i = 0; i < PF; ++i) fr[i] = ring[NF + i];
+      };
+
+      // replace the scores of keys at or past `lim` (0..32, within a half) by -inf
+      auto mask_half = [&](f32x16 (&s)[QG], int lim) {
+        int key0 = 4 * (lane >> 5);
+        asm volatile("" : "+v"(key0));
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const bool dead = key0 + 8 * (i >> 2) + (i & 3) >= lim;
+#pragma unroll
+          for (int c = 0; c < QG; ++c) s[c][i] = dead ? -INFINITY : s[c][i];
+        }
+      };
+
+      // scores of one half of the block in K stage kst, with masking
+      auto scores = [&](f32x16 (&s)[QG], int kst, int kh, int mask) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const bf16x8 x = kfrag(kst, kh, ks);
+#pragma unroll
+          for (int c = 0; c < QG; ++c)
+            s[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, qf[c][ks], ks == 0 ? f32x16{} : s[c], 0, 0, 0);
+        }
+        if (mask - 32 * kh < 32) mask_half(s, mask - 32 * kh);
+      };
+
+      // Streaming (main pass): blocks 0 and 1 are fetched before the first
+      // barrier; after the barrier of block j (which follows the wait for
+      // this wave's own loads) block j + 2 is fetched, K into K stage j % 2
+      // and V into V stage (j + 2) % 3. K(j) was last read in half-step 2j
+      // and V(j - 1) in half-step 2j, both before that barrier; K(j + 2) is
+      // first read in half-step 2j + 3 and V(j + 2) at the end of half-step
+      // 2j + 4, both after the next barrier.
+      auto voff_of = [](int j) { return (j % 3) * BLKB; };
+
+      // ---- an idle wave of a partial unit: the same loads and barriers
+      auto idle_main = [&]() {
+        reset_walk();
+        const KeyBlock s0 = decode(0);
+        issue(s0, 0, true);
+        issue(s0, 2 * BLKB + voff_of(0), false);
+        if (n_blk > 1) {
+          const KeyBlock s1 = decode(1);
+          issue(s1, BLKB, true);
+          issue(s1, 2 * BLKB + voff_of(1), false);
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        for (int j = 0; j < n_blk; ++j) {
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+          __syncthreads();
+          if (j + 2 < n_blk) {
+            const KeyBlock s2 = decode(j + 2);
+            issue(s2, (j & 1) * BLKB, true);
+            issue(s2, 2 * BLKB + voff_of(j + 2), false);
+          }
+        }
+      };
+      auto idle_max = [&]() {
+        reset_walk();
+        for (int j = 0; j < n_blk; ++j) {
+          const KeyBlock s = decode(j);
+          issue(s, 0, true);
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+          __syncthreads();
+          __syncthreads();
+        }
+      };
+
+      // ---- pass 1 (rare): the exact row maxima over all keys, scores only
+      auto max_pass = [&]() {
+        float mx[QG];
+#pragma unroll
+        for (int c = 0; c < QG; ++c) mx[c] = -INFINITY;
+        reset_walk();
+        for (int j = 0; j < n_blk; ++j) {
+          const KeyBlock s = decode(j);
+          issue(s, 0, true);
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+          __syncthreads();
+#pragma unroll
+          for (int kh = 0; kh < 2; ++kh) {
+            f32x16 sc[QG];
+            scores(sc, 0, kh, s.mask);
+#pragma unroll
+            for (int c = 0; c < QG; ++c)
+#pragma unroll
+              for (int i = 0; i < 16; ++i) mx[c] = fmaxf(mx[c], sc[c][i]);
+          }
+          __syncthreads();  // every wave has read the stage before it is refilled
+        }
+#pragma unroll
+        for (int c = 0; c < QG; ++c) m_run[c] = swap32_max(mx[c]) * qs;
+      };
+
+      // ---- the pipelined pass; m_run was set by max_pass when `known`
+      auto main_pass = [&](bool known) {
+        using T = std::true_type;
+        using F = std::false_type;
+#pragma unroll
+        for (int c = 0; c < QG; ++c) {
+#pragma unroll
+          for (int d = 0; d < DT; ++d) acc[c][d] = f32x16{};
+          lsum[c] = 0.f;
+        }
+        reset_walk();
+        const KeyBlock s0 = decode(0);
+        issue(s0, 0, true);
+        issue(s0, 2 * BLKB + voff_of(0), false);
+        int mask1 = 64;  // mask of block j + 1 in body(j)
+        int mask2 = 64;  // mask of block j + 2
+        if (n_blk > 1) {
+          const KeyBlock s1 = decode(1);
+          issue(s1, BLKB, true);
+          issue(s1, 2 * BLKB + voff_of(1), false);
+          mask1 = s1.mask;
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        f32x16 sa[QG], sb[QG];
+        uint32_t pa[QG][8], pb[QG][8];
+        scores(sa, 0, 0, s0.mask);  // S(0), masked
+        if (!known) {
+          // the reference: exact maximum of each row's scaled scores over half 0
+#pragma unroll
+          for (int c = 0; c < QG; ++c) {
+            float x = sa[c][0];
+#pragma unroll
+            for (int i = 1; i < 16; ++i) x = fmaxf(x, sa[c][i]);
+            m_run[c] = swap32_max(x) * qs;
+          }
+        }
+        bf16x8 fr[PF];
+#pragma unroll
+        for (int i = 0; i < PF; ++i) fr[i] = vfrag_at(voff_of(0), 0, i);
+        asm volatile("s_nop 2" ::: "memory");  // accumulator writes before the first asm MFMA
+        // half-step 0: S(1) (K(0) half 1) and P(0); no P V yet
+        step(T{}, F{}, T{}, F{}, std::integral_constant<int, 0>{}, voff_of(0), 0, 1, voff_of(0), 0, 64, fr, sb, sa,
+             pb, pa);
+        if (s0.mask < 64) mask_half(sb, s0.mask - 32);  // S(1): block 0 half 1
+        // body(j): half-steps 2j + 1 (scores K(j + 1) half 0 into S(2j + 2),
+        // P V of half 2j = V(j) half 0, softmax of S(2j + 1): block j half 1)
+        // and 2j + 2 (scores K(j + 1) half 1, P V of half 2j + 1, softmax of
+        // S(2j + 2): block j + 1 half 0). mask_a, mask_b: the masks of the
+        // halves consumed (64 when nothing is masked).
+        auto body = [&](auto mask_first_c, auto mask_second_c, auto kst, int j, int mask_a, int mask_b) {
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+          __syncthreads();
+          if (j + 2 < n_blk) {
+            const KeyBlock s2 = decode(j + 2);
+            issue(s2, (j & 1) * BLKB, true);
+            issue(s2, 2 * BLKB + voff_of(j + 2), false);
+            mask2 = s2.mask;
+          }
+          const int vj = voff_of(j), vj1 = voff_of(j + 1);
+          step(T{}, T{}, T{}, mask_first_c, kst, vj, 0, 0, vj, 1, mask_a, fr, sa, sb, pa, pb);
+          step(T{}, T{}, T{}, mask_second_c, kst, vj, 1, 1, vj1, 0, mask_b, fr, sb, sa, pb, pa);
+        };
+        int mask0 = s0.mask;  // mask of block j in body(j)
+        auto advance = [&]() {
+          mask0 = mask1;
+          mask1 = mask2;
+          mask2 = 64;
+        };
+        // bodies j with j + 1 < n_plain consume unmasked halves only
+        int j = 0;
+        for (; j + 2 < n_plain; j += 2) {
+          body(F{}, F{}, std::integral_constant<int, 1>{}, j, 64, 64);
+          advance();
+          body(F{}, F{}, std::integral_constant<int, 0>{}, j + 1, 64, 64);
+          advance();
+        }
+        if (j + 1 < n_plain) {
+          body(F{}, F{}, std::integral_constant<int, 1>{}, j, 64, 64);
+          advance();
+          ++j;
+        }
+        if constexpr (!PAD) {
+          // only the last block can be masked: body(n_blk - 2) consumes its half 0
+          if (j + 1 < n_blk) {
+            body(F{}, T{}, 1 - (j & 1), j, 64, mask1);
+            advance();
+            ++j;
+          }
+        } else {
+          for (; j + 1 < n_blk; ++j) {  // the masked tail
+            body(T{}, T{}, 1 - (j & 1), j, mask0 - 32, mask1);
+            advance();
+          }
+        }
+        // the last block j = n_blk - 1: half-step 2j + 1 (P V of half 2j,
+        // softmax of block j half 1, masked) and 2j + 2 (P V of half 2j + 1)
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        const int vj = voff_of(j);
+        step(F{}, T{}, T{}, T{}, 0, vj, 0, 0, vj, 1, mask0 - 32, fr, sa, sb, pa, pb);
+        step(F{}, T{}, F{}, F{}, 0, vj, 1, 0, vj, 1, 64, fr, sb, sa, pb, pa);
+        asm volatile("s_nop 15\n\ts_nop 7" ::: "memory");  // last MFMA results before any read
+      };
+
+      if (!active) {
+        idle_main();
+        __syncthreads();
+        if (__builtin_amdgcn_readfirstlane(shared_word[1]) != 0) {
+          __syncthreads();
+          idle_max();
+          idle_main();
         }
         return;
       }
-    }
+      // a second pass, with the exact row maxima as reference, when some
+      // row's sum (relative to its first half's maximum) got large
+      for (bool known = false;; known = true) {
+        main_pass(known);
+        if (known) break;
+        bool redo = false;
 #pragma unroll
-    for (int i = 0; i < IPW; ++i) {
-      const int q = wave * IPW + i;
-      const size_t urow = size_t(kbase + ((q * RPI) >> 3) * krs + ((q * RPI) & 7));
-      const int rin = (lane >> 2) % RPI;
-      const int chunk = 4 * (lane / (4 * RPI)) + ((lane & 3) ^ sw(q * RPI + rin));
-      const unsigned o = unsigned(rin * ROWB + chunk * 16);
-      dma16(kr + urow * ROWB + o, &lds[st][0][q * 1024]);
-    }
-  };
-  // Fetch the packed V^T block starting at tile-major row vrow (contiguous).
-  auto issue_v = [&](int st, int vrow) {
-    int lane = opaque_lane<PAD>(this_lane);
-    const char* src = vtr + size_t(vrow) * ROWB;
-    const unsigned o = unsigned(lane) * 16u;
-#pragma unroll
-    for (int i = 0; i < IPW; ++i) {
-      const int q = wave * IPW + i;
-      dma16(src + q * 1024 + o, &lds[st][1][q * 1024]);
-    }
-  };
-
-  // The rest runs with QT query column groups per wave: 3 (8 x 48 = 384 rows)
-  // for a video tile, 2 (8 x 32 = 256 rows) for the text query slots; a
-  // partial tile also uses 1 (16 rows per wave) or 3 with only waves 0-3
-  // holding rows.
-  auto run = [&](auto qt_c) {
-    constexpr int QT = decltype(qt_c)::value;
-    constexpr int RPW = QT * 16;  // query rows per wave
-    // a wave whose rows all lie past a partial tile's tokens only loads and
-    // synchronises (its SIMD then runs one wave of the unit instead of two)
-    const bool active = !PAD || wave * RPW < q_rows;
-    // Q^T fragments for this wave's RPW rows, read from the caller's raster q
-    // (row r of the unit: see query_raster; rows past the unit are clamped to
-    // a valid row and their results discarded).
-    const float qs = a.q_scale;  // log2(e)/sqrt(D), applied to the fp32 scores
-    bf16x8 qf[QT][KS];
-  #pragma unroll
-    for (int c = 0; c < QT; ++c) {
-      int row = wave * RPW + c * 16 + (lane & 15);
-      row = row < q_rows ? row : q_rows - 1;
-      const int rr = query_raster(row);
-      const bf16x8* src = reinterpret_cast<const bf16x8*>(qr + size_t(rr) * D + (lane >> 4) * 8);
-  #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) qf[c][ks] = src[ks * 4];
-    }
-
-    f32x4 acc[QT][DT];
-    float l_part[QT];  // this lane's share of the row sum of p
-    float m_run[QT];   // reference max of the scaled scores (log2 units)
-  #pragma unroll
-    for (int c = 0; c < QT; ++c) {
-  #pragma unroll
-      for (int d = 0; d < DT; ++d) acc[c][d] = f32x4{0.f, 0.f, 0.f, 0.f};
-      l_part[c] = 0.f;
-      m_run[c] = 0.f;
-    }
-    bf16x2 ones2;
-    ones2[0] = (__bf16)1.0f;
-    ones2[1] = (__bf16)1.0f;
-
-    // K fragment (row 16kt + lane%16, chunk 4ks + lane/16) of a block sits at
-    // kofs + kt * 16 * ROWB + ks * 64 * RPI; V^T fragment (h, dt) at
-    // (h * DT + dt) * 1024 + lane * 16.
-    const int l15 = lane & 15;
-    const int kofs = (l15 / RPI) * 1024 + (l15 % RPI) * 64 + (((lane >> 4) ^ sw(l15)) << 4);
-
-    auto issue = [&](int j, int st) {
-      int kbase, krs, vrow;
-      block_rows(j, kbase, krs, vrow);
-      issue_k(st, kbase, krs);
-      issue_v(st, vrow);
-    };
-
-    issue(0, 0);
-    if (!active) {
-      // the same loads and barriers as the loop below; once every wave has
-      // passed barrier j, no wave reads the other stage any more
-      for (int j = 0; j < n_blk; ++j) {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        for (int c = 0; c < QG; ++c) redo |= !(swap32_sum(lsum[c]) < kRedoSum);
+        if (__builtin_amdgcn_ballot_w64(redo) != 0 && lane == 0) shared_word[1] = 1;
         __syncthreads();
-        if (j + 1 < n_blk) issue(j + 1, (j & 1) ^ 1);
-      }
-      return;
-    }
-    for (int j = 0; j < n_blk; ++j) {
-      const int stage = j & 1;
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
-
-      // ---- raw scores S^T = K Q^T (fp32); p = 2^(c s - m) below
-      const char* kb = lds[stage][0];
-      f32x4 s[QT][4];
-      {
-        constexpr int NF = 4 * KS;
-        bf16x8 kf[NF];
-        auto kload = [&](int f) {
-          kf[f] = *reinterpret_cast<const bf16x8*>(kb + kofs + (f & 3) * 16 * ROWB + (f >> 2) * 64 * RPI);
-        };
-  #pragma unroll
-        for (int f = 0; f < kKPrefetch; ++f) kload(f);
-  #pragma unroll
-        for (int f = 0; f < NF; ++f) {
-          const int ks = f >> 2, kt = f & 3;
-  #pragma unroll
-          for (int c = 0; c < QT; ++c)
-            s[c][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[f], qf[c][ks],
-                                                                ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : s[c][kt], 0, 0, 0);
-          if (f + kKPrefetch < NF) kload(f + kKPrefetch);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        if (ragged && j == n_blk - 1) {
-          int key0 = (j - n_vid) * kKeyBlock + 4 * (lane >> 4);
-          asm volatile("" : "+v"(key0));  // build the 16 lane masks here, not before the loop
-  #pragma unroll
-          for (int kt = 0; kt < 4; ++kt)
-  #pragma unroll
-            for (int r = 0; r < 4; ++r)
-              if (key0 + 16 * kt + r >= text_len)
-  #pragma unroll
-                for (int c = 0; c < QT; ++c) s[c][kt][r] = -INFINITY;
-        }
-        if constexpr (PAD) {
-          // the last block of a tile whose token count is not a multiple of
-          // 64: keys past the tile's tokens (the tile state still describes
-          // block j; block j + 1 is decoded below)
-          const int n_tok = extent_tokens(tile_ext);
-          if (j < n_vid && (cur_sub + 1) * kKeyBlock > n_tok) {
-            int key0 = cur_sub * kKeyBlock + 4 * (lane >> 4);
-            asm volatile("" : "+v"(key0));
-  #pragma unroll
-            for (int kt = 0; kt < 4; ++kt)
-  #pragma unroll
-              for (int r = 0; r < 4; ++r)
-                if (key0 + 16 * kt + r >= n_tok)
-  #pragma unroll
-                  for (int c = 0; c < QT; ++c) s[c][kt][r] = -INFINITY;
-          }
-        }
-      }
-      if (j + 1 < n_blk) issue(j + 1, stage ^ 1);
-      // per-lane max of the scaled scores; the reference moves only past the
-      // slack, and then only m, l and the accumulator change (the scores are
-      // raw, so nothing is recomputed)
-      float lm[QT];
-      bool need = false;
-  #pragma unroll
-      for (int c = 0; c < QT; ++c) {
-        float x = fmaxf(fmaxf(s[c][0][0], s[c][0][1]), s[c][0][2]);
-        x = fmaxf(fmaxf(x, s[c][0][3]), s[c][1][0]);
-        x = fmaxf(fmaxf(x, s[c][1][1]), s[c][1][2]);
-        x = fmaxf(fmaxf(x, s[c][1][3]), s[c][2][0]);
-        x = fmaxf(fmaxf(x, s[c][2][1]), s[c][2][2]);
-        x = fmaxf(fmaxf(x, s[c][2][3]), s[c][3][0]);
-        x = fmaxf(fmaxf(x, s[c][3][1]), s[c][3][2]);
-        lm[c] = fmaxf(x, s[c][3][3]) * qs;
-        need |= lm[c] - m_run[c] > kRescaleSlack;
-      }
-      const bool first = j == 0;
-      if (first || __builtin_amdgcn_ballot_w64(need) != 0) {
-  #pragma unroll
-        for (int c = 0; c < QT; ++c) {
-          // exact row max across the 4 lanes holding this query
-          const float mx = swap32_max(swap16_max(lm[c]));
-          if (first) {
-            m_run[c] = mx;  // nothing accumulated yet
-          } else if (mx > m_run[c]) {
-            const float alpha = __builtin_amdgcn_exp2f(m_run[c] - mx);
-            m_run[c] = mx;
-            l_part[c] *= alpha;
-  #pragma unroll
-            for (int d = 0; d < DT; ++d) acc[c][d] *= alpha;
-          }
-        }
+        if (__builtin_amdgcn_readfirstlane(shared_word[1]) == 0) break;
+        __syncthreads();
+        max_pass();
       }
 
-      // ---- p = 2^(c s - m) rounded to bf16; O^T += V^T P^T; row sums += 1^T P^T
-      const bf16x8* vl = reinterpret_cast<const bf16x8*>(lds[stage][1]);
-  #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        bf16x8 pb[QT];
-  #pragma unroll
-        for (int c = 0; c < QT; ++c) {
-          f32x8 p;
-  #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[c][2 * h][r], qs, -m_run[c]));
-            p[4 + r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[c][2 * h + 1][r], qs, -m_run[c]));
-          }
-          pb[c] = __builtin_convertvector(p, bf16x8);
-          // row sum of the rounded p, two at a time
-  #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const bf16x2 pair = {pb[c][2 * i], pb[c][2 * i + 1]};
-            l_part[c] = __builtin_amdgcn_fdot2_f32_bf16(pair, ones2, l_part[c], false);
-          }
-        }
-  #pragma unroll
-        for (int d = 0; d < DT; ++d) {
-          const bf16x8 vf = vl[(h * DT + d) * 64 + lane];
-  #pragma unroll
-          for (int c = 0; c < QT; ++c)
-            acc[c][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[c], acc[c][d], 0, 0, 0);
+      // ---- epilogue: O = O^T / l (bf16) and lse at raster rows; lane l holds
+      // query 32 c + l % 32, columns 32 dt + 8 g + 4 (l / 32) + 0..3 in
+      // accumulator registers 4 g .. 4 g + 3
+      __bf16* __restrict__ outr = reinterpret_cast<__bf16*>(a.out) + slab;
+      float* __restrict__ lser = a.lse == nullptr ? nullptr : a.lse + size_t(bh) * g.S;
+#pragma unroll
+      for (int c = 0; c < QG; ++c) {
+        const float l = swap32_sum(lsum[c]);
+        const float inv = __builtin_amdgcn_rcpf(l);
+        const int row = wave * RPW + 32 * c + (lane & 31);
+        if (row < q_rows) {
+          const int rr = query_raster(row);
+          __bf16* dst = outr + size_t(rr) * D + 4 * (lane >> 5);
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+              const f32x4 o = {acc[c][dt][4 * gq] * inv, acc[c][dt][4 * gq + 1] * inv, acc[c][dt][4 * gq + 2] * inv,
+                               acc[c][dt][4 * gq + 3] * inv};
+              *reinterpret_cast<bf16x4*>(dst + 32 * dt + 8 * gq) = __builtin_convertvector(o, bf16x4);
+            }
+          if (lser != nullptr && lane < 32) lser[rr] = (m_run[c] + __builtin_amdgcn_logf(l)) * kLn2;
         }
       }
-    }
-
-    // ---- epilogue: O = O^T / l in bf16 and lse, straight to raster positions
-    __bf16* __restrict__ outr = reinterpret_cast<__bf16*>(a.out) + slab;
-    float* __restrict__ lser = a.lse == nullptr ? nullptr : a.lse + size_t(bh) * g.S;
-  #pragma unroll
-    for (int c = 0; c < QT; ++c) {
-      const float l = swap32_sum(swap16_sum(l_part[c]));
-      const float inv = __builtin_amdgcn_rcpf(l);
-      const int row = wave * RPW + c * 16 + (lane & 15);
-      if (row < q_rows) {
-        const int rr = query_raster(row);
-        __bf16* dst = outr + size_t(rr) * D + (lane >> 4) * 4;
-  #pragma unroll
-        for (int d = 0; d < DT; ++d) {
-          const f32x4 o = acc[c][d] * inv;
-          *reinterpret_cast<bf16x4*>(dst + d * 16) = __builtin_convertvector(o, bf16x4);
-        }
-        if (lser != nullptr && lane < 16) lser[rr] = (m_run[c] + __builtin_amdgcn_logf(l)) * kLn2;
-      }
-    }
-  };
-  if constexpr (PAD) {
-    if (q_rows <= 16 * kWaves) {  // a small partial tile: 8 (or 4) waves x 16 rows
+    };
+    if (text_unit || (PAD && q_rows > 4 * 32 && q_rows <= kTextSlots))
+      run(std::integral_constant<int, 2>{});
+    else if (PAD && q_rows <= 4 * 32)
       run(std::integral_constant<int, 1>{});
-      continue;
-    }
-  }
-  // 8 waves x 32 rows for the text slots and for partial tiles of 193 to 256
-  // tokens; otherwise 48 rows per wave (4 waves do the work for at most 192)
-  if (text_unit || (PAD && q_rows > 4 * 16 * kQT && q_rows <= kTextSlots))
-    run(std::integral_constant<int, kTextSlots / 16 / kWaves>{});
-  else
-    run(std::integral_constant<int, kQT>{});
+    else
+      run(std::integral_constant<int, 3>{});
   }
 }
 

@@ -84,11 +84,12 @@ __host__ __device__ inline void compact_token(int r, int e, int& dt, int& dh, in
   dw = rem - dh * cols;
 }
 
-// Blocks of 64 tokens over a box of tiles [lo, lo + len) per axis, each tile
-// counting ceil(tokens / 64). Along an axis every tile but the grid's last is
-// full, so the sum has at most eight distinct terms.
-__host__ __device__ inline int box_blocks(int lo_t, int len_t, int lo_h, int len_h, int lo_w, int len_w,
-                                          const Geom& g) {
+// Blocks of 64 tokens over a box of tiles [lo, lo + len) per axis: each tile
+// has floor(tokens / 64) full blocks (`full`) and, when 64 does not divide its
+// tokens, one remainder block (`rem`). Along an axis every tile but the grid's
+// last is full, so the sums have at most eight distinct terms.
+__host__ __device__ inline void box_block_counts(int lo_t, int len_t, int lo_h, int len_h, int lo_w, int len_w,
+                                                 const Geom& g, int& full, int& rem) {
   int n_full[3], n_part[3], ext[3];
   const int lo[3] = {lo_t, lo_h, lo_w}, len[3] = {len_t, len_h, len_w};
   const int n[3] = {g.nt, g.nh, g.nw}, size[3] = {g.T, g.H, g.W}, tile[3] = {kTileT, kTileH, kTileW};
@@ -97,15 +98,129 @@ __host__ __device__ inline int box_blocks(int lo_t, int len_t, int lo_h, int len
     n_part[a] = (lo[a] + len[a] == n[a] && ext[a] < tile[a]) ? 1 : 0;
     n_full[a] = len[a] - n_part[a];
   }
-  int sum = 0;
+  full = 0;
+  rem = 0;
   for (int m = 0; m < 8; ++m) {
     const int ct = (m & 1) ? n_part[0] : n_full[0], ch = (m & 2) ? n_part[1] : n_full[1];
     const int cw = (m & 4) ? n_part[2] : n_full[2];
     const int tok = ((m & 1) ? ext[0] : kTileT) * ((m & 2) ? ext[1] : kTileH) * ((m & 4) ? ext[2] : kTileW);
-    sum += ct * ch * cw * ((tok + kKeyBlock - 1) / kKeyBlock);
+    full += ct * ch * cw * (tok / kKeyBlock);
+    rem += ct * ch * cw * ((tok % kKeyBlock) != 0 ? 1 : 0);
   }
-  return sum;
 }
+// All blocks of the box: each tile counting ceil(tokens / 64).
+__host__ __device__ inline int box_blocks(int lo_t, int len_t, int lo_h, int len_h, int lo_w, int len_w,
+                                          const Geom& g) {
+  int full, rem;
+  box_block_counts(lo_t, len_t, lo_h, len_h, lo_w, len_w, g, full, rem);
+  return full + rem;
+}
+
+// One 64-key block of a query unit's key stream (scalar values).
+struct KeyBlock {
+  // 0: a full frame of a key tile, block row r at raster base + (r / 8) W + r % 8;
+  // 1: consecutive raster rows base + r, valid while r < lim (text);
+  // 2: compact token 64 sub + r of the partial key tile with raster origin
+  //    base and extent ext, valid while the token exists.
+  int kind;
+  int base, lim, ext, sub;
+  int mask;  // first block row that must not contribute (64: none)
+};
+
+// The key blocks of one query unit, in the order the forward kernel streams
+// them: the full blocks of the window's key tiles (n_vfull), the full text
+// blocks (n_tfull), then, when the video is not a tile multiple (PAD), one
+// remainder block for every key tile whose tokens are not a multiple of 64
+// (n_vrem), and last the partial text block when 64 does not divide the text
+// length. Blocks before n_plain are whole; only the trailing ones are masked.
+// Key tiles are walked by the residues of their coordinates modulo the window
+// size (the window starts at (st, sh, sw) and spans (bt, bh, bw) tiles): query
+// tiles whose windows overlap then reach each shared key tile at the same
+// step of the walk. The text unit walks every tile (a box from the origin).
+// block(j) must be called for j = 0, 1, 2, ... after reset().
+template <bool PAD>
+struct KeyStream {
+  int st, sh, sw, bt, bh, bw;
+  int n_vfull, n_vrem, n_tfull, n_plain, n_blk, text_len;
+  int walk_a, walk_b, walk_c, tile_org, tile_ext, tile_sub, tile_nblk;
+
+  __host__ __device__ void init(const Geom& g, int st_, int bt_, int sh_, int bh_, int sw_, int bw_) {
+    st = st_;
+    sh = sh_;
+    sw = sw_;
+    bt = bt_;
+    bh = bh_;
+    bw = bw_;
+    n_vfull = bt * bh * bw * (kTileRows / kKeyBlock);
+    n_vrem = 0;
+    if (PAD) box_block_counts(st, bt, sh, bh, sw, bw, g, n_vfull, n_vrem);
+    text_len = g.has_text ? g.text_length : 0;
+    n_tfull = text_len / kKeyBlock;
+    n_plain = n_vfull + n_tfull;
+    n_blk = n_plain + n_vrem + (text_len % kKeyBlock != 0 ? 1 : 0);
+    reset();
+  }
+  __host__ __device__ void reset() {
+    walk_a = 0;
+    walk_b = 0;
+    walk_c = -1;
+    tile_org = 0;
+    tile_ext = kFullExtent;
+    tile_sub = 0;
+    tile_nblk = 0;
+  }
+  // coordinate in [s, s + w) congruent to r mod w (r in [0, w))
+  __host__ __device__ static int residue_coord(int r, int s, int w) {
+    const int d = (r - s) % w;
+    return s + (d < 0 ? d + w : d);
+  }
+  // advance the walk to the next key tile; the remainder walk takes only its
+  // last, partial block, the first walk only its full blocks
+  __host__ __device__ void next_tile(const Geom& g, bool rem_walk) {
+    if (++walk_c == bw) {
+      walk_c = 0;
+      if (++walk_b == bh) {
+        walk_b = 0;
+        ++walk_a;
+      }
+    }
+    const int kt = residue_coord(walk_a, st, bt), kh = residue_coord(walk_b, sh, bh);
+    const int kw = residue_coord(walk_c, sw, bw);
+    tile_org = (kt * kTileT * g.H + kh * kTileH) * g.W + kw * kTileW;
+    tile_ext = PAD ? tile_extent(kt, kh, kw, g) : kFullExtent;
+    const int n_tok = extent_tokens(tile_ext);
+    tile_sub = rem_walk ? n_tok / kKeyBlock : 0;
+    tile_nblk = rem_walk ? tile_sub + (n_tok % kKeyBlock != 0 ? 1 : 0) : n_tok / kKeyBlock;
+  }
+  __host__ __device__ KeyBlock block(const Geom& g, int j) {
+    KeyBlock s;
+    const bool rem_walk = PAD && j >= n_plain;
+    if (j < n_vfull || (rem_walk && j < n_plain + n_vrem)) {
+      if (PAD && j == n_plain) reset();               // the first remainder block
+      while (tile_sub == tile_nblk) next_tile(g, rem_walk);  // skips tiles without such blocks
+      const int n_tok = extent_tokens(tile_ext);
+      const bool frames = (tile_ext >> 8) == (kFullExtent >> 8);  // every row and column exists
+      s.kind = frames ? 0 : 2;
+      s.base = frames ? tile_org + tile_sub * g.H * g.W : tile_org;
+      s.lim = kKeyBlock;
+      s.ext = tile_ext;
+      s.sub = tile_sub;
+      const int left = n_tok - tile_sub * kKeyBlock;
+      s.mask = left < kKeyBlock ? left : kKeyBlock;
+      ++tile_sub;
+    } else {
+      const int tb = j < n_plain ? j - n_vfull : n_tfull;
+      s.kind = 1;
+      s.base = g.n_video + tb * kKeyBlock;
+      const int left = text_len - tb * kKeyBlock;
+      s.lim = left < kKeyBlock ? left : kKeyBlock;
+      s.ext = kFullExtent;
+      s.sub = 0;
+      s.mask = s.lim;
+    }
+    return s;
+  }
+};
 
 // Tile-major row r (within one [S_t] slab) -> raster row, or -1 for a padding
 // row. Tile t owns rows 384t .. 384t + 383; a video size that is not a
@@ -160,9 +275,10 @@ hipError_t launch_schedule_lists(const Geom& g, const Windows& win, int32_t* off
                                  int32_t* ids, hipStream_t stream);
 // Work order (one query unit per entry, grouped into 8 per-XCD queues: queue x
 // holds entries 8k + x). `claim`, when not null, receives kClaimInts zeros:
-// the queue heads the attention kernel advances.
+// the queue heads the attention kernel advances; `zero_row`, when not null,
+// receives kZeroRowBytes zeros.
 hipError_t launch_schedule_work(const Geom& g, const Windows& win, int32_t* work,
-                                int32_t* claim, hipStream_t stream);
+                                int32_t* claim, void* zero_row, hipStream_t stream);
 constexpr int kQueues = 8;        // one per XCD
 constexpr int kClaimStride = 64;  // ints between queue heads (own 256-byte line each)
 constexpr int kClaimInts = kQueues * kClaimStride;
@@ -170,15 +286,15 @@ constexpr int kClaimInts = kQueues * kClaimStride;
 struct FwdArgs {
   const void* q;         // bf16 raster rows (the caller's q)
   const void* k;         // bf16 raster rows (the caller's k)
-  const void* vt;        // packed V^T fragments (launch_pack_v)
+  const void* v;         // bf16 raster rows (the caller's v)
   void* out;             // bf16 raster rows (the caller's out)
   float* lse;            // fp32 raster (the caller's lse), or nullptr
-  const int32_t* offsets;
-  const int32_t* ids;
   const int32_t* work;   // per-XCD queues of query units (launch_schedule_work)
   int32_t* claim;        // queue heads, zeroed by launch_schedule_work
+  const void* zero_row;  // kZeroRowBytes of zeros (written by launch_schedule_work)
   float q_scale;         // log2(e) / sqrt(D), applied to the fp32 scores
 };
+constexpr int kZeroRowBytes = 256;  // one row of D = 128 bf16
 hipError_t launch_attention(const Geom& g, const Windows& win, const FwdArgs& a, hipStream_t stream);
 
 // Backward (gradients of the forward for an upstream gradient dout).

@@ -82,9 +82,12 @@ static_assert(kXcds == 8, "the queue index is the XCD id mod 8");
 // resolves one entry to its query unit; block 0 also zeroes the queue heads.
 __global__ __launch_bounds__(kWorkThreads) void schedule_work_kernel(Geom g, Windows win,
                                                                      int32_t* __restrict__ work,
-                                                                     int32_t* __restrict__ claim) {
+                                                                     int32_t* __restrict__ claim,
+                                                                     int32_t* __restrict__ zero_row) {
   if (claim != nullptr && blockIdx.x == 0)
     for (int i = threadIdx.x; i < kClaimInts; i += kWorkThreads) claim[i] = 0;
+  if (zero_row != nullptr && blockIdx.x == 0)
+    for (int i = threadIdx.x; i < kZeroRowBytes / 4; i += kWorkThreads) zero_row[i] = 0;
   __shared__ long long cost[kMaxClasses];
   __shared__ int count[kMaxClasses];
   __shared__ int order[kMaxClasses];  // order[rank] = class
@@ -156,10 +159,11 @@ hipError_t launch_schedule_lists(const Geom& g, const Windows& win, int32_t* off
 }
 
 hipError_t launch_schedule_work(const Geom& g, const Windows& win, int32_t* work,
-                                int32_t* claim, hipStream_t stream) {
+                                int32_t* claim, void* zero_row, hipStream_t stream) {
   const int total = g.B * g.heads * g.n_q;
   dim3 grid((total + kWorkThreads - 1) / kWorkThreads);
-  schedule_work_kernel<<<grid, kWorkThreads, 0, stream>>>(g, win, work, claim);
+  schedule_work_kernel<<<grid, kWorkThreads, 0, stream>>>(g, win, work, claim,
+                                                           static_cast<int32_t*>(zero_row));
   return hipGetLastError();
 }
 

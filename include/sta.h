@@ -118,16 +118,16 @@ size_t sta_workspace_bytes(const sta_dims* dims, const int32_t* window_sizes,
  *             bytes, 256-byte aligned; contents on entry are ignored and on
  *             return are unspecified. Calls that share a workspace must be
  *             ordered on one stream.
- * Returns STA_OK once the four launches (V^T pack into tile-major MFMA
- * fragment order, schedule lists, work order, fused attention reading q and k
- * and writing out/lse in raster order, all through the tile map) are
- * enqueued on `stream`. The workspace holds the packed V^T (the size of v,
- * its video rows padded to whole tiles),
- * the schedule (a few MB at most) and 2 KB of work-queue heads. The attention
- * launch is a persistent grid (one workgroup per resident slot on the current
- * device) whose workgroups take query units from per-XCD queues, their own
- * XCD's first; which workgroup runs which unit varies from call to call, the
- * results do not.
+ * Returns STA_OK once the two launches (the work order of query units, and
+ * the fused attention kernel, which reads q, k and v and writes out/lse in
+ * raster order, all through the tile map, and enumerates each unit's window
+ * of key tiles itself) are enqueued on `stream`. The workspace holds the work
+ * order (4 bytes per query unit: B*heads*(n_t*n_h*n_w + has_text) units), 2 KB
+ * of work-queue heads and a 256-byte zero row: a few KB to a few hundred KB.
+ * The attention launch is a persistent grid (one workgroup per resident slot
+ * on the current device) whose workgroups take query units from per-XCD
+ * queues, their own XCD's first; which workgroup runs which unit varies from
+ * call to call, the results do not.
  */
 sta_status sta_forward(const sta_dims* dims, const void* q, const void* k,
                        const void* v, const int32_t* window_sizes,
@@ -139,12 +139,11 @@ sta_status sta_forward(const sta_dims* dims, const void* q, const void* k,
  * sta_forward with stage timing, for measurement. `events` holds
  * STA_TIMED_EVENTS hipEvent_t handles (as void*, created by the caller);
  * events[0] is recorded on `stream` before the first launch and events[i]
- * after launch i of: 1 pack v, 2 schedule lists, 3 work order,
- * 4 fused attention. hipEventElapsedTime between consecutive events then
- * gives each kernel's duration. Nothing else differs from sta_forward;
- * STA_ERR_NULL if events or an entry is NULL.
+ * after launch i of: 1 work order, 2 fused attention. hipEventElapsedTime
+ * between consecutive events then gives each kernel's duration. Nothing else
+ * differs from sta_forward; STA_ERR_NULL if events or an entry is NULL.
  */
-#define STA_TIMED_EVENTS 5
+#define STA_TIMED_EVENTS 3
 sta_status sta_forward_timed(const sta_dims* dims, const void* q, const void* k,
                              const void* v, const int32_t* window_sizes,
                              int32_t text_length, int32_t has_text, void* out,

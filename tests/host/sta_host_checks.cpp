@@ -14,6 +14,10 @@
 //       prints the helpers' values for one geometry (every head gets the
 //       window (wt, wh, ww)); the Python test compares them with maps built
 //       from the oracle's token coordinates
+//   sta_host_checks stream <T> <H> <W> <has_text> <ell> <wt> <wh> <ww>
+//       checks the forward kernel's key stream of every query unit and prints
+//       its key rows (compared with the oracle's mask by the Python test)
+#include <algorithm>
 #include <cstdint>
 #include <cstdio>
 #include <cstdlib>
@@ -66,13 +70,13 @@ hipError_t launch_schedule_lists(const Geom& g, const Windows&, int32_t* offsets
   return hipSuccess;
 }
 hipError_t launch_schedule_work(const Geom& g, const Windows&, int32_t* work, int32_t* claim,
-                                hipStream_t) {
-  record("schedule_work", g, {P(work), P(claim)});
+                                void* zero_row, hipStream_t) {
+  record("schedule_work", g, {P(work), P(claim), P(zero_row)});
   return hipSuccess;
 }
 hipError_t launch_attention(const Geom& g, const Windows&, const FwdArgs& a, hipStream_t) {
-  record("attention", g, {P(a.q), P(a.k), P(a.vt), P(a.out), P(a.lse), P(a.offsets), P(a.ids),
-                          P(a.work), P(a.claim)});
+  record("attention", g, {P(a.q), P(a.k), P(a.v), P(a.out), P(a.lse), P(a.work), P(a.claim),
+                          P(a.zero_row)});
   return hipSuccess;
 }
 hipError_t launch_bwd_prep(const Geom& g, const void* out, const void* dout, const float* lse,
@@ -309,6 +313,83 @@ void dump(int argc, char** argv) {
   }
 }
 
+// The forward kernel's key stream of every query unit (sta::KeyStream, the
+// same code the kernel runs): checks the block order (blocks before n_plain
+// whole, masked ones after), the bounds of every key row, and that no key is
+// streamed twice; prints each unit's valid key rows as sorted half-open
+// ranges "unit <u> <n_blk> <n_plain> <lo>:<hi> ...".
+template <bool PAD>
+void stream_units(const sta::Geom& g, int wt, int wh, int ww) {
+  for (int u = 0; u < g.n_q; ++u) {
+    const bool text_unit = g.has_text && u == g.n_tiles;
+    sta::KeyStream<PAD> ks;
+    if (text_unit) {
+      ks.init(g, 0, g.nt, 0, g.nh, 0, g.nw);
+    } else {
+      const int tw = u % g.nw, th = (u / g.nw) % g.nh, tt = u / (g.nw * g.nh);
+      ks.init(g, sta::window_start(tt, wt, g.nt), wt, sta::window_start(th, wh, g.nh), wh,
+              sta::window_start(tw, ww, g.nw), ww);
+    }
+    std::vector<int> keys;
+    for (int j = 0; j < ks.n_blk; ++j) {
+      const sta::KeyBlock b = ks.block(g, j);
+      CHECK(b.mask >= 1 && b.mask <= sta::kKeyBlock, "unit %d block %d mask %d", u, j, b.mask);
+      CHECK(j >= ks.n_plain || b.mask == sta::kKeyBlock, "unit %d block %d masked before n_plain %d", u, j,
+            ks.n_plain);
+      CHECK(PAD || b.kind != 2, "unit %d block %d: compact block without partial tiles", u, j);
+      for (int r = 0; r < b.mask; ++r) {
+        int row;
+        if (b.kind == 0) {
+          row = b.base + (r >> 3) * g.W + (r & 7);
+        } else if (b.kind == 1) {
+          CHECK(b.mask == b.lim, "unit %d block %d text limit", u, j);
+          row = b.base + r;
+          CHECK(row >= g.n_video && row < g.n_video + g.text_length, "unit %d block %d text row %d", u, j, row);
+        } else {
+          const int tok = b.sub * sta::kKeyBlock + r;
+          CHECK(tok < sta::extent_tokens(b.ext), "unit %d block %d token %d past the tile", u, j, tok);
+          int dt, dh, dw;
+          sta::compact_token(tok, b.ext, dt, dh, dw);
+          row = b.base + (dt * g.H + dh) * g.W + dw;
+        }
+        CHECK(row >= 0 && row < g.S, "unit %d block %d row %d outside the sequence", u, j, row);
+        keys.push_back(row);
+      }
+    }
+    std::sort(keys.begin(), keys.end());
+    for (size_t i = 1; i < keys.size(); ++i) CHECK(keys[i] != keys[i - 1], "unit %d key %d twice", u, keys[i]);
+    std::printf("unit %d %d %d", u, ks.n_blk, ks.n_plain);
+    for (size_t i = 0; i < keys.size();) {
+      size_t e = i + 1;
+      while (e < keys.size() && keys[e] == keys[e - 1] + 1) ++e;
+      std::printf(" %d:%d", keys[i], keys[e - 1] + 1);
+      i = e;
+    }
+    std::printf("\n");
+  }
+}
+
+void stream(int argc, char** argv) {
+  if (argc != 10) {
+    std::fprintf(stderr, "stream needs 8 integers\n");
+    std::exit(2);
+  }
+  int a[8];
+  for (int i = 0; i < 8; ++i) a[i] = std::atoi(argv[2 + i]);
+  const sta_dims d{1, 1, 128, a[0], a[1], a[2]};
+  const int text = a[3], ell = a[4];
+  std::vector<int32_t> w = windows_for(1, a[5], a[6], a[7]);
+  const size_t n = sta_workspace_bytes(&d, w.data(), text);
+  CHECK(fwd(&d, w.data(), ell, text, fake(0), fake(1), fake(2), fake(3), static_cast<float*>(fake(4)), fake(8),
+            n) == STA_OK,
+        "forward on the streamed geometry");
+  const sta::Geom g = g_launches.back().g;
+  if (g.full)
+    stream_units<false>(g, a[5], a[6], a[7]);
+  else
+    stream_units<true>(g, a[5], a[6], a[7]);
+}
+
 }  // namespace
 
 int main(int argc, char** argv) {
@@ -320,6 +401,11 @@ int main(int argc, char** argv) {
     dump(argc, argv);
     return 0;
   }
-  std::fprintf(stderr, "usage: %s validate | dump B heads D T H W has_text ell wt wh ww\n", argv[0]);
+  if (argc >= 2 && std::strcmp(argv[1], "stream") == 0) {
+    stream(argc, argv);
+    return 0;
+  }
+  std::fprintf(stderr, "usage: %s validate | dump B heads D T H W has_text ell wt wh ww | stream T H W has_text ell wt wh ww\n",
+               argv[0]);
   return 2;
 }

@@ -137,10 +137,9 @@ def test_sizes(lib, B, heads, D, video, windows, text):
 
     def up(x):
         return (x + 255) // 256 * 256
-    S_t = n_tiles * 384 + (256 if text else 0)  # packed rows: video padded to whole tiles
-    tensor = B * heads * S_t * D * 2
     queue_heads = 8 * 64 * 4  # one int per XCD queue, each on its own 256-byte line
-    expect = up(tensor) + up(n_off * 4) + up(n_ids * 4) + up(n_work * 4) + queue_heads
+    zero_row = 256            # the source of keys that must not contribute
+    expect = up(n_work * 4) + queue_heads + zero_row
     assert sta.sta_workspace_bytes(d, windows, text) == expect
 
 

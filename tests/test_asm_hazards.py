@@ -1,0 +1,95 @@
+"""The forward kernels' inline-asm MFMAs, checked in the compiled assembly.
+
+The P V products are inline-asm MFMAs whose accumulators the compiler cannot
+see as MFMA results, so the wait states around them, and the absence of spill
+code that would move the accumulators, are checked here on the gfx950
+assembly of the source the library is built from (same flags). The checker is
+first shown to catch planted mistakes on small hand-written listings.
+"""
+
+import os
+import shutil
+import subprocess
+
+import pytest
+
+import asm_hazards as H
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _kernel(body: str) -> H.Kernel:
+    text = "_ZN3sta12_GLOBAL__N_120sta_attention_kernelTEST:\n" + body + "\n.Lfunc_end0:\n"
+    ks = H.parse(text)
+    assert len(ks) == 1
+    return ks[0]
+
+
+ASM_MFMA = "\t;;#ASMSTART\n\tv_mfma_f32_32x32x16_bf16 a[0:15], v[8:11], v[12:15], a[0:15]\n\t;;#ASMEND\n"
+
+
+def test_checker_flags_early_accumulator_read():
+    bad = _kernel(ASM_MFMA + "\ts_nop 7\n\tv_accvgpr_read_b32 v0, a3\n\ts_endpgm\n")
+    assert len(H.check_result_reads(bad)) == 1
+    good = _kernel(ASM_MFMA + "\ts_nop 15\n\ts_nop 1\n\tv_accvgpr_read_b32 v0, a3\n\ts_endpgm\n")
+    assert H.check_result_reads(good) == []
+
+
+def test_checker_flags_spill_store_of_accumulator():
+    bad = _kernel(ASM_MFMA + "\tscratch_store_dwordx4 off, a[0:3], off offset:400\n\ts_endpgm\n")
+    assert len(H.check_result_reads(bad)) == 1
+
+
+def test_checker_allows_accumulation_chain_and_other_accumulators():
+    other = ASM_MFMA.replace("a[0:15], v[8:11], v[12:15], a[0:15]", "a[16:31], v[8:11], v[12:15], a[16:31]")
+    k = _kernel(ASM_MFMA + ASM_MFMA + other + "\ts_endpgm\n")
+    assert H.check_result_reads(k) == []
+    # an MFMA that reads the accumulator as a plain operand is not a chain
+    k = _kernel(ASM_MFMA + ASM_MFMA.replace("a[0:15], v[8:11], v[12:15], a[0:15]",
+                                            "a[16:31], v[8:11], v[12:15], a[0:15]") + "\ts_endpgm\n")
+    assert len(H.check_result_reads(k)) == 1
+
+
+def test_checker_follows_branches():
+    body = (ASM_MFMA + "\ts_cbranch_scc1 .LBB0_2\n\ts_nop 15\n\ts_nop 15\n.LBB0_2:\n"
+            "\tv_accvgpr_read_b32 v0, a0\n\ts_endpgm\n")
+    assert len(H.check_result_reads(_kernel(body))) == 1  # the taken branch reaches the read early
+
+
+def test_checker_flags_operand_written_just_before():
+    bad = _kernel("\tv_cvt_pk_bf16_f32 v13, v1, v2\n" + ASM_MFMA + "\ts_endpgm\n")
+    assert len(H.check_operand_writes(bad)) == 1
+    bad2 = _kernel("\tv_cvt_pk_bf16_f32 v13, v1, v2\n\ts_nop 0\n" + ASM_MFMA + "\ts_endpgm\n")
+    assert len(H.check_operand_writes(bad2)) == 1
+    good = _kernel("\tv_cvt_pk_bf16_f32 v13, v1, v2\n\ts_nop 1\n" + ASM_MFMA + "\ts_endpgm\n")
+    assert H.check_operand_writes(good) == []
+    unrelated = _kernel("\tv_cvt_pk_bf16_f32 v20, v1, v2\n" + ASM_MFMA + "\ts_endpgm\n")
+    assert H.check_operand_writes(unrelated) == []
+
+
+@pytest.fixture(scope="module")
+def attention_asm(tmp_path_factory):
+    hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(hipcc):
+        pytest.skip("hipcc not available")
+    from block_sparse_sliding_amd import build as B
+
+    out = tmp_path_factory.mktemp("asm") / "sta_attention.s"
+    cmd = [hipcc, *B.HIPCC_FLAGS, *B.EXTRA_FLAGS.get("sta_attention.hip", []), "--cuda-device-only", "-S",
+           os.path.join(B.CSRC, "sta_attention.hip"), "-o", str(out)]
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    assert r.returncode == 0, r.stdout[-4000:]
+    return out.read_text()
+
+
+def test_forward_kernels_no_spills_no_asm_hazards(attention_asm):
+    kernels = H.parse(attention_asm)
+    names = sorted(k.name for k in kernels)
+    assert len(kernels) == 4, names  # D in {64, 128} x (tile-multiple video, partial tiles)
+    for k in kernels:
+        n_mfma = sum(H.is_asm_mfma(i) for i in k.instrs)
+        assert n_mfma > 0, k.name
+        assert k.scratch == 0, f"{k.name}: {k.scratch} bytes of scratch per lane"
+        assert k.vgpr_spills == 0, f"{k.name}: {k.vgpr_spills} VGPR spills"
+        problems = H.check_result_reads(k) + H.check_operand_writes(k)
+        assert problems == [], "\n".join(problems[:10])

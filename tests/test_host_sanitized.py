@@ -157,3 +157,50 @@ def test_helpers_match_oracle_maps(checks_bin, shape):
     if text:
         expect[n_tiles * 384:] = nv + np.arange(256)
     assert np.array_equal(t2r, expect)
+
+
+STREAM_SHAPES = [
+    # video, has_text, ell, window
+    ((18, 24, 24), 0, 0, (1, 3, 3)),
+    ((12, 16, 24), 1, 226, (1, 2, 3)),
+    ((13, 17, 20), 1, 226, (2, 2, 2)),   # partial tiles on every axis, ragged text
+    ((33, 45, 80), 0, 0, (3, 3, 3)),
+    ((7, 9, 11), 1, 50, (2, 2, 2)),
+    ((5, 7, 9), 0, 0, (1, 1, 2)),         # one partial tile: remainder blocks only
+    ((1, 1, 1), 1, 256, (1, 1, 1)),
+    ((6, 8, 8), 1, 17, (1, 1, 1)),
+    ((1, 100, 100), 1, 64, (1, 6, 6)),
+    ((9, 11, 3), 1, 1, (2, 2, 1)),
+]
+
+
+@pytest.mark.parametrize("shape", STREAM_SHAPES, ids=[f"{s[0]}w{s[3]}t{s[2] if s[1] else '-'}"
+                                                      for s in STREAM_SHAPES])
+def test_forward_key_stream_matches_oracle_mask(checks_bin, shape):
+    """Every query unit's key stream (as the forward kernel walks it) holds
+    exactly the keys the oracle's mask allows a query of that unit, each once;
+    masked blocks come only after the whole ones (checked in the program)."""
+    video, text, ell, win = shape
+    T, H, W = video
+    out = run(checks_bin, "stream", T, H, W, text, ell, *win).splitlines()
+    n, tile_of_row, tokens = oracle_maps(video)
+    n_tiles = int(np.prod(n))
+    nv = T * H * W
+    assert len(out) == n_tiles + text
+    first_row = np.full(n_tiles, -1)
+    first_row[tile_of_row[::-1]] = np.arange(nv)[::-1]  # a raster row of each tile
+    for ln in out:
+        f = ln.split()
+        u, n_blk, n_plain = int(f[1]), int(f[2]), int(f[3])
+        keys = np.concatenate([np.arange(*map(int, r.split(":"))) for r in f[4:]]) if f[4:] else np.zeros(0, int)
+        row = nv if u == n_tiles else int(first_row[u])
+        allowed = np.nonzero(oracle.allowed_mask([row], video, win, ell, bool(text))[0])[0]
+        assert np.array_equal(keys, allowed), f"unit {u}"
+        # block counts: every key tile in ceil(tokens / 64) blocks, then the text
+        if u == n_tiles:
+            ids = range(n_tiles)
+        else:
+            ids = oracle.key_tiles_of_query_tile(video, win, u) if n_tiles <= 40 else None
+        if ids is not None:
+            assert n_blk == sum(-(-int(tokens[i]) // 64) for i in ids) + -(-ell // 64), f"unit {u}"
+            assert n_plain == sum(int(tokens[i]) // 64 for i in ids) + ell // 64, f"unit {u}"
