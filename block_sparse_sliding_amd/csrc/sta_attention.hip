@@ -130,12 +130,34 @@ __device__ inline const KernelArgs* kernel_args() {
 
 // LDS-DMA of 16 bytes per lane from base + soff (wave-uniform) + voff (per
 // lane) into lds_dst + 16 lane, through a buffer resource over base (the
-// uniform part stays in a scalar register). (The buffer-resource type exists
-// in the device pass only.)
+// uniform part stays in scalar registers). The instruction is written as
+// inline asm on purpose: the compiler treats an LDS-DMA it can see as a store
+// to all of LDS and makes every later LDS read wait for it (vmcnt(0)), which
+// would expose the whole memory latency inside the MFMA loop. The kernel
+// orders these writes itself: every read of a block follows the s_waitcnt
+// vmcnt(0) and the barrier that close the block before it. (M0 holds the LDS
+// destination: it is saved and restored around the load, and one wait state
+// separates its write from the load that reads it. The statements exist in
+// the device pass only, as the host pass checks the constraints against the
+// host target.)
 __device__ inline void dma16_buf(const char* base, int voff, int soff, char* lds_dst) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, 0x7fffffff, 0x00020000);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_dst, 16, voff, soff, 0, 0);
+  typedef int i32x4 __attribute__((ext_vector_type(4)));
+  const unsigned long long b = reinterpret_cast<unsigned long long>(base);
+  const i32x4 rsrc = {int(unsigned(b)), int(unsigned(b >> 32) & 0xffffu), 0x7fffffff, 0x00020000};
+  const unsigned m0 = unsigned(reinterpret_cast<unsigned long long>((lds_void*)lds_dst));
+  unsigned saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, %4 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(rsrc), "s"(m0), "s"(soff)
+      : "memory");
+#else
+  (void)base, (void)voff, (void)soff, (void)lds_dst;
 #endif
 }
 
@@ -279,6 +301,21 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(KernelArgs) 
       }
     };
 
+    // One group (op < GPW: K group op, else V group op - GPW) of a full-frame
+    // block (kind 0), for DMA spread over the MFMA slots of a half-step.
+    auto issue_frame_op = [&](const KeyBlock& s, int k_stage_off, int v_stage_off, int op) {
+      const bool is_k = op < L::GPW;
+      const int i = is_k ? op : op - L::GPW;
+      const int ln = opaque_lane<true>(this_lane);
+      const int rr = (ln >> 2) % RPG, j4 = ln & 3, q4 = 4 * (ln / (4 * RPG));
+      const int G = wave * L::GPW + i, r0 = G * RPG;
+      const int x = ((G * RPG + rr) >> 2) & 3;
+      const int chunk = q4 + (is_k ? (j4 ^ x) : j4);
+      const int row0 = s.base + (r0 >> 3) * g.W + (r0 & 7);
+      dma16_buf(is_k ? kr : vr, rr * ROWB + chunk * 16, row0 * ROWB,
+                lds + (is_k ? k_stage_off : v_stage_off) + wave * L::GPW * 1024 + i * 1024);
+    };
+
     // ---- per-lane LDS read bases
     const int kl = lane & 31, kx = (kl >> 2) & 3;
     const int k_lane = (kl / RPG) * 1024 + (kl % RPG) * 64;
@@ -383,9 +420,10 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(KernelArgs) 
       // has scores of its own. voff / nvoff: byte offsets of the V stages of
       // this step's and the next step's P V; kst: K stage of the next half.
       constexpr int PF = 3;
+      auto no_hook = [](int) {};
       auto step = [&](auto do_s_c, auto do_pv_c, auto do_p_c, auto do_mask_c, auto kst, int voff, int vh, int kh,
                       int nvoff, int nvh, int lim, bf16x8 (&fr)[PF], f32x16 (&s_next)[QG], f32x16 (&s_cur)[QG],
-                      uint32_t (&p_prev)[QG][8], uint32_t (&p_cur)[QG][8]) {
+                      uint32_t (&p_prev)[QG][8], uint32_t (&p_cur)[QG][8], auto&& hook) {
         constexpr bool DO_S = decltype(do_s_c)::value, DO_PV = decltype(do_pv_c)::value;
         constexpr bool DO_P = decltype(do_p_c)::value, DO_MASK = decltype(do_mask_c)::value;
         const int KST = kst;
@@ -434,6 +472,7 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(KernelArgs) 
             s_next[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[f], qf[c][ks], ks == 0 ? f32x16{} : s_next[c],
                                                                 0, 0, 0);
           }
+          hook(k);
           if constexpr (DO_PV) {  // a previous half exists: finish its last scores
             if (k == 0) vstage(SLOTS, s_cur, p_prev, false, false, 0);
             if (k == 1) vstage(SLOTS + 1, s_cur, p_prev, false, false, 0);
@@ -581,25 +620,40 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(KernelArgs) 
         asm volatile("s_nop 2" ::: "memory");  // accumulator writes before the first asm MFMA
         // half-step 0: S(1) (K(0) half 1) and P(0); no P V yet
         step(T{}, F{}, T{}, F{}, std::integral_constant<int, 0>{}, voff_of(0), 0, 1, voff_of(0), 0, 64, fr, sb, sa,
-             pb, pa);
+             pb, pa, no_hook);
         if (s0.mask < 64) mask_half(sb, s0.mask - 32);  // S(1): block 0 half 1
         // body(j): half-steps 2j + 1 (scores K(j + 1) half 0 into S(2j + 2),
         // P V of half 2j = V(j) half 0, softmax of S(2j + 1): block j half 1)
         // and 2j + 2 (scores K(j + 1) half 1, P V of half 2j + 1, softmax of
         // S(2j + 2): block j + 1 half 0). mask_a, mask_b: the masks of the
         // halves consumed (64 when nothing is masked).
+        // Block j + 2 is fetched after the barrier; a block of full frames
+        // (the common case) one group at a time, spread over the MFMA slots
+        // of the first half-step, any other block at once.
         auto body = [&](auto mask_first_c, auto mask_second_c, auto kst, int j, int mask_a, int mask_b) {
           asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
           __syncthreads();
+          KeyBlock s2{};
+          bool spread = false;
+          const int k_off = (j & 1) * BLKB, v_off = 2 * BLKB + voff_of(j + 2);
           if (j + 2 < n_blk) {
-            const KeyBlock s2 = decode(j + 2);
-            issue(s2, (j & 1) * BLKB, true);
-            issue(s2, 2 * BLKB + voff_of(j + 2), false);
+            s2 = decode(j + 2);
             mask2 = s2.mask;
+            spread = s2.kind == 0;
+            if (!spread) {
+              issue(s2, k_off, true);
+              issue(s2, v_off, false);
+            }
           }
+          auto dma = [&](int k) {
+            constexpr int NOPS = 2 * L::GPW;
+            constexpr int SP = (SLOTS - 2) / NOPS > 0 ? (SLOTS - 2) / NOPS : 1;
+            if (k >= 2 && (k - 2) % SP == 0 && (k - 2) / SP < NOPS && spread)
+              issue_frame_op(s2, k_off, v_off, (k - 2) / SP);
+          };
           const int vj = voff_of(j), vj1 = voff_of(j + 1);
-          step(T{}, T{}, T{}, mask_first_c, kst, vj, 0, 0, vj, 1, mask_a, fr, sa, sb, pa, pb);
-          step(T{}, T{}, T{}, mask_second_c, kst, vj, 1, 1, vj1, 0, mask_b, fr, sb, sa, pb, pa);
+          step(T{}, T{}, T{}, mask_first_c, kst, vj, 0, 0, vj, 1, mask_a, fr, sa, sb, pa, pb, dma);
+          step(T{}, T{}, T{}, mask_second_c, kst, vj, 1, 1, vj1, 0, mask_b, fr, sb, sa, pb, pa, no_hook);
         };
         int mask0 = s0.mask;  // mask of block j in body(j)
         auto advance = [&]() {
@@ -638,8 +692,8 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(KernelArgs) 
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
         const int vj = voff_of(j);
-        step(F{}, T{}, T{}, T{}, 0, vj, 0, 0, vj, 1, mask0 - 32, fr, sa, sb, pa, pb);
-        step(F{}, T{}, F{}, F{}, 0, vj, 1, 0, vj, 1, 64, fr, sb, sa, pb, pa);
+        step(F{}, T{}, T{}, T{}, 0, vj, 0, 0, vj, 1, mask0 - 32, fr, sa, sb, pa, pb, no_hook);
+        step(F{}, T{}, F{}, F{}, 0, vj, 1, 0, vj, 1, 64, fr, sb, sa, pb, pa, no_hook);
         asm volatile("s_nop 15\n\ts_nop 7" ::: "memory");  // last MFMA results before any read
       };
 

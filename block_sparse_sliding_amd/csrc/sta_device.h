@@ -36,10 +36,33 @@ __device__ inline float swap32_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// LDS-DMA: each lane moves 16 bytes from its own global address into
-// `lds + lane * 16` (the LDS base is wave-uniform).
+// LDS-DMA: each lane moves 16 (dma16) or 4 (dma4) bytes from its own global
+// address into `lds + lane * 16` (or `lane * 4`); the LDS base is
+// wave-uniform. The instructions are written as inline asm on purpose: an
+// LDS-DMA the compiler can see counts as a store to all of LDS, so the
+// compiler makes every later LDS read wait for all outstanding loads
+// (vmcnt(0)), exposing the full memory latency in the middle of a block's
+// arithmetic. Every kernel here orders these writes itself: a block fetched
+// by LDS-DMA is read only after an explicit s_waitcnt vmcnt(0) and a
+// workgroup barrier. M0 holds the LDS destination; it is saved and restored
+// around the load, and one wait state separates its write from the load.
+// (The statements exist in the device pass only: the host pass checks asm
+// constraints against the host target.)
+#if defined(__HIP_DEVICE_COMPILE__)
+#define STA_GLOBAL_LOAD_LDS(OP, gsrc, lds_dst)                                                      \
+  do {                                                                                              \
+    unsigned saved_m0_;                                                                             \
+    const unsigned m0_ = unsigned(reinterpret_cast<unsigned long long>((lds_void*)(lds_dst)));      \
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t" OP " %1, off\n\ts_mov_b32 m0, %0" \
+                 : "=&s"(saved_m0_)                                                                  \
+                 : "v"(gsrc), "s"(m0_)                                                               \
+                 : "memory");                                                                       \
+  } while (0)
+#else
+#define STA_GLOBAL_LOAD_LDS(OP, gsrc, lds_dst) ((void)(gsrc), (void)(lds_dst))
+#endif
 __device__ inline void dma16(const char* gsrc, char* lds_dst) {
-  __builtin_amdgcn_global_load_lds(gsrc, (lds_void*)lds_dst, 16, 0, 0);
+  STA_GLOBAL_LOAD_LDS("global_load_lds_dwordx4", gsrc, lds_dst);
 }
 
 // Next query unit for a workgroup on XCD `xcd`, or -1 once every queue is
@@ -65,10 +88,9 @@ __device__ inline int div_by(int n, int d, uint32_t m) {
   return d == 1 ? n : int(__umulhi(uint32_t(n), m));
 }
 
-// LDS-DMA of one dword per lane: `lds + lane * 4` receives 4 bytes from the
-// lane's own global address.
+// LDS-DMA of one dword per lane (see dma16).
 __device__ inline void dma4(const char* gsrc, char* lds_dst) {
-  __builtin_amdgcn_global_load_lds(gsrc, (lds_void*)lds_dst, 4, 0, 0);
+  STA_GLOBAL_LOAD_LDS("global_load_lds_dword", gsrc, lds_dst);
 }
 
 // The lane id through an empty asm when OPAQUE: values derived from it are
