@@ -8,78 +8,69 @@
 // length is not a multiple of 64 (and, for video sizes that are not tile
 // multiples, the last block of a partial key tile).
 //
-// Work decomposition. A workgroup of 4 waves (one per SIMD) works on one query
-// unit at a time: a 384-row query tile (96 rows per wave), or the 256 text
-// query slots of one head (64 rows per wave). The grid is persistent: each
-// workgroup pops units from the queue of the XCD it runs on and, once that
-// queue is empty, from the other XCDs' queues. The key tiles of a unit's
-// window are enumerated in the kernel (residue order, see key_tile), so no
-// schedule list is read. Q rows are read from the caller's raster q through
-// the tile map, K and V rows from the caller's raster k and v (LDS-DMA, one
-// source address per lane, which applies the tile map), and O / lse are
-// written to raster positions.
+// Work decomposition. A workgroup works on one query unit at a time: a
+// 384-row query tile, 8 waves of 48 rows each (three 16-row column groups),
+// or the 256 text query slots of one head, 8 waves of 32 rows each; two waves
+// per SIMD, one workgroup per CU. The grid is persistent: each workgroup pops
+// units from the queue of the XCD it runs on and, once that queue is empty,
+// from the other XCDs' queues. The kernel enumerates each unit's key blocks
+// itself (KeyStream: the window's key tiles in residue order, then the text),
+// reads Q rows from the caller's raster q through the tile map, streams K and
+// V rows from the caller's raster k and v into LDS with LDS-DMA (one source
+// address per lane, which applies the tile map), and writes O and lse to
+// raster positions. Two LDS stages of one 64-key block (K and V), one barrier
+// per block; block j + 1 is fetched while block j is computed.
 //
-// Products: v_mfma_f32_32x32x16_bf16 throughout.
-//   S^T = K Q^T    A = K fragment (lane l: key 32h + l%32, d 16ks + 8(l/32)
-//                  .. +8), B = Q^T fragment (registers, loaded once per unit).
-//                  Lane l then holds the scores of query l%32 for keys
-//                  8(i/4) + 4(l/32) + i%4, i = 0..15, of each 32-key half.
-//   O^T += V^T P^T A = V^T fragment read with ds_read_b64_tr_b16 from V rows
-//                  in LDS (the transposing read turns 4 keys x 16 columns of
-//                  row-major V into the k-contiguous operand), B = P^T from
-//                  the lane's own registers: the 16 scores of a half are two
-//                  16-key chunks in exactly the key order the A operand uses.
-//                  The accumulators live in AGPRs (inline-asm MFMAs with "+a"
-//                  operands); the score MFMAs write VGPRs.
+// Per block and wave, with v_mfma_f32_16x16x32_bf16:
+//   S^T = K Q^T   A = K fragment (lane l: key 16kt + l%16, d 32ks + 8(l/16)
+//                 .. +8), B = Q^T fragment (registers, loaded once per unit).
+//                 Lane l then holds the scores of query l%16 for keys
+//                 16kt + 4(l/16) + r, r = 0..3.
+//   softmax       p = 2^(c s - m), c = log2(e)/sqrt(D) applied in fp32 (one
+//                 v_fma_f32 and one v_exp_f32 per score), p rounded to bf16;
+//                 the row sums accumulate the rounded p (v_dot2_f32_bf16).
+//   O^T += V^T P^T  B = P^T from the lane's own registers (half h: keys
+//                 32h + 4(l/16) + r and 32h + 16 + 4(l/16) + r), A = V^T
+//                 fragment in the same key order, two ds_read_b64_tr_b16 from
+//                 V rows in LDS (each gives lane l four consecutive keys of one
+//                 column; see the V layout below).
 //
-// Software pipeline. Each 64-key block is two 32-key halves; half-step hh
-// issues, for all 96 rows of the wave, the score MFMAs of half hh + 1 and the
-// P V MFMAs of half hh - 1, and between consecutive MFMAs one slice of the
-// softmax of half hh: p = 2^(c s - m) (one v_fma_f32, one v_exp_f32), pairs
-// rounded to bf16 (v_cvt_pk_bf16_f32, the P operand) and summed into the row
-// sum (v_dot2_f32_bf16 with ones). The fma, exp and pack of one score sit in
-// three consecutive MFMA slots, so no VALU instruction waits on the one
-// before it; one wave per SIMD then keeps the matrix core busy while it
-// issues the softmax. K and V each have two LDS stages; the K stream runs one
-// block ahead of the V stream, and one barrier per block orders the LDS-DMA
-// writes against the reads.
-//
-// Softmax reference. The reference m of a row is the exact maximum of its
-// scaled scores over the first 32 keys of the unit, and it never moves:
-// p = 2^(c s - m) stays within fp32 as long as no later score exceeds m by
-// about 127 (log2 units). At the end of a unit, a row whose sum of p reaches
-// 2^32 (some later key scored at least 32 above the first half's maximum)
+// Softmax reference. m of a row is the exact maximum of its scaled scores
+// over the first key block of the unit, and it never moves: p = 2^(c s - m)
+// stays finite while no later score exceeds m by about 127 (log2 units). A
+// row whose sum of p reaches 2^32 (some key at least 32 above the reference)
 // makes the workgroup redo the unit with m set to the row's maximum over all
 // its keys, found by a pass that computes only the scores. With random data
 // the redo never happens; large score jumps between key tiles trigger it.
+// Any reference gives the same softmax up to rounding.
 //
-// LDS layouts (row-major rows of D bf16 = 2D bytes, grouped by 1 KB: RPG rows
-// per group, 4 for D = 128 and 8 for D = 64; a group is one LDS-DMA
-// instruction). Inside a group, 16-byte chunk c of group row rr sits at
-// (c / 4) * RPG * 64 + rr * 64 + 16 * (c % 4) for V, and at the same place
-// with c % 4 replaced by (c % 4) XOR ((row / 4) % 4) for K. A score-MFMA K
-// read (16 lanes per LDS cycle, rows {0-3, 12-15, 20-23, 24-27} or the other
-// parity class, one chunk) then covers all 64 banks, and so does a V^T
-// transposing read (4 rows x 64 bytes per 32 lanes); every read address is one
-// of a few per-lane bases plus a compile-time offset.
+// LDS layouts. K block (64 rows of D bf16): each 1 KB LDS-DMA transfer fills
+// a group of 1024 / (2D) consecutive rows, interleaved at 64-byte granularity
+// (quad k of every row of the group, then quad k + 1, ...), chunk j of row r
+// of a quad at position j XOR (2 * bit 3 of r): every K fragment read (16 rows
+// x one 16-byte chunk, served 16 lanes per LDS cycle) covers all 64 banks.
+// V block: column-pair major, pair P = columns 32P .. 32P + 31 of all 64 rows,
+// 64 bytes per row (4 KB per pair). A transposing read of column unit d (16
+// columns) then takes 8 bytes at (lane / 4) * 64 + (lane % 4) * 8 from a
+// compile-time offset: each 16 lanes read 4 rows x 32 bytes at a 64-byte
+// stride, which fall in distinct banks; the LDS-DMA that fills a pair fetches
+// 64 contiguous bytes of each row.
 //
 // Masking. Keys that must not contribute (text slots at or after text_length;
 // with PAD, keys past a partial tile's tokens) are fetched from a zero row in
 // the workspace, K and V alike, and their scores are replaced by -inf before
-// the exponential; their p is exactly 0 and their V rows are zeros, so the
-// contents of padded text slots never reach a result.
+// the exponential: their p is exactly 0 and their V rows are zeros, so the
+// contents of padded text slots never reach a result. KeyStream puts every
+// block that can hold such keys after all whole blocks.
 //
 // Video sizes that are not tile multiples (PAD): the last tile along an axis
 // holds the remainder. A partial key tile streams ceil(tokens / 64) blocks of
-// its existing tokens in compact order (frame, row, column); its full blocks
-// take their place in the walk, and its last, partial block is deferred to a
-// tail of masked blocks after all whole ones (KeyStream), so the main loop
-// runs the unmasked half-steps only and the masked variant appears in the
-// tail alone (one loop holding both would exceed the register file). A video unit's
-// rows are its tile's existing tokens in compact order; a tile of at most 128
-// or 256 tokens runs with 32 or 64 rows per wave, and a wave whose rows all lie
-// past the tokens only loads and synchronises. Rows past the tokens compute on
-// a valid row and are not written.
+// its existing tokens in compact order (frame, row, column). A video unit's
+// rows are its tile's existing tokens in compact order; a partial tile of at
+// most 128, 192 or 256 tokens runs with 8 waves x 16 rows, 4 waves x 48 or 8
+// waves x 32; a wave whose rows all lie past the tokens only loads and
+// synchronises; rows past the tokens compute on a valid row and are not
+// written.
 // Epilogue: O = O^T / l rounded to bf16, lse = (m + log2 l) * ln 2, at raster rows.
 #include <type_traits>
 
@@ -89,13 +80,15 @@
 namespace sta {
 namespace {
 
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-constexpr int kWaves = 4;  // one wave per SIMD
+constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
+constexpr int kRowsPerWave = kUnitRows / kWaves;  // 48
+constexpr int kQT = kRowsPerWave / 16;            // 3 query column groups per wave
+constexpr int kKPrefetch = 4;                     // K fragments in flight in the score loop
+constexpr int kVPrefetch = 2;                     // V^T fragments in flight in the P V loop
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kRedoSum = 4294967296.0f;  // 2^32: a row sum this large redoes the unit
 
@@ -113,33 +106,12 @@ __device__ inline const KernelArgs* kernel_args() {
   return (const KernelArgs*)kp;
 }
 
-// O^T += V^T P^T on AGPR accumulators (the compiler's hazard checks do not see
-// inline asm: every VGPR this reads was written at least two instructions
-// earlier, see the slot order, and the accumulators are read only after an
-// explicit wait).
-// (The host pass of this single-source file checks asm constraints against
-// the host target, where "a" means a general register: the statements exist
-// in the device pass only.)
-#if defined(__HIP_DEVICE_COMPILE__)
-#define STA_PV_MFMA_ASM(NOP, acc, vf, pf) \
-  asm volatile(NOP "v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(vf), "v"(pf))
-#else
-#define STA_PV_MFMA_ASM(NOP, acc, vf, pf) ((void)(acc), (void)(vf), (void)(pf))
-#endif
-#define STA_PV_MFMA(acc, vf, pf) STA_PV_MFMA_ASM("", acc, vf, pf)
-
 // LDS-DMA of 16 bytes per lane from base + soff (wave-uniform) + voff (per
 // lane) into lds_dst + 16 lane, through a buffer resource over base (the
-// uniform part stays in scalar registers). The instruction is written as
-// inline asm on purpose: the compiler treats an LDS-DMA it can see as a store
-// to all of LDS and makes every later LDS read wait for it (vmcnt(0)), which
-// would expose the whole memory latency inside the MFMA loop. The kernel
-// orders these writes itself: every read of a block follows the s_waitcnt
-// vmcnt(0) and the barrier that close the block before it. (M0 holds the LDS
-// destination: it is saved and restored around the load, and one wait state
-// separates its write from the load that reads it. The statements exist in
-// the device pass only, as the host pass checks the constraints against the
-// host target.)
+// uniform part stays in scalar registers). Written as inline asm for the
+// reason given at dma16: the kernel orders these writes itself. M0 holds the
+// LDS destination: saved and restored around the load, one wait state between
+// its write and the load. (Device pass only.)
 __device__ inline void dma16_buf(const char* base, int voff, int soff, char* lds_dst) {
 #if defined(__HIP_DEVICE_COMPILE__)
   typedef int i32x4 __attribute__((ext_vector_type(4)));
@@ -161,29 +133,18 @@ __device__ inline void dma16_buf(const char* base, int voff, int soff, char* lds
 #endif
 }
 
-template <int D>
-struct Lay {
-  static constexpr int ROWB = 2 * D;        // bytes per row
-  static constexpr int RPG = 1024 / ROWB;   // rows per 1 KB group
-  static constexpr int KS = D / 16;         // k-steps of the score MFMAs
-  static constexpr int DT = D / 32;         // 32-column tiles of O
-  static constexpr int BLKB = 64 * ROWB;    // bytes of a 64-row K or V block
-  static constexpr int GPB = 64 / RPG;      // 1 KB groups per block
-  static constexpr int GPW = GPB / kWaves;  // groups per wave
-  static constexpr int NVF = 2 * DT;        // V^T fragments per half (2 chunks of 16 keys x DT)
-  static constexpr int NF = NVF + KS;       // fragments per half-step
-  static constexpr int SPS = 16 / NF;       // scores (per lane and query group) per MFMA slot
-  static constexpr int QSEG = RPG * 64;     // bytes between chunk quads inside a group
-  static_assert(GPW >= 1 && GPB % kWaves == 0, "groups split evenly over the waves");
-};
-
 template <int D, bool PAD>
 __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(KernelArgs) {
-  using L = Lay<D>;
-  constexpr int ROWB = L::ROWB, RPG = L::RPG, KS = L::KS, DT = L::DT, BLKB = L::BLKB;
-  // K stages at [0, 2 BLKB), V stages at [2 BLKB, 5 BLKB)
-  __shared__ __attribute__((aligned(1024))) char lds[5 * BLKB];
-  __shared__ int shared_word[2];
+  constexpr int KS = D / 32;                  // k-steps of S^T
+  constexpr int DT = D / 16;                  // d groups of O^T (and V column units)
+  constexpr int ROWB = D * 2;                 // bytes per row
+  constexpr int BLK = kKeyBlock * ROWB;       // bytes of one K (or V) block
+  constexpr int RPI = 1024 / ROWB;            // K rows per 1 KB LDS-DMA instruction
+  constexpr int IPW = BLK / 1024 / kWaves;    // DMA instructions per wave per tensor
+  constexpr int VPAIR = kKeyBlock * 64;       // bytes of one V column pair (4 KB)
+  static_assert(IPW >= 1 && BLK % (1024 * kWaves) == 0, "block must split over the waves");
+  __shared__ __attribute__((aligned(1024))) char lds[2][2][BLK];  // [stage][K|V]
+  __shared__ int shared_word[2];                                  // claimed unit, redo flag
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   for (;;) {
@@ -255,446 +216,256 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(KernelArgs) 
     const char* __restrict__ vr = reinterpret_cast<const char*>(a.v) + slab * 2;
     const char* __restrict__ zr = reinterpret_cast<const char*>(a.zero_row);
 
-    auto decode = [&](int j) { return keys.block(g, j); };
-    auto reset_walk = [&]() { keys.reset(); };
+    // Chunk permutation of K row r inside its 64-byte quad (see the layout above).
+    auto sw = [](int row) { return (row >> 2) & 2; };
 
-    // ---- LDS-DMA of one block (this wave's GPW groups). Lane p of a group
-    // covers group row rr = (p / 4) % RPG and chunk 4 (p / (4 RPG)) + p % 4,
-    // XOR-ed with the row's (row / 4) % 4 for K. The source of a full frame's
-    // rows (the common case) is a wave-uniform row pointer plus a per-lane
-    // offset; text rows past the valid length and, with PAD, keys past a
-    // partial tile's tokens come from the zero row.
-    auto issue = [&](const KeyBlock& s, int stage_off, bool is_k) {
+    // ---- LDS-DMA of one key block into stage st: this wave's IPW groups of K
+    // and of V. K group q holds rows q RPI .. + RPI - 1; lane p covers row
+    // rin = (p / 4) % RPI and chunk 4 (p / (4 RPI)) + (p % 4 XOR sw). V group q
+    // holds rows 16 (q % 4) .. + 15 of column pair q / 4; lane p covers row
+    // 16 (q % 4) + p / 4 and bytes 64 (q / 4) + 16 (p % 4) .. + 15 of it.
+    auto issue = [&](const KeyBlock& s, int st) {
       const int ln = opaque_lane<true>(this_lane);
-      const int rr = (ln >> 2) % RPG, j4 = ln & 3, q4 = 4 * (ln / (4 * RPG));
-      const char* base = is_k ? kr : vr;
-      char* dst = lds + stage_off + wave * L::GPW * 1024;
-      auto chunk = [&](int G) {  // this lane's chunk for group G
-        const int x = ((G * RPG + rr) >> 2) & 3;
-        return q4 + (is_k ? (j4 ^ x) : j4);
-      };
+      const int rin = (ln >> 2) % RPI;
+      const int kchunk_hi = 4 * (ln / (4 * RPI));
+      const int vr_lane = ln >> 2, vb_lane = 16 * (ln & 3);
       if (s.kind == 0) {
+        // full frames: block row r at raster s.base + (r / 8) W + r % 8; each
+        // K group lies in one 8-row run, each V group spans 2 runs
 #pragma unroll
-        for (int i = 0; i < L::GPW; ++i) {
-          const int G = wave * L::GPW + i, r0 = G * RPG;
-          // rows r0 .. r0 + RPG - 1 lie in one 8-row run of the frame
-          const int row0 = s.base + (r0 >> 3) * g.W + (r0 & 7);
-          dma16_buf(base, rr * ROWB + chunk(G) * 16, row0 * ROWB, dst + i * 1024);
+        for (int i = 0; i < IPW; ++i) {
+          const int q = wave * IPW + i, r0 = q * RPI;
+          const int chunk = kchunk_hi + ((ln & 3) ^ sw(r0 + rin));
+          const int krow0 = s.base + (r0 >> 3) * g.W + (r0 & 7);
+          dma16_buf(kr, rin * ROWB + chunk * 16, krow0 * ROWB, &lds[st][0][q * 1024]);
+          const int vrow0 = s.base + 2 * (q & 3) * g.W;
+          const int voff = ((vr_lane >> 3) * g.W + (vr_lane & 7)) * ROWB + vb_lane;
+          dma16_buf(vr, voff, vrow0 * ROWB + 64 * (q >> 2), &lds[st][1][q * 1024]);
         }
       } else if (!PAD || s.kind == 1) {
+        // consecutive raster rows s.base + r, valid while r < s.lim
 #pragma unroll
-        for (int i = 0; i < L::GPW; ++i) {
-          const int G = wave * L::GPW + i, r = G * RPG + rr;
-          const char* src = r < s.lim ? base + size_t(s.base + r) * ROWB : zr;
-          dma16(src + chunk(G) * 16, dst + i * 1024);
+        for (int i = 0; i < IPW; ++i) {
+          const int q = wave * IPW + i, r = q * RPI + rin;
+          const int chunk = kchunk_hi + ((ln & 3) ^ sw(r));
+          const char* ks = r < s.lim ? kr + size_t(s.base + r) * ROWB : zr;
+          dma16(ks + chunk * 16, &lds[st][0][q * 1024]);
+          const int rv = 16 * (q & 3) + vr_lane;
+          const char* vs = rv < s.lim ? vr + size_t(s.base + rv) * ROWB : zr;
+          dma16(vs + 64 * (q >> 2) + vb_lane, &lds[st][1][q * 1024]);
         }
       } else {
+        // PAD: compact token 64 s.sub + r of a partial tile, valid while it exists
         const int n_tok = extent_tokens(s.ext);
-#pragma unroll
-        for (int i = 0; i < L::GPW; ++i) {
-          const int G = wave * L::GPW + i, tok = s.sub * kKeyBlock + G * RPG + rr;
+        auto src = [&](const char* base, int r) -> const char* {
+          const int tok = s.sub * kKeyBlock + r;
           int dt, dh, dw;
           compact_token(tok < n_tok ? tok : 0, s.ext, dt, dh, dw);
-          const char* src = tok < n_tok ? base + size_t(s.base + (dt * g.H + dh) * g.W + dw) * ROWB : zr;
-          dma16(src + chunk(G) * 16, dst + i * 1024);
-        }
-      }
-    };
-
-    // One group (op < GPW: K group op, else V group op - GPW) of a full-frame
-    // block (kind 0), for DMA spread over the MFMA slots of a half-step.
-    auto issue_frame_op = [&](const KeyBlock& s, int k_stage_off, int v_stage_off, int op) {
-      const bool is_k = op < L::GPW;
-      const int i = is_k ? op : op - L::GPW;
-      const int ln = opaque_lane<true>(this_lane);
-      const int rr = (ln >> 2) % RPG, j4 = ln & 3, q4 = 4 * (ln / (4 * RPG));
-      const int G = wave * L::GPW + i, r0 = G * RPG;
-      const int x = ((G * RPG + rr) >> 2) & 3;
-      const int chunk = q4 + (is_k ? (j4 ^ x) : j4);
-      const int row0 = s.base + (r0 >> 3) * g.W + (r0 & 7);
-      dma16_buf(is_k ? kr : vr, rr * ROWB + chunk * 16, row0 * ROWB,
-                lds + (is_k ? k_stage_off : v_stage_off) + wave * L::GPW * 1024 + i * 1024);
-    };
-
-    // ---- per-lane LDS read bases
-    const int kl = lane & 31, kx = (kl >> 2) & 3;
-    const int k_lane = (kl / RPG) * 1024 + (kl % RPG) * 64;
-    const int kb_even = k_lane + (((lane >> 5)) ^ kx) * 16;
-    const int kb_odd = k_lane + ((2 | (lane >> 5)) ^ kx) * 16;
-    const int vi = lane & 15;
-    const int vrow = 4 * (lane >> 5) + (vi >> 2);  // row inside a 16-key chunk
-    const int vb = 2 * BLKB + (vrow / RPG) * 1024 + (vrow % RPG) * 64 + 32 * ((lane >> 4) & 1) + 8 * (vi & 1) +
-                   16 * ((vi & 3) >> 1);
-    const char* lds_ke = lds + kb_even;
-    const char* lds_ko = lds + kb_odd;
-    const char* lds_v = lds + vb;
-
-    const float qs = a.q_scale;  // log2(e)/sqrt(D)
-    const bf16x2 ones2 = {(__bf16)1.0f, (__bf16)1.0f};
-
-    // The rest runs with QG query groups of 32 rows per wave: 3 for a video
-    // tile, 2 for the text slots (and partial tiles of 129..256 tokens), 1 for
-    // partial tiles of at most 128 tokens.
-    auto run = [&](auto qg_c) {
-      constexpr int QG = decltype(qg_c)::value;
-      constexpr int RPW = 32 * QG;
-      constexpr int NF = L::NF, NVF = L::NVF, SPS = L::SPS;
-      constexpr int SLOTS = NF * QG;  // MFMAs per half-step
-      constexpr int NSC = 16 * QG;    // scores per lane per half-step
-      const bool active = wave * RPW < q_rows;
-      (void)active;
-
-      // Q^T fragments: lane l, group c, step ks: row 32 c + l % 32 of this wave,
-      // columns 16 ks + 8 (l / 32) .. + 8 (rows past the unit clamp to its last)
-      bf16x8 qf[QG][KS];
-#pragma unroll
-      for (int c = 0; c < QG; ++c) {
-        int row = wave * RPW + 32 * c + (lane & 31);
-        row = row < q_rows ? row : q_rows - 1;
-        const __bf16* src = reinterpret_cast<const __bf16*>(a.q) + slab + size_t(query_raster(row)) * D +
-                            8 * (lane >> 5);
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) qf[c][ks] = *reinterpret_cast<const bf16x8*>(src + 16 * ks);
-      }
-
-      f32x16 acc[QG][DT];
-      float lsum[QG], m_run[QG];
-
-      // K fragment ks of K half kh in K stage kst (compile-time offsets when
-      // the stage is)
-      auto kfrag = [&](int kst, int kh, int ks) -> bf16x8 {
-        return *reinterpret_cast<const bf16x8*>(((ks & 1) ? lds_ko : lds_ke) + kst * BLKB + (32 * kh) / RPG * 1024 +
-                                                (ks >> 1) * L::QSEG);
-      };
-      // V^T fragment f (chunk f / DT, tile f % DT) of V half vh at V offset voff
-      auto vfrag_at = [&](int voff, int vh, int f) -> bf16x8 {
-        const int kc = f / DT, dt = f % DT;
-        const char* p = lds_v + voff + (32 * vh + 16 * kc) / RPG * 1024 + dt * L::QSEG;
-        const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
-        const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 8 / RPG * 1024));
-        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
-      };
-
-      // softmax pipeline state: t = c s - m of the last scores (stage A),
-      // e = exponentials by group and element parity (stage B)
-      float vt[2 * SPS];
-      float ve[QG][2];
-      // slot k, stage A of scores SPS k .. SPS k + SPS - 1, B of the SPS
-      // before, C (pack + row sum) of those before that; score sc is element
-      // i = sc / QG of group c = sc % QG
-      auto vstage = [&](int k, f32x16 (&s)[QG], uint32_t (&pw)[QG][8], bool do_a, bool do_mask, int lim_lane) {
-#pragma unroll
-        for (int x = 0; x < SPS; ++x) {
-          const int c2 = SPS * (k - 2) + x;  // stage C
-          if (c2 >= 0 && c2 < NSC && ((c2 / QG) & 1)) {
-            const int c = c2 % QG, i = c2 / QG;
-            const bf16x2 pr = __builtin_convertvector((f32x2){ve[c][0], ve[c][1]}, bf16x2);
-            lsum[c] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones2, lsum[c], false);
-            pw[c][i >> 1] = __builtin_bit_cast(uint32_t, pr);
-          }
-        }
-#pragma unroll
-        for (int x = 0; x < SPS; ++x) {
-          const int b1 = SPS * (k - 1) + x;  // stage B
-          if (b1 >= 0 && b1 < NSC) ve[b1 % QG][(b1 / QG) & 1] = __builtin_amdgcn_exp2f(vt[b1 % (2 * SPS)]);
-        }
-        if (do_a) {
-#pragma unroll
-          for (int x = 0; x < SPS; ++x) {
-            const int a0 = SPS * k + x;  // stage A
-            const int i = a0 / QG;
-            const float t = __builtin_fmaf(s[a0 % QG][i], qs, -m_run[a0 % QG]);
-            // masked half: key 8 (i / 4) + 4 (l / 32) + i % 4 at or past the limit
-            vt[a0 % (2 * SPS)] = (do_mask && 8 * (i >> 2) + (i & 3) >= lim_lane) ? -INFINITY : t;
-          }
-        }
-      };
-
-      // One half-step: SLOTS MFMA slots over NF fragments x QG groups.
-      // Fragment f + PF is read when fragment f is first used; V^T fragments
-      // of the next half-step are read during the last slots. Scores of
-      // s_cur pass through the softmax stages, one group of SPS per slot; the
-      // last scores' B and C stages run in the first slots of the next
-      // half-step (carried through vt / ve). DO_S, DO_PV, DO_P: whether the
-      // step scores the next half, multiplies the previous half's P by V, and
-      // has scores of its own. voff / nvoff: byte offsets of the V stages of
-      // this step's and the next step's P V; kst: K stage of the next half.
-      constexpr int PF = 3;
-      auto no_hook = [](int) {};
-      auto step = [&](auto do_s_c, auto do_pv_c, auto do_p_c, auto do_mask_c, auto kst, int voff, int vh, int kh,
-                      int nvoff, int nvh, int lim, bf16x8 (&fr)[PF], f32x16 (&s_next)[QG], f32x16 (&s_cur)[QG],
-                      uint32_t (&p_prev)[QG][8], uint32_t (&p_cur)[QG][8], auto&& hook) {
-        constexpr bool DO_S = decltype(do_s_c)::value, DO_PV = decltype(do_pv_c)::value;
-        constexpr bool DO_P = decltype(do_p_c)::value, DO_MASK = decltype(do_mask_c)::value;
-        const int KST = kst;
-        // masked half: this lane's keys 8 (i / 4) + 4 (l / 32) + i % 4 at or past lim are dead
-        const int lim_lane = lim - 4 * (lane >> 5);
-        // opaque stage offsets (32-bit LDS byte offsets): every V^T read is
-        // one of them plus an immediate
-        int vcur = vb + voff + (32 * vh) / RPG * 1024;
-        int vnext = vb + nvoff + (32 * nvh) / RPG * 1024;
-        asm volatile("" : "+v"(vcur), "+v"(vnext));
-        auto vfrag = [&](int vb0, int f) -> bf16x8 {
-          const int kc = f / DT, dt = f % DT;
-          const char* p = lds + vb0 + (16 * kc) / RPG * 1024 + dt * L::QSEG;
-          const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
-          const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 8 / RPG * 1024));
-          return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+          return tok < n_tok ? base + size_t(s.base + (dt * g.H + dh) * g.W + dw) * ROWB : zr;
         };
-        bf16x8 ring[NF + PF];
 #pragma unroll
-        for (int i = 0; i < PF; ++i) ring[i] = fr[i];
+        for (int i = 0; i < IPW; ++i) {
+          const int q = wave * IPW + i, r = q * RPI + rin;
+          const int chunk = kchunk_hi + ((ln & 3) ^ sw(r));
+          dma16(src(kr, r) + chunk * 16, &lds[st][0][q * 1024]);
+          dma16(src(vr, 16 * (q & 3) + vr_lane) + 64 * (q >> 2) + vb_lane, &lds[st][1][q * 1024]);
+        }
+      }
+    };
+
+    // The rest runs with QT query column groups per wave: 3 (8 x 48 = 384
+    // rows) for a video tile, 2 (8 x 32 = 256 rows) for the text query slots;
+    // a partial tile also uses 1 (16 rows per wave) or 3 with only waves 0-3
+    // holding rows.
+    auto run = [&](auto qt_c) {
+      constexpr int QT = decltype(qt_c)::value;
+      constexpr int RPW = QT * 16;  // query rows per wave
+      const bool active = wave * RPW < q_rows;
+      const float qs = a.q_scale;  // log2(e)/sqrt(D), applied to the fp32 scores
+
+      // Q^T fragments for this wave's rows (rows past the unit clamp to its last)
+      bf16x8 qf[QT][KS];
 #pragma unroll
-        for (int k = 0; k < SLOTS; ++k) {
-          const int f = k / QG, c = k % QG;
-          if (c == 0) {
-            const int nf = f + PF;
-            if (nf < NVF) {
-              if (DO_PV) ring[nf] = vfrag(vcur, nf);
-            } else if (nf < NF) {
-              if (DO_S) ring[nf] = kfrag(KST, kh, nf - NVF);
-            } else {
-              ring[nf] = vfrag(vnext, nf - NF);  // next half-step's V^T
-            }
-          }
-          if (f < NVF) {
-            if constexpr (DO_PV) {
-              const int kc = f / DT, dt = f % DT;
-              const bf16x8 pb = __builtin_bit_cast(
-                  bf16x8, (uint4){p_prev[c][4 * kc], p_prev[c][4 * kc + 1], p_prev[c][4 * kc + 2], p_prev[c][4 * kc + 3]});
-              if (kc == 1 && dt == 0)  // its last dwords may have been packed in slot 0 or 1
-                STA_PV_MFMA_ASM("s_nop 1\n\t", acc[c][dt], ring[f], pb);
-              else
-                STA_PV_MFMA(acc[c][dt], ring[f], pb);
-            }
-          } else if constexpr (DO_S) {
-            const int ks = f - NVF;
-            s_next[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[f], qf[c][ks], ks == 0 ? f32x16{} : s_next[c],
-                                                                0, 0, 0);
-          }
-          hook(k);
-          if constexpr (DO_PV) {  // a previous half exists: finish its last scores
-            if (k == 0) vstage(SLOTS, s_cur, p_prev, false, false, 0);
-            if (k == 1) vstage(SLOTS + 1, s_cur, p_prev, false, false, 0);
-          }
-          if constexpr (DO_P) vstage(k, s_cur, p_cur, true, DO_MASK, lim_lane);
+      for (int c = 0; c < QT; ++c) {
+        int row = wave * RPW + c * 16 + (lane & 15);
+        row = row < q_rows ? row : q_rows - 1;
+        const bf16x8* src = reinterpret_cast<const bf16x8*>(reinterpret_cast<const __bf16*>(a.q) + slab +
+                                                            size_t(query_raster(row)) * D + (lane >> 4) * 8);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) qf[c][ks] = src[ks * 4];
+      }
+
+      f32x4 acc[QT][DT];
+      float l_part[QT];  // this lane's share of the row sum of p
+      float m_run[QT];   // reference of the scaled scores (log2 units)
+      bf16x2 ones2;
+      ones2[0] = (__bf16)1.0f;
+      ones2[1] = (__bf16)1.0f;
+
+      // K fragment (row 16kt + lane%16, chunk 4ks + lane/16) of a block sits at
+      // kofs + kt * 16 * ROWB + ks * 64 * RPI
+      const int l15 = lane & 15;
+      const int kofs = (l15 / RPI) * 1024 + (l15 % RPI) * 64 + (((lane >> 4) ^ sw(l15)) << 4);
+
+      // S^T of the block in stage `stage`, keys at or past `mask` (< 64) set to -inf
+      auto scores = [&](f32x4 (&s)[QT][4], int stage, int mask) {
+        const char* kb = lds[stage][0];
+        constexpr int NF = 4 * KS;
+        bf16x8 kf[NF];
+        auto kload = [&](int f) {
+          kf[f] = *reinterpret_cast<const bf16x8*>(kb + kofs + (f & 3) * 16 * ROWB + (f >> 2) * 64 * RPI);
+        };
+#pragma unroll
+        for (int f = 0; f < kKPrefetch; ++f) kload(f);
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+          const int ks = f >> 2, kt = f & 3;
+#pragma unroll
+          for (int c = 0; c < QT; ++c)
+            s[c][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[f], qf[c][ks],
+                                                              ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : s[c][kt], 0, 0, 0);
+          if (f + kKPrefetch < NF) kload(f + kKPrefetch);
           __builtin_amdgcn_sched_barrier(0);
         }
+        if (mask < kKeyBlock) {
+          int key0 = 4 * (lane >> 4);
+          asm volatile("" : "+v"(key0));  // build the lane masks here, not before the loop
 #pragma unroll
-        for (int i = 0; i < PF; ++i) fr[i] = ring[NF + i];
+          for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (key0 + 16 * kt + r >= mask)
+#pragma unroll
+                for (int c = 0; c < QT; ++c) s[c][kt][r] = -INFINITY;
+        }
       };
-
-      // replace the scores of keys at or past `lim` (0..32, within a half) by -inf
-      auto mask_half = [&](f32x16 (&s)[QG], int lim) {
-        int key0 = 4 * (lane >> 5);
-        asm volatile("" : "+v"(key0));
+      // exact scaled row maxima of a block's scores (each row's 64 keys are
+      // spread over the 4 lanes l%16 + 16i)
+      auto row_max = [&](const f32x4 (&s)[QT][4], float (&mx)[QT]) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const bool dead = key0 + 8 * (i >> 2) + (i & 3) >= lim;
+        for (int c = 0; c < QT; ++c) {
+          float x = s[c][0][0];
 #pragma unroll
-          for (int c = 0; c < QG; ++c) s[c][i] = dead ? -INFINITY : s[c][i];
+          for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) x = fmaxf(x, s[c][kt][r]);
+          mx[c] = swap32_max(swap16_max(x));
         }
       };
 
-      // scores of one half of the block in K stage kst, with masking
-      auto scores = [&](f32x16 (&s)[QG], int kst, int kh, int mask) {
+      // ---- the main pass; m_run is known (from the max pass) when `known`
+      auto main_pass = [&](bool known) {
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const bf16x8 x = kfrag(kst, kh, ks);
+        for (int c = 0; c < QT; ++c) {
 #pragma unroll
-          for (int c = 0; c < QG; ++c)
-            s[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, qf[c][ks], ks == 0 ? f32x16{} : s[c], 0, 0, 0);
+          for (int d = 0; d < DT; ++d) acc[c][d] = f32x4{0.f, 0.f, 0.f, 0.f};
+          l_part[c] = 0.f;
         }
-        if (mask - 32 * kh < 32) mask_half(s, mask - 32 * kh);
-      };
-
-      // Streaming (main pass): blocks 0 and 1 are fetched before the first
-      // barrier; after the barrier of block j (which follows the wait for
-      // this wave's own loads) block j + 2 is fetched, K into K stage j % 2
-      // and V into V stage (j + 2) % 3. K(j) was last read in half-step 2j
-      // and V(j - 1) in half-step 2j, both before that barrier; K(j + 2) is
-      // first read in half-step 2j + 3 and V(j + 2) at the end of half-step
-      // 2j + 4, both after the next barrier.
-      auto voff_of = [](int j) { return (j % 3) * BLKB; };
-
-      // ---- an idle wave of a partial unit: the same loads and barriers
-      auto idle_main = [&]() {
-        reset_walk();
-        const KeyBlock s0 = decode(0);
-        issue(s0, 0, true);
-        issue(s0, 2 * BLKB + voff_of(0), false);
-        if (n_blk > 1) {
-          const KeyBlock s1 = decode(1);
-          issue(s1, BLKB, true);
-          issue(s1, 2 * BLKB + voff_of(1), false);
-        }
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
+        keys.reset();
+        KeyBlock s_cur = keys.block(g, 0);
+        issue(s_cur, 0);
         for (int j = 0; j < n_blk; ++j) {
+          const int stage = j & 1;
           asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
           __syncthreads();
-          if (j + 2 < n_blk) {
-            const KeyBlock s2 = decode(j + 2);
-            issue(s2, (j & 1) * BLKB, true);
-            issue(s2, 2 * BLKB + voff_of(j + 2), false);
+          f32x4 s[QT][4];
+          scores(s, stage, j >= n_plain ? s_cur.mask : kKeyBlock);
+          if (j + 1 < n_blk) {
+            s_cur = keys.block(g, j + 1);
+            issue(s_cur, stage ^ 1);
+          }
+          if (j == 0 && !known) {
+            float mx[QT];
+            row_max(s, mx);
+#pragma unroll
+            for (int c = 0; c < QT; ++c) m_run[c] = mx[c] * qs;
+          }
+          // p = 2^(c s - m) rounded to bf16; O^T += V^T P^T; row sums += 1^T P^T
+          const char* vb = lds[stage][1] + (lane >> 2) * 64 + (lane & 3) * 8;
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            // V^T fragment d of this half: keys 32h + 4(l/16) + e and
+            // 32h + 16 + 4(l/16) + e of column 16d + l%16; kVPrefetch of them
+            // are read ahead (the first ones under the exponentials)
+            bf16x8 vf[DT];
+            auto vload = [&](int d) {
+              const char* p0 = vb + (d >> 1) * VPAIR + 32 * (d & 1) + 32 * h * 64;
+              const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p0);
+              const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0 + 16 * 64));
+              vf[d] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+            };
+#pragma unroll
+            for (int d = 0; d < kVPrefetch; ++d) vload(d);
+            bf16x8 pb[QT];
+#pragma unroll
+            for (int c = 0; c < QT; ++c) {
+              f32x8 p;
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[c][2 * h][r], qs, -m_run[c]));
+                p[4 + r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[c][2 * h + 1][r], qs, -m_run[c]));
+              }
+              pb[c] = __builtin_convertvector(p, bf16x8);
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const bf16x2 pair = {pb[c][2 * i], pb[c][2 * i + 1]};
+                l_part[c] = __builtin_amdgcn_fdot2_f32_bf16(pair, ones2, l_part[c], false);
+              }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int d = 0; d < DT; ++d) {
+#pragma unroll
+              for (int c = 0; c < QT; ++c)
+                acc[c][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[d], pb[c], acc[c][d], 0, 0, 0);
+              if (d + kVPrefetch < DT) vload(d + kVPrefetch);
+              __builtin_amdgcn_sched_barrier(0);
+            }
           }
         }
       };
-      auto idle_max = [&]() {
-        reset_walk();
-        for (int j = 0; j < n_blk; ++j) {
-          const KeyBlock s = decode(j);
-          issue(s, 0, true);
-          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-          __syncthreads();
-          __syncthreads();
-        }
-      };
 
-      // ---- pass 1 (rare): the exact row maxima over all keys, scores only
+      // ---- pass 1 of a redo: the exact row maxima over all keys, scores only
       auto max_pass = [&]() {
-        float mx[QG];
+        float mx[QT];
 #pragma unroll
-        for (int c = 0; c < QG; ++c) mx[c] = -INFINITY;
-        reset_walk();
+        for (int c = 0; c < QT; ++c) mx[c] = -INFINITY;
+        keys.reset();
         for (int j = 0; j < n_blk; ++j) {
-          const KeyBlock s = decode(j);
-          issue(s, 0, true);
+          const KeyBlock s_j = keys.block(g, j);
+          issue(s_j, 0);
           asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
           __syncthreads();
+          f32x4 s[QT][4];
+          scores(s, 0, j >= n_plain ? s_j.mask : kKeyBlock);
+          float bm[QT];
+          row_max(s, bm);
 #pragma unroll
-          for (int kh = 0; kh < 2; ++kh) {
-            f32x16 sc[QG];
-            scores(sc, 0, kh, s.mask);
-#pragma unroll
-            for (int c = 0; c < QG; ++c)
-#pragma unroll
-              for (int i = 0; i < 16; ++i) mx[c] = fmaxf(mx[c], sc[c][i]);
-          }
+          for (int c = 0; c < QT; ++c) mx[c] = fmaxf(mx[c], bm[c]);
           __syncthreads();  // every wave has read the stage before it is refilled
         }
 #pragma unroll
-        for (int c = 0; c < QG; ++c) m_run[c] = swap32_max(mx[c]) * qs;
+        for (int c = 0; c < QT; ++c) m_run[c] = mx[c] * qs;
       };
 
-      // ---- the pipelined pass; m_run was set by max_pass when `known`
-      auto main_pass = [&](bool known) {
-        using T = std::true_type;
-        using F = std::false_type;
-#pragma unroll
-        for (int c = 0; c < QG; ++c) {
-#pragma unroll
-          for (int d = 0; d < DT; ++d) acc[c][d] = f32x16{};
-          lsum[c] = 0.f;
-        }
-        reset_walk();
-        const KeyBlock s0 = decode(0);
-        issue(s0, 0, true);
-        issue(s0, 2 * BLKB + voff_of(0), false);
-        int mask1 = 64;  // mask of block j + 1 in body(j)
-        int mask2 = 64;  // mask of block j + 2
-        if (n_blk > 1) {
-          const KeyBlock s1 = decode(1);
-          issue(s1, BLKB, true);
-          issue(s1, 2 * BLKB + voff_of(1), false);
-          mask1 = s1.mask;
-        }
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        f32x16 sa[QG], sb[QG];
-        uint32_t pa[QG][8], pb[QG][8];
-        scores(sa, 0, 0, s0.mask);  // S(0), masked
-        if (!known) {
-          // the reference: exact maximum of each row's scaled scores over half 0
-#pragma unroll
-          for (int c = 0; c < QG; ++c) {
-            float x = sa[c][0];
-#pragma unroll
-            for (int i = 1; i < 16; ++i) x = fmaxf(x, sa[c][i]);
-            m_run[c] = swap32_max(x) * qs;
-          }
-        }
-        bf16x8 fr[PF];
-#pragma unroll
-        for (int i = 0; i < PF; ++i) fr[i] = vfrag_at(voff_of(0), 0, i);
-        asm volatile("s_nop 2" ::: "memory");  // accumulator writes before the first asm MFMA
-        // half-step 0: S(1) (K(0) half 1) and P(0); no P V yet
-        step(T{}, F{}, T{}, F{}, std::integral_constant<int, 0>{}, voff_of(0), 0, 1, voff_of(0), 0, 64, fr, sb, sa,
-             pb, pa, no_hook);
-        if (s0.mask < 64) mask_half(sb, s0.mask - 32);  // S(1): block 0 half 1
-        // body(j): half-steps 2j + 1 (scores K(j + 1) half 0 into S(2j + 2),
-        // P V of half 2j = V(j) half 0, softmax of S(2j + 1): block j half 1)
-        // and 2j + 2 (scores K(j + 1) half 1, P V of half 2j + 1, softmax of
-        // S(2j + 2): block j + 1 half 0). mask_a, mask_b: the masks of the
-        // halves consumed (64 when nothing is masked).
-        // Block j + 2 is fetched after the barrier; a block of full frames
-        // (the common case) one group at a time, spread over the MFMA slots
-        // of the first half-step, any other block at once.
-        auto body = [&](auto mask_first_c, auto mask_second_c, auto kst, int j, int mask_a, int mask_b) {
+      // ---- a wave without rows: the same loads and barriers
+      auto idle_main = [&]() {
+        keys.reset();
+        issue(keys.block(g, 0), 0);
+        for (int j = 0; j < n_blk; ++j) {
           asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
           __syncthreads();
-          KeyBlock s2{};
-          bool spread = false;
-          const int k_off = (j & 1) * BLKB, v_off = 2 * BLKB + voff_of(j + 2);
-          if (j + 2 < n_blk) {
-            s2 = decode(j + 2);
-            mask2 = s2.mask;
-            spread = s2.kind == 0;
-            if (!spread) {
-              issue(s2, k_off, true);
-              issue(s2, v_off, false);
-            }
-          }
-          auto dma = [&](int k) {
-            constexpr int NOPS = 2 * L::GPW;
-            constexpr int SP = (SLOTS - 2) / NOPS > 0 ? (SLOTS - 2) / NOPS : 1;
-            if (k >= 2 && (k - 2) % SP == 0 && (k - 2) / SP < NOPS && spread)
-              issue_frame_op(s2, k_off, v_off, (k - 2) / SP);
-          };
-          const int vj = voff_of(j), vj1 = voff_of(j + 1);
-          step(T{}, T{}, T{}, mask_first_c, kst, vj, 0, 0, vj, 1, mask_a, fr, sa, sb, pa, pb, dma);
-          step(T{}, T{}, T{}, mask_second_c, kst, vj, 1, 1, vj1, 0, mask_b, fr, sb, sa, pb, pa, no_hook);
-        };
-        int mask0 = s0.mask;  // mask of block j in body(j)
-        auto advance = [&]() {
-          mask0 = mask1;
-          mask1 = mask2;
-          mask2 = 64;
-        };
-        // bodies j with j + 1 < n_plain consume unmasked halves only
-        int j = 0;
-        for (; j + 2 < n_plain; j += 2) {
-          body(F{}, F{}, std::integral_constant<int, 1>{}, j, 64, 64);
-          advance();
-          body(F{}, F{}, std::integral_constant<int, 0>{}, j + 1, 64, 64);
-          advance();
+          if (j + 1 < n_blk) issue(keys.block(g, j + 1), (j & 1) ^ 1);
         }
-        if (j + 1 < n_plain) {
-          body(F{}, F{}, std::integral_constant<int, 1>{}, j, 64, 64);
-          advance();
-          ++j;
+      };
+      auto idle_max = [&]() {
+        keys.reset();
+        for (int j = 0; j < n_blk; ++j) {
+          issue(keys.block(g, j), 0);
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+          __syncthreads();
+          __syncthreads();
         }
-        if constexpr (!PAD) {
-          // only the last block can be masked: body(n_blk - 2) consumes its half 0
-          if (j + 1 < n_blk) {
-            body(F{}, T{}, 1 - (j & 1), j, 64, mask1);
-            advance();
-            ++j;
-          }
-        } else {
-          for (; j + 1 < n_blk; ++j) {  // the masked tail
-            body(T{}, T{}, 1 - (j & 1), j, mask0 - 32, mask1);
-            advance();
-          }
-        }
-        // the last block j = n_blk - 1: half-step 2j + 1 (P V of half 2j,
-        // softmax of block j half 1, masked) and 2j + 2 (P V of half 2j + 1)
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        const int vj = voff_of(j);
-        step(F{}, T{}, T{}, T{}, 0, vj, 0, 0, vj, 1, mask0 - 32, fr, sa, sb, pa, pb, no_hook);
-        step(F{}, T{}, F{}, F{}, 0, vj, 1, 0, vj, 1, 64, fr, sb, sa, pb, pa, no_hook);
-        asm volatile("s_nop 15\n\ts_nop 7" ::: "memory");  // last MFMA results before any read
       };
 
       if (!active) {
@@ -708,13 +479,13 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(KernelArgs) 
         return;
       }
       // a second pass, with the exact row maxima as reference, when some
-      // row's sum (relative to its first half's maximum) got large
+      // row's sum (relative to the first block's maximum) got large
       for (bool known = false;; known = true) {
         main_pass(known);
         if (known) break;
         bool redo = false;
 #pragma unroll
-        for (int c = 0; c < QG; ++c) redo |= !(swap32_sum(lsum[c]) < kRedoSum);
+        for (int c = 0; c < QT; ++c) redo |= !(swap32_sum(swap16_sum(l_part[c])) < kRedoSum);
         if (__builtin_amdgcn_ballot_w64(redo) != 0 && lane == 0) shared_word[1] = 1;
         __syncthreads();
         if (__builtin_amdgcn_readfirstlane(shared_word[1]) == 0) break;
@@ -722,37 +493,38 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(KernelArgs) 
         max_pass();
       }
 
-      // ---- epilogue: O = O^T / l (bf16) and lse at raster rows; lane l holds
-      // query 32 c + l % 32, columns 32 dt + 8 g + 4 (l / 32) + 0..3 in
-      // accumulator registers 4 g .. 4 g + 3
+      // ---- epilogue: O = O^T / l in bf16 and lse, straight to raster positions
       __bf16* __restrict__ outr = reinterpret_cast<__bf16*>(a.out) + slab;
       float* __restrict__ lser = a.lse == nullptr ? nullptr : a.lse + size_t(bh) * g.S;
 #pragma unroll
-      for (int c = 0; c < QG; ++c) {
-        const float l = swap32_sum(lsum[c]);
+      for (int c = 0; c < QT; ++c) {
+        const float l = swap32_sum(swap16_sum(l_part[c]));
         const float inv = __builtin_amdgcn_rcpf(l);
-        const int row = wave * RPW + 32 * c + (lane & 31);
+        const int row = wave * RPW + c * 16 + (lane & 15);
         if (row < q_rows) {
           const int rr = query_raster(row);
-          __bf16* dst = outr + size_t(rr) * D + 4 * (lane >> 5);
+          __bf16* dst = outr + size_t(rr) * D + (lane >> 4) * 4;
 #pragma unroll
-          for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-            for (int gq = 0; gq < 4; ++gq) {
-              const f32x4 o = {acc[c][dt][4 * gq] * inv, acc[c][dt][4 * gq + 1] * inv, acc[c][dt][4 * gq + 2] * inv,
-                               acc[c][dt][4 * gq + 3] * inv};
-              *reinterpret_cast<bf16x4*>(dst + 32 * dt + 8 * gq) = __builtin_convertvector(o, bf16x4);
-            }
-          if (lser != nullptr && lane < 32) lser[rr] = (m_run[c] + __builtin_amdgcn_logf(l)) * kLn2;
+          for (int d = 0; d < DT; ++d) {
+            const f32x4 o = acc[c][d] * inv;
+            *reinterpret_cast<bf16x4*>(dst + d * 16) = __builtin_convertvector(o, bf16x4);
+          }
+          if (lser != nullptr && lane < 16) lser[rr] = (m_run[c] + __builtin_amdgcn_logf(l)) * kLn2;
         }
       }
     };
-    if (text_unit || (PAD && q_rows > 4 * 32 && q_rows <= kTextSlots))
-      run(std::integral_constant<int, 2>{});
-    else if (PAD && q_rows <= 4 * 32)
-      run(std::integral_constant<int, 1>{});
+    if constexpr (PAD) {
+      if (!text_unit && q_rows <= 16 * kWaves) {  // a small partial tile: 8 (or fewer) waves x 16 rows
+        run(std::integral_constant<int, 1>{});
+        continue;
+      }
+    }
+    // 8 waves x 32 rows for the text slots and for partial tiles of 193 to 256
+    // tokens; otherwise 48 rows per wave (4 waves do the work for at most 192)
+    if (text_unit || (PAD && q_rows > 4 * 16 * kQT && q_rows <= kTextSlots))
+      run(std::integral_constant<int, kTextSlots / 16 / kWaves>{});
     else
-      run(std::integral_constant<int, 3>{});
+      run(std::integral_constant<int, kQT>{});
   }
 }
 
