@@ -23,10 +23,11 @@ LIB_PATH = os.path.join(_PKG, "libsta.so")
 STATUS = {
     0: "STA_OK", 1: "STA_ERR_NULL", 2: "STA_ERR_SHAPE", 3: "STA_ERR_WINDOW", 4: "STA_ERR_TEXT",
     5: "STA_ERR_ALIGN", 6: "STA_ERR_WORKSPACE", 7: "STA_ERR_HIP", 8: "STA_ERR_ALIAS",
+    9: "STA_ERR_SCRATCH",
 }
 EXPORTS = (
     "sta_status_str", "sta_seq_len", "sta_tiled_seq_len", "sta_workspace_bytes", "sta_forward",
-    "sta_forward_timed",
+    "sta_forward_timed", "sta_forward_noalloc",
     "sta_tile_gather",
     "sta_tile_scatter", "sta_schedule_sizes", "sta_build_schedule",
     "sta_backward_workspace_bytes", "sta_backward", "sta_backward_timed",
@@ -75,6 +76,8 @@ def load_library() -> ctypes.CDLL:
     lib.sta_forward_timed.argtypes = [PD, P, P, P, PI32, I32, I32, P, P, P, ctypes.c_size_t, P,
                                       ctypes.POINTER(ctypes.c_void_p)]
     lib.sta_forward_timed.restype = ctypes.c_int
+    lib.sta_forward_noalloc.argtypes = [PD, P, P, P, PI32, I32, I32, P, P, P]
+    lib.sta_forward_noalloc.restype = ctypes.c_int
     lib.sta_tile_gather.argtypes = [PD, I32, P, P, P]
     lib.sta_tile_gather.restype = ctypes.c_int
     lib.sta_tile_scatter.argtypes = [PD, I32, P, P, P]
@@ -158,14 +161,28 @@ def sta_forward(dims: sta_dims, q, k, v, window_sizes, text_length: int, has_tex
     _check(code, "sta_forward")
 
 
+NOALLOC_SCRATCH_BYTES = 1 << 20  # STA_NOALLOC_SCRATCH_BYTES
+
+
+def sta_forward_noalloc(dims: sta_dims, q, k, v, window_sizes, text_length: int, has_text: bool,
+                        out, lse, stream=None) -> None:
+    """sta_forward without a workspace argument: the library's fixed per-GPU
+    scratch array takes its place (nothing is allocated); see include/sta.h."""
+    wa = window_array(window_sizes, dims.heads)
+    code = load_library().sta_forward_noalloc(
+        ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), wa, int(text_length), int(has_text),
+        _ptr(out), _ptr(lse), _stream(stream))
+    _check(code, "sta_forward_noalloc")
+
+
 TIMED_EVENTS = 3
 STAGES = ("schedule_work", "attention")
 
 
 def sta_forward_timed(dims: sta_dims, q, k, v, window_sizes, text_length: int, has_text: bool,
                       out, lse, workspace, events, stream=None) -> None:
-    """sta_forward that records ``events`` (5 torch.cuda.Event, timing enabled)
-    before the first launch and after each of the 4 launches on the stream."""
+    """sta_forward that records ``events`` (3 torch.cuda.Event, timing enabled)
+    before the first launch and after each of the 2 launches on the stream."""
     if len(events) != TIMED_EVENTS:
         raise ValueError(f"need {TIMED_EVENTS} events")
     handles = (ctypes.c_void_p * TIMED_EVENTS)(*[e.cuda_event for e in events])

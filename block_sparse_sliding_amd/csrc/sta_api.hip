@@ -3,6 +3,7 @@
 //
 // Validation is plain C++ and runs before any HIP call, so argument errors
 // are reported synchronously and can be exercised without a GPU.
+#include <atomic>
 #include <cmath>
 #include <cstring>
 
@@ -125,6 +126,8 @@ const char* sta_status_str(sta_status s) {
     case STA_ERR_WORKSPACE: return "STA_ERR_WORKSPACE: workspace missing or too small";
     case STA_ERR_HIP: return "STA_ERR_HIP: HIP runtime error at launch";
     case STA_ERR_ALIAS: return "STA_ERR_ALIAS: output overlaps an input";
+    case STA_ERR_SCRATCH:
+      return "STA_ERR_SCRATCH: the shape needs more workspace than sta_forward_noalloc's fixed scratch";
   }
   return "STA_ERR_UNKNOWN";
 }
@@ -292,6 +295,58 @@ sta_status sta_forward_timed(const sta_dims* dims, const void* q, const void* k,
     if (events[i] == nullptr) return STA_ERR_NULL;
   return forward_impl(dims, q, k, v, window_sizes, text_length, has_text, out, lse, workspace,
                       workspace_bytes, stream, events);
+}
+
+}  // extern "C"
+
+// ------------------------------------------- forward without a workspace
+namespace {
+
+// (Plain C++ builds of this file, which check the host logic with the HIP
+// calls stubbed, lack the HIP compiler's spellings of these two.)
+#ifndef __align__
+#define __align__(n) __attribute__((aligned(n)))
+#endif
+#ifndef HIP_SYMBOL
+#define HIP_SYMBOL(x) x
+#endif
+
+// The workspace of sta_forward_noalloc: a fixed array in device memory, one
+// per GPU. In host code `scratch` is only a stand-in for the symbol; its
+// device address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) char scratch[STA_NOALLOC_SCRATCH_BYTES];
+constexpr int kScratchDevices = 64;
+std::atomic<void*> g_scratch_addr[kScratchDevices];
+
+sta_status scratch_address(void** addr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kScratchDevices) return STA_ERR_HIP;
+  void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    // the current device is the one the array's address is taken on
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return STA_ERR_HIP;
+    g_scratch_addr[dev].store(p, std::memory_order_release);
+  }
+  *addr = p;
+  return STA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+sta_status sta_forward_noalloc(const sta_dims* dims, const void* q, const void* k, const void* v,
+                               const int32_t* window_sizes, int32_t text_length, int32_t has_text,
+                               void* out, float* lse, void* stream) {
+  Geom g;
+  sta_status st = make_geom(dims, has_text, text_length, &g);
+  if (st != STA_OK) return st;
+  if (carve(g).total > STA_NOALLOC_SCRATCH_BYTES) return STA_ERR_SCRATCH;
+  void* ws = nullptr;
+  st = scratch_address(&ws);
+  if (st != STA_OK) return st;
+  return forward_impl(dims, q, k, v, window_sizes, text_length, has_text, out, lse, ws,
+                      STA_NOALLOC_SCRATCH_BYTES, stream, nullptr);
 }
 
 }  // extern "C"

@@ -63,7 +63,9 @@ typedef enum {
   STA_ERR_ALIGN = 5,     /* a device pointer is not 16-byte aligned             */
   STA_ERR_WORKSPACE = 6, /* workspace NULL or smaller than sta_workspace_bytes  */
   STA_ERR_HIP = 7,       /* the HIP runtime reported an error at launch         */
-  STA_ERR_ALIAS = 8      /* out (or lse) overlaps an input                      */
+  STA_ERR_ALIAS = 8,     /* out (or lse) overlaps an input                      */
+  STA_ERR_SCRATCH = 9    /* sta_forward_noalloc: the shape needs more workspace
+                            than its fixed scratch (STA_NOALLOC_SCRATCH_BYTES)  */
 } sta_status;
 
 #define STA_MAX_HEADS 256
@@ -149,6 +151,29 @@ sta_status sta_forward_timed(const sta_dims* dims, const void* q, const void* k,
                              int32_t text_length, int32_t has_text, void* out,
                              float* lse, void* workspace, size_t workspace_bytes,
                              void* stream, void* const* events);
+
+/*
+ * sta_forward for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc. The
+ * arguments and results are those of sta_forward without the workspace; its
+ * place is taken by a fixed device array of STA_NOALLOC_SCRATCH_BYTES inside
+ * the library, one per GPU, which the GPU holds until the process ends (its
+ * address is looked up once per device, on the first call there). Nothing is
+ * allocated or freed, by this call or by anything it calls. Every call on a
+ * GPU uses that GPU's one array and finds it as the previous call left it;
+ * the work-queue heads and the zero row that must start at zero are cleared
+ * by the call's own first kernel. Calls that overlap on one GPU (other
+ * streams, other threads) race on the array: order them on one stream.
+ * Returns STA_ERR_SCRATCH, before any launch, when sta_workspace_bytes for
+ * the shape exceeds STA_NOALLOC_SCRATCH_BYTES (enough for about 260 000
+ * query units, B*heads*(n_t*n_h*n_w + has_text)), STA_ERR_HIP when the
+ * array's address cannot be obtained, otherwise what sta_forward returns.
+ */
+#define STA_NOALLOC_SCRATCH_BYTES (1u << 20)
+sta_status sta_forward_noalloc(const sta_dims* dims, const void* q, const void* k,
+                               const void* v, const int32_t* window_sizes,
+                               int32_t text_length, int32_t has_text, void* out,
+                               float* lse, void* stream);
 
 /*
  * Tile-major gather of one bf16 tensor. The tile is the one the STA README

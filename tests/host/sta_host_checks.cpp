@@ -50,6 +50,17 @@ extern "C" hipError_t hipEventRecord(hipEvent_t, hipStream_t) {
   ++g_events;
   return hipSuccess;
 }
+// the no-workspace forward's scratch: one fake device address, looked up once
+int g_symbol_lookups = 0;
+extern "C" hipError_t hipGetDevice(int* dev) {
+  *dev = 0;
+  return hipSuccess;
+}
+extern "C" hipError_t hipGetSymbolAddress(void** p, const void*) {
+  ++g_symbol_lookups;
+  *p = reinterpret_cast<void*>(uintptr_t(40) * 64 * (uintptr_t(1) << 30));
+  return hipSuccess;
+}
 
 namespace sta {
 hipError_t launch_rows_permute(const Geom& g, const void* src, void* dst, bool, hipStream_t) {
@@ -260,6 +271,33 @@ void validate() {
     st = sta_backward(&s.d, q, k, v, out, lse, dout, ws_win.data(), s.ell, s.text, dq, dq, dv, ws,
                       nb, nullptr);
     CHECK(st == STA_ERR_ALIAS && g_launches.empty(), "backward, dk over dq");
+  }
+  // the forward without a workspace: its kernels get the scratch array only
+  {
+    const uintptr_t scratch = uintptr_t(40) * 64 * (uintptr_t(1) << 30);
+    const sta_dims d{2, 24, 128, 30, 48, 80};
+    std::vector<int32_t> w = windows_for(d.heads, 3, 3, 3);
+    for (int call = 0; call < 2; ++call) {
+      g_launches.clear();
+      sta_status st = sta_forward_noalloc(&d, q, k, v, w.data(), 226, 1, out, lse, nullptr);
+      CHECK(st == STA_OK, "noalloc forward returned %s", sta_status_str(st));
+      CHECK(!g_launches.empty() && g_launches.back().name == "attention", "noalloc: attention launched last");
+      for (const Launch& l : g_launches)
+        check_in_workspace(l, {P(q), P(k), P(v), P(out), P(lse)}, scratch, STA_NOALLOC_SCRATCH_BYTES);
+    }
+    CHECK(g_symbol_lookups == 1, "scratch address looked up %d times", g_symbol_lookups);
+    // a shape whose workspace exceeds the scratch is rejected before any launch
+    const sta_dims big{16, 256, 64, 60, 64, 64};
+    std::vector<int32_t> wb = windows_for(big.heads, 1, 1, 1);
+    CHECK(sta_workspace_bytes(&big, wb.data(), 0) > STA_NOALLOC_SCRATCH_BYTES, "big shape");
+    g_launches.clear();
+    sta_status st = sta_forward_noalloc(&big, q, k, v, wb.data(), 0, 0, out, lse, nullptr);
+    CHECK(st == STA_ERR_SCRATCH && g_launches.empty(), "noalloc, oversize: %s", sta_status_str(st));
+    // argument errors are those of sta_forward
+    st = sta_forward_noalloc(&d, q, k, v, w.data(), 300, 1, out, lse, nullptr);
+    CHECK(st == STA_ERR_TEXT && g_launches.empty(), "noalloc, bad text length: %s", sta_status_str(st));
+    st = sta_forward_noalloc(&d, q, k, v, w.data(), 226, 1, q, lse, nullptr);
+    CHECK(st == STA_ERR_ALIAS && g_launches.empty(), "noalloc, out over q: %s", sta_status_str(st));
   }
   std::printf("ok %d\n", g_checks);
 }
