@@ -15,3 +15,11 @@ from .sta_oracle import (  # noqa: F401
     sta_reference,
     sta_reference_backward,
 )
+from .hilbert_oracle import (  # noqa: F401
+    hilbert_d2xy,
+    hilbert_xy2d,
+    hilbert_token_order,
+    hilbert_allowed_mask,
+    hilbert_reference,
+    block_counts,
+)
