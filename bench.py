@@ -73,6 +73,24 @@ def effective_flops(wl, include_pad_rows=False) -> float:
     return 4.0 * wl.head_dim * pairs * wl.batch
 
 
+def hilbert_flops(wl) -> float:
+    """4*D per allowed pair of Hilbert slide/window attention: a video query sees
+    the 64 tokens of each key tile of its window (W tiles for slide; the tiles of
+    its aligned group for window) and the valid text keys; valid text queries
+    see every video token and the valid text keys."""
+    _, H, W = wl.video
+    nv = H * W
+    n = nv // 64
+    ell = wl.text_length if wl.has_text else 0
+    Wl = wl.hilbert_len
+    if wl.hilbert_mode == 1:
+        key_tiles = n * Wl
+    else:
+        key_tiles = sum(min(Wl, n - (i // Wl) * Wl) for i in range(n))
+    pairs = 64 * (64 * key_tiles) + nv * ell + ell * (nv + ell)
+    return 4.0 * wl.head_dim * pairs * wl.heads * wl.batch
+
+
 def kernel_suffix(wl) -> str:
     """Template arguments of the kernels a workload runs: <D, PAD>, PAD when a
     video size is not a tile multiple."""
@@ -201,6 +219,10 @@ def main():
     ws = torch.empty(sta.sta_workspace_bytes(dims, windows, wl.has_text), dtype=torch.uint8,
                      device="cuda")
     stream = torch.cuda.current_stream()
+    if wl.hilbert_len:
+        if args.which == "backward":
+            raise SystemExit("the Hilbert workload has no backward")
+        return bench_hilbert(args, wl, q, k, v, dims, out, lse)
     if args.which == "backward":
         return bench_backward(args, wl, windows, q, k, v, dims, out, lse, ws)
 
@@ -272,6 +294,64 @@ def main():
         result["copy_calibration_bytes"] = copy_calibration(args.copy_calibration_mib)
     if args.cpu_budget > 0:
         result["cpu_baseline"] = cpu_baseline(wl, q, k, v, args.cpu_budget, flops)
+    print(json.dumps(result), flush=True)
+
+
+def bench_hilbert(args, wl, q, k, v, dims, out, lse):
+    """Hilbert-window attention (sta_hilbert_forward) on a 2D image workload:
+    whole calls timed with events on the launch stream."""
+    import numpy as np
+    import torch
+
+    import block_sparse_sliding_amd as sta
+    import oracle
+
+    lens = [w[2] for w in wl.windows]
+    ws = torch.empty(sta.sta_hilbert_workspace_bytes(dims, wl.has_text), dtype=torch.uint8, device="cuda")
+
+    def step():
+        sta.sta_hilbert_forward(dims, q, k, v, lens, wl.hilbert_mode, wl.text_length, wl.has_text, out, lse, ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(args.steps):
+        step()
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+    flops = hilbert_flops(wl)
+    tflops = flops / (ms * 1e-3) / 1e12
+    result = {
+        "metric": "Hilbert-window attention fwd ms/call + effective TFLOP/s (% bf16 MFMA peak)",
+        "value": tflops, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic", "config": wl.describe(), "ms_per_call": ms,
+        "pct_bf16_peak": 100.0 * tflops / PEAK_BF16_TFLOPS, "effective_flop_per_call": flops,
+        "roofline": {"kernel": "sta_attention_kernel<%d, true, true> (whole call)" % wl.head_dim,
+                     "bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tflops / PEAK_BF16_TFLOPS, "traffic": None, "launch_ms": ms},
+    }
+    if args.cpu_budget > 0:
+        mode = "slide" if wl.hilbert_mode == 1 else "window"
+        rows = np.arange(0, wl.seq_len, max(1, wl.seq_len // 256))
+        done, elapsed, heads = 0, 0.0, 0
+        for h in range(wl.heads):
+            t0 = time.perf_counter()
+            oracle.hilbert_reference(q[:, h:h + 1].cpu(), k[:, h:h + 1].cpu(), v[:, h:h + 1].cpu(), [lens[h]],
+                                     mode, wl.text_length, wl.has_text, wl.video[1:], rows=rows)
+            elapsed += time.perf_counter() - t0
+            done += len(rows)
+            heads += 1
+            if elapsed >= args.cpu_budget:
+                break
+        full_s = elapsed / done * wl.batch * wl.heads * wl.seq_len
+        result["cpu_baseline"] = {"value": flops / full_s / 1e12, "unit": "TFLOP/s",
+                                  "cores": int(os.cpu_count() or 1), "kind": "oracle", "host": host_cpu(),
+                                  "sample": f"{done} evenly spaced rows x {heads} heads, {elapsed:.1f} s, "
+                                            f"extrapolated to {wl.batch * wl.heads * wl.seq_len} rows"}
     print(json.dumps(result), flush=True)
 
 

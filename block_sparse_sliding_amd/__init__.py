@@ -28,6 +28,7 @@ STATUS = {
 EXPORTS = (
     "sta_status_str", "sta_seq_len", "sta_tiled_seq_len", "sta_workspace_bytes", "sta_forward",
     "sta_forward_timed", "sta_forward_noalloc",
+    "sta_hilbert_workspace_bytes", "sta_hilbert_forward", "sta_hilbert_gather", "sta_hilbert_scatter",
     "sta_tile_gather",
     "sta_tile_scatter", "sta_schedule_sizes", "sta_build_schedule",
     "sta_backward_workspace_bytes", "sta_backward", "sta_backward_timed",
@@ -76,6 +77,14 @@ def load_library() -> ctypes.CDLL:
     lib.sta_forward_timed.argtypes = [PD, P, P, P, PI32, I32, I32, P, P, P, ctypes.c_size_t, P,
                                       ctypes.POINTER(ctypes.c_void_p)]
     lib.sta_forward_timed.restype = ctypes.c_int
+    lib.sta_hilbert_workspace_bytes.argtypes = [PD, I32]
+    lib.sta_hilbert_workspace_bytes.restype = ctypes.c_size_t
+    lib.sta_hilbert_forward.argtypes = [PD, P, P, P, PI32, I32, I32, I32, P, P, P, ctypes.c_size_t, P]
+    lib.sta_hilbert_forward.restype = ctypes.c_int
+    lib.sta_hilbert_gather.argtypes = [PD, I32, P, P, P]
+    lib.sta_hilbert_gather.restype = ctypes.c_int
+    lib.sta_hilbert_scatter.argtypes = [PD, I32, P, P, P]
+    lib.sta_hilbert_scatter.restype = ctypes.c_int
     lib.sta_forward_noalloc.argtypes = [PD, P, P, P, PI32, I32, I32, P, P, P]
     lib.sta_forward_noalloc.restype = ctypes.c_int
     lib.sta_tile_gather.argtypes = [PD, I32, P, P, P]
@@ -159,6 +168,38 @@ def sta_forward(dims: sta_dims, q, k, v, window_sizes, text_length: int, has_tex
         ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), wa, int(text_length), int(has_text),
         _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes, _stream(stream))
     _check(code, "sta_forward")
+
+
+HILBERT_SLIDE = 1   # STA_HILBERT_SLIDE
+HILBERT_WINDOW = 2  # STA_HILBERT_WINDOW
+
+
+def sta_hilbert_workspace_bytes(dims: sta_dims, has_text: bool) -> int:
+    return int(load_library().sta_hilbert_workspace_bytes(ctypes.byref(dims), int(has_text)))
+
+
+def sta_hilbert_forward(dims: sta_dims, q, k, v, window_lens, mode: int, text_length: int,
+                        has_text: bool, out, lse, workspace, stream=None) -> None:
+    """Hilbert-window attention on a 2D image (raster in, raster out); see include/sta.h."""
+    lens = list(window_lens) if hasattr(window_lens, "__len__") else [int(window_lens)] * dims.heads
+    if len(lens) != dims.heads:
+        raise ValueError("one window length per head")
+    la = (ctypes.c_int32 * len(lens))(*[int(x) for x in lens])
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    code = load_library().sta_hilbert_forward(
+        ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), la, int(mode), int(text_length), int(has_text),
+        _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes, _stream(stream))
+    _check(code, "sta_hilbert_forward")
+
+
+def sta_hilbert_gather(dims: sta_dims, has_text: bool, x_raster, x_hilbert, stream=None) -> None:
+    _check(load_library().sta_hilbert_gather(ctypes.byref(dims), int(has_text), _ptr(x_raster),
+                                             _ptr(x_hilbert), _stream(stream)), "sta_hilbert_gather")
+
+
+def sta_hilbert_scatter(dims: sta_dims, has_text: bool, x_hilbert, x_raster, stream=None) -> None:
+    _check(load_library().sta_hilbert_scatter(ctypes.byref(dims), int(has_text), _ptr(x_hilbert),
+                                              _ptr(x_raster), _stream(stream)), "sta_hilbert_scatter")
 
 
 NOALLOC_SCRATCH_BYTES = 1 << 20  # STA_NOALLOC_SCRATCH_BYTES

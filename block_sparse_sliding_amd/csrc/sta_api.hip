@@ -68,6 +68,36 @@ sta_status make_geom(const sta_dims* d, int32_t has_text, int32_t text_length, G
   auto magic = [](int64_t d) { return d == 1 ? 0u : uint32_t(((int64_t(1) << 32) + d - 1) / d); };
   g->mag_nw = magic(nw);
   g->mag_nh = magic(nh);
+  g->hilbert = 0;
+  g->hil_m = 0;
+  return STA_OK;
+}
+
+// A 2D image for the Hilbert entry points: one frame, square, its side 8 * 2^m
+// tokens (a 2^m x 2^m tile grid); sets g->hil_m.
+sta_status make_hilbert_geom(const sta_dims* d, int32_t has_text, int32_t text_length, Geom* g) {
+  sta_status st = make_geom(d, has_text, text_length, g);
+  if (st != STA_OK) return st;
+  if (d->T != 1 || d->H != d->W || d->H % sta::kTileH != 0) return STA_ERR_SHAPE;
+  const int side = d->H / sta::kTileH;
+  if ((side & (side - 1)) != 0) return STA_ERR_SHAPE;
+  int m = 0;
+  while ((1 << m) < side) ++m;
+  g->hil_m = m;
+  return STA_OK;
+}
+
+// Hilbert windows: one length per head in [1, min(n_tiles, 1023)] tiles, kept
+// as the w component of a (1, 1, W) window (which also prices the work order).
+sta_status make_hilbert_windows(const Geom& g, const int32_t* lens, int32_t mode, Windows* win) {
+  if (lens == nullptr) return STA_ERR_NULL;
+  if (mode != STA_HILBERT_SLIDE && mode != STA_HILBERT_WINDOW) return STA_ERR_WINDOW;
+  std::memset(win, 0, sizeof(*win));
+  for (int h = 0; h < g.heads; ++h) {
+    const int32_t w = lens[h];
+    if (w < 1 || w > g.n_tiles || w > 1023) return STA_ERR_WINDOW;
+    win->w[h] = 1u | (1u << 10) | (uint32_t(w) << 20);
+  }
   return STA_OK;
 }
 
@@ -218,17 +248,11 @@ sta_status sta_tile_scatter(const sta_dims* dims, int32_t has_text, const void* 
 
 namespace {
 
-sta_status forward_impl(const sta_dims* dims, const void* q, const void* k, const void* v,
-                        const int32_t* window_sizes, int32_t text_length, int32_t has_text,
-                        void* out, float* lse, void* workspace, size_t workspace_bytes,
-                        void* stream, void* const* events) {
-  Geom g;
-  sta_status st = make_geom(dims, has_text, text_length, &g);
-  if (st != STA_OK) return st;
-  Windows win;
-  int64_t n_ids = 0;
-  st = make_windows(g, window_sizes, &win, &n_ids);
-  if (st != STA_OK) return st;
+// The forward's launches for a validated geometry and windows.
+sta_status forward_launch(Geom g, const Windows& win, const void* q, const void* k, const void* v,
+                          void* out, float* lse, void* workspace, size_t workspace_bytes, void* stream,
+                          void* const* events) {
+  sta_status st = STA_OK;
   if (q == nullptr || k == nullptr || v == nullptr || out == nullptr) return STA_ERR_NULL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
       (lse != nullptr && !aligned16(lse)))
@@ -274,6 +298,20 @@ sta_status forward_impl(const sta_dims* dims, const void* q, const void* k, cons
   return st;
 }
 
+sta_status forward_impl(const sta_dims* dims, const void* q, const void* k, const void* v,
+                        const int32_t* window_sizes, int32_t text_length, int32_t has_text,
+                        void* out, float* lse, void* workspace, size_t workspace_bytes,
+                        void* stream, void* const* events) {
+  Geom g;
+  sta_status st = make_geom(dims, has_text, text_length, &g);
+  if (st != STA_OK) return st;
+  Windows win;
+  int64_t n_ids = 0;
+  st = make_windows(g, window_sizes, &win, &n_ids);
+  if (st != STA_OK) return st;
+  return forward_launch(g, win, q, k, v, out, lse, workspace, workspace_bytes, stream, events);
+}
+
 }  // namespace
 
 extern "C" {
@@ -295,6 +333,55 @@ sta_status sta_forward_timed(const sta_dims* dims, const void* q, const void* k,
     if (events[i] == nullptr) return STA_ERR_NULL;
   return forward_impl(dims, q, k, v, window_sizes, text_length, has_text, out, lse, workspace,
                       workspace_bytes, stream, events);
+}
+
+}  // extern "C"
+
+// ------------------------------------------------- Hilbert-window attention
+extern "C" {
+
+size_t sta_hilbert_workspace_bytes(const sta_dims* dims, int32_t has_text) {
+  Geom g;
+  if (make_hilbert_geom(dims, has_text, 0, &g) != STA_OK) return 0;
+  return carve(g).total;
+}
+
+sta_status sta_hilbert_forward(const sta_dims* dims, const void* q, const void* k, const void* v,
+                               const int32_t* window_lens, int32_t mode, int32_t text_length,
+                               int32_t has_text, void* out, float* lse, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  Geom g;
+  sta_status st = make_hilbert_geom(dims, has_text, text_length, &g);
+  if (st != STA_OK) return st;
+  Windows win;
+  st = make_hilbert_windows(g, window_lens, mode, &win);
+  if (st != STA_OK) return st;
+  g.hilbert = mode;
+  return forward_launch(g, win, q, k, v, out, lse, workspace, workspace_bytes, stream, nullptr);
+}
+
+namespace {
+sta_status hilbert_rows(const sta_dims* dims, int32_t has_text, const void* src, void* dst, bool to_hilbert,
+                        void* stream) {
+  Geom g;
+  sta_status st = make_hilbert_geom(dims, has_text, 0, &g);
+  if (st != STA_OK) return st;
+  if (src == nullptr || dst == nullptr) return STA_ERR_NULL;
+  if (!aligned16(src) || !aligned16(dst)) return STA_ERR_ALIGN;
+  const size_t bytes = size_t(g.B) * g.heads * g.S * g.D * 2;
+  if (overlaps(src, bytes, dst, bytes)) return STA_ERR_ALIAS;
+  return hip_status(sta::launch_rows_hilbert(g, src, dst, to_hilbert, reinterpret_cast<hipStream_t>(stream)));
+}
+}  // namespace
+
+sta_status sta_hilbert_gather(const sta_dims* dims, int32_t has_text, const void* x_raster,
+                              void* x_hilbert, void* stream) {
+  return hilbert_rows(dims, has_text, x_raster, x_hilbert, true, stream);
+}
+
+sta_status sta_hilbert_scatter(const sta_dims* dims, int32_t has_text, const void* x_hilbert,
+                               void* x_raster, void* stream) {
+  return hilbert_rows(dims, has_text, x_hilbert, x_raster, false, stream);
 }
 
 }  // extern "C"

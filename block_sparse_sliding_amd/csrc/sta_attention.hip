@@ -133,7 +133,10 @@ __device__ inline void dma16_buf(const char* base, int voff, int soff, char* lds
 #endif
 }
 
-template <int D, bool PAD>
+// HIL: Hilbert-window attention on a 2D image (Geom::hilbert): query unit u < n_tiles
+// is the tile at Hilbert curve position u, and its key tiles come from
+// HilbertKeyStream; everything else is the same kernel.
+template <int D, bool PAD, bool HIL>
 __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(KernelArgs) {
   constexpr int KS = D / 32;                  // k-steps of S^T
   constexpr int DT = D / 16;                  // d groups of O^T (and V column units)
@@ -177,7 +180,12 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(KernelArgs) 
     int qtt = 0, qth = 0, qtw = 0;
     int q_ext = kFullExtent, q_base = 0;
     int q_rows = text_unit ? kTextSlots : kTileRows;
-    if (!text_unit) {
+    if (HIL && !text_unit) {
+      hilbert_d2xy(g.hil_m, u, qtw, qth);
+      q_base = (qth * kTileH) * g.W + qtw * kTileW;
+      q_ext = tile_extent(0, qth, qtw, g);
+      q_rows = extent_tokens(q_ext);
+    } else if (!text_unit) {
       const int rest = div_by(u, g.nw, g.mag_nw);
       qtw = u - rest * g.nw;
       qtt = div_by(rest, g.nh, g.mag_nh);
@@ -204,11 +212,19 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(KernelArgs) 
 
     // key blocks: the window of the query tile, or every tile for the text unit
     const int wt = win_t(wp), wh = win_h(wp), ww = win_w(wp);
-    KeyStream<PAD> keys;
-    if (text_unit)
-      keys.init(g, 0, g.nt, 0, g.nh, 0, g.nw);
-    else
-      keys.init(g, window_start(qtt, wt, g.nt), wt, window_start(qth, wh, g.nh), wh, window_start(qtw, ww, g.nw), ww);
+    typename std::conditional<HIL, HilbertKeyStream, KeyStream<PAD>>::type keys;
+    if constexpr (HIL) {
+      // the window length is the w component of the head's window
+      int first = 0, count = g.n_tiles;
+      if (!text_unit) hilbert_window(u, ww, g.n_tiles, g.hilbert, first, count);
+      keys.init(g, first, count);
+    } else {
+      if (text_unit)
+        keys.init(g, 0, g.nt, 0, g.nh, 0, g.nw);
+      else
+        keys.init(g, window_start(qtt, wt, g.nt), wt, window_start(qth, wh, g.nh), wh, window_start(qtw, ww, g.nw),
+                  ww);
+    }
     const int n_plain = keys.n_plain, n_blk = keys.n_blk;
 
     const size_t slab = size_t(bh) * g.S * D;
@@ -529,25 +545,27 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(KernelArgs) 
 }
 
 // Resident workgroups of the kernel on the current device (cached per device).
-template <int D, bool PAD>
+template <int D, bool PAD, bool HIL>
 int persistent_grid() {
   static int cache[kMaxDevices] = {};
-  return resident_workgroups(sta_attention_kernel<D, PAD>, kThreads, cache);
+  return resident_workgroups(sta_attention_kernel<D, PAD, HIL>, kThreads, cache);
 }
 
-template <int D, bool PAD>
+template <int D, bool PAD, bool HIL = false>
 hipError_t launch(const Geom& g, const Windows& win, const FwdArgs& a, hipStream_t stream) {
   const int units = g.B * g.heads * g.n_q;
-  const int resident = persistent_grid<D, PAD>();
+  const int resident = persistent_grid<D, PAD, HIL>();
   if (resident <= 0) return hipErrorInvalidDevice;
   const int grid = units < resident ? units : resident;
-  sta_attention_kernel<D, PAD><<<grid, kThreads, 0, stream>>>(KernelArgs{g, a, win});
+  sta_attention_kernel<D, PAD, HIL><<<grid, kThreads, 0, stream>>>(KernelArgs{g, a, win});
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_attention(const Geom& g, const Windows& win, const FwdArgs& a, hipStream_t stream) {
+  if (g.hilbert != 0)  // a one-frame image: never a tile multiple
+    return g.D == 128 ? launch<128, true, true>(g, win, a, stream) : launch<64, true, true>(g, win, a, stream);
   if (g.full) return g.D == 128 ? launch<128, false>(g, win, a, stream) : launch<64, false>(g, win, a, stream);
   return g.D == 128 ? launch<128, true>(g, win, a, stream) : launch<64, true>(g, win, a, stream);
 }

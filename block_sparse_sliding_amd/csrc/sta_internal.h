@@ -38,6 +38,9 @@ struct Geom {
   // floor(n / d) = umulhi(n, m) exactly whenever n * d < 2^32, which holds for
   // every tile index (n_tiles * max(nw, nh) < 2^32 is checked on the host).
   uint32_t mag_nw, mag_nh;
+  // Hilbert-window attention (2D images, T = 1, a 2^hil_m x 2^hil_m tile grid):
+  // 0 = the STA box windows; 1 = Hilbert slide windows; 2 = Hilbert windows
+  int32_t hilbert, hil_m;
 };
 
 // Per-head windows, packed as wt | wh << 10 | ww << 20 (kernel-argument copy).
@@ -114,6 +117,77 @@ __host__ __device__ inline int box_blocks(int lo_t, int len_t, int lo_h, int len
   int full, rem;
   box_block_counts(lo_t, len_t, lo_h, len_h, lo_w, len_w, g, full, rem);
   return full + rem;
+}
+
+// Hilbert curve of order k on the 2^k x 2^k grid (x = column, y = row), from
+// (0, 0) to (2^k - 1, 0): order k visits the quadrants (x low, y low),
+// (x low, y high), (x high, y high), (x high, y low), running the order k - 1
+// curve transposed, shifted, shifted, and reflected through the anti-diagonal
+// ("Boosting 2D Local Attention Efficiency with Hilbert-Guided Sparsity",
+// "The Hilbert Curve Advantage": tokens reordered along a Hilbert curve).
+// Position d -> cell: the level transforms applied from the innermost digit
+// of d (base 4) outwards.
+__host__ __device__ inline void hilbert_d2xy(int k, int d, int& x, int& y) {
+  x = 0;
+  y = 0;
+  for (int j = 1; j <= k; ++j) {
+    const int h = 1 << (j - 1);
+    const int q = (d >> (2 * (j - 1))) & 3;
+    if (q == 0) {
+      const int t = x;
+      x = y;
+      y = t;
+    } else if (q == 1) {
+      y += h;
+    } else if (q == 2) {
+      x += h;
+      y += h;
+    } else {
+      const int nx = 2 * h - 1 - y, ny = h - 1 - x;
+      x = nx;
+      y = ny;
+    }
+  }
+}
+// Cell -> position: the quadrants peeled from the outermost level inwards.
+__host__ __device__ inline int hilbert_xy2d(int k, int x, int y) {
+  int d = 0;
+  for (int j = k; j >= 1; --j) {
+    const int h = 1 << (j - 1);
+    int q;
+    if (x < h && y < h) {
+      q = 0;
+      const int t = x;
+      x = y;
+      y = t;
+    } else if (x < h) {
+      q = 1;
+      y -= h;
+    } else if (y >= h) {
+      q = 2;
+      x -= h;
+      y -= h;
+    } else {
+      q = 3;
+      const int nx = h - 1 - y, ny = 2 * h - 1 - x;
+      x = nx;
+      y = ny;
+    }
+    d += q * h * h;
+  }
+  return d;
+}
+// Key tiles of the query tile at curve position i: positions [first, first + count).
+// mode 1 (slide): the STA window rule in one dimension, W tiles centred on i and
+// shifted inward at the ends; mode 2 (window): the block of W positions holding i.
+__host__ __device__ inline void hilbert_window(int i, int W, int n, int mode, int& first, int& count) {
+  if (mode == 1) {
+    first = window_start(i, W, n);
+    count = W;
+  } else {
+    first = (i / W) * W;
+    count = n - first < W ? n - first : W;
+  }
 }
 
 // One 64-key block of a query unit's key stream (scalar values).
@@ -222,6 +296,54 @@ struct KeyStream {
   }
 };
 
+// The key blocks of a Hilbert-window query unit (2D image, T = 1): one block per
+// key tile (its single 8x8 frame), the tiles at curve positions
+// [first, first + count) walked by the residues of the positions modulo count
+// (so units whose windows overlap reach each shared tile at the same step),
+// then the text blocks as in KeyStream. block(j) may be called in any order.
+struct HilbertKeyStream {
+  int first, count, m;
+  int n_vfull, n_vrem, n_tfull, n_plain, n_blk, text_len;
+
+  __host__ __device__ void init(const Geom& g, int first_, int count_) {
+    first = first_;
+    count = count_;
+    m = g.hil_m;
+    n_vfull = count;
+    n_vrem = 0;
+    text_len = g.has_text ? g.text_length : 0;
+    n_tfull = text_len / kKeyBlock;
+    n_plain = n_vfull + n_tfull;
+    n_blk = n_plain + (text_len % kKeyBlock != 0 ? 1 : 0);
+  }
+  __host__ __device__ void reset() {}
+  __host__ __device__ KeyBlock block(const Geom& g, int j) const {
+    KeyBlock s;
+    if (j < n_vfull) {
+      int d = (j - first) % count;
+      d = d < 0 ? d + count : d;
+      int tx, ty;
+      hilbert_d2xy(m, first + d, tx, ty);
+      s.kind = 0;
+      s.base = ty * kTileH * g.W + tx * kTileW;
+      s.lim = kKeyBlock;
+      s.ext = tile_extent(0, ty, tx, g);
+      s.sub = 0;
+      s.mask = kKeyBlock;
+    } else {
+      const int tb = j < n_plain ? j - n_vfull : n_tfull;
+      s.kind = 1;
+      s.base = g.n_video + tb * kKeyBlock;
+      const int left = text_len - tb * kKeyBlock;
+      s.lim = left < kKeyBlock ? left : kKeyBlock;
+      s.ext = kFullExtent;
+      s.sub = 0;
+      s.mask = s.lim;
+    }
+    return s;
+  }
+};
+
 // Tile-major row r (within one [S_t] slab) -> raster row, or -1 for a padding
 // row. Tile t owns rows 384t .. 384t + 383; a video size that is not a
 // multiple of the tile is covered by the same tile grid, the last tile along
@@ -260,6 +382,11 @@ __host__ __device__ inline int tiled_to_raster(int r, const Geom& g) {
 
 // Launchers (each enqueues one kernel on `stream` and returns hipGetLastError()).
 hipError_t launch_rows_permute(const Geom& g, const void* src, void* dst, bool to_tiled,
+                               hipStream_t stream);
+// Raster <-> Hilbert order of the video rows of a 2D image (g.hil_m set; text
+// rows copied unchanged): row d of the Hilbert side is the token at curve
+// position d of the order hil_m + 3 curve.
+hipError_t launch_rows_hilbert(const Geom& g, const void* src, void* dst, bool to_hilbert,
                                hipStream_t stream);
 // V^T fragments: every 64-row tile-major block of v (rows at or after the
 // valid text length zeroed) as (2 key halves) x (D/16 column groups) 1 KB

@@ -37,6 +37,34 @@ __global__ __launch_bounds__(kThreads) void rows_permute_kernel(Geom g, const ui
   }
 }
 
+// Raster <-> Hilbert order of a 2D image's rows (one frame, side 8 * 2^hil_m):
+// Hilbert row d holds the token at position d of the order hil_m + 3 curve
+// ("Boosting 2D Local Attention Efficiency with Hilbert-Guided Sparsity",
+// "The Hilbert Curve Advantage"); text rows keep their place. grid (S / 64,
+// B * heads): one workgroup per 64 Hilbert rows (one 8x8 tile).
+template <int D>
+__global__ __launch_bounds__(kThreads) void rows_hilbert_kernel(Geom g, const uint4* __restrict__ src,
+                                                                uint4* __restrict__ dst, int to_hilbert) {
+  constexpr int CPR = D / 8;  // 16-byte chunks per row
+  const size_t slab = size_t(blockIdx.y) * g.S * CPR;
+  const int r0 = blockIdx.x * kKeyBlock;
+  const int k = g.hil_m + 3;
+  for (int c = threadIdx.x; c < kKeyBlock * CPR; c += kThreads) {
+    const int rh = r0 + c / CPR;
+    const int col = c % CPR;
+    int rr = rh;  // text rows
+    if (rh < g.n_video) {
+      int x, y;
+      hilbert_d2xy(k, rh, x, y);
+      rr = y * g.W + x;
+    }
+    if (to_hilbert)
+      dst[slab + size_t(rh) * CPR + col] = src[slab + size_t(rr) * CPR + col];
+    else
+      dst[slab + size_t(rr) * CPR + col] = src[slab + size_t(rh) * CPR + col];
+  }
+}
+
 // Pack v for the PV product of the attention kernel, tile-major. Block b (64
 // tile-major rows) becomes 2 x (D/16) fragments of 1 KB; in fragment
 // (h, dt) lane l (group gq = l/16, column i = l%16) holds, for e = 0..7,
@@ -96,6 +124,16 @@ hipError_t launch_rows_permute(const Geom& g, const void* src, void* dst, bool t
     rows_permute_kernel<128><<<grid, kThreads, 0, stream>>>(g, (const uint4*)src, (uint4*)dst, to_tiled);
   else
     rows_permute_kernel<64><<<grid, kThreads, 0, stream>>>(g, (const uint4*)src, (uint4*)dst, to_tiled);
+  return hipGetLastError();
+}
+
+hipError_t launch_rows_hilbert(const Geom& g, const void* src, void* dst, bool to_hilbert,
+                               hipStream_t stream) {
+  dim3 grid(g.S / kKeyBlock, g.B * g.heads);
+  if (g.D == 128)
+    rows_hilbert_kernel<128><<<grid, kThreads, 0, stream>>>(g, (const uint4*)src, (uint4*)dst, to_hilbert);
+  else
+    rows_hilbert_kernel<64><<<grid, kThreads, 0, stream>>>(g, (const uint4*)src, (uint4*)dst, to_hilbert);
   return hipGetLastError();
 }
 

@@ -176,6 +176,53 @@ sta_status sta_forward_noalloc(const sta_dims* dims, const void* q, const void* 
                                float* lse, void* stream);
 
 /*
+ * Hilbert-window attention on a 2D image ("Boosting 2D Local Attention
+ * Efficiency with Hilbert-Guided Sparsity", TLDR and "The Hilbert Curve
+ * Advantage": tokens reordered along a Hilbert curve, windows built on that
+ * 1D order, run by a block-sparse kernel unchanged). The image is a one-frame
+ * video: dims->T = 1 and H = W = 8 * 2^m, so its 8x8 tiles form a 2^m x 2^m
+ * grid (n = 4^m tiles); other sizes are STA_ERR_SHAPE. The Hilbert curve of
+ * order m on the tile grid runs from tile (0, 0) to tile (2^m - 1, 0) (x =
+ * column, y = row); order j visits the quadrants (x low, y low), (x low, y
+ * high), (x high, y high), (x high, y low), running the order j - 1 curve
+ * transposed, shifted, shifted, and reflected through the anti-diagonal. A
+ * 64-token block of the token-level curve is exactly one tile, so the pattern
+ * is one of whole tiles. A video query of the tile at curve position i sees
+ * the key tiles at positions
+ *   STA_HILBERT_SLIDE:  [s, s + W), s = clamp(i - W / 2, 0, n - W)
+ *   STA_HILBERT_WINDOW: [W * (i / W), min(W * (i / W) + W, n))
+ * with W = window_lens[head] in [1, min(n, 1023)] (else STA_ERR_WINDOW, as is
+ * another mode), plus the valid text keys; text queries see every video key
+ * and the valid text keys, as in sta_forward. q, k, v, out and lse are laid
+ * out as in sta_forward (raster token order; the curve only picks the key
+ * tiles, and softmax attention does not depend on the order of the keys).
+ * workspace: >= sta_hilbert_workspace_bytes(dims, has_text) bytes, 256-byte
+ * aligned, same rules as sta_forward's. Two launches on `stream`, as in
+ * sta_forward; the same argument errors.
+ */
+#define STA_HILBERT_SLIDE 1
+#define STA_HILBERT_WINDOW 2
+size_t sta_hilbert_workspace_bytes(const sta_dims* dims, int32_t has_text);
+sta_status sta_hilbert_forward(const sta_dims* dims, const void* q, const void* k,
+                               const void* v, const int32_t* window_lens, int32_t mode,
+                               int32_t text_length, int32_t has_text, void* out,
+                               float* lse, void* workspace, size_t workspace_bytes,
+                               void* stream);
+
+/*
+ * Raster <-> Hilbert order of the rows of one bf16 tensor [B][heads][S][D] of
+ * a 2D image (same shape rules as sta_hilbert_forward; same post): row d of
+ * x_hilbert is the token at position d of the order m + 3 curve over the
+ * image's tokens (the curve above, at token level), for d < H * W; the 256
+ * text rows, when has_text, keep their place. The two buffers must not
+ * overlap. sta_hilbert_scatter is the inverse.
+ */
+sta_status sta_hilbert_gather(const sta_dims* dims, int32_t has_text,
+                              const void* x_raster, void* x_hilbert, void* stream);
+sta_status sta_hilbert_scatter(const sta_dims* dims, int32_t has_text,
+                               const void* x_hilbert, void* x_raster, void* stream);
+
+/*
  * Tile-major gather of one bf16 tensor. The tile is the one the STA README
  * ("Usage") fixes: a cube of (6, 8, 8) video tokens; laying each tile's 384
  * tokens out contiguously turns every dense (query tile, key tile) block of

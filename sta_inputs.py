@@ -36,6 +36,10 @@ class Workload:
     has_text: bool
     text_length: int
     seed_base: int
+    # Hilbert-window attention on a 2D image (video (1, 8*2^m, 8*2^m)): window
+    # length in tiles and mode (1 slide, 2 window); 0 for STA workloads
+    hilbert_len: int = 0
+    hilbert_mode: int = 0
 
     @property
     def seq_len(self) -> int:
@@ -53,6 +57,9 @@ class Workload:
             "windows": sorted(set(self.windows)),
             "has_text": self.has_text,
             "text_length": self.text_length,
+            **({"hilbert_window_tiles": self.hilbert_len,
+                "hilbert_mode": "slide" if self.hilbert_mode == 1 else "window"}
+               if self.hilbert_len else {}),
         }
 
 
@@ -84,6 +91,11 @@ WORKLOADS = {
     # h 5 of 8 rows; tile grid (6, 6, 10)
     "ragged": Workload("ragged", 1, 24, 128, (33, 45, 80),
                        _per_head(24, [(3, 3, 3)]), True, 226, 70),
+    # Hilbert slide attention on a 512x512 image (a 64x64 grid of 8x8 tiles),
+    # 27 key tiles per query tile along the curve, the headline's heads, head
+    # size and text; the pages give no size for the Hilbert row
+    "hilbert": Workload("hilbert", 1, 24, 128, (1, 512, 512),
+                        _per_head(24, [(1, 1, 27)]), True, 226, 80, hilbert_len=27, hilbert_mode=1),
 }
 
 

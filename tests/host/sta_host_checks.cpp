@@ -14,6 +14,9 @@
 //       prints the helpers' values for one geometry (every head gets the
 //       window (wt, wh, ww)); the Python test compares them with maps built
 //       from the oracle's token coordinates
+//   sta_host_checks hcurve <k> | hstream <side> <has_text> <ell> <W> <mode>
+//       the Hilbert curve and the Hilbert units' key streams (compared with
+//       the Hilbert oracle by the Python test)
 //   sta_host_checks stream <T> <H> <W> <has_text> <ell> <wt> <wh> <ww>
 //       checks the forward kernel's key stream of every query unit and prints
 //       its key rows (compared with the oracle's mask by the Python test)
@@ -65,6 +68,10 @@ extern "C" hipError_t hipGetSymbolAddress(void** p, const void*) {
 namespace sta {
 hipError_t launch_rows_permute(const Geom& g, const void* src, void* dst, bool, hipStream_t) {
   record("rows_permute", g, {P(src), P(dst)});
+  return hipSuccess;
+}
+hipError_t launch_rows_hilbert(const Geom& g, const void* src, void* dst, bool, hipStream_t) {
+  record("rows_hilbert", g, {P(src), P(dst)});
   return hipSuccess;
 }
 hipError_t launch_pack_v(const Geom& g, const void* v, void* vt, hipStream_t) {
@@ -272,6 +279,47 @@ void validate() {
                       nb, nullptr);
     CHECK(st == STA_ERR_ALIAS && g_launches.empty(), "backward, dk over dq");
   }
+  // Hilbert entry points: shape, window and mode errors before any launch
+  {
+    const sta_dims ok{1, 2, 64, 1, 32, 32};
+    const int32_t lens[2] = {3, 16};
+    const size_t n = sta_hilbert_workspace_bytes(&ok, 1);
+    CHECK(n > 0, "hilbert workspace");
+    struct HCase {
+      sta_dims d;
+      int32_t l0, l1, mode;
+      sta_status expect;
+      const char* what;
+    } hc[] = {
+        {{1, 2, 64, 1, 32, 32}, 3, 16, STA_HILBERT_SLIDE, STA_OK, "valid slide"},
+        {{1, 2, 64, 1, 32, 32}, 4, 16, STA_HILBERT_WINDOW, STA_OK, "valid window"},
+        {{1, 2, 64, 2, 32, 32}, 3, 16, STA_HILBERT_SLIDE, STA_ERR_SHAPE, "two frames"},
+        {{1, 2, 64, 1, 32, 64}, 3, 16, STA_HILBERT_SLIDE, STA_ERR_SHAPE, "not square"},
+        {{1, 2, 64, 1, 24, 24}, 3, 9, STA_HILBERT_SLIDE, STA_ERR_SHAPE, "3x3 tile grid"},
+        {{1, 2, 64, 1, 36, 36}, 3, 9, STA_HILBERT_SLIDE, STA_ERR_SHAPE, "side not a tile multiple"},
+        {{1, 2, 64, 1, 32, 32}, 0, 16, STA_HILBERT_SLIDE, STA_ERR_WINDOW, "window 0"},
+        {{1, 2, 64, 1, 32, 32}, 3, 17, STA_HILBERT_SLIDE, STA_ERR_WINDOW, "window past the grid"},
+        {{1, 2, 64, 1, 32, 32}, 3, 16, 0, STA_ERR_WINDOW, "mode 0"},
+        {{1, 2, 64, 1, 32, 32}, 3, 16, 3, STA_ERR_WINDOW, "mode 3"},
+    };
+    for (const HCase& c : hc) {
+      const int32_t l[2] = {c.l0, c.l1};
+      g_launches.clear();
+      const sta_status st = sta_hilbert_forward(&c.d, q, k, v, l, c.mode, 100, 1, out, lse, ws, n, nullptr);
+      CHECK(st == c.expect, "hilbert %s: expected %s, got %s", c.what, sta_status_str(c.expect), sta_status_str(st));
+      CHECK((st == STA_OK) == !g_launches.empty(), "hilbert %s: launches", c.what);
+      if (st == STA_OK)
+        for (const Launch& l2 : g_launches) check_in_workspace(l2, {P(q), P(k), P(v), P(out), P(lse)}, P(ws), n);
+    }
+    CHECK(sta_hilbert_forward(&ok, q, k, v, lens, STA_HILBERT_SLIDE, 100, 1, out, lse, ws, n - 1, nullptr) ==
+              STA_ERR_WORKSPACE,
+          "hilbert workspace short by one byte");
+    CHECK(sta_hilbert_gather(&ok, 1, q, q, nullptr) == STA_ERR_ALIAS, "hilbert gather in place");
+    CHECK(sta_hilbert_gather(&ok, 1, q, out, nullptr) == STA_OK && g_launches.back().name == "rows_hilbert",
+          "hilbert gather");
+    const sta_dims bad{1, 2, 64, 1, 40, 40};
+    CHECK(sta_hilbert_scatter(&bad, 1, q, out, nullptr) == STA_ERR_SHAPE, "hilbert scatter, 5x5 tiles");
+  }
   // the forward without a workspace: its kernels get the scratch array only
   {
     const uintptr_t scratch = uintptr_t(40) * 64 * (uintptr_t(1) << 30);
@@ -428,6 +476,80 @@ void stream(int argc, char** argv) {
     stream_units<true>(g, a[5], a[6], a[7]);
 }
 
+// The Hilbert curve helpers: "hcurve <k>" prints x y of every position of the
+// order-k curve (and checks the inverse); "hstream <side> <has_text> <ell> <W>
+// <mode>" prints every Hilbert unit's key rows like `stream`, with the query
+// tile's coordinates.
+void hcurve(int argc, char** argv) {
+  if (argc != 3) {
+    std::fprintf(stderr, "hcurve needs the order\n");
+    std::exit(2);
+  }
+  const int k = std::atoi(argv[2]);
+  for (int d = 0; d < (1 << (2 * k)); ++d) {
+    int x, y;
+    sta::hilbert_d2xy(k, d, x, y);
+    CHECK(sta::hilbert_xy2d(k, x, y) == d, "order %d position %d: inverse", k, d);
+    std::printf("%d %d\n", x, y);
+  }
+}
+
+void hstream(int argc, char** argv) {
+  if (argc != 7) {
+    std::fprintf(stderr, "hstream needs 5 integers\n");
+    std::exit(2);
+  }
+  const int side = std::atoi(argv[2]), text = std::atoi(argv[3]), ell = std::atoi(argv[4]);
+  const int W = std::atoi(argv[5]), mode = std::atoi(argv[6]);
+  const sta_dims d{1, 1, 128, 1, side, side};
+  const int32_t lens[1] = {W};
+  const size_t n = sta_hilbert_workspace_bytes(&d, text);
+  CHECK(n > 0, "hilbert workspace bytes");
+  g_launches.clear();
+  CHECK(sta_hilbert_forward(&d, fake(0), fake(1), fake(2), lens, mode, ell, text, fake(3),
+                            static_cast<float*>(fake(4)), fake(8), n, nullptr) == STA_OK,
+        "hilbert forward on the streamed geometry");
+  const sta::Geom g = g_launches.back().g;
+  CHECK(g.hilbert == mode && (8 << g.hil_m) == side && !g.full, "hilbert geometry");
+  for (int u = 0; u < g.n_q; ++u) {
+    const bool text_unit = g.has_text && u == g.n_tiles;
+    int first = 0, count = g.n_tiles, tx = -1, ty = -1;
+    if (!text_unit) {
+      sta::hilbert_d2xy(g.hil_m, u, tx, ty);
+      sta::hilbert_window(u, W, g.n_tiles, g.hilbert, first, count);
+    }
+    sta::HilbertKeyStream ks;
+    ks.init(g, first, count);
+    std::vector<int> keys;
+    for (int j = 0; j < ks.n_blk; ++j) {
+      const sta::KeyBlock b = ks.block(g, j);
+      CHECK(j >= ks.n_plain || b.mask == sta::kKeyBlock, "unit %d block %d masked early", u, j);
+      for (int r = 0; r < b.mask; ++r) {
+        int row;
+        if (b.kind == 0) {
+          CHECK(sta::extent_tokens(b.ext) == 64, "unit %d block %d: tile of %d tokens", u, j, sta::extent_tokens(b.ext));
+          row = b.base + (r >> 3) * g.W + (r & 7);
+        } else {
+          CHECK(b.kind == 1, "unit %d block %d kind %d", u, j, b.kind);
+          row = b.base + r;
+        }
+        CHECK(row >= 0 && row < g.S, "unit %d block %d row %d outside the sequence", u, j, row);
+        keys.push_back(row);
+      }
+    }
+    std::sort(keys.begin(), keys.end());
+    for (size_t i = 1; i < keys.size(); ++i) CHECK(keys[i] != keys[i - 1], "unit %d key %d twice", u, keys[i]);
+    std::printf("unit %d %d %d", u, tx, ty);
+    for (size_t i = 0; i < keys.size();) {
+      size_t e = i + 1;
+      while (e < keys.size() && keys[e] == keys[e - 1] + 1) ++e;
+      std::printf(" %d:%d", keys[i], keys[e - 1] + 1);
+      i = e;
+    }
+    std::printf("\n");
+  }
+}
+
 }  // namespace
 
 int main(int argc, char** argv) {
@@ -441,6 +563,14 @@ int main(int argc, char** argv) {
   }
   if (argc >= 2 && std::strcmp(argv[1], "stream") == 0) {
     stream(argc, argv);
+    return 0;
+  }
+  if (argc >= 2 && std::strcmp(argv[1], "hcurve") == 0) {
+    hcurve(argc, argv);
+    return 0;
+  }
+  if (argc >= 2 && std::strcmp(argv[1], "hstream") == 0) {
+    hstream(argc, argv);
     return 0;
   }
   std::fprintf(stderr, "usage: %s validate | dump B heads D T H W has_text ell wt wh ww | stream T H W has_text ell wt wh ww\n",

@@ -91,11 +91,11 @@ def test_forward_kernels_no_asm_hazards(attention_asm):
     tile-multiple videos (the fast path) spill nothing."""
     kernels = H.parse(attention_asm)
     names = sorted(k.name for k in kernels)
-    assert len(kernels) == 4, names  # D in {64, 128} x (tile-multiple video, partial tiles)
+    assert len(kernels) == 6, names  # D in {64, 128} x (tile-multiple video, partial tiles, Hilbert)
     for k in kernels:
         assert len(k.instrs) > 1000, k.name
         problems = H.check_result_reads(k) + H.check_operand_writes(k)
         assert problems == [], "\n".join(problems[:10])
-        if "Lb0E" in k.name:
+        if "ELb0ELb0E" in k.name:  # PAD = false, HIL = false
             assert k.scratch == 0, f"{k.name}: {k.scratch} bytes of scratch per lane"
             assert k.vgpr_spills == 0, f"{k.name}: {k.vgpr_spills} VGPR spills"

@@ -40,3 +40,17 @@ def test_headline_count_is_the_tile_product():
     assert bench.effective_flops(wl) == 4.0 * 128 * pairs
     assert bench.kernel_suffix(wl) == "<128, false>"
     assert bench.kernel_suffix(sta_inputs.WORKLOADS["ragged"]) == "<128, true>"
+
+
+@pytest.mark.parametrize("mode,W", [(1, 5), (1, 16), (2, 3), (2, 4)])
+def test_hilbert_flop_count_matches_the_oracle_mask(mode, W):
+    """bench.hilbert_flops counts 4*D per pair the Hilbert oracle's mask allows
+    (video rows and the valid text rows)."""
+    from oracle import hilbert_oracle as HO
+    side, ell = 32, 77
+    wl = sta_inputs.Workload("h", 1, 2, 64, (1, side, side), ((1, 1, W),) * 2, True, ell, 0,
+                             hilbert_len=W, hilbert_mode=mode)
+    nv = side * side
+    rows = list(range(nv)) + list(range(nv, nv + ell))
+    mask = HO.hilbert_allowed_mask(rows, (side, side), W, "slide" if mode == 1 else "window", ell, True)
+    assert bench.hilbert_flops(wl) == 4.0 * 64 * int(mask.sum()) * 2

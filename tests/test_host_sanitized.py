@@ -204,3 +204,50 @@ def test_forward_key_stream_matches_oracle_mask(checks_bin, shape):
         if ids is not None:
             assert n_blk == sum(-(-int(tokens[i]) // 64) for i in ids) + -(-ell // 64), f"unit {u}"
             assert n_plain == sum(int(tokens[i]) // 64 for i in ids) + ell // 64, f"unit {u}"
+
+
+@pytest.mark.parametrize("k", range(0, 7))
+def test_hilbert_curve_helpers_match_oracle(checks_bin, k):
+    """The library's iterative Hilbert helpers give the oracle's recursive curve."""
+    from oracle import hilbert_oracle
+    out = run(checks_bin, "hcurve", k).split("\n")[:-1]
+    assert [tuple(map(int, ln.split())) for ln in out] == \
+        [hilbert_oracle.hilbert_d2xy(k, d) for d in range(1 << (2 * k))]
+
+
+HSHAPES = [
+    # side, has_text, ell, W, mode (1 slide, 2 window)
+    (8, 1, 226, 1, 1),
+    (16, 0, 0, 1, 1),
+    (16, 1, 100, 3, 1),
+    (32, 1, 64, 5, 1),
+    (32, 0, 0, 16, 1),
+    (32, 1, 1, 4, 2),
+    (64, 1, 226, 5, 2),
+    (64, 0, 0, 16, 2),
+    (64, 1, 200, 9, 1),
+]
+
+
+@pytest.mark.parametrize("shape", HSHAPES, ids=[f"{s[0]}W{s[3]}m{s[4]}t{s[2] if s[1] else '-'}" for s in HSHAPES])
+def test_hilbert_key_stream_matches_oracle_mask(checks_bin, shape):
+    """Every Hilbert unit's key stream (as the kernel walks it) is exactly the
+    oracle's mask row for a query of that tile, each key once."""
+    from oracle import hilbert_oracle
+    side, text, ell, W, mode = shape
+    out = run(checks_bin, "hstream", side, text, ell, W, mode).splitlines()
+    n_tiles = (side // 8) ** 2
+    nv = side * side
+    assert len(out) == n_tiles + text
+    for ln in out:
+        f = ln.split()
+        u, tx, ty = int(f[1]), int(f[2]), int(f[3])
+        keys = np.concatenate([np.arange(*map(int, r.split(":"))) for r in f[4:]])
+        if u < n_tiles:
+            assert (tx, ty) == hilbert_oracle.hilbert_d2xy((side // 8).bit_length() - 1, u)
+            row = ty * 8 * side + tx * 8
+        else:
+            row = nv
+        allowed = np.nonzero(hilbert_oracle.hilbert_allowed_mask(
+            [row], (side, side), W, "slide" if mode == 1 else "window", ell, bool(text))[0])[0]
+        assert np.array_equal(keys, allowed), f"unit {u}"
