@@ -37,8 +37,8 @@ HIPCC_FLAGS = [
 
 # The attention kernel never creates a NaN (keys that must not contribute are
 # masked to -inf and read from a zero row), so its max reductions need no NaN
-# quieting. Its score MFMAs are selected in the VGPR form (the softmax reads
-# the scores from VGPRs); the P V accumulators are AGPRs, named by inline asm.
+# quieting; its MFMAs are selected in the VGPR form (the configuration it was
+# measured in).
 EXTRA_FLAGS = {"sta_attention.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 

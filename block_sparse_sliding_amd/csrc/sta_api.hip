@@ -70,6 +70,7 @@ sta_status make_geom(const sta_dims* d, int32_t has_text, int32_t text_length, G
   g->mag_nh = magic(nh);
   g->hilbert = 0;
   g->hil_m = 0;
+  g->hil_group = 1;
   return STA_OK;
 }
 
@@ -280,7 +281,11 @@ sta_status forward_launch(Geom g, const Windows& win, const void* q, const void*
   if (st != STA_OK) return st;
   int32_t* work = reinterpret_cast<int32_t*>(ws + c.work);
   int32_t* claim = reinterpret_cast<int32_t*>(ws + c.claim);
-  st = hip_status(sta::launch_schedule_work(g, win, work, claim, ws + c.zero_row, s));
+  // the work order counts query units: with grouped Hilbert units, a head has
+  // n_tiles / hil_group video units
+  Geom gs = g;
+  if (g.hilbert != 0) gs.n_tiles = g.n_tiles / g.hil_group;
+  st = hip_status(sta::launch_schedule_work(gs, win, work, claim, ws + c.zero_row, s));
   if (st == STA_OK) st = mark(1);
   if (st != STA_OK) return st;
   sta::FwdArgs a;
@@ -357,6 +362,17 @@ sta_status sta_hilbert_forward(const sta_dims* dims, const void* q, const void* 
   st = make_hilbert_windows(g, window_lens, mode, &win);
   if (st != STA_OK) return st;
   g.hilbert = mode;
+  // Query units of four consecutive curve positions (an aligned 2x2 square of
+  // tiles, 256 rows) when every head's windows allow it: slide windows of at
+  // least 4 tiles (the four windows then share a core), windows of a multiple
+  // of 4 tiles (the four tiles then share their window); single tiles otherwise.
+  bool group = g.n_tiles % 4 == 0;
+  for (int h = 0; h < g.heads; ++h) {
+    const int w = window_lens[h];
+    group = group && (mode == STA_HILBERT_SLIDE ? w >= 4 : w % 4 == 0);
+  }
+  g.hil_group = group ? 4 : 1;
+  g.n_q = g.n_tiles / g.hil_group + (g.has_text ? 1 : 0);
   return forward_launch(g, win, q, k, v, out, lse, workspace, workspace_bytes, stream, nullptr);
 }
 

@@ -133,9 +133,12 @@ __device__ inline void dma16_buf(const char* base, int voff, int soff, char* lds
 #endif
 }
 
-// HIL: Hilbert-window attention on a 2D image (Geom::hilbert): query unit u < n_tiles
-// is the tile at Hilbert curve position u, and its key tiles come from
-// HilbertKeyStream; everything else is the same kernel.
+// HIL: Hilbert-window attention on a 2D image (Geom::hilbert): video query unit u
+// is the hil_group tiles at Hilbert curve positions hil_group * u .. + hil_group
+// - 1 (their rows in that order, 64 per tile), its key tiles come from
+// HilbertKeyStream, and a block that only some of the unit's tiles see gives
+// the other rows a reference of +inf, so their p is exactly 0; everything
+// else is the same kernel.
 template <int D, bool PAD, bool HIL>
 __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(KernelArgs) {
   constexpr int KS = D / 32;                  // k-steps of S^T
@@ -174,17 +177,15 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(KernelArgs) 
     const int bh = unit / g.n_q;
     const int hd = bh % g.heads;
     const uint32_t wp = ka->win.w[hd];
-    const bool text_unit = g.has_text && u == g.n_tiles;
+    const int n_vunits = HIL ? g.n_tiles / g.hil_group : g.n_tiles;
+    const bool text_unit = g.has_text && u == n_vunits;
 
     // query tile coordinates and rows (PAD: its existing tokens, compact order)
     int qtt = 0, qth = 0, qtw = 0;
     int q_ext = kFullExtent, q_base = 0;
     int q_rows = text_unit ? kTextSlots : kTileRows;
     if (HIL && !text_unit) {
-      hilbert_d2xy(g.hil_m, u, qtw, qth);
-      q_base = (qth * kTileH) * g.W + qtw * kTileW;
-      q_ext = tile_extent(0, qth, qtw, g);
-      q_rows = extent_tokens(q_ext);
+      q_rows = kKeyBlock * g.hil_group;  // 64 rows per tile
     } else if (!text_unit) {
       const int rest = div_by(u, g.nw, g.mag_nw);
       qtw = u - rest * g.nw;
@@ -199,6 +200,11 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(KernelArgs) 
     // raster row of unit row `row` (< q_rows)
     auto query_raster = [&](int row) {
       if (text_unit) return g.n_video + row;
+      if constexpr (HIL) {  // row r of tile t = row / 64 of the unit's curve run
+        int tx, ty;
+        hilbert_d2xy(g.hil_m, g.hil_group * u + (row >> 6), tx, ty);
+        return (ty * kTileH + ((row >> 3) & 7)) * g.W + tx * kTileW + (row & 7);
+      }
       int dt, dh, dw;
       if constexpr (PAD) {
         compact_token(row, q_ext, dt, dh, dw);
@@ -215,9 +221,7 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(KernelArgs) 
     typename std::conditional<HIL, HilbertKeyStream, KeyStream<PAD>>::type keys;
     if constexpr (HIL) {
       // the window length is the w component of the head's window
-      int first = 0, count = g.n_tiles;
-      if (!text_unit) hilbert_window(u, ww, g.n_tiles, g.hilbert, first, count);
-      keys.init(g, first, count);
+      keys.init(g, g.hil_group * u, ww, text_unit);
     } else {
       if (text_unit)
         keys.init(g, 0, g.nt, 0, g.nh, 0, g.nw);
@@ -386,6 +390,7 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(KernelArgs) 
           __syncthreads();
           f32x4 s[QT][4];
           scores(s, stage, j >= n_plain ? s_cur.mask : kKeyBlock);
+          const int rows_lo = s_cur.rows_lo, rows_hi = s_cur.rows_hi;  // of block j
           if (j + 1 < n_blk) {
             s_cur = keys.block(g, j + 1);
             issue(s_cur, stage ^ 1);
@@ -395,6 +400,19 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(KernelArgs) 
             row_max(s, mx);
 #pragma unroll
             for (int c = 0; c < QT; ++c) m_run[c] = mx[c] * qs;
+          }
+          // the reference of each row for this block: +inf for rows that do not see it
+          float mb[QT];
+#pragma unroll
+          for (int c = 0; c < QT; ++c) mb[c] = m_run[c];
+          if constexpr (HIL) {
+            if (rows_lo > 0 || rows_hi < q_rows) {
+#pragma unroll
+              for (int c = 0; c < QT; ++c) {
+                const int row = wave * RPW + c * 16 + (lane & 15);
+                mb[c] = (row >= rows_lo && row < rows_hi) ? m_run[c] : INFINITY;
+              }
+            }
           }
           // p = 2^(c s - m) rounded to bf16; O^T += V^T P^T; row sums += 1^T P^T
           const char* vb = lds[stage][1] + (lane >> 2) * 64 + (lane & 3) * 8;
@@ -418,8 +436,8 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(KernelArgs) 
               f32x8 p;
 #pragma unroll
               for (int r = 0; r < 4; ++r) {
-                p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[c][2 * h][r], qs, -m_run[c]));
-                p[4 + r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[c][2 * h + 1][r], qs, -m_run[c]));
+                p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[c][2 * h][r], qs, -mb[c]));
+                p[4 + r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[c][2 * h + 1][r], qs, -mb[c]));
               }
               pb[c] = __builtin_convertvector(p, bf16x8);
 #pragma unroll
@@ -457,7 +475,11 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(KernelArgs) 
           float bm[QT];
           row_max(s, bm);
 #pragma unroll
-          for (int c = 0; c < QT; ++c) mx[c] = fmaxf(mx[c], bm[c]);
+          for (int c = 0; c < QT; ++c) {
+            const int row = wave * RPW + c * 16 + (lane & 15);
+            const bool sees = !HIL || (row >= s_j.rows_lo && row < s_j.rows_hi);
+            mx[c] = sees ? fmaxf(mx[c], bm[c]) : mx[c];
+          }
           __syncthreads();  // every wave has read the stage before it is refilled
         }
 #pragma unroll

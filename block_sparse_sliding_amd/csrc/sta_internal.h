@@ -41,6 +41,9 @@ struct Geom {
   // Hilbert-window attention (2D images, T = 1, a 2^hil_m x 2^hil_m tile grid):
   // 0 = the STA box windows; 1 = Hilbert slide windows; 2 = Hilbert windows
   int32_t hilbert, hil_m;
+  // tiles per Hilbert query unit (1 or 4: four consecutive curve positions,
+  // an aligned 2x2 square of tiles); n_q counts n_tiles / hil_group video units
+  int32_t hil_group;
 };
 
 // Per-head windows, packed as wt | wh << 10 | ww << 20 (kernel-argument copy).
@@ -199,6 +202,9 @@ struct KeyBlock {
   int kind;
   int base, lim, ext, sub;
   int mask;  // first block row that must not contribute (64: none)
+  // query rows of the unit that see this block: [rows_lo, rows_hi) (all of
+  // them except in grouped Hilbert units, whose tiles' windows differ)
+  int rows_lo, rows_hi;
 };
 
 // The key blocks of one query unit, in the order the forward kernel streams
@@ -282,6 +288,8 @@ struct KeyStream {
       const int left = n_tok - tile_sub * kKeyBlock;
       s.mask = left < kKeyBlock ? left : kKeyBlock;
       ++tile_sub;
+      s.rows_lo = 0;
+      s.rows_hi = kTileRows;
     } else {
       const int tb = j < n_plain ? j - n_vfull : n_tfull;
       s.kind = 1;
@@ -291,25 +299,61 @@ struct KeyStream {
       s.ext = kFullExtent;
       s.sub = 0;
       s.mask = s.lim;
+      s.rows_lo = 0;
+      s.rows_hi = kTileRows;
     }
     return s;
   }
 };
 
 // The key blocks of a Hilbert-window query unit (2D image, T = 1): one block per
-// key tile (its single 8x8 frame), the tiles at curve positions
-// [first, first + count) walked by the residues of the positions modulo count
-// (so units whose windows overlap reach each shared tile at the same step),
-// then the text blocks as in KeyStream. block(j) may be called in any order.
+// key tile (its single 8x8 frame). A video unit is G = hil_group consecutive
+// curve positions; their windows, which may differ by a shift, are streamed as
+// their common core [first, first + count), walked by the residues of the
+// positions modulo count (units whose windows overlap reach a shared tile at
+// the same step), then the positions left of the core [lfirst, lfirst +
+// lcount) and right of it [rfirst, rfirst + rcount), each seen by the unit's
+// rows of a contiguous range of its tiles (rows_lo, rows_hi), then the text
+// blocks as in KeyStream. Every row of the unit sees every core block. The
+// text unit streams every tile. block(j) may be called in any order.
 struct HilbertKeyStream {
-  int first, count, m;
+  int first, count, lfirst, lcount, rfirst, rcount, m, G, W, mode;
+  // slide, four tiles: the window start of each (scalars: an array indexed at
+  // run time would put the whole stream in per-lane memory)
+  int st0, st1, st2, st3;
   int n_vfull, n_vrem, n_tfull, n_plain, n_blk, text_len;
 
-  __host__ __device__ void init(const Geom& g, int first_, int count_) {
-    first = first_;
-    count = count_;
+  // pos0: curve position of the unit's first tile; text: the text unit
+  __host__ __device__ void init(const Geom& g, int pos0, int W_, bool text) {
     m = g.hil_m;
-    n_vfull = count;
+    W = W_;
+    mode = g.hilbert;
+    st0 = st1 = st2 = st3 = 0;
+    G = text ? 1 : g.hil_group;
+    lcount = rcount = 0;
+    lfirst = rfirst = 0;
+    if (text) {
+      first = 0;
+      count = g.n_tiles;
+    } else {
+      int c0;
+      hilbert_window(pos0, W, g.n_tiles, mode, first, c0);
+      count = c0;
+      st0 = st1 = st2 = st3 = first;
+      if (G == 4 && mode == 1) {
+        st1 = window_start(pos0 + 1, W, g.n_tiles);
+        st2 = window_start(pos0 + 2, W, g.n_tiles);
+        st3 = window_start(pos0 + 3, W, g.n_tiles);
+        const int lo = st0, hi = st3;
+        first = hi;               // core [hi, lo + W)
+        count = lo + W - hi;
+        lfirst = lo;
+        lcount = hi - lo;
+        rfirst = lo + W;
+        rcount = hi - lo;
+      }
+    }
+    n_vfull = count + lcount + rcount;
     n_vrem = 0;
     text_len = g.has_text ? g.text_length : 0;
     n_tfull = text_len / kKeyBlock;
@@ -319,11 +363,28 @@ struct HilbertKeyStream {
   __host__ __device__ void reset() {}
   __host__ __device__ KeyBlock block(const Geom& g, int j) const {
     KeyBlock s;
+    s.rows_lo = 0;
+    s.rows_hi = kTileRows;
     if (j < n_vfull) {
-      int d = (j - first) % count;
-      d = d < 0 ? d + count : d;
+      int p;
+      if (j < count) {
+        int d = (j - first) % count;
+        d = d < 0 ? d + count : d;
+        p = first + d;
+      } else if (j < count + lcount) {
+        // left of the core: tiles 0 .. t whose window starts at or before p
+        // (the starts never decrease along the curve)
+        p = lfirst + (j - count);
+        const int t = (st1 <= p ? 1 : 0) + (st2 <= p ? 1 : 0) + (st3 <= p ? 1 : 0);
+        s.rows_hi = kKeyBlock * (t + 1);
+      } else {
+        // right of the core: tiles t .. 3 whose window ends after p
+        p = rfirst + (j - count - lcount);
+        const int t = (st0 + W <= p ? 1 : 0) + (st1 + W <= p ? 1 : 0) + (st2 + W <= p ? 1 : 0);
+        s.rows_lo = kKeyBlock * t;
+      }
       int tx, ty;
-      hilbert_d2xy(m, first + d, tx, ty);
+      hilbert_d2xy(m, p, tx, ty);
       s.kind = 0;
       s.base = ty * kTileH * g.W + tx * kTileW;
       s.lim = kKeyBlock;

@@ -511,42 +511,48 @@ void hstream(int argc, char** argv) {
         "hilbert forward on the streamed geometry");
   const sta::Geom g = g_launches.back().g;
   CHECK(g.hilbert == mode && (8 << g.hil_m) == side && !g.full, "hilbert geometry");
+  const int G = g.hil_group, n_vunits = g.n_tiles / G;
+  CHECK(G == 1 || G == 4, "hilbert group %d", G);
+  CHECK(g.n_q == n_vunits + g.has_text, "hilbert units %d", g.n_q);
   for (int u = 0; u < g.n_q; ++u) {
-    const bool text_unit = g.has_text && u == g.n_tiles;
-    int first = 0, count = g.n_tiles, tx = -1, ty = -1;
-    if (!text_unit) {
-      sta::hilbert_d2xy(g.hil_m, u, tx, ty);
-      sta::hilbert_window(u, W, g.n_tiles, g.hilbert, first, count);
-    }
+    const bool text_unit = g.has_text && u == n_vunits;
     sta::HilbertKeyStream ks;
-    ks.init(g, first, count);
-    std::vector<int> keys;
-    for (int j = 0; j < ks.n_blk; ++j) {
-      const sta::KeyBlock b = ks.block(g, j);
-      CHECK(j >= ks.n_plain || b.mask == sta::kKeyBlock, "unit %d block %d masked early", u, j);
-      for (int r = 0; r < b.mask; ++r) {
-        int row;
-        if (b.kind == 0) {
-          CHECK(sta::extent_tokens(b.ext) == 64, "unit %d block %d: tile of %d tokens", u, j, sta::extent_tokens(b.ext));
-          row = b.base + (r >> 3) * g.W + (r & 7);
-        } else {
-          CHECK(b.kind == 1, "unit %d block %d kind %d", u, j, b.kind);
-          row = b.base + r;
+    ks.init(g, G * u, W, text_unit);
+    const int tiles = text_unit ? 1 : G;
+    for (int t = 0; t < tiles; ++t) {
+      int tx = -1, ty = -1;
+      if (!text_unit) sta::hilbert_d2xy(g.hil_m, G * u + t, tx, ty);
+      std::vector<int> keys;
+      for (int j = 0; j < ks.n_blk; ++j) {
+        const sta::KeyBlock b = ks.block(g, j);
+        CHECK(j >= ks.n_plain || b.mask == sta::kKeyBlock, "unit %d block %d masked early", u, j);
+        CHECK(j != 0 || (b.rows_lo == 0 && b.rows_hi >= sta::kKeyBlock * tiles), "unit %d: block 0 not seen by all", u);
+        if (!(b.rows_lo <= sta::kKeyBlock * t && sta::kKeyBlock * t < b.rows_hi)) continue;
+        for (int r = 0; r < b.mask; ++r) {
+          int row;
+          if (b.kind == 0) {
+            CHECK(sta::extent_tokens(b.ext) == 64, "unit %d block %d: tile of %d tokens", u, j,
+                  sta::extent_tokens(b.ext));
+            row = b.base + (r >> 3) * g.W + (r & 7);
+          } else {
+            CHECK(b.kind == 1, "unit %d block %d kind %d", u, j, b.kind);
+            row = b.base + r;
+          }
+          CHECK(row >= 0 && row < g.S, "unit %d block %d row %d outside the sequence", u, j, row);
+          keys.push_back(row);
         }
-        CHECK(row >= 0 && row < g.S, "unit %d block %d row %d outside the sequence", u, j, row);
-        keys.push_back(row);
       }
+      std::sort(keys.begin(), keys.end());
+      for (size_t i = 1; i < keys.size(); ++i) CHECK(keys[i] != keys[i - 1], "unit %d key %d twice", u, keys[i]);
+      std::printf("unit %d %d %d %d", u, t, tx, ty);
+      for (size_t i = 0; i < keys.size();) {
+        size_t e = i + 1;
+        while (e < keys.size() && keys[e] == keys[e - 1] + 1) ++e;
+        std::printf(" %d:%d", keys[i], keys[e - 1] + 1);
+        i = e;
+      }
+      std::printf("\n");
     }
-    std::sort(keys.begin(), keys.end());
-    for (size_t i = 1; i < keys.size(); ++i) CHECK(keys[i] != keys[i - 1], "unit %d key %d twice", u, keys[i]);
-    std::printf("unit %d %d %d", u, tx, ty);
-    for (size_t i = 0; i < keys.size();) {
-      size_t e = i + 1;
-      while (e < keys.size() && keys[e] == keys[e - 1] + 1) ++e;
-      std::printf(" %d:%d", keys[i], keys[e - 1] + 1);
-      i = e;
-    }
-    std::printf("\n");
   }
 }
 

@@ -226,6 +226,9 @@ HSHAPES = [
     (64, 1, 226, 5, 2),
     (64, 0, 0, 16, 2),
     (64, 1, 200, 9, 1),
+    (64, 0, 0, 4, 1),
+    (64, 1, 30, 6, 2),
+    (128, 1, 226, 27, 1),
 ]
 
 
@@ -238,16 +241,18 @@ def test_hilbert_key_stream_matches_oracle_mask(checks_bin, shape):
     out = run(checks_bin, "hstream", side, text, ell, W, mode).splitlines()
     n_tiles = (side // 8) ** 2
     nv = side * side
-    assert len(out) == n_tiles + text
+    m = (side // 8).bit_length() - 1
+    G = 4 if n_tiles % 4 == 0 and (W >= 4 if mode == 1 else W % 4 == 0) else 1
+    assert len(out) == n_tiles + text  # one line per query tile (and one for the text unit)
     for ln in out:
         f = ln.split()
-        u, tx, ty = int(f[1]), int(f[2]), int(f[3])
-        keys = np.concatenate([np.arange(*map(int, r.split(":"))) for r in f[4:]])
-        if u < n_tiles:
-            assert (tx, ty) == hilbert_oracle.hilbert_d2xy((side // 8).bit_length() - 1, u)
+        u, t, tx, ty = int(f[1]), int(f[2]), int(f[3]), int(f[4])
+        keys = np.concatenate([np.arange(*map(int, r.split(":"))) for r in f[5:]])
+        if tx >= 0:
+            assert (tx, ty) == hilbert_oracle.hilbert_d2xy(m, G * u + t)
             row = ty * 8 * side + tx * 8
         else:
             row = nv
         allowed = np.nonzero(hilbert_oracle.hilbert_allowed_mask(
             [row], (side, side), W, "slide" if mode == 1 else "window", ell, bool(text))[0])[0]
-        assert np.array_equal(keys, allowed), f"unit {u}"
+        assert np.array_equal(keys, allowed), f"unit {u} tile {t}"
