@@ -34,6 +34,10 @@
 //                 fragment in the same key order, two ds_read_b64_tr_b16 from
 //                 V rows in LDS (each gives lane l four consecutive keys of one
 //                 column; see the V layout below).
+//   The exponentials of key half 1 are scheduled between the MFMAs of half 0.
+//   The kernel runs at the chip's power limit (the same cycle count takes
+//   about 20% longer on random data than on zeros), so this overlap saves
+//   cycles but little time.
 //
 // Softmax reference. m of a row is the exact maximum of its scaled scores
 // over the first key block of the unit, and it never moves: p = 2^(c s - m)
@@ -414,23 +418,20 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(KernelArgs) 
               }
             }
           }
-          // p = 2^(c s - m) rounded to bf16; O^T += V^T P^T; row sums += 1^T P^T
+          // p = 2^(c s - m) rounded to bf16; O^T += V^T P^T; row sums += 1^T P^T.
+          // The exponentials of key half 1 are interleaved with the MFMAs of
+          // half 0 (they are independent), so the VALU work of that half runs
+          // under the matrix core.
           const char* vb = lds[stage][1] + (lane >> 2) * 64 + (lane & 3) * 8;
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            // V^T fragment d of this half: keys 32h + 4(l/16) + e and
-            // 32h + 16 + 4(l/16) + e of column 16d + l%16; kVPrefetch of them
-            // are read ahead (the first ones under the exponentials)
-            bf16x8 vf[DT];
-            auto vload = [&](int d) {
-              const char* p0 = vb + (d >> 1) * VPAIR + 32 * (d & 1) + 32 * h * 64;
-              const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p0);
-              const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0 + 16 * 64));
-              vf[d] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
-            };
-#pragma unroll
-            for (int d = 0; d < kVPrefetch; ++d) vload(d);
-            bf16x8 pb[QT];
+          // V^T fragment d of half h: keys 32h + 4(l/16) + e and
+          // 32h + 16 + 4(l/16) + e of column 16d + l%16
+          auto vload = [&](int h, int d) -> bf16x8 {
+            const char* p0 = vb + (d >> 1) * VPAIR + 32 * (d & 1) + 32 * h * 64;
+            const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p0);
+            const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0 + 16 * 64));
+            return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+          };
+          auto probs = [&](int h, bf16x8 (&pb)[QT]) {
 #pragma unroll
             for (int c = 0; c < QT; ++c) {
               f32x8 p;
@@ -446,15 +447,37 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(KernelArgs) 
                 l_part[c] = __builtin_amdgcn_fdot2_f32_bf16(pair, ones2, l_part[c], false);
               }
             }
+          };
+          bf16x8 vf0[DT], vf1[DT], pb0[QT], pb1[QT];
+#pragma unroll
+          for (int d = 0; d < kVPrefetch; ++d) vf0[d] = vload(0, d);
+          probs(0, pb0);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int d = 0; d < DT; ++d) {
+#pragma unroll
+            for (int c = 0; c < QT; ++c)
+              acc[c][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf0[d], pb0[c], acc[c][d], 0, 0, 0);
+            if (d + kVPrefetch < DT) vf0[d + kVPrefetch] = vload(0, d + kVPrefetch);
+          }
+          probs(1, pb1);
+#pragma unroll
+          for (int d = 0; d < kVPrefetch; ++d) vf1[d] = vload(1, d);
+          // per MFMA of half 0: one LDS read and up to 3 VALU instructions
+#pragma unroll
+          for (int i = 0; i < QT * DT; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int d = 0; d < DT; ++d) {
+#pragma unroll
+            for (int c = 0; c < QT; ++c)
+              acc[c][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf1[d], pb1[c], acc[c][d], 0, 0, 0);
+            if (d + kVPrefetch < DT) vf1[d + kVPrefetch] = vload(1, d + kVPrefetch);
             __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int d = 0; d < DT; ++d) {
-#pragma unroll
-              for (int c = 0; c < QT; ++c)
-                acc[c][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[d], pb[c], acc[c][d], 0, 0, 0);
-              if (d + kVPrefetch < DT) vload(d + kVPrefetch);
-              __builtin_amdgcn_sched_barrier(0);
-            }
           }
         }
       };
