@@ -1,9 +1,9 @@
 #!/usr/bin/env python3
 """Benchmark of the STA forward (one GPU); ``--pass backward`` times the backward.
 
-One step = one sta_forward call (pack v to tile-major V^T fragments, build
-the tile-window schedule and work order, fused attention reading q and k and
-writing out/lse in raster order) on the workload's synthetic bf16 inputs,
+One step = one sta_forward call (the work order, then the fused attention
+kernel reading q, k and v and writing out/lse in raster order; it enumerates
+each query tile's window itself) on the workload's synthetic bf16 inputs,
 which are resident in HBM before timing starts. Prints one JSON line with the
 end-to-end effective TFLOP/s, the roofline of the fused attention kernel
 (timed live with HIP events on the launch stream) and the fp64 CPU oracle's
@@ -14,7 +14,7 @@ rows (video rows and the first text_length text rows), i.e. only the tiles
 that are computed.
 
 With ``--pass backward`` one step is one sta_backward call (row statistics,
-fragment packing of k, q and dout, tile lists, the dq pass, the dk/dv pass)
+tile lists, the dq pass, the dk/dv pass)
 for the forward's out/lse and a synthetic dout; its effective FLOPs are
 10*D per allowed pair (five products of 2*D: the recomputed scores, dP, dV,
 dQ and dK), the usual count for an attention backward.

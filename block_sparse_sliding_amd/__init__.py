@@ -297,8 +297,8 @@ def sliding_tile_attention(q, k, v, window_size, text_length: int = 0, has_text:
 
 
 # ----------------------------------------------------------------- backward
-BWD_TIMED_EVENTS = 6
-BWD_STAGES = ("row_stats", "pack_k_q_dout", "schedule_lists", "dq", "dkv")
+BWD_TIMED_EVENTS = 5
+BWD_STAGES = ("row_stats", "schedule_lists", "dq", "dkv")
 
 
 def sta_backward_workspace_bytes(dims: sta_dims, window_sizes, has_text: bool) -> int:

@@ -458,23 +458,20 @@ sta_status sta_forward_noalloc(const sta_dims* dims, const void* q, const void* 
 namespace {
 
 struct BwdCarve {
-  size_t kt, qt, dot, lse2, delta, offsets, ids, claim_q, claim_kv, total;
+  size_t lse2, delta, offsets, ids, claim_q, claim_kv, zero_row, total;
 };
 
 BwdCarve bwd_carve(const Geom& g, int64_t n_ids) {
   BwdCarve c{};
-  const size_t tensor = size_t(g.B) * g.heads * g.S_t * g.D * 2;  // packed, tile-major
-  const size_t rows = size_t(g.B) * g.heads * g.S_t * 4;          // tile-major rows
+  const size_t rows = size_t(g.B) * g.heads * g.S_t * 4;  // tile-major rows
   size_t at = 0;
-  c.kt = at; at = align_up(at + tensor);
-  c.qt = at; at = align_up(at + tensor);
-  c.dot = at; at = align_up(at + tensor);
   c.lse2 = at; at = align_up(at + rows);
   c.delta = at; at = align_up(at + rows);
   c.offsets = at; at = align_up(at + (size_t(g.heads) * g.n_q + 1) * 4);
   c.ids = at; at = align_up(at + size_t(n_ids) * 4);
   c.claim_q = at; at = align_up(at + size_t(sta::kClaimInts) * 4);
   c.claim_kv = at; at = align_up(at + size_t(sta::kClaimInts) * 4);
+  c.zero_row = at; at = align_up(at + size_t(sta::kZeroRowBytes));
   c.total = at;
   return c;
 }
@@ -527,9 +524,7 @@ sta_status backward_impl(const sta_dims* dims, const void* q, const void* k, con
   a.k = k;
   a.v = v;
   a.dout = dout;
-  a.kt = ws + c.kt;
-  a.qt = ws + c.qt;
-  a.dot = ws + c.dot;
+  a.zero_row = ws + c.zero_row;
   a.lse2 = reinterpret_cast<float*>(ws + c.lse2);
   a.delta = reinterpret_cast<float*>(ws + c.delta);
   a.dq = dq;
@@ -548,19 +543,14 @@ sta_status backward_impl(const sta_dims* dims, const void* q, const void* k, con
   if (st == STA_OK)
     st = hip_status(sta::launch_bwd_prep(g, out, dout, lse, reinterpret_cast<float*>(ws + c.lse2),
                                          reinterpret_cast<float*>(ws + c.delta), a.claim_q,
-                                         a.claim_kv, s));
+                                         a.claim_kv, ws + c.zero_row, s));
   if (st == STA_OK) st = mark(1);
-  if (st == STA_OK)
-    st = hip_status(sta::launch_pack_rows(g, k, ws + c.kt, g.n_vt + (g.has_text ? g.text_length : 0), s));
-  if (st == STA_OK) st = hip_status(sta::launch_pack_rows(g, q, ws + c.qt, g.S_t, s));
-  if (st == STA_OK) st = hip_status(sta::launch_pack_rows(g, dout, ws + c.dot, g.S_t, s));
-  if (st == STA_OK) st = mark(2);
   if (st == STA_OK) st = hip_status(sta::launch_schedule_lists(g, win, offsets, ids, s));
-  if (st == STA_OK) st = mark(3);
+  if (st == STA_OK) st = mark(2);
   if (st == STA_OK) st = hip_status(sta::launch_bwd_dq(g, win, a, s));
-  if (st == STA_OK) st = mark(4);
+  if (st == STA_OK) st = mark(3);
   if (st == STA_OK) st = hip_status(sta::launch_bwd_dkv(g, win, a, s));
-  if (st == STA_OK) st = mark(5);
+  if (st == STA_OK) st = mark(4);
   return st;
 }
 

@@ -10,23 +10,33 @@
 //   dq = c dS k,     dk = c dS^T q,     dv = P^T dout.
 // The page shows only the forward call; these follow from its definition.
 //
-// Three passes over the inputs, each a launch on the caller's stream:
+// Three launches on the caller's stream:
 //   prep   lse2 = lse * log2(e) and -delta, per row in tile-major order;
-//   pack   K^T, Q^T and dout^T as MFMA A-operand fragments (the forward's V^T
-//          packing, applied to these tensors);
 //   dq     query-stationary: the forward's loop with S^T = K Q^T and
-//          dP^T = V dout^T from LDS (K and V raw, same swizzled layout), then
-//          dq^T += K^T dS^T with K^T fragments from LDS;
+//          dP^T = V dout^T, K and V rows streamed into LDS, then
+//          dq^T += K^T dS^T with K^T fragments read transposed from the same
+//          K rows in LDS;
 //   dk/dv  key-stationary: units of 256 keys (32 per wave) or 128 keys (16
 //          per wave), their K and V rows held as MFMA B operands, streaming
 //          every query block that sees the keys: S = Q K^T and dP = dout V^T
-//          with Q and dout raw in LDS, then dv^T += dout^T P and
-//          dk^T += Q^T dS with Q^T / dout^T fragments, each 64-row block in
-//          two halves of 32 queries (so two key groups fit the registers and
-//          every fragment read from LDS feeds two MFMAs).
-// The packed fragments present their 64 rows in the order in which a
-// 16x16x32 MFMA accumulator leaves its rows in the lanes, so P and dS go from
-// the accumulator straight into the B operand, as in the forward's PV step.
+//          with Q and dout rows in LDS, then dv^T += dout^T P and
+//          dk^T += Q^T dS with Q^T / dout^T fragments read transposed from
+//          the same rows, each 64-row block in two halves of 32 queries (so
+//          two key groups fit the registers and every fragment read from LDS
+//          feeds two MFMAs).
+// A transposed fragment (two ds_read_b64_tr_b16) presents its 32 rows in the
+// order in which a 16x16x32 MFMA accumulator leaves its rows in the lanes, so
+// P and dS go from the accumulator straight into the B operand, as in the
+// forward's PV step.
+//
+// LDS layout of a streamed 64-row block: column pair P (columns 32P ..
+// 32P + 31) takes 4 KB, 64 bytes per row, row r at 64 r; the four 16-byte
+// chunks of a row are permuted, chunk c of row r sitting at position
+// c XOR sigma((r / 4) mod 4), sigma = (0, 2, 1, 3). A row fragment (lane l:
+// 16 bytes of row R + l%16, chunk l/16) and a transposed read (lane l: 8
+// bytes of row R + l/4) then both touch every bank once per LDS cycle. The
+// LDS-DMA that fills a block applies the permutation through its per-lane
+// source addresses.
 //
 // Key-side work: a key tile is seen by the query tiles whose clamped window
 // holds it. Along one axis the window start clamp(c - w/2, 0, n - w) never
@@ -39,13 +49,13 @@
 // tile along an axis holds the remainder, and a partial tile's tile-major
 // slot holds its existing tokens first, in compact order (frame, row,
 // column), then padding. Stationary rows and keys are those tokens; streamed
-// tiles contribute ceil(tokens / 64) blocks whose raw rows are fetched per
-// lane through the compact map, clamped to the last token (every address
-// stays inside the video). Packed padding rows are zeros and prep gives
-// padding query rows lse2 = +inf and -delta = 0, so their P and dS are
-// exactly 0 wherever they are streamed; padding key rows add nothing to dq
-// (their packed K^T rows are zero and their dS finite, computed on a copy of
-// a key of the same tile), and padding rows of dq, dk, dv are not written.
+// tiles contribute ceil(tokens / 64) blocks whose rows are fetched per lane
+// through the compact map. Streamed rows that are not tokens (and, in the dq
+// pass, text key slots at or after text_length) are fetched from a zero row
+// in the workspace. prep gives padding query rows lse2 = +inf and -delta = 0,
+// so their P and dS are exactly 0 wherever they are streamed; zero key rows
+// add nothing to dq (their K^T is zero and their dS finite), and padding rows
+// of dq, dk, dv are not written.
 #include <type_traits>
 
 #include "sta_device.h"
@@ -58,11 +68,37 @@ constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int kQueryBlock = 64;                     // query rows per streamed block (dk/dv)
 constexpr int kKPrefetch = 4;                       // A fragments in flight (dq contractions)
-constexpr int kKvPrefetch = 2;                      // A fragments in flight (dk/dv contractions)
+constexpr int kKvPrefetch = 1;                      // A fragments in flight (dk/dv contractions)
 constexpr float kLog2e = 1.44269504088896340736f;
 
-static_assert(kKeyBlock == kQueryBlock, "one packed block size for keys and queries");
+static_assert(kKeyBlock == kQueryBlock, "one block size for keys and queries");
 static_assert(kTileRows == 256 + 128 && kTextSlots == 256, "dk/dv unit shapes below");
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+constexpr int kPair = kQueryBlock * 64;  // bytes of one column pair of a block
+
+// the chunk permutation of the block layout: sigma(k), k = (row / 4) mod 4
+__device__ inline int sigma(int k) { return ((k & 1) << 1) | ((k >> 1) & 1); }
+// this lane's offset for row fragments: row l%16 of a 16-row group, chunk l/16
+__device__ inline int row_frag_offset(int l) { return (l & 15) * 64 + 16 * ((l >> 4) ^ sigma((l >> 2) & 3)); }
+// this lane's offset for transposed reads of column half e (columns 16e ..
+// 16e + 15 of a pair): 8 bytes of row l/4, columns 16e + 4 (l%4) ..
+__device__ inline int tr_offset(int l, int e) {
+  return (l >> 2) * 64 + 16 * ((2 * e + ((l >> 1) & 1)) ^ sigma((l >> 4) & 3)) + 8 * (l & 1);
+}
+// A operand for a product over 32 block rows: lane l gets, for column
+// 16 dt + l%16, the rows 32 h + 4 (l/16) + e and 32 h + 16 + 4 (l/16) + e
+// (e = 0..3); tro = tr_offset(lane, dt % 2)
+__device__ inline bf16x8 tr_frag(const char* blk, int h, int dt, int tro) {
+  const char* p0 = blk + (dt >> 1) * kPair + 32 * h * 64 + tro;
+  const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p0);
+  const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0 + 16 * 64));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+// source byte offset, inside its row, of the 16 bytes lane l of an LDS-DMA
+// group q writes: group q fills rows 16 (q % 4) + l/4 of column pair q / 4
+__device__ inline int dma_col_offset(int q, int l) { return 64 * (q >> 2) + 16 * ((l & 3) ^ sigma((l >> 4) & 3)); }
 
 struct KernelArgs {
   Geom g;
@@ -178,12 +214,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(KernelArgs) {
   constexpr int DT = D / 16;
   constexpr int ROWB = D * 2;
   constexpr int BLK = kKeyBlock * ROWB;
-  constexpr int RPI = 1024 / ROWB;
   constexpr int IPW = BLK / 1024 / kWaves;
   constexpr int BPT = kTileRows / kKeyBlock;
   static_assert(IPW >= 1 && BLK % (1024 * kWaves) == 0, "block must split over the waves");
-  // [stage][K raw | V raw | K^T packed]
-  __shared__ __attribute__((aligned(1024))) char lds[2][3][BLK];
+  // [stage][K | V], 64-row blocks in the column-pair layout
+  __shared__ __attribute__((aligned(1024))) char lds[2][2][BLK];
   __shared__ int claimed;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
@@ -262,8 +297,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(KernelArgs) {
     const __bf16* __restrict__ dor = reinterpret_cast<const __bf16*>(a.dout) + slab;
     const char* __restrict__ kr = reinterpret_cast<const char*>(a.k) + slab * 2;
     const char* __restrict__ vr = reinterpret_cast<const char*>(a.v) + slab * 2;
-    const size_t slab_t = size_t(bh) * g.S_t * D;  // packed tile-major tensors
-    const char* __restrict__ ktr = reinterpret_cast<const char*>(a.kt) + slab_t * 2;
+    const char* __restrict__ zr = reinterpret_cast<const char*>(a.zero_row);
     const float* __restrict__ lse2 = a.lse2 + size_t(bh) * g.S_t;
     const float* __restrict__ dlt = a.delta + size_t(bh) * g.S_t;
 
@@ -287,16 +321,15 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(KernelArgs) {
     const int text_len = g.has_text ? g.text_length : 0;
     const int n_blk = n_valid > 0 ? n_vid + (text_len + kKeyBlock - 1) / kKeyBlock : 0;
     const bool ragged = (text_len % kKeyBlock) != 0;
-    auto sw = [](int row) { return (row >> 2) & 2; };
     const __attribute__((address_space(4))) int32_t* ids =
         (const __attribute__((address_space(4))) int32_t*)(a.ids + l0);
 
     // with PAD, tile_ext: packed extent of the current key tile (the frames,
     // rows and columns that exist); its blocks are 64 compact tokens each
-    int tile_kbase = 0, tile_vrow = 0;
+    int tile_kbase = 0;
     int tile_ext = kFullExtent;  // PAD: packed extent of the current tile
     int cur_t = 0, cur_sub = -1;  // PAD: the forward's walk over existing frames
-    auto block_rows = [&](int j, int& kbase, int& krs, int& vrow) {
+    auto block_rows = [&](int j, int& kbase, int& krs) {
       if (j < n_vid) {
         int t, sub;
         if constexpr (PAD) {
@@ -317,39 +350,37 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(KernelArgs) {
           const int tt = div_by(rest, g.nh, g.mag_nh);
           const int th = rest - tt * g.nh;
           tile_kbase = (tt * kTileT * g.H + th * kTileH) * g.W + tw * kTileW;
-          tile_vrow = tile * kTileRows;
           if constexpr (PAD) tile_ext = tile_extent(tt, th, tw, g);
         }
         kbase = tile_kbase + sub * g.H * g.W;
         krs = g.W;
-        vrow = tile_vrow + sub * kKeyBlock;
       } else {
         kbase = g.n_video + (j - n_vid) * kKeyBlock;
-        vrow = g.n_vt + (j - n_vid) * kKeyBlock;
         krs = kTileW;
         if constexpr (PAD) tile_ext = kFullExtent;
       }
     };
-    // raw rows kbase + (rr/8)*krs + rr%8 of tensor `src` into LDS region `dst`
-    // (the forward's swizzled K layout)
-    auto issue_raw = [&](const char* src, char* dst, int kbase, int krs) {
-      // PAD: per-lane offsets from a fresh opaque lane id, rebuilt per block
-      // rather than hoisted (and spilled) as 64-bit addresses
-      int lane = opaque_lane<PAD>(this_lane);
+    // rows 0 .. 63 of a key block of tensor `src` into LDS region `dst` (the
+    // block layout): block row r is raster row kbase + (r / 8) krs + r % 8
+    // while r < lim and the zero row from lim on; PAD, in a tile with missing
+    // rows or columns: row r is token 64 sub + r of the tile in compact order,
+    // the zero row past its tokens
+    auto issue_rows = [&](const char* src, char* dst, int kbase, int krs, int lim) {
+      // per-lane offsets from a fresh opaque lane id, rebuilt per block rather
+      // than hoisted (and spilled) across the loop
+      int lane = opaque_lane<true>(this_lane);
       if constexpr (PAD) {
         if ((tile_ext >> 8) != (kFullExtent >> 8)) {
-          // a tile with missing rows or columns: block row r is token 64 sub + r
-          // of the tile in compact order, clamped to the last one that exists
-          const int last = extent_tokens(tile_ext) - 1;
+          const int n_tok = extent_tokens(tile_ext);
 #pragma unroll
           for (int i = 0; i < IPW; ++i) {
             const int q = wave * IPW + i;
-            const int rin = (lane >> 2) % RPI;
+            const int tok = cur_sub * kKeyBlock + 16 * (q & 3) + (lane >> 2);
             int dt, dh, dw;
-            compact_token(min(cur_sub * kKeyBlock + q * RPI + rin, last), tile_ext, dt, dh, dw);
+            compact_token(tok < n_tok ? tok : 0, tile_ext, dt, dh, dw);
             const int row = tile_kbase + (dt * g.H + dh) * g.W + dw;
-            const int chunk = 4 * (lane / (4 * RPI)) + ((lane & 3) ^ sw(q * RPI + rin));
-            dma16(src + size_t(row) * ROWB + chunk * 16, dst + q * 1024);
+            const int col = dma_col_offset(q, lane);
+            dma16(tok < n_tok ? src + size_t(row) * ROWB + col : zr + col, dst + q * 1024);
           }
           return;
         }
@@ -357,21 +388,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(KernelArgs) {
 #pragma unroll
       for (int i = 0; i < IPW; ++i) {
         const int q = wave * IPW + i;
-        const size_t urow = size_t(kbase + ((q * RPI) >> 3) * krs + ((q * RPI) & 7));
-        const int rin = (lane >> 2) % RPI;
-        const int chunk = 4 * (lane / (4 * RPI)) + ((lane & 3) ^ sw(q * RPI + rin));
-        const unsigned o = unsigned(rin * ROWB + chunk * 16);
-        dma16(src + urow * ROWB + o, dst + q * 1024);
-      }
-    };
-    auto issue_packed = [&](const char* src, char* dst, int vrow) {
-      int lane = opaque_lane<PAD>(this_lane);
-      const char* p = src + size_t(vrow) * ROWB;
-      const unsigned o = unsigned(lane) * 16u;
-#pragma unroll
-      for (int i = 0; i < IPW; ++i) {
-        const int q = wave * IPW + i;
-        dma16(p + q * 1024 + o, dst + q * 1024);
+        const int r = 16 * (q & 3) + (lane >> 2);
+        const size_t urow = size_t(kbase + (r >> 3) * krs + (r & 7));
+        const unsigned o = unsigned(dma_col_offset(q, lane));
+        dma16(r < lim ? src + urow * ROWB + o : zr + o, dst + q * 1024);
       }
     };
 
@@ -402,14 +422,14 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(KernelArgs) {
 #pragma unroll
         for (int d = 0; d < DT; ++d) acc[c][d] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-      const int l15 = lane & 15;
-      const int kofs = (l15 / RPI) * 1024 + (l15 % RPI) * 64 + (((lane >> 4) ^ sw(l15)) << 4);
+      const int rfo = row_frag_offset(lane);
+      const int tro[2] = {tr_offset(lane, 0), tr_offset(lane, 1)};
       auto issue = [&](int j, int st) {
-        int kbase, krs, vrow;
-        block_rows(j, kbase, krs, vrow);
-        issue_raw(kr, lds[st][0], kbase, krs);
-        issue_raw(vr, lds[st][1], kbase, krs);
-        issue_packed(ktr, lds[st][2], vrow);
+        int kbase, krs;
+        block_rows(j, kbase, krs);
+        const int lim = j < n_vid ? kKeyBlock : text_len - (j - n_vid) * kKeyBlock;
+        issue_rows(kr, lds[st][0], kbase, krs, lim);
+        issue_rows(vr, lds[st][1], kbase, krs, lim);
       };
 
       // A x B^T-style score product over one raw block in LDS: out[c][kt] =
@@ -419,7 +439,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(KernelArgs) {
         constexpr int NF = 4 * KS;
         bf16x8 kf[NF];
         auto kload = [&](int f) {
-          kf[f] = *reinterpret_cast<const bf16x8*>(blk + kofs + (f & 3) * 16 * ROWB + (f >> 2) * 64 * RPI);
+          kf[f] = *reinterpret_cast<const bf16x8*>(blk + (f >> 2) * kPair + (f & 3) * 16 * 64 + rfo);
         };
 #pragma unroll
         for (int f = 0; f < kKPrefetch; ++f) kload(f);
@@ -486,8 +506,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(KernelArgs) {
 #pragma unroll
                 for (int c = 0; c < QT; ++c) dp[c][kt][r] = 0.f;
         }
-        // dq^T += K^T dS^T
-        const bf16x8* ktl = reinterpret_cast<const bf16x8*>(lds[stage][2]);
+        // dq^T += K^T dS^T, K^T read transposed from the K rows
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           bf16x8 db[QT];
@@ -503,7 +522,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(KernelArgs) {
           }
 #pragma unroll
           for (int d = 0; d < DT; ++d) {
-            const bf16x8 kf = ktl[(h * DT + d) * 64 + lane];
+            const bf16x8 kf = tr_frag(lds[stage][0], h, d, tro[d & 1]);
 #pragma unroll
             for (int c = 0; c < QT; ++c)
               acc[c][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, db[c], acc[c][d], 0, 0, 0);
@@ -547,12 +566,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(KernelArgs) {
   constexpr int DT = D / 16;
   constexpr int ROWB = D * 2;
   constexpr int BLK = kQueryBlock * ROWB;
-  constexpr int RPI = 1024 / ROWB;
   constexpr int IPW = BLK / 1024 / kWaves;
   constexpr int BPT = kTileRows / kQueryBlock;
   static_assert(IPW >= 1 && BLK % (1024 * kWaves) == 0, "block must split over the waves");
-  // [stage][Q raw | dout raw | Q^T packed | dout^T packed], then lse2 and delta
-  __shared__ __attribute__((aligned(1024))) char lds[2][4][BLK];
+  // [stage][Q | dout], 64-row blocks in the column-pair layout, then lse2 and delta
+  __shared__ __attribute__((aligned(1024))) char lds[2][2][BLK];
   __shared__ __attribute__((aligned(16))) float rowv[2][2][kQueryBlock];
   __shared__ int claimed;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -612,7 +630,6 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(KernelArgs) {
       }
     }
     const size_t slab = size_t(bh) * g.S * D;
-    const size_t slab_t = size_t(bh) * g.S_t * D;  // packed tile-major tensors
     const int text_len = g.has_text ? g.text_length : 0;
     // text key slots at or after text_len are seen by nobody
     const int valid_keys = text_unit ? min(max(g.n_vt + text_len - key_row0, 0), unit_keys)
@@ -628,11 +645,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(KernelArgs) {
 
     const char* __restrict__ qr = reinterpret_cast<const char*>(a.q) + slab * 2;
     const char* __restrict__ dor = reinterpret_cast<const char*>(a.dout) + slab * 2;
-    const char* __restrict__ qtr = reinterpret_cast<const char*>(a.qt) + slab_t * 2;
-    const char* __restrict__ dotr = reinterpret_cast<const char*>(a.dot) + slab_t * 2;
+    const char* __restrict__ zr = reinterpret_cast<const char*>(a.zero_row);
     const char* __restrict__ lse2 = reinterpret_cast<const char*>(a.lse2 + size_t(bh) * g.S_t);
     const char* __restrict__ dlt = reinterpret_cast<const char*>(a.delta + size_t(bh) * g.S_t);
-    auto sw = [](int row) { return (row >> 2) & 2; };
 
     // query block j: raster origin of its rows and its first tile-major row;
     // with PAD, tile_ext describes the current query tile as in the dq kernel
@@ -680,20 +695,25 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(KernelArgs) {
         if constexpr (PAD) tile_ext = kFullExtent;
       }
     };
-    auto issue_raw = [&](const char* src, char* dst, int qbase, int qrs) {
-      int lane = opaque_lane<PAD>(this_lane);  // as in the dq kernel
+    // rows 0 .. 63 of a query block of tensor `src` into LDS region `dst`
+    // (the block layout), as in the dq kernel: block row r is raster row
+    // qbase + (r / 8) qrs + r % 8; PAD, in a tile with missing rows or columns,
+    // token 64 sub + r of the tile in compact order, the zero row past its
+    // tokens (prep gives those rows lse2 = +inf and -delta = 0)
+    auto issue_rows = [&](const char* src, char* dst, int qbase, int qrs) {
+      int lane = opaque_lane<true>(this_lane);  // as in the dq kernel
       if constexpr (PAD) {
-        if ((tile_ext >> 8) != (kFullExtent >> 8)) {  // compact order, as in the dq kernel
-          const int last = extent_tokens(tile_ext) - 1;
+        if ((tile_ext >> 8) != (kFullExtent >> 8)) {
+          const int n_tok = extent_tokens(tile_ext);
 #pragma unroll
           for (int i = 0; i < IPW; ++i) {
             const int q = wave * IPW + i;
-            const int rin = (lane >> 2) % RPI;
+            const int tok = cur_sub * kQueryBlock + 16 * (q & 3) + (lane >> 2);
             int dt, dh, dw;
-            compact_token(min(cur_sub * kQueryBlock + q * RPI + rin, last), tile_ext, dt, dh, dw);
+            compact_token(tok < n_tok ? tok : 0, tile_ext, dt, dh, dw);
             const int row = tile_qbase + (dt * g.H + dh) * g.W + dw;
-            const int chunk = 4 * (lane / (4 * RPI)) + ((lane & 3) ^ sw(q * RPI + rin));
-            dma16(src + size_t(row) * ROWB + chunk * 16, dst + q * 1024);
+            const int col = dma_col_offset(q, lane);
+            dma16(tok < n_tok ? src + size_t(row) * ROWB + col : zr + col, dst + q * 1024);
           }
           return;
         }
@@ -701,31 +721,18 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(KernelArgs) {
 #pragma unroll
       for (int i = 0; i < IPW; ++i) {
         const int q = wave * IPW + i;
-        const size_t urow = size_t(qbase + ((q * RPI) >> 3) * qrs + ((q * RPI) & 7));
-        const int rin = (lane >> 2) % RPI;
-        const int chunk = 4 * (lane / (4 * RPI)) + ((lane & 3) ^ sw(q * RPI + rin));
-        unsigned o = unsigned(rin * ROWB + chunk * 16);
+        const int r = 16 * (q & 3) + (lane >> 2);
+        const size_t urow = size_t(qbase + (r >> 3) * qrs + (r & 7));
+        unsigned o = unsigned(dma_col_offset(q, lane));
         asm volatile("" : "+v"(o));  // keep base + offset per block (no hoisted 64-bit address)
         dma16(src + urow * ROWB + o, dst + q * 1024);
-      }
-    };
-    auto issue_packed = [&](const char* src, char* dst, int vrow) {
-      const char* p = src + size_t(vrow) * ROWB;
-      unsigned o = unsigned(lane) * 16u;
-      asm volatile("" : "+v"(o));
-#pragma unroll
-      for (int i = 0; i < IPW; ++i) {
-        const int q = wave * IPW + i;
-        dma16(p + q * 1024 + o, dst + q * 1024);
       }
     };
     auto issue = [&](int j, int st) {
       int qbase, qrs, vrow;
       block_rows(j, qbase, qrs, vrow);
-      issue_raw(qr, lds[st][0], qbase, qrs);
-      issue_raw(dor, lds[st][1], qbase, qrs);
-      issue_packed(qtr, lds[st][2], vrow);
-      issue_packed(dotr, lds[st][3], vrow);
+      issue_rows(qr, lds[st][0], qbase, qrs);
+      issue_rows(dor, lds[st][1], qbase, qrs);
       unsigned o4 = unsigned(lane) * 4u;
       asm volatile("" : "+v"(o4));
       if (wave == 0) dma4(lse2 + size_t(vrow) * 4 + o4, reinterpret_cast<char*>(rowv[st][0]));
@@ -733,30 +740,36 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(KernelArgs) {
     };
 
     const float qs = a.q_scale;
-    const int l15 = lane & 15;
-    const int qofs = (l15 / RPI) * 1024 + (l15 % RPI) * 64 + (((lane >> 4) ^ sw(l15)) << 4);
+    const int rfo = row_frag_offset(lane);
+    const int tro[2] = {tr_offset(lane, 0), tr_offset(lane, 1)};
 
     auto run = [&](auto kt_c) {
       constexpr int KT = decltype(kt_c)::value;  // 16-key groups per wave
-      // this wave's keys: K and V rows as B operands (lane: key l%16, d chunk l/16)
-      int kras[KT];
-      bool key_ok[KT];
-      bf16x8 kf[KT][KS], vf[KT][KS];
-#pragma unroll
-      for (int kg = 0; kg < KT; ++kg) {
-        const int local = wave * 16 * KT + 16 * kg + (lane & 15);
-        const int key = key_row0 + local;
-        key_ok[kg] = !text_unit || key < g.n_vt + text_len;
-        kras[kg] = PAD ? tiled_to_raster(key, g) : tiled_to_raster_full(key, g);
-        int ksrc = kras[kg];
+      // lane ln's key of group kg: the raster row its gradients go to (PAD:
+      // -1 for a key past the unit's tokens) and, in ksrc, the row its K and V
+      // are read from
+      auto key_rows = [&](int ln, int kg, int& ksrc) {
+        const int local = wave * 16 * KT + 16 * kg + (ln & 15);
+        int kras = PAD ? tiled_to_raster(key_row0 + local, g) : tiled_to_raster_full(key_row0 + local, g);
+        ksrc = kras;
         if constexpr (PAD) {
           if (!text_unit) {  // compact order; a key past n_keys computes on the last one, never written
             int dt, dh, dw;
             compact_token(k_first + (local < n_keys ? local : n_keys - 1), k_ext, dt, dh, dw);
             ksrc = k_base + (dt * g.H + dh) * g.W + dw;
-            kras[kg] = local < n_keys ? ksrc : -1;
+            kras = local < n_keys ? ksrc : -1;
           }
         }
+        return kras;
+      };
+      // this wave's keys: K and V rows as B operands (lane: key l%16, d chunk l/16)
+      bool key_ok[KT];
+      bf16x8 kf[KT][KS], vf[KT][KS];
+#pragma unroll
+      for (int kg = 0; kg < KT; ++kg) {
+        key_ok[kg] = !text_unit || key_row0 + wave * 16 * KT + 16 * kg + (lane & 15) < g.n_vt + text_len;
+        int ksrc;
+        key_rows(lane, kg, ksrc);
         const bf16x8* k8 = reinterpret_cast<const bf16x8*>(reinterpret_cast<const __bf16*>(a.k) + slab +
                                                            size_t(ksrc) * D + (lane >> 4) * 8);
         const bf16x8* v8 = reinterpret_cast<const bf16x8*>(reinterpret_cast<const __bf16*>(a.v) + slab +
@@ -782,7 +795,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(KernelArgs) {
         constexpr int NF = 2 * KS;
         bf16x8 af[NF];
         auto aload = [&](int f) {
-          af[f] = *reinterpret_cast<const bf16x8*>(blk + qofs + (2 * hq + (f & 1)) * 16 * ROWB + (f >> 1) * 64 * RPI);
+          af[f] = *reinterpret_cast<const bf16x8*>(blk + (f >> 1) * kPair + (2 * hq + (f & 1)) * 16 * 64 + rfo);
         };
 #pragma unroll
         for (int f = 0; f < kKvPrefetch; ++f) aload(f);
@@ -816,8 +829,6 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(KernelArgs) {
         __syncthreads();
         const f32x4* l2v = reinterpret_cast<const f32x4*>(rowv[stage][0]);
         const f32x4* dlv = reinterpret_cast<const f32x4*>(rowv[stage][1]);
-        const bf16x8* qtl = reinterpret_cast<const bf16x8*>(lds[stage][2]);
-        const bf16x8* dotl = reinterpret_cast<const bf16x8*>(lds[stage][3]);
 #pragma unroll
         for (int hq = 0; hq < 2; ++hq) {
           f32x4 s[KT][2], dp[KT][2];
@@ -866,11 +877,12 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(KernelArgs) {
             pb[kg] = __builtin_convertvector(x, bf16x8);
             db[kg] = __builtin_convertvector(y, bf16x8);
           }
-          // dv^T += dout^T P, dk^T += Q^T dS over this half's 32 queries
+          // dv^T += dout^T P, dk^T += Q^T dS over this half's 32 queries, with
+          // dout^T and Q^T read transposed from the rows
 #pragma unroll
           for (int d = 0; d < DT; ++d) {
-            const bf16x8 fo = dotl[(hq * DT + d) * 64 + lane];
-            const bf16x8 fq = qtl[(hq * DT + d) * 64 + lane];
+            const bf16x8 fo = tr_frag(lds[stage][1], hq, d, tro[d & 1]);
+            const bf16x8 fq = tr_frag(lds[stage][0], hq, d, tro[d & 1]);
 #pragma unroll
             for (int kg = 0; kg < KT; ++kg) {
               dv[kg][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fo, pb[kg], dv[kg][d], 0, 0, 0);
@@ -880,11 +892,15 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(KernelArgs) {
         }
       }
       // dk = c * acc, dv = acc; C row = d (4 (l/16) + r of each 16-group), column = key
+      // (the key rows recomputed here rather than kept live across the loop)
+      const int ln = opaque_lane<true>(this_lane);
 #pragma unroll
       for (int kg = 0; kg < KT; ++kg) {
-        if (PAD && kras[kg] < 0) continue;
-        __bf16* dkr = reinterpret_cast<__bf16*>(a.dk) + slab + size_t(kras[kg]) * D + (lane >> 4) * 4;
-        __bf16* dvr = reinterpret_cast<__bf16*>(a.dv) + slab + size_t(kras[kg]) * D + (lane >> 4) * 4;
+        int ksrc;
+        const int kras = key_rows(ln, kg, ksrc);
+        if (PAD && kras < 0) continue;
+        __bf16* dkr = reinterpret_cast<__bf16*>(a.dk) + slab + size_t(kras) * D + (ln >> 4) * 4;
+        __bf16* dvr = reinterpret_cast<__bf16*>(a.dv) + slab + size_t(kras) * D + (ln >> 4) * 4;
 #pragma unroll
         for (int d = 0; d < DT; ++d) {
           *reinterpret_cast<bf16x4*>(dkr + d * 16) = __builtin_convertvector(dk[kg][d] * a.scale, bf16x4);
@@ -920,22 +936,24 @@ hipError_t launch_dkv(const Geom& g, const Windows& win, const BwdArgs& a, hipSt
   return hipGetLastError();
 }
 
-__global__ void zero_claims_kernel(int32_t* a, int32_t* b) {
+__global__ void zero_claims_kernel(int32_t* a, int32_t* b, int32_t* zero_row) {
   a[threadIdx.x] = 0;
   b[threadIdx.x] = 0;
+  if (threadIdx.x < kZeroRowBytes / 4) zero_row[threadIdx.x] = 0;
 }
 
 }  // namespace
 
 hipError_t launch_bwd_prep(const Geom& g, const void* out, const void* dout, const float* lse,
                            float* lse2, float* delta, int32_t* claim_q, int32_t* claim_kv,
-                           hipStream_t stream) {
+                           void* zero_row, hipStream_t stream) {
   dim3 grid(g.S_t / 64, g.B * g.heads);
   if (g.D == 128)
     bwd_prep_kernel<128><<<grid, 256, 0, stream>>>(g, (const __bf16*)out, (const __bf16*)dout, lse, lse2, delta);
   else
     bwd_prep_kernel<64><<<grid, 256, 0, stream>>>(g, (const __bf16*)out, (const __bf16*)dout, lse, lse2, delta);
-  zero_claims_kernel<<<1, kClaimInts, 0, stream>>>(claim_q, claim_kv);
+  static_assert(kClaimInts >= kZeroRowBytes / 4, "one thread per int of both");
+  zero_claims_kernel<<<1, kClaimInts, 0, stream>>>(claim_q, claim_kv, static_cast<int32_t*>(zero_row));
   return hipGetLastError();
 }
 

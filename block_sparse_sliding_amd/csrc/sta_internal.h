@@ -13,7 +13,7 @@ constexpr int kTileH = 8;
 constexpr int kTileW = 8;
 constexpr int kTileRows = kTileT * kTileH * kTileW;  // 384
 constexpr int kTextSlots = 256;
-// Key rows per packed block / per LDS stage of the attention kernel.
+// Rows per streamed block / per LDS stage of the attention kernels.
 constexpr int kKeyBlock = 64;
 // Query rows per attention workgroup: one whole tile.
 constexpr int kUnitRows = kTileRows;
@@ -29,7 +29,7 @@ struct Geom {
   int32_t n_video;     // T * H * W (raster video rows)
   int32_t S;           // n_video + (has_text ? 256 : 0): rows of the caller's tensors
   int32_t n_vt;        // n_tiles * 384: tile-major video rows, padding rows of partial tiles included
-  int32_t S_t;         // n_vt + (has_text ? 256 : 0): rows of the tile-major (packed) tensors
+  int32_t S_t;         // n_vt + (has_text ? 256 : 0): rows of tile-major tensors
   int32_t full;        // 1 when T, H, W are multiples of the tile (no padding rows)
   int32_t has_text;
   int32_t text_length;
@@ -449,16 +449,6 @@ hipError_t launch_rows_permute(const Geom& g, const void* src, void* dst, bool t
 // position d of the order hil_m + 3 curve.
 hipError_t launch_rows_hilbert(const Geom& g, const void* src, void* dst, bool to_hilbert,
                                hipStream_t stream);
-// V^T fragments: every 64-row tile-major block of v (rows at or after the
-// valid text length zeroed) as (2 key halves) x (D/16 column groups) 1 KB
-// fragments, the A operand of O^T += V^T P^T (layout documented at the pack
-// kernel).
-hipError_t launch_pack_v(const Geom& g, const void* v, void* vt, hipStream_t stream);
-// The same fragment packing for any [B][heads][S][D] bf16 raster tensor, into
-// [B][heads][S_t][D] tile-major fragments; tile-major rows at or after
-// valid_end, and padding rows of partial tiles, are written as zeros.
-hipError_t launch_pack_rows(const Geom& g, const void* src, void* dst, int valid_end,
-                            hipStream_t stream);
 hipError_t launch_schedule_lists(const Geom& g, const Windows& win, int32_t* offsets,
                                  int32_t* ids, hipStream_t stream);
 // Work order (one query unit per entry, grouped into 8 per-XCD queues: queue x
@@ -491,9 +481,7 @@ struct BwdArgs {
   const void* k;
   const void* v;
   const void* dout;
-  const void* kt;        // packed K^T fragments, text rows past the valid length zero
-  const void* qt;        // packed Q^T fragments
-  const void* dot;       // packed dout^T fragments
+  const void* zero_row;  // kZeroRowBytes of zeros (written by launch_bwd_prep)
   const float* lse2;     // tile-major lse * log2(e)
   const float* delta;    // tile-major -rowsum(dout * out), negated: it starts the dP accumulators
   void* dq;              // bf16 raster rows (the caller's dq, dk, dv)
@@ -508,7 +496,7 @@ struct BwdArgs {
 };
 hipError_t launch_bwd_prep(const Geom& g, const void* out, const void* dout, const float* lse,
                            float* lse2, float* delta, int32_t* claim_q, int32_t* claim_kv,
-                           hipStream_t stream);
+                           void* zero_row, hipStream_t stream);
 hipError_t launch_bwd_dq(const Geom& g, const Windows& win, const BwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_dkv(const Geom& g, const Windows& win, const BwdArgs& a, hipStream_t stream);
 

@@ -1,7 +1,7 @@
 // Layout kernels: tile-major gather / scatter of token rows (the public
-// sta_tile_gather / sta_tile_scatter), and the V^T fragment pack the fused
-// attention kernel streams. The attention kernel applies the same tile map
-// itself when it reads q and k and writes out / lse.
+// sta_tile_gather / sta_tile_scatter) and the Hilbert-order gather / scatter.
+// The attention kernels apply the tile map themselves when they read q, k and
+// v and write their outputs.
 //
 // Tile-major order (each (6,8,8) tile becomes 384 contiguous rows) follows the
 // tile definition of the STA README "Usage" section; it turns every dense
@@ -65,56 +65,6 @@ __global__ __launch_bounds__(kThreads) void rows_hilbert_kernel(Geom g, const ui
   }
 }
 
-// Pack v for the PV product of the attention kernel, tile-major. Block b (64
-// tile-major rows) becomes 2 x (D/16) fragments of 1 KB; in fragment
-// (h, dt) lane l (group gq = l/16, column i = l%16) holds, for e = 0..7,
-// V[64b + 32h + 16(e/4) + 4gq + e%4][16dt + i]. That is the A operand of a
-// 16x16x32 MFMA computing O^T += V^T P^T, with the keys in the order in which
-// an S^T = K Q^T accumulator leaves them in the lanes (lane l holds keys
-// 4(l/16) .. +3 of each 16-key group), so P^T is used where it is produced.
-// Rows at or after valid_end (for V: the valid text length) are written as
-// zeros, so padded text slots (whatever they hold) contribute exactly nothing.
-// The backward packs K, Q and dout the same way.
-template <int D>
-__global__ __launch_bounds__(kThreads) void pack_v_kernel(Geom g, const uint4* __restrict__ v,
-                                                          uint4* __restrict__ vt, int valid_end) {
-  constexpr int CPR = D / 8;     // 16-byte chunks per row
-  constexpr int DT = D / 16;     // column groups
-  constexpr int PITCH = D + 2;   // LDS row pitch in bf16 (odd word count: no bank aliasing)
-  __shared__ uint16_t rows[kKeyBlock * PITCH];
-  const size_t slab_in = size_t(blockIdx.y) * g.S * CPR;     // raster rows
-  const size_t slab_out = size_t(blockIdx.y) * g.S_t * CPR;  // tile-major rows
-  const int r0 = blockIdx.x * kKeyBlock;
-#pragma unroll
-  for (int c = threadIdx.x; c < kKeyBlock * CPR; c += kThreads) {
-    const int r = c / CPR, col = c % CPR;
-    uint4 x = make_uint4(0, 0, 0, 0);
-    const int rr = r0 + r < valid_end ? tiled_to_raster(r0 + r, g) : -1;
-    if (rr >= 0) x = v[slab_in + size_t(rr) * CPR + col];
-    uint32_t* dst = reinterpret_cast<uint32_t*>(&rows[r * PITCH]) + col * 4;
-    dst[0] = x.x;
-    dst[1] = x.y;
-    dst[2] = x.z;
-    dst[3] = x.w;
-  }
-  __syncthreads();
-  uint4* out = vt + slab_out + size_t(r0) * CPR;
-#pragma unroll
-  for (int o = threadIdx.x; o < kKeyBlock * CPR; o += kThreads) {
-    const int frag = o >> 6, l = o & 63;
-    const int h = frag / DT, dt = frag % DT;
-    const int col = 16 * dt + (l & 15);
-    const int key = 32 * h + 4 * (l >> 4);
-    uint32_t w[4];
-#pragma unroll
-    for (int e = 0; e < 8; e += 2) {
-      const int r = key + 16 * (e >> 2) + (e & 3);
-      w[e >> 1] = uint32_t(rows[r * PITCH + col]) | (uint32_t(rows[(r + 1) * PITCH + col]) << 16);
-    }
-    out[o] = make_uint4(w[0], w[1], w[2], w[3]);
-  }
-}
-
 }  // namespace
 
 hipError_t launch_rows_permute(const Geom& g, const void* src, void* dst, bool to_tiled,
@@ -135,20 +85,6 @@ hipError_t launch_rows_hilbert(const Geom& g, const void* src, void* dst, bool t
   else
     rows_hilbert_kernel<64><<<grid, kThreads, 0, stream>>>(g, (const uint4*)src, (uint4*)dst, to_hilbert);
   return hipGetLastError();
-}
-
-hipError_t launch_pack_rows(const Geom& g, const void* src, void* dst, int valid_end,
-                            hipStream_t stream) {
-  dim3 grid(g.S_t / kKeyBlock, g.B * g.heads);
-  if (g.D == 128)
-    pack_v_kernel<128><<<grid, kThreads, 0, stream>>>(g, (const uint4*)src, (uint4*)dst, valid_end);
-  else
-    pack_v_kernel<64><<<grid, kThreads, 0, stream>>>(g, (const uint4*)src, (uint4*)dst, valid_end);
-  return hipGetLastError();
-}
-
-hipError_t launch_pack_v(const Geom& g, const void* v, void* vt, hipStream_t stream) {
-  return launch_pack_rows(g, v, vt, g.n_vt + (g.has_text ? g.text_length : 0), stream);
 }
 
 }  // namespace sta

@@ -279,9 +279,9 @@ sta_status sta_build_schedule(const sta_dims* dims, const int32_t* window_sizes,
 
 /*
  * Bytes of device workspace sta_backward needs for these arguments, or 0 if
- * they are invalid: three packed copies of a [B][heads][S][D] bf16 tensor
- * and two fp32 values per row (video rows padded to whole tiles), the
- * forward's tile lists and 4 KB of queue heads.
+ * they are invalid: two fp32 values per row (video rows padded to whole
+ * tiles), the forward's tile lists, 4 KB of queue heads and one 256-byte
+ * zero row.
  * Pure host arithmetic: no HIP call.
  */
 size_t sta_backward_workspace_bytes(const sta_dims* dims, const int32_t* window_sizes,
@@ -313,10 +313,10 @@ size_t sta_backward_workspace_bytes(const sta_dims* dims, const int32_t* window_
  *             aligned; contents on entry ignored, on return unspecified.
  *             Calls that share a workspace must be ordered on one stream.
  * Errors as for sta_forward (all found on the host before any launch).
- * Returns STA_OK once the launches (row statistics, fragment packing of k,
- * q and dout, the tile lists, the dq pass, the dk/dv pass) are enqueued on
- * `stream`. The dq and dk/dv launches are persistent grids pulling units
- * from per-XCD queues, like the forward's attention launch.
+ * Returns STA_OK once the launches (row statistics, the tile lists, the dq
+ * pass, the dk/dv pass) are enqueued on `stream`. The dq and dk/dv launches
+ * are persistent grids pulling units from per-XCD queues, like the forward's
+ * attention launch.
  */
 sta_status sta_backward(const sta_dims* dims, const void* q, const void* k, const void* v,
                         const void* out, const float* lse, const void* dout,
@@ -327,10 +327,10 @@ sta_status sta_backward(const sta_dims* dims, const void* q, const void* k, cons
 /*
  * sta_backward with stage timing. `events` holds STA_BWD_TIMED_EVENTS
  * hipEvent_t handles (as void*): events[0] before the first launch, then
- * after 1 row statistics, 2 the three packings, 3 tile lists, 4 the dq pass,
- * 5 the dk/dv pass. STA_ERR_NULL if events or an entry is NULL.
+ * after 1 row statistics, 2 tile lists, 3 the dq pass, 4 the dk/dv pass.
+ * STA_ERR_NULL if events or an entry is NULL.
  */
-#define STA_BWD_TIMED_EVENTS 6
+#define STA_BWD_TIMED_EVENTS 5
 sta_status sta_backward_timed(const sta_dims* dims, const void* q, const void* k,
                               const void* v, const void* out, const float* lse,
                               const void* dout, const int32_t* window_sizes,

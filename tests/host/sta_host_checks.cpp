@@ -74,14 +74,6 @@ hipError_t launch_rows_hilbert(const Geom& g, const void* src, void* dst, bool, 
   record("rows_hilbert", g, {P(src), P(dst)});
   return hipSuccess;
 }
-hipError_t launch_pack_v(const Geom& g, const void* v, void* vt, hipStream_t) {
-  record("pack_v", g, {P(v), P(vt)});
-  return hipSuccess;
-}
-hipError_t launch_pack_rows(const Geom& g, const void* src, void* dst, int, hipStream_t) {
-  record("pack_rows", g, {P(src), P(dst)});
-  return hipSuccess;
-}
 hipError_t launch_schedule_lists(const Geom& g, const Windows&, int32_t* offsets, int32_t* ids,
                                  hipStream_t) {
   record("schedule_lists", g, {P(offsets), P(ids)});
@@ -99,18 +91,18 @@ hipError_t launch_attention(const Geom& g, const Windows&, const FwdArgs& a, hip
 }
 hipError_t launch_bwd_prep(const Geom& g, const void* out, const void* dout, const float* lse,
                            float* lse2, float* delta, int32_t* claim_q, int32_t* claim_kv,
-                           hipStream_t) {
-  record("bwd_prep", g, {P(out), P(dout), P(lse), P(lse2), P(delta), P(claim_q), P(claim_kv)});
+                           void* zero_row, hipStream_t) {
+  record("bwd_prep", g, {P(out), P(dout), P(lse), P(lse2), P(delta), P(claim_q), P(claim_kv), P(zero_row)});
   return hipSuccess;
 }
 hipError_t launch_bwd_dq(const Geom& g, const Windows&, const BwdArgs& a, hipStream_t) {
-  record("bwd_dq", g, {P(a.kt), P(a.qt), P(a.dot), P(a.lse2), P(a.delta), P(a.offsets), P(a.ids),
-                       P(a.claim_q), P(a.claim_kv)});
+  record("bwd_dq", g, {P(a.zero_row), P(a.lse2), P(a.delta), P(a.offsets), P(a.ids), P(a.claim_q),
+                       P(a.claim_kv)});
   return hipSuccess;
 }
 hipError_t launch_bwd_dkv(const Geom& g, const Windows&, const BwdArgs& a, hipStream_t) {
-  record("bwd_dkv", g, {P(a.kt), P(a.qt), P(a.dot), P(a.lse2), P(a.delta), P(a.offsets),
-                        P(a.ids), P(a.claim_q), P(a.claim_kv)});
+  record("bwd_dkv", g, {P(a.zero_row), P(a.lse2), P(a.delta), P(a.offsets), P(a.ids), P(a.claim_q),
+                        P(a.claim_kv)});
   return hipSuccess;
 }
 }  // namespace sta

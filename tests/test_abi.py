@@ -202,9 +202,9 @@ def test_backward_workspace_bytes(lib, B, heads, D, video, windows, text):
 
     def up(x):
         return (x + 255) // 256 * 256
-    tensor = B * heads * S_t * D * 2
     rows = B * heads * S_t * 4
     queue_heads = 8 * 64 * 4
-    expect = (3 * up(tensor) + 2 * up(rows) + up(n_off * 4) + up(n_ids * 4) + 2 * queue_heads)
+    zero_row = 256
+    expect = 2 * up(rows) + up(n_off * 4) + up(n_ids * 4) + 2 * queue_heads + zero_row
     assert sta.sta_backward_workspace_bytes(d, windows, text) == expect
     assert sta.sta_backward_workspace_bytes(sta.make_dims(B, heads, 96, video), windows, text) == 0
