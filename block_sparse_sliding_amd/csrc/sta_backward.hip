@@ -32,9 +32,11 @@
 // LDS layout of a streamed 64-row block: column pair P (columns 32P ..
 // 32P + 31) takes 4 KB, 64 bytes per row, row r at 64 r; the four 16-byte
 // chunks of a row are permuted, chunk c of row r sitting at position
-// c XOR sigma((r / 4) mod 4), sigma = (0, 2, 1, 3). A row fragment (lane l:
-// 16 bytes of row R + l%16, chunk l/16) and a transposed read (lane l: 8
-// bytes of row R + l/4) then both touch every bank once per LDS cycle. The
+// c XOR 3 (bit 2 of r). A row fragment (lane l: 16 bytes of row R + l%16,
+// chunk l/16) and a transposed read (lane l: 8 bytes of row R + l/4) then
+// touch every bank once per LDS cycle. (Measured on gfx950: a 16-byte read
+// serves the 16 lanes l with equal (l/16) XOR bit 2 XOR bit 3 of l in one
+// cycle, an 8-byte read lanes 0-31, then 32-63, over 64 4-byte banks.) The
 // LDS-DMA that fills a block applies the permutation through its per-lane
 // source addresses.
 //
@@ -79,7 +81,7 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 constexpr int kPair = kQueryBlock * 64;  // bytes of one column pair of a block
 
 // the chunk permutation of the block layout: sigma(k), k = (row / 4) mod 4
-__device__ inline int sigma(int k) { return ((k & 1) << 1) | ((k >> 1) & 1); }
+__device__ inline int sigma(int k) { return 3 * (k & 1); }
 // this lane's offset for row fragments: row l%16 of a 16-row group, chunk l/16
 __device__ inline int row_frag_offset(int l) { return (l & 15) * 64 + 16 * ((l >> 4) ^ sigma((l >> 2) & 3)); }
 // this lane's offset for transposed reads of column half e (columns 16e ..
