@@ -205,9 +205,10 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(Geom g, const __bf16* __r
 
 // ---------------------------------------------------------------- dq
 // Query units per (b, head): two per video tile (rows 0..255 with 8 waves x
-// 32 rows, rows 256..383 with 8 waves x 16 rows; with PAD, a unit of at most
-// 128 existing rows also runs 8 x 16), plus the 256 text query slots (8 waves
-// x 32 rows). Unit order: text units first, then the tiles.
+// 32 rows; rows 256..383, and with PAD any unit of at most 128 existing rows,
+// with two groups of 4 waves x 32 rows that take alternate key blocks), plus
+// the 256 text query slots (8 waves x 32 rows). Unit order: text units first,
+// then the tiles.
 __device__ inline int dq_units_per_head(const Geom& g) { return 2 * g.n_tiles + (g.has_text ? 1 : 0); }
 
 template <int D, bool PAD>
@@ -219,8 +220,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(KernelArgs) {
   constexpr int IPW = BLK / 1024 / kWaves;
   constexpr int BPT = kTileRows / kKeyBlock;
   static_assert(IPW >= 1 && BLK % (1024 * kWaves) == 0, "block must split over the waves");
-  // [stage][K | V], 64-row blocks in the column-pair layout
-  __shared__ __attribute__((aligned(1024))) char lds[2][2][BLK];
+  // [stage][K | V of block 2s | K | V of block 2s + 1], 64-row blocks in the
+  // column-pair layout (units that split their blocks over two wave groups
+  // use all four; the others the first two)
+  __shared__ __attribute__((aligned(1024))) char lds[2][4][BLK];
   __shared__ int claimed;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
@@ -397,15 +400,25 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(KernelArgs) {
       }
     };
 
-    auto run = [&](auto qt_c) {
+    // QT query column groups (16 rows each) per wave. SPLIT = 1: the 8 waves
+    // hold 8 QT 16 rows and every wave streams every key block. SPLIT = 2 (a
+    // unit of at most 128 rows): waves w and w + 4 hold the same 32 rows,
+    // group w / 4 takes the blocks j = 2 s + w / 4 of each step s, and the two
+    // partial sums of dq meet in LDS at the end (per wave, the LDS traffic of
+    // a 32-row wave instead of a 16-row one).
+    auto run = [&](auto qt_c, auto split_c) {
       constexpr int QT = decltype(qt_c)::value;
+      constexpr int SPLIT = decltype(split_c)::value;
+      static_assert(SPLIT == 1 || (SPLIT == 2 && QT * 16 * kWaves / 2 == 128), "wave groups");
       constexpr int RPW = QT * 16;
+      const int grp = SPLIT == 2 ? wave >> 2 : 0;    // wave group
+      const int wrow = SPLIT == 2 ? wave & 3 : wave;  // row slot
       const float qs = a.q_scale;
       bf16x8 qf[QT][KS], dof[QT][KS];
       float l2[QT], dl[QT];  // lse2 and -delta of this lane's query rows
 #pragma unroll
       for (int c = 0; c < QT; ++c) {
-        const int row = wave * RPW + c * 16 + (lane & 15);  // < q_rows for every unit shape
+        const int row = wrow * RPW + c * 16 + (lane & 15);  // < q_rows for every unit shape
         int rr, rt;
         query_rows(row, rr, rt);
         const bf16x8* qs8 = reinterpret_cast<const bf16x8*>(qr + size_t(rr) * D + (lane >> 4) * 8);
@@ -426,13 +439,25 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(KernelArgs) {
 
       const int rfo = row_frag_offset(lane);
       const int tro[2] = {tr_offset(lane, 0), tr_offset(lane, 1)};
-      auto issue = [&](int j, int st) {
-        int kbase, krs;
-        block_rows(j, kbase, krs);
-        const int lim = j < n_vid ? kKeyBlock : text_len - (j - n_vid) * kKeyBlock;
-        issue_rows(kr, lds[st][0], kbase, krs, lim);
-        issue_rows(vr, lds[st][1], kbase, krs, lim);
+      // the blocks of step s (SPLIT of them, in order) into stage st
+      const int n_steps = (n_blk + SPLIT - 1) / SPLIT;
+      auto issue = [&](int s, int st) {
+#pragma unroll
+        for (int b = 0; b < SPLIT; ++b) {
+          const int j = SPLIT * s + b;
+          if (j < n_blk) {
+            int kbase, krs;
+            block_rows(j, kbase, krs);
+            const int lim = j < n_vid ? kKeyBlock : text_len - (j - n_vid) * kKeyBlock;
+            issue_rows(kr, lds[st][2 * b], kbase, krs, lim);
+            issue_rows(vr, lds[st][2 * b + 1], kbase, krs, lim);
+          }
+        }
       };
+      // SPLIT = 2: group 1 hands its partial dq to group 0 through LDS (the
+      // stages are free once every wave has passed the first barrier)
+      f32x4* red = reinterpret_cast<f32x4*>(&lds[0][0][0]);
+      static_assert(SPLIT == 1 || 4 * QT * DT * 64 * 16 <= int(sizeof(lds)), "partial sums fit");
 
       // A x B^T-style score product over one raw block in LDS: out[c][kt] =
       // init[c] + sum over d of blk[16 kt + l%16][d] * frag[c][d]
@@ -458,33 +483,46 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(KernelArgs) {
       };
 
       if (!PAD || n_blk > 0) issue(0, 0);
+      wait_loads();  // the query rows above (and block 0) have landed
       // a wave whose rows all lie past a partial tile's tokens only loads
-      if (PAD && wave * RPW >= n_valid) {
+      // (with SPLIT = 2 so does its partner, which holds the same rows)
+      if (PAD && wrow * RPW >= n_valid) {
         // the same loads and barriers as the loop below; once every wave has
-        // passed barrier j, no wave reads the other stage any more
-        for (int j = 0; j < n_blk; ++j) {
+        // passed barrier s, no wave reads the other stage any more
+        for (int st = 0; st < n_steps; ++st) {
           asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
           __syncthreads();
-          if (j + 1 < n_blk) issue(j + 1, (j & 1) ^ 1);
+          if (st + 1 < n_steps) issue(st + 1, (st & 1) ^ 1);
+        }
+        if constexpr (SPLIT == 2) {
+          __syncthreads();
+          __syncthreads();
         }
         return;
       }
-      for (int j = 0; j < n_blk; ++j) {
-        const int stage = j & 1;
+      for (int step = 0; step < n_steps; ++step) {
+        const int stage = step & 1;
+        const int j = SPLIT * step + grp;  // this wave's block
+        const bool has = j < n_blk;
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
+        const char* kblk = lds[stage][2 * grp];
+        const char* vblk = lds[stage][2 * grp + 1];
         f32x4 s[QT][4], dp[QT][4];
-        f32x4 zero[QT], nd[QT];  // dP^T starts at -delta of its query (column)
+        if (has) {
+          f32x4 zero[QT], nd[QT];  // dP^T starts at -delta of its query (column)
 #pragma unroll
-        for (int c = 0; c < QT; ++c) {
-          float x = dl[c];
-          asm volatile("" : "+v"(x));  // built here, per block, not kept live across the loop
-          zero[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-          nd[c] = f32x4{x, x, x, x};
+          for (int c = 0; c < QT; ++c) {
+            float x = dl[c];
+            asm volatile("" : "+v"(x));  // built here, per block, not kept live across the loop
+            zero[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+            nd[c] = f32x4{x, x, x, x};
+          }
+          scores(kblk, qf, zero, s);
+          scores(vblk, dof, nd, dp);
         }
-        scores(lds[stage][0], qf, zero, s);
-        scores(lds[stage][1], dof, nd, dp);
-        if (j + 1 < n_blk) issue(j + 1, stage ^ 1);
+        if (step + 1 < n_steps) issue(step + 1, stage ^ 1);
+        if (!has) continue;
         // P = 2^(c' s - lse2), dS = P (dP - delta) with dP - delta from the MFMAs
 #pragma unroll
         for (int c = 0; c < QT; ++c)
@@ -524,18 +562,34 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(KernelArgs) {
           }
 #pragma unroll
           for (int d = 0; d < DT; ++d) {
-            const bf16x8 kf = tr_frag(lds[stage][0], h, d, tro[d & 1]);
+            const bf16x8 kf = tr_frag(kblk, h, d, tro[d & 1]);
 #pragma unroll
             for (int c = 0; c < QT; ++c)
               acc[c][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, db[c], acc[c][d], 0, 0, 0);
           }
         }
       }
+      if constexpr (SPLIT == 2) {
+        __syncthreads();  // every wave is past its last read of the stages
+        f32x4* mine = red + wrow * (QT * DT * 64) + lane;
+        if (grp == 1) {
+#pragma unroll
+          for (int c = 0; c < QT; ++c)
+#pragma unroll
+            for (int d = 0; d < DT; ++d) mine[(c * DT + d) * 64] = acc[c][d];
+        }
+        __syncthreads();
+        if (grp == 1) return;
+#pragma unroll
+        for (int c = 0; c < QT; ++c)
+#pragma unroll
+          for (int d = 0; d < DT; ++d) acc[c][d] += mine[(c * DT + d) * 64];
+      }
       // dq = c * acc, rows to raster positions
       __bf16* __restrict__ dqr = reinterpret_cast<__bf16*>(a.dq) + slab;
 #pragma unroll
       for (int c = 0; c < QT; ++c) {
-        const int row = wave * RPW + c * 16 + (lane & 15);
+        const int row = wrow * RPW + c * 16 + (lane & 15);
         if (PAD && row >= n_valid) continue;  // no such token
         int rr, rt;
         query_rows(row, rr, rt);
@@ -547,17 +601,20 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(KernelArgs) {
         }
       }
     };
-    if (q_rows == 256 && !(PAD && n_valid <= 128))  // PAD: a small partial tile runs 8 x 16 rows
-      run(std::integral_constant<int, 2>{});
+    // 256 rows: 8 waves x 32; at most 128 rows (part 1 of a tile, or a small
+    // partial tile): two groups of 4 waves x 32 rows over alternate blocks
+    if (q_rows == 256 && !(PAD && n_valid <= 128))
+      run(std::integral_constant<int, 2>{}, std::integral_constant<int, 1>{});
     else
-      run(std::integral_constant<int, 1>{});
+      run(std::integral_constant<int, 2>{}, std::integral_constant<int, 2>{});
   }
 }
 
 // ---------------------------------------------------------------- dk, dv
 // Key units per (b, head): per video tile keys 0..255 (8 waves x 32 keys) and
-// keys 256..383 (8 waves x 16 keys; with PAD, a unit of at most 128 existing
-// keys also runs 8 x 16), plus the 256 text slots (8 waves x 32).
+// keys 256..383 (two groups of 4 waves x 32 keys that take alternate query
+// blocks; with PAD, 8 waves x 16 keys, as any unit of at most 128 existing
+// keys), plus the 256 text slots (8 waves x 32).
 // Unit order: the text units first (each streams every query row), then
 // (bh, tile, part).
 __device__ inline int kv_units_per_head(const Geom& g) { return 2 * g.n_tiles + (g.has_text ? 1 : 0); }
@@ -571,9 +628,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(KernelArgs) {
   constexpr int IPW = BLK / 1024 / kWaves;
   constexpr int BPT = kTileRows / kQueryBlock;
   static_assert(IPW >= 1 && BLK % (1024 * kWaves) == 0, "block must split over the waves");
-  // [stage][Q | dout], 64-row blocks in the column-pair layout, then lse2 and delta
-  __shared__ __attribute__((aligned(1024))) char lds[2][2][BLK];
-  __shared__ __attribute__((aligned(16))) float rowv[2][2][kQueryBlock];
+  // [stage][Q | dout of block 2s | Q | dout of block 2s + 1], 64-row blocks in
+  // the column-pair layout (as in the dq kernel), then lse2 and delta
+  __shared__ __attribute__((aligned(1024))) char lds[2][4][BLK];
+  __shared__ __attribute__((aligned(16))) float rowv[2][2][2][kQueryBlock];  // [stage][block][lse2 | delta]
   __shared__ int claimed;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
@@ -730,28 +788,45 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(KernelArgs) {
         dma16(src + urow * ROWB + o, dst + q * 1024);
       }
     };
-    auto issue = [&](int j, int st) {
+    // query block j into slot b of stage st (Q, dout, and its lse2 and delta
+    // rows, fetched by waves 2b and 2b + 1)
+    auto issue_block = [&](int j, int st, int b) {
       int qbase, qrs, vrow;
       block_rows(j, qbase, qrs, vrow);
-      issue_rows(qr, lds[st][0], qbase, qrs);
-      issue_rows(dor, lds[st][1], qbase, qrs);
+      issue_rows(qr, lds[st][2 * b], qbase, qrs);
+      issue_rows(dor, lds[st][2 * b + 1], qbase, qrs);
       unsigned o4 = unsigned(lane) * 4u;
       asm volatile("" : "+v"(o4));
-      if (wave == 0) dma4(lse2 + size_t(vrow) * 4 + o4, reinterpret_cast<char*>(rowv[st][0]));
-      if (wave == 1) dma4(dlt + size_t(vrow) * 4 + o4, reinterpret_cast<char*>(rowv[st][1]));
+      if (wave == 2 * b) dma4(lse2 + size_t(vrow) * 4 + o4, reinterpret_cast<char*>(rowv[st][b][0]));
+      if (wave == 2 * b + 1) dma4(dlt + size_t(vrow) * 4 + o4, reinterpret_cast<char*>(rowv[st][b][1]));
     };
 
     const float qs = a.q_scale;
-    const int rfo = row_frag_offset(lane);
-    const int tro[2] = {tr_offset(lane, 0), tr_offset(lane, 1)};
 
-    auto run = [&](auto kt_c) {
-      constexpr int KT = decltype(kt_c)::value;  // 16-key groups per wave
+    // KT key groups (16 keys each) per wave. SPLIT = 1: the 8 waves hold
+    // 8 KT 16 keys and every wave streams every query block. SPLIT = 2 (a unit
+    // of at most 128 keys): waves w and w + 4 hold the same 32 keys, group w / 4
+    // takes the blocks j = 2 s + w / 4 of each step s, and the two partial sums
+    // of dk and dv meet in LDS at the end (as in the dq kernel).
+    auto run = [&](auto kt_c, auto split_c) {
+      constexpr int KT = decltype(kt_c)::value;
+      constexpr int SPLIT = decltype(split_c)::value;
+      static_assert(SPLIT == 1 || (SPLIT == 2 && KT * 16 * kWaves / 2 == 128), "wave groups");
+      const int grp = SPLIT == 2 ? wave >> 2 : 0;     // wave group
+      const int wslot = SPLIT == 2 ? wave & 3 : wave;  // key slot
+      const int n_steps = (n_blk + SPLIT - 1) / SPLIT;
+      auto issue = [&](int s, int st) {
+#pragma unroll
+        for (int b = 0; b < SPLIT; ++b)
+          if (SPLIT * s + b < n_blk) issue_block(SPLIT * s + b, st, b);
+      };
+      f32x4* red = reinterpret_cast<f32x4*>(&lds[0][0][0]);
+      static_assert(SPLIT == 1 || 4 * 2 * KT * DT * 64 * 16 <= int(sizeof(lds)), "partial sums fit");
       // lane ln's key of group kg: the raster row its gradients go to (PAD:
       // -1 for a key past the unit's tokens) and, in ksrc, the row its K and V
       // are read from
       auto key_rows = [&](int ln, int kg, int& ksrc) {
-        const int local = wave * 16 * KT + 16 * kg + (ln & 15);
+        const int local = wslot * 16 * KT + 16 * kg + (ln & 15);
         int kras = PAD ? tiled_to_raster(key_row0 + local, g) : tiled_to_raster_full(key_row0 + local, g);
         ksrc = kras;
         if constexpr (PAD) {
@@ -769,7 +844,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(KernelArgs) {
       bf16x8 kf[KT][KS], vf[KT][KS];
 #pragma unroll
       for (int kg = 0; kg < KT; ++kg) {
-        key_ok[kg] = !text_unit || key_row0 + wave * 16 * KT + 16 * kg + (lane & 15) < g.n_vt + text_len;
+        key_ok[kg] = !text_unit || key_row0 + wslot * 16 * KT + 16 * kg + (lane & 15) < g.n_vt + text_len;
         int ksrc;
         key_rows(lane, kg, ksrc);
         const bf16x8* k8 = reinterpret_cast<const bf16x8*>(reinterpret_cast<const __bf16*>(a.k) + slab +
@@ -796,6 +871,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(KernelArgs) {
                         f32x4 (&out)[KT][2]) {
         constexpr int NF = 2 * KS;
         bf16x8 af[NF];
+        // lane offsets are rebuilt per call from an opaque lane id: kept live
+        // across the loop they would push its registers past the budget
+        const int rfo = row_frag_offset(opaque_lane<true>(this_lane));
         auto aload = [&](int f) {
           af[f] = *reinterpret_cast<const bf16x8*>(blk + (f >> 1) * kPair + (2 * hq + (f & 1)) * 16 * 64 + rfo);
         };
@@ -814,23 +892,36 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(KernelArgs) {
       };
 
       if (n_blk > 0) issue(0, 0);
+      wait_loads();  // the key rows above (and block 0) have landed
       // a wave whose keys all lie past a partial tile's tokens only loads
-      if (PAD && !text_unit && wave * 16 * KT >= n_keys) {
+      // (with SPLIT = 2 so does its partner, which holds the same keys)
+      if (PAD && !text_unit && wslot * 16 * KT >= n_keys) {
         // the same loads and barriers as the loop below; once every wave has
-        // passed barrier j, no wave reads the other stage any more
-        for (int j = 0; j < n_blk; ++j) {
+        // passed barrier s, no wave reads the other stage any more
+        for (int st = 0; st < n_steps; ++st) {
           asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
           __syncthreads();
-          if (j + 1 < n_blk) issue(j + 1, (j & 1) ^ 1);
+          if (st + 1 < n_steps) issue(st + 1, (st & 1) ^ 1);
+        }
+        if constexpr (SPLIT == 2) {
+          __syncthreads();
+          __syncthreads();
         }
         return;
       }
-      for (int j = 0; j < n_blk; ++j) {
-        const int stage = j & 1;
+      for (int step = 0; step < n_steps; ++step) {
+        const int stage = step & 1;
+        const int j = SPLIT * step + grp;  // this wave's block
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        const f32x4* l2v = reinterpret_cast<const f32x4*>(rowv[stage][0]);
-        const f32x4* dlv = reinterpret_cast<const f32x4*>(rowv[stage][1]);
+        if (j >= n_blk) {  // SPLIT = 2, odd block count: the last step has one block
+          if (step + 1 < n_steps) issue(step + 1, stage ^ 1);
+          continue;
+        }
+        const char* qblk = lds[stage][2 * grp];
+        const char* dblk = lds[stage][2 * grp + 1];
+        const f32x4* l2v = reinterpret_cast<const f32x4*>(rowv[stage][grp][0]);
+        const f32x4* dlv = reinterpret_cast<const f32x4*>(rowv[stage][grp][1]);
 #pragma unroll
         for (int hq = 0; hq < 2; ++hq) {
           f32x4 s[KT][2], dp[KT][2];
@@ -838,9 +929,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(KernelArgs) {
           // starts at -delta of those rows
           const f32x4 zero[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
           const f32x4 nd[2] = {dlv[(2 * hq) * 4 + (lane >> 4)], dlv[(2 * hq + 1) * 4 + (lane >> 4)]};
-          scores(lds[stage][0], hq, kf, zero, s);
-          scores(lds[stage][1], hq, vf, nd, dp);
-          if (hq == 0 && j + 1 < n_blk) issue(j + 1, stage ^ 1);
+          scores(qblk, hq, kf, zero, s);
+          scores(dblk, hq, vf, nd, dp);
+          if (hq == 0 && step + 1 < n_steps) issue(step + 1, stage ^ 1);
 #pragma unroll
           for (int i = 0; i < 2; ++i) {
             const f32x4 l2 = l2v[(2 * hq + i) * 4 + (lane >> 4)];
@@ -881,10 +972,12 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(KernelArgs) {
           }
           // dv^T += dout^T P, dk^T += Q^T dS over this half's 32 queries, with
           // dout^T and Q^T read transposed from the rows
+          const int tl = opaque_lane<true>(this_lane);
+          const int tro[2] = {tr_offset(tl, 0), tr_offset(tl, 1)};
 #pragma unroll
           for (int d = 0; d < DT; ++d) {
-            const bf16x8 fo = tr_frag(lds[stage][1], hq, d, tro[d & 1]);
-            const bf16x8 fq = tr_frag(lds[stage][0], hq, d, tro[d & 1]);
+            const bf16x8 fo = tr_frag(dblk, hq, d, tro[d & 1]);
+            const bf16x8 fq = tr_frag(qblk, hq, d, tro[d & 1]);
 #pragma unroll
             for (int kg = 0; kg < KT; ++kg) {
               dv[kg][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fo, pb[kg], dv[kg][d], 0, 0, 0);
@@ -892,6 +985,28 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(KernelArgs) {
             }
           }
         }
+      }
+      if constexpr (SPLIT == 2) {
+        __syncthreads();  // every wave is past its last read of the stages
+        f32x4* mine = red + wslot * (2 * KT * DT * 64) + lane;
+        if (grp == 1) {
+#pragma unroll
+          for (int kg = 0; kg < KT; ++kg)
+#pragma unroll
+            for (int d = 0; d < DT; ++d) {
+              mine[(kg * DT + d) * 64] = dk[kg][d];
+              mine[((KT + kg) * DT + d) * 64] = dv[kg][d];
+            }
+        }
+        __syncthreads();
+        if (grp == 1) return;
+#pragma unroll
+        for (int kg = 0; kg < KT; ++kg)
+#pragma unroll
+          for (int d = 0; d < DT; ++d) {
+            dk[kg][d] += mine[(kg * DT + d) * 64];
+            dv[kg][d] += mine[((KT + kg) * DT + d) * 64];
+          }
       }
       // dk = c * acc, dv = acc; C row = d (4 (l/16) + r of each 16-group), column = key
       // (the key rows recomputed here rather than kept live across the loop)
@@ -910,10 +1025,17 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(KernelArgs) {
         }
       }
     };
-    if (unit_keys == 256 && !(PAD && !text_unit && n_keys <= 128))  // PAD: a small partial tile runs 8 x 16 keys
-      run(std::integral_constant<int, 2>{});
+    // 256 keys: 8 waves x 32; at most 128 keys (part 1 of a tile, or a small
+    // partial tile): two groups of 4 waves x 32 keys over alternate blocks.
+    // With PAD (whose block walk keeps more state live) the small units run
+    // 8 waves x 16 keys over every block instead, which keeps the loop free
+    // of spills.
+    if (unit_keys == 256 && !(PAD && !text_unit && n_keys <= 128))
+      run(std::integral_constant<int, 2>{}, std::integral_constant<int, 1>{});
+    else if constexpr (PAD)
+      run(std::integral_constant<int, 1>{}, std::integral_constant<int, 1>{});
     else
-      run(std::integral_constant<int, 1>{});
+      run(std::integral_constant<int, 2>{}, std::integral_constant<int, 2>{});
   }
 }
 

@@ -36,6 +36,13 @@ __device__ inline float swap32_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// A wait for all vector-memory loads that the compiler sees (the inline-asm
+// waits of the kernels are opaque to it). After it the compiler knows that
+// every load it issued has returned, so it puts no waits of its own for those
+// loads inside the block loops that follow: such a wait would also count the
+// LDS-DMA in flight, which the compiler cannot see, and stall on it.
+__device__ inline void wait_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0) only
+
 // LDS-DMA: each lane moves 16 (dma16) or 4 (dma4) bytes from its own global
 // address into `lds + lane * 16` (or `lane * 4`); the LDS base is
 // wave-uniform. The instructions are written as inline asm on purpose: an
