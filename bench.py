@@ -185,6 +185,10 @@ def cpu_baseline(wl, q, k, v, budget_s: float, flops: float):
     }
 
 
+def data_label(args) -> str:
+    return "zeros (power study, not a throughput figure)" if args.zero_inputs else "synthetic"
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -197,6 +201,10 @@ def main():
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after timing, run a plain device copy of this many MiB (3 times) so "
                          "that hardware byte counters can be scaled against known traffic")
+    ap.add_argument("--zero-inputs", action="store_true",
+                    help="power study: q, k, v (and dout) all zero. The kernels do the same "
+                         "work on inputs that toggle no multiplier bits; the line's data field "
+                         "says so and it is not a throughput figure")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "the STA benchmark runs on one GPU only; --gpus must be 1",
@@ -213,6 +221,10 @@ def main():
     wl = sta_inputs.WORKLOADS[args.workload]
     windows = list(wl.windows)
     q, k, v = sta_inputs.make_qkv(wl, "cuda")
+    if args.zero_inputs:
+        for t in (q, k, v):
+            t.zero_()
+        args.cpu_budget = 0.0
     dims = sta.make_dims(wl.batch, wl.heads, wl.head_dim, wl.video)
     out = torch.empty_like(q)
     lse = torch.empty(wl.batch, wl.heads, wl.seq_len, dtype=torch.float32, device="cuda")
@@ -273,7 +285,7 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic",
+        "data": data_label(args),
         "config": wl.describe(),
         "ms_per_call": ms_per_step,
         "pct_bf16_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
@@ -328,12 +340,17 @@ def bench_hilbert(args, wl, q, k, v, dims, out, lse):
         "metric": "Hilbert-window attention fwd ms/call + effective TFLOP/s (% bf16 MFMA peak)",
         "value": tflops, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16", "data": "synthetic", "config": wl.describe(), "ms_per_call": ms,
+        "dtype": "bf16", "data": data_label(args), "config": wl.describe(), "ms_per_call": ms,
         "pct_bf16_peak": 100.0 * tflops / PEAK_BF16_TFLOPS, "effective_flop_per_call": flops,
         "roofline": {"kernel": "sta_attention_kernel<%d, true, true> (whole call)" % wl.head_dim,
                      "bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": tflops / PEAK_BF16_TFLOPS, "traffic": None, "launch_ms": ms},
+                     "frac": tflops / PEAK_BF16_TFLOPS,
+                     "traffic": measured_traffic("hilbert_pmc.txt", "sta_attention_kernel<%d, true, true>"
+                                                 % wl.head_dim, "sta_attention.hip"),
+                     "launch_ms": ms},
     }
+    if args.copy_calibration_mib > 0:
+        result["copy_calibration_bytes"] = copy_calibration(args.copy_calibration_mib)
     if args.cpu_budget > 0:
         mode = "slide" if wl.hilbert_mode == 1 else "window"
         rows = np.arange(0, wl.seq_len, max(1, wl.seq_len // 256))
@@ -378,6 +395,8 @@ def bench_backward(args, wl, windows, q, k, v, dims, out, lse, fwd_ws):
     del fwd_ws
     g = torch.Generator(device="cuda").manual_seed(10 * wl.seed_base + 3)
     dout = torch.randn(q.shape, generator=g, device="cuda").to(torch.bfloat16)
+    if args.zero_inputs:
+        dout.zero_()
     dq, dk, dv = (torch.empty_like(q) for _ in range(3))
     ws = torch.empty(sta.sta_backward_workspace_bytes(dims, windows, wl.has_text),
                      dtype=torch.uint8, device="cuda")
@@ -438,7 +457,7 @@ def bench_backward(args, wl, windows, q, k, v, dims, out, lse, fwd_ws):
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic",
+        "data": data_label(args),
         "config": wl.describe(),
         "pct_bf16_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
         "effective_flop_per_call": flops,
