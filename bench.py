@@ -92,10 +92,15 @@ def hilbert_flops(wl) -> float:
 
 
 def kernel_suffix(wl) -> str:
-    """Template arguments of the kernels a workload runs: <D, PAD>, PAD when a
-    video size is not a tile multiple."""
+    """Template arguments of the backward kernels a workload runs: <D, PAD>, PAD
+    when a video size is not a tile multiple."""
     pad = any(size % tile for size, tile in zip(wl.video, TILE))
     return f"<{wl.head_dim}, {'true' if pad else 'false'}>"
+
+
+def attention_kernel(wl) -> str:
+    """Name of the forward attention kernel a workload runs: <D, PAD, HIL>."""
+    return f"sta_attention_kernel{kernel_suffix(wl)[:-1]}, {'true' if wl.hilbert_len else 'false'}>"
 
 
 def measured_traffic(summary: str, kernel: str, source: str):
@@ -271,7 +276,7 @@ def main():
     tflops = flops / (ms_per_step * 1e-3) / 1e12
     attn_ms = stage_ms["attention"]
     attn_tflops = flops / (attn_ms * 1e-3) / 1e12
-    attn_kernel = "sta_attention_kernel" + kernel_suffix(wl)
+    attn_kernel = attention_kernel(wl)
     traffic = measured_traffic(f"attention_{args.workload}_pmc.txt", attn_kernel, "sta_attention.hip")
     result = {
         "metric": METRIC,
@@ -342,11 +347,10 @@ def bench_hilbert(args, wl, q, k, v, dims, out, lse):
         "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": data_label(args), "config": wl.describe(), "ms_per_call": ms,
         "pct_bf16_peak": 100.0 * tflops / PEAK_BF16_TFLOPS, "effective_flop_per_call": flops,
-        "roofline": {"kernel": "sta_attention_kernel<%d, true, true> (whole call)" % wl.head_dim,
+        "roofline": {"kernel": attention_kernel(wl) + " (whole call)",
                      "bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": tflops / PEAK_BF16_TFLOPS,
-                     "traffic": measured_traffic("hilbert_pmc.txt", "sta_attention_kernel<%d, true, true>"
-                                                 % wl.head_dim, "sta_attention.hip"),
+                     "traffic": measured_traffic("hilbert_pmc.txt", attention_kernel(wl), "sta_attention.hip"),
                      "launch_ms": ms},
     }
     if args.copy_calibration_mib > 0:
