@@ -388,6 +388,7 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(KernelArgs) 
         keys.reset();
         KeyBlock s_cur = keys.block(g, 0);
         issue(s_cur, 0);
+        wait_loads();  // the Q rows (and block 0) have landed: no compiler waits inside the loop
         for (int j = 0; j < n_blk; ++j) {
           const int stage = j & 1;
           asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -488,6 +489,7 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(KernelArgs) 
 #pragma unroll
         for (int c = 0; c < QT; ++c) mx[c] = -INFINITY;
         keys.reset();
+        wait_loads();
         for (int j = 0; j < n_blk; ++j) {
           const KeyBlock s_j = keys.block(g, j);
           issue(s_j, 0);

@@ -1,4 +1,4 @@
-"""Static checks of the forward attention kernels' gfx950 assembly.
+"""Static checks of the attention kernels' gfx950 assembly.
 
 The P V products of the forward kernel are inline-asm MFMAs on AGPR
 accumulators. The compiler's hazard recognizer does not look inside inline
@@ -15,6 +15,14 @@ from every inline-asm MFMA, forward for the first rule and backward for the
 second. It also reports the scratch (spill) size of each kernel from the
 assembler metadata: spill code around the inline asm would move accumulators
 behind the kernel's back.
+
+A third check looks at the innermost loops that hold the kernels' MFMAs (the
+per-block loops). The kernels fill LDS with LDS-DMA written as inline asm,
+which the compiler does not count, so any vector-memory wait the compiler puts
+inside such a loop (for a spill reload, or for a load issued before the loop)
+also waits for the DMA of the next block in flight. Those loops must hold no
+scratch access and no compiler-placed vmcnt wait; the kernels' own waits are
+inline asm.
 """
 
 from __future__ import annotations
@@ -200,4 +208,37 @@ def check_operand_writes(k: Kernel) -> list[str]:
                                     f"asm MFMA #{i} after {w} wait states")
                     continue
             stack.extend((p, w + prev.waits) for p in preds[j])
+    return problems
+
+
+def innermost_loops(k: Kernel) -> list[tuple[int, int]]:
+    """(first, last) instruction index of each innermost loop: a header and its
+    furthest back edge, holding no other loop."""
+    last_of: dict[int, int] = {}
+    for i, ins in enumerate(k.instrs):
+        tgt = _branch_target(ins)
+        if tgt is not None and k.labels[tgt] <= i:
+            h = k.labels[tgt]
+            last_of[h] = max(last_of.get(h, i), i)
+    regions = sorted(last_of.items())
+    out = []
+    for h, e in regions:
+        if not any((h2, e2) != (h, e) and h <= h2 and e2 <= e for h2, e2 in regions):
+            out.append((h, e))
+    return out
+
+
+def check_block_loops(k: Kernel, min_mfma: int = 32) -> list[str]:
+    """Scratch accesses and compiler-placed vmcnt waits inside the innermost
+    loops with at least `min_mfma` MFMAs."""
+    problems = []
+    for h, e in innermost_loops(k):
+        body = k.instrs[h:e + 1]
+        if sum(ins.op.startswith("v_mfma") for ins in body) < min_mfma:
+            continue
+        for j, ins in enumerate(body):
+            if ins.op.startswith("scratch_"):
+                problems.append(f"{k.name}: {ins.op} {ins.operands} at #{h + j} inside the block loop #{h}-#{e}")
+            if ins.op == "s_waitcnt" and "vmcnt" in ins.operands and not ins.asm:
+                problems.append(f"{k.name}: compiler wait {ins.operands} at #{h + j} inside the block loop #{h}-#{e}")
     return problems

@@ -1,4 +1,5 @@
-"""Inline-asm MFMAs in the forward kernels, checked in the compiled assembly.
+"""Inline-asm MFMAs and the per-block loops of the attention kernels, checked
+in the compiled assembly.
 
 An MFMA written as inline asm has accumulators the compiler cannot see as
 MFMA results: the wait states around it, and the absence of spill code that
@@ -70,19 +71,41 @@ def test_checker_flags_operand_written_just_before():
     assert H.check_operand_writes(unrelated) == []
 
 
-@pytest.fixture(scope="module")
-def attention_asm(tmp_path_factory):
+def _compile_asm(tmp_path_factory, src):
     hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
     if not os.path.exists(hipcc):
         pytest.skip("hipcc not available")
     from block_sparse_sliding_amd import build as B
 
-    out = tmp_path_factory.mktemp("asm") / "sta_attention.s"
-    cmd = [hipcc, *B.HIPCC_FLAGS, *B.EXTRA_FLAGS.get("sta_attention.hip", []), "--cuda-device-only", "-S",
-           os.path.join(B.CSRC, "sta_attention.hip"), "-o", str(out)]
+    out = tmp_path_factory.mktemp("asm") / src.replace(".hip", ".s")
+    cmd = [hipcc, *B.HIPCC_FLAGS, *B.EXTRA_FLAGS.get(src, []), "--cuda-device-only", "-S",
+           os.path.join(B.CSRC, src), "-o", str(out)]
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     assert r.returncode == 0, r.stdout[-4000:]
     return out.read_text()
+
+
+@pytest.fixture(scope="module")
+def attention_asm(tmp_path_factory):
+    return _compile_asm(tmp_path_factory, "sta_attention.hip")
+
+
+@pytest.fixture(scope="module")
+def backward_asm(tmp_path_factory):
+    return _compile_asm(tmp_path_factory, "sta_backward.hip")
+
+
+def test_loop_checker_flags_waits_and_spills():
+    loop = ("\ts_mov_b32 s0, 0\n.LBB0_1:\n" + ASM_MFMA * 40 + "{}\ts_cbranch_scc1 .LBB0_1\n\ts_endpgm\n")
+    assert H.check_block_loops(_kernel(loop.format(""))) == []
+    asm_wait = "\t;;#ASMSTART\n\ts_waitcnt vmcnt(0)\n\t;;#ASMEND\n"
+    assert H.check_block_loops(_kernel(loop.format(asm_wait))) == []
+    assert len(H.check_block_loops(_kernel(loop.format("\ts_waitcnt vmcnt(3)\n")))) == 1
+    assert len(H.check_block_loops(_kernel(loop.format("\tscratch_load_dword v0, off, off\n")))) == 1
+    # a loop with few MFMAs (not a block loop) and an outer loop around the block loop are not checked
+    assert H.check_block_loops(_kernel(loop.format("\ts_waitcnt vmcnt(3)\n")), min_mfma=64) == []
+    outer = ".LBB0_0:\n\ts_waitcnt vmcnt(1)\n" + loop.format("").replace("\ts_endpgm\n", "\ts_cbranch_scc0 .LBB0_0\n\ts_endpgm\n")
+    assert H.check_block_loops(_kernel(outer)) == []
 
 
 def test_forward_kernels_no_asm_hazards(attention_asm):
@@ -99,3 +122,16 @@ def test_forward_kernels_no_asm_hazards(attention_asm):
         if "ELb0ELb0E" in k.name:  # PAD = false, HIL = false
             assert k.scratch == 0, f"{k.name}: {k.scratch} bytes of scratch per lane"
             assert k.vgpr_spills == 0, f"{k.name}: {k.vgpr_spills} VGPR spills"
+
+
+def test_block_loops_wait_only_on_their_own_loads(attention_asm, backward_asm):
+    """No spill reload and no compiler-placed vector-memory wait inside any
+    per-block loop of the forward, Hilbert, dq and dk/dv kernels: such a wait
+    would also count the next block's LDS-DMA in flight."""
+    kernels = H.parse(attention_asm) + H.parse(backward_asm, name_filter="bwd_d")
+    names = sorted(k.name for k in kernels)
+    assert len(kernels) == 6 + 4 + 4, names
+    for k in kernels:
+        assert H.innermost_loops(k), k.name
+        problems = H.check_block_loops(k)
+        assert problems == [], "\n".join(problems[:10])
