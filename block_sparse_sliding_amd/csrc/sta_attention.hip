@@ -110,33 +110,6 @@ __device__ inline const KernelArgs* kernel_args() {
   return (const KernelArgs*)kp;
 }
 
-// LDS-DMA of 16 bytes per lane from base + soff (wave-uniform) + voff (per
-// lane) into lds_dst + 16 lane, through a buffer resource over base (the
-// uniform part stays in scalar registers). Written as inline asm for the
-// reason given at dma16: the kernel orders these writes itself. M0 holds the
-// LDS destination: saved and restored around the load, one wait state between
-// its write and the load. (Device pass only.)
-__device__ inline void dma16_buf(const char* base, int voff, int soff, char* lds_dst) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  typedef int i32x4 __attribute__((ext_vector_type(4)));
-  const unsigned long long b = reinterpret_cast<unsigned long long>(base);
-  const i32x4 rsrc = {int(unsigned(b)), int(unsigned(b >> 32) & 0xffffu), 0x7fffffff, 0x00020000};
-  const unsigned m0 = unsigned(reinterpret_cast<unsigned long long>((lds_void*)lds_dst));
-  unsigned saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %3\n\t"
-      "s_nop 0\n\t"
-      "buffer_load_dwordx4 %1, %2, %4 offen lds\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(voff), "s"(rsrc), "s"(m0), "s"(soff)
-      : "memory");
-#else
-  (void)base, (void)voff, (void)soff, (void)lds_dst;
-#endif
-}
-
 // HIL: Hilbert-window attention on a 2D image (Geom::hilbert): video query unit u
 // is the hil_group tiles at Hilbert curve positions hil_group * u .. + hil_group
 // - 1 (their rows in that order, 64 per tile), its key tiles come from
@@ -261,10 +234,10 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(KernelArgs) 
           const int q = wave * IPW + i, r0 = q * RPI;
           const int chunk = kchunk_hi + ((ln & 3) ^ sw(r0 + rin));
           const int krow0 = s.base + (r0 >> 3) * g.W + (r0 & 7);
-          dma16_buf(kr, rin * ROWB + chunk * 16, krow0 * ROWB, &lds[st][0][q * 1024]);
+          dma16_buf(kr, unsigned(rin * ROWB + chunk * 16), unsigned(krow0) * ROWB, &lds[st][0][q * 1024]);
           const int vrow0 = s.base + 2 * (q & 3) * g.W;
           const int voff = ((vr_lane >> 3) * g.W + (vr_lane & 7)) * ROWB + vb_lane;
-          dma16_buf(vr, voff, vrow0 * ROWB + 64 * (q >> 2), &lds[st][1][q * 1024]);
+          dma16_buf(vr, unsigned(voff), unsigned(vrow0) * ROWB + 64 * (q >> 2), &lds[st][1][q * 1024]);
         }
       } else if (!PAD || s.kind == 1) {
         // consecutive raster rows s.base + r, valid while r < s.lim

@@ -72,6 +72,34 @@ __device__ inline void dma16(const char* gsrc, char* lds_dst) {
   STA_GLOBAL_LOAD_LDS("global_load_lds_dwordx4", gsrc, lds_dst);
 }
 
+// LDS-DMA of 16 bytes per lane from base + soff (wave-uniform) + voff (per
+// lane) into lds_dst + 16 lane, through a buffer resource over base (the
+// uniform part stays in scalar registers). Written as inline asm for the
+// reason given at dma16: the kernel orders these writes itself. M0 holds the
+// LDS destination: saved and restored around the load, one wait state between
+// its write and the load. The offsets are unsigned byte offsets (the caller's
+// tensors are limited to 2^32 bytes per (batch, head) slab). (Device pass only.)
+__device__ inline void dma16_buf(const char* base, unsigned voff, unsigned soff, char* lds_dst) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  typedef int i32x4 __attribute__((ext_vector_type(4)));
+  const unsigned long long b = reinterpret_cast<unsigned long long>(base);
+  const i32x4 rsrc = {int(unsigned(b)), int(unsigned(b >> 32) & 0xffffu), 0x7fffffff, 0x00020000};
+  const unsigned m0 = unsigned(reinterpret_cast<unsigned long long>((lds_void*)lds_dst));
+  unsigned saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, %4 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(rsrc), "s"(m0), "s"(soff)
+      : "memory");
+#else
+  (void)base, (void)voff, (void)soff, (void)lds_dst;
+#endif
+}
+
 // Next query unit for a workgroup on XCD `xcd`, or -1 once every queue is
 // empty. Queue y holds work[8k + y], k < ceil((total - y) / 8); its head
 // claim[y * kClaimStride] counts the items taken (it may run past the end).
