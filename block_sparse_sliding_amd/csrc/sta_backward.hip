@@ -390,10 +390,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(KernelArgs) {
           return;
         }
       }
-      if (lim >= kKeyBlock) {
+      if (!PAD && lim >= kKeyBlock) {
         // every row a source row: a buffer resource over src, the group's first
         // row in the wave-uniform offset, the lane's row of the group (2 runs of
-        // 8) and its chunk in the per-lane offset
+        // 8) and its chunk in the per-lane offset (the partial-tile build keeps
+        // the per-lane addresses below: measured faster there)
 #pragma unroll
         for (int i = 0; i < IPW; ++i) {
           const int q = wave * IPW + i;
@@ -792,14 +793,25 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(KernelArgs) {
           return;
         }
       }
-      // a buffer resource over src, as in the dq kernel
+      if constexpr (!PAD) {  // a buffer resource over src, as in the dq kernel
 #pragma unroll
-      for (int i = 0; i < IPW; ++i) {
-        const int q = wave * IPW + i;
-        const unsigned soff = unsigned(qbase + 2 * (q & 3) * qrs) * ROWB;
-        const unsigned voff =
-            unsigned((lane >> 5) * qrs + ((lane >> 2) & 7)) * ROWB + unsigned(dma_col_offset(q, lane));
-        dma16_buf(src, voff, soff, dst + q * 1024);
+        for (int i = 0; i < IPW; ++i) {
+          const int q = wave * IPW + i;
+          const unsigned soff = unsigned(qbase + 2 * (q & 3) * qrs) * ROWB;
+          const unsigned voff =
+              unsigned((lane >> 5) * qrs + ((lane >> 2) & 7)) * ROWB + unsigned(dma_col_offset(q, lane));
+          dma16_buf(src, voff, soff, dst + q * 1024);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < IPW; ++i) {
+          const int q = wave * IPW + i;
+          const int r = 16 * (q & 3) + (lane >> 2);
+          const size_t urow = size_t(qbase + (r >> 3) * qrs + (r & 7));
+          unsigned o = unsigned(dma_col_offset(q, lane));
+          asm volatile("" : "+v"(o));  // keep base + offset per block (no hoisted 64-bit address)
+          dma16(src + urow * ROWB + o, dst + q * 1024);
+        }
       }
     };
     // query block j into slot b of stage st (Q, dout, and its lse2 and delta
