@@ -70,7 +70,7 @@ constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int kQueryBlock = 64;                     // query rows per streamed block (dk/dv)
 constexpr int kKPrefetch = 4;                       // A fragments in flight (dq contractions)
-constexpr int kKvPrefetch = 1;                      // A fragments in flight (dk/dv contractions)
+constexpr int kKvPrefetch = 2;                      // A fragments in flight (dk/dv contractions)
 constexpr float kLog2e = 1.44269504088896340736f;
 
 static_assert(kKeyBlock == kQueryBlock, "one block size for keys and queries");
