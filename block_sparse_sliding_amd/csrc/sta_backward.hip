@@ -15,15 +15,16 @@
 //   dq     query-stationary: the forward's loop with S^T = K Q^T and
 //          dP^T = V dout^T, K and V rows streamed into LDS, then
 //          dq^T += K^T dS^T with K^T fragments read transposed from the same
-//          K rows in LDS;
-//   dk/dv  key-stationary: units of 256 keys (32 per wave) or 128 keys (16
-//          per wave), their K and V rows held as MFMA B operands, streaming
-//          every query block that sees the keys: S = Q K^T and dP = dout V^T
-//          with Q and dout rows in LDS, then dv^T += dout^T P and
-//          dk^T += Q^T dS with Q^T / dout^T fragments read transposed from
-//          the same rows, each 64-row block in two halves of 32 queries (so
-//          two key groups fit the registers and every fragment read from LDS
-//          feeds two MFMAs).
+//          K rows in LDS. Units of 256 rows (32 per wave) or at most 128 rows
+//          (two groups of 4 waves x 32 rows over alternate key blocks);
+//   dk/dv  key-stationary: units of 256 keys (32 per wave) or at most 128
+//          keys (as dq; with partial tiles 16 per wave), their K and V rows
+//          held as MFMA B operands, streaming every query block that sees the
+//          keys: S = Q K^T and dP = dout V^T with Q and dout rows in LDS, then
+//          dv^T += dout^T P and dk^T += Q^T dS with Q^T / dout^T fragments
+//          read transposed from the same rows, each 64-row block in two halves
+//          of 32 queries (so two key groups fit the registers and every
+//          fragment read from LDS feeds two MFMAs).
 // A transposed fragment (two ds_read_b64_tr_b16) presents its 32 rows in the
 // order in which a 16x16x32 MFMA accumulator leaves its rows in the lanes, so
 // P and dS go from the accumulator straight into the B operand, as in the
