@@ -16,6 +16,11 @@ using sta::Geom;
 using sta::Windows;
 
 constexpr size_t kAlign = 256;
+// smallest Hilbert slide window (in tiles) run with six-tile query units
+constexpr int kHilbertGroup6Window = 6;
+// Hilbert text units: at most this many, each with at least this many key tiles
+constexpr int kHilbertTextParts = 8;
+constexpr int kHilbertTextPartTiles = 128;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -71,6 +76,7 @@ sta_status make_geom(const sta_dims* d, int32_t has_text, int32_t text_length, G
   g->hilbert = 0;
   g->hil_m = 0;
   g->hil_group = 1;
+  g->text_parts = 1;
   return STA_OK;
 }
 
@@ -85,6 +91,15 @@ sta_status make_hilbert_geom(const sta_dims* d, int32_t has_text, int32_t text_l
   int m = 0;
   while ((1 << m) < side) ++m;
   g->hil_m = m;
+  // The text query rows see every key tile: one unit would stream all of them
+  // alone, longer than the rest of the call on a large image. Their keys are
+  // split over up to 8 units of at least 128 tiles each, merged afterwards.
+  if (g->has_text) {
+    const int parts = g->n_tiles / kHilbertTextPartTiles;
+    g->text_parts = parts < 1 ? 1 : parts > kHilbertTextParts ? kHilbertTextParts : parts;
+  }
+  // the most query units any grouping gives (single tiles); sizes the workspace
+  g->n_q = g->n_tiles + (g->has_text ? g->text_parts : 0);
   return STA_OK;
 }
 
@@ -120,7 +135,7 @@ sta_status make_windows(const Geom& g, const int32_t* ws, Windows* win, int64_t*
 // Forward workspace: the work order (one int32 per query unit), the queue
 // heads and a zero row (the source of keys that must not contribute).
 struct Carve {
-  size_t work, claim, zero_row, total;
+  size_t work, claim, zero_row, text_partial, total;
 };
 
 Carve carve(const Geom& g) {
@@ -129,6 +144,10 @@ Carve carve(const Geom& g) {
   c.work = at; at = align_up(at + size_t(g.B) * g.heads * g.n_q * 4);
   c.claim = at; at = align_up(at + size_t(sta::kClaimInts) * 4);
   c.zero_row = at; at = align_up(at + size_t(sta::kZeroRowBytes));
+  // partial results of split text units (FwdArgs::text_partial)
+  c.text_partial = at;
+  if (g.text_parts > 1)
+    at = align_up(at + size_t(g.B) * g.heads * g.text_parts * STA_TEXT_SLOTS * (g.D + 2) * 4);
   c.total = at;
   return c;
 }
@@ -282,9 +301,9 @@ sta_status forward_launch(Geom g, const Windows& win, const void* q, const void*
   int32_t* work = reinterpret_cast<int32_t*>(ws + c.work);
   int32_t* claim = reinterpret_cast<int32_t*>(ws + c.claim);
   // the work order counts query units: with grouped Hilbert units, a head has
-  // n_tiles / hil_group video units
+  // ceil(n_tiles / hil_group) video units
   Geom gs = g;
-  if (g.hilbert != 0) gs.n_tiles = g.n_tiles / g.hil_group;
+  if (g.hilbert != 0) gs.n_tiles = (g.n_tiles + g.hil_group - 1) / g.hil_group;
   st = hip_status(sta::launch_schedule_work(gs, win, work, claim, ws + c.zero_row, s));
   if (st == STA_OK) st = mark(1);
   if (st != STA_OK) return st;
@@ -297,6 +316,7 @@ sta_status forward_launch(Geom g, const Windows& win, const void* q, const void*
   a.work = work;
   a.claim = claim;
   a.zero_row = ws + c.zero_row;
+  a.text_partial = g.text_parts > 1 ? reinterpret_cast<float*>(ws + c.text_partial) : nullptr;
   a.q_scale = float(1.4426950408889634 / std::sqrt(double(g.D)));  // log2(e)/sqrt(D)
   st = hip_status(sta::launch_attention(g, win, a, s));
   if (st == STA_OK) st = mark(2);
@@ -362,17 +382,22 @@ sta_status sta_hilbert_forward(const sta_dims* dims, const void* q, const void* 
   st = make_hilbert_windows(g, window_lens, mode, &win);
   if (st != STA_OK) return st;
   g.hilbert = mode;
-  // Query units of four consecutive curve positions (an aligned 2x2 square of
-  // tiles, 256 rows) when every head's windows allow it: slide windows of at
-  // least 4 tiles (the four windows then share a core), windows of a multiple
-  // of 4 tiles (the four tiles then share their window); single tiles otherwise.
-  bool group = g.n_tiles % 4 == 0;
+  // Query units of several consecutive curve positions when every head's
+  // windows allow it. Slide windows of at least kHilbertGroup6Window tiles: six
+  // positions (384 rows, the shape of a video tile unit; their windows share a
+  // core of at least W - 5 tiles, and the last unit of a head holds what is
+  // left). Slide windows of at least 4 tiles, or windows of a multiple of 4
+  // tiles: four (an aligned 2x2 square of tiles, 256 rows; slide windows then
+  // share a core, fixed windows are the same for the four). Single tiles
+  // otherwise.
+  bool group4 = g.n_tiles % 4 == 0, group6 = mode == STA_HILBERT_SLIDE;
   for (int h = 0; h < g.heads; ++h) {
     const int w = window_lens[h];
-    group = group && (mode == STA_HILBERT_SLIDE ? w >= 4 : w % 4 == 0);
+    group4 = group4 && (mode == STA_HILBERT_SLIDE ? w >= 4 : w % 4 == 0);
+    group6 = group6 && w >= kHilbertGroup6Window;
   }
-  g.hil_group = group ? 4 : 1;
-  g.n_q = g.n_tiles / g.hil_group + (g.has_text ? 1 : 0);
+  g.hil_group = group6 ? 6 : group4 ? 4 : 1;
+  g.n_q = (g.n_tiles + g.hil_group - 1) / g.hil_group + (g.has_text ? g.text_parts : 0);
   return forward_launch(g, win, q, k, v, out, lse, workspace, workspace_bytes, stream, nullptr);
 }
 

@@ -114,7 +114,8 @@ __device__ inline const KernelArgs* kernel_args() {
 
 // HIL: Hilbert-window attention on a 2D image (Geom::hilbert): video query unit u
 // is the hil_group tiles at Hilbert curve positions hil_group * u .. + hil_group
-// - 1 (their rows in that order, 64 per tile), its key tiles come from
+// - 1, or those of them that exist (their rows in that order, 64 per tile),
+// its key tiles come from
 // HilbertKeyStream, and a block that only some of the unit's tiles see gives
 // the other rows a reference of +inf, so their p is exactly 0; everything
 // else is the same kernel.
@@ -156,15 +157,16 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(KernelArgs) 
     const int bh = unit / g.n_q;
     const int hd = bh % g.heads;
     const uint32_t wp = ka->win.w[hd];
-    const int n_vunits = HIL ? g.n_tiles / g.hil_group : g.n_tiles;
-    const bool text_unit = g.has_text && u == n_vunits;
+    const int n_vunits = HIL ? (g.n_tiles + g.hil_group - 1) / g.hil_group : g.n_tiles;
+    const bool text_unit = g.has_text && u >= n_vunits;  // (Hilbert: text part u - n_vunits)
 
     // query tile coordinates and rows (PAD: its existing tokens, compact order)
     int qtt = 0, qth = 0, qtw = 0;
     int q_ext = kFullExtent, q_base = 0;
     int q_rows = text_unit ? kTextSlots : kTileRows;
     if (HIL && !text_unit) {
-      q_rows = kKeyBlock * g.hil_group;  // 64 rows per tile
+      const int left = g.n_tiles - g.hil_group * u;
+      q_rows = kKeyBlock * (left < g.hil_group ? left : g.hil_group);  // 64 rows per tile
     } else if (!text_unit) {
       const int rest = div_by(u, g.nw, g.mag_nw);
       qtw = u - rest * g.nw;
@@ -200,7 +202,7 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(KernelArgs) 
     typename std::conditional<HIL, HilbertKeyStream, KeyStream<PAD>>::type keys;
     if constexpr (HIL) {
       // the window length is the w component of the head's window
-      keys.init(g, g.hil_group * u, ww, text_unit);
+      keys.init(g, g.hil_group * u, ww, text_unit, text_unit ? u - n_vunits : 0);
     } else {
       if (text_unit)
         keys.init(g, 0, g.nt, 0, g.nh, 0, g.nw);
@@ -531,6 +533,26 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(KernelArgs) 
         max_pass();
       }
 
+      if constexpr (HIL) {
+        // a text unit that holds a part of the keys: O (not normalised), the
+        // reference and the row sum, merged by text_merge_kernel
+        if (text_unit && g.text_parts > 1) {
+          const size_t slot = size_t(bh) * g.text_parts + (u - n_vunits);
+          float* __restrict__ op = a.text_partial + slot * kTextSlots * D;
+          float* __restrict__ ml =
+              a.text_partial + size_t(g.B) * g.heads * g.text_parts * kTextSlots * D + slot * kTextSlots * 2;
+#pragma unroll
+          for (int c = 0; c < QT; ++c) {
+            const float l = swap32_sum(swap16_sum(l_part[c]));
+            const int row = wave * RPW + c * 16 + (lane & 15);
+            float* dst = op + size_t(row) * D + (lane >> 4) * 4;
+#pragma unroll
+            for (int d = 0; d < DT; ++d) *reinterpret_cast<f32x4*>(dst + d * 16) = acc[c][d];
+            if (lane < 16) *reinterpret_cast<float2*>(ml + 2 * row) = float2{m_run[c], l};
+          }
+          return;
+        }
+      }
       // ---- epilogue: O = O^T / l in bf16 and lse, straight to raster positions
       __bf16* __restrict__ outr = reinterpret_cast<__bf16*>(a.out) + slab;
       float* __restrict__ lser = a.lse == nullptr ? nullptr : a.lse + size_t(bh) * g.S;
@@ -566,6 +588,38 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(KernelArgs) 
   }
 }
 
+// The text rows of a Hilbert call whose text units each took a part of the
+// keys: per row, with M = max over the parts of their reference m_p and
+// w_p = 2^(m_p - M), out = sum_p w_p O_p / sum_p w_p l_p in bf16 and lse =
+// (M + log2 sum_p w_p l_p) ln 2. Grid (B heads, 256 / 4), 4 rows of 64 threads
+// per workgroup, D / 64 columns per thread.
+template <int D>
+__global__ __launch_bounds__(256) void text_merge_kernel(Geom g, const float* __restrict__ part,
+                                                         __bf16* __restrict__ out, float* __restrict__ lse) {
+  constexpr int CPT = D / 64;
+  const int bh = blockIdx.x;
+  const int row = blockIdx.y * 4 + (threadIdx.x >> 6);
+  const int col = (threadIdx.x & 63) * CPT;
+  const int P = g.text_parts;
+  const float* ml = part + size_t(g.B) * g.heads * P * kTextSlots * D;
+  float M = -INFINITY;
+  for (int p = 0; p < P; ++p) M = fmaxf(M, ml[((size_t(bh) * P + p) * kTextSlots + row) * 2]);
+  float L = 0.f, o[CPT] = {};
+  for (int p = 0; p < P; ++p) {
+    const size_t slot = size_t(bh) * P + p;
+    const float w = __builtin_amdgcn_exp2f(ml[(slot * kTextSlots + row) * 2] - M);
+    L += w * ml[(slot * kTextSlots + row) * 2 + 1];
+    const float* op = part + (slot * kTextSlots + row) * D + col;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) o[i] += w * op[i];
+  }
+  const float inv = 1.f / L;
+  const size_t orow = size_t(bh) * g.S + g.n_video + row;
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) out[orow * D + col + i] = __bf16(o[i] * inv);
+  if (lse != nullptr && col == 0) lse[orow] = (M + __builtin_amdgcn_logf(L)) * kLn2;
+}
+
 // Resident workgroups of the kernel on the current device (cached per device).
 template <int D, bool PAD, bool HIL>
 int persistent_grid() {
@@ -580,6 +634,12 @@ hipError_t launch(const Geom& g, const Windows& win, const FwdArgs& a, hipStream
   if (resident <= 0) return hipErrorInvalidDevice;
   const int grid = units < resident ? units : resident;
   sta_attention_kernel<D, PAD, HIL><<<grid, kThreads, 0, stream>>>(KernelArgs{g, a, win});
+  if (HIL && g.has_text && g.text_parts > 1) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    text_merge_kernel<D><<<dim3(g.B * g.heads, kTextSlots / 4), 256, 0, stream>>>(
+        g, a.text_partial, static_cast<__bf16*>(a.out), a.lse);
+  }
   return hipGetLastError();
 }
 

@@ -41,9 +41,14 @@ struct Geom {
   // Hilbert-window attention (2D images, T = 1, a 2^hil_m x 2^hil_m tile grid):
   // 0 = the STA box windows; 1 = Hilbert slide windows; 2 = Hilbert windows
   int32_t hilbert, hil_m;
-  // tiles per Hilbert query unit (1 or 4: four consecutive curve positions,
-  // an aligned 2x2 square of tiles); n_q counts n_tiles / hil_group video units
+  // tiles per Hilbert query unit: 1, 4 (an aligned 2x2 square of tiles) or 6
+  // consecutive curve positions; n_q counts ceil(n_tiles / hil_group) video
+  // units, the last of which may hold fewer tiles
   int32_t hil_group;
+  // query units that share the text query rows (Hilbert: each takes a
+  // contiguous run of the key tiles, the last one also the text keys, and
+  // their partial results are merged after the attention kernel); 1 otherwise
+  int32_t text_parts;
 };
 
 // Per-head windows, packed as wt | wh << 10 | ww << 20 (kernel-argument copy).
@@ -307,45 +312,57 @@ struct KeyStream {
 };
 
 // The key blocks of a Hilbert-window query unit (2D image, T = 1): one block per
-// key tile (its single 8x8 frame). A video unit is G = hil_group consecutive
-// curve positions; their windows, which may differ by a shift, are streamed as
-// their common core [first, first + count), walked by the residues of the
-// positions modulo count (units whose windows overlap reach a shared tile at
-// the same step), then the positions left of the core [lfirst, lfirst +
-// lcount) and right of it [rfirst, rfirst + rcount), each seen by the unit's
-// rows of a contiguous range of its tiles (rows_lo, rows_hi), then the text
-// blocks as in KeyStream. Every row of the unit sees every core block. The
-// text unit streams every tile. block(j) may be called in any order.
+// key tile (its single 8x8 frame). A video unit is up to G = hil_group
+// consecutive curve positions (the last unit of a head may hold fewer); their
+// windows, which may differ by a shift, are streamed as their common core
+// [first, first + count), walked by the residues of the positions modulo count
+// (units whose windows overlap reach a shared tile at the same step), then the
+// positions left of the core [lfirst, lfirst + lcount) and right of it
+// [rfirst, rfirst + rcount), each seen by the unit's rows of a contiguous range
+// of its tiles (rows_lo, rows_hi), then the text blocks as in KeyStream. Every
+// row of the unit sees every core block. The text unit streams every tile.
+// block(j) may be called in any order.
 struct HilbertKeyStream {
   int first, count, lfirst, lcount, rfirst, rcount, m, G, W, mode;
-  // slide, four tiles: the window start of each (scalars: an array indexed at
-  // run time would put the whole stream in per-lane memory)
-  int st0, st1, st2, st3;
+  // slide: the window start of each of the unit's tiles, a large value past
+  // its last tile (scalars: an array indexed at run time would put the whole
+  // stream in per-lane memory)
+  int st0, st1, st2, st3, st4, st5;
   int n_vfull, n_vrem, n_tfull, n_plain, n_blk, text_len;
 
-  // pos0: curve position of the unit's first tile; text: the text unit
-  __host__ __device__ void init(const Geom& g, int pos0, int W_, bool text) {
+  // pos0: curve position of the unit's first tile; text: a text unit, part
+  // `part` of g.text_parts (tiles [part n / parts, (part + 1) n / parts) of
+  // the n = n_tiles, the text keys with the last part)
+  __host__ __device__ void init(const Geom& g, int pos0, int W_, bool text, int part = 0) {
+    constexpr int kPast = 1 << 29;
     m = g.hil_m;
     W = W_;
     mode = g.hilbert;
-    st0 = st1 = st2 = st3 = 0;
     G = text ? 1 : g.hil_group;
     lcount = rcount = 0;
     lfirst = rfirst = 0;
     if (text) {
-      first = 0;
-      count = g.n_tiles;
+      first = int(int64_t(part) * g.n_tiles / g.text_parts);
+      count = int(int64_t(part + 1) * g.n_tiles / g.text_parts) - first;
+      st0 = st1 = st2 = st3 = st4 = st5 = kPast;
     } else {
       int c0;
       hilbert_window(pos0, W, g.n_tiles, mode, first, c0);
       count = c0;
-      st0 = st1 = st2 = st3 = first;
-      if (G == 4 && mode == 1) {
-        st1 = window_start(pos0 + 1, W, g.n_tiles);
-        st2 = window_start(pos0 + 2, W, g.n_tiles);
-        st3 = window_start(pos0 + 3, W, g.n_tiles);
-        const int lo = st0, hi = st3;
-        first = hi;               // core [hi, lo + W)
+      st0 = first;
+      st1 = st2 = st3 = st4 = st5 = kPast;
+      // tiles of this unit: G, or what is left of the curve
+      const int tiles = g.n_tiles - pos0 < G ? g.n_tiles - pos0 : G;
+      if (tiles > 1 && mode == 1) {
+        const int n = g.n_tiles;
+        st1 = window_start(pos0 + 1, W, n);
+        int hi = st1;
+        if (tiles > 2) hi = st2 = window_start(pos0 + 2, W, n);
+        if (tiles > 3) hi = st3 = window_start(pos0 + 3, W, n);
+        if (tiles > 4) hi = st4 = window_start(pos0 + 4, W, n);
+        if (tiles > 5) hi = st5 = window_start(pos0 + 5, W, n);
+        const int lo = st0;
+        first = hi;  // core [hi, lo + W): the starts grow by at most 1 per position
         count = lo + W - hi;
         lfirst = lo;
         lcount = hi - lo;
@@ -355,7 +372,7 @@ struct HilbertKeyStream {
     }
     n_vfull = count + lcount + rcount;
     n_vrem = 0;
-    text_len = g.has_text ? g.text_length : 0;
+    text_len = g.has_text && (!text || part == g.text_parts - 1) ? g.text_length : 0;
     n_tfull = text_len / kKeyBlock;
     n_plain = n_vfull + n_tfull;
     n_blk = n_plain + (text_len % kKeyBlock != 0 ? 1 : 0);
@@ -375,12 +392,14 @@ struct HilbertKeyStream {
         // left of the core: tiles 0 .. t whose window starts at or before p
         // (the starts never decrease along the curve)
         p = lfirst + (j - count);
-        const int t = (st1 <= p ? 1 : 0) + (st2 <= p ? 1 : 0) + (st3 <= p ? 1 : 0);
+        const int t = (st1 <= p ? 1 : 0) + (st2 <= p ? 1 : 0) + (st3 <= p ? 1 : 0) + (st4 <= p ? 1 : 0) +
+                      (st5 <= p ? 1 : 0);
         s.rows_hi = kKeyBlock * (t + 1);
       } else {
         // right of the core: tiles t .. 3 whose window ends after p
         p = rfirst + (j - count - lcount);
-        const int t = (st0 + W <= p ? 1 : 0) + (st1 + W <= p ? 1 : 0) + (st2 + W <= p ? 1 : 0);
+        const int t = (st0 + W <= p ? 1 : 0) + (st1 + W <= p ? 1 : 0) + (st2 + W <= p ? 1 : 0) +
+                      (st3 + W <= p ? 1 : 0) + (st4 + W <= p ? 1 : 0);
         s.rows_lo = kKeyBlock * t;
       }
       int tx, ty;
@@ -470,6 +489,10 @@ struct FwdArgs {
   const int32_t* work;   // per-XCD queues of query units (launch_schedule_work)
   int32_t* claim;        // queue heads, zeroed by launch_schedule_work
   const void* zero_row;  // kZeroRowBytes of zeros (written by launch_schedule_work)
+  // g.text_parts > 1: partial results of the text units, [B heads][text_parts]
+  // [256 rows][D] fp32 (O, not normalised), then [B heads][text_parts][256
+  // rows][2] fp32 (reference m in log2 units, row sum l); nullptr otherwise
+  float* text_partial;
   float q_scale;         // log2(e) / sqrt(D), applied to the fp32 scores
 };
 constexpr int kZeroRowBytes = 256;  // one row of D = 128 bf16

@@ -101,9 +101,9 @@ __global__ __launch_bounds__(kWorkThreads) void schedule_work_kernel(Geom g, Win
       count[c] = g.B * g.n_tiles;
       cost[c] = (long long)kTileRows *
                 ((long long)win_t(p) * win_h(p) * win_w(p) * kTileRows + keys_extra);
-    } else {
-      count[c] = g.has_text ? g.B : 0;
-      cost[c] = (long long)kTextSlots * ((long long)g.n_tiles * kTileRows + keys_extra);
+    } else {  // the text rows, split over text_parts units by key tiles
+      count[c] = g.has_text ? g.B * g.text_parts : 0;
+      cost[c] = (long long)kTextSlots * ((long long)g.n_tiles * kTileRows + keys_extra) / g.text_parts;
     }
   }
   __syncthreads();
@@ -140,7 +140,8 @@ __global__ __launch_bounds__(kWorkThreads) void schedule_work_kernel(Geom g, Win
         const int b = idx / g.n_tiles, qt = idx % g.n_tiles;
         unit = (b * g.heads + hd) * g.n_q + qt;
       } else {
-        unit = (idx * g.heads + hd) * g.n_q + g.n_tiles;
+        const int b = idx / g.text_parts, part = idx % g.text_parts;
+        unit = (b * g.heads + hd) * g.n_q + g.n_tiles + part;
       }
       work[i] = unit;
       return;

@@ -197,8 +197,12 @@ sta_status sta_forward_noalloc(const sta_dims* dims, const void* q, const void* 
  * out as in sta_forward (raster token order; the curve only picks the key
  * tiles, and softmax attention does not depend on the order of the keys).
  * workspace: >= sta_hilbert_workspace_bytes(dims, has_text) bytes, 256-byte
- * aligned, same rules as sta_forward's. Two launches on `stream`, as in
- * sta_forward; the same argument errors.
+ * aligned, same rules as sta_forward's. With text on images of 256 tiles or
+ * more (128 x 128 tokens), it also holds fp32 partial results of the text
+ * rows, up to 8 x 256 x (D + 2) floats per (batch, head). Two launches on
+ * `stream`, as in sta_forward, and on such images a third, which merges
+ * those partial results into the text rows of out and lse; the same argument
+ * errors.
  */
 #define STA_HILBERT_SLIDE 1
 #define STA_HILBERT_WINDOW 2

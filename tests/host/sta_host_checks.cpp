@@ -86,7 +86,7 @@ hipError_t launch_schedule_work(const Geom& g, const Windows&, int32_t* work, in
 }
 hipError_t launch_attention(const Geom& g, const Windows&, const FwdArgs& a, hipStream_t) {
   record("attention", g, {P(a.q), P(a.k), P(a.v), P(a.out), P(a.lse), P(a.work), P(a.claim),
-                          P(a.zero_row)});
+                          P(a.zero_row), P(a.text_partial)});
   return hipSuccess;
 }
 hipError_t launch_bwd_prep(const Geom& g, const void* out, const void* dout, const float* lse,
@@ -306,6 +306,26 @@ void validate() {
     CHECK(sta_hilbert_forward(&ok, q, k, v, lens, STA_HILBERT_SLIDE, 100, 1, out, lse, ws, n - 1, nullptr) ==
               STA_ERR_WORKSPACE,
           "hilbert workspace short by one byte");
+    // large images split the text rows' keys over several units, whose
+    // partial results sit in the workspace: it must hold them whole (the size
+    // query covers single-tile units, so it may exceed what a call uses)
+    for (int side : {128, 256, 512}) {
+      const sta_dims big{2, 3, 128, 1, side, side};
+      const int32_t bl[3] = {27, 9, 64};
+      const size_t nb = sta_hilbert_workspace_bytes(&big, 1);
+      g_launches.clear();
+      CHECK(sta_hilbert_forward(&big, q, k, v, bl, STA_HILBERT_SLIDE, 226, 1, out, lse, ws, nb, nullptr) == STA_OK,
+            "hilbert %d^2 forward", side);
+      const Launch& l = g_launches.back();
+      const sta::Geom& gb = l.g;
+      const int parts = gb.n_tiles / 128 < 8 ? gb.n_tiles / 128 : 8;
+      CHECK(l.name == "attention" && gb.text_parts == parts && gb.hil_group == 6, "hilbert %d^2: %d text parts",
+            side, gb.text_parts);
+      check_in_workspace(l, {P(q), P(k), P(v), P(out), P(lse)}, P(ws), nb);
+      const uintptr_t tp = l.ptrs.back();
+      CHECK(tp != 0 && tp + size_t(2) * 3 * parts * 256 * (128 + 2) * 4 <= P(ws) + nb,
+            "hilbert %d^2: text partials inside the workspace", side);
+    }
     CHECK(sta_hilbert_gather(&ok, 1, q, q, nullptr) == STA_ERR_ALIAS, "hilbert gather in place");
     CHECK(sta_hilbert_gather(&ok, 1, q, out, nullptr) == STA_OK && g_launches.back().name == "rows_hilbert",
           "hilbert gather");
@@ -503,35 +523,42 @@ void hstream(int argc, char** argv) {
         "hilbert forward on the streamed geometry");
   const sta::Geom g = g_launches.back().g;
   CHECK(g.hilbert == mode && (8 << g.hil_m) == side && !g.full, "hilbert geometry");
-  const int G = g.hil_group, n_vunits = g.n_tiles / G;
-  CHECK(G == 1 || G == 4, "hilbert group %d", G);
-  CHECK(g.n_q == n_vunits + g.has_text, "hilbert units %d", g.n_q);
-  for (int u = 0; u < g.n_q; ++u) {
+  const int G = g.hil_group, n_vunits = (g.n_tiles + G - 1) / G;
+  CHECK(G == 1 || G == 4 || G == 6, "hilbert group %d", G);
+  CHECK(G != 6 || (mode == 1 && W >= 6), "six-tile units need a slide window of at least 6");
+  const int parts = g.has_text ? g.text_parts : 0;
+  CHECK(g.has_text ? (parts >= 1 && parts <= 8 && (parts == 1 || g.n_tiles / parts >= 128)) : g.text_parts == 1,
+        "hilbert text parts %d", g.text_parts);
+  CHECK(g.n_q == n_vunits + parts, "hilbert units %d", g.n_q);
+  // one line per query tile; the text units' parts are listed together
+  for (int u = 0; u < n_vunits + (g.has_text ? 1 : 0); ++u) {
     const bool text_unit = g.has_text && u == n_vunits;
-    sta::HilbertKeyStream ks;
-    ks.init(g, G * u, W, text_unit);
-    const int tiles = text_unit ? 1 : G;
+    const int tiles = text_unit ? 1 : std::min(G, g.n_tiles - G * u);
     for (int t = 0; t < tiles; ++t) {
       int tx = -1, ty = -1;
       if (!text_unit) sta::hilbert_d2xy(g.hil_m, G * u + t, tx, ty);
       std::vector<int> keys;
-      for (int j = 0; j < ks.n_blk; ++j) {
-        const sta::KeyBlock b = ks.block(g, j);
-        CHECK(j >= ks.n_plain || b.mask == sta::kKeyBlock, "unit %d block %d masked early", u, j);
-        CHECK(j != 0 || (b.rows_lo == 0 && b.rows_hi >= sta::kKeyBlock * tiles), "unit %d: block 0 not seen by all", u);
-        if (!(b.rows_lo <= sta::kKeyBlock * t && sta::kKeyBlock * t < b.rows_hi)) continue;
-        for (int r = 0; r < b.mask; ++r) {
-          int row;
-          if (b.kind == 0) {
-            CHECK(sta::extent_tokens(b.ext) == 64, "unit %d block %d: tile of %d tokens", u, j,
-                  sta::extent_tokens(b.ext));
-            row = b.base + (r >> 3) * g.W + (r & 7);
-          } else {
-            CHECK(b.kind == 1, "unit %d block %d kind %d", u, j, b.kind);
-            row = b.base + r;
+      for (int part = 0; part < (text_unit ? parts : 1); ++part) {
+        sta::HilbertKeyStream ks;
+        ks.init(g, G * u, W, text_unit, part);
+        for (int j = 0; j < ks.n_blk; ++j) {
+          const sta::KeyBlock b = ks.block(g, j);
+          CHECK(j >= ks.n_plain || b.mask == sta::kKeyBlock, "unit %d block %d masked early", u, j);
+          CHECK(j != 0 || (b.rows_lo == 0 && b.rows_hi >= sta::kKeyBlock * tiles), "unit %d: block 0 not seen by all", u);
+          if (!(b.rows_lo <= sta::kKeyBlock * t && sta::kKeyBlock * t < b.rows_hi)) continue;
+          for (int r = 0; r < b.mask; ++r) {
+            int row;
+            if (b.kind == 0) {
+              CHECK(sta::extent_tokens(b.ext) == 64, "unit %d block %d: tile of %d tokens", u, j,
+                    sta::extent_tokens(b.ext));
+              row = b.base + (r >> 3) * g.W + (r & 7);
+            } else {
+              CHECK(b.kind == 1, "unit %d block %d kind %d", u, j, b.kind);
+              row = b.base + r;
+            }
+            CHECK(row >= 0 && row < g.S, "unit %d block %d row %d outside the sequence", u, j, row);
+            keys.push_back(row);
           }
-          CHECK(row >= 0 && row < g.S, "unit %d block %d row %d outside the sequence", u, j, row);
-          keys.push_back(row);
         }
       }
       std::sort(keys.begin(), keys.end());

@@ -85,6 +85,9 @@ SMALL = [
     (32, 2, 128, True, 256, "window", [4, 3]),
     (64, 2, 128, True, 64, "window", [16, 1]),
     (64, 2, 64, False, 0, "slide", [9, 64]),
+    (32, 1, 128, True, 226, "slide", [6]),
+    (64, 2, 128, True, 17, "slide", [27, 7]),
+    (128, 1, 128, True, 226, "slide", [27]),
 ]
 
 
@@ -101,32 +104,36 @@ def test_hilbert_forward_all_rows(case):
            f"hilbert {case}")
 
 
-def test_hilbert_forward_score_jumps_redo():
+@pytest.mark.parametrize("lens", [[5, 7], [6, 11]], ids=["four-tile-units", "six-tile-units"])
+def test_hilbert_forward_score_jumps_redo(lens):
     """Key tiles scaled by large, uneven factors: scores jump by tens of log2
     units between blocks, which triggers the redo pass of the fixed reference."""
     side, heads, D = 32, 2, 128
-    note("hilbert forward, score jumps")
+    note(f"hilbert forward, score jumps, {lens}")
     q, k, v = inputs(41, 1, heads, side, D, True, 150)
     y, x = np.divmod(np.arange(side * side), side)
     factor = torch.ones(side * side + 256, device="cuda")
     factor[torch.as_tensor(((y // 8) * 4 + (x // 8)) % 5 == 3, device="cuda").nonzero()[:, 0]] = 6.0
     factor[side * side:side * side + 150] = 4.0
     k = (k.float() * factor[None, None, :, None]).to(torch.bfloat16)
-    out, lse = run_hilbert(q, k, v, [5, 7], "slide", 150, True, side)
+    out, lse = run_hilbert(q, k, v, lens, "slide", 150, True, side)
     rows = np.arange(q.shape[2])
-    ref_o, ref_l = oracle_rows(q, k, v, [5, 7], "slide", 150, True, side, rows)
+    ref_o, ref_l = oracle_rows(q, k, v, lens, "slide", 150, True, side, rows)
     _check(out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64), ref_o, ref_l,
            "hilbert score jumps")
 
 
-def test_hilbert_forward_full_size_sampled():
+@pytest.mark.parametrize("slide_lens", [[1, 9, 27, 64], [6, 9, 27, 64]], ids=["single-tile-units", "six-tile-units"])
+def test_hilbert_forward_full_size_sampled(slide_lens):
     """A 256x256 image (1024 tiles), 8 heads of different slide and window
-    lengths, D = 128, ragged text; 384 rows per head: every corner, the text
-    slots' ends and a seeded uniform draw."""
+    lengths, D = 128, ragged text; per head every text row (their keys are
+    split over 8 units and merged), every corner and a seeded uniform draw of
+    377 rows. The slide heads run with single-tile query units when one of them
+    has a window of 1 tile, else with six-tile units."""
     side, heads, D, ell = 256, 8, 128, 226
-    lens = [1, 9, 27, 64, 4, 16, 64, 256]
+    lens = slide_lens + [4, 16, 64, 256]
     modes = ["slide"] * 4 + ["window"] * 4
-    note("hilbert full size 256x256, 8 heads")
+    note(f"hilbert full size 256x256, 8 heads, slide {slide_lens}")
     q, k, v = inputs(99, 1, heads, side, D, True, ell)
     S = q.shape[2]
     rng = np.random.default_rng(5)
@@ -136,7 +143,7 @@ def test_hilbert_forward_full_size_sampled():
         qm, km, vm = q[:, hs].contiguous(), k[:, hs].contiguous(), v[:, hs].contiguous()
         lm = [lens[h] for h in hs]
         out, lse = run_hilbert(qm, km, vm, lm, mode, ell, True, side)
-        rows = np.unique(np.concatenate([fixed, rng.integers(0, S, 377)]))
+        rows = np.unique(np.concatenate([fixed, rng.integers(0, S, 377), np.arange(side * side, S)]))
         ref_o, ref_l = oracle_rows(qm, km, vm, lm, mode, ell, True, side, rows)
         idx = torch.as_tensor(rows, device="cuda")
         _check(out[:, :, idx].float().cpu().numpy().astype(np.float64),

@@ -229,6 +229,8 @@ HSHAPES = [
     (64, 0, 0, 4, 1),
     (64, 1, 30, 6, 2),
     (128, 1, 226, 27, 1),
+    (64, 1, 17, 6, 1),
+    (16, 1, 256, 4, 1),
 ]
 
 
@@ -242,7 +244,13 @@ def test_hilbert_key_stream_matches_oracle_mask(checks_bin, shape):
     n_tiles = (side // 8) ** 2
     nv = side * side
     m = (side // 8).bit_length() - 1
-    G = 4 if n_tiles % 4 == 0 and (W >= 4 if mode == 1 else W % 4 == 0) else 1
+    # tiles per unit as the host picks them: six consecutive positions for
+    # slide windows of at least 6 tiles, four for slide windows of at least 4
+    # or fixed windows of a multiple of 4, one otherwise
+    if mode == 1 and W >= 6:
+        G = 6
+    else:
+        G = 4 if n_tiles % 4 == 0 and (W >= 4 if mode == 1 else W % 4 == 0) else 1
     assert len(out) == n_tiles + text  # one line per query tile (and one for the text unit)
     for ln in out:
         f = ln.split()
