@@ -18,7 +18,7 @@ using sta::Windows;
 constexpr size_t kAlign = 256;
 // smallest Hilbert slide window (in tiles) run with six-tile query units
 constexpr int kHilbertGroup6Window = 6;
-// Hilbert text units: at most this many, each with at least this many key tiles
+// Text units of grouped calls: at most this many, each with at least this many key tiles
 constexpr int kHilbertTextParts = 8;
 constexpr int kHilbertTextPartTiles = 128;
 
@@ -80,6 +80,36 @@ sta_status make_geom(const sta_dims* d, int32_t has_text, int32_t text_length, G
   return STA_OK;
 }
 
+// Text query rows of a grouped call: they see every key tile, and as one unit
+// they would stream all of them alone, longer than the rest of the call on a
+// large image. Their keys are split over up to 8 units of at least 128 tiles
+// each, merged afterwards.
+int32_t grouped_text_parts(const Geom& g) {
+  if (!g.has_text) return 1;
+  const int parts = g.n_tiles / kHilbertTextPartTiles;
+  return parts < 1 ? 1 : parts > kHilbertTextParts ? kHilbertTextParts : parts;
+}
+
+// STA on a one-frame video of whole 8x8 tiles (a 2D image under the one-frame
+// reading): each tile holds 64 tokens, so a single-tile query unit keeps one
+// wave per SIMD busy. When every head's window spans at least two tiles along
+// each axis that has two tile rows (columns), query units become 2x2 squares
+// of tiles (Geom::hilbert = kSquareUnits), whose windows share a non-empty
+// core; the text rows are split by key tiles when split_text. Leaves g
+// unchanged otherwise.
+void plan_square_units(Geom* g, const Windows& win, bool split_text) {
+  if (g->T != 1 || g->H % sta::kTileH != 0 || g->W % sta::kTileW != 0) return;
+  if (g->nh < 2 && g->nw < 2) return;
+  for (int h = 0; h < g->heads; ++h) {
+    const uint32_t p = win.w[h];
+    if ((sta::win_h(p) < 2 && g->nh > 1) || (sta::win_w(p) < 2 && g->nw > 1)) return;
+  }
+  g->hilbert = sta::kSquareUnits;
+  g->hil_group = 4;
+  g->text_parts = split_text ? grouped_text_parts(*g) : 1;
+  g->n_q = ((g->nh + 1) / 2) * ((g->nw + 1) / 2) + (g->has_text ? g->text_parts : 0);
+}
+
 // A 2D image for the Hilbert entry points: one frame, square, its side 8 * 2^m
 // tokens (a 2^m x 2^m tile grid); sets g->hil_m.
 sta_status make_hilbert_geom(const sta_dims* d, int32_t has_text, int32_t text_length, Geom* g) {
@@ -91,13 +121,7 @@ sta_status make_hilbert_geom(const sta_dims* d, int32_t has_text, int32_t text_l
   int m = 0;
   while ((1 << m) < side) ++m;
   g->hil_m = m;
-  // The text query rows see every key tile: one unit would stream all of them
-  // alone, longer than the rest of the call on a large image. Their keys are
-  // split over up to 8 units of at least 128 tiles each, merged afterwards.
-  if (g->has_text) {
-    const int parts = g->n_tiles / kHilbertTextPartTiles;
-    g->text_parts = parts < 1 ? 1 : parts > kHilbertTextParts ? kHilbertTextParts : parts;
-  }
+  g->text_parts = grouped_text_parts(*g);
   // the most query units any grouping gives (single tiles); sizes the workspace
   g->n_q = g->n_tiles + (g->has_text ? g->text_parts : 0);
   return STA_OK;
@@ -200,6 +224,7 @@ size_t sta_workspace_bytes(const sta_dims* dims, const int32_t* window_sizes, in
   Windows win;
   int64_t n_ids = 0;
   if (make_windows(g, window_sizes, &win, &n_ids) != STA_OK) return 0;
+  plan_square_units(&g, win, true);
   return carve(g).total;
 }
 
@@ -300,10 +325,10 @@ sta_status forward_launch(Geom g, const Windows& win, const void* q, const void*
   if (st != STA_OK) return st;
   int32_t* work = reinterpret_cast<int32_t*>(ws + c.work);
   int32_t* claim = reinterpret_cast<int32_t*>(ws + c.claim);
-  // the work order counts query units: with grouped Hilbert units, a head has
-  // ceil(n_tiles / hil_group) video units
+  // the work order counts query units: with grouped units, a head has
+  // n_q - text_parts video units
   Geom gs = g;
-  if (g.hilbert != 0) gs.n_tiles = (g.n_tiles + g.hil_group - 1) / g.hil_group;
+  if (g.hilbert != 0) gs.n_tiles = g.n_q - (g.has_text ? g.text_parts : 0);
   st = hip_status(sta::launch_schedule_work(gs, win, work, claim, ws + c.zero_row, s));
   if (st == STA_OK) st = mark(1);
   if (st != STA_OK) return st;
@@ -323,10 +348,12 @@ sta_status forward_launch(Geom g, const Windows& win, const void* q, const void*
   return st;
 }
 
+// split_text: grouped calls may split their text rows (sta_forward_noalloc
+// keeps them whole when its scratch cannot hold the partial results)
 sta_status forward_impl(const sta_dims* dims, const void* q, const void* k, const void* v,
                         const int32_t* window_sizes, int32_t text_length, int32_t has_text,
                         void* out, float* lse, void* workspace, size_t workspace_bytes,
-                        void* stream, void* const* events) {
+                        void* stream, void* const* events, bool split_text = true) {
   Geom g;
   sta_status st = make_geom(dims, has_text, text_length, &g);
   if (st != STA_OK) return st;
@@ -334,6 +361,7 @@ sta_status forward_impl(const sta_dims* dims, const void* q, const void* k, cons
   int64_t n_ids = 0;
   st = make_windows(g, window_sizes, &win, &n_ids);
   if (st != STA_OK) return st;
+  plan_square_units(&g, win, split_text);
   return forward_launch(g, win, q, k, v, out, lse, workspace, workspace_bytes, stream, events);
 }
 
@@ -469,12 +497,22 @@ sta_status sta_forward_noalloc(const sta_dims* dims, const void* q, const void* 
   Geom g;
   sta_status st = make_geom(dims, has_text, text_length, &g);
   if (st != STA_OK) return st;
+  Windows win;
+  int64_t n_ids = 0;
+  st = make_windows(g, window_sizes, &win, &n_ids);
+  if (st != STA_OK) return st;
+  // square units with split text rows when their partial results fit the
+  // scratch, else with whole text units
+  Geom gs = g;
+  plan_square_units(&gs, win, true);
+  const bool split_text = carve(gs).total <= STA_NOALLOC_SCRATCH_BYTES;
+  plan_square_units(&g, win, false);
   if (carve(g).total > STA_NOALLOC_SCRATCH_BYTES) return STA_ERR_SCRATCH;
   void* ws = nullptr;
   st = scratch_address(&ws);
   if (st != STA_OK) return st;
   return forward_impl(dims, q, k, v, window_sizes, text_length, has_text, out, lse, ws,
-                      STA_NOALLOC_SCRATCH_BYTES, stream, nullptr);
+                      STA_NOALLOC_SCRATCH_BYTES, stream, nullptr, split_text);
 }
 
 }  // extern "C"

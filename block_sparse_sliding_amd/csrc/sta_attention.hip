@@ -112,14 +112,19 @@ __device__ inline const KernelArgs* kernel_args() {
   return (const KernelArgs*)kp;
 }
 
-// HIL: Hilbert-window attention on a 2D image (Geom::hilbert): video query unit u
-// is the hil_group tiles at Hilbert curve positions hil_group * u .. + hil_group
-// - 1, or those of them that exist (their rows in that order, 64 per tile),
-// its key tiles come from
-// HilbertKeyStream, and a block that only some of the unit's tiles see gives
-// the other rows a reference of +inf, so their p is exactly 0; everything
-// else is the same kernel.
-template <int D, bool PAD, bool HIL>
+// GRP: query units of several 64-token tiles of a one-frame video (their rows
+// in unit order, 64 per tile). kGrpHilbert, Hilbert-window attention
+// (Geom::hilbert 1 or 2): video unit u is the hil_group tiles at Hilbert curve
+// positions hil_group * u .. + hil_group - 1, or those of them that exist,
+// with key tiles from HilbertKeyStream. kGrpSquares, STA on a one-frame video
+// (Geom::hilbert == kSquareUnits): unit u is a 2x2 square of tiles, with key
+// tiles from SquareKeyStream. A block that only some of the unit's tiles see
+// (KeyBlock::seen) gives the other rows a reference of +inf, so their p is
+// exactly 0. With GRP, the text rows may be split over text_parts units by
+// key tiles. Everything else is the same kernel.
+constexpr int kGrpNone = 0, kGrpHilbert = 1, kGrpSquares = 2;
+
+template <int D, bool PAD, int GRP>
 __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(KernelArgs) {
   constexpr int KS = D / 32;                  // k-steps of S^T
   constexpr int DT = D / 16;                  // d groups of O^T (and V column units)
@@ -129,6 +134,8 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(KernelArgs) 
   constexpr int IPW = BLK / 1024 / kWaves;    // DMA instructions per wave per tensor
   constexpr int VPAIR = kKeyBlock * 64;       // bytes of one V column pair (4 KB)
   static_assert(IPW >= 1 && BLK % (1024 * kWaves) == 0, "block must split over the waves");
+  constexpr bool HIL = GRP != kGrpNone;  // grouped units of 64-token tiles
+  static_assert(!HIL || PAD, "grouped units are one-frame tiles");
   __shared__ __attribute__((aligned(1024))) char lds[2][2][BLK];  // [stage][K|V]
   __shared__ int shared_word[2];                                  // claimed unit, redo flag
 
@@ -157,16 +164,19 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(KernelArgs) 
     const int bh = unit / g.n_q;
     const int hd = bh % g.heads;
     const uint32_t wp = ka->win.w[hd];
-    const int n_vunits = HIL ? (g.n_tiles + g.hil_group - 1) / g.hil_group : g.n_tiles;
-    const bool text_unit = g.has_text && u >= n_vunits;  // (Hilbert: text part u - n_vunits)
+    const int n_vunits = HIL ? g.n_q - (g.has_text ? g.text_parts : 0) : g.n_tiles;
+    const bool text_unit = g.has_text && u >= n_vunits;  // (grouped: text part u - n_vunits)
 
     // query tile coordinates and rows (PAD: its existing tokens, compact order)
     int qtt = 0, qth = 0, qtw = 0;
     int q_ext = kFullExtent, q_base = 0;
     int q_rows = text_unit ? kTextSlots : kTileRows;
-    if (HIL && !text_unit) {
+    int sq_y = 0, sq_x = 0, sq_layout = 0;  // kGrpSquares: the unit's square
+    if (GRP == kGrpHilbert && !text_unit) {
       const int left = g.n_tiles - g.hil_group * u;
       q_rows = kKeyBlock * (left < g.hil_group ? left : g.hil_group);  // 64 rows per tile
+    } else if (GRP == kGrpSquares && !text_unit) {
+      q_rows = kKeyBlock * square_tiles(g, u, sq_y, sq_x, sq_layout);
     } else if (!text_unit) {
       const int rest = div_by(u, g.nw, g.mag_nw);
       qtw = u - rest * g.nw;
@@ -181,9 +191,15 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(KernelArgs) 
     // raster row of unit row `row` (< q_rows)
     auto query_raster = [&](int row) {
       if (text_unit) return g.n_video + row;
-      if constexpr (HIL) {  // row r of tile t = row / 64 of the unit's curve run
+      if constexpr (HIL) {  // row r of unit tile row / 64
         int tx, ty;
-        hilbert_d2xy(g.hil_m, g.hil_group * u + (row >> 6), tx, ty);
+        if constexpr (GRP == kGrpSquares) {
+          square_tile(row >> 6, sq_layout, ty, tx);
+          ty += 2 * sq_y;
+          tx += 2 * sq_x;
+        } else {
+          hilbert_d2xy(g.hil_m, g.hil_group * u + (row >> 6), tx, ty);
+        }
         return (ty * kTileH + ((row >> 3) & 7)) * g.W + tx * kTileW + (row & 7);
       }
       int dt, dh, dw;
@@ -199,8 +215,11 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(KernelArgs) 
 
     // key blocks: the window of the query tile, or every tile for the text unit
     const int wt = win_t(wp), wh = win_h(wp), ww = win_w(wp);
-    typename std::conditional<HIL, HilbertKeyStream, KeyStream<PAD>>::type keys;
-    if constexpr (HIL) {
+    typename std::conditional<GRP == kGrpSquares, SquareKeyStream,
+                              typename std::conditional<HIL, HilbertKeyStream, KeyStream<PAD>>::type>::type keys;
+    if constexpr (GRP == kGrpSquares) {
+      keys.init(g, text_unit ? u - n_vunits : u, wh, ww, text_unit);
+    } else if constexpr (HIL) {
       // the window length is the w component of the head's window
       keys.init(g, g.hil_group * u, ww, text_unit, text_unit ? u - n_vunits : 0);
     } else {
@@ -372,7 +391,7 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(KernelArgs) 
           __syncthreads();
           f32x4 s[QT][4];
           scores(s, stage, j >= n_plain ? s_cur.mask : kKeyBlock);
-          const int rows_lo = s_cur.rows_lo, rows_hi = s_cur.rows_hi;  // of block j
+          const int seen = s_cur.seen;  // of block j
           if (j + 1 < n_blk) {
             s_cur = keys.block(g, j + 1);
             issue(s_cur, stage ^ 1);
@@ -388,11 +407,11 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(KernelArgs) 
 #pragma unroll
           for (int c = 0; c < QT; ++c) mb[c] = m_run[c];
           if constexpr (HIL) {
-            if (rows_lo > 0 || rows_hi < q_rows) {
+            if (seen != -1) {
 #pragma unroll
               for (int c = 0; c < QT; ++c) {
                 const int row = wave * RPW + c * 16 + (lane & 15);
-                mb[c] = (row >= rows_lo && row < rows_hi) ? m_run[c] : INFINITY;
+                mb[c] = ((seen >> (row >> 6)) & 1) != 0 ? m_run[c] : INFINITY;
               }
             }
           }
@@ -479,7 +498,7 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(KernelArgs) 
 #pragma unroll
           for (int c = 0; c < QT; ++c) {
             const int row = wave * RPW + c * 16 + (lane & 15);
-            const bool sees = !HIL || (row >= s_j.rows_lo && row < s_j.rows_hi);
+            const bool sees = !HIL || ((s_j.seen >> (row >> 6)) & 1) != 0;
             mx[c] = sees ? fmaxf(mx[c], bm[c]) : mx[c];
           }
           __syncthreads();  // every wave has read the stage before it is refilled
@@ -588,7 +607,7 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(KernelArgs) 
   }
 }
 
-// The text rows of a Hilbert call whose text units each took a part of the
+// The text rows of a grouped call whose text units each took a part of the
 // keys: per row, with M = max over the parts of their reference m_p and
 // w_p = 2^(m_p - M), out = sum_p w_p O_p / sum_p w_p l_p in bf16 and lse =
 // (M + log2 sum_p w_p l_p) ln 2. Grid (B heads, 256 / 4), 4 rows of 64 threads
@@ -621,20 +640,20 @@ __global__ __launch_bounds__(256) void text_merge_kernel(Geom g, const float* __
 }
 
 // Resident workgroups of the kernel on the current device (cached per device).
-template <int D, bool PAD, bool HIL>
+template <int D, bool PAD, int GRP>
 int persistent_grid() {
   static int cache[kMaxDevices] = {};
-  return resident_workgroups(sta_attention_kernel<D, PAD, HIL>, kThreads, cache);
+  return resident_workgroups(sta_attention_kernel<D, PAD, GRP>, kThreads, cache);
 }
 
-template <int D, bool PAD, bool HIL = false>
+template <int D, bool PAD, int GRP = kGrpNone>
 hipError_t launch(const Geom& g, const Windows& win, const FwdArgs& a, hipStream_t stream) {
   const int units = g.B * g.heads * g.n_q;
-  const int resident = persistent_grid<D, PAD, HIL>();
+  const int resident = persistent_grid<D, PAD, GRP>();
   if (resident <= 0) return hipErrorInvalidDevice;
   const int grid = units < resident ? units : resident;
-  sta_attention_kernel<D, PAD, HIL><<<grid, kThreads, 0, stream>>>(KernelArgs{g, a, win});
-  if (HIL && g.has_text && g.text_parts > 1) {
+  sta_attention_kernel<D, PAD, GRP><<<grid, kThreads, 0, stream>>>(KernelArgs{g, a, win});
+  if (GRP != kGrpNone && g.has_text && g.text_parts > 1) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     text_merge_kernel<D><<<dim3(g.B * g.heads, kTextSlots / 4), 256, 0, stream>>>(
@@ -646,8 +665,13 @@ hipError_t launch(const Geom& g, const Windows& win, const FwdArgs& a, hipStream
 }  // namespace
 
 hipError_t launch_attention(const Geom& g, const Windows& win, const FwdArgs& a, hipStream_t stream) {
-  if (g.hilbert != 0)  // a one-frame image: never a tile multiple
-    return g.D == 128 ? launch<128, true, true>(g, win, a, stream) : launch<64, true, true>(g, win, a, stream);
+  // one-frame images (grouped units): never a tile multiple
+  if (g.hilbert == kSquareUnits)
+    return g.D == 128 ? launch<128, true, kGrpSquares>(g, win, a, stream)
+                      : launch<64, true, kGrpSquares>(g, win, a, stream);
+  if (g.hilbert != 0)
+    return g.D == 128 ? launch<128, true, kGrpHilbert>(g, win, a, stream)
+                      : launch<64, true, kGrpHilbert>(g, win, a, stream);
   if (g.full) return g.D == 128 ? launch<128, false>(g, win, a, stream) : launch<64, false>(g, win, a, stream);
   return g.D == 128 ? launch<128, true>(g, win, a, stream) : launch<64, true>(g, win, a, stream);
 }

@@ -39,17 +39,23 @@ struct Geom {
   // every tile index (n_tiles * max(nw, nh) < 2^32 is checked on the host).
   uint32_t mag_nw, mag_nh;
   // Hilbert-window attention (2D images, T = 1, a 2^hil_m x 2^hil_m tile grid):
-  // 0 = the STA box windows; 1 = Hilbert slide windows; 2 = Hilbert windows
+  // 0 = the STA box windows; 1 = Hilbert slide windows; 2 = Hilbert windows;
+  // kSquareUnits = the STA box windows on a one-frame video of whole 8x8
+  // tiles, with query units of 2x2 squares of tiles (SquareKeyStream)
   int32_t hilbert, hil_m;
-  // tiles per Hilbert query unit: 1, 4 (an aligned 2x2 square of tiles) or 6
-  // consecutive curve positions; n_q counts ceil(n_tiles / hil_group) video
-  // units, the last of which may hold fewer tiles
+  // tiles per grouped query unit: Hilbert 1, 4 (an aligned 2x2 square of
+  // tiles) or 6 consecutive curve positions, ceil(n_tiles / hil_group) video
+  // units, the last of which may hold fewer tiles; squares 4, ceil(nh / 2) x
+  // ceil(nw / 2) video units, those on an odd last tile row or column holding
+  // 2 or 1 tiles. n_q counts the video units plus text_parts text units
   int32_t hil_group;
-  // query units that share the text query rows (Hilbert: each takes a
+  // query units that share the text query rows (grouped units: each takes a
   // contiguous run of the key tiles, the last one also the text keys, and
   // their partial results are merged after the attention kernel); 1 otherwise
   int32_t text_parts;
 };
+
+constexpr int32_t kSquareUnits = 3;  // Geom::hilbert of STA with 2x2-square query units
 
 // Per-head windows, packed as wt | wh << 10 | ww << 20 (kernel-argument copy).
 struct Windows {
@@ -207,9 +213,10 @@ struct KeyBlock {
   int kind;
   int base, lim, ext, sub;
   int mask;  // first block row that must not contribute (64: none)
-  // query rows of the unit that see this block: [rows_lo, rows_hi) (all of
-  // them except in grouped Hilbert units, whose tiles' windows differ)
-  int rows_lo, rows_hi;
+  // the tiles of a grouped query unit (64 rows each, tile i = unit rows
+  // 64 i .. 64 i + 63) that see this block: bit i; -1 (every bit) when all of
+  // them do, as in every unit of one tile or of the text rows
+  int seen;
 };
 
 // The key blocks of one query unit, in the order the forward kernel streams
@@ -293,8 +300,7 @@ struct KeyStream {
       const int left = n_tok - tile_sub * kKeyBlock;
       s.mask = left < kKeyBlock ? left : kKeyBlock;
       ++tile_sub;
-      s.rows_lo = 0;
-      s.rows_hi = kTileRows;
+      s.seen = -1;
     } else {
       const int tb = j < n_plain ? j - n_vfull : n_tfull;
       s.kind = 1;
@@ -304,8 +310,7 @@ struct KeyStream {
       s.ext = kFullExtent;
       s.sub = 0;
       s.mask = s.lim;
-      s.rows_lo = 0;
-      s.rows_hi = kTileRows;
+      s.seen = -1;
     }
     return s;
   }
@@ -318,8 +323,8 @@ struct KeyStream {
 // [first, first + count), walked by the residues of the positions modulo count
 // (units whose windows overlap reach a shared tile at the same step), then the
 // positions left of the core [lfirst, lfirst + lcount) and right of it
-// [rfirst, rfirst + rcount), each seen by the unit's rows of a contiguous range
-// of its tiles (rows_lo, rows_hi), then the text blocks as in KeyStream. Every
+// [rfirst, rfirst + rcount), each seen by a contiguous range of the unit's
+// tiles (KeyBlock::seen), then the text blocks as in KeyStream. Every
 // row of the unit sees every core block. The text unit streams every tile.
 // block(j) may be called in any order.
 struct HilbertKeyStream {
@@ -380,8 +385,7 @@ struct HilbertKeyStream {
   __host__ __device__ void reset() {}
   __host__ __device__ KeyBlock block(const Geom& g, int j) const {
     KeyBlock s;
-    s.rows_lo = 0;
-    s.rows_hi = kTileRows;
+    s.seen = -1;
     if (j < n_vfull) {
       int p;
       if (j < count) {
@@ -394,13 +398,13 @@ struct HilbertKeyStream {
         p = lfirst + (j - count);
         const int t = (st1 <= p ? 1 : 0) + (st2 <= p ? 1 : 0) + (st3 <= p ? 1 : 0) + (st4 <= p ? 1 : 0) +
                       (st5 <= p ? 1 : 0);
-        s.rows_hi = kKeyBlock * (t + 1);
+        s.seen = (2 << t) - 1;
       } else {
         // right of the core: tiles t .. 3 whose window ends after p
         p = rfirst + (j - count - lcount);
         const int t = (st0 + W <= p ? 1 : 0) + (st1 + W <= p ? 1 : 0) + (st2 + W <= p ? 1 : 0) +
                       (st3 + W <= p ? 1 : 0) + (st4 + W <= p ? 1 : 0);
-        s.rows_lo = kKeyBlock * t;
+        s.seen = -(1 << t);
       }
       int tx, ty;
       hilbert_d2xy(m, p, tx, ty);
@@ -418,6 +422,144 @@ struct HilbertKeyStream {
       s.lim = left < kKeyBlock ? left : kKeyBlock;
       s.ext = kFullExtent;
       s.sub = 0;
+      s.mask = s.lim;
+    }
+    return s;
+  }
+};
+
+// The key blocks of an STA query unit of a 2x2 square of tiles (a one-frame
+// video of whole 8x8 tiles, Geom::hilbert == kSquareUnits). Unit u of a head
+// is square (sy, sx) = (u / ceil(nw / 2), u % ceil(nw / 2)): the tiles
+// (2 sy + dy, 2 sx + dx) that exist, in the order (0,0), (0,1), (1,1), (1,0)
+// of (dy, dx) (square_tile), unit tile i being unit rows 64 i .. 64 i + 63.
+// Along h, the windows of the two tile rows start at sh0 and sh1 = sh0 or
+// sh0 + 1 (window_start never grows by more than one per tile), so the tiles
+// they cover are a core [sh1, sh0 + wh) seen by both, plus, when sh1 > sh0,
+// one row above the core seen by dy = 0 only and one below it seen by dy = 1
+// only; the same along w. The unit streams its core first, walked by the
+// residues of the key tile coordinates modulo the core's size (units whose
+// cores overlap reach a shared tile at the same step), then the rows above
+// and below the core across the full width, then the columns left and right
+// of the core over its rows, each block with the mask of the unit's tiles
+// that see it (KeyBlock::seen), then the text blocks as in KeyStream. The
+// core is never empty when wh >= 2 and ww >= 2, or the square has a single
+// tile row (column) along the axis where the window is 1, so block 0 is seen
+// by every row of the unit. A text unit streams the key tiles of its part in
+// raster tile order. block(j) may be called in any order.
+__host__ __device__ inline void square_tile(int i, int layout, int& dy, int& dx) {
+  // layout: 0 a full square, 1 one tile row (no dy = 1), 2 one tile column
+  // (no dx = 1), 3 a single tile
+  if (layout == 2) {
+    dy = i;
+    dx = 0;
+  } else {
+    dy = i >> 1;
+    dx = (i ^ (i >> 1)) & 1;
+  }
+}
+
+// Tiles of square unit u (1, 2 or 4) and its layout for square_tile.
+__host__ __device__ inline int square_tiles(const Geom& g, int u, int& sy, int& sx, int& layout) {
+  const int n_sx = (g.nw + 1) >> 1;
+  sy = u / n_sx;
+  sx = u - sy * n_sx;
+  const bool h1 = 2 * sy + 1 < g.nh, w1 = 2 * sx + 1 < g.nw;
+  layout = h1 ? (w1 ? 0 : 2) : (w1 ? 1 : 3);
+  return (h1 ? 2 : 1) * (w1 ? 2 : 1);
+}
+
+struct SquareKeyStream {
+  int ch, cw, Ch, Cw;  // the core: tile rows [ch, ch + Ch), tile columns [cw, cw + Cw)
+  int mh, mw;          // 1 when the square's windows differ along h (w): one row (column) on each side
+  int layout;          // square_tile's layout
+  int first;           // text unit: its first key tile (raster tile order)
+  int n_core, n_vfull, n_tfull, n_plain, n_blk, text_len;
+
+  // u: the unit's square, or the text part when `text`
+  __host__ __device__ void init(const Geom& g, int u, int wh, int ww, bool text) {
+    if (text) {
+      first = int(int64_t(u) * g.n_tiles / g.text_parts);
+      n_core = int(int64_t(u + 1) * g.n_tiles / g.text_parts) - first;
+      ch = cw = Ch = Cw = 0;
+      mh = mw = 0;
+      layout = 3;
+    } else {
+      first = 0;
+      int sy, sx;
+      square_tiles(g, u, sy, sx, layout);
+      const int h0 = 2 * sy, w0 = 2 * sx;
+      const int sh0 = window_start(h0, wh, g.nh);
+      const int sh1 = (layout == 0 || layout == 2) ? window_start(h0 + 1, wh, g.nh) : sh0;
+      const int sw0 = window_start(w0, ww, g.nw);
+      const int sw1 = (layout == 0 || layout == 1) ? window_start(w0 + 1, ww, g.nw) : sw0;
+      mh = sh1 - sh0;
+      mw = sw1 - sw0;
+      ch = sh1;
+      Ch = wh - mh;
+      cw = sw1;
+      Cw = ww - mw;
+      n_core = Ch * Cw;
+    }
+    // edge blocks: two rows of Cw + 2 mw tiles when mh, two columns of Ch tiles when mw
+    n_vfull = n_core + 2 * mh * (Cw + 2 * mw) + 2 * mw * Ch;
+    text_len = g.has_text && (!text || u == g.text_parts - 1) ? g.text_length : 0;
+    n_tfull = text_len / kKeyBlock;
+    n_plain = n_vfull + n_tfull;
+    n_blk = n_plain + (text_len % kKeyBlock != 0 ? 1 : 0);
+  }
+  __host__ __device__ void reset() {}
+  __host__ __device__ KeyBlock block(const Geom& g, int j) const {
+    KeyBlock s;
+    s.seen = -1;
+    s.sub = 0;
+    if (j < n_vfull) {
+      int kh, kw;
+      if (Ch == 0) {  // a text unit: key tile first + j in raster tile order
+        kh = (first + j) / g.nw;
+        kw = first + j - kh * g.nw;
+      } else if (j < n_core) {
+        const int jh = j / Cw, jw = j - jh * Cw;
+        const int dh = (jh - ch) % Ch, dw = (jw - cw) % Cw;
+        kh = ch + (dh < 0 ? dh + Ch : dh);
+        kw = cw + (dw < 0 ? dw + Cw : dw);
+      } else {
+        // the tile rows (bit dy) and columns (bit dx) of the square that see the block
+        int hsee = 3, wsee = 3;
+        const int e = j - n_core, Uw = Cw + 2 * mw;
+        if (e < 2 * mh * Uw) {
+          const int r = e / Uw, c = e - r * Uw;
+          kh = r == 0 ? ch - 1 : ch + Ch;
+          hsee = r == 0 ? 1 : 2;
+          kw = cw - mw + c;
+          wsee = mw == 0 ? 3 : c == 0 ? 1 : c == Uw - 1 ? 2 : 3;
+        } else {
+          const int e2 = e - 2 * mh * Uw, side = e2 / Ch;
+          kh = ch + (e2 - side * Ch);
+          kw = side == 0 ? cw - 1 : cw + Cw;
+          wsee = side == 0 ? 1 : 2;
+        }
+        int seen = 0;
+        const int tiles = layout == 0 ? 4 : layout == 3 ? 1 : 2;
+        for (int i = 0; i < tiles; ++i) {
+          int dy, dx;
+          square_tile(i, layout, dy, dx);
+          seen |= ((hsee >> dy) & (wsee >> dx) & 1) << i;
+        }
+        s.seen = seen;
+      }
+      s.kind = 0;
+      s.base = kh * kTileH * g.W + kw * kTileW;
+      s.lim = kKeyBlock;
+      s.ext = tile_extent(0, kh, kw, g);
+      s.mask = kKeyBlock;
+    } else {
+      const int tb = j < n_plain ? j - n_vfull : n_tfull;
+      s.kind = 1;
+      s.base = g.n_video + tb * kKeyBlock;
+      const int left = text_len - tb * kKeyBlock;
+      s.lim = left < kKeyBlock ? left : kKeyBlock;
+      s.ext = kFullExtent;
       s.mask = s.lim;
     }
     return s;

@@ -91,6 +91,12 @@ WORKLOADS = {
     # h 5 of 8 rows; tile grid (6, 6, 10)
     "ragged": Workload("ragged", 1, 24, 128, (33, 45, 80),
                        _per_head(24, [(3, 3, 3)]), True, 226, 70),
+    # 2D STA on a 512x512 image: a one-frame video, so each tile holds one
+    # 8x8 frame (64 tokens) and the grid is 1x64x64 tiles; window 5x5 tiles
+    # (25 key tiles, as many as the Hilbert workload's 27 nearly), the
+    # headline's heads, head size and text
+    "image": Workload("image", 1, 24, 128, (1, 512, 512),
+                      _per_head(24, [(1, 5, 5)]), True, 226, 90),
     # Hilbert slide attention on a 512x512 image (a 64x64 grid of 8x8 tiles),
     # 27 key tiles per query tile along the curve, the headline's heads, head
     # size and text; the pages give no size for the Hilbert row

@@ -482,6 +482,7 @@ void stream(int argc, char** argv) {
             n) == STA_OK,
         "forward on the streamed geometry");
   const sta::Geom g = g_launches.back().g;
+  CHECK(g.hilbert == 0, "stream: single-tile units expected");
   if (g.full)
     stream_units<false>(g, a[5], a[6], a[7]);
   else
@@ -544,8 +545,8 @@ void hstream(int argc, char** argv) {
         for (int j = 0; j < ks.n_blk; ++j) {
           const sta::KeyBlock b = ks.block(g, j);
           CHECK(j >= ks.n_plain || b.mask == sta::kKeyBlock, "unit %d block %d masked early", u, j);
-          CHECK(j != 0 || (b.rows_lo == 0 && b.rows_hi >= sta::kKeyBlock * tiles), "unit %d: block 0 not seen by all", u);
-          if (!(b.rows_lo <= sta::kKeyBlock * t && sta::kKeyBlock * t < b.rows_hi)) continue;
+          CHECK(j != 0 || b.seen == -1, "unit %d: block 0 not seen by all", u);
+          if (((b.seen >> t) & 1) == 0) continue;
           for (int r = 0; r < b.mask; ++r) {
             int row;
             if (b.kind == 0) {
@@ -575,6 +576,94 @@ void hstream(int argc, char** argv) {
   }
 }
 
+
+// "sqstream <H> <W> <has_text> <ell> <wh> <ww>": STA on a one-frame video
+// (T = 1) as the forward plans it; with square units, one line per query tile
+// of every unit, "unit u i tile_h tile_w" then its key rows as in `stream`,
+// and one line for the text rows (tile -1 -1, every part's keys); "single"
+// when the forward keeps single-tile units.
+void sqstream(int argc, char** argv) {
+  if (argc != 8) {
+    std::fprintf(stderr, "sqstream needs 6 integers\n");
+    std::exit(2);
+  }
+  int a[6];
+  for (int i = 0; i < 6; ++i) a[i] = std::atoi(argv[2 + i]);
+  const sta_dims d{1, 1, 128, 1, a[0], a[1]};
+  const int text = a[2], ell = a[3];
+  std::vector<int32_t> w = windows_for(1, 1, a[4], a[5]);
+  const size_t n = sta_workspace_bytes(&d, w.data(), text);
+  CHECK(n > 0, "square workspace bytes");
+  g_launches.clear();
+  CHECK(fwd(&d, w.data(), ell, text, fake(0), fake(1), fake(2), fake(3), static_cast<float*>(fake(4)), fake(8),
+            n) == STA_OK,
+        "forward on the streamed geometry");
+  const sta::Geom g = g_launches.back().g;
+  if (g.hilbert == 0) {
+    std::printf("single\n");
+    return;
+  }
+  CHECK(g.hilbert == sta::kSquareUnits && g.hil_group == 4 && g.T == 1, "square geometry");
+  const int n_su = ((g.nh + 1) / 2) * ((g.nw + 1) / 2);
+  const int parts = g.has_text ? g.text_parts : 0;
+  CHECK(g.n_q == n_su + parts, "square units %d", g.n_q);
+  CHECK(g.has_text ? (parts >= 1 && parts <= 8 && (parts == 1 || g.n_tiles / parts >= 128)) : g.text_parts == 1,
+        "square text parts %d", g.text_parts);
+  std::vector<int> covered(g.n_tiles, 0);
+  for (int u = 0; u < n_su + (g.has_text ? 1 : 0); ++u) {
+    const bool text_unit = g.has_text && u == n_su;
+    int sy = 0, sx = 0, layout = 3, tiles = 1;
+    if (!text_unit) tiles = sta::square_tiles(g, u, sy, sx, layout);
+    for (int i = 0; i < tiles; ++i) {
+      int th = -1, tw = -1;
+      if (!text_unit) {
+        int dy, dx;
+        sta::square_tile(i, layout, dy, dx);
+        th = 2 * sy + dy;
+        tw = 2 * sx + dx;
+        CHECK(th < g.nh && tw < g.nw, "unit %d tile %d outside the grid", u, i);
+        ++covered[th * g.nw + tw];
+      }
+      std::vector<int> keys;
+      for (int part = 0; part < (text_unit ? parts : 1); ++part) {
+        sta::SquareKeyStream ks;
+        ks.init(g, text_unit ? part : u, a[4], a[5], text_unit);
+        for (int j = 0; j < ks.n_blk; ++j) {
+          const sta::KeyBlock b = ks.block(g, j);
+          CHECK(j >= ks.n_plain || b.mask == sta::kKeyBlock, "unit %d block %d masked early", u, j);
+          CHECK(j != 0 || b.seen == -1, "unit %d: block 0 not seen by all", u);
+          CHECK(b.seen == -1 || (b.seen & ~((1 << tiles) - 1)) == 0, "unit %d block %d: seen bits past the unit", u, j);
+          CHECK(b.seen != 0, "unit %d block %d seen by no tile", u, j);
+          if (((b.seen >> i) & 1) == 0) continue;
+          for (int r = 0; r < b.mask; ++r) {
+            int row;
+            if (b.kind == 0) {
+              CHECK(sta::extent_tokens(b.ext) == 64, "unit %d block %d: tile of %d tokens", u, j,
+                    sta::extent_tokens(b.ext));
+              row = b.base + (r >> 3) * g.W + (r & 7);
+            } else {
+              CHECK(b.kind == 1, "unit %d block %d kind %d", u, j, b.kind);
+              row = b.base + r;
+            }
+            CHECK(row >= 0 && row < g.S, "unit %d block %d row %d outside the sequence", u, j, row);
+            keys.push_back(row);
+          }
+        }
+      }
+      std::sort(keys.begin(), keys.end());
+      for (size_t k = 1; k < keys.size(); ++k) CHECK(keys[k] != keys[k - 1], "unit %d key %d twice", u, keys[k]);
+      std::printf("unit %d %d %d %d", u, i, th, tw);
+      for (size_t k = 0; k < keys.size();) {
+        size_t e = k + 1;
+        while (e < keys.size() && keys[e] == keys[e - 1] + 1) ++e;
+        std::printf(" %d:%d", keys[k], keys[e - 1] + 1);
+        k = e;
+      }
+      std::printf("\n");
+    }
+  }
+  for (int t = 0; t < g.n_tiles; ++t) CHECK(covered[t] == 1, "tile %d in %d units", t, covered[t]);
+}
 }  // namespace
 
 int main(int argc, char** argv) {
@@ -596,6 +685,10 @@ int main(int argc, char** argv) {
   }
   if (argc >= 2 && std::strcmp(argv[1], "hstream") == 0) {
     hstream(argc, argv);
+    return 0;
+  }
+  if (argc >= 2 && std::strcmp(argv[1], "sqstream") == 0) {
+    sqstream(argc, argv);
     return 0;
   }
   std::fprintf(stderr, "usage: %s validate | dump B heads D T H W has_text ell wt wh ww | stream T H W has_text ell wt wh ww\n",

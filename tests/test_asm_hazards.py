@@ -114,23 +114,24 @@ def test_forward_kernels_no_asm_hazards(attention_asm):
     tile-multiple videos (the fast path) spill nothing."""
     kernels = H.parse(attention_asm)
     names = sorted(k.name for k in kernels)
-    assert len(kernels) == 6, names  # D in {64, 128} x (tile-multiple video, partial tiles, Hilbert)
+    # D in {64, 128} x (tile-multiple video, partial tiles, Hilbert units, square units)
+    assert len(kernels) == 8, names
     for k in kernels:
         assert len(k.instrs) > 1000, k.name
         problems = H.check_result_reads(k) + H.check_operand_writes(k)
         assert problems == [], "\n".join(problems[:10])
-        if "ELb0ELb0E" in k.name:  # PAD = false, HIL = false
+        if "ELb0ELi0E" in k.name:  # PAD = false, single-tile units
             assert k.scratch == 0, f"{k.name}: {k.scratch} bytes of scratch per lane"
             assert k.vgpr_spills == 0, f"{k.name}: {k.vgpr_spills} VGPR spills"
 
 
 def test_block_loops_wait_only_on_their_own_loads(attention_asm, backward_asm):
     """No spill reload and no compiler-placed vector-memory wait inside any
-    per-block loop of the forward, Hilbert, dq and dk/dv kernels: such a wait
+    per-block loop of the forward (all unit kinds), dq and dk/dv kernels: such a wait
     would also count the next block's LDS-DMA in flight."""
     kernels = H.parse(attention_asm) + H.parse(backward_asm, name_filter="bwd_d")
     names = sorted(k.name for k in kernels)
-    assert len(kernels) == 6 + 4 + 4, names
+    assert len(kernels) == 8 + 4 + 4, names
     for k in kernels:
         assert H.innermost_loops(k), k.name
         problems = H.check_block_loops(k)

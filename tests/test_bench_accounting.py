@@ -40,9 +40,10 @@ def test_headline_count_is_the_tile_product():
     assert bench.effective_flops(wl) == 4.0 * 128 * pairs
     assert bench.kernel_suffix(wl) == "<128, false>"
     assert bench.kernel_suffix(sta_inputs.WORKLOADS["ragged"]) == "<128, true>"
-    assert bench.attention_kernel(wl) == "sta_attention_kernel<128, false, false>"
-    assert bench.attention_kernel(sta_inputs.WORKLOADS["ragged"]) == "sta_attention_kernel<128, true, false>"
-    assert bench.attention_kernel(sta_inputs.WORKLOADS["hilbert"]) == "sta_attention_kernel<128, true, true>"
+    assert bench.attention_kernel(wl) == "sta_attention_kernel<128, false, 0>"
+    assert bench.attention_kernel(sta_inputs.WORKLOADS["ragged"]) == "sta_attention_kernel<128, true, 0>"
+    assert bench.attention_kernel(sta_inputs.WORKLOADS["hilbert"]) == "sta_attention_kernel<128, true, 1>"
+    assert bench.attention_kernel(sta_inputs.WORKLOADS["image"]) == "sta_attention_kernel<128, true, 2>"
 
 
 @pytest.mark.parametrize("mode,W", [(1, 5), (1, 16), (2, 3), (2, 4)])

@@ -92,6 +92,21 @@ def oracle_maps(video):
     return n, tile, np.bincount(tile, minlength=n[0] * n[1] * n[2])
 
 
+def forward_units(video, win, text):
+    """Query units per head of the forward: single tiles (plus one text unit),
+    or, on a one-frame video of whole 8x8 tiles whose window spans at least
+    two tiles along each axis with two or more tiles, 2x2 squares of tiles
+    plus the text rows split into min(8, max(1, tiles // 128)) parts."""
+    T, H, W = video
+    nh, nw = -(-H // 8), -(-W // 8)
+    n_tiles = -(-T // 6) * nh * nw
+    if T == 1 and H % 8 == 0 and W % 8 == 0 and (nh > 1 or nw > 1) and \
+            (win[1] >= 2 or nh == 1) and (win[2] >= 2 or nw == 1):
+        parts = min(8, max(1, n_tiles // 128)) if text else 0
+        return ((nh + 1) // 2) * ((nw + 1) // 2) + parts
+    return n_tiles + text
+
+
 @pytest.mark.parametrize("shape", SHAPES, ids=[f"{s[3]}w{s[6]}t{s[5] if s[4] else '-'}"
                                                for s in SHAPES])
 def test_helpers_match_oracle_maps(checks_bin, shape):
@@ -110,7 +125,7 @@ def test_helpers_match_oracle_maps(checks_bin, shape):
                      B * heads * (n_tiles + text)]
     geom = [int(x) for x in out[1].split()[1:]]
     assert geom == [*n, n_tiles, nv, S, n_tiles * 384, S_t, int(n_tiles * 384 == nv),
-                    n_tiles + text, ell]
+                    forward_units(video, win, text), ell]
 
     ws = [ln for ln in out if ln.startswith("ws ")]
     assert len(ws) == sum(m * m for m in n)
@@ -264,3 +279,51 @@ def test_hilbert_key_stream_matches_oracle_mask(checks_bin, shape):
         allowed = np.nonzero(hilbert_oracle.hilbert_allowed_mask(
             [row], (side, side), W, "slide" if mode == 1 else "window", ell, bool(text))[0])[0]
         assert np.array_equal(keys, allowed), f"unit {u} tile {t}"
+
+
+SQSHAPES = [
+    # H, W (one frame), has_text, ell, window (wh, ww) in tiles
+    (64, 64, 1, 226, 5, 5),      # 8x8 tiles, clamped windows at the border
+    (72, 88, 0, 0, 3, 4),        # 9x11 tiles: odd last row and column of squares, even window
+    (40, 48, 1, 100, 2, 2),      # the smallest windows that group
+    (32, 32, 1, 64, 4, 4),       # window = the whole grid
+    (8, 96, 1, 17, 1, 5),        # one tile row: a window of 1 along h still groups
+    (96, 8, 0, 0, 6, 1),         # one tile column
+    (128, 128, 1, 226, 5, 7),    # 256 tiles: the text rows split in two parts
+    (256, 256, 1, 1, 3, 3),      # 1024 tiles: eight text parts
+    (24, 24, 1, 256, 3, 3),      # 3x3 tiles, window = the grid
+    (64, 64, 1, 50, 1, 3),       # a window of 1 along h: single-tile units
+]
+
+
+@pytest.mark.parametrize("shape", SQSHAPES, ids=[f"{s[0]}x{s[1]}w{s[4]}{s[5]}t{s[3] if s[2] else '-'}"
+                                                 for s in SQSHAPES])
+def test_square_key_stream_matches_oracle_mask(checks_bin, shape):
+    """STA on a one-frame video with query units of 2x2 squares of tiles:
+    every tile of every unit sees, through the blocks whose mask holds it,
+    exactly the oracle's mask row for a query of that tile, each key once;
+    every tile is in one unit (checked in the program); the text rows (all
+    their parts together) see every video key and the valid text keys."""
+    H, W, text, ell, wh, ww = shape
+    out = run(checks_bin, "sqstream", H, W, text, ell, wh, ww).splitlines()
+    video = (1, H, W)
+    win = (1, wh, ww)
+    nh, nw = -(-H // 8), -(-W // 8)
+    groups = (wh >= 2 or nh == 1) and (ww >= 2 or nw == 1)
+    if not groups:
+        assert out == ["single"]
+        return
+    assert len(out) == nh * nw + text  # one line per query tile (and one for the text rows)
+    seen_tiles = set()
+    for ln in out:
+        f = ln.split()
+        th, tw = int(f[3]), int(f[4])
+        keys = np.concatenate([np.arange(*map(int, r.split(":"))) for r in f[5:]])
+        if th >= 0:
+            seen_tiles.add((th, tw))
+            row = th * 8 * W + tw * 8
+        else:
+            row = H * W
+        allowed = np.nonzero(oracle.allowed_mask([row], video, win, ell, bool(text))[0])[0]
+        assert np.array_equal(keys, allowed), f"unit {f[1]} tile ({th}, {tw})"
+    assert seen_tiles == {(a, b) for a in range(nh) for b in range(nw)}
