@@ -373,6 +373,13 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(KernelArgs) 
         }
       };
 
+      // grouped units: whether some row of this wave lies in a unit tile that
+      // sees a block (the wave's rows span unit tiles t_lo .. t_hi)
+      auto wave_sees = [&](int seen) {
+        const int t_lo = (wave * RPW) >> 6, t_hi = (wave * RPW + RPW - 1) >> 6;
+        return ((seen >> t_lo) & ((2 << (t_hi - t_lo)) - 1)) != 0;
+      };
+
       // ---- the main pass; m_run is known (from the max pass) when `known`
       auto main_pass = [&](bool known) {
 #pragma unroll
@@ -389,92 +396,99 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(KernelArgs) 
           const int stage = j & 1;
           asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
           __syncthreads();
-          f32x4 s[QT][4];
-          scores(s, stage, j >= n_plain ? s_cur.mask : kKeyBlock);
           const int seen = s_cur.seen;  // of block j
+          // grouped units of 32 or 16 rows per wave: a wave none of whose
+          // rows sees the block only issues its share of the next block's
+          // loads (block 0 is seen by every row; 48-row waves, whose registers
+          // leave no room for the branch, compute every block)
+          const bool work = !HIL || QT == kQT || wave_sees(seen);
+          f32x4 s[QT][4];
+          if (work) scores(s, stage, j >= n_plain ? s_cur.mask : kKeyBlock);
           if (j + 1 < n_blk) {
             s_cur = keys.block(g, j + 1);
             issue(s_cur, stage ^ 1);
           }
-          if (j == 0 && !known) {
-            float mx[QT];
-            row_max(s, mx);
+          if (work) {
+            if (j == 0 && !known) {
+              float mx[QT];
+              row_max(s, mx);
 #pragma unroll
-            for (int c = 0; c < QT; ++c) m_run[c] = mx[c] * qs;
-          }
-          // the reference of each row for this block: +inf for rows that do not see it
-          float mb[QT];
+              for (int c = 0; c < QT; ++c) m_run[c] = mx[c] * qs;
+            }
+            // the reference of each row for this block: +inf for rows that do not see it
+            float mb[QT];
 #pragma unroll
-          for (int c = 0; c < QT; ++c) mb[c] = m_run[c];
-          if constexpr (HIL) {
-            if (seen != -1) {
+            for (int c = 0; c < QT; ++c) mb[c] = m_run[c];
+            if constexpr (HIL) {
+              if (seen != -1) {
+#pragma unroll
+                for (int c = 0; c < QT; ++c) {
+                  const int row = wave * RPW + c * 16 + (lane & 15);
+                  mb[c] = ((seen >> (row >> 6)) & 1) != 0 ? m_run[c] : INFINITY;
+                }
+              }
+            }
+            // p = 2^(c s - m) rounded to bf16; O^T += V^T P^T; row sums += 1^T P^T.
+            // The exponentials of key half 1 are interleaved with the MFMAs of
+            // half 0 (they are independent), so the VALU work of that half runs
+            // under the matrix core.
+            const char* vb = lds[stage][1] + (lane >> 2) * 64 + (lane & 3) * 8;
+            // V^T fragment d of half h: keys 32h + 4(l/16) + e and
+            // 32h + 16 + 4(l/16) + e of column 16d + l%16
+            auto vload = [&](int h, int d) -> bf16x8 {
+              const char* p0 = vb + (d >> 1) * VPAIR + 32 * (d & 1) + 32 * h * 64;
+              const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p0);
+              const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0 + 16 * 64));
+              return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+            };
+            auto probs = [&](int h, bf16x8 (&pb)[QT]) {
 #pragma unroll
               for (int c = 0; c < QT; ++c) {
-                const int row = wave * RPW + c * 16 + (lane & 15);
-                mb[c] = ((seen >> (row >> 6)) & 1) != 0 ? m_run[c] : INFINITY;
+                f32x8 p;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                  p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[c][2 * h][r], qs, -mb[c]));
+                  p[4 + r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[c][2 * h + 1][r], qs, -mb[c]));
+                }
+                pb[c] = __builtin_convertvector(p, bf16x8);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                  const bf16x2 pair = {pb[c][2 * i], pb[c][2 * i + 1]};
+                  l_part[c] = __builtin_amdgcn_fdot2_f32_bf16(pair, ones2, l_part[c], false);
+                }
               }
-            }
-          }
-          // p = 2^(c s - m) rounded to bf16; O^T += V^T P^T; row sums += 1^T P^T.
-          // The exponentials of key half 1 are interleaved with the MFMAs of
-          // half 0 (they are independent), so the VALU work of that half runs
-          // under the matrix core.
-          const char* vb = lds[stage][1] + (lane >> 2) * 64 + (lane & 3) * 8;
-          // V^T fragment d of half h: keys 32h + 4(l/16) + e and
-          // 32h + 16 + 4(l/16) + e of column 16d + l%16
-          auto vload = [&](int h, int d) -> bf16x8 {
-            const char* p0 = vb + (d >> 1) * VPAIR + 32 * (d & 1) + 32 * h * 64;
-            const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p0);
-            const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0 + 16 * 64));
-            return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
-          };
-          auto probs = [&](int h, bf16x8 (&pb)[QT]) {
+            };
+            bf16x8 vf0[DT], vf1[DT], pb0[QT], pb1[QT];
 #pragma unroll
-            for (int c = 0; c < QT; ++c) {
-              f32x8 p;
-#pragma unroll
-              for (int r = 0; r < 4; ++r) {
-                p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[c][2 * h][r], qs, -mb[c]));
-                p[4 + r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[c][2 * h + 1][r], qs, -mb[c]));
-              }
-              pb[c] = __builtin_convertvector(p, bf16x8);
-#pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                const bf16x2 pair = {pb[c][2 * i], pb[c][2 * i + 1]};
-                l_part[c] = __builtin_amdgcn_fdot2_f32_bf16(pair, ones2, l_part[c], false);
-              }
-            }
-          };
-          bf16x8 vf0[DT], vf1[DT], pb0[QT], pb1[QT];
-#pragma unroll
-          for (int d = 0; d < kVPrefetch; ++d) vf0[d] = vload(0, d);
-          probs(0, pb0);
-          __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-          for (int d = 0; d < DT; ++d) {
-#pragma unroll
-            for (int c = 0; c < QT; ++c)
-              acc[c][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf0[d], pb0[c], acc[c][d], 0, 0, 0);
-            if (d + kVPrefetch < DT) vf0[d + kVPrefetch] = vload(0, d + kVPrefetch);
-          }
-          probs(1, pb1);
-#pragma unroll
-          for (int d = 0; d < kVPrefetch; ++d) vf1[d] = vload(1, d);
-          // per MFMA of half 0: one LDS read and up to 3 VALU instructions
-#pragma unroll
-          for (int i = 0; i < QT * DT; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
-          }
-          __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-          for (int d = 0; d < DT; ++d) {
-#pragma unroll
-            for (int c = 0; c < QT; ++c)
-              acc[c][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf1[d], pb1[c], acc[c][d], 0, 0, 0);
-            if (d + kVPrefetch < DT) vf1[d + kVPrefetch] = vload(1, d + kVPrefetch);
+            for (int d = 0; d < kVPrefetch; ++d) vf0[d] = vload(0, d);
+            probs(0, pb0);
             __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int d = 0; d < DT; ++d) {
+#pragma unroll
+              for (int c = 0; c < QT; ++c)
+                acc[c][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf0[d], pb0[c], acc[c][d], 0, 0, 0);
+              if (d + kVPrefetch < DT) vf0[d + kVPrefetch] = vload(0, d + kVPrefetch);
+            }
+            probs(1, pb1);
+#pragma unroll
+            for (int d = 0; d < kVPrefetch; ++d) vf1[d] = vload(1, d);
+            // per MFMA of half 0: one LDS read and up to 3 VALU instructions
+#pragma unroll
+            for (int i = 0; i < QT * DT; ++i) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+              __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+              __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int d = 0; d < DT; ++d) {
+#pragma unroll
+              for (int c = 0; c < QT; ++c)
+                acc[c][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf1[d], pb1[c], acc[c][d], 0, 0, 0);
+              if (d + kVPrefetch < DT) vf1[d + kVPrefetch] = vload(1, d + kVPrefetch);
+              __builtin_amdgcn_sched_barrier(0);
+            }
           }
         }
       };
@@ -491,6 +505,10 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(KernelArgs) 
           issue(s_j, 0);
           asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
           __syncthreads();
+          if (HIL && !wave_sees(s_j.seen)) {
+            __syncthreads();  // every wave has read the stage before it is refilled
+            continue;
+          }
           f32x4 s[QT][4];
           scores(s, 0, j >= n_plain ? s_j.mask : kKeyBlock);
           float bm[QT];
