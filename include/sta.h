@@ -93,8 +93,8 @@ int64_t sta_tiled_seq_len(const sta_dims* dims, int32_t has_text);
 
 /*
  * Bytes of device workspace sta_forward needs for these arguments, or 0 if
- * the arguments are invalid. Depends on the windows (the key-tile lists of
- * the schedule are sized by them). Pure host arithmetic: no HIP call.
+ * the arguments are invalid. Depends on the windows (they decide the query
+ * units, see sta_forward). Pure host arithmetic: no HIP call.
  */
 size_t sta_workspace_bytes(const sta_dims* dims, const int32_t* window_sizes,
                            int32_t has_text);
@@ -126,6 +126,15 @@ size_t sta_workspace_bytes(const sta_dims* dims, const int32_t* window_sizes,
  * of key tiles itself) are enqueued on `stream`. The workspace holds the work
  * order (4 bytes per query unit: B*heads*(n_t*n_h*n_w + has_text) units), 2 KB
  * of work-queue heads and a 256-byte zero row: a few KB to a few hundred KB.
+ * One-frame videos (T = 1, the 2D-image reading of README "How Does STA
+ * Work?"; H and W multiples of 8, so every tile is one 8x8 frame): when
+ * every head's window spans at least 2 tiles along each axis that has at
+ * least 2 tiles, a query unit is a 2x2 square of tiles (B*heads*
+ * ceil(n_h/2)*ceil(n_w/2) video units), and with text on images of 256 tiles
+ * or more the text rows are split over P = min(8, tiles/128) units by key
+ * tiles, whose fp32 partial results (B*heads*P*256*(D+2)*4 bytes of
+ * workspace) a third launch merges. The results are the same function of
+ * the inputs either way.
  * The attention launch is a persistent grid (one workgroup per resident slot
  * on the current device) whose workgroups take query units from per-XCD
  * queues, their own XCD's first; which workgroup runs which unit varies from
@@ -141,7 +150,8 @@ sta_status sta_forward(const sta_dims* dims, const void* q, const void* k,
  * sta_forward with stage timing, for measurement. `events` holds
  * STA_TIMED_EVENTS hipEvent_t handles (as void*, created by the caller);
  * events[0] is recorded on `stream` before the first launch and events[i]
- * after launch i of: 1 work order, 2 fused attention. hipEventElapsedTime
+ * after launch i of: 1 work order, 2 fused attention (with, for split text
+ * rows, their merge). hipEventElapsedTime
  * between consecutive events then gives each kernel's duration. Nothing else
  * differs from sta_forward; STA_ERR_NULL if events or an entry is NULL.
  */
@@ -164,10 +174,13 @@ sta_status sta_forward_timed(const sta_dims* dims, const void* q, const void* k,
  * the work-queue heads and the zero row that must start at zero are cleared
  * by the call's own first kernel. Calls that overlap on one GPU (other
  * streams, other threads) race on the array: order them on one stream.
- * Returns STA_ERR_SCRATCH, before any launch, when sta_workspace_bytes for
- * the shape exceeds STA_NOALLOC_SCRATCH_BYTES (enough for about 260 000
- * query units, B*heads*(n_t*n_h*n_w + has_text)), STA_ERR_HIP when the
- * array's address cannot be obtained, otherwise what sta_forward returns.
+ * Split text rows of one-frame videos are used only when their partial
+ * results fit the array; otherwise the text rows stay whole (same results
+ * up to rounding order). Returns STA_ERR_SCRATCH, before any launch, when
+ * the work order still exceeds STA_NOALLOC_SCRATCH_BYTES (enough for about
+ * 260 000 query units, B*heads*(n_t*n_h*n_w + has_text)), STA_ERR_HIP when
+ * the array's address cannot be obtained, otherwise what sta_forward
+ * returns.
  */
 #define STA_NOALLOC_SCRATCH_BYTES (1u << 20)
 sta_status sta_forward_noalloc(const sta_dims* dims, const void* q, const void* k,
