@@ -115,12 +115,27 @@ def attention_kernel(wl) -> str:
     return f"sta_attention_kernel{kernel_suffix(wl)[:-1]}, {grp}>"
 
 
-def measured_traffic(summary: str, kernel: str, source: str):
+# the files each kernel is compiled from; a counter summary applies only to the
+# build whose sources hash to the value recorded with it
+FORWARD_SOURCES = ("sta_attention.hip", "sta_device.h", "sta_internal.h")
+BACKWARD_SOURCES = ("sta_backward.hip", "sta_device.h", "sta_internal.h")
+
+
+def sources_hash(sources) -> str:
+    """First 16 hex digits of the SHA-256 of the source files, concatenated in order."""
+    h = hashlib.sha256()
+    for name in sources:
+        with open(os.path.join(ROOT, "block_sparse_sliding_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(summary: str, kernel: str, sources):
     """HBM bytes per launch of `kernel` from a committed rocprofv3 counter summary.
 
     `summary` is a file under profiles/; None when it is missing, holds no figure
-    for the kernel, or when `source` (the kernel's file) changed since the
-    counters were taken.
+    for the kernel, or when `sources` (the files the kernel is compiled from)
+    changed since the counters were taken.
     """
     path = os.path.join(ROOT, "profiles", summary)
     if not os.path.exists(path):
@@ -131,9 +146,8 @@ def measured_traffic(summary: str, kernel: str, source: str):
             if not line.startswith("#") and ":" in line:
                 key, _, val = line.partition(":")
                 vals[key.strip()] = val.strip()
-    with open(os.path.join(ROOT, "block_sparse_sliding_amd", "csrc", source), "rb") as f:
-        sha = hashlib.sha256(f.read()).hexdigest()[:16]
-    if vals.get("kernel_source_sha256_16") != sha:
+    if vals.get("kernel_sources") != " ".join(sources) or \
+            vals.get("kernel_sources_sha256_16") != sources_hash(sources):
         return None
     try:
         return float(vals[f"hbm_bytes_per_launch[{kernel}]"])
@@ -289,7 +303,7 @@ def main():
     attn_ms = stage_ms["attention"]
     attn_tflops = flops / (attn_ms * 1e-3) / 1e12
     attn_kernel = attention_kernel(wl)
-    traffic = measured_traffic(f"attention_{args.workload}_pmc.txt", attn_kernel, "sta_attention.hip")
+    traffic = measured_traffic(f"attention_{args.workload}_pmc.txt", attn_kernel, FORWARD_SOURCES)
     result = {
         "metric": METRIC,
         "value": tflops,
@@ -362,7 +376,7 @@ def bench_hilbert(args, wl, q, k, v, dims, out, lse):
         "roofline": {"kernel": attention_kernel(wl) + " (whole call)",
                      "bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": tflops / PEAK_BF16_TFLOPS,
-                     "traffic": measured_traffic("hilbert_pmc.txt", attention_kernel(wl), "sta_attention.hip"),
+                     "traffic": measured_traffic("hilbert_pmc.txt", attention_kernel(wl), FORWARD_SOURCES),
                      "launch_ms": ms},
     }
     if args.copy_calibration_mib > 0:
@@ -460,7 +474,7 @@ def bench_backward(args, wl, windows, q, k, v, dims, out, lse, fwd_ws):
                          "frac": t / PEAK_BF16_TFLOPS, "launch_ms": stage_ms[name],
                          "executed_flop": kfl,
                          "traffic": measured_traffic(f"backward_{args.workload}_pmc.txt", kname,
-                                                     "sta_backward.hip")}
+                                                     BACKWARD_SOURCES)}
     result = {
         "metric": "STA bwd ms/call + effective TFLOP/s (% bf16 MFMA peak)",
         "value": tflops,

@@ -430,8 +430,8 @@ struct HilbertKeyStream {
 
 // The key blocks of an STA query unit of a 2x2 square of tiles (a one-frame
 // video of whole 8x8 tiles, Geom::hilbert == kSquareUnits). Unit u of a head
-// is square (sy, sx) = (u / ceil(nw / 2), u % ceil(nw / 2)): the tiles
-// (2 sy + dy, 2 sx + dx) that exist, in the order (0,0), (0,1), (1,1), (1,0)
+// is square (sy, sx) (square_tiles: panels of square rows, column by column):
+// the tiles (2 sy + dy, 2 sx + dx) that exist, in the order (0,0), (0,1), (1,1), (1,0)
 // of (dy, dx) (square_tile), unit tile i being unit rows 64 i .. 64 i + 63.
 // Along h, the windows of the two tile rows start at sh0 and sh1 = sh0 or
 // sh0 + 1 (window_start never grows by more than one per tile), so the tiles
@@ -459,11 +459,22 @@ __host__ __device__ inline void square_tile(int i, int layout, int& dy, int& dx)
   }
 }
 
-// Tiles of square unit u (1, 2 or 4) and its layout for square_tile.
+// Square rows per panel of the unit order (below).
+constexpr int kSquarePanel = 8;
+
+// Square (sy, sx) of unit u, its tiles (1, 2 or 4) and its layout for
+// square_tile. Units run over panels of kSquarePanel square rows (the last
+// panel may be lower), each panel column by column, so a run of consecutive
+// units (what the resident workgroups of one XCD hold at once) is a compact
+// block of squares whose windows overlap in both directions.
 __host__ __device__ inline int square_tiles(const Geom& g, int u, int& sy, int& sx, int& layout) {
-  const int n_sx = (g.nw + 1) >> 1;
-  sy = u / n_sx;
-  sx = u - sy * n_sx;
+  const int n_sx = (g.nw + 1) >> 1, n_sy = (g.nh + 1) >> 1;
+  const int panel = u / (kSquarePanel * n_sx);
+  const int y0 = panel * kSquarePanel;
+  const int ph = n_sy - y0 < kSquarePanel ? n_sy - y0 : kSquarePanel;  // this panel's square rows
+  const int within = u - y0 * n_sx;
+  sx = within / ph;
+  sy = y0 + (within - sx * ph);
   const bool h1 = 2 * sy + 1 < g.nh, w1 = 2 * sx + 1 < g.nw;
   layout = h1 ? (w1 ? 0 : 2) : (w1 ? 1 : 3);
   return (h1 ? 2 : 1) * (w1 ? 2 : 1);
