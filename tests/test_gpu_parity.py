@@ -97,7 +97,7 @@ def test_small_all_rows(case):
             label=str(case))
 
 
-@pytest.mark.parametrize("name", ["notext", "text", "mixed", "large", "headline", "ragged"])
+@pytest.mark.parametrize("name", ["notext", "text", "mixed", "large", "headline", "ragged", "image"])
 def test_full_size_sampled(name):
     wl = sta_inputs.WORKLOADS[name]
     note(f"full-size {name}: {wl.describe()}")
