@@ -100,18 +100,21 @@ def kernel_suffix(wl) -> str:
 
 def square_units(wl) -> bool:
     """Whether the forward runs the workload with query units of 2x2 squares of
-    tiles: a one-frame video of whole 8x8 tiles whose every window spans at
-    least two tiles along each axis that has two or more."""
+    tiles: a one-frame video whose every window spans at least two tiles
+    along each axis that has two or more."""
     T, H, W = wl.video
     nh, nw = -(-H // TILE[1]), -(-W // TILE[2])
-    return (not wl.hilbert_len and T == 1 and H % TILE[1] == 0 and W % TILE[2] == 0 and (nh > 1 or nw > 1)
+    return (not wl.hilbert_len and T == 1 and (nh > 1 or nw > 1)
             and all((w[1] >= 2 or nh == 1) and (w[2] >= 2 or nw == 1) for w in wl.windows))
 
 
 def attention_kernel(wl) -> str:
     """Name of the forward attention kernel a workload runs: <D, PAD, GRP>, GRP
-    0 for single-tile query units, 1 for Hilbert units, 2 for 2x2 squares."""
-    grp = 1 if wl.hilbert_len else 2 if square_units(wl) else 0
+    0 for single-tile query units, 1 for Hilbert units, 2 for 2x2 squares, 3
+    for 2x2 squares on an image whose last tile row or column is partial."""
+    T, H, W = wl.video
+    partial = H % TILE[1] != 0 or W % TILE[2] != 0
+    grp = 1 if wl.hilbert_len else (3 if partial else 2) if square_units(wl) else 0
     return f"sta_attention_kernel{kernel_suffix(wl)[:-1]}, {grp}>"
 
 

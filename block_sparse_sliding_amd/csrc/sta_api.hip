@@ -90,15 +90,15 @@ int32_t grouped_text_parts(const Geom& g) {
   return parts < 1 ? 1 : parts > kHilbertTextParts ? kHilbertTextParts : parts;
 }
 
-// STA on a one-frame video of whole 8x8 tiles (a 2D image under the one-frame
-// reading): each tile holds 64 tokens, so a single-tile query unit keeps one
-// wave per SIMD busy. When every head's window spans at least two tiles along
+// STA on a one-frame video (a 2D image under the one-frame reading): each tile
+// holds at most 8x8 tokens, so a single-tile query unit keeps one wave per
+// SIMD busy. When every head's window spans at least two tiles along
 // each axis that has two tile rows (columns), query units become 2x2 squares
 // of tiles (Geom::hilbert = kSquareUnits), whose windows share a non-empty
 // core; the text rows are split by key tiles when split_text. Leaves g
 // unchanged otherwise.
 void plan_square_units(Geom* g, const Windows& win, bool split_text) {
-  if (g->T != 1 || g->H % sta::kTileH != 0 || g->W % sta::kTileW != 0) return;
+  if (g->T != 1) return;
   if (g->nh < 2 && g->nw < 2) return;
   for (int h = 0; h < g->heads; ++h) {
     const uint32_t p = win.w[h];

@@ -122,7 +122,9 @@ __device__ inline const KernelArgs* kernel_args() {
 // (KeyBlock::seen) gives the other rows a reference of +inf, so their p is
 // exactly 0. With GRP, the text rows may be split over text_parts units by
 // key tiles. Everything else is the same kernel.
-constexpr int kGrpNone = 0, kGrpHilbert = 1, kGrpSquares = 2;
+// kGrpSquaresPartial: squares on an image whose last tile row or column is
+// partial (H or W not a multiple of 8).
+constexpr int kGrpNone = 0, kGrpHilbert = 1, kGrpSquares = 2, kGrpSquaresPartial = 3;
 
 template <int D, bool PAD, int GRP>
 __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(KernelArgs) {
@@ -135,6 +137,8 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(KernelArgs) 
   constexpr int VPAIR = kKeyBlock * 64;       // bytes of one V column pair (4 KB)
   static_assert(IPW >= 1 && BLK % (1024 * kWaves) == 0, "block must split over the waves");
   constexpr bool HIL = GRP != kGrpNone;  // grouped units of 64-token tiles
+  constexpr bool SQ = GRP == kGrpSquares || GRP == kGrpSquaresPartial;  // 2x2-square units
+  constexpr bool SQP = GRP == kGrpSquaresPartial;                       // ... with partial tiles
   static_assert(!HIL || PAD, "grouped units are one-frame tiles");
   __shared__ __attribute__((aligned(1024))) char lds[2][2][BLK];  // [stage][K|V]
   __shared__ int shared_word[2];                                  // claimed unit, redo flag
@@ -171,11 +175,11 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(KernelArgs) 
     int qtt = 0, qth = 0, qtw = 0;
     int q_ext = kFullExtent, q_base = 0;
     int q_rows = text_unit ? kTextSlots : kTileRows;
-    int sq_y = 0, sq_x = 0, sq_layout = 0;  // kGrpSquares: the unit's square
+    int sq_y = 0, sq_x = 0, sq_layout = 0;  // square units: the unit's square
     if (GRP == kGrpHilbert && !text_unit) {
       const int left = g.n_tiles - g.hil_group * u;
       q_rows = kKeyBlock * (left < g.hil_group ? left : g.hil_group);  // 64 rows per tile
-    } else if (GRP == kGrpSquares && !text_unit) {
+    } else if (SQ && !text_unit) {
       q_rows = kKeyBlock * square_tiles(g, u, sq_y, sq_x, sq_layout);
     } else if (!text_unit) {
       const int rest = div_by(u, g.nw, g.mag_nw);
@@ -193,10 +197,20 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(KernelArgs) 
       if (text_unit) return g.n_video + row;
       if constexpr (HIL) {  // row r of unit tile row / 64
         int tx, ty;
-        if constexpr (GRP == kGrpSquares) {
+        if constexpr (SQ) {
           square_tile(row >> 6, sq_layout, ty, tx);
           ty += 2 * sq_y;
           tx += 2 * sq_x;
+          if constexpr (SQP) {
+            // tile (ty, tx) holds at most 8x8 tokens; a row past a partial
+            // tile's tokens maps to its last one (computed, never written)
+            const int e = tile_extent(0, ty, tx, g);
+            const int n = extent_tokens(e);
+            int r = row & 63;
+            r = r < n ? r : n - 1;
+            const int cols = extent_cols(e), dh = r / cols;
+            return (ty * kTileH + dh) * g.W + tx * kTileW + (r - dh * cols);
+          }
         } else {
           hilbert_d2xy(g.hil_m, g.hil_group * u + (row >> 6), tx, ty);
         }
@@ -215,9 +229,9 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(KernelArgs) 
 
     // key blocks: the window of the query tile, or every tile for the text unit
     const int wt = win_t(wp), wh = win_h(wp), ww = win_w(wp);
-    typename std::conditional<GRP == kGrpSquares, SquareKeyStream,
+    typename std::conditional<SQ, SquareKeyStream<SQP>,
                               typename std::conditional<HIL, HilbertKeyStream, KeyStream<PAD>>::type>::type keys;
-    if constexpr (GRP == kGrpSquares) {
+    if constexpr (SQ) {
       keys.init(g, text_unit ? u - n_vunits : u, wh, ww, text_unit);
     } else if constexpr (HIL) {
       // the window length is the w component of the head's window
@@ -403,7 +417,8 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(KernelArgs) 
           // leave no room for the branch, compute every block)
           const bool work = !HIL || QT == kQT || wave_sees(seen);
           f32x4 s[QT][4];
-          if (work) scores(s, stage, j >= n_plain ? s_cur.mask : kKeyBlock);
+          // squares with partial tiles: every block's own mask (they may come anywhere)
+          if (work) scores(s, stage, SQP || j >= n_plain ? s_cur.mask : kKeyBlock);
           if (j + 1 < n_blk) {
             s_cur = keys.block(g, j + 1);
             issue(s_cur, stage ^ 1);
@@ -510,7 +525,7 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(KernelArgs) 
             continue;
           }
           f32x4 s[QT][4];
-          scores(s, 0, j >= n_plain ? s_j.mask : kKeyBlock);
+          scores(s, 0, SQP || j >= n_plain ? s_j.mask : kKeyBlock);
           float bm[QT];
           row_max(s, bm);
 #pragma unroll
@@ -598,7 +613,16 @@ __global__ __launch_bounds__(kThreads, 1) void sta_attention_kernel(KernelArgs) 
         const float l = swap32_sum(swap16_sum(l_part[c]));
         const float inv = __builtin_amdgcn_rcpf(l);
         const int row = wave * RPW + c * 16 + (lane & 15);
-        if (row < q_rows) {
+        bool written = row < q_rows;
+        if constexpr (SQP) {
+          // rows past a partial tile's tokens are computed on its last token, not written
+          if (!text_unit && written) {
+            int ty, tx;
+            square_tile(row >> 6, sq_layout, ty, tx);
+            written = (row & 63) < extent_tokens(tile_extent(0, ty + 2 * sq_y, tx + 2 * sq_x, g));
+          }
+        }
+        if (written) {
           const int rr = query_raster(row);
           __bf16* dst = outr + size_t(rr) * D + (lane >> 4) * 4;
 #pragma unroll
@@ -684,6 +708,9 @@ hipError_t launch(const Geom& g, const Windows& win, const FwdArgs& a, hipStream
 
 hipError_t launch_attention(const Geom& g, const Windows& win, const FwdArgs& a, hipStream_t stream) {
   // one-frame images (grouped units): never a tile multiple
+  if (g.hilbert == kSquareUnits && (g.H % kTileH != 0 || g.W % kTileW != 0))
+    return g.D == 128 ? launch<128, true, kGrpSquaresPartial>(g, win, a, stream)
+                      : launch<64, true, kGrpSquaresPartial>(g, win, a, stream);
   if (g.hilbert == kSquareUnits)
     return g.D == 128 ? launch<128, true, kGrpSquares>(g, win, a, stream)
                       : launch<64, true, kGrpSquares>(g, win, a, stream);

@@ -40,8 +40,8 @@ struct Geom {
   uint32_t mag_nw, mag_nh;
   // Hilbert-window attention (2D images, T = 1, a 2^hil_m x 2^hil_m tile grid):
   // 0 = the STA box windows; 1 = Hilbert slide windows; 2 = Hilbert windows;
-  // kSquareUnits = the STA box windows on a one-frame video of whole 8x8
-  // tiles, with query units of 2x2 squares of tiles (SquareKeyStream)
+  // kSquareUnits = the STA box windows on a one-frame video (tiles of at
+  // most 8x8 tokens), with query units of 2x2 squares of tiles (SquareKeyStream)
   int32_t hilbert, hil_m;
   // tiles per grouped query unit: Hilbert 1, 4 (an aligned 2x2 square of
   // tiles) or 6 consecutive curve positions, ceil(n_tiles / hil_group) video
@@ -429,7 +429,9 @@ struct HilbertKeyStream {
 };
 
 // The key blocks of an STA query unit of a 2x2 square of tiles (a one-frame
-// video of whole 8x8 tiles, Geom::hilbert == kSquareUnits). Unit u of a head
+// video, Geom::hilbert == kSquareUnits; a tile is one frame of at most 8x8
+// tokens, fewer in the last tile row or column when H or W is not a multiple
+// of 8). Unit u of a head
 // is square (sy, sx) (square_tiles: panels of square rows, column by column):
 // the tiles (2 sy + dy, 2 sx + dx) that exist, in the order (0,0), (0,1), (1,1), (1,0)
 // of (dy, dx) (square_tile), unit tile i being unit rows 64 i .. 64 i + 63.
@@ -442,7 +444,9 @@ struct HilbertKeyStream {
 // cores overlap reach a shared tile at the same step), then the rows above
 // and below the core across the full width, then the columns left and right
 // of the core over its rows, each block with the mask of the unit's tiles
-// that see it (KeyBlock::seen), then the text blocks as in KeyStream. The
+// that see it (KeyBlock::seen), then the text blocks as in KeyStream. With
+// partial tiles every block carries its own mask (the tokens of a partial
+// tile, the valid text keys), which the kernel applies to every block. The
 // core is never empty when wh >= 2 and ww >= 2, or the square has a single
 // tile row (column) along the axis where the window is 1, so block 0 is seen
 // by every row of the unit. A text unit streams the key tiles of its part in
@@ -480,6 +484,9 @@ __host__ __device__ inline int square_tiles(const Geom& g, int u, int& sy, int& 
   return (h1 ? 2 : 1) * (w1 ? 2 : 1);
 }
 
+// PARTIAL: the image has a partial last tile row or column (H or W not a
+// multiple of 8); with PARTIAL false every tile is a whole 8x8 frame.
+template <bool PARTIAL>
 struct SquareKeyStream {
   int ch, cw, Ch, Cw;  // the core: tile rows [ch, ch + Ch), tile columns [cw, cw + Cw)
   int mh, mw;          // 1 when the square's windows differ along h (w): one row (column) on each side
@@ -559,11 +566,14 @@ struct SquareKeyStream {
         }
         s.seen = seen;
       }
-      s.kind = 0;
+      // a whole 8x8 tile is one full frame; a partial one (last tile row or
+      // column of an image whose side is not a multiple of 8) holds fewer
+      // tokens, fetched in compact order, the rest of its block masked
       s.base = kh * kTileH * g.W + kw * kTileW;
-      s.lim = kKeyBlock;
       s.ext = tile_extent(0, kh, kw, g);
-      s.mask = kKeyBlock;
+      s.lim = PARTIAL ? extent_tokens(s.ext) : kKeyBlock;
+      s.kind = !PARTIAL || s.lim == kKeyBlock ? 0 : 2;
+      s.mask = s.lim;
     } else {
       const int tb = j < n_plain ? j - n_vfull : n_tfull;
       s.kind = 1;

@@ -127,7 +127,7 @@ size_t sta_workspace_bytes(const sta_dims* dims, const int32_t* window_sizes,
  * order (4 bytes per query unit: B*heads*(n_t*n_h*n_w + has_text) units), 2 KB
  * of work-queue heads and a 256-byte zero row: a few KB to a few hundred KB.
  * One-frame videos (T = 1, the 2D-image reading of README "How Does STA
- * Work?"; H and W multiples of 8, so every tile is one 8x8 frame): when
+ * Work?"; every tile is one frame of at most 8x8 tokens): when
  * every head's window spans at least 2 tiles along each axis that has at
  * least 2 tiles, a query unit is a 2x2 square of tiles (B*heads*
  * ceil(n_h/2)*ceil(n_w/2) video units), and with text on images of 256 tiles

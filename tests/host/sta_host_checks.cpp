@@ -577,7 +577,7 @@ void hstream(int argc, char** argv) {
 }
 
 
-// "sqstream <H> <W> <has_text> <ell> <wh> <ww>": STA on a one-frame video
+// "sqstream <H> <W> <has_text> <ell> <wh> <ww>": STA on a one-frame video (any H, W)
 // (T = 1) as the forward plans it; with square units, one line per query tile
 // of every unit, "unit u i tile_h tile_w" then its key rows as in `stream`,
 // and one line for the text rows (tile -1 -1, every part's keys); "single"
@@ -626,11 +626,21 @@ void sqstream(int argc, char** argv) {
       }
       std::vector<int> keys;
       for (int part = 0; part < (text_unit ? parts : 1); ++part) {
-        sta::SquareKeyStream ks;
+        // the kernel's stream: with partial tiles when H or W is not a multiple of 8
+        sta::SquareKeyStream<true> ks;
+        sta::SquareKeyStream<false> kw;
+        const bool partial = g.H % 8 != 0 || g.W % 8 != 0;
         ks.init(g, text_unit ? part : u, a[4], a[5], text_unit);
+        kw.init(g, text_unit ? part : u, a[4], a[5], text_unit);
+        CHECK(ks.n_blk == kw.n_blk, "unit %d: block counts differ", u);
         for (int j = 0; j < ks.n_blk; ++j) {
-          const sta::KeyBlock b = ks.block(g, j);
-          CHECK(j >= ks.n_plain || b.mask == sta::kKeyBlock, "unit %d block %d masked early", u, j);
+          const sta::KeyBlock b = partial ? ks.block(g, j) : kw.block(g, j);
+          if (!partial) {
+            const sta::KeyBlock bp = ks.block(g, j);
+            CHECK(bp.kind == b.kind && bp.base == b.base && bp.mask == b.mask && bp.seen == b.seen,
+                  "unit %d block %d: streams differ on whole tiles", u, j);
+          }
+          CHECK(b.mask >= 1 && b.mask <= sta::kKeyBlock, "unit %d block %d mask %d", u, j, b.mask);
           CHECK(j != 0 || b.seen == -1, "unit %d: block 0 not seen by all", u);
           CHECK(b.seen == -1 || (b.seen & ~((1 << tiles) - 1)) == 0, "unit %d block %d: seen bits past the unit", u, j);
           CHECK(b.seen != 0, "unit %d block %d seen by no tile", u, j);
@@ -638,9 +648,15 @@ void sqstream(int argc, char** argv) {
           for (int r = 0; r < b.mask; ++r) {
             int row;
             if (b.kind == 0) {
-              CHECK(sta::extent_tokens(b.ext) == 64, "unit %d block %d: tile of %d tokens", u, j,
+              CHECK(sta::extent_tokens(b.ext) == 64 && b.mask == 64, "unit %d block %d: tile of %d tokens", u, j,
                     sta::extent_tokens(b.ext));
               row = b.base + (r >> 3) * g.W + (r & 7);
+            } else if (b.kind == 2) {
+              CHECK(b.sub == 0 && b.mask == sta::extent_tokens(b.ext) && b.mask < 64, "unit %d block %d partial", u, j);
+              int dt, dh, dw;
+              sta::compact_token(r, b.ext, dt, dh, dw);
+              CHECK(dt == 0, "unit %d block %d frame %d", u, j, dt);
+              row = b.base + dh * g.W + dw;
             } else {
               CHECK(b.kind == 1, "unit %d block %d kind %d", u, j, b.kind);
               row = b.base + r;

@@ -2,7 +2,8 @@
 with query units of 2x2 squares of tiles.
 
 Reading (the page's 2D STA names no tile size): a 2D image is a video of one
-frame, so each (6, 8, 8) tile holds one 8x8 frame of 64 tokens. When every
+frame, so each (6, 8, 8) tile holds one frame of at most 8x8 tokens (fewer
+in the last tile row or column when H or W is not a multiple of 8). When every
 head's window spans at least two tiles along each axis that has two tile
 rows (columns), the forward groups the query tiles in 2x2 squares; the
 blocks on the edge of the four windows' union are seen by only some of the
@@ -36,6 +37,10 @@ CASES = [
     (1, 64, (96, 8), [(6, 1), (3, 1)], 0, False),        # one tile column
     (1, 128, (24, 24), [(3, 3)], 256, True),             # 3x3 tiles, window = grid, every text slot valid
     (1, 128, (56, 40), [(4, 2), (7, 5)], 1, True),       # 7x5 tiles
+    (1, 128, (100, 100), [(6, 6), (3, 2)], 64, True),    # 13x13 tiles, last row and column 4 wide
+    (1, 64, (44, 30), [(3, 2)], 0, False),               # partial tiles along both axes
+    (2, 128, (90, 40), [(5, 5)], 226, True),             # a last tile row 2 rows high
+    (1, 128, (5, 100), [(1, 4)], 10, True),              # one partial tile row
 ]
 IDS = [f"i{i}" for i in range(len(CASES))]
 
@@ -59,7 +64,7 @@ def square_units(video, windows, has_text):
     """Video query units per head the forward plans: 2x2 squares, or None."""
     T, H, W = video
     nh, nw = -(-H // 8), -(-W // 8)
-    ok = T == 1 and H % 8 == 0 and W % 8 == 0 and (nh > 1 or nw > 1) and \
+    ok = T == 1 and (nh > 1 or nw > 1) and \
         all((w[1] >= 2 or nh == 1) and (w[2] >= 2 or nw == 1) for w in windows)
     return ((nh + 1) // 2) * ((nw + 1) // 2) if ok else None
 

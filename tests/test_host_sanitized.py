@@ -94,14 +94,13 @@ def oracle_maps(video):
 
 def forward_units(video, win, text):
     """Query units per head of the forward: single tiles (plus one text unit),
-    or, on a one-frame video of whole 8x8 tiles whose window spans at least
+    or, on a one-frame video whose window spans at least
     two tiles along each axis with two or more tiles, 2x2 squares of tiles
     plus the text rows split into min(8, max(1, tiles // 128)) parts."""
     T, H, W = video
     nh, nw = -(-H // 8), -(-W // 8)
     n_tiles = -(-T // 6) * nh * nw
-    if T == 1 and H % 8 == 0 and W % 8 == 0 and (nh > 1 or nw > 1) and \
-            (win[1] >= 2 or nh == 1) and (win[2] >= 2 or nw == 1):
+    if T == 1 and (nh > 1 or nw > 1) and (win[1] >= 2 or nh == 1) and (win[2] >= 2 or nw == 1):
         parts = min(8, max(1, n_tiles // 128)) if text else 0
         return ((nh + 1) // 2) * ((nw + 1) // 2) + parts
     return n_tiles + text
@@ -184,7 +183,7 @@ STREAM_SHAPES = [
     ((5, 7, 9), 0, 0, (1, 1, 2)),         # one partial tile: remainder blocks only
     ((1, 1, 1), 1, 256, (1, 1, 1)),
     ((6, 8, 8), 1, 17, (1, 1, 1)),
-    ((1, 100, 100), 1, 64, (1, 6, 6)),
+    ((1, 100, 100), 1, 64, (1, 1, 6)),   # one frame, a window of 1 tile along h: single-tile units
     ((9, 11, 3), 1, 1, (2, 2, 1)),
 ]
 
@@ -293,6 +292,11 @@ SQSHAPES = [
     (256, 256, 1, 1, 3, 3),      # 1024 tiles: eight text parts
     (24, 24, 1, 256, 3, 3),      # 3x3 tiles, window = the grid
     (64, 64, 1, 50, 1, 3),       # a window of 1 along h: single-tile units
+    (100, 100, 1, 64, 6, 6),     # 13x13 tiles, the last row and column of 4 rows / 4 columns
+    (90, 160, 1, 226, 5, 5),     # a 720p latent: 12x20 tiles, the last tile row 2 rows high
+    (44, 30, 0, 0, 3, 2),        # partial tiles along both axes
+    (5, 100, 1, 10, 1, 4),       # one partial tile row
+    (100, 3, 0, 0, 3, 1),        # one partial tile column
 ]
 
 
