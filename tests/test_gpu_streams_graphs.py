@@ -2,9 +2,10 @@
 
 * Captured in a HIP graph (torch.cuda.CUDAGraph), sta_forward followed by
   sta_backward replays to the same bits as the eager calls, replay after
-  replay, with other eager work and synchronisations in between. Every
-  launch is a kernel (the queue heads are zeroed by a kernel, not a memset),
-  so the calls are capturable.
+  replay, with other eager work and synchronisations in between, on a video,
+  on partial tiles and on 2D images whose text rows are split and merged.
+  Every launch is a kernel (the queue heads are zeroed by a kernel, not a
+  memset), so the calls are capturable.
 * Two sta_forward calls running at once on two streams, each with its own
   workspace, give the same bits as the same calls run one after the other:
   the per-XCD queues and their heads live in each call's workspace.
@@ -40,20 +41,27 @@ def bits(t):
     return t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
 
 
-@pytest.mark.parametrize("video", [VIDEO, (17, 21, 30)])
-def test_graph_replays_match_eager(video):
-    note(f"graph capture of forward + backward {video}")
+# a video, partial tiles, and 2D images of 272 and 289 tiles: square query
+# units whose text rows are split in two parts and merged by a third launch
+# (whole 8x8 tiles, and a partial last tile row and column)
+GRAPH_CASES = [(VIDEO, WINDOWS), ((17, 21, 30), WINDOWS),
+               ((1, 128, 136), [(1, 3, 3), (1, 2, 5)]), ((1, 130, 133), [(1, 3, 3), (1, 2, 5)])]
+
+
+@pytest.mark.parametrize("video,windows", GRAPH_CASES, ids=["video", "partial", "image", "image-partial"])
+def test_graph_replays_match_eager(video, windows):
+    note(f"graph capture of forward + backward {video} {windows}")
     q, k, v, dout = tensors(11, video=video)
     dims = sta.make_dims(1, 2, 128, video)
-    fws = torch.empty(sta.sta_workspace_bytes(dims, WINDOWS, True), dtype=torch.uint8, device="cuda")
-    bws = torch.empty(sta.sta_backward_workspace_bytes(dims, WINDOWS, True), dtype=torch.uint8,
+    fws = torch.empty(sta.sta_workspace_bytes(dims, windows, True), dtype=torch.uint8, device="cuda")
+    bws = torch.empty(sta.sta_backward_workspace_bytes(dims, windows, True), dtype=torch.uint8,
                       device="cuda")
     out, dq, dk, dv = (torch.empty_like(q) for _ in range(4))
     lse = torch.empty(1, 2, seq(video), dtype=torch.float32, device="cuda")
 
     def step():
-        sta.sta_forward(dims, q, k, v, WINDOWS, ELL, True, out, lse, fws)
-        sta.sta_backward(dims, q, k, v, out, lse, dout, WINDOWS, ELL, True, dq, dk, dv, bws)
+        sta.sta_forward(dims, q, k, v, windows, ELL, True, out, lse, fws)
+        sta.sta_backward(dims, q, k, v, out, lse, dout, windows, ELL, True, dq, dk, dv, bws)
 
     # eager reference (and warm-up on a side stream, as graph capture expects)
     side = torch.cuda.Stream()
