@@ -5,6 +5,8 @@
 // are reported synchronously and can be exercised without a GPU.
 #include <atomic>
 #include <cmath>
+#include <cstdio>
+#include <cstdlib>
 #include <cstring>
 
 #include "../../include/sta.h"
@@ -23,6 +25,36 @@ constexpr int kHilbertTextParts = 8;
 constexpr int kHilbertTextPartTiles = 128;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// STA_LOG set (and not "0") in the environment: every forward and backward
+// call prints its derived schedule to stderr before it enqueues anything.
+bool log_enabled() {
+  static const bool on = [] {
+    const char* e = std::getenv("STA_LOG");
+    return e != nullptr && e[0] != '\0' && std::strcmp(e, "0") != 0;
+  }();
+  return on;
+}
+
+// One line: the call, its geometry, the query units and their kind, the
+// window of head 0 and how many heads have other windows, the workspace.
+void log_schedule(const char* call, const sta::Geom& g, const sta::Windows& win, int64_t units_per_head,
+                  size_t workspace) {
+  if (!log_enabled()) return;
+  const char* kind = g.hilbert == sta::kSquareUnits ? "2x2-square"
+                     : g.hilbert != 0               ? "hilbert"
+                                                    : "single-tile";
+  int other = 0;
+  for (int h = 1; h < g.heads; ++h) other += win.w[h] != win.w[0] ? 1 : 0;
+  std::fprintf(stderr,
+               "[sta] %s: B=%d heads=%d D=%d video=(%d,%d,%d) tiles=(%d,%d,%d)=%d text=%d/%d S=%d "
+               "units/head=%lld (%s%s, text parts %d) window[0]=(%d,%d,%d) heads with another window=%d "
+               "workspace=%zu bytes\n",
+               call, g.B, g.heads, g.D, g.T, g.H, g.W, g.nt, g.nh, g.nw, g.n_tiles, g.text_length,
+               g.has_text ? 256 : 0, g.S, static_cast<long long>(units_per_head), kind,
+               g.full ? "" : ", partial tiles", g.text_parts, sta::win_t(win.w[0]), sta::win_h(win.w[0]),
+               sta::win_w(win.w[0]), other, workspace);
+}
 
 sta_status make_geom(const sta_dims* d, int32_t has_text, int32_t text_length, Geom* g) {
   if (d == nullptr) return STA_ERR_NULL;
@@ -313,6 +345,7 @@ sta_status forward_launch(Geom g, const Windows& win, const void* q, const void*
     if (lse != nullptr && overlaps(lse, lbytes, in, n)) return STA_ERR_ALIAS;
   }
   if (lse != nullptr && overlaps(lse, lbytes, out, tbytes)) return STA_ERR_ALIAS;
+  log_schedule("sta_forward", g, win, g.n_q, c.total);
 
   char* ws = static_cast<char*>(workspace);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -575,6 +608,8 @@ sta_status backward_impl(const sta_dims* dims, const void* q, const void* k, con
     for (int o2 = o + 1; o2 < 3; ++o2)
       if (overlaps(outs[o], tbytes, outs[o2], tbytes)) return STA_ERR_ALIAS;
   }
+  // dq units: two parts per tile (+ the text slots); dk/dv the same
+  log_schedule("sta_backward", g, win, 2 * int64_t(g.n_tiles) + (g.has_text ? 1 : 0), c.total);
 
   char* ws = static_cast<char*>(workspace);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);

@@ -36,6 +36,12 @@
  *   Work is enqueued asynchronously; the return value reports argument
  *   errors (found on the host before anything is enqueued) and launch
  *   errors. Faults inside kernels surface at the caller's next stream sync.
+ * - Environment: with STA_LOG set to anything but "" or "0", every
+ *   sta_forward and sta_backward call (and their _timed and _noalloc forms)
+ *   prints one line to stderr, after its arguments are validated and before
+ *   it enqueues anything: the geometry, the query units per head and their
+ *   kind (single tiles, 2x2 squares, Hilbert runs), the text parts, head 0's
+ *   window and the workspace bytes.
  * - window_sizes is a HOST array of heads*3 int32: (w_t, w_h, w_w) in tiles
  *   for head 0, then head 1, ... Each component must lie in [1, n_axis]
  *   where (n_t, n_h, n_w) = (ceil(T/6), ceil(H/8), ceil(W/8)). At the grid

@@ -331,3 +331,32 @@ def test_square_key_stream_matches_oracle_mask(checks_bin, shape):
         allowed = np.nonzero(oracle.allowed_mask([row], video, win, ell, bool(text))[0])[0]
         assert np.array_equal(keys, allowed), f"unit {f[1]} tile ({th}, {tw})"
     assert seen_tiles == {(a, b) for a in range(nh) for b in range(nw)}
+
+
+def test_sta_log_prints_the_schedule(checks_bin):
+    """STA_LOG=1: a forward call prints its derived schedule to stderr (the
+    query units and their kind, the text parts, the workspace) before any
+    launch; without STA_LOG nothing is printed."""
+    def stderr_of(env_extra, *args):
+        env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:abort_on_error=0",
+                   UBSAN_OPTIONS="print_stacktrace=1:halt_on_error=1", **env_extra)
+        env.pop("LD_PRELOAD", None)
+        if not env_extra:
+            env.pop("STA_LOG", None)
+        r = subprocess.run([checks_bin, *map(str, args)], stdout=subprocess.PIPE,
+                           stderr=subprocess.PIPE, text=True, env=env)
+        assert r.returncode == 0, r.stderr[-4000:]
+        return r.stderr
+    # a 512x512 image, window 5x5 tiles: 32x32 squares plus 8 text parts
+    err = stderr_of({"STA_LOG": "1"}, "sqstream", 512, 512, 1, 226, 5, 5)
+    lines = [ln for ln in err.splitlines() if ln.startswith("[sta] sta_forward:")]
+    assert lines, err[-2000:]
+    ln = lines[-1]
+    assert "video=(1,512,512)" in ln and "tiles=(1,64,64)=4096" in ln, ln
+    assert "units/head=1032 (2x2-square, partial tiles, text parts 8)" in ln, ln
+    assert "window[0]=(1,5,5)" in ln, ln
+    # a video: single-tile units, one text unit
+    err = stderr_of({"STA_LOG": "1"}, "stream", 30, 48, 80, 1, 226, 3, 3, 3)
+    ln = [x for x in err.splitlines() if x.startswith("[sta] sta_forward:")][-1]
+    assert "tiles=(5,6,10)=300" in ln and "units/head=301 (single-tile, text parts 1)" in ln, ln
+    assert "[sta]" not in stderr_of({}, "stream", 30, 48, 80, 1, 226, 3, 3, 3)
