@@ -608,8 +608,19 @@ sta_status backward_impl(const sta_dims* dims, const void* q, const void* k, con
     for (int o2 = o + 1; o2 < 3; ++o2)
       if (overlaps(outs[o], tbytes, outs[o2], tbytes)) return STA_ERR_ALIAS;
   }
-  // dq units: two parts per tile (+ the text slots); dk/dv the same
-  log_schedule("sta_backward", g, win, 2 * int64_t(g.n_tiles) + (g.has_text ? 1 : 0), c.total);
+  // one-frame videos whose windows allow the forward's 2x2-square units: the
+  // dq pass uses them too (Geom::hilbert marks it; the key lists, indexed by
+  // n_q, stay those of single tiles for the dk/dv pass)
+  {
+    Geom gs = g;
+    plan_square_units(&gs, win, false);
+    if (gs.hilbert == sta::kSquareUnits) g.hilbert = sta::kSquareUnits;
+  }
+  // dq units: two parts per tile, or one square of tiles, (+ the text slots)
+  log_schedule("sta_backward", g, win,
+               g.hilbert == sta::kSquareUnits ? int64_t((g.nh + 1) / 2) * ((g.nw + 1) / 2) + (g.has_text ? 1 : 0)
+                                              : 2 * int64_t(g.n_tiles) + (g.has_text ? 1 : 0),
+               c.total);
 
   char* ws = static_cast<char*>(workspace);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);

@@ -211,9 +211,21 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(Geom g, const __bf16* __r
 // the 256 text query slots (8 waves x 32 rows). Unit order: text units first,
 // then the tiles.
 __device__ inline int dq_units_per_head(const Geom& g) { return 2 * g.n_tiles + (g.has_text ? 1 : 0); }
+// SQ: a one-frame video whose query units are 2x2 squares of tiles (as in the
+// forward, SquareKeyStream): one unit of 64 rows per tile per square, plus the
+// text slots
+__device__ inline int dq_square_units_per_head(const Geom& g) {
+  return ((g.nh + 1) >> 1) * ((g.nw + 1) >> 1) + (g.has_text ? 1 : 0);
+}
 
-template <int D, bool PAD>
-__global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(KernelArgs) {
+// The dq pass, for single-tile units (SQ false: bwd_dq_kernel) or 2x2-square
+// units (SQ true: bwd_dq_square_kernel). In a square unit a wave's 32 rows
+// lie in one tile, and a wave whose tile does not see a key block (edge
+// blocks of the four windows' union, KeyBlock::seen) skips it: its rows'
+// P would be 0. Key rows past a partial tile's tokens come from the zero row,
+// so they add nothing to dq.
+template <int D, bool PAD, bool SQ>
+__device__ __forceinline__ void dq_pass() {
   constexpr int KS = D / 32;
   constexpr int DT = D / 16;
   constexpr int ROWB = D * 2;
@@ -235,7 +247,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(KernelArgs) {
     __syncthreads();
     if (threadIdx.x == 0) {
       const KernelArgs* ka = kernel_args();
-      const int n_qu = dq_units_per_head(ka->g);
+      const int n_qu = SQ ? dq_square_units_per_head(ka->g) : dq_units_per_head(ka->g);
       claimed = claim_entry(ka->a.claim_q, ka->g.B * ka->g.heads * n_qu, xcd_id());
     }
     __syncthreads();
@@ -250,14 +262,24 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(KernelArgs) {
 
     // entry -> unit: the B*heads text units first, then (bh, tile, part)
     const int n_text_units = g.has_text ? g.B * g.heads : 0;
-    const int unit = entry_unit(entry, g.B * g.heads * dq_units_per_head(g), n_text_units);
+    const int unit = entry_unit(
+        entry, g.B * g.heads * (SQ ? dq_square_units_per_head(g) : dq_units_per_head(g)), n_text_units);
     int bh, u;  // u: list index into the forward schedule (tile, or n_tiles for text)
     int q_row0, q_rows;
+    const bool vsq = SQ && unit >= n_text_units;  // a square of video tiles
+    int sq_y = 0, sq_x = 0, sq_layout = 0;
     if (unit < n_text_units) {
       bh = unit;
       u = g.n_tiles;
       q_row0 = g.n_vt;
       q_rows = kTextSlots;
+    } else if (SQ) {
+      const int n_sq = dq_square_units_per_head(g) - (g.has_text ? 1 : 0);
+      const int e = unit - n_text_units;
+      bh = e / n_sq;
+      u = 0;  // (no key list: the square's key stream)
+      q_row0 = 0;
+      q_rows = kKeyBlock * square_tiles(g, e - bh * n_sq, sq_y, sq_x, sq_layout);
     } else {
       const int e = unit - n_text_units;
       bh = e / (2 * g.n_tiles);
@@ -270,7 +292,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(KernelArgs) {
     // order (frame, row, column), part 1 starting at token 256; n_valid of
     // them exist (possibly none: the unit then streams nothing)
     int q_ext = kFullExtent, q_base = 0, n_valid = q_rows;
-    if constexpr (PAD) {
+    if constexpr (PAD && !SQ) {
       if (unit >= n_text_units) {
         const int rest = div_by(u, g.nw, g.mag_nw);
         const int tw = u - rest * g.nw;
@@ -284,6 +306,21 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(KernelArgs) {
     // unit row `row` -> raster row and tile-major row (the index of lse2 and
     // delta); rows at or past n_valid map to the last existing one
     auto query_rows = [&](int row, int& raster, int& tiled) {
+      if constexpr (SQ) {
+        if (vsq) {  // row r of unit tile row / 64; rows past a tile's tokens map to its last one
+          int ty, tx;
+          square_tile(row >> 6, sq_layout, ty, tx);
+          ty += 2 * sq_y;
+          tx += 2 * sq_x;
+          const int e = tile_extent(0, ty, tx, g);
+          const int n = extent_tokens(e);
+          const int r = (row & 63) < n ? (row & 63) : n - 1;
+          const int cols = extent_cols(e), dh = r / cols;
+          raster = (ty * kTileH + dh) * g.W + tx * kTileW + (r - dh * cols);
+          tiled = (ty * g.nw + tx) * kTileRows + r;  // compact layout, one frame per tile
+          return;
+        }
+      }
       if constexpr (PAD) {
         if (unit >= n_text_units) {
           const int first = q_row0 - u * kTileRows;  // 0 or 256
@@ -307,12 +344,22 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(KernelArgs) {
     const float* __restrict__ lse2 = a.lse2 + size_t(bh) * g.S_t;
     const float* __restrict__ dlt = a.delta + size_t(bh) * g.S_t;
 
+    SquareKeyStream<true> keys;
+    if constexpr (SQ) {
+      if (vsq) {
+        const uint32_t p = ka->win.w[hd];
+        keys.init(g, (unit - n_text_units) % (dq_square_units_per_head(g) - (g.has_text ? 1 : 0)), win_h(p),
+                  win_w(p), false);
+      }
+    }
     const int l0 = a.offsets[hd * g.n_q + u];
     const int l1 = a.offsets[hd * g.n_q + u + 1];
     // video key blocks: six per listed tile; with PAD, ceil(tokens / 64) per
     // tile (as in the forward)
     int n_vid = (l1 - l0) * BPT;
-    if constexpr (PAD) {
+    if (vsq) {
+      n_vid = keys.n_vfull;
+    } else if constexpr (PAD) {
       if (unit < n_text_units) {
         n_vid = box_blocks(0, g.nt, 0, g.nh, 0, g.nw, g);
       } else {  // the list is the query tile's window, a box
@@ -336,6 +383,15 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(KernelArgs) {
     int tile_ext = kFullExtent;  // PAD: packed extent of the current tile
     int cur_t = 0, cur_sub = -1;  // PAD: the forward's walk over existing frames
     auto block_rows = [&](int j, int& kbase, int& krs) {
+      if (vsq && j < n_vid) {  // one block per key tile (at most 8x8 tokens)
+        const KeyBlock b = keys.block(g, j);
+        tile_kbase = b.base;
+        tile_ext = b.ext;
+        cur_sub = 0;
+        kbase = b.base;
+        krs = g.W;
+        return;
+      }
       if (j < n_vid) {
         int t, sub;
         if constexpr (PAD) {
@@ -519,7 +575,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(KernelArgs) {
       for (int step = 0; step < n_steps; ++step) {
         const int stage = step & 1;
         const int j = SPLIT * step + grp;  // this wave's block
-        const bool has = j < n_blk;
+        bool has = j < n_blk;
+        if (vsq && has && j < n_vid)  // square units: blocks this wave's tile does not see
+          has = ((keys.block(g, j).seen >> ((wrow * RPW) >> 6)) & 1) != 0;
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
         const char* kblk = lds[stage][2 * grp];
@@ -607,6 +665,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(KernelArgs) {
       for (int c = 0; c < QT; ++c) {
         const int row = wrow * RPW + c * 16 + (lane & 15);
         if (PAD && row >= n_valid) continue;  // no such token
+        if (vsq) {  // rows past a partial tile's tokens
+          int ty, tx;
+          square_tile(row >> 6, sq_layout, ty, tx);
+          if ((row & 63) >= extent_tokens(tile_extent(0, ty + 2 * sq_y, tx + 2 * sq_x, g))) continue;
+        }
         int rr, rt;
         query_rows(row, rr, rt);
         __bf16* dst = dqr + size_t(rr) * D + (lane >> 4) * 4;
@@ -624,6 +687,15 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(KernelArgs) {
     else
       run(std::integral_constant<int, 2>{}, std::integral_constant<int, 2>{});
   }
+}
+
+template <int D, bool PAD>
+__global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(KernelArgs) {
+  dq_pass<D, PAD, false>();
+}
+template <int D>
+__global__ __launch_bounds__(kThreads, 1) void bwd_dq_square_kernel(KernelArgs) {
+  dq_pass<D, true, true>();
 }
 
 // ---------------------------------------------------------------- dk, dv
@@ -1076,6 +1148,16 @@ hipError_t launch_dq(const Geom& g, const Windows& win, const BwdArgs& a, hipStr
   bwd_dq_kernel<D, PAD><<<grid, kThreads, 0, stream>>>(KernelArgs{g, win, a});
   return hipGetLastError();
 }
+template <int D>
+hipError_t launch_dq_square(const Geom& g, const Windows& win, const BwdArgs& a, hipStream_t stream) {
+  static int cache[kMaxDevices] = {};
+  const int units = g.B * g.heads * (((g.nh + 1) / 2) * ((g.nw + 1) / 2) + (g.has_text ? 1 : 0));
+  const int resident = resident_workgroups(bwd_dq_square_kernel<D>, kThreads, cache);
+  if (resident <= 0) return hipErrorInvalidDevice;
+  const int grid = units < resident ? units : resident;
+  bwd_dq_square_kernel<D><<<grid, kThreads, 0, stream>>>(KernelArgs{g, win, a});
+  return hipGetLastError();
+}
 template <int D, bool PAD>
 hipError_t launch_dkv(const Geom& g, const Windows& win, const BwdArgs& a, hipStream_t stream) {
   static int cache[kMaxDevices] = {};
@@ -1109,6 +1191,8 @@ hipError_t launch_bwd_prep(const Geom& g, const void* out, const void* dout, con
 }
 
 hipError_t launch_bwd_dq(const Geom& g, const Windows& win, const BwdArgs& a, hipStream_t stream) {
+  if (g.hilbert == kSquareUnits)  // a one-frame video with 2x2-square query units
+    return g.D == 128 ? launch_dq_square<128>(g, win, a, stream) : launch_dq_square<64>(g, win, a, stream);
   if (g.full) return g.D == 128 ? launch_dq<128, false>(g, win, a, stream) : launch_dq<64, false>(g, win, a, stream);
   return g.D == 128 ? launch_dq<128, true>(g, win, a, stream) : launch_dq<64, true>(g, win, a, stream);
 }

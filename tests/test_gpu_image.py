@@ -24,7 +24,9 @@ import pytest
 import torch
 
 import block_sparse_sliding_amd as sta
+import oracle
 from _parity import compare, note, oracle_rows, run_sta, scale_key_tiles
+from test_gpu_backward import compare_grad, run_backward
 
 pytestmark = pytest.mark.gpu
 
@@ -160,3 +162,33 @@ def test_square_units_noalloc_matches():
     rows = np.arange(nv, S)
     ro, rl = oracle_rows(q, k, v, windows, ell, True, video, rows=rows)
     compare(o2, l2, ro, rl, rows=torch.as_tensor(rows, device="cuda"), label="squares noalloc text")
+
+
+BWD_CASES = [
+    # (B, D, image (H, W), windows (wh, ww) per head, text_length, has_text)
+    (1, 128, (64, 64), [(5, 5), (2, 3)], 226, True),
+    (1, 64, (72, 88), [(3, 4)], 0, False),
+    (1, 128, (100, 100), [(6, 6)], 64, True),     # partial last tile row and column
+    (2, 128, (44, 30), [(3, 2)], 17, True),
+]
+
+
+@pytest.mark.parametrize("case", BWD_CASES, ids=[f"b{i}" for i in range(len(BWD_CASES))])
+def test_square_units_backward_all_rows(case):
+    """The backward on one-frame videos: the dq pass runs 2x2-square query
+    units (waves skip the edge blocks their tile does not see), the dk/dv pass
+    single key tiles; every gradient row against the oracle's."""
+    B, D, (H, W), hw, ell, has_text = case
+    video = (1, H, W)
+    windows = [(1, a, b) for a, b in hw]
+    assert square_units(video, windows, has_text) is not None
+    S = H * W + (256 if has_text else 0)
+    note(f"square units backward {case}")
+    q, k, v, dout = inputs(7000 + S + D, B, len(windows), S, D) + inputs(7001 + S, B, len(windows), S, D)[:1]
+    out, lse = run_sta(q, k, v, windows, ell, has_text, video)
+    dq, dk, dv = run_backward(q, k, v, out, lse, dout, windows, ell, has_text, video)
+    rq, rk, rv = oracle.sta_reference_backward(q.cpu(), k.cpu(), v.cpu(), dout.cpu(), windows, ell,
+                                               has_text, video)
+    compare_grad(dq, rq, f"dq {case}")
+    compare_grad(dk, rk, f"dk {case}")
+    compare_grad(dv, rv, f"dv {case}")
