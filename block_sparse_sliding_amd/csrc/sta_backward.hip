@@ -707,8 +707,16 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_square_kernel(KernelArgs) 
 // (bh, tile, part).
 __device__ inline int kv_units_per_head(const Geom& g) { return 2 * g.n_tiles + (g.has_text ? 1 : 0); }
 
-template <int D, bool PAD>
-__global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(KernelArgs) {
+// SQ: a one-frame video whose key units are 2x2 squares of tiles: 64 keys per
+// tile, so a wave's keys lie in one tile; the unit streams the union of its
+// tiles' query boxes, and a wave skips the query tiles that do not see its key
+// tile (there P is not 0: the skip is what keeps them out).
+__device__ inline int kv_square_units_per_head(const Geom& g) {
+  return ((g.nh + 1) >> 1) * ((g.nw + 1) >> 1) + (g.has_text ? 1 : 0);
+}
+
+template <int D, bool PAD, bool SQ>
+__device__ __forceinline__ void dkv_pass() {
   constexpr int KS = D / 32;
   constexpr int DT = D / 16;
   constexpr int ROWB = D * 2;
@@ -727,7 +735,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(KernelArgs) {
     __syncthreads();  // as in the dq kernel
     if (threadIdx.x == 0) {
       const KernelArgs* ka = kernel_args();
-      const int n_ku = kv_units_per_head(ka->g);
+      const int n_ku = SQ ? kv_square_units_per_head(ka->g) : kv_units_per_head(ka->g);
       claimed = claim_entry(ka->a.claim_kv, ka->g.B * ka->g.heads * n_ku, xcd_id());
     }
     __syncthreads();
@@ -741,9 +749,12 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(KernelArgs) {
     const BwdArgs a = ka->a;
 
     const int n_text_units = g.has_text ? g.B * g.heads : 0;
-    const int unit = entry_unit(entry, g.B * g.heads * kv_units_per_head(g), n_text_units);
+    const int unit = entry_unit(
+        entry, g.B * g.heads * (SQ ? kv_square_units_per_head(g) : kv_units_per_head(g)), n_text_units);
     int bh, key_row0, unit_keys;
     bool text_unit;
+    const bool ksq = SQ && unit >= n_text_units;  // a square of key tiles
+    int sq_y = 0, sq_x = 0, sq_layout = 0;
     int box_t = 0, box_h = 0, box_w = 0, lo_t = 0, lo_h = 0, lo_w = 0;
     // PAD: the keys of a video unit are its tile's existing tokens in compact
     // order (frame, row, column), part 1 starting at token 256; n_keys of them
@@ -754,6 +765,24 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(KernelArgs) {
       key_row0 = g.n_vt;
       unit_keys = kTextSlots;
       text_unit = true;
+    } else if (SQ) {
+      const int n_sq = kv_square_units_per_head(g) - (g.has_text ? 1 : 0);
+      const int e = unit - n_text_units;
+      bh = e / n_sq;
+      unit_keys = kKeyBlock * square_tiles(g, e - bh * n_sq, sq_y, sq_x, sq_layout);
+      key_row0 = 0;
+      n_keys = unit_keys;
+      text_unit = false;
+      const uint32_t p = ka->win.w[bh % g.heads];
+      const bool h1 = sq_layout == 0 || sq_layout == 2, w1 = sq_layout == 0 || sq_layout == 1;
+      int lo1, len1;
+      seeing_interval(0, win_t(p), g.nt, lo_t, box_t);
+      seeing_interval(2 * sq_y, win_h(p), g.nh, lo_h, box_h);
+      seeing_interval(2 * sq_y + (h1 ? 1 : 0), win_h(p), g.nh, lo1, len1);
+      box_h = lo1 + len1 - lo_h;
+      seeing_interval(2 * sq_x, win_w(p), g.nw, lo_w, box_w);
+      seeing_interval(2 * sq_x + (w1 ? 1 : 0), win_w(p), g.nw, lo1, len1);
+      box_w = lo1 + len1 - lo_w;
     } else {
       const int e = unit - n_text_units;
       bh = e / (2 * g.n_tiles);
@@ -926,6 +955,20 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(KernelArgs) {
       // are read from
       auto key_rows = [&](int ln, int kg, int& ksrc) {
         const int local = wslot * 16 * KT + 16 * kg + (ln & 15);
+        if constexpr (SQ) {
+          if (ksq) {  // key local & 63 of unit tile local / 64; past its tokens: its last, never written
+            int ty, tx;
+            square_tile(local >> 6, sq_layout, ty, tx);
+            ty += 2 * sq_y;
+            tx += 2 * sq_x;
+            const int e = tile_extent(0, ty, tx, g);
+            const int n = extent_tokens(e);
+            const int r = (local & 63) < n ? (local & 63) : n - 1;
+            const int cols = extent_cols(e), dh = r / cols;
+            ksrc = (ty * kTileH + dh) * g.W + tx * kTileW + (r - dh * cols);
+            return (local & 63) < n ? ksrc : -1;
+          }
+        }
         int kras = PAD ? tiled_to_raster(key_row0 + local, g) : tiled_to_raster_full(key_row0 + local, g);
         ksrc = kras;
         if constexpr (PAD) {
@@ -1008,12 +1051,31 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(KernelArgs) {
         }
         return;
       }
+      // square units: the query rows [sh0, sh1) and columns [sw0, sw1) of the
+      // box whose tiles see this wave's key tile (block j is box tile j)
+      int sh0 = 0, sh1 = 0, sw0 = 0, sw1 = 0;
+      if (ksq) {
+        const uint32_t p = ka->win.w[bh % g.heads];
+        int ky, kx;
+        square_tile((wslot * 16 * KT) >> 6, sq_layout, ky, kx);
+        seeing_interval(2 * sq_y + ky, win_h(p), g.nh, sh0, sh1);
+        seeing_interval(2 * sq_x + kx, win_w(p), g.nw, sw0, sw1);
+        sh0 -= lo_h;
+        sh1 += sh0;
+        sw0 -= lo_w;
+        sw1 += sw0;
+      }
       for (int step = 0; step < n_steps; ++step) {
         const int stage = step & 1;
         const int j = SPLIT * step + grp;  // this wave's block
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        if (j >= n_blk) {  // SPLIT = 2, odd block count: the last step has one block
+        bool seen = true;
+        if (ksq && j < n_vblk) {
+          const int r = j / box_w, c = j - r * box_w;
+          seen = sh0 <= r && r < sh1 && sw0 <= c && c < sw1;
+        }
+        if (j >= n_blk || !seen) {  // (SPLIT = 2, odd block count: the last step has one block)
           if (step + 1 < n_steps) issue(step + 1, stage ^ 1);
           continue;
         }
@@ -1139,6 +1201,15 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(KernelArgs) {
 }
 
 template <int D, bool PAD>
+__global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(KernelArgs) {
+  dkv_pass<D, PAD, false>();
+}
+template <int D>
+__global__ __launch_bounds__(kThreads, 1) void bwd_dkv_square_kernel(KernelArgs) {
+  dkv_pass<D, true, true>();
+}
+
+template <int D, bool PAD>
 hipError_t launch_dq(const Geom& g, const Windows& win, const BwdArgs& a, hipStream_t stream) {
   static int cache[kMaxDevices] = {};
   const int units = g.B * g.heads * (2 * g.n_tiles + (g.has_text ? 1 : 0));
@@ -1156,6 +1227,16 @@ hipError_t launch_dq_square(const Geom& g, const Windows& win, const BwdArgs& a,
   if (resident <= 0) return hipErrorInvalidDevice;
   const int grid = units < resident ? units : resident;
   bwd_dq_square_kernel<D><<<grid, kThreads, 0, stream>>>(KernelArgs{g, win, a});
+  return hipGetLastError();
+}
+template <int D>
+hipError_t launch_dkv_square(const Geom& g, const Windows& win, const BwdArgs& a, hipStream_t stream) {
+  static int cache[kMaxDevices] = {};
+  const int units = g.B * g.heads * (((g.nh + 1) / 2) * ((g.nw + 1) / 2) + (g.has_text ? 1 : 0));
+  const int resident = resident_workgroups(bwd_dkv_square_kernel<D>, kThreads, cache);
+  if (resident <= 0) return hipErrorInvalidDevice;
+  const int grid = units < resident ? units : resident;
+  bwd_dkv_square_kernel<D><<<grid, kThreads, 0, stream>>>(KernelArgs{g, win, a});
   return hipGetLastError();
 }
 template <int D, bool PAD>
@@ -1198,6 +1279,8 @@ hipError_t launch_bwd_dq(const Geom& g, const Windows& win, const BwdArgs& a, hi
 }
 
 hipError_t launch_bwd_dkv(const Geom& g, const Windows& win, const BwdArgs& a, hipStream_t stream) {
+  if (g.hilbert == kSquareUnits)  // a one-frame video with 2x2-square units
+    return g.D == 128 ? launch_dkv_square<128>(g, win, a, stream) : launch_dkv_square<64>(g, win, a, stream);
   if (g.full) return g.D == 128 ? launch_dkv<128, false>(g, win, a, stream) : launch_dkv<64, false>(g, win, a, stream);
   return g.D == 128 ? launch_dkv<128, true>(g, win, a, stream) : launch_dkv<64, true>(g, win, a, stream);
 }
