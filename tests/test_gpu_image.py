@@ -176,8 +176,8 @@ BWD_CASES = [
 @pytest.mark.parametrize("case", BWD_CASES, ids=[f"b{i}" for i in range(len(BWD_CASES))])
 def test_square_units_backward_all_rows(case):
     """The backward on one-frame videos: the dq pass runs 2x2-square query
-    units (waves skip the edge blocks their tile does not see), the dk/dv pass
-    single key tiles; every gradient row against the oracle's."""
+    units and the dk/dv pass 2x2-square key units (waves skip the blocks their
+    tile does not see); every gradient row against the oracle's."""
     B, D, (H, W), hw, ell, has_text = case
     video = (1, H, W)
     windows = [(1, a, b) for a, b in hw]
